@@ -1,0 +1,256 @@
+"""Float64 CPU oracle for the fused edge tensor-product convolution.
+
+TEST INFRASTRUCTURE. Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import this module. The product (the HIP
+library and its Python binding) never imports it, and the two share no code.
+
+This module is a thin ctypes wrapper over ``etp_oracle.c`` (plain C, double
+precision, loops edge by edge). It compiles that file with gcc on first use if
+the shared library is missing or older than the source.
+
+Array conventions (all numpy, C-contiguous):
+  row_ptr[n_dst+1], src[E]          int32, destination-sorted CSR
+  vec[E, 3]                         bond vectors r_src - r_dst
+  x[n_src, Din, C]                  Din = (lin+1)^2, row l*l + l + m
+  w[E, P, C]                        per-edge, per-path, per-channel weight
+  out / G[n_dst, Dout, C]           Dout = sum_p (2 l3_p + 1)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "etp_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i8p = ctypes.POINTER(ctypes.c_int8)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+
+def build(force: bool = False) -> str:
+    """Compile etp_oracle.c into liboracle.so (gcc, -O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC",
+                               _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        # ORACLE_LIB lets the mutation test load a deliberately broken copy
+        path = os.environ.get("ORACLE_LIB")
+        if not path:
+            path = build()
+        lib = ctypes.CDLL(path)
+        lib.oracle_cg_complex.restype = ctypes.c_double
+        lib.oracle_cg_complex.argtypes = [ctypes.c_int] * 6
+        lib.oracle_cg_real_dense.restype = ctypes.c_double
+        lib.oracle_cg_real_dense.argtypes = [ctypes.c_int] * 3 + [_f64p]
+        lib.oracle_paths.restype = ctypes.c_int
+        lib.oracle_paths.argtypes = [ctypes.c_int] * 3 + [_i32p, ctypes.c_int]
+        lib.oracle_cg_sparse.restype = ctypes.c_int
+        lib.oracle_cg_sparse.argtypes = [ctypes.c_int] * 3 + [_i32p, _i8p, _f64p, ctypes.c_int]
+        lib.oracle_dims.restype = ctypes.c_int
+        lib.oracle_dims.argtypes = [ctypes.c_int] * 3 + [_i32p]
+        lib.oracle_sh_point.restype = None
+        lib.oracle_sh_point.argtypes = [ctypes.c_int, _f64p, _f64p, _f64p, _f64p, _f64p]
+        lib.oracle_sh.restype = None
+        lib.oracle_sh.argtypes = [ctypes.c_int, ctypes.c_int64, _f64p, _f64p, _f64p]
+        lib.oracle_transpose.restype = None
+        lib.oracle_transpose.argtypes = [ctypes.c_int, ctypes.c_int, _i32p, _i32p,
+                                         _i32p, _i32p, _i32p]
+        lib.oracle_fwd.restype = ctypes.c_int
+        lib.oracle_fwd.argtypes = [ctypes.c_int] * 5 + [_i32p, _i32p] + [_f64p] * 4
+        lib.oracle_vjp.restype = ctypes.c_int
+        lib.oracle_vjp.argtypes = [ctypes.c_int] * 6 + [_i32p, _i32p] + [_f64p] * 7
+        lib.oracle_vjp2.restype = ctypes.c_int
+        lib.oracle_vjp2.argtypes = [ctypes.c_int] * 6 + [_i32p, _i32p] + [_f64p] * 11
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def _lmax(L):
+    if isinstance(L, (tuple, list)):
+        return int(L[0]), int(L[1]), int(L[2])
+    return int(L), int(L), int(L)
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _p(a, t):
+    if a is None:
+        return None
+    return a.ctypes.data_as(t)
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def cg_complex(j1, m1, j2, m2, J, M) -> float:
+    return _load().oracle_cg_complex(j1, m1, j2, m2, J, M)
+
+
+def cg_real_dense(l1, l2, l3):
+    """Dense real coupling tensor [2l1+1, 2l2+1, 2l3+1] and the largest discarded part."""
+    out = np.zeros((2 * l1 + 1) * (2 * l2 + 1) * (2 * l3 + 1), np.float64)
+    disc = _load().oracle_cg_real_dense(l1, l2, l3, _p(out, _f64p))
+    return out.reshape(2 * l1 + 1, 2 * l2 + 1, 2 * l3 + 1), disc
+
+
+def paths(L) -> np.ndarray:
+    lin, lsh, lout = _lmax(L)
+    n = _load().oracle_paths(lin, lsh, lout, None, 0)
+    out = np.zeros((n, 3), np.int32)
+    _load().oracle_paths(lin, lsh, lout, _p(out, _i32p), n)
+    return out
+
+
+def cg_sparse(L):
+    """(ptr[P+1], m[nnz, 3] signed m values, val[nnz]) for all paths of L."""
+    lin, lsh, lout = _lmax(L)
+    lib = _load()
+    P = lib.oracle_paths(lin, lsh, lout, None, 0)
+    nnz = lib.oracle_cg_sparse(lin, lsh, lout, None, None, None, 0)
+    ptr = np.zeros(P + 1, np.int32)
+    m = np.zeros((nnz, 3), np.int8)
+    val = np.zeros(nnz, np.float64)
+    lib.oracle_cg_sparse(lin, lsh, lout, _p(ptr, _i32p), _p(m, _i8p), _p(val, _f64p), nnz)
+    return ptr, m, val
+
+
+def dims(L):
+    """dict(P, nnz, Din, Dsh, Dout) -- Din/Dout per channel."""
+    lin, lsh, lout = _lmax(L)
+    d = np.zeros(5, np.int32)
+    if _load().oracle_dims(lin, lsh, lout, _p(d, _i32p)):
+        raise ValueError("unsupported l_max")
+    return dict(P=int(d[0]), nnz=int(d[1]), Din=int(d[2]), Dsh=int(d[3]), Dout=int(d[4]))
+
+
+def sh_point(L: int, r, v=None):
+    """(Y[D], dY[3, D], HV[3, D] or None) at one point r; HV_k = d/dr_k (grad Y . v)."""
+    D = (L + 1) ** 2
+    r = _f64(r)
+    Y = np.zeros(D)
+    dY = np.zeros((3, D))
+    HV = np.zeros((3, D)) if v is not None else None
+    vv = _f64(v) if v is not None else None
+    _load().oracle_sh_point(L, _p(r, _f64p), _p(vv, _f64p), _p(Y, _f64p), _p(dY, _f64p),
+                            _p(HV, _f64p))
+    return Y, dY, HV
+
+
+def sh(L: int, vec, grad: bool = False):
+    """Y[E, D] (and dY[E, 3, D] if grad) for bond vectors vec[E, 3]."""
+    vec = _f64(vec).reshape(-1, 3)
+    E = vec.shape[0]
+    D = (L + 1) ** 2
+    Y = np.zeros((E, D))
+    dY = np.zeros((E, 3, D)) if grad else None
+    _load().oracle_sh(L, E, _p(vec, _f64p), _p(Y, _f64p), _p(dY, _f64p))
+    return (Y, dY) if grad else Y
+
+
+def transpose(row_ptr, src, n_src):
+    """Stable CSR transpose: (src_ptr[n_src+1], perm[E], perm_dst[E]), int32."""
+    row_ptr = _i32(row_ptr)
+    src = _i32(src)
+    n_dst = row_ptr.shape[0] - 1
+    E = int(row_ptr[-1])
+    sp = np.zeros(n_src + 1, np.int32)
+    perm = np.zeros(max(E, 1), np.int32)
+    pdst = np.zeros(max(E, 1), np.int32)
+    _load().oracle_transpose(n_dst, n_src, _p(row_ptr, _i32p), _p(src, _i32p),
+                             _p(sp, _i32p), _p(perm, _i32p), _p(pdst, _i32p))
+    return sp, perm[:E], pdst[:E]
+
+
+def _graph(row_ptr, src):
+    row_ptr = _i32(row_ptr)
+    src = _i32(src) if len(src) else np.zeros(1, np.int32)
+    return row_ptr, src, row_ptr.shape[0] - 1
+
+
+def fwd(L, row_ptr, src, vec, x, w):
+    """out[n_dst, Dout, C]."""
+    lin, lsh, lout = _lmax(L)
+    row_ptr, src, n_dst = _graph(row_ptr, src)
+    x = _f64(x)
+    C = x.shape[2]
+    d = dims(L)
+    out = np.zeros((n_dst, d["Dout"], C))
+    vec = _f64(vec).reshape(-1)
+    w = _f64(w).reshape(-1)
+    rc = _load().oracle_fwd(lin, lsh, lout, C, n_dst, _p(row_ptr, _i32p), _p(src, _i32p),
+                            _p(_nz(vec), _f64p), _p(x, _f64p), _p(_nz(w), _f64p), _p(out, _f64p))
+    if rc:
+        raise ValueError("oracle_fwd failed")
+    return out
+
+
+def _nz(a):
+    return a if a.size else np.zeros(1)
+
+
+def vjp(L, row_ptr, src, vec, x, w, G):
+    """(gx[n_src, Din, C], gw[E, P, C], gr[E, 3])."""
+    lin, lsh, lout = _lmax(L)
+    row_ptr, src, n_dst = _graph(row_ptr, src)
+    x = _f64(x)
+    n_src, _, C = x.shape
+    E = int(row_ptr[-1])
+    d = dims(L)
+    gx = np.zeros_like(x)
+    gw = np.zeros((max(E, 1), d["P"], C))
+    gr = np.zeros((max(E, 1), 3))
+    rc = _load().oracle_vjp(lin, lsh, lout, C, n_dst, n_src, _p(row_ptr, _i32p), _p(src, _i32p),
+                            _p(_nz(_f64(vec).reshape(-1)), _f64p), _p(x, _f64p),
+                            _p(_nz(_f64(w).reshape(-1)), _f64p), _p(_nz(_f64(G).reshape(-1)), _f64p),
+                            _p(gx, _f64p), _p(gw, _f64p), _p(gr, _f64p))
+    if rc:
+        raise ValueError("oracle_vjp failed")
+    return gx, gw[:E], gr[:E]
+
+
+def vjp2(L, row_ptr, src, vec, x, w, G, Xp=None, Wp=None, Rp=None):
+    """(dx[n_src, Din, C], dw[E, P, C], dr[E, 3], dG[n_dst, Dout, C]); None cotangent = 0."""
+    lin, lsh, lout = _lmax(L)
+    row_ptr, src, n_dst = _graph(row_ptr, src)
+    x = _f64(x)
+    n_src, _, C = x.shape
+    E = int(row_ptr[-1])
+    d = dims(L)
+    dx = np.zeros_like(x)
+    dw = np.zeros((max(E, 1), d["P"], C))
+    dr = np.zeros((max(E, 1), 3))
+    dG = np.zeros((n_dst, d["Dout"], C))
+    Xp = _f64(Xp) if Xp is not None else None
+    Wp = _nz(_f64(Wp).reshape(-1)) if Wp is not None else None
+    Rp = _nz(_f64(Rp).reshape(-1)) if Rp is not None else None
+    rc = _load().oracle_vjp2(lin, lsh, lout, C, n_dst, n_src, _p(row_ptr, _i32p), _p(src, _i32p),
+                             _p(_nz(_f64(vec).reshape(-1)), _f64p), _p(x, _f64p),
+                             _p(_nz(_f64(w).reshape(-1)), _f64p),
+                             _p(_nz(_f64(G).reshape(-1)), _f64p),
+                             _p(Xp, _f64p), _p(Wp, _f64p), _p(Rp, _f64p),
+                             _p(dx, _f64p), _p(dw, _f64p), _p(dr, _f64p), _p(dG, _f64p))
+    if rc:
+        raise ValueError("oracle_vjp2 failed")
+    return dx, dw[:E], dr[:E], dG
