@@ -1,0 +1,257 @@
+"""Benchmark of the fused edge tensor-product convolution on one MI355X.
+
+One step = one pass of the whole device path over the synthetic
+microbenchmark graph (1024 nodes x 128 random neighbours, C = 128 channels,
+l_max = 2, fp32 -- the edge-convolution microbenchmark shape of "How does
+FlashCart make equivariant interatomic potentials faster and more
+accurate?", section "Generated kernels beat SH baselines at high order"):
+
+    CSR transpose -> forward -> VJP (gx, gw, forces) -> VJP-of-VJP
+    (dG destination pass, then dx / dw / dr source pass)
+
+value = edges per second of the whole step (inputs resident in HBM).
+Per-op times come from HIP events recorded on the launch stream inside the
+timed region; the roofline is reported for the op that takes the most time,
+with its algorithmic bytes (every tensor it must touch, once) and
+algorithmic FLOPs per edge. The float64 oracle is timed on the host on a
+bounded sample of destination rows of the same graph.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload micro]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "edges/sec for fused edge TP conv (fwd, fwd+VJP) + % of HBM/VALU roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+VALU_PEAK_TFLOPS = 157.3       # MI355X fp32 vector (packed); 78.6 without packing
+WORKLOADS = {
+    "micro": "1024 nodes x 128 random neighbours (131072 edges), C=128, l_max=2, fp32",
+    "micro3": "1024 nodes x 128 random neighbours (131072 edges), C=128, l_max=3, fp32",
+    "micro4": "1024 nodes x 128 random neighbours (131072 edges), C=128, l_max=4, fp32",
+    "water": "5184-atom water box, 6 A cutoff, C=64, l_max=2, fp32",
+    "tiny": "32 nodes x 8 random neighbours (256 edges), C=8, l_max=1, fp32",
+}
+OPS = ("transpose", "fwd", "vjp", "vjp2_dst", "vjp2_src")
+
+
+def table_counts(L):
+    """(P, nnz, pairs, Din, Dout) from the library's own tables."""
+    from equivariant_interatomic_potentials_amd import etp
+    plan = etp.etp_plan_create(L, 8)
+    t = etp.etp_plan_tables(plan)
+    P = plan.P
+    pairs = 0
+    d1 = []
+    d3 = []
+    for p in range(P):
+        l1, l2, l3 = t["paths"][p]
+        ms = t["cg_m"][t["cg_ptr"][p]:t["cg_ptr"][p + 1]]
+        pairs += len({(int(a), int(c)) for a, _, c in ms})
+        d1.append(2 * l1 + 1)
+        d3.append(2 * l3 + 1)
+    return dict(P=P, nnz=plan.nnz, pairs=pairs, Din=plan.din_rows, Dout=plan.dout_rows,
+                d1=np.array(d1), d3=np.array(d3))
+
+
+def algorithmic(L, C, N, E, n_src):
+    """Per-op algorithmic bytes (each tensor touched once) and FLOPs (2 per FMA)."""
+    k = table_counts(L)
+    P, nnz, pairs, Din, Dout = k["P"], k["nnz"], k["pairs"], k["Din"], k["Dout"]
+    f4 = 4
+    w = E * P * C * f4
+    x = n_src * Din * C * f4
+    out = N * Dout * C * f4
+    vec = E * 3 * f4
+    idx = E * 4
+    by = {
+        "transpose": idx * 4 + (n_src + 1) * 4 + (N + 1) * 4,
+        "fwd": w + x + out + vec + idx + (N + 1) * 4,
+        "vjp": 2 * w + x + out + 2 * vec + 2 * idx + x + (n_src + 1) * 4,
+        "vjp2_dst": 2 * w + 2 * x + out + 2 * vec + idx + (N + 1) * 4,
+        "vjp2_src": 3 * w + 2 * x + out + 3 * vec + 2 * idx + x + (n_src + 1) * 4,
+    }
+    sum_min = int(np.minimum(k["d1"], k["d3"]).sum())
+    s1 = int(k["d1"].sum())
+    fma_ch = {
+        "transpose": 0,
+        "fwd": nnz + sum_min,
+        "vjp": 2 * nnz + pairs + 3 * s1,
+        "vjp2_dst": 2 * nnz + 3 * s1,
+        "vjp2_src": 4 * nnz + 2 * pairs + 6 * s1,
+    }
+    fl = {op: 2 * fma_ch[op] * C * E for op in by}
+    return by, fl
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "equivariant_interatomic_potentials_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(op):
+    """HBM bytes per launch of `op` from committed rocprofv3 counter runs, if
+    they were taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch", {}).get(op)
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The oracle, as it is, on the first R destination rows of the graph
+    (R sized to about budget_s of host time); edges/s of fwd + VJP + VJP2."""
+    import oracle
+    L = wl.L
+
+    def run(R):
+        rp = wl.row_ptr[:R + 1].copy()
+        e1 = int(rp[-1])
+        src, vec, w = wl.src[:e1], wl.vec[:e1], wl.w[:e1]
+        G = wl.G[:R]
+        t0 = time.perf_counter()
+        oracle.transpose(rp, src, wl.n)
+        oracle.fwd(L, rp, src, vec, wl.x, w)
+        oracle.vjp(L, rp, src, vec, wl.x, w, G)
+        oracle.vjp2(L, rp, src, vec, wl.x, w, G, wl.ggx, wl.ggw[:e1], wl.ggvec[:e1])
+        return e1, time.perf_counter() - t0
+
+    e_probe, t_probe = run(min(4, wl.n_dst))
+    per_edge = t_probe / max(e_probe, 1)
+    R = int(min(wl.n_dst, max(4, budget_s / max(per_edge, 1e-9) / max(wl.E / wl.n_dst, 1))))
+    e1, t = run(R)
+    return {"value": e1 / t, "unit": "edges/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {R} destination rows ({e1} edges) of the same graph; transpose + fwd + VJP + "
+                      f"VJP2 in float64, {t:.1f} s wall"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="micro", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    a = ap.parse_args(argv)
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the convolution would shard by destination node with halo exchanges; "
+              "that exchange is not built). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads
+    from equivariant_interatomic_potentials_amd import etp
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    wl = workloads.get(a.workload)
+    L, C, N, E, n_src = wl.L, wl.C, wl.n_dst, wl.E, wl.n
+    cuda = lambda arr: torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+    plan = etp.etp_plan_create(L, C)
+    row_ptr, src, vec, x, w, G = (cuda(wl.row_ptr), cuda(wl.src), cuda(wl.vec), cuda(wl.x), cuda(wl.w),
+                                  cuda(wl.G))
+    ggx, ggw, ggv = cuda(wl.ggx), cuda(wl.ggw), cuda(wl.ggvec)
+    src_ptr = torch.empty(n_src + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(E, dtype=torch.int32, device="cuda")
+    perm_dst = torch.empty(E, dtype=torch.int32, device="cuda")
+    ws = torch.empty(etp.etp_csr_transpose_workspace(n_src) // 4 + 1, dtype=torch.int32, device="cuda")
+    g0 = etp.Graph(N, n_src, row_ptr, src)
+    g = etp.Graph(N, n_src, row_ptr, src, src_ptr, perm, perm_dst)
+    out = torch.empty(N, wl.Dout, C, device="cuda")
+    gx, gw, gr = torch.empty_like(x), torch.empty_like(w), torch.empty_like(vec)
+    dx, dw, dr, dG = torch.empty_like(x), torch.empty_like(w), torch.empty_like(vec), torch.empty_like(G)
+
+    ops = {
+        "transpose": lambda: etp.etp_csr_transpose(g0, src_ptr, perm, perm_dst, ws),
+        "fwd": lambda: etp.etp_edge_conv_fwd(plan, g, vec, x, w, out),
+        "vjp": lambda: etp.etp_edge_conv_vjp(plan, g, vec, x, w, G, gx, gw, gr),
+        "vjp2_dst": lambda: etp.etp_edge_conv_vjp2(plan, g, vec, x, w, G, ggx, ggw, ggv, d_grad_out=dG),
+        "vjp2_src": lambda: etp.etp_edge_conv_vjp2(plan, g, vec, x, w, G, ggx, ggw, ggv, d_x=dx, d_w=dw, d_vec=dr),
+    }
+
+    def step(events=None):
+        for i, op in enumerate(OPS):
+            if events is not None:
+                events[i][0].record()
+            ops[op]()
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in OPS]
+           for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(a.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_op_ms = {op: float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(a.steps)]))
+                 for i, op in enumerate(OPS)}
+
+    by, fl = algorithmic(L, C, N, E, n_src)
+    ms_step = wall / a.steps * 1e3
+    value = E * a.steps / wall
+    op_report = {}
+    for op in OPS:
+        t = per_op_ms[op] * 1e-3
+        op_report[op] = {"ms": round(per_op_ms[op], 4), "edges_per_s": E / t,
+                         "algo_GBps": by[op] / t / 1e9, "algo_TFLOPs": fl[op] / t / 1e12,
+                         "hbm_frac": by[op] / t / 1e9 / HBM_PEAK_GBS,
+                         "valu_frac": fl[op] / t / 1e12 / VALU_PEAK_TFLOPS}
+    fwd_vjp = E / ((per_op_ms["fwd"] + per_op_ms["vjp"]) * 1e-3)
+    dom = max(("fwd", "vjp", "vjp2_dst", "vjp2_src"), key=lambda o: per_op_ms[o])
+    d = op_report[dom]
+    if d["hbm_frac"] >= d["valu_frac"]:
+        roof = {"bound": "hbm", "achieved": round(d["algo_GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(d["hbm_frac"], 4)}
+    else:
+        roof = {"bound": "alu", "achieved": round(d["algo_TFLOPs"], 2), "peak": VALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(d["valu_frac"], 4)}
+    tr = measured_traffic(dom)
+    roof["traffic"] = tr
+    roof["kernel"] = dom
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "edges/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{a.workload}: {WORKLOADS[a.workload]}", "n_nodes": N, "n_edges": E,
+                   "channels": C, "l_max": L,
+                   "step": "csr_transpose + fwd + vjp + vjp2(dG) + vjp2(dx,dw,dr)"},
+        "fwd_edges_per_s": op_report["fwd"]["edges_per_s"],
+        "fwd_vjp_edges_per_s": fwd_vjp,
+        "ops": op_report,
+        "roofline": roof,
+    }
+    if not a.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,407 @@
+// etp_api.hip -- the C ABI declared in include/etp.h: plan creation and
+// table readback, host-side argument validation, and dispatch to the
+// per-l_max kernel launchers.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "../../include/etp.h"
+#include "etp_conv_common.hpp"
+
+namespace etp {
+
+hipError_t launch_sh(int L, int64_t n, const float *vec, float *Y, float *dY, hipStream_t stream);
+size_t transpose_workspace_bytes(int n_src);
+hipError_t launch_transpose(int n_dst, int n_src, int64_t E, const int *row_ptr, const int *src, int *src_ptr,
+                            int *perm, int *perm_dst, void *ws, hipStream_t stream);
+hipError_t launch_validate(int n_dst, int n_src, int64_t E, const int *row_ptr, const int *src, int *bad,
+                           hipStream_t stream);
+
+const Table *table_for(int L)
+{
+    switch (L) {
+    case 0: return &kTab<0>;
+    case 1: return &kTab<1>;
+    case 2: return &kTab<2>;
+    case 3: return &kTab<3>;
+    case 4: return &kTab<4>;
+    default: return nullptr;
+    }
+}
+
+}  // namespace etp
+
+struct etp_plan_s {
+    int L, C, dtype;
+    const etp::Table *T;
+};
+
+namespace {
+
+constexpr int64_t kMaxEdges = 0x7FFFFFFF;
+
+etp_status hip_status(hipError_t e) { return e == hipSuccess ? ETP_OK : ETP_ERR_HIP; }
+
+etp_status check_graph(const etp_graph *g, bool need_transpose)
+{
+    if (!g)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (g->n_dst < 0 || g->n_src < 0 || g->n_edges < 0)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (g->n_edges >= kMaxEdges)
+        return ETP_ERR_UNSUPPORTED;
+    if (g->n_dst > 0 && !g->row_ptr)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (g->n_edges > 0 && (!g->src || g->n_src == 0 || g->n_dst == 0))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (need_transpose) {
+        if (g->n_src > 0 && !g->src_ptr)
+            return ETP_ERR_INVALID_ARGUMENT;
+        if (g->n_edges > 0 && (!g->perm || !g->perm_dst))
+            return ETP_ERR_INVALID_ARGUMENT;
+    }
+    return ETP_OK;
+}
+
+// ETP_FLAG_VALIDATE: count CSR violations on the device (allocates one int
+// and synchronises the stream).
+etp_status validate_graph(const etp_graph *g, hipStream_t stream)
+{
+    if (g->n_dst == 0)
+        return g->n_edges == 0 ? ETP_OK : ETP_ERR_INTERNAL;
+    int *bad = nullptr;
+    if (hipMalloc(&bad, sizeof(int)) != hipSuccess)
+        return ETP_ERR_ALLOC;
+    int host = 0;
+    etp_status st = ETP_OK;
+    if (hipMemsetAsync(bad, 0, sizeof(int), stream) != hipSuccess ||
+        etp::launch_validate(g->n_dst, g->n_src, g->n_edges, g->row_ptr, g->src, bad, stream) != hipSuccess ||
+        hipMemcpyAsync(&host, bad, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        st = ETP_ERR_HIP;
+    (void)hipFree(bad);
+    if (st == ETP_OK && host != 0)
+        st = ETP_ERR_INTERNAL;
+    return st;
+}
+
+#define ETP_RUN_CASES(kind, L, XT)                                                      \
+    case (L * 4 + XT * 2 + 0): return etp::ETP_RUN_NAME(kind, L, XT, 0)(a);              \
+    case (L * 4 + XT * 2 + 1): return etp::ETP_RUN_NAME(kind, L, XT, 1)(a);
+
+hipError_t run_dst(int L, bool bf16, int mode, const etp::ConvArgs &a)
+{
+    switch (L * 4 + (bf16 ? 2 : 0) + mode) {
+        ETP_RUN_CASES(dst, 0, 0) ETP_RUN_CASES(dst, 0, 1) ETP_RUN_CASES(dst, 1, 0) ETP_RUN_CASES(dst, 1, 1)
+        ETP_RUN_CASES(dst, 2, 0) ETP_RUN_CASES(dst, 2, 1) ETP_RUN_CASES(dst, 3, 0) ETP_RUN_CASES(dst, 3, 1)
+        ETP_RUN_CASES(dst, 4, 0) ETP_RUN_CASES(dst, 4, 1)
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t run_src(int L, bool bf16, int mode, const etp::ConvArgs &a)
+{
+    switch (L * 4 + (bf16 ? 2 : 0) + mode) {
+        ETP_RUN_CASES(src, 0, 0) ETP_RUN_CASES(src, 0, 1) ETP_RUN_CASES(src, 1, 0) ETP_RUN_CASES(src, 1, 1)
+        ETP_RUN_CASES(src, 2, 0) ETP_RUN_CASES(src, 2, 1) ETP_RUN_CASES(src, 3, 0) ETP_RUN_CASES(src, 3, 1)
+        ETP_RUN_CASES(src, 4, 0) ETP_RUN_CASES(src, 4, 1)
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+etp_status etp_plan_create(const etp_plan_desc *desc, etp_plan_t *plan)
+{
+    if (!desc || !plan)
+        return ETP_ERR_INVALID_ARGUMENT;
+    *plan = nullptr;
+    const int L = desc->l_max_in;
+    for (int l : {desc->l_max_in, desc->l_max_sh, desc->l_max_out})
+        if (l < 0 || l > etp::kLMax)
+            return ETP_ERR_INVALID_ARGUMENT;
+    if (desc->channels < 1 || desc->channels > 1024)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (desc->x_dtype != ETP_F32 && desc->x_dtype != ETP_BF16)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (desc->l_max_sh != L || desc->l_max_out != L)
+        return ETP_ERR_UNSUPPORTED;
+    if (desc->channels > 64 && (desc->channels & 1))
+        return ETP_ERR_UNSUPPORTED;
+    const etp::Table *T = etp::table_for(L);
+    if (desc->paths) {
+        if (desc->n_paths <= 0)
+            return ETP_ERR_INVALID_ARGUMENT;
+        for (int p = 0; p < desc->n_paths; ++p) {
+            const int l1 = desc->paths[3 * p], l2 = desc->paths[3 * p + 1], l3 = desc->paths[3 * p + 2];
+            const int lo = l1 > l2 ? l1 - l2 : l2 - l1;
+            if (l1 < 0 || l2 < 0 || l3 < lo || l3 > l1 + l2 || l1 > L || l2 > L || l3 > L)
+                return ETP_ERR_INVALID_ARGUMENT;
+        }
+        if (desc->n_paths != T->P)
+            return ETP_ERR_UNSUPPORTED;
+        for (int p = 0; p < T->P; ++p)
+            if (desc->paths[3 * p] != T->path[p].l1 || desc->paths[3 * p + 1] != T->path[p].l2 ||
+                desc->paths[3 * p + 2] != T->path[p].l3)
+                return ETP_ERR_UNSUPPORTED;
+    } else if (desc->n_paths != 0 && desc->n_paths != T->P) {
+        return ETP_ERR_INVALID_ARGUMENT;
+    }
+    etp_plan_s *p = new (std::nothrow) etp_plan_s;
+    if (!p)
+        return ETP_ERR_ALLOC;
+    p->L = L;
+    p->C = desc->channels;
+    p->dtype = desc->x_dtype;
+    p->T = T;
+    *plan = p;
+    return ETP_OK;
+}
+
+etp_status etp_plan_destroy(etp_plan_t plan)
+{
+    delete plan;
+    return ETP_OK;
+}
+
+etp_status etp_plan_info(etp_plan_t plan, etp_plan_info_t *info)
+{
+    if (!plan || !info)
+        return ETP_ERR_INVALID_ARGUMENT;
+    info->l_max = plan->L;
+    info->channels = plan->C;
+    info->x_dtype = plan->dtype;
+    info->n_paths = plan->T->P;
+    info->nnz = plan->T->nnz;
+    info->din_rows = plan->T->din_rows;
+    info->dsh = plan->T->dsh;
+    info->dout_rows = plan->T->dout_rows;
+    return ETP_OK;
+}
+
+etp_status etp_plan_tables(etp_plan_t plan, int32_t *paths, int32_t *out_off, int32_t *cg_ptr, int8_t *cg_m,
+                           float *cg_val)
+{
+    if (!plan)
+        return ETP_ERR_INVALID_ARGUMENT;
+    const etp::Table &T = *plan->T;
+    for (int p = 0; p < T.P; ++p) {
+        if (paths) {
+            paths[3 * p] = T.path[p].l1;
+            paths[3 * p + 1] = T.path[p].l2;
+            paths[3 * p + 2] = T.path[p].l3;
+        }
+        if (out_off)
+            out_off[p] = T.path[p].out_row;
+        if (cg_ptr)
+            cg_ptr[p] = T.path[p].nz0;
+    }
+    if (out_off)
+        out_off[T.P] = T.dout_rows;
+    if (cg_ptr)
+        cg_ptr[T.P] = T.nnz;
+    for (int t = 0; t < T.nnz; ++t) {
+        if (cg_m) {
+            cg_m[3 * t] = static_cast<int8_t>(T.nz[t].m1);
+            cg_m[3 * t + 1] = static_cast<int8_t>(T.nz[t].m2);
+            cg_m[3 * t + 2] = static_cast<int8_t>(T.nz[t].m3);
+        }
+        if (cg_val)
+            cg_val[t] = T.nz[t].fval;
+    }
+    return ETP_OK;
+}
+
+etp_status etp_csr_transpose_workspace(int32_t n_src, size_t *bytes)
+{
+    if (!bytes || n_src < 0)
+        return ETP_ERR_INVALID_ARGUMENT;
+    *bytes = etp::transpose_workspace_bytes(n_src);
+    return ETP_OK;
+}
+
+etp_status etp_csr_transpose(const etp_graph *g, int32_t *src_ptr, int32_t *perm, int32_t *perm_dst, void *ws,
+                             size_t ws_bytes, void *stream)
+{
+    etp_status st = check_graph(g, false);
+    if (st != ETP_OK)
+        return st;
+    if (!src_ptr || (g->n_edges > 0 && (!perm || !perm_dst)))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (!ws || ws_bytes < etp::transpose_workspace_bytes(g->n_src))
+        return ETP_ERR_WORKSPACE;
+    return hip_status(etp::launch_transpose(g->n_dst, g->n_src, g->n_edges, g->row_ptr, g->src, src_ptr, perm,
+                                            perm_dst, ws, static_cast<hipStream_t>(stream)));
+}
+
+etp_status etp_sh(etp_plan_t plan, int64_t n_edges, const float *vec, float *Y, float *dY, void *stream)
+{
+    if (!plan || n_edges < 0)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (n_edges == 0)
+        return ETP_OK;
+    if (!vec || !Y)
+        return ETP_ERR_INVALID_ARGUMENT;
+    return hip_status(etp::launch_sh(plan->L, n_edges, vec, Y, dY, static_cast<hipStream_t>(stream)));
+}
+
+etp_status etp_edge_conv_fwd(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x, const float *w,
+                             float *out, uint32_t flags, void *stream)
+{
+    if (!plan)
+        return ETP_ERR_INVALID_ARGUMENT;
+    etp_status st = check_graph(g, false);
+    if (st != ETP_OK)
+        return st;
+    if (g->n_dst > 0 && !out)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (g->n_edges > 0 && (!vec || !x || !w))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (flags & ~3u)
+        return ETP_ERR_INVALID_ARGUMENT;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (flags & ETP_FLAG_VALIDATE) {
+        st = validate_graph(g, s);
+        if (st != ETP_OK)
+            return st;
+    }
+    etp::ConvArgs a{};
+    a.C = plan->C;
+    a.n_dst = g->n_dst;
+    a.n_src = g->n_src;
+    a.row_ptr = g->row_ptr;
+    a.src = g->src;
+    a.vec = vec;
+    a.x = x;
+    a.w = w;
+    a.out = out;
+    a.flags = flags & ETP_FLAG_ACCUMULATE;
+    a.stream = s;
+    return hip_status(run_dst(plan->L, plan->dtype == ETP_BF16, etp::DST_FWD, a));
+}
+
+etp_status etp_edge_conv_vjp(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x, const float *w,
+                             const float *grad_out, float *grad_x, float *grad_w, float *grad_vec, uint32_t flags,
+                             void *stream)
+{
+    if (!plan)
+        return ETP_ERR_INVALID_ARGUMENT;
+    etp_status st = check_graph(g, true);
+    if (st != ETP_OK)
+        return st;
+    if (plan->C > 128)
+        return ETP_ERR_UNSUPPORTED;
+    if (flags & ~3u)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (!grad_x && !grad_w && !grad_vec)
+        return ETP_OK;
+    if (g->n_src > 0 && (!x || !grad_out))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (g->n_edges > 0 && (!vec || !w || !grad_out))
+        return ETP_ERR_INVALID_ARGUMENT;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (flags & ETP_FLAG_VALIDATE) {
+        st = validate_graph(g, s);
+        if (st != ETP_OK)
+            return st;
+    }
+    etp::ConvArgs a{};
+    a.C = plan->C;
+    a.n_dst = g->n_dst;
+    a.n_src = g->n_src;
+    a.row_ptr = g->row_ptr;
+    a.src = g->src;
+    a.src_ptr = g->src_ptr;
+    a.perm = g->perm;
+    a.perm_dst = g->perm_dst;
+    a.vec = vec;
+    a.x = x;
+    a.w = w;
+    a.G = grad_out;
+    a.ox = grad_x;
+    a.ow = grad_w;
+    a.ovec = grad_vec;
+    a.flags = flags & ETP_FLAG_ACCUMULATE;
+    a.stream = s;
+    return hip_status(run_src(plan->L, plan->dtype == ETP_BF16, etp::SRC_VJP, a));
+}
+
+etp_status etp_edge_conv_vjp2(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x, const float *w,
+                              const float *grad_out, const float *gg_x, const float *gg_w, const float *gg_vec,
+                              float *d_x, float *d_w, float *d_vec, float *d_grad_out, uint32_t flags, void *stream)
+{
+    if (!plan)
+        return ETP_ERR_INVALID_ARGUMENT;
+    etp_status st = check_graph(g, true);
+    if (st != ETP_OK)
+        return st;
+    if (plan->C > 128)
+        return ETP_ERR_UNSUPPORTED;
+    if (flags & ~3u)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (g->n_edges > 0 && (!vec || !x || !w))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if ((d_x || d_w || d_vec) && g->n_edges > 0 && !grad_out)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (g->n_src > 0 && d_x && !x)
+        return ETP_ERR_INVALID_ARGUMENT;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (flags & ETP_FLAG_VALIDATE) {
+        st = validate_graph(g, s);
+        if (st != ETP_OK)
+            return st;
+    }
+    etp::ConvArgs a{};
+    a.C = plan->C;
+    a.n_dst = g->n_dst;
+    a.n_src = g->n_src;
+    a.row_ptr = g->row_ptr;
+    a.src = g->src;
+    a.src_ptr = g->src_ptr;
+    a.perm = g->perm;
+    a.perm_dst = g->perm_dst;
+    a.vec = vec;
+    a.x = x;
+    a.w = w;
+    a.G = grad_out;
+    a.ggx = gg_x;
+    a.ggw = gg_w;
+    a.ggvec = gg_vec;
+    a.out = d_grad_out;
+    a.ox = d_x;
+    a.ow = d_w;
+    a.ovec = d_vec;
+    a.flags = flags & ETP_FLAG_ACCUMULATE;
+    a.stream = s;
+    const bool bf16 = plan->dtype == ETP_BF16;
+    if (d_grad_out) {
+        st = hip_status(run_dst(plan->L, bf16, etp::DST_DG, a));
+        if (st != ETP_OK)
+            return st;
+    }
+    if (d_x || d_w || d_vec)
+        return hip_status(run_src(plan->L, bf16, etp::SRC_VJP2, a));
+    return ETP_OK;
+}
+
+const char *etp_status_string(etp_status s)
+{
+    switch (s) {
+    case ETP_OK: return "ok";
+    case ETP_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case ETP_ERR_UNSUPPORTED: return "unsupported by this implementation";
+    case ETP_ERR_WORKSPACE: return "workspace missing or too small";
+    case ETP_ERR_HIP: return "HIP runtime error";
+    case ETP_ERR_ALLOC: return "allocation failed";
+    case ETP_ERR_INTERNAL: return "malformed graph or internal error";
+    }
+    return "unknown status";
+}
+
+int32_t etp_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,257 @@
+// etp_dst.hip -- destination-segmented passes of the edge tensor-product
+// convolution: the forward, and the dG term of the VJP-of-VJP.
+//
+//   fwd  out[i, p, m3, u] = sum_{e in in(i)} sum_{m1} T[e, p, m1, m3] w[e, p, u] x[src_e, m1, u]
+//   dG   dG[i, p, m3, u]  = sum_{e in in(i)} sum_{m1} T (w X' + W' x) + Td w x
+//        with T[e, p, m1, m3] = sum_m2 C Y_m2(r_e) and Td the same with
+//        Yd = grad Y . R'_e (the JVP of the forward along (X', W', R')).
+//
+// (the CG tensor product with sparse Wigner 3-j coefficients of "High-
+// performance training and inference for deep equivariant interatomic
+// potentials", section "Proposed method"; the edge-convolution forward and
+// VJP-of-VJP stages of "How does FlashCart make equivariant interatomic
+// potentials faster and more accurate?", section "Generated kernels beat SH
+// baselines at high order").
+//
+// Mapping (gfx950, wave64):
+//   * one workgroup per (destination node, 64*CPL-channel chunk, path
+//     group); its S waves split the node's in-edges into contiguous parts; a
+//     lane owns CPL consecutive channels, so every feature / weight row
+//     access is one coalesced 256*CPL-byte wave load;
+//   * path groups bound the per-lane register accumulators (output rows of
+//     the group x CPL);
+//   * per batch of B edges, lane k evaluates the SH of edge k in registers
+//     and the edge-uniform T (and Td) of the group's (p, m1, m3) pairs into
+//     the wave's LDS slice; the edge loop reads them as broadcast float4;
+//   * messages live in registers only; the sum over a wave's edges is a
+//     fixed-order register sum and the S waves meet in a fixed-order LDS
+//     tree, so results are deterministic without atomics;
+//   * w / W' are streamed with non-temporal loads, x / X' rows gathered
+//     cached; the forward issues the next edge's loads before the current
+//     edge's FMAs.
+#include "etp_conv_common.hpp"
+
+namespace etp {
+
+template <int L, int CPL, int MODE>
+struct DstCfg {
+    static constexpr int S = 4;
+    static constexpr int B = L <= 2 ? 32 : (L == 3 ? 16 : 8);
+    static constexpr int MAXROWS = (MODE == DST_FWD ? 56 : 40) / CPL;
+    static constexpr int TCOPIES = MODE == DST_FWD ? 1 : 2;  // T (and Td) per edge
+};
+
+template <int L, int CPL, typename XT, int MODE, int G>
+__device__ __forceinline__ void dst_group(const int n_dst, const int C, const int nchunk,
+                                          const int *__restrict__ row_ptr, const int *__restrict__ src,
+                                          const float *__restrict__ vec, const XT *__restrict__ x,
+                                          const float *__restrict__ w, const float *__restrict__ ggx,
+                                          const float *__restrict__ ggw, const float *__restrict__ ggvec,
+                                          float *__restrict__ out, const uint32_t flags, float *lds)
+{
+    using V = chv_t<CPL>;
+    using Cfg = DstCfg<L, CPL, MODE>;
+    constexpr int S = Cfg::S, B = Cfg::B, TC = Cfg::TCOPIES;
+    constexpr bool DG = MODE == DST_DG;
+    constexpr Groups GR = make_groups(kTab<L>, Cfg::MAXROWS);
+    constexpr GroupInfo GI = group_info(kTab<L>, GR, G);
+    constexpr int P = kTab<L>.P, DIN = kTab<L>.din_rows, DOUT = kTab<L>.dout_rows, DSH = kTab<L>.dsh;
+    constexpr int NP = GI.np, NXR = GI.nxr, NROW = GI.nrow, STRIDE = GI.stride;
+    constexpr int LDS_FLOATS = S * TC * B * max_stride(kTab<L>, GR);
+
+    const int lane = threadIdx.x & 63, wv = wave_id();
+    const int lb = xcd_remap(blockIdx.x, gridDim.x);
+    const int node = lb / nchunk, chunk = lb - node * nchunk;
+    if (node >= n_dst)
+        return;
+    const int u0 = chunk * 64 * CPL + lane * CPL;
+    const bool active = u0 < C;
+    const bool has_xp = DG && ggx != nullptr, has_wp = DG && ggw != nullptr, has_rp = DG && ggvec != nullptr;
+
+    const int rb = row_ptr[node], re = row_ptr[node + 1];
+    const int len = re - rb;
+    const int e_begin = rb + static_cast<int>((static_cast<int64_t>(len) * wv) / S);
+    const int e_end = rb + static_cast<int>((static_cast<int64_t>(len) * (wv + 1)) / S);
+    float *tl = lds + wv * (TC * B * STRIDE);  // T[B][STRIDE] (then Td[B][STRIDE])
+
+    V acc[NROW];
+    static_range<0, NROW>([&](auto r) { acc[r] = vzero<V>(); });
+
+    // per-edge operands: w (and W') rows of the group's paths, x (and X')
+    // rows of the group's l1 values
+    struct Ops {
+        V w[NP], x[NXR], wp[DG ? NP : 1], xp[DG ? NXR : 1];
+    };
+    auto load = [&](int e, Ops &o) {
+        const int j = src[e];
+        const float *we = w + static_cast<int64_t>(e) * (P * C) + u0;
+        const XT *xj = x + static_cast<int64_t>(j) * (DIN * C) + u0;
+        static_range<0, NP>([&](auto q) { o.w[q] = active ? load_stream<V>(we + (GI.p0 + q) * C) : vzero<V>(); });
+        static_range<0, NXR>([&](auto q) { o.x[q] = active ? load_cached<V>(xj + (GI.xr0 + q) * C) : vzero<V>(); });
+        if constexpr (DG) {
+            const float *wpe = has_wp ? ggw + static_cast<int64_t>(e) * (P * C) + u0 : nullptr;
+            const float *xpj = has_xp ? ggx + static_cast<int64_t>(j) * (DIN * C) + u0 : nullptr;
+            static_range<0, NP>([&](auto q) {
+                o.wp[q] = (has_wp && active) ? load_stream<V>(wpe + (GI.p0 + q) * C) : vzero<V>();
+            });
+            static_range<0, NXR>([&](auto q) {
+                o.xp[q] = (has_xp && active) ? load_cached<V>(xpj + (GI.xr0 + q) * C) : vzero<V>();
+            });
+        }
+    };
+
+    // SH (and Yd) and the T (and Td) coefficients of edges [eb, eb + nb)
+    auto prologue = [&](int eb, int nb) {
+        wave_sync_lds();
+        if (lane < nb) {
+            const int e = eb + lane;
+            const float rx = vec[3 * e], ry = vec[3 * e + 1], rz = vec[3 * e + 2];
+            if constexpr (!DG) {
+                float Y[DSH];
+                sh_value<L>(rx, ry, rz, Y);
+                write_T<L, GI.pr0, GI.npr, STRIDE>(Y, tl + lane * STRIDE);
+            } else {
+                D3 Yg[DSH];
+                sh_grad<L>(rx, ry, rz, Yg);
+                float px = 0.f, py = 0.f, pz = 0.f;
+                if (has_rp) {
+                    px = ggvec[3 * e];
+                    py = ggvec[3 * e + 1];
+                    pz = ggvec[3 * e + 2];
+                }
+                float Y[DSH], Yd[DSH];
+                static_range<0, DSH>([&](auto b) {
+                    Y[b] = Yg[b].v;
+                    Yd[b] = Yg[b].g0 * px + Yg[b].g1 * py + Yg[b].g2 * pz;
+                });
+                write_T<L, GI.pr0, GI.npr, STRIDE>(Y, tl + lane * STRIDE);
+                write_T<L, GI.pr0, GI.npr, STRIDE>(Yd, tl + B * STRIDE + lane * STRIDE);
+            }
+        }
+        wave_sync_lds();
+    };
+
+    // Forward, per pair (p, m1, m3): either acc[p, m3] += T (w x[m1]) with the
+    // inputs pre-scaled by w, or y[m3] += T x[m1] followed by
+    // acc[p, m3] += w y[m3], whichever form needs fewer multiplies.
+    // dG: acc[p, m3] += T (w X' + W' x)[m1] + Td (w x)[m1].
+    auto compute = [&](const Ops &o, const float *tk) {
+        float4 tq = make_float4(0.f, 0.f, 0.f, 0.f), tdq = tq;
+        V xw[9], y[9], xx[DG ? 9 : 1];
+        static_range<GI.pr0, GI.pr1>([&](auto q) {
+            constexpr Pair pr = kTab<L>.pair[q];
+            constexpr Path pa = kTab<L>.path[pr.path];
+            constexpr int d1 = 2 * pa.l1 + 1, d3 = 2 * pa.l3 + 1;
+            constexpr int XO = pa.x_row - GI.xr0, OO = pa.out_row - GI.row0, WQ = pr.path - GI.p0;
+            constexpr bool XW = DG || d1 <= d3;
+            constexpr int a = pr.m1 + pa.l1, c3 = pr.m3 + pa.l3, ql = q - GI.pr0;
+            if constexpr (XW && q == pa.pr0) {
+                static_range<0, d1>([&](auto k) {
+                    xw[k] = o.w[WQ] * o.x[XO + k];
+                    if constexpr (DG)
+                        xx[k] = vfma(o.w[WQ], o.xp[XO + k], o.wp[WQ] * o.x[XO + k]);
+                });
+            }
+            if constexpr (ql % 4 == 0) {
+                tq = *reinterpret_cast<const float4 *>(tk + ql);
+                if constexpr (DG)
+                    tdq = *reinterpret_cast<const float4 *>(tk + B * STRIDE + ql);
+            }
+            const float t = pick4<ql % 4>(tq);
+            if constexpr (DG) {
+                const float td = pick4<ql % 4>(tdq);
+                acc[OO + c3] = vfma(t, xx[a], vfma(td, xw[a], acc[OO + c3]));
+            } else if constexpr (XW) {
+                acc[OO + c3] = vfma(t, xw[a], acc[OO + c3]);
+            } else if constexpr (first_m3_in_path(kTab<L>, q)) {
+                y[c3] = t * o.x[XO + a];
+            } else {
+                y[c3] = vfma(t, o.x[XO + a], y[c3]);
+            }
+            if constexpr (!XW && q == pa.pr1 - 1)
+                static_range<0, d3>([&](auto m) { acc[OO + m] = vfma(o.w[WQ], y[m], acc[OO + m]); });
+        });
+    };
+
+    Ops opA, opB;
+    int e = e_begin, kb = 0;
+    if (e < e_end)
+        load(e, opA);
+    while (e < e_end) {
+        if (kb == 0)
+            prologue(e, min(B, e_end - e));
+        if (e + 1 < e_end)
+            load(e + 1, opB);
+        compute(opA, tl + kb * STRIDE);
+        ++e;
+        kb = (kb + 1 == B) ? 0 : kb + 1;
+        if (e >= e_end)
+            break;
+        if (kb == 0)
+            prologue(e, min(B, e_end - e));
+        if (e + 1 < e_end)
+            load(e + 1, opA);
+        compute(opB, tl + kb * STRIDE);
+        ++e;
+        kb = (kb + 1 == B) ? 0 : kb + 1;
+    }
+
+    reduce_waves<S, NROW, V, LDS_FLOATS>(acc, lds, lane, wv);
+
+    if (wv == 0 && active) {
+        float *op = out + static_cast<int64_t>(node) * (DOUT * C) + u0 + GI.row0 * C;
+        if (flags & 1u) {
+            static_range<0, NROW>([&](auto r) { store_v<V>(op + r * C, acc[r] + load_cached<V>(op + r * C)); });
+        } else {
+            static_range<0, NROW>([&](auto r) { store_v<V>(op + r * C, acc[r]); });
+        }
+    }
+}
+
+template <int L, int CPL, typename XT, int MODE>
+__global__ void __launch_bounds__((64 * DstCfg<L, CPL, MODE>::S))
+    dst_kernel(const int n_dst, const int C, const int nchunk, const int *__restrict__ row_ptr,
+               const int *__restrict__ src, const float *__restrict__ vec, const XT *__restrict__ x,
+               const float *__restrict__ w, const float *__restrict__ ggx, const float *__restrict__ ggw,
+               const float *__restrict__ ggvec, float *__restrict__ out, const uint32_t flags)
+{
+    extern __shared__ float lds[];
+    constexpr Groups GR = make_groups(kTab<L>, DstCfg<L, CPL, MODE>::MAXROWS);
+    const int g = blockIdx.y;
+    static_range<0, GR.n>([&](auto G) {
+        if (g == G)
+            dst_group<L, CPL, XT, MODE, G>(n_dst, C, nchunk, row_ptr, src, vec, x, w, ggx, ggw, ggvec, out, flags,
+                                           lds);
+    });
+}
+
+template <int L, int CPL, typename XT, int MODE>
+static hipError_t launch_dst_t(const ConvArgs &a)
+{
+    using Cfg = DstCfg<L, CPL, MODE>;
+    constexpr Groups GR = make_groups(kTab<L>, Cfg::MAXROWS);
+    constexpr int LDS_FLOATS = Cfg::S * Cfg::TCOPIES * Cfg::B * max_stride(kTab<L>, GR);
+    const int nchunk = (a.C + 64 * CPL - 1) / (64 * CPL);
+    const int64_t nblk = static_cast<int64_t>(a.n_dst) * nchunk;
+    if (nblk == 0)
+        return hipSuccess;
+    if (nblk > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    dim3 grid(static_cast<unsigned>(nblk), GR.n), block(64 * Cfg::S);
+    hipLaunchKernelGGL((dst_kernel<L, CPL, XT, MODE>), grid, block, LDS_FLOATS * sizeof(float), a.stream, a.n_dst,
+                       a.C, nchunk, a.row_ptr, a.src, a.vec, static_cast<const XT *>(a.x), a.w, a.ggx, a.ggw,
+                       a.ggvec, a.out, a.flags);
+    return hipGetLastError();
+}
+
+#if !defined(ETP_L) || !defined(ETP_XT) || !defined(ETP_MODE)
+#error "compile this file once per (l_max, dtype, mode) with -DETP_L=0..4 -DETP_XT=0|1 -DETP_MODE=0|1"
+#endif
+
+hipError_t ETP_RUN_NAME(dst, ETP_L, ETP_XT, ETP_MODE)(const ConvArgs &a)
+{
+    using XT = std::conditional_t<ETP_XT == 1, bf16raw, float>;
+    return a.C > 64 ? launch_dst_t<ETP_L, 2, XT, ETP_MODE>(a) : launch_dst_t<ETP_L, 1, XT, ETP_MODE>(a);
+}
+
+}  // namespace etp

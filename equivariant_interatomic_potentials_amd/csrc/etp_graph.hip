@@ -1,0 +1,274 @@
+// etp_graph.hip -- graph preparation: the stable transpose of a
+// destination-sorted CSR edge list (source offsets, edge ids grouped by
+// source in edge-id order, and each such edge's destination), plus an
+// optional validity check of the CSR.
+//
+// The neighbour list is the structure the convolution walks ("edges per
+// atom" in "How does FlashCart make equivariant interatomic potentials faster
+// and more accurate?", section on the SPICE-MACE-OFF model); the source-side
+// passes of the VJP need it grouped by source.
+//
+// Steps (all integer, bit-exact and deterministic):
+//   1. counts[src[e]]++ with integer atomics (the totals do not depend on
+//      the order of the increments);
+//   2. exclusive scan of the counts into src_ptr (tile scan + scan of tile
+//      totals + offsets);
+//   3. each edge takes a slot in its source's segment with an atomic
+//      cursor (arbitrary order), then every segment is sorted by edge id
+//      (LDS bitonic sort, or rank-by-counting for segments longer than the
+//      LDS tile), which makes the result independent of the atomic order;
+//   4. perm_dst[k] = the row of perm[k], by binary search in row_ptr.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+namespace etp {
+
+constexpr int kScanThreads = 256, kScanItems = 8, kScanTile = kScanThreads * kScanItems;
+constexpr int kSortCap = 2048;
+
+__global__ void __launch_bounds__(256) fill_kernel(int *__restrict__ p, int64_t n, int v)
+{
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        p[i] = v;
+}
+
+__global__ void __launch_bounds__(256) hist_kernel(int64_t E, const int *__restrict__ src, int *__restrict__ counts)
+{
+    for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < E;
+         e += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        atomicAdd(&counts[src[e]], 1);
+}
+
+// Inclusive scan of the 256 thread totals of a block (returns the inclusive
+// value of this thread; *total receives the block total).
+__device__ int block_inclusive_scan(int v, int *total)
+{
+    __shared__ int wsum[kScanThreads / 64];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(v, d, 64);
+        if (lane >= d)
+            v += t;
+    }
+    if (lane == 63)
+        wsum[wid] = v;
+    __syncthreads();
+    int off = 0, tot = 0;
+    for (int k = 0; k < kScanThreads / 64; ++k) {
+        if (k < wid)
+            off += wsum[k];
+        tot += wsum[k];
+    }
+    __syncthreads();
+    *total = tot;
+    return v + off;
+}
+
+// In-place inclusive scan of each tile of a[0, n); tile totals to bsum.
+__global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(int *__restrict__ a, int64_t n, int *__restrict__ bsum)
+{
+    const int64_t base = blockIdx.x * static_cast<int64_t>(kScanTile) + threadIdx.x * kScanItems;
+    int v[kScanItems];
+    int run = 0;
+    for (int k = 0; k < kScanItems; ++k) {
+        v[k] = (base + k < n) ? a[base + k] : 0;
+        run += v[k];
+        v[k] = run;
+    }
+    int total;
+    const int incl = block_inclusive_scan(run, &total);
+    const int excl = incl - run;
+    for (int k = 0; k < kScanItems; ++k)
+        if (base + k < n)
+            a[base + k] = v[k] + excl;
+    if (threadIdx.x == 0)
+        bsum[blockIdx.x] = total;
+}
+
+// Single-block inclusive scan of b[0, n) in place.
+__global__ void __launch_bounds__(kScanThreads) scan_single_kernel(int *__restrict__ b, int64_t n)
+{
+    int carry = 0;
+    for (int64_t base = 0; base < n; base += kScanThreads) {
+        const int64_t i = base + threadIdx.x;
+        const int v = i < n ? b[i] : 0;
+        int total;
+        const int incl = block_inclusive_scan(v, &total);
+        if (i < n)
+            b[i] = incl + carry;
+        carry += total;
+    }
+}
+
+__global__ void __launch_bounds__(kScanThreads) add_offsets_kernel(int *__restrict__ a, int64_t n,
+                                                                   const int *__restrict__ bsum)
+{
+    if (blockIdx.x == 0)
+        return;
+    const int off = bsum[blockIdx.x - 1];
+    const int64_t base = blockIdx.x * static_cast<int64_t>(kScanTile);
+    for (int k = threadIdx.x; k < kScanTile; k += kScanThreads)
+        if (base + k < n)
+            a[base + k] += off;
+}
+
+__global__ void __launch_bounds__(256) copy_kernel(int *__restrict__ dst, const int *__restrict__ srcp, int64_t n)
+{
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        dst[i] = srcp[i];
+}
+
+__global__ void __launch_bounds__(256) scatter_kernel(int64_t E, const int *__restrict__ src, int *__restrict__ cursor,
+                                                      int *__restrict__ perm)
+{
+    for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < E;
+         e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int pos = atomicAdd(&cursor[src[e]], 1);
+        perm[pos] = static_cast<int>(e);
+    }
+}
+
+// Sort each source segment of perm by edge id. scratch (E ints) backs the
+// rank-by-counting path for segments longer than kSortCap.
+__global__ void __launch_bounds__(256) seg_sort_kernel(int n_src, const int *__restrict__ src_ptr, int *__restrict__ perm,
+                                                       int *__restrict__ scratch)
+{
+    __shared__ int buf[kSortCap];
+    const int j = blockIdx.x;
+    if (j >= n_src)
+        return;
+    const int s = src_ptr[j], len = src_ptr[j + 1] - s;
+    if (len <= 1)
+        return;
+    if (len <= kSortCap) {
+        int n2 = 1;
+        while (n2 < len)
+            n2 <<= 1;
+        for (int i = threadIdx.x; i < n2; i += blockDim.x)
+            buf[i] = i < len ? perm[s + i] : INT_MAX;
+        __syncthreads();
+        for (int k = 2; k <= n2; k <<= 1) {
+            for (int jj = k >> 1; jj > 0; jj >>= 1) {
+                for (int i = threadIdx.x; i < n2; i += blockDim.x) {
+                    const int ixj = i ^ jj;
+                    if (ixj > i) {
+                        const bool up = (i & k) == 0;
+                        const int a = buf[i], b = buf[ixj];
+                        if ((a > b) == up) {
+                            buf[i] = b;
+                            buf[ixj] = a;
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        for (int i = threadIdx.x; i < len; i += blockDim.x)
+            perm[s + i] = buf[i];
+    } else {
+        for (int i = threadIdx.x; i < len; i += blockDim.x)
+            scratch[s + i] = perm[s + i];
+        __syncthreads();
+        for (int i = threadIdx.x; i < len; i += blockDim.x) {
+            const int v = scratch[s + i];
+            int r = 0;
+            for (int k = 0; k < len; ++k)
+                r += scratch[s + k] < v;
+            perm[s + r] = v;
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256) dst_lookup_kernel(int64_t E, int n_dst, const int *__restrict__ row_ptr,
+                                                         const int *__restrict__ perm, int *__restrict__ perm_dst)
+{
+    for (int64_t k = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; k < E;
+         k += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int e = perm[k];
+        // first index with row_ptr[idx] > e, minus one
+        int lo = 0, hi = n_dst + 1;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (row_ptr[mid] > e)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        perm_dst[k] = lo - 1;
+    }
+}
+
+// Counts violations of: row_ptr[0] == 0, row_ptr non-decreasing,
+// row_ptr[n_dst] == E, 0 <= src[e] < n_src.
+__global__ void __launch_bounds__(256) validate_kernel(int n_dst, int n_src, int64_t E, const int *__restrict__ row_ptr,
+                                                       const int *__restrict__ src, int *__restrict__ bad)
+{
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    const int64_t t0 = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+    int nbad = 0;
+    for (int64_t i = t0; i < n_dst; i += stride)
+        nbad += row_ptr[i] > row_ptr[i + 1];
+    for (int64_t e = t0; e < E; e += stride)
+        nbad += (src[e] < 0 || src[e] >= n_src);
+    if (t0 == 0)
+        nbad += (row_ptr[0] != 0) + (static_cast<int64_t>(row_ptr[n_dst]) != E);
+    if (nbad)
+        atomicAdd(bad, nbad);
+}
+
+static unsigned grid_for(int64_t n)
+{
+    const int64_t b = (n + 255) / 256;
+    return static_cast<unsigned>(b < 1 ? 1 : (b > 16384 ? 16384 : b));
+}
+
+size_t transpose_workspace_bytes(int n_src)
+{
+    const int64_t ntile = (static_cast<int64_t>(n_src) + kScanTile - 1) / kScanTile;
+    return sizeof(int) * static_cast<size_t>(n_src + ntile + 64);
+}
+
+hipError_t launch_transpose(int n_dst, int n_src, int64_t E, const int *row_ptr, const int *src, int *src_ptr,
+                            int *perm, int *perm_dst, void *ws, hipStream_t stream)
+{
+    int *cursor = static_cast<int *>(ws);
+    const int64_t ntile = (static_cast<int64_t>(n_src) + kScanTile - 1) / kScanTile;
+    int *bsum = cursor + n_src;
+    hipLaunchKernelGGL(fill_kernel, dim3(grid_for(n_src + 1)), dim3(256), 0, stream, src_ptr,
+                       static_cast<int64_t>(n_src) + 1, 0);
+    if (E > 0)
+        hipLaunchKernelGGL(hist_kernel, dim3(grid_for(E)), dim3(256), 0, stream, E, src, src_ptr + 1);
+    if (n_src > 0) {
+        hipLaunchKernelGGL(scan_tiles_kernel, dim3(static_cast<unsigned>(ntile)), dim3(kScanThreads), 0, stream,
+                           src_ptr + 1, static_cast<int64_t>(n_src), bsum);
+        if (ntile > 1) {
+            hipLaunchKernelGGL(scan_single_kernel, dim3(1), dim3(kScanThreads), 0, stream, bsum, ntile);
+            hipLaunchKernelGGL(add_offsets_kernel, dim3(static_cast<unsigned>(ntile)), dim3(kScanThreads), 0, stream,
+                               src_ptr + 1, static_cast<int64_t>(n_src), bsum);
+        }
+        hipLaunchKernelGGL(copy_kernel, dim3(grid_for(n_src)), dim3(256), 0, stream, cursor, src_ptr,
+                           static_cast<int64_t>(n_src));
+    }
+    if (E > 0) {
+        hipLaunchKernelGGL(scatter_kernel, dim3(grid_for(E)), dim3(256), 0, stream, E, src, cursor, perm);
+        hipLaunchKernelGGL(seg_sort_kernel, dim3(static_cast<unsigned>(n_src)), dim3(256), 0, stream, n_src,
+                           src_ptr, perm, perm_dst);
+        hipLaunchKernelGGL(dst_lookup_kernel, dim3(grid_for(E)), dim3(256), 0, stream, E, n_dst, row_ptr, perm,
+                           perm_dst);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_validate(int n_dst, int n_src, int64_t E, const int *row_ptr, const int *src, int *bad,
+                           hipStream_t stream)
+{
+    hipLaunchKernelGGL(validate_kernel, dim3(grid_for(E > n_dst ? E : n_dst)), dim3(256), 0, stream, n_dst, n_src, E,
+                       row_ptr, src, bad);
+    return hipGetLastError();
+}
+
+}  // namespace etp

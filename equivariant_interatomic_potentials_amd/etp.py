@@ -1,0 +1,290 @@
+"""Thin Python binding of libetp (include/etp.h), same names as the C ABI.
+
+Argument marshalling only: tensors are passed by device pointer
+(``tensor.data_ptr()``), the stream is torch's current HIP stream unless
+given, and every non-zero status raises ``EtpError``. All the computation
+runs in libetp's HIP kernels; there is no fallback path -- importing this
+module fails loudly if libetp.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libetp.so")
+
+ETP_OK = 0
+ETP_ERR_INVALID_ARGUMENT = 1
+ETP_ERR_UNSUPPORTED = 2
+ETP_ERR_WORKSPACE = 3
+ETP_ERR_HIP = 4
+ETP_ERR_ALLOC = 5
+ETP_ERR_INTERNAL = 6
+ETP_F32 = 0
+ETP_BF16 = 1
+ETP_FLAG_ACCUMULATE = 1
+ETP_FLAG_VALIDATE = 2
+
+# every symbol include/etp.h declares
+ABI_SYMBOLS = ("etp_plan_create", "etp_plan_destroy", "etp_plan_info", "etp_plan_tables",
+               "etp_csr_transpose_workspace", "etp_csr_transpose", "etp_sh", "etp_edge_conv_fwd",
+               "etp_edge_conv_vjp", "etp_edge_conv_vjp2", "etp_status_string", "etp_version")
+
+
+class EtpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {etp_status_string(status)} (status {status})")
+
+
+class etp_plan_desc(ctypes.Structure):
+    _fields_ = [("l_max_in", ctypes.c_int32), ("l_max_sh", ctypes.c_int32), ("l_max_out", ctypes.c_int32),
+                ("channels", ctypes.c_int32), ("x_dtype", ctypes.c_int32), ("n_paths", ctypes.c_int32),
+                ("paths", ctypes.POINTER(ctypes.c_int32))]
+
+
+class etp_graph(ctypes.Structure):
+    _fields_ = [("n_dst", ctypes.c_int32), ("n_src", ctypes.c_int32), ("n_edges", ctypes.c_int64),
+                ("row_ptr", ctypes.c_void_p), ("src", ctypes.c_void_p), ("src_ptr", ctypes.c_void_p),
+                ("perm", ctypes.c_void_p), ("perm_dst", ctypes.c_void_p)]
+
+
+class etp_plan_info_t(ctypes.Structure):
+    _fields_ = [("l_max", ctypes.c_int32), ("channels", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
+                ("n_paths", ctypes.c_int32), ("nnz", ctypes.c_int32), ("din_rows", ctypes.c_int32),
+                ("dsh", ctypes.c_int32), ("dout_rows", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run "
+                          "`python -m equivariant_interatomic_potentials_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, st, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
+    sig = {
+        "etp_plan_create": (st, [ctypes.POINTER(etp_plan_desc), ctypes.POINTER(vp)]),
+        "etp_plan_destroy": (st, [vp]),
+        "etp_plan_info": (st, [vp, ctypes.POINTER(etp_plan_info_t)]),
+        "etp_plan_tables": (st, [vp, vp, vp, vp, vp, vp]),
+        "etp_csr_transpose_workspace": (st, [i32, ctypes.POINTER(ctypes.c_size_t)]),
+        "etp_csr_transpose": (st, [ctypes.POINTER(etp_graph), vp, vp, vp, vp, ctypes.c_size_t, vp]),
+        "etp_sh": (st, [vp, i64, vp, vp, vp, vp]),
+        "etp_edge_conv_fwd": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, u32, vp]),
+        "etp_edge_conv_vjp": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, vp, vp, vp, u32, vp]),
+        "etp_edge_conv_vjp2": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                    vp, u32, vp]),
+        "etp_status_string": (ctypes.c_char_p, [st]),
+        "etp_version": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int, where: str):
+    if status != ETP_OK:
+        raise EtpError(status, where)
+
+
+def _ptr(t, name, dtype=None, numel=None, optional=False):
+    """Device pointer of a contiguous tensor (None -> NULL if optional)."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def etp_status_string(status: int) -> str:
+    return lib.etp_status_string(status).decode()
+
+
+def etp_version() -> int:
+    return lib.etp_version()
+
+
+class Plan:
+    """An etp_plan_t handle (destroyed with the object)."""
+
+    def __init__(self, handle: int):
+        self.handle = handle
+        info = etp_plan_info(self)
+        self.L = info["l_max"]
+        self.C = info["channels"]
+        self.x_dtype = info["x_dtype"]
+        self.P = info["n_paths"]
+        self.nnz = info["nnz"]
+        self.din_rows = info["din_rows"]
+        self.dsh = info["dsh"]
+        self.dout_rows = info["dout_rows"]
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            lib.etp_plan_destroy(self.handle)
+            self.handle = None
+
+
+def etp_plan_create(l_max, channels: int, x_dtype: int = ETP_F32, paths=None) -> Plan:
+    """l_max: int or (l_max_in, l_max_sh, l_max_out); paths: optional host [P, 3] int array."""
+    lin, lsh, lout = (l_max, l_max, l_max) if isinstance(l_max, int) else tuple(l_max)
+    d = etp_plan_desc(lin, lsh, lout, channels, x_dtype, 0, None)
+    keep = None
+    if paths is not None:
+        keep = np.ascontiguousarray(paths, dtype=np.int32).reshape(-1, 3)
+        d.n_paths = keep.shape[0]
+        d.paths = keep.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    h = ctypes.c_void_p()
+    _check(lib.etp_plan_create(ctypes.byref(d), ctypes.byref(h)), "etp_plan_create")
+    return Plan(h.value)
+
+
+def etp_plan_destroy(plan: Plan):
+    if plan.handle:
+        _check(lib.etp_plan_destroy(plan.handle), "etp_plan_destroy")
+        plan.handle = None
+
+
+def etp_plan_info(plan: Plan) -> dict:
+    info = etp_plan_info_t()
+    _check(lib.etp_plan_info(plan.handle, ctypes.byref(info)), "etp_plan_info")
+    return {k: getattr(info, k) for k, _ in etp_plan_info_t._fields_}
+
+
+def etp_plan_tables(plan: Plan) -> dict:
+    info = etp_plan_info(plan)
+    P, nnz = info["n_paths"], info["nnz"]
+    paths = np.zeros((P, 3), np.int32)
+    out_off = np.zeros(P + 1, np.int32)
+    cg_ptr = np.zeros(P + 1, np.int32)
+    cg_m = np.zeros((nnz, 3), np.int8)
+    cg_val = np.zeros(nnz, np.float32)
+    _check(lib.etp_plan_tables(plan.handle, paths.ctypes.data, out_off.ctypes.data, cg_ptr.ctypes.data,
+                               cg_m.ctypes.data, cg_val.ctypes.data), "etp_plan_tables")
+    return dict(paths=paths, out_off=out_off, cg_ptr=cg_ptr, cg_m=cg_m, cg_val=cg_val)
+
+
+class Graph:
+    """Device CSR (+ optional transpose) with the etp_graph struct."""
+
+    def __init__(self, n_dst, n_src, row_ptr, src, src_ptr=None, perm=None, perm_dst=None, n_edges=None):
+        self.n_dst, self.n_src = int(n_dst), int(n_src)
+        self.n_edges = int(src.numel()) if n_edges is None else int(n_edges)
+        self.row_ptr, self.src = row_ptr, src
+        self.src_ptr, self.perm, self.perm_dst = src_ptr, perm, perm_dst
+
+    def struct(self) -> etp_graph:
+        import torch
+        g = etp_graph()
+        g.n_dst, g.n_src, g.n_edges = self.n_dst, self.n_src, self.n_edges
+        g.row_ptr = _ptr(self.row_ptr, "row_ptr", torch.int32, self.n_dst + 1, optional=True)
+        g.src = _ptr(self.src, "src", torch.int32, self.n_edges, optional=True)
+        g.src_ptr = _ptr(self.src_ptr, "src_ptr", torch.int32, self.n_src + 1, optional=True)
+        g.perm = _ptr(self.perm, "perm", torch.int32, self.n_edges, optional=True)
+        g.perm_dst = _ptr(self.perm_dst, "perm_dst", torch.int32, self.n_edges, optional=True)
+        return g
+
+
+def etp_csr_transpose_workspace(n_src: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib.etp_csr_transpose_workspace(n_src, ctypes.byref(b)), "etp_csr_transpose_workspace")
+    return b.value
+
+
+def etp_csr_transpose(graph: Graph, src_ptr, perm, perm_dst, ws, stream=None):
+    import torch
+    g = graph.struct()
+    _check(lib.etp_csr_transpose(ctypes.byref(g), _ptr(src_ptr, "src_ptr", torch.int32, graph.n_src + 1),
+                                 _ptr(perm, "perm", torch.int32, graph.n_edges, optional=True),
+                                 _ptr(perm_dst, "perm_dst", torch.int32, graph.n_edges, optional=True),
+                                 _ptr(ws, "ws", optional=True), ws.numel() * ws.element_size() if ws is not None else 0,
+                                 _stream(stream)), "etp_csr_transpose")
+
+
+def etp_sh(plan: Plan, vec, Y, dY=None, stream=None):
+    import torch
+    n = vec.numel() // 3
+    _check(lib.etp_sh(plan.handle, n, _ptr(vec, "vec", torch.float32, 3 * n, optional=True),
+                      _ptr(Y, "Y", torch.float32, n * plan.dsh, optional=True),
+                      _ptr(dY, "dY", torch.float32, 3 * n * plan.dsh, optional=True), _stream(stream)), "etp_sh")
+
+
+def _xdtype(plan):
+    import torch
+    return torch.bfloat16 if plan.x_dtype == ETP_BF16 else torch.float32
+
+
+def etp_edge_conv_fwd(plan: Plan, graph: Graph, vec, x, w, out, flags: int = 0, stream=None):
+    import torch
+    E, C = graph.n_edges, plan.C
+    g = graph.struct()
+    _check(lib.etp_edge_conv_fwd(plan.handle, ctypes.byref(g),
+                                 _ptr(vec, "vec", torch.float32, 3 * E, optional=True),
+                                 _ptr(x, "x", _xdtype(plan), graph.n_src * plan.din_rows * C, optional=True),
+                                 _ptr(w, "w", torch.float32, E * plan.P * C, optional=True),
+                                 _ptr(out, "out", torch.float32, graph.n_dst * plan.dout_rows * C, optional=True),
+                                 flags, _stream(stream)), "etp_edge_conv_fwd")
+
+
+def etp_edge_conv_vjp(plan: Plan, graph: Graph, vec, x, w, grad_out, grad_x=None, grad_w=None, grad_vec=None,
+                      flags: int = 0, stream=None):
+    import torch
+    E, C = graph.n_edges, plan.C
+    f32 = torch.float32
+    g = graph.struct()
+    _check(lib.etp_edge_conv_vjp(plan.handle, ctypes.byref(g),
+                                 _ptr(vec, "vec", f32, 3 * E, optional=True),
+                                 _ptr(x, "x", _xdtype(plan), graph.n_src * plan.din_rows * C, optional=True),
+                                 _ptr(w, "w", f32, E * plan.P * C, optional=True),
+                                 _ptr(grad_out, "grad_out", f32, graph.n_dst * plan.dout_rows * C, optional=True),
+                                 _ptr(grad_x, "grad_x", f32, graph.n_src * plan.din_rows * C, optional=True),
+                                 _ptr(grad_w, "grad_w", f32, E * plan.P * C, optional=True),
+                                 _ptr(grad_vec, "grad_vec", f32, 3 * E, optional=True),
+                                 flags, _stream(stream)), "etp_edge_conv_vjp")
+
+
+def etp_edge_conv_vjp2(plan: Plan, graph: Graph, vec, x, w, grad_out, gg_x=None, gg_w=None, gg_vec=None,
+                       d_x=None, d_w=None, d_vec=None, d_grad_out=None, flags: int = 0, stream=None):
+    import torch
+    E, C = graph.n_edges, plan.C
+    f32 = torch.float32
+    nx, nw, no = graph.n_src * plan.din_rows * C, E * plan.P * C, graph.n_dst * plan.dout_rows * C
+    g = graph.struct()
+    _check(lib.etp_edge_conv_vjp2(plan.handle, ctypes.byref(g),
+                                  _ptr(vec, "vec", f32, 3 * E, optional=True),
+                                  _ptr(x, "x", _xdtype(plan), nx, optional=True),
+                                  _ptr(w, "w", f32, nw, optional=True),
+                                  _ptr(grad_out, "grad_out", f32, no, optional=True),
+                                  _ptr(gg_x, "gg_x", f32, nx, optional=True),
+                                  _ptr(gg_w, "gg_w", f32, nw, optional=True),
+                                  _ptr(gg_vec, "gg_vec", f32, 3 * E, optional=True),
+                                  _ptr(d_x, "d_x", f32, nx, optional=True),
+                                  _ptr(d_w, "d_w", f32, nw, optional=True),
+                                  _ptr(d_vec, "d_vec", f32, 3 * E, optional=True),
+                                  _ptr(d_grad_out, "d_grad_out", f32, no, optional=True),
+                                  flags, _stream(stream)), "etp_edge_conv_vjp2")

@@ -1,0 +1,194 @@
+/*
+ * etp.h -- C ABI of libetp: the fused edge tensor-product convolution of
+ * equivariant interatomic potentials on AMD Instinct MI355X (gfx950).
+ *
+ * The operation. For every edge i <- j of a destination-sorted CSR graph,
+ * the real spherical harmonics Y(r_e) of the bond vector r_e (r_src - r_dst)
+ * are coupled with the source node's irrep features x[j] through the sparse
+ * real Clebsch-Gordan (Wigner 3-j) coefficients of every path (l1, l2, l3),
+ * channel by channel ("uvu": one weight per edge, path and channel), scaled
+ * by the per-edge weight and summed into the destination node:
+ *
+ *   out[i, p, m3, u] = sum_{e in in(i)} w[e, p, u]
+ *                      sum_{(m1, m2, m3) in p} C[m1, m2, m3] Y_{l2, m2}(r_e) x[src_e, l1, m1, u]
+ *
+ * This tensor product with sparse Wigner 3-j coefficients is the costly step
+ * named in "High-performance training and inference for deep equivariant
+ * interatomic potentials" (review page, section "Proposed method") and in
+ * "Machine Learning Interatomic Potentials: Advancing Open-Source
+ * Software..." (section on the e3j backend); the edge convolution's forward,
+ * VJP and VJP-of-VJP are the three stages measured in "How does FlashCart
+ * make equivariant interatomic potentials faster and more accurate?"
+ * (section "Generated kernels beat SH baselines at high order"). The pages
+ * give no formulas; the conventions below are this library's reading of the
+ * textbook definitions:
+ *   - paths: every (l1, l2, l3) with |l1-l2| <= l3 <= min(l1+l2, l_max) in
+ *     lexicographic order (SO(3), no parity selection);
+ *   - CG: Racah's formula (Condon-Shortley phase) turned real by the basis
+ *     m'>0: (Y^{-m'} + (-1)^m' Y^{m'})/sqrt2, m'<0: i(Y^{m'} - (-1)^m' Y^{-m'})/sqrt2,
+ *     keeping the real part for even l1+l2+l3 and the imaginary part for odd;
+ *     stored as float32 (round to nearest);
+ *   - SH: real, component-normalised (sum_m Y_lm^2 = 2l+1), m = -l..l, z
+ *     polar, evaluated at r/|r| (so 1x1->0 is -a.b/sqrt3 and 1x1->1 is
+ *     (a x b)/sqrt2 in (y, z, x) order); a zero vector gives Y = (1, 0, ...)
+ *     and zero derivatives;
+ *   - no path normalisation; one output block per path (block order = path
+ *     order).
+ *
+ * Layouts (row-major, contiguous, channel fastest):
+ *   x[n_src][(l_max+1)^2][C]           row l*l + l + m           (f32 or bf16)
+ *   w[n_edges][P][C]                   f32
+ *   out, grad_out[n_dst][Dout][C]      row off_p + l3 + m3, off_p = sum_{q<p} (2 l3_q + 1)
+ *   vec[n_edges][3]                    f32
+ *   Y[n_edges][(l_max+1)^2], dY[n_edges][3][(l_max+1)^2]
+ * Gradients have the shape of their primals; every float output is f32.
+ *
+ * Ownership and memory. Every array argument is a DEVICE pointer owned by
+ * the caller, at least 16-byte aligned, except where a comment says HOST.
+ * The library allocates device memory only in etp_plan_create (nothing
+ * today: its tables are compiled in) and for ETP_FLAG_VALIDATE. Calls are
+ * asynchronous on the given stream (a hipStream_t passed as void*, NULL =
+ * the null stream) and never synchronise it, except ETP_FLAG_VALIDATE.
+ * Outputs must not alias inputs. A NULL optional output is not computed; a
+ * NULL cotangent means zero.
+ *
+ * Errors. Argument validation runs on the host before any launch; on error
+ * nothing is launched. Device-side data (row_ptr monotone, src in range) is
+ * trusted unless ETP_FLAG_VALIDATE is passed. Launch failures return
+ * ETP_ERR_HIP.
+ *
+ * Limits of this implementation: l_max_in = l_max_sh = l_max_out = L in
+ * [0, 4]; all paths (paths == NULL or the full list); channels in [1, 1024],
+ * even when above 64; the VJP and VJP-of-VJP need channels <= 128; the graph
+ * has fewer than 2^31 edges.
+ */
+#ifndef ETP_H
+#define ETP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define ETP_API __attribute__((visibility("default")))
+#else
+#define ETP_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct etp_plan_s *etp_plan_t;
+
+typedef enum {
+    ETP_OK = 0,
+    ETP_ERR_INVALID_ARGUMENT = 1, /* null required pointer, negative size, out-of-range value */
+    ETP_ERR_UNSUPPORTED = 2,      /* valid request outside this implementation's limits */
+    ETP_ERR_WORKSPACE = 3,        /* workspace missing or too small */
+    ETP_ERR_HIP = 4,              /* a HIP runtime call or kernel launch failed */
+    ETP_ERR_ALLOC = 5,            /* host or device allocation failed */
+    ETP_ERR_INTERNAL = 6,         /* ETP_FLAG_VALIDATE found a malformed graph */
+} etp_status;
+
+typedef enum { ETP_F32 = 0, ETP_BF16 = 1 } etp_dtype;
+
+/* Plan descriptor. paths: HOST int32 [n_paths][3] (l1, l2, l3), or NULL for
+ * all paths; only the full list is supported. */
+typedef struct {
+    int32_t l_max_in, l_max_sh, l_max_out;
+    int32_t channels;
+    int32_t x_dtype; /* etp_dtype of x */
+    int32_t n_paths;
+    const int32_t *paths;
+} etp_plan_desc;
+
+/* A destination-sorted CSR graph. row_ptr[n_dst+1] (row_ptr[0] = 0,
+ * row_ptr[n_dst] = n_edges), src[n_edges] in [0, n_src). The stable
+ * transpose (from etp_csr_transpose) is needed by the VJP and VJP-of-VJP:
+ * src_ptr[n_src+1], perm[n_edges] = edge ids grouped by source in edge-id
+ * order, perm_dst[n_edges] = destination of perm[k]. All DEVICE pointers. */
+typedef struct {
+    int32_t n_dst, n_src;
+    int64_t n_edges;
+    const int32_t *row_ptr, *src;
+    const int32_t *src_ptr, *perm, *perm_dst;
+} etp_graph;
+
+typedef struct {
+    int32_t l_max, channels, x_dtype;
+    int32_t n_paths;   /* P */
+    int32_t nnz;       /* CG entries over all paths */
+    int32_t din_rows;  /* (l_max+1)^2: rows of x per node */
+    int32_t dsh;       /* (l_max+1)^2: SH per edge */
+    int32_t dout_rows; /* sum_p (2 l3_p + 1): rows of out per node */
+} etp_plan_info_t;
+
+enum {
+    ETP_FLAG_ACCUMULATE = 1u, /* node outputs (out, grad_x, d_x, d_grad_out) are added to, not overwritten */
+    ETP_FLAG_VALIDATE = 2u,   /* check the CSR on the device first (allocates and synchronises) */
+};
+
+/* Build a plan for (l_max, channels, x dtype). Host only; immutable after
+ * creation and usable from several streams. Errors: INVALID_ARGUMENT (null
+ * pointers, l_max outside [0, 4], channels outside [1, 1024], unknown
+ * dtype, malformed path list), UNSUPPORTED (unequal l_max, a partial path
+ * list, odd channels above 64). */
+ETP_API etp_status etp_plan_create(const etp_plan_desc *desc, etp_plan_t *plan);
+ETP_API etp_status etp_plan_destroy(etp_plan_t plan);
+ETP_API etp_status etp_plan_info(etp_plan_t plan, etp_plan_info_t *info);
+
+/* Copy the plan's tables into HOST buffers (any may be NULL):
+ * paths[P][3], out_off[P+1] (first output row of each path), cg_ptr[P+1]
+ * (CG entries of path p are [cg_ptr[p], cg_ptr[p+1])), cg_m[nnz][3] (m1, m2,
+ * m3, signed, entries ordered by (m1, m2, m3) within a path), cg_val[nnz]
+ * (float32 coefficients). */
+ETP_API etp_status etp_plan_tables(etp_plan_t plan, int32_t *paths, int32_t *out_off, int32_t *cg_ptr, int8_t *cg_m,
+                           float *cg_val);
+
+/* Device workspace (bytes) that etp_csr_transpose needs for n_src sources. */
+ETP_API etp_status etp_csr_transpose_workspace(int32_t n_src, size_t *bytes);
+
+/* Stable transpose of g's CSR (row_ptr, src, counts in g) into src_ptr,
+ * perm, perm_dst (the transpose fields of g are ignored). Integer work,
+ * bit-exact and deterministic: perm lists edge ids grouped by source, each
+ * group in increasing edge id. ws: DEVICE workspace of at least
+ * etp_csr_transpose_workspace(n_src) bytes. perm_dst doubles as scratch
+ * during the call. */
+ETP_API etp_status etp_csr_transpose(const etp_graph *g, int32_t *src_ptr, int32_t *perm, int32_t *perm_dst, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/* Spherical harmonics of n_edges bond vectors: Y[n][dsh] and, if dY is not
+ * NULL, dY[n][3][dsh] = dY/dr (with respect to the unnormalised vector). */
+ETP_API etp_status etp_sh(etp_plan_t plan, int64_t n_edges, const float *vec, float *Y, float *dY, void *stream);
+
+/* Forward: out[n_dst][Dout][C] from vec, x (plan dtype), w. */
+ETP_API etp_status etp_edge_conv_fwd(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x, const float *w,
+                             float *out, uint32_t flags, void *stream);
+
+/* VJP: given grad_out = dL/dout, grad_x = dL/dx (source-segmented),
+ * grad_w = dL/dw and grad_vec = dL/dvec (forces on the edges). Each output
+ * may be NULL. Needs the transpose in g. */
+ETP_API etp_status etp_edge_conv_vjp(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x, const float *w,
+                             const float *grad_out, float *grad_x, float *grad_w, float *grad_vec, uint32_t flags,
+                             void *stream);
+
+/* VJP of the VJP: with cotangents (gg_x, gg_w, gg_vec) on (grad_x, grad_w,
+ * grad_vec), the gradients of S = <gg_x, grad_x> + <gg_w, grad_w> +
+ * <gg_vec, grad_vec> with respect to x (d_x), w (d_w), vec (d_vec) and
+ * grad_out (d_grad_out). Cotangents may be NULL (zero; gg_x is f32 even for
+ * bf16 plans); outputs may be NULL. Needs the transpose in g. */
+ETP_API etp_status etp_edge_conv_vjp2(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x, const float *w,
+                              const float *grad_out, const float *gg_x, const float *gg_w, const float *gg_vec,
+                              float *d_x, float *d_w, float *d_vec, float *d_grad_out, uint32_t flags,
+                              void *stream);
+
+ETP_API const char *etp_status_string(etp_status s);
+
+/* Version of this ABI (major * 10000 + minor * 100 + patch). */
+ETP_API int32_t etp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ETP_H */

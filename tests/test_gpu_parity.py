@@ -1,0 +1,253 @@
+"""GPU parity of libetp (through its C ABI) against the float64 oracle.
+
+Bar (per output tensor, max |gpu - oracle| / max |oracle|): 1e-5 for fp32
+features; 1e-2 for bf16-stored features against the oracle fed the
+unrounded values, plus 1e-5 against the oracle fed the bf16-rounded values.
+Integer work (the CSR transpose) is compared bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+from gpu_common import (BF16_TOL, FP32_TOL, DeviceProblem, dst_subgraph, np_, rel_err,
+                        src_subgraph)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def edge_dst(row_ptr):
+    return np.repeat(np.arange(len(row_ptr) - 1), np.diff(row_ptr))
+
+
+# ---------------------------------------------------------------- transpose
+
+@pytest.mark.parametrize("case", ["tiny", "ragged", "fan_in", "fan_out_long", "empty_edges", "micro"])
+def test_transpose_bit_exact(case):
+    say("transpose", case)
+    wl = {"tiny": lambda: workloads.get("tiny"),
+          "ragged": lambda: workloads.small(1, 1, 300, 40, seed=3),
+          "fan_in": lambda: workloads.bipartite(1, 1, 7, 700, 300, 600, seed=1),
+          "fan_out_long": lambda: workloads.bipartite(1, 1, 3000, 3, 2, 3, seed=2),
+          "empty_edges": lambda: workloads.bipartite(1, 1, 5, 9, 0, 0, seed=0),
+          "micro": lambda: workloads.get("micro")}[case]()
+    p = DeviceProblem(wl, need=())
+    sp, perm, pdst = oracle.transpose(wl.row_ptr, wl.src, wl.n)
+    np.testing.assert_array_equal(np_(p.src_ptr), sp)
+    np.testing.assert_array_equal(np_(p.perm)[:wl.E], perm)
+    np.testing.assert_array_equal(np_(p.perm_dst)[:wl.E], pdst)
+    # and against a brute-force stable sort
+    order = np.argsort(wl.src, kind="stable")
+    np.testing.assert_array_equal(np_(p.perm)[:wl.E], order)
+
+
+# ----------------------------------------------------------------------- SH
+
+@pytest.mark.parametrize("L", [0, 1, 2, 3, 4])
+def test_sh_and_gradient(L):
+    import torch
+    from equivariant_interatomic_potentials_amd import etp
+    say("sh", L)
+    vec = workloads.random_vectors(1000, 0.8, 6.0, seed=L)
+    plan = etp.etp_plan_create(L, 8)
+    D = (L + 1) ** 2
+    v = torch.from_numpy(vec).cuda()
+    Y = torch.empty(1000, D, device="cuda")
+    dY = torch.empty(1000, 3, D, device="cuda")
+    etp.etp_sh(plan, v, Y, dY)
+    Y2 = torch.empty(1000, D, device="cuda")
+    etp.etp_sh(plan, v, Y2)
+    rY, rdY = oracle.sh(L, vec.astype(np.float64), grad=True)
+    assert rel_err(np_(Y), rY) < FP32_TOL
+    assert rel_err(np_(Y2), rY) < FP32_TOL
+    assert rel_err(np_(dY), rdY) < FP32_TOL
+
+
+# ------------------------------------------------------------ small graphs
+
+SMALL = [
+    # (L, C, graph kind) -- ragged rows incl. empty ones, channel masking
+    (0, 8, "ragged"), (1, 8, "ragged"), (1, 5, "ragged"), (2, 8, "ragged"), (2, 64, "ragged"),
+    (2, 96, "ragged"), (2, 128, "ragged"), (3, 16, "ragged"), (3, 128, "ragged"), (4, 8, "ragged"),
+    (4, 128, "ragged"),
+    # long destination segments (several T batches per wave) and long source segments
+    (2, 128, "fan_in"), (2, 64, "fan_out"), (3, 128, "fan_in"), (4, 64, "fan_out"), (1, 8, "fan_out"),
+]
+
+
+def small_wl(L, C, kind):
+    if kind == "ragged":
+        return workloads.small(L, C, 23, 14, seed=L * 100 + C)
+    if kind == "fan_in":
+        return workloads.bipartite(L, C, 5, 400, 250, 390, seed=L + C)
+    return workloads.bipartite(L, C, 300, 6, 1, 6, seed=L + 7 * C)
+
+
+@pytest.mark.parametrize("L,C,kind", SMALL)
+def test_fwd_small(L, C, kind):
+    say("fwd", L, C, kind)
+    wl = small_wl(L, C, kind)
+    p = DeviceProblem(wl)
+    out = np_(p.fwd())
+    ref = oracle.fwd(L, wl.row_ptr, wl.src, wl.vec, wl.x, wl.w)
+    assert rel_err(out, ref) < FP32_TOL, rel_err(out, ref)
+
+
+@pytest.mark.parametrize("L,C,kind", SMALL)
+def test_vjp_small(L, C, kind):
+    say("vjp", L, C, kind)
+    wl = small_wl(L, C, kind)
+    p = DeviceProblem(wl)
+    gx, gw, gr = (np_(t) for t in p.vjp())
+    rgx, rgw, rgr = oracle.vjp(L, wl.row_ptr, wl.src, wl.vec, wl.x, wl.w, wl.G)
+    assert rel_err(gx, rgx) < FP32_TOL, rel_err(gx, rgx)
+    assert rel_err(gw, rgw) < FP32_TOL, rel_err(gw, rgw)
+    assert rel_err(gr, rgr) < FP32_TOL, rel_err(gr, rgr)
+
+
+@pytest.mark.parametrize("L,C,kind", SMALL)
+def test_vjp2_small(L, C, kind):
+    say("vjp2", L, C, kind)
+    wl = small_wl(L, C, kind)
+    p = DeviceProblem(wl)
+    dx, dw, dr, dG = (np_(t) for t in p.vjp2())
+    r = oracle.vjp2(L, wl.row_ptr, wl.src, wl.vec, wl.x, wl.w, wl.G, wl.ggx, wl.ggw, wl.ggvec)
+    for name, got, ref in zip(("dx", "dw", "dr", "dG"), (dx, dw, dr, dG), r):
+        assert rel_err(got, ref) < FP32_TOL, (name, rel_err(got, ref))
+
+
+@pytest.mark.parametrize("cot", [("ggx",), ("ggw",), ("ggvec",), ("ggx", "ggw"), ()])
+def test_vjp2_null_cotangents(cot):
+    L, C = 2, 64
+    say("vjp2-null", cot)
+    wl = small_wl(L, C, "ragged")
+    p = DeviceProblem(wl)
+    dx, dw, dr, dG = (np_(t) for t in p.vjp2(cot=cot))
+    r = oracle.vjp2(L, wl.row_ptr, wl.src, wl.vec, wl.x, wl.w, wl.G,
+                    wl.ggx if "ggx" in cot else None, wl.ggw if "ggw" in cot else None,
+                    wl.ggvec if "ggvec" in cot else None)
+    for name, got, ref in zip(("dx", "dw", "dr", "dG"), (dx, dw, dr, dG), r):
+        if np.abs(ref).max() == 0:
+            assert np.abs(got).max() == 0, name
+        else:
+            assert rel_err(got, ref) < FP32_TOL, (name, rel_err(got, ref))
+
+
+def test_null_outputs_and_accumulate():
+    import torch
+    from equivariant_interatomic_potentials_amd import etp
+    L, C = 2, 128
+    say("null-outputs/accumulate")
+    wl = small_wl(L, C, "ragged")
+    p = DeviceProblem(wl)
+    full = p.fwd()
+    acc = full.clone()
+    p.fwd(flags=etp.ETP_FLAG_ACCUMULATE, out=acc)
+    assert rel_err(np_(acc), 2 * np_(full)) < FP32_TOL
+    gx, gw, gr = p.vjp()
+    gx2, gw2, gr2 = p.vjp(want=("gr",))
+    assert gx2 is None and gw2 is None
+    assert torch.equal(gr, gr2)
+    gx3 = gx.clone()
+    p.vjp(want=("gx",), flags=etp.ETP_FLAG_ACCUMULATE, gx=gx3)
+    assert rel_err(np_(gx3), 2 * np_(gx)) < FP32_TOL
+    dx, dw, dr, dG = p.vjp2()
+    _, dw2, _, _ = p.vjp2(want=("dw",))
+    assert torch.equal(dw, dw2)
+
+
+def test_bitwise_determinism():
+    import torch
+    L, C = 2, 128
+    say("determinism")
+    wl = small_wl(L, C, "fan_in")
+    p = DeviceProblem(wl)
+    a = [p.fwd(), *p.vjp(), *p.vjp2()]
+    b = [p.fwd(), *p.vjp(), *p.vjp2()]
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_validate_flag_rejects_malformed_graph():
+    import torch
+    from equivariant_interatomic_potentials_amd import etp
+    say("validate")
+    wl = small_wl(1, 8, "ragged")
+    p = DeviceProblem(wl)
+    out = p.empty(wl.n_dst, wl.Dout, wl.C)
+    p.fwd(flags=etp.ETP_FLAG_VALIDATE, out=out)       # well-formed: passes
+    bad_src = p.src.clone()
+    bad_src[0] = wl.n + 5                              # out of range, caught before any conv launch
+    g = etp.Graph(wl.n_dst, wl.n, p.row_ptr, bad_src)
+    with pytest.raises(etp.EtpError) as ei:
+        etp.etp_edge_conv_fwd(p.plan, g, p.vec, p.x, p.w, out, etp.ETP_FLAG_VALIDATE)
+    assert ei.value.status == etp.ETP_ERR_INTERNAL
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------- bf16
+
+@pytest.mark.parametrize("L,C", [(1, 8), (2, 128), (3, 128)])
+def test_bf16_features(L, C):
+    say("bf16", L, C)
+    wl = small_wl(L, C, "ragged")
+    p = DeviceProblem(wl, bf16=True)
+    out = np_(p.fwd())
+    gx, gw, gr = (np_(t) for t in p.vjp())
+    dx, dw, dr, dG = (np_(t) for t in p.vjp2())
+    got = dict(out=out, gx=gx, gw=gw, gr=gr, dx=dx, dw=dw, dr=dr, dG=dG)
+    for xin, tol in ((p.x_seen, FP32_TOL), (wl.x, BF16_TOL)):
+        ref = dict(out=oracle.fwd(L, wl.row_ptr, wl.src, wl.vec, xin, wl.w))
+        ref.update(zip(("gx", "gw", "gr"), oracle.vjp(L, wl.row_ptr, wl.src, wl.vec, xin, wl.w, wl.G)))
+        ref.update(zip(("dx", "dw", "dr", "dG"),
+                       oracle.vjp2(L, wl.row_ptr, wl.src, wl.vec, xin, wl.w, wl.G, wl.ggx, wl.ggw, wl.ggvec)))
+        for k in got:
+            assert rel_err(got[k], ref[k]) < tol, (k, tol, rel_err(got[k], ref[k]))
+
+
+# ------------------------------------------------- full-size configurations
+
+FULL = ["tiny", "micro", "micro3", "micro4", "water"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_config_sampled(name):
+    """The benchmarked shapes at full size; outputs checked on sampled rows
+    (destination rows for out / dG, source nodes and their edges for
+    gx / gw / gr / dx / dw / dr) against the oracle run on those rows."""
+    say("full", name)
+    wl = workloads.get(name)
+    p = DeviceProblem(wl)
+    L = wl.L
+    g = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, wl.n_dst - 1], g.choice(wl.n_dst, 6, replace=False)]))
+    cols = np.unique(np.concatenate([[0, wl.n - 1], g.choice(wl.n, 6, replace=False)]))
+
+    out = p.fwd()
+    rp, eidx = dst_subgraph(wl, rows)
+    ref = oracle.fwd(L, rp, wl.src[eidx], wl.vec[eidx], wl.x, wl.w[eidx])
+    assert rel_err(np_(out)[rows], ref) < FP32_TOL
+    del out
+
+    gx, gw, gr = p.vjp()
+    rp2, eidx2 = src_subgraph(wl, cols)
+    rgx, rgw, rgr = oracle.vjp(L, rp2, wl.src[eidx2], wl.vec[eidx2], wl.x, wl.w[eidx2], wl.G)
+    assert rel_err(np_(gx)[cols], rgx[cols]) < FP32_TOL
+    assert rel_err(np_(gw)[eidx2], rgw) < FP32_TOL
+    assert rel_err(np_(gr)[eidx2], rgr) < FP32_TOL
+    del gx, gw, gr
+
+    dx, dw, dr, dG = p.vjp2()
+    r_dst = oracle.vjp2(L, rp, wl.src[eidx], wl.vec[eidx], wl.x, wl.w[eidx], wl.G[rows], wl.ggx,
+                        wl.ggw[eidx], wl.ggvec[eidx])
+    assert rel_err(np_(dG)[rows], r_dst[3]) < FP32_TOL
+    r_src = oracle.vjp2(L, rp2, wl.src[eidx2], wl.vec[eidx2], wl.x, wl.w[eidx2], wl.G, wl.ggx,
+                        wl.ggw[eidx2], wl.ggvec[eidx2])
+    assert rel_err(np_(dx)[cols], r_src[0][cols]) < FP32_TOL
+    assert rel_err(np_(dw)[eidx2], r_src[1]) < FP32_TOL
+    assert rel_err(np_(dr)[eidx2], r_src[2]) < FP32_TOL

@@ -1,0 +1,136 @@
+"""Host-side checks of libetp that need no GPU: the exported ABI, plan
+validation and error codes, and the plan's tables against the oracle
+(integer pattern bit-exact, coefficients equal to the float32 rounding of
+the oracle's float64 values)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "equivariant_interatomic_potentials_amd", "libetp.so")
+
+
+def _ensure_built():
+    if not os.path.exists(LIB):
+        from equivariant_interatomic_potentials_amd import build
+        build.build()
+
+
+_ensure_built()
+from equivariant_interatomic_potentials_amd import etp  # noqa: E402
+import oracle  # noqa: E402
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "etp.h")).read()
+    return sorted(set(re.findall(r"ETP_API\s+[\w\s\*]+?\b(etp_\w+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = header_symbols()
+    assert len(names) == 12
+    assert sorted(etp.ABI_SYMBOLS) == names
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (etp_\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_version_and_status_strings():
+    assert etp.etp_version() == 100
+    for s in range(7):
+        assert etp.etp_status_string(s)
+    assert etp.etp_status_string(99) == "unknown status"
+
+
+def _create(lin, lsh, lout, C, dtype=0, paths=None, n_paths=0):
+    d = etp.etp_plan_desc(lin, lsh, lout, C, dtype, n_paths, None)
+    keep = None
+    if paths is not None:
+        keep = np.ascontiguousarray(paths, np.int32)
+        d.paths = keep.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        d.n_paths = keep.shape[0]
+    h = ctypes.c_void_p()
+    st = etp.lib.etp_plan_create(ctypes.byref(d), ctypes.byref(h))
+    if st == 0:
+        etp.lib.etp_plan_destroy(h)
+    return st
+
+
+def test_plan_validation_codes():
+    INV, UNS = etp.ETP_ERR_INVALID_ARGUMENT, etp.ETP_ERR_UNSUPPORTED
+    assert _create(2, 2, 2, 128) == 0
+    assert _create(0, 0, 0, 1) == 0
+    assert _create(4, 4, 4, 1024, 1) == 0
+    assert _create(5, 5, 5, 8) == INV
+    assert _create(-1, 2, 2, 8) == INV
+    assert _create(2, 2, 2, 0) == INV
+    assert _create(2, 2, 2, 1025) == INV
+    assert _create(2, 2, 2, 8, dtype=7) == INV
+    assert _create(2, 1, 2, 8) == UNS
+    assert _create(2, 2, 2, 65) == UNS
+    assert _create(2, 2, 2, 63) == 0
+    full = oracle.paths(2)
+    assert _create(2, 2, 2, 8, paths=full) == 0
+    assert _create(2, 2, 2, 8, paths=full[:-1]) == UNS
+    bad = full.copy()
+    bad[0] = (0, 0, 3)
+    assert _create(2, 2, 2, 8, paths=bad) == INV
+    d = etp.etp_plan_desc(2, 2, 2, 8, 0, 0, None)
+    assert etp.lib.etp_plan_create(ctypes.byref(d), None) == INV
+    assert etp.lib.etp_plan_create(None, None) == INV
+
+
+@pytest.mark.parametrize("L", [0, 1, 2, 3, 4])
+def test_plan_tables_match_oracle(L):
+    plan = etp.etp_plan_create(L, 16)
+    t = etp.etp_plan_tables(plan)
+    d = oracle.dims(L)
+    info = etp.etp_plan_info(plan)
+    assert (info["n_paths"], info["nnz"], info["din_rows"], info["dsh"], info["dout_rows"]) == \
+        (d["P"], d["nnz"], d["Din"], d["Dsh"], d["Dout"])
+    np.testing.assert_array_equal(t["paths"], oracle.paths(L))
+    ptr, m, val = oracle.cg_sparse(L)
+    np.testing.assert_array_equal(t["cg_ptr"], ptr)
+    np.testing.assert_array_equal(t["cg_m"], m)
+    # float32 coefficients: exactly the round-to-nearest of the oracle's float64
+    np.testing.assert_array_equal(t["cg_val"], val.astype(np.float32))
+    off = np.concatenate([[0], np.cumsum(2 * oracle.paths(L)[:, 2] + 1)])
+    np.testing.assert_array_equal(t["out_off"], off)
+
+
+def test_call_validation_without_device():
+    """Argument errors are reported before any HIP call."""
+    INV, UNS, WS = etp.ETP_ERR_INVALID_ARGUMENT, etp.ETP_ERR_UNSUPPORTED, etp.ETP_ERR_WORKSPACE
+    plan = etp.etp_plan_create(2, 128)
+    big = etp.etp_plan_create(2, 256)
+    g = etp.etp_graph(4, 4, 8, None, None, None, None, None)
+    lib = etp.lib
+    assert lib.etp_edge_conv_fwd(plan.handle, None, None, None, None, None, 0, None) == INV
+    assert lib.etp_edge_conv_fwd(None, ctypes.byref(g), None, None, None, None, 0, None) == INV
+    assert lib.etp_edge_conv_fwd(plan.handle, ctypes.byref(g), None, None, None, None, 0, None) == INV
+    g2 = etp.etp_graph(4, 4, 2 ** 31, 8, 8, 8, 8, 8)
+    assert lib.etp_edge_conv_fwd(plan.handle, ctypes.byref(g2), 8, 8, 8, 8, 0, None) == UNS
+    g3 = etp.etp_graph(-1, 4, 0, 8, 8, None, None, None)
+    assert lib.etp_edge_conv_fwd(plan.handle, ctypes.byref(g3), 8, 8, 8, 8, 0, None) == INV
+    g4 = etp.etp_graph(4, 4, 8, 8, 8, None, None, None)      # no transpose
+    assert lib.etp_edge_conv_vjp(plan.handle, ctypes.byref(g4), 8, 8, 8, 8, 8, 8, 8, 0, None) == INV
+    assert lib.etp_edge_conv_vjp2(plan.handle, ctypes.byref(g4), 8, 8, 8, 8, None, None, None,
+                                  8, 8, 8, 8, 0, None) == INV
+    g5 = etp.etp_graph(4, 4, 8, 8, 8, 8, 8, 8)
+    assert lib.etp_edge_conv_vjp(big.handle, ctypes.byref(g5), 8, 8, 8, 8, 8, 8, 8, 0, None) == UNS
+    assert lib.etp_edge_conv_fwd(plan.handle, ctypes.byref(g5), 8, 8, 8, 8, 4, None) == INV   # unknown flag
+    assert lib.etp_csr_transpose(ctypes.byref(g5), 8, 8, 8, None, 0, None) == WS
+    assert lib.etp_csr_transpose(ctypes.byref(g5), 8, 8, 8, 8, 1, None) == WS
+    assert lib.etp_sh(None, 4, 8, 8, None, None) == INV
+    assert lib.etp_sh(plan.handle, -1, 8, 8, None, None) == INV
+    assert lib.etp_sh(plan.handle, 0, None, None, None, None) == 0
+    b = ctypes.c_size_t()
+    assert lib.etp_csr_transpose_workspace(1000, ctypes.byref(b)) == 0 and b.value >= 4000
+    assert lib.etp_csr_transpose_workspace(-1, ctypes.byref(b)) == INV

@@ -120,8 +120,9 @@ def diamond_positions(seed: int, n_side: int = 16, a: float = 3.567, sigma: floa
 
 @dataclasses.dataclass
 class Workload:
-    """A graph plus lazily drawn arrays. Shapes: x[n_src, (L+1)^2, C],
-    w[E, P, C], G/ggG[n_dst, Dout, C], vec[E, 3]; all float32."""
+    """A graph plus lazily drawn arrays. Shapes: x[n, (L+1)^2, C] (n source
+    nodes), w[E, P, C], G[n_dst, Dout, C], vec[E, 3]; all float32. n_dst
+    defaults to n."""
     name: str
     L: int
     C: int
@@ -131,6 +132,11 @@ class Workload:
     vec: np.ndarray
     seed: int = 0
     x_bf16: bool = False
+    n_dst: int = -1
+
+    def __post_init__(self):
+        if self.n_dst < 0:
+            self.n_dst = self.n
 
     @property
     def E(self) -> int:
@@ -160,7 +166,7 @@ class Workload:
 
     @functools.cached_property
     def G(self) -> np.ndarray:
-        return rng(self.seed, "G").standard_normal((self.n, self.Dout, self.C), np.float32)
+        return rng(self.seed, "G").standard_normal((self.n_dst, self.Dout, self.C), np.float32)
 
     @functools.cached_property
     def ggx(self) -> np.ndarray:
@@ -214,6 +220,24 @@ def get(name: str, seed: int = 0) -> Workload:
         row_ptr, src, vec = cutoff_csr(pos, box, 6.0)
         return Workload("diamond", 3, 128, pos.shape[0], row_ptr, src, vec, seed, x_bf16=True)
     raise KeyError(name)
+
+
+def bipartite(L: int, C: int, n_dst: int, n_src: int, k_min: int, k_max: int, seed: int = 0,
+              lo: float = 0.8, hi: float = 5.0) -> "Workload":
+    """n_dst destinations drawing k in [k_min, k_max] distinct sources each
+    from n_src nodes (rows sorted by src). Few destinations with many sources
+    exercise long destination segments; few sources, long source segments."""
+    g = rng(seed, "graph")
+    deg = g.integers(k_min, k_max + 1, size=n_dst)
+    deg = np.minimum(deg, n_src)
+    rows = [np.sort(g.choice(n_src, size=int(d), replace=False)) for d in deg]
+    row_ptr = np.zeros(n_dst + 1, np.int64)
+    row_ptr[1:] = np.cumsum(deg)
+    src = np.concatenate(rows).astype(np.int32) if n_dst else np.zeros(0, np.int32)
+    vec = random_vectors(int(row_ptr[-1]), lo, hi, seed)
+    w = Workload(f"bip_L{L}_C{C}_{n_dst}x{n_src}", L, C, n_src, row_ptr.astype(np.int32), src, vec, seed)
+    w.n_dst = n_dst
+    return w
 
 
 def small(L: int, C: int, n: int, k_max: int, seed: int = 0, lo: float = 0.8, hi: float = 5.0,
