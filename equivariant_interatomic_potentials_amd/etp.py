@@ -57,11 +57,32 @@ class etp_plan_info_t(ctypes.Structure):
                 ("dsh", ctypes.c_int32), ("dout_rows", ctypes.c_int32)]
 
 
+def _hip_runtimes():
+    """Distinct libamdhip64 files mapped into this process."""
+    found = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                path = line.split()[-1]
+                if "libamdhip64.so" in os.path.basename(path):
+                    found.add(os.path.realpath(path))
+    except OSError:
+        pass
+    return found
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is not built; run "
                           "`python -m equivariant_interatomic_potentials_amd.build`")
+    # torch provides device memory and streams and ships its own HIP runtime
+    # (same soname as the system one). Loading torch first makes libetp bind
+    # to that runtime, so there is exactly one HIP runtime in the process.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(_LIB_PATH)
+    rts = _hip_runtimes()
+    if len(rts) > 1:
+        raise ImportError(f"two HIP runtimes are loaded ({sorted(rts)}); import torch before loading libetp")
     vp, st, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
     sig = {
         "etp_plan_create": (st, [ctypes.POINTER(etp_plan_desc), ctypes.POINTER(vp)]),

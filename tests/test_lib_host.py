@@ -42,6 +42,11 @@ def test_header_symbols_exported():
         assert getattr(lib, n) is not None
 
 
+def test_single_hip_runtime():
+    """libetp binds to the HIP runtime torch loaded (one runtime per process)."""
+    assert len(etp._hip_runtimes()) == 1
+
+
 def test_version_and_status_strings():
     assert etp.etp_version() == 100
     for s in range(7):
