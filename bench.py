@@ -150,6 +150,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="micro", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (a kernel of known traffic "
+                         "for scaling hardware byte counters)")
     a = ap.parse_args(argv)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -198,6 +201,12 @@ def main(argv=None):
             if events is not None:
                 events[i][1].record()
 
+    if a.calib_copy_mib:
+        n = a.calib_copy_mib * (1 << 20) // 4
+        cs, cd = torch.ones(n, device="cuda"), torch.empty(n, device="cuda")
+        cd.copy_(cs)
+        torch.cuda.synchronize()
+        del cs, cd
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()

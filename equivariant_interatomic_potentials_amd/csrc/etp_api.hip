@@ -293,7 +293,7 @@ etp_status etp_edge_conv_vjp(etp_plan_t plan, const etp_graph *g, const float *v
     etp_status st = check_graph(g, true);
     if (st != ETP_OK)
         return st;
-    if (plan->C > 128)
+    if (plan->C > 256)
         return ETP_ERR_UNSUPPORTED;
     if (flags & ~3u)
         return ETP_ERR_INVALID_ARGUMENT;
@@ -339,7 +339,7 @@ etp_status etp_edge_conv_vjp2(etp_plan_t plan, const etp_graph *g, const float *
     etp_status st = check_graph(g, true);
     if (st != ETP_OK)
         return st;
-    if (plan->C > 128)
+    if (plan->C > 256)
         return ETP_ERR_UNSUPPORTED;
     if (flags & ~3u)
         return ETP_ERR_INVALID_ARGUMENT;

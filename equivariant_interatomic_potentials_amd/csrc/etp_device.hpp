@@ -296,4 +296,64 @@ __device__ __forceinline__ V vzero()
     return V(0.f);
 }
 
+// ------------------------------------------------------ buffer resources
+// Raw buffer descriptors over one contiguous block (a node's or an edge's
+// rows). Lanes whose channel lies beyond C use a byte offset past the end
+// of the block: the hardware's range check then returns 0 for their loads
+// and drops their stores, so partially filled channel chunks need no
+// branches around memory operations.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kNT = 2;  // cache policy: non-temporal (streamed once)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
+
+// One or two f32 channels at byte offset voff (+ row offset soff) of r.
+template <typename V, int AUX = 0>
+__device__ __forceinline__ V bload(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    if constexpr (sizeof(V) == 4) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX));
+    } else {
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX));
+    }
+}
+// One or two bf16 channels, widened to f32.
+template <typename V>
+__device__ __forceinline__ V bload_bf16(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    if constexpr (sizeof(V) == 4) {
+        const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+        return __uint_as_float(h << 16);
+    } else {
+        const uint32_t t = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+        V v;
+        v.x = __uint_as_float(t << 16);
+        v.y = __uint_as_float(t & 0xFFFF0000u);
+        return v;
+    }
+}
+template <typename V, typename XT>
+__device__ __forceinline__ V bload_x(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    if constexpr (sizeof(XT) == 2)
+        return bload_bf16<V>(r, voff, soff);
+    else
+        return bload<V>(r, voff, soff);
+}
+template <typename V, int AUX = 0>
+__device__ __forceinline__ void bstore(V v, rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    if constexpr (sizeof(V) == 4) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, AUX);
+    } else {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, soff, AUX);
+    }
+}
+
 }  // namespace etp

@@ -66,6 +66,11 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
         return;
     const int u0 = chunk * 64 * CPL + lane * CPL;
     const bool active = u0 < C;
+    // byte offsets of this lane's channels; lanes past C use an offset
+    // beyond every block, so their buffer loads read 0 and stores are dropped
+    const uint32_t off4 = active ? static_cast<uint32_t>(u0) * 4u : kOOB;
+    const uint32_t offx = active ? static_cast<uint32_t>(u0) * static_cast<uint32_t>(sizeof(XT)) : kOOB;
+    const uint32_t rowb = static_cast<uint32_t>(C) * 4u, rowx = static_cast<uint32_t>(C) * sizeof(XT);
     const bool has_xp = DG && ggx != nullptr, has_wp = DG && ggw != nullptr, has_rp = DG && ggvec != nullptr;
 
     const int rb = row_ptr[node], re = row_ptr[node + 1];
@@ -84,19 +89,18 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
     };
     auto load = [&](int e, Ops &o) {
         const int j = src[e];
-        const float *we = w + static_cast<int64_t>(e) * (P * C) + u0;
-        const XT *xj = x + static_cast<int64_t>(j) * (DIN * C) + u0;
-        static_range<0, NP>([&](auto q) { o.w[q] = active ? load_stream<V>(we + (GI.p0 + q) * C) : vzero<V>(); });
-        static_range<0, NXR>([&](auto q) { o.x[q] = active ? load_cached<V>(xj + (GI.xr0 + q) * C) : vzero<V>(); });
+        const rsrc_t rw = make_rsrc(w + static_cast<int64_t>(e) * (P * C), P * C * 4u);
+        const rsrc_t rx = make_rsrc(x + static_cast<int64_t>(j) * (DIN * C), DIN * C * sizeof(XT));
+        static_range<0, NP>([&](auto q) { o.w[q] = bload<V, kNT>(rw, off4, (GI.p0 + q) * rowb); });
+        static_range<0, NXR>([&](auto q) { o.x[q] = bload_x<V, XT>(rx, offx, (GI.xr0 + q) * rowx); });
         if constexpr (DG) {
-            const float *wpe = has_wp ? ggw + static_cast<int64_t>(e) * (P * C) + u0 : nullptr;
-            const float *xpj = has_xp ? ggx + static_cast<int64_t>(j) * (DIN * C) + u0 : nullptr;
-            static_range<0, NP>([&](auto q) {
-                o.wp[q] = (has_wp && active) ? load_stream<V>(wpe + (GI.p0 + q) * C) : vzero<V>();
-            });
-            static_range<0, NXR>([&](auto q) {
-                o.xp[q] = (has_xp && active) ? load_cached<V>(xpj + (GI.xr0 + q) * C) : vzero<V>();
-            });
+            // a missing cotangent is a zero-length block: its loads read 0
+            const rsrc_t rwp = make_rsrc(has_wp ? ggw + static_cast<int64_t>(e) * (P * C) : nullptr,
+                                         has_wp ? P * C * 4u : 0u);
+            const rsrc_t rxp = make_rsrc(has_xp ? ggx + static_cast<int64_t>(j) * (DIN * C) : nullptr,
+                                         has_xp ? DIN * C * 4u : 0u);
+            static_range<0, NP>([&](auto q) { o.wp[q] = bload<V, kNT>(rwp, off4, (GI.p0 + q) * rowb); });
+            static_range<0, NXR>([&](auto q) { o.xp[q] = bload<V>(rxp, off4, (GI.xr0 + q) * rowb); });
         }
     };
 
@@ -198,12 +202,15 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
 
     reduce_waves<S, NROW, V, LDS_FLOATS>(acc, lds, lane, wv);
 
-    if (wv == 0 && active) {
-        float *op = out + static_cast<int64_t>(node) * (DOUT * C) + u0 + GI.row0 * C;
+    if (wv == 0) {
+        const rsrc_t ro = make_rsrc(out + static_cast<int64_t>(node) * (DOUT * C), DOUT * C * 4u);
         if (flags & 1u) {
-            static_range<0, NROW>([&](auto r) { store_v<V>(op + r * C, acc[r] + load_cached<V>(op + r * C)); });
+            static_range<0, NROW>([&](auto r) {
+                const uint32_t so = (GI.row0 + r) * rowb;
+                bstore<V>(acc[r] + bload<V>(ro, off4, so), ro, off4, so);
+            });
         } else {
-            static_range<0, NROW>([&](auto r) { store_v<V>(op + r * C, acc[r]); });
+            static_range<0, NROW>([&](auto r) { bstore<V>(acc[r], ro, off4, (GI.row0 + r) * rowb); });
         }
     }
 }

@@ -95,39 +95,40 @@ constexpr bool first_m1_in_path(const Table &T, int q)
     return true;
 }
 
-// Source-side passes: groups are unions of whole l1 blocks (so the node
-// accumulators of one group are rows no other group touches), closed when
-// the group's paths plus x rows would exceed max_cost.
+// Source-side passes: contiguous path groups sized so that one edge's
+// streamed operands (wmul weight rows per path + the G rows of the group's
+// paths), double buffered, plus the resident x rows fit the VGPR budget:
+// cost = wmul * paths + G rows + 2 * x rows <= max_cost. A group may start
+// inside an l1 block; the node rows of that l1 are then added to the rows
+// the previous group stored.
 struct SrcGroupInfo {
     int p0, p1, np;        // paths
     int ab0, ab1;          // (m1, m2) groups
     int xr0, xr1, nxr;     // x rows
+    int gr0, gr1, ngr;     // G rows (out rows of the group's paths)
+    bool shares_first_l1;  // an earlier group also touched the first l1
 };
 
-constexpr Groups make_src_groups(const Table &T, int max_cost)
+constexpr int src_cost(const Table &T, int p0, int p1, int wmul)
+{
+    const int l1a = T.path[p0].l1, l1b = T.path[p1 - 1].l1;
+    const int xrows = (l1b + 1) * (l1b + 1) - l1a * l1a;
+    const int grows = T.path[p1 - 1].out_row + 2 * T.path[p1 - 1].l3 + 1 - T.path[p0].out_row;
+    return wmul * (p1 - p0) + grows + 2 * xrows;
+}
+
+constexpr Groups make_src_groups(const Table &T, int max_cost, int wmul)
 {
     Groups g{};
-    int start = 0, cost = 0;
-    int p = 0;
-    while (p < T.P) {
-        // the block of paths with the same l1
-        int q = p;
-        while (q < T.P && T.path[q].l1 == T.path[p].l1)
-            ++q;
-        const int c = (q - p) + 2 * T.path[p].l1 + 1;
-        if (cost > 0 && cost + c > max_cost) {
+    int start = 0;
+    for (int p = 1; p <= T.P; ++p) {
+        if (p == T.P || src_cost(T, start, p + 1, wmul) > max_cost) {
             g.p0[g.n] = start;
             g.p1[g.n] = p;
             ++g.n;
             start = p;
-            cost = 0;
         }
-        cost += c;
-        p = q;
     }
-    g.p0[g.n] = start;
-    g.p1[g.n] = T.P;
-    ++g.n;
     return g;
 }
 
@@ -143,6 +144,10 @@ constexpr SrcGroupInfo src_group_info(const Table &T, const Groups &g, int k)
     gi.xr0 = l1a * l1a;
     gi.xr1 = (l1b + 1) * (l1b + 1);
     gi.nxr = gi.xr1 - gi.xr0;
+    gi.gr0 = T.path[gi.p0].out_row;
+    gi.gr1 = T.path[gi.p1 - 1].out_row + 2 * T.path[gi.p1 - 1].l3 + 1;
+    gi.ngr = gi.gr1 - gi.gr0;
+    gi.shares_first_l1 = gi.p0 > 0 && T.path[gi.p0 - 1].l1 == l1a;
     return gi;
 }
 

@@ -15,30 +15,42 @@
 //         Z1_b = sum (w X' + W' x) K,  Z2_b = sum w x K,  Yd = grad Y . R'.
 //
 // Mapping (gfx950, wave64):
-//   * one workgroup per source node j; its S waves split j's out-edges
-//     (the stable transpose of the destination-sorted CSR) into contiguous
-//     parts; a lane owns CPL = C/64 channels (C <= 128) so Z reduces within
-//     one wave;
-//   * x[j] (and X'[j]) rows and the gx / dx accumulators stay in registers;
-//     G[i] rows are gathered per path (cached), w / W' streamed
-//     non-temporally, gw / dw written once per edge;
-//   * per batch of B edges, lane k evaluates the SH of edge k (and Yd) into
-//     LDS; per edge the wave reads them as broadcast float4;
-//   * Z is reduced over the wave with DPP in a fixed order, parked in LDS,
-//     and at the end of the batch lane k turns it into gr / dr of edge k with
-//     forward-mode SH derivatives; no float atomics anywhere.
+//   * one workgroup per source node j with one wave per 64-channel chunk
+//     (one channel per lane); every wave walks all of j's out-edges (the
+//     stable transpose of the destination-sorted CSR), so the gx / dx rows
+//     of a chunk stay in one wave's registers and need no reduction;
+//   * x[j] (and X'[j]) rows stay in registers; per edge the wave streams the
+//     w (and W') rows of its path group and gathers the group's G[i] rows
+//     with raw buffer loads (lanes past C read 0 and their stores are
+//     dropped by the buffer range check, so there are no branches around
+//     memory operations); the next edge's operands are loaded before the
+//     current edge's FMAs;
+//   * per batch of B edges each wave evaluates the SH of the batch (lane =
+//     edge) into its LDS slice; the edge loop reads them as broadcast float4;
+//   * Z is reduced over each wave's lanes with DPP in a fixed order, parked
+//     in LDS per chunk, and at the end of the batch lane k of wave 0 sums the
+//     chunks in order and turns Z into gr / dr of edge k with forward-mode SH
+//     derivatives; no float atomics anywhere.
 #include "etp_conv_common.hpp"
 
 namespace etp {
 
-template <int L, int CPL>
+template <int L, int MODE>
 struct SrcCfg {
-    static constexpr int S = 4;
     static constexpr int B = L <= 2 ? 64 : 32;
-    static constexpr int MAXCOST = 40 / CPL;
+    static constexpr int WMUL = MODE == SRC_VJP2 ? 2 : 1;
+    static constexpr int MAXCOST = 60;
 };
 
-template <int L, int CPL, typename XT, int MODE, int SG>
+template <int L, int MODE>
+constexpr int src_lds_floats(int nch)
+{
+    constexpr int DSH = kTab<L>.dsh, DSHP = (DSH + 3) & ~3;
+    constexpr int NV = MODE == SRC_VJP2 ? 2 : 1;
+    return nch * NV * SrcCfg<L, MODE>::B * (DSHP + DSH);
+}
+
+template <int L, typename XT, int MODE, int SG>
 __device__ __forceinline__ void src_group(const int n_src, const int C, const int *__restrict__ src_ptr,
                                           const int *__restrict__ perm, const int *__restrict__ perm_dst,
                                           const float *__restrict__ vec, const XT *__restrict__ x,
@@ -48,47 +60,64 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                                           float *__restrict__ ow, float *__restrict__ ovec,
                                           const uint32_t flags, float *lds)
 {
-    using V = chv_t<CPL>;
-    using Cfg = SrcCfg<L, CPL>;
-    constexpr int S = Cfg::S, B = Cfg::B;
-    constexpr Groups GR = make_src_groups(kTab<L>, Cfg::MAXCOST);
+    using Cfg = SrcCfg<L, MODE>;
+    constexpr int B = Cfg::B;
+    constexpr bool V2 = MODE == SRC_VJP2;
+    constexpr Groups GR = make_src_groups(kTab<L>, Cfg::MAXCOST, Cfg::WMUL);
     constexpr SrcGroupInfo GI = src_group_info(kTab<L>, GR, SG);
     constexpr int P = kTab<L>.P, DIN = kTab<L>.din_rows, DOUT = kTab<L>.dout_rows, DSH = kTab<L>.dsh;
-    constexpr int NXR = GI.nxr;
+    constexpr int NP = GI.np, NXR = GI.nxr, NGR = GI.ngr;
     constexpr int BLO = sh_lo(kTab<L>, GI.p0, GI.p1), BHI = sh_hi(kTab<L>, GI.p0, GI.p1);
     constexpr int DSHP = (DSH + 3) & ~3;
-    constexpr bool V2 = MODE == SRC_VJP2;
-    // per-wave LDS: Y[B][DSHP] (+ Yd[B][DSHP]) and Z[B][DSH] (+ Z2[B][DSH])
-    constexpr int WAVE_FLOATS = (V2 ? 2 : 1) * B * (DSHP + DSH);
+    constexpr int NV = V2 ? 2 : 1;  // SH copies (Y, Yd) and Z copies (Z1, Z2)
 
-    const int lane = threadIdx.x & 63, wv = wave_id();
+    const int lane = threadIdx.x & 63, wv = wave_id(), nch = blockDim.x >> 6;
     const int j = xcd_remap(blockIdx.x, gridDim.x);
     if (j >= n_src)
         return;
-    const int u0 = lane * CPL;
-    const bool active = u0 < C;
+    const int u = wv * 64 + lane;
+    const bool active = u < C;
+    const uint32_t off4 = active ? static_cast<uint32_t>(u) * 4u : kOOB;
+    const uint32_t offx = active ? static_cast<uint32_t>(u) * static_cast<uint32_t>(sizeof(XT)) : kOOB;
     const bool want_vec = ovec != nullptr;
     const bool has_xp = V2 && ggx != nullptr, has_wp = V2 && ggw != nullptr, has_rp = V2 && ggvec != nullptr;
+    const uint32_t rowb = static_cast<uint32_t>(C) * 4u;  // bytes per f32 row
 
-    float *ylds = lds + wv * WAVE_FLOATS;         // Y, then Yd
-    float *zlds = ylds + (V2 ? 2 : 1) * B * DSHP;  // Z, then Z2
+    // LDS: per wave Y[B][DSHP] (+ Yd[B][DSHP]); then per chunk Z[B][DSH] (+ Z2[B][DSH])
+    float *ylds = lds + wv * (NV * B * DSHP);
+    float *zall = lds + nch * (NV * B * DSHP);
+    float *zlds = zall + wv * (NV * B * DSH);
 
     const int kb0 = src_ptr[j], kb1 = src_ptr[j + 1];
-    const int len = kb1 - kb0;
-    const int k_begin = kb0 + static_cast<int>((static_cast<int64_t>(len) * wv) / S);
-    const int k_end = kb0 + static_cast<int>((static_cast<int64_t>(len) * (wv + 1)) / S);
 
     // node-resident rows of x[j] (and X'[j]) for this group's l1 values
-    V xr[NXR], xpr[NXR], acc[NXR];
+    float xr[NXR], xpr[NXR], acc[NXR];
     {
-        const XT *xj = x + static_cast<int64_t>(j) * (DIN * C) + u0;
-        const float *xpj = has_xp ? ggx + static_cast<int64_t>(j) * (DIN * C) + u0 : nullptr;
+        const rsrc_t rx = make_rsrc(x + static_cast<int64_t>(j) * (DIN * C), DIN * C * sizeof(XT));
+        const rsrc_t rxp = make_rsrc(has_xp ? ggx + static_cast<int64_t>(j) * (DIN * C) : nullptr,
+                                     has_xp ? DIN * C * 4u : 0u);
         static_range<0, NXR>([&](auto q) {
-            xr[q] = active ? load_cached<V>(xj + (GI.xr0 + q) * C) : vzero<V>();
-            xpr[q] = (has_xp && active) ? load_cached<V>(xpj + (GI.xr0 + q) * C) : vzero<V>();
-            acc[q] = vzero<V>();
+            xr[q] = bload_x<float, XT>(rx, offx, (GI.xr0 + q) * C * sizeof(XT));
+            xpr[q] = V2 ? bload<float>(rxp, off4, (GI.xr0 + q) * rowb) : 0.f;
+            acc[q] = 0.f;
         });
     }
+
+    struct Ops {
+        float w[NP], wp[V2 ? NP : 1], g[NGR];
+    };
+    auto load = [&](int k, Ops &o) {
+        const int e = perm[k], i = perm_dst[k];
+        const rsrc_t rw = make_rsrc(w + static_cast<int64_t>(e) * (P * C), P * C * 4u);
+        const rsrc_t rg = make_rsrc(G + static_cast<int64_t>(i) * (DOUT * C), DOUT * C * 4u);
+        static_range<0, NP>([&](auto q) { o.w[q] = bload<float, kNT>(rw, off4, (GI.p0 + q) * rowb); });
+        static_range<0, NGR>([&](auto r) { o.g[r] = bload<float>(rg, off4, (GI.gr0 + r) * rowb); });
+        if constexpr (V2) {
+            const rsrc_t rwp = make_rsrc(has_wp ? ggw + static_cast<int64_t>(e) * (P * C) : nullptr,
+                                         has_wp ? P * C * 4u : 0u);
+            static_range<0, NP>([&](auto q) { o.wp[q] = bload<float, kNT>(rwp, off4, (GI.p0 + q) * rowb); });
+        }
+    };
 
     auto prologue = [&](int kb, int nb) {
         wave_sync_lds();
@@ -96,18 +125,15 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
             const int e = perm[kb + lane];
             const float rx = vec[3 * e], ry = vec[3 * e + 1], rz = vec[3 * e + 2];
             float *yp = ylds + lane * DSHP;
+            float yv[DSHP], ydv[DSHP];
             if constexpr (!V2) {
-                float Y[DSH], yv[DSHP];
+                float Y[DSH];
                 sh_value<L>(rx, ry, rz, Y);
                 static_range<0, DSHP>([&](auto b) {
                     if constexpr (b < DSH)
                         yv[b] = Y[b];
                     else
                         yv[b] = 0.f;
-                });
-                static_range<0, DSHP / 4>([&](auto q) {
-                    *reinterpret_cast<float4 *>(yp + 4 * q) =
-                        make_float4(yv[4 * q], yv[4 * q + 1], yv[4 * q + 2], yv[4 * q + 3]);
                 });
             } else {
                 D3 Y[DSH];
@@ -118,37 +144,56 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                     py = ggvec[3 * e + 1];
                     pz = ggvec[3 * e + 2];
                 }
-                float *ydp = ylds + B * DSHP + lane * DSHP;
                 static_range<0, DSHP>([&](auto b) {
                     if constexpr (b < DSH) {
-                        yp[b] = Y[b].v;
-                        ydp[b] = Y[b].g0 * px + Y[b].g1 * py + Y[b].g2 * pz;
+                        yv[b] = Y[b].v;
+                        ydv[b] = Y[b].g0 * px + Y[b].g1 * py + Y[b].g2 * pz;
                     } else {
-                        yp[b] = 0.f;
-                        ydp[b] = 0.f;
+                        yv[b] = 0.f;
+                        ydv[b] = 0.f;
                     }
                 });
             }
+            static_range<0, DSHP / 4>([&](auto q) {
+                *reinterpret_cast<float4 *>(yp + 4 * q) =
+                    make_float4(yv[4 * q], yv[4 * q + 1], yv[4 * q + 2], yv[4 * q + 3]);
+                if constexpr (V2)
+                    *reinterpret_cast<float4 *>(yp + B * DSHP + 4 * q) =
+                        make_float4(ydv[4 * q], ydv[4 * q + 1], ydv[4 * q + 2], ydv[4 * q + 3]);
+            });
         }
         wave_sync_lds();
     };
 
-    // gr / dr of the batch's edges from the parked Z sums (lane = edge).
+    // gr / dr of the batch's edges from the parked per-chunk Z sums (lane =
+    // edge of the batch, wave 0 only; chunks summed in order).
     auto epilogue = [&](int kb, int nb) {
-        wave_sync_lds();
-        if (want_vec && lane < nb) {
+        __syncthreads();
+        if (want_vec && wv == 0 && lane < nb) {
             const int e = perm[kb + lane];
             const float rx = vec[3 * e], ry = vec[3 * e + 1], rz = vec[3 * e + 2];
-            const float *zp = zlds + lane * DSH;
+            float z1[DSH], z2[V2 ? DSH : 1];
+            static_range<BLO, BHI>([&](auto b) {
+                z1[b] = 0.f;
+                if constexpr (V2)
+                    z2[b] = 0.f;
+            });
+            for (int c = 0; c < nch; ++c) {
+                const float *zp = zall + c * (NV * B * DSH) + lane * DSH;
+                static_range<BLO, BHI>([&](auto b) {
+                    z1[b] += zp[b];
+                    if constexpr (V2)
+                        z2[b] += zp[B * DSH + b];
+                });
+            }
             float g0 = 0.f, g1 = 0.f, g2 = 0.f;
             if constexpr (!V2) {
                 D3 Y[DSH];
                 sh_grad<L>(rx, ry, rz, Y);
                 static_range<BLO, BHI>([&](auto b) {
-                    const float z = zp[b];
-                    g0 = fmaf(z, Y[b].g0, g0);
-                    g1 = fmaf(z, Y[b].g1, g1);
-                    g2 = fmaf(z, Y[b].g2, g2);
+                    g0 = fmaf(z1[b], Y[b].g0, g0);
+                    g1 = fmaf(z1[b], Y[b].g1, g1);
+                    g2 = fmaf(z1[b], Y[b].g2, g2);
                 });
             } else {
                 float px = 0.f, py = 0.f, pz = 0.f;
@@ -159,12 +204,10 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                 }
                 Jet Y[DSH];
                 sh_jet<L>(rx, ry, rz, px, py, pz, Y);
-                const float *z2p = zlds + B * DSH + lane * DSH;
                 static_range<BLO, BHI>([&](auto b) {
-                    const float z1 = zp[b], z2 = z2p[b];
-                    g0 = fmaf(z1, Y[b].b0, fmaf(z2, Y[b].d0, g0));
-                    g1 = fmaf(z1, Y[b].b1, fmaf(z2, Y[b].d1, g1));
-                    g2 = fmaf(z1, Y[b].b2, fmaf(z2, Y[b].d2, g2));
+                    g0 = fmaf(z1[b], Y[b].b0, fmaf(z2[b], Y[b].d0, g0));
+                    g1 = fmaf(z1[b], Y[b].b1, fmaf(z2[b], Y[b].d1, g1));
+                    g2 = fmaf(z1[b], Y[b].b2, fmaf(z2[b], Y[b].d2, g2));
                 });
             }
             float *gp = ovec + 3 * static_cast<int64_t>(e);
@@ -177,24 +220,18 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
             gp[1] = g1;
             gp[2] = g2;
         }
-        wave_sync_lds();
+        __syncthreads();
     };
 
-    int kb = 0;
-    for (int k = k_begin; k < k_end; ++k) {
-        const int batch0 = k - kb;
-        const int nb = min(B, k_end - batch0);
-        if (kb == 0)
-            prologue(k, nb);
-        const int e = perm[k], i = perm_dst[k];
-        const float *wrow = w + static_cast<int64_t>(e) * (P * C) + u0;
-        const float *wprow = has_wp ? ggw + static_cast<int64_t>(e) * (P * C) + u0 : nullptr;
-        const float *grow = G + static_cast<int64_t>(i) * (DOUT * C) + u0;
-        float *owrow = ow ? ow + static_cast<int64_t>(e) * (P * C) + u0 : nullptr;
-        const float *yk = ylds + kb * DSHP;
-        const float *ydk = ylds + B * DSHP + kb * DSHP;
-
-        // broadcast SH (and Yd) of this edge
+    // One edge: per path, the K contraction of the gathered G rows, the node
+    // accumulators, the weight cotangent (stored) and the Z partial sums.
+    float Z[DSH], Z2[V2 ? DSH : 1];
+    static_range<0, DSH>([&](auto b) {
+        Z[b] = 0.f;
+        if constexpr (V2)
+            Z2[b] = 0.f;
+    });
+    auto compute = [&](const Ops &o, const float *yk, int e) {
         float Yb[DSHP], Ydb[V2 ? DSHP : 1];
         static_range<0, DSHP / 4>([&](auto q) {
             const float4 v = *reinterpret_cast<const float4 *>(yk + 4 * q);
@@ -203,144 +240,155 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
             Yb[4 * q + 2] = v.z;
             Yb[4 * q + 3] = v.w;
             if constexpr (V2) {
-                const float4 d = *reinterpret_cast<const float4 *>(ydk + 4 * q);
+                const float4 d = *reinterpret_cast<const float4 *>(yk + B * DSHP + 4 * q);
                 Ydb[4 * q] = d.x;
                 Ydb[4 * q + 1] = d.y;
                 Ydb[4 * q + 2] = d.z;
                 Ydb[4 * q + 3] = d.w;
             }
         });
-
-        V Z[DSH], Z2[V2 ? DSH : 1];
-        static_range<0, DSH>([&](auto b) {
-            if constexpr (!ab_touches_b(kTab<L>, GI.ab0, GI.ab1, b)) {
-                Z[b] = vzero<V>();
-                if constexpr (V2)
-                    Z2[b] = vzero<V>();
-            }
-        });
-
+        const rsrc_t rgw = make_rsrc(ow ? ow + static_cast<int64_t>(e) * (P * C) : nullptr, ow ? P * C * 4u : 0u);
         static_range<GI.p0, GI.p1>([&](auto p) {
             constexpr Path pa = kTab<L>.path[p];
-            constexpr int d1 = 2 * pa.l1 + 1, d3 = 2 * pa.l3 + 1;
-            constexpr int XO = pa.x_row - GI.xr0;
-            const V wp = active ? load_stream<V>(wrow + p * C) : vzero<V>();
-            V wpp = vzero<V>();
+            constexpr int d1 = 2 * pa.l1 + 1;
+            constexpr int XO = pa.x_row - GI.xr0, GO = pa.out_row - GI.gr0, WQ = p - GI.p0;
+            const float wp = o.w[WQ];
+            float wpp = 0.f;
             if constexpr (V2)
-                wpp = (has_wp && active) ? load_stream<V>(wprow + p * C) : vzero<V>();
-            V gv[d3];
-            static_range<0, d3>([&](auto m) {
-                gv[m] = active ? load_cached<V>(grow + (pa.out_row + m) * C) : vzero<V>();
-            });
-            V wx[d1], xx[V2 ? d1 : 1], s[d1], sd[V2 ? d1 : 1];
+                wpp = o.wp[WQ];
+            float wx[d1], xx[V2 ? d1 : 1], s[d1], sd[V2 ? d1 : 1];
             static_range<0, d1>([&](auto a) {
                 wx[a] = wp * xr[XO + a];
                 if constexpr (V2)
-                    xx[a] = vfma(wp, xpr[XO + a], wpp * xr[XO + a]);
+                    xx[a] = fmaf(wp, xpr[XO + a], wpp * xr[XO + a]);
             });
             static_range<kTab<L>.path_ab0[p], kTab<L>.path_ab0[p + 1]>([&](auto g) {
                 constexpr ABGroup ag = kTab<L>.ab[g];
                 constexpr int a = ag.m1 + pa.l1, b = pa.y_row + pa.l2 + ag.m2;
-                V K;
+                float K;
                 static_range<ag.t0, ag.t1>([&](auto ti) {
                     constexpr Entry en = kTab<L>.nz[kTab<L>.ab_entries[ti]];
                     if constexpr (ti == ag.t0)
-                        K = en.fval * gv[en.m3 + pa.l3];
+                        K = en.fval * o.g[GO + en.m3 + pa.l3];
                     else
-                        K = vfma(en.fval, gv[en.m3 + pa.l3], K);
+                        K = fmaf(en.fval, o.g[GO + en.m3 + pa.l3], K);
                 });
                 if constexpr (ab_first_m1(kTab<L>, g)) {
                     s[a] = Yb[b] * K;
                     if constexpr (V2)
                         sd[a] = Ydb[b] * K;
                 } else {
-                    s[a] = vfma(Yb[b], K, s[a]);
+                    s[a] = fmaf(Yb[b], K, s[a]);
                     if constexpr (V2)
-                        sd[a] = vfma(Ydb[b], K, sd[a]);
+                        sd[a] = fmaf(Ydb[b], K, sd[a]);
                 }
-                if constexpr (!V2) {
-                    if constexpr (ab_first_b(kTab<L>, GI.ab0, g))
-                        Z[b] = wx[a] * K;
-                    else
-                        Z[b] = vfma(wx[a], K, Z[b]);
-                } else {
-                    if constexpr (ab_first_b(kTab<L>, GI.ab0, g)) {
+                if constexpr (ab_first_b(kTab<L>, GI.ab0, g)) {
+                    if constexpr (V2) {
                         Z[b] = xx[a] * K;
                         Z2[b] = wx[a] * K;
                     } else {
-                        Z[b] = vfma(xx[a], K, Z[b]);
-                        Z2[b] = vfma(wx[a], K, Z2[b]);
+                        Z[b] = wx[a] * K;
+                    }
+                } else {
+                    if constexpr (V2) {
+                        Z[b] = fmaf(xx[a], K, Z[b]);
+                        Z2[b] = fmaf(wx[a], K, Z2[b]);
+                    } else {
+                        Z[b] = fmaf(wx[a], K, Z[b]);
                     }
                 }
             });
-            // node accumulators and the per-edge weight cotangent
-            V gwv;
+            float gwv;
             static_range<0, d1>([&](auto a) {
                 if constexpr (!V2) {
-                    acc[XO + a] = vfma(wp, s[a], acc[XO + a]);
+                    acc[XO + a] = fmaf(wp, s[a], acc[XO + a]);
                     if constexpr (a == 0)
                         gwv = xr[XO + a] * s[a];
                     else
-                        gwv = vfma(xr[XO + a], s[a], gwv);
+                        gwv = fmaf(xr[XO + a], s[a], gwv);
                 } else {
-                    acc[XO + a] = vfma(wpp, s[a], vfma(wp, sd[a], acc[XO + a]));
+                    acc[XO + a] = fmaf(wpp, s[a], fmaf(wp, sd[a], acc[XO + a]));
                     if constexpr (a == 0)
-                        gwv = vfma(xpr[XO + a], s[a], xr[XO + a] * sd[a]);
+                        gwv = fmaf(xpr[XO + a], s[a], xr[XO + a] * sd[a]);
                     else
-                        gwv = vfma(xpr[XO + a], s[a], vfma(xr[XO + a], sd[a], gwv));
+                        gwv = fmaf(xpr[XO + a], s[a], fmaf(xr[XO + a], sd[a], gwv));
                 }
             });
-            if (owrow && active)
-                __builtin_nontemporal_store(gwv, reinterpret_cast<V *>(owrow + p * C));
+            bstore<float, kNT>(gwv, rgw, off4, p * rowb);
         });
+    };
 
-        if (want_vec) {
-            // channel sums, then the fixed-order DPP wave sum; lane 63 parks them
-            float *zk = zlds + kb * DSH;
-            static_range<BLO, BHI>([&](auto b) {
-                float z;
-                if constexpr (CPL == 1)
-                    z = Z[b];
-                else
-                    z = Z[b].x + Z[b].y;
-                z = wave_sum_to_lane63(z);
+    // the batch's Z sums: fixed-order DPP wave sum, lane 63 parks them
+    auto park_z = [&](int kb) {
+        float *zk = zlds + kb * DSH;
+        static_range<BLO, BHI>([&](auto b) {
+            const float z = wave_sum_to_lane63(Z[b]);
+            if (lane == 63)
+                zk[b] = z;
+            if constexpr (V2) {
+                const float z2 = wave_sum_to_lane63(Z2[b]);
                 if (lane == 63)
-                    zk[b] = z;
-                if constexpr (V2) {
-                    float z2;
-                    if constexpr (CPL == 1)
-                        z2 = Z2[b];
-                    else
-                        z2 = Z2[b].x + Z2[b].y;
-                    z2 = wave_sum_to_lane63(z2);
-                    if (lane == 63)
-                        zk[B * DSH + b] = z2;
-                }
-            });
-        }
+                    zk[B * DSH + b] = z2;
+            }
+        });
+    };
 
-        ++kb;
-        if (kb == nb) {
-            epilogue(batch0, nb);
-            kb = 0;
+    Ops opA, opB;
+    int kb = 0;
+    if (kb0 < kb1)
+        load(kb0, opA);
+    for (int k = kb0; k < kb1; k += 2) {
+        // edge k uses opA, edge k + 1 uses opB
+        {
+            const int batch0 = k - kb, nb = min(B, kb1 - batch0);
+            if (kb == 0)
+                prologue(k, nb);
+            if (k + 1 < kb1)
+                load(k + 1, opB);
+            compute(opA, ylds + kb * DSHP, perm[k]);
+            if (want_vec)
+                park_z(kb);
+            if (++kb == nb) {
+                epilogue(batch0, nb);
+                kb = 0;
+            }
+        }
+        if (k + 1 >= kb1)
+            break;
+        {
+            const int batch0 = k + 1 - kb, nb = min(B, kb1 - batch0);
+            if (kb == 0)
+                prologue(k + 1, nb);
+            if (k + 2 < kb1)
+                load(k + 2, opA);
+            compute(opB, ylds + kb * DSHP, perm[k + 1]);
+            if (want_vec)
+                park_z(kb);
+            if (++kb == nb) {
+                epilogue(batch0, nb);
+                kb = 0;
+            }
         }
     }
 
-    // combine the S waves' node accumulators and store gx / dx rows of j
-    constexpr int LDS_FLOATS = S * WAVE_FLOATS;
-    reduce_waves<S, NXR, V, LDS_FLOATS>(acc, lds, lane, wv);
-    if (ox && wv == 0 && active) {
-        float *op = ox + static_cast<int64_t>(j) * (DIN * C) + u0 + GI.xr0 * C;
-        if (flags & 1u) {
-            static_range<0, NXR>([&](auto r) { store_v<V>(op + r * C, acc[r] + load_cached<V>(op + r * C)); });
-        } else {
-            static_range<0, NXR>([&](auto r) { store_v<V>(op + r * C, acc[r]); });
-        }
+    // node rows of j: stored, or added where the user asked to accumulate or
+    // an earlier path group already stored part of the same l1 rows
+    if (ox) {
+        const rsrc_t rox = make_rsrc(ox + static_cast<int64_t>(j) * (DIN * C), DIN * C * 4u);
+        constexpr int L1A = kTab<L>.path[GI.p0].l1;
+        constexpr int SHARED_ROWS = GI.shares_first_l1 ? 2 * L1A + 1 : 0;
+        const bool acc_all = flags & 1u;
+        static_range<0, NXR>([&](auto r) {
+            float v = acc[r];
+            if (acc_all || r < SHARED_ROWS)
+                v += bload<float>(rox, off4, (GI.xr0 + r) * rowb);
+            bstore<float>(v, rox, off4, (GI.xr0 + r) * rowb);
+        });
     }
 }
 
-template <int L, int CPL, typename XT, int MODE, int SG>
-__global__ void __launch_bounds__((64 * SrcCfg<L, CPL>::S))
+template <int L, typename XT, int MODE, int SG>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
     src_kernel(const int n_src, const int C, const int *__restrict__ src_ptr, const int *__restrict__ perm,
                const int *__restrict__ perm_dst, const float *__restrict__ vec, const XT *__restrict__ x,
                const float *__restrict__ w, const float *__restrict__ G, const float *__restrict__ ggx,
@@ -348,28 +396,28 @@ __global__ void __launch_bounds__((64 * SrcCfg<L, CPL>::S))
                float *__restrict__ ow, float *__restrict__ ovec, const uint32_t flags)
 {
     extern __shared__ float lds[];
-    src_group<L, CPL, XT, MODE, SG>(n_src, C, src_ptr, perm, perm_dst, vec, x, w, G, ggx, ggw, ggvec, ox, ow,
-                                    ovec, flags, lds);
+    src_group<L, XT, MODE, SG>(n_src, C, src_ptr, perm, perm_dst, vec, x, w, G, ggx, ggw, ggvec, ox, ow, ovec, flags,
+                               lds);
 }
 
-template <int L, int CPL, typename XT, int MODE>
+template <int L, typename XT, int MODE>
 static hipError_t launch_src_t(const ConvArgs &a)
 {
-    using Cfg = SrcCfg<L, CPL>;
-    constexpr Groups GR = make_src_groups(kTab<L>, Cfg::MAXCOST);
-    constexpr int DSH = kTab<L>.dsh, DSHP = (DSH + 3) & ~3;
-    constexpr int WAVE_FLOATS = (MODE == SRC_VJP2 ? 2 : 1) * Cfg::B * (DSHP + DSH);
-    constexpr size_t lds_bytes = sizeof(float) * Cfg::S * WAVE_FLOATS;
+    using Cfg = SrcCfg<L, MODE>;
+    constexpr Groups GR = make_src_groups(kTab<L>, Cfg::MAXCOST, Cfg::WMUL);
+    const int nch = (a.C + 63) / 64;
+    const size_t lds_bytes = sizeof(float) * src_lds_floats<L, MODE>(nch);
     if (a.n_src == 0)
         return hipSuccess;
     hipError_t err = hipSuccess;
-    // one launch per source group, in order: later groups add to gr / dr
+    // one launch per path group, in order: later groups add to gr / dr and to
+    // the node rows an earlier group started
     static_range<0, GR.n>([&](auto g) {
         if (err != hipSuccess)
             return;
-        hipLaunchKernelGGL((src_kernel<L, CPL, XT, MODE, g>), dim3(a.n_src), dim3(64 * Cfg::S), lds_bytes, a.stream,
-                           a.n_src, a.C, a.src_ptr, a.perm, a.perm_dst, a.vec, static_cast<const XT *>(a.x), a.w,
-                           a.G, a.ggx, a.ggw, a.ggvec, a.ox, a.ow, a.ovec, a.flags);
+        hipLaunchKernelGGL((src_kernel<L, XT, MODE, g>), dim3(a.n_src), dim3(64 * nch), lds_bytes, a.stream, a.n_src,
+                           a.C, a.src_ptr, a.perm, a.perm_dst, a.vec, static_cast<const XT *>(a.x), a.w, a.G, a.ggx,
+                           a.ggw, a.ggvec, a.ox, a.ow, a.ovec, a.flags);
         err = hipGetLastError();
     });
     return err;
@@ -382,7 +430,7 @@ static hipError_t launch_src_t(const ConvArgs &a)
 hipError_t ETP_RUN_NAME(src, ETP_L, ETP_XT, ETP_MODE)(const ConvArgs &a)
 {
     using XT = std::conditional_t<ETP_XT == 1, bf16raw, float>;
-    return a.C > 64 ? launch_src_t<ETP_L, 2, XT, ETP_MODE>(a) : launch_src_t<ETP_L, 1, XT, ETP_MODE>(a);
+    return launch_src_t<ETP_L, XT, ETP_MODE>(a);
 }
 
 }  // namespace etp

@@ -59,7 +59,7 @@
  *
  * Limits of this implementation: l_max_in = l_max_sh = l_max_out = L in
  * [0, 4]; all paths (paths == NULL or the full list); channels in [1, 1024],
- * even when above 64; the VJP and VJP-of-VJP need channels <= 128; the graph
+ * even when above 64; the VJP and VJP-of-VJP need channels <= 256; the graph
  * has fewer than 2^31 edges.
  */
 #ifndef ETP_H

@@ -77,6 +77,8 @@ SMALL = [
     (4, 128, "ragged"),
     # long destination segments (several T batches per wave) and long source segments
     (2, 128, "fan_in"), (2, 64, "fan_out"), (3, 128, "fan_in"), (4, 64, "fan_out"), (1, 8, "fan_out"),
+    # several channel chunks per node, the last one partly filled
+    (2, 200, "ragged"), (1, 256, "fan_out"),
 ]
 
 

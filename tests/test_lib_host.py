@@ -114,7 +114,7 @@ def test_call_validation_without_device():
     """Argument errors are reported before any HIP call."""
     INV, UNS, WS = etp.ETP_ERR_INVALID_ARGUMENT, etp.ETP_ERR_UNSUPPORTED, etp.ETP_ERR_WORKSPACE
     plan = etp.etp_plan_create(2, 128)
-    big = etp.etp_plan_create(2, 256)
+    big = etp.etp_plan_create(2, 258)
     g = etp.etp_graph(4, 4, 8, None, None, None, None, None)
     lib = etp.lib
     assert lib.etp_edge_conv_fwd(plan.handle, None, None, None, None, None, 0, None) == INV
