@@ -37,7 +37,7 @@ template <int L, int CPL, int MODE>
 struct DstCfg {
     static constexpr int S = 4;
     static constexpr int B = L <= 2 ? 32 : (L == 3 ? 16 : 8);
-    static constexpr int MAXROWS = (MODE == DST_FWD ? 56 : 40) / CPL;
+    static constexpr int MAXROWS = MODE == DST_FWD ? 56 / CPL : (L >= 4 ? 24 : 40 / CPL);
     static constexpr int TCOPIES = MODE == DST_FWD ? 1 : 2;  // T (and Td) per edge
 };
 
@@ -258,7 +258,13 @@ static hipError_t launch_dst_t(const ConvArgs &a)
 hipError_t ETP_RUN_NAME(dst, ETP_L, ETP_XT, ETP_MODE)(const ConvArgs &a)
 {
     using XT = std::conditional_t<ETP_XT == 1, bf16raw, float>;
-    return a.C > 64 ? launch_dst_t<ETP_L, 2, XT, ETP_MODE>(a) : launch_dst_t<ETP_L, 1, XT, ETP_MODE>(a);
+    // two channels per lane above 64 channels, except for the l_max = 4 dG
+    // pass whose doubled operands (w, W', x, X') need one channel per lane
+    constexpr bool ONE = ETP_MODE == DST_DG && ETP_L >= 4;
+    if constexpr (ONE)
+        return launch_dst_t<ETP_L, 1, XT, ETP_MODE>(a);
+    else
+        return a.C > 64 ? launch_dst_t<ETP_L, 2, XT, ETP_MODE>(a) : launch_dst_t<ETP_L, 1, XT, ETP_MODE>(a);
 }
 
 }  // namespace etp

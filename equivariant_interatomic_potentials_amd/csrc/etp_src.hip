@@ -39,7 +39,7 @@ template <int L, int MODE>
 struct SrcCfg {
     static constexpr int B = L <= 2 ? 64 : 32;
     static constexpr int WMUL = MODE == SRC_VJP2 ? 2 : 1;
-    static constexpr int MAXCOST = 60;
+    static constexpr int MAXCOST = L <= 2 ? 60 : (L == 3 ? 32 : 40);
 };
 
 template <int L, int MODE>
