@@ -182,6 +182,21 @@ class Workload:
         return rng(self.seed, "ggvec").standard_normal((self.E, 3), np.float32)
 
 
+def device_normal(shape, seed: int, name: str, chunk: int, scale: float = 1.0):
+    """N(0, scale^2) float32 tensor drawn on the GPU by torch's generator,
+    seeded from (seed, name, chunk): for arrays too large to draw on the
+    host (the diamond workload's per-edge weights, drawn per chunk of
+    destination rows). Same inputs for every caller with the same key."""
+    import torch
+    key = np.random.SeedSequence([seed, STREAMS.index(name), chunk]).generate_state(1, np.uint64)[0]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(int(key) & ((1 << 63) - 1))
+    t = torch.randn(*shape, generator=g, device="cuda", dtype=torch.float32)
+    if scale != 1.0:
+        t.mul_(scale)
+    return t
+
+
 def random_vectors(E: int, lo: float, hi: float, seed: int) -> np.ndarray:
     d = rng(seed, "dirs").standard_normal((E, 3))
     d /= np.linalg.norm(d, axis=1, keepdims=True)
