@@ -33,11 +33,27 @@
 
 namespace etp {
 
+// Launch shape of the destination pass: S waves per workgroup, B edges per
+// SH/T batch, MAXROWS output rows per path group (register accumulators =
+// MAXROWS x channels per lane). The ETP_DST_* macros override the defaults
+// for tuning builds.
+#ifndef ETP_DST_S
+#define ETP_DST_S 4
+#endif
+#ifndef ETP_DST_B2
+#define ETP_DST_B2 32
+#endif
+#ifndef ETP_DST_ROWS_FWD
+#define ETP_DST_ROWS_FWD 112
+#endif
+#ifndef ETP_DST_ROWS_DG
+#define ETP_DST_ROWS_DG 40
+#endif
 template <int L, int CPL, int MODE>
 struct DstCfg {
-    static constexpr int S = 4;
-    static constexpr int B = L <= 2 ? 32 : (L == 3 ? 16 : 8);
-    static constexpr int MAXROWS = MODE == DST_FWD ? 56 / CPL : (L >= 4 ? 24 : 40 / CPL);
+    static constexpr int S = ETP_DST_S;
+    static constexpr int B = L <= 2 ? ETP_DST_B2 : (L == 3 ? 16 : 8);
+    static constexpr int MAXROWS = MODE == DST_FWD ? ETP_DST_ROWS_FWD / CPL : (L >= 4 ? 24 : ETP_DST_ROWS_DG / CPL);
     static constexpr int TCOPIES = MODE == DST_FWD ? 1 : 2;  // T (and Td) per edge
 };
 
@@ -260,7 +276,10 @@ hipError_t ETP_RUN_NAME(dst, ETP_L, ETP_XT, ETP_MODE)(const ConvArgs &a)
     using XT = std::conditional_t<ETP_XT == 1, bf16raw, float>;
     // two channels per lane above 64 channels, except for the l_max = 4 dG
     // pass whose doubled operands (w, W', x, X') need one channel per lane
-    constexpr bool ONE = ETP_MODE == DST_DG && ETP_L >= 4;
+#ifndef ETP_DST_CPL1
+#define ETP_DST_CPL1 0
+#endif
+    constexpr bool ONE = (ETP_MODE == DST_DG && ETP_L >= 4) || ETP_DST_CPL1;
     if constexpr (ONE)
         return launch_dst_t<ETP_L, 1, XT, ETP_MODE>(a);
     else

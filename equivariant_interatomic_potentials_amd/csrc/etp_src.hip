@@ -15,10 +15,12 @@
 //         Z1_b = sum (w X' + W' x) K,  Z2_b = sum w x K,  Yd = grad Y . R'.
 //
 // Mapping (gfx950, wave64):
-//   * one workgroup per source node j with one wave per 64-channel chunk
-//     (one channel per lane); every wave walks all of j's out-edges (the
-//     stable transpose of the destination-sorted CSR), so the gx / dx rows
-//     of a chunk stay in one wave's registers and need no reduction;
+//   * one workgroup per source node j with one wave per (64-channel chunk,
+//     edge split): the splits divide j's out-edges (the stable transpose of
+//     the destination-sorted CSR) into contiguous parts; a wave's gx / dx
+//     rows stay in registers and the splits meet in a fixed-order LDS sum at
+//     the end; every wave runs the same number of SH batches so workgroup
+//     barriers stay aligned;
 //   * x[j] (and X'[j]) rows stay in registers; per edge the wave streams the
 //     w (and W') rows of its path group and gathers the group's G[i] rows
 //     with raw buffer loads (lanes past C read 0 and their stores are
@@ -35,19 +37,37 @@
 
 namespace etp {
 
+// Launch shape of the source pass: B edges per SH batch, MAXCOST bounds the
+// registers of one path group (see make_src_groups). The ETP_SRC_* macros
+// override the defaults for tuning builds.
+#ifndef ETP_SRC_B2
+#define ETP_SRC_B2 64
+#endif
+#ifndef ETP_SRC_COST2
+#define ETP_SRC_COST2 60
+#endif
+#ifndef ETP_SRC_WPE
+#define ETP_SRC_WPE 2
+#endif
 template <int L, int MODE>
 struct SrcCfg {
-    static constexpr int B = L <= 2 ? 64 : 32;
+    static constexpr int B = L <= 2 ? ETP_SRC_B2 : 32;
     static constexpr int WMUL = MODE == SRC_VJP2 ? 2 : 1;
-    static constexpr int MAXCOST = L <= 2 ? 60 : (L == 3 ? 32 : 40);
+    static constexpr int MAXCOST = L <= 2 ? ETP_SRC_COST2 : (L == 3 ? 32 : 40);
 };
+
+// Edge splits per channel chunk: four waves per workgroup in total.
+constexpr int src_splits(int nch) { return nch >= 4 ? 1 : 4 / nch; }
 
 template <int L, int MODE>
 constexpr int src_lds_floats(int nch)
 {
     constexpr int DSH = kTab<L>.dsh, DSHP = (DSH + 3) & ~3;
     constexpr int NV = MODE == SRC_VJP2 ? 2 : 1;
-    return nch * NV * SrcCfg<L, MODE>::B * (DSHP + DSH);
+    const int nw = nch * src_splits(nch);
+    const int batch = nw * NV * SrcCfg<L, MODE>::B * (DSHP + DSH);
+    const int reduce = (src_splits(nch) - 1) * nch * kTab<L>.din_rows * 64;  // node rows of the splits
+    return batch > reduce ? batch : reduce;
 }
 
 template <int L, typename XT, int MODE, int SG>
@@ -71,11 +91,13 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
     constexpr int DSHP = (DSH + 3) & ~3;
     constexpr int NV = V2 ? 2 : 1;  // SH copies (Y, Yd) and Z copies (Z1, Z2)
 
-    const int lane = threadIdx.x & 63, wv = wave_id(), nch = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63, wv = wave_id();
+    const int nch = (C + 63) >> 6, nsp = src_splits(nch);
+    const int ch = wv % nch, sp = wv / nch;  // channel chunk, edge split
     const int j = xcd_remap(blockIdx.x, gridDim.x);
     if (j >= n_src)
         return;
-    const int u = wv * 64 + lane;
+    const int u = ch * 64 + lane;
     const bool active = u < C;
     const uint32_t off4 = active ? static_cast<uint32_t>(u) * 4u : kOOB;
     const uint32_t offx = active ? static_cast<uint32_t>(u) * static_cast<uint32_t>(sizeof(XT)) : kOOB;
@@ -83,12 +105,17 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
     const bool has_xp = V2 && ggx != nullptr, has_wp = V2 && ggw != nullptr, has_rp = V2 && ggvec != nullptr;
     const uint32_t rowb = static_cast<uint32_t>(C) * 4u;  // bytes per f32 row
 
-    // LDS: per wave Y[B][DSHP] (+ Yd[B][DSHP]); then per chunk Z[B][DSH] (+ Z2[B][DSH])
+    // LDS: per wave Y[B][DSHP] (+ Yd[B][DSHP]); then per wave Z[B][DSH] (+ Z2[B][DSH])
+    const int nw = nch * nsp;
     float *ylds = lds + wv * (NV * B * DSHP);
-    float *zall = lds + nch * (NV * B * DSHP);
+    float *zall = lds + nw * (NV * B * DSHP);
     float *zlds = zall + wv * (NV * B * DSH);
 
-    const int kb0 = src_ptr[j], kb1 = src_ptr[j + 1];
+    // this wave's split of j's out-edges; every wave runs nbatch batches
+    const int len = src_ptr[j + 1] - src_ptr[j];
+    const int part = (len + nsp - 1) / nsp;
+    const int kb0 = src_ptr[j] + min(len, sp * part), kb1 = src_ptr[j] + min(len, (sp + 1) * part);
+    const int nbatch = (part + B - 1) / B;
 
     // node-resident rows of x[j] (and X'[j]) for this group's l1 values
     float xr[NXR], xpr[NXR], acc[NXR];
@@ -169,7 +196,7 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
     // edge of the batch, wave 0 only; chunks summed in order).
     auto epilogue = [&](int kb, int nb) {
         __syncthreads();
-        if (want_vec && wv == 0 && lane < nb) {
+        if (want_vec && ch == 0 && lane < nb) {
             const int e = perm[kb + lane];
             const float rx = vec[3 * e], ry = vec[3 * e + 1], rz = vec[3 * e + 2];
             float z1[DSH], z2[V2 ? DSH : 1];
@@ -179,7 +206,7 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                     z2[b] = 0.f;
             });
             for (int c = 0; c < nch; ++c) {
-                const float *zp = zall + c * (NV * B * DSH) + lane * DSH;
+                const float *zp = zall + (sp * nch + c) * (NV * B * DSH) + lane * DSH;
                 static_range<BLO, BHI>([&](auto b) {
                     z1[b] += zp[b];
                     if constexpr (V2)
@@ -334,7 +361,7 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
     };
 
     Ops opA, opB;
-    int kb = 0;
+    int kb = 0, done = 0;
     if (kb0 < kb1)
         load(kb0, opA);
     for (int k = kb0; k < kb1; k += 2) {
@@ -351,6 +378,7 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
             if (++kb == nb) {
                 epilogue(batch0, nb);
                 kb = 0;
+                ++done;
             }
         }
         if (k + 1 >= kb1)
@@ -367,13 +395,29 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
             if (++kb == nb) {
                 epilogue(batch0, nb);
                 kb = 0;
+                ++done;
             }
         }
     }
 
+    // splits with fewer edges still meet every batch barrier
+    for (; done < nbatch; ++done)
+        epilogue(kb1, 0);
+
+    // the splits' node accumulators meet in wave sp = 0 of each chunk, in order
+    if (nsp > 1) {
+        __syncthreads();
+        if (sp > 0)
+            static_range<0, NXR>([&](auto r) { lds[((sp - 1) * nch + ch) * (NXR * 64) + r * 64 + lane] = acc[r]; });
+        __syncthreads();
+        if (sp == 0)
+            for (int q = 1; q < nsp; ++q)
+                static_range<0, NXR>([&](auto r) { acc[r] += lds[((q - 1) * nch + ch) * (NXR * 64) + r * 64 + lane]; });
+    }
+
     // node rows of j: stored, or added where the user asked to accumulate or
     // an earlier path group already stored part of the same l1 rows
-    if (ox) {
+    if (ox && sp == 0) {
         const rsrc_t rox = make_rsrc(ox + static_cast<int64_t>(j) * (DIN * C), DIN * C * 4u);
         constexpr int L1A = kTab<L>.path[GI.p0].l1;
         constexpr int SHARED_ROWS = GI.shares_first_l1 ? 2 * L1A + 1 : 0;
@@ -388,7 +432,7 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
 }
 
 template <int L, typename XT, int MODE, int SG>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ETP_SRC_WPE)))
     src_kernel(const int n_src, const int C, const int *__restrict__ src_ptr, const int *__restrict__ perm,
                const int *__restrict__ perm_dst, const float *__restrict__ vec, const XT *__restrict__ x,
                const float *__restrict__ w, const float *__restrict__ G, const float *__restrict__ ggx,
@@ -415,8 +459,8 @@ static hipError_t launch_src_t(const ConvArgs &a)
     static_range<0, GR.n>([&](auto g) {
         if (err != hipSuccess)
             return;
-        hipLaunchKernelGGL((src_kernel<L, XT, MODE, g>), dim3(a.n_src), dim3(64 * nch), lds_bytes, a.stream, a.n_src,
-                           a.C, a.src_ptr, a.perm, a.perm_dst, a.vec, static_cast<const XT *>(a.x), a.w, a.G, a.ggx,
+        hipLaunchKernelGGL((src_kernel<L, XT, MODE, g>), dim3(a.n_src), dim3(64 * nch * src_splits(nch)), lds_bytes,
+                           a.stream, a.n_src, a.C, a.src_ptr, a.perm, a.perm_dst, a.vec, static_cast<const XT *>(a.x), a.w, a.G, a.ggx,
                            a.ggw, a.ggvec, a.ox, a.ow, a.ovec, a.flags);
         err = hipGetLastError();
     });
