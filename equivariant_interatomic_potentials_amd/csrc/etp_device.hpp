@@ -107,43 +107,48 @@ constexpr double dfact_odd(int m)  // (2m-1)!!
 // with Q_l^m the associated Legendre function stripped of (1-z^2)^(m/2) and
 // of the Condon-Shortley phase (Q_m^m = (2m-1)!!, Q_{m+1}^m = (2m+1) z Q_m^m,
 // (l-m) Q_l^m = (2l-1) z Q_{l-1}^m - (l+m-1) Q_{l-2}^m).
+// The components are produced one column m at a time, emit(b, value) with
+// b = l*l + l + m, so only one column of Q and one power of (x + iy) are live.
+template <int L, typename N, typename F>
+__device__ __forceinline__ void sh_unit_emit(const N &x, const N &y, const N &z, F &&emit)
+{
+    N cm = num_const(1.f, x), sm = num_const(0.f, x);  // Re, Im (x + iy)^m
+    static_range<0, L + 1>([&](auto m) {
+        if constexpr (m > 0) {
+            const N c2 = cm * x - sm * y;
+            sm = sm * x + cm * y;
+            cm = c2;
+        }
+        N q2 = num_const(0.f, x), q1 = num_const(0.f, x);  // Q_{l-2}^m, Q_{l-1}^m
+        static_range<m, L + 1>([&](auto l) {
+            N q;
+            if constexpr (l == m) {
+                q = num_const(static_cast<float>(dfact_odd(m)), x);
+            } else if constexpr (l == m + 1) {
+                q = static_cast<float>(2 * m + 1) * (z * q1);
+            } else {
+                constexpr float a = static_cast<float>((2.0 * l - 1.0) / (l - m));
+                constexpr float b = static_cast<float>((l + m - 1.0) / (l - m));
+                q = a * (z * q1) - b * q2;
+            }
+            constexpr double k0 = cx_sqrt((2.0 * l + 1.0) * cx_fact(l - m) / cx_fact(l + m));
+            if constexpr (m == 0) {
+                emit(static_cast<int>(l * l + l), static_cast<float>(k0) * q);
+            } else {
+                constexpr float k = static_cast<float>(k0 * 1.41421356237309504880);
+                emit(static_cast<int>(l * l + l + m), k * (q * cm));
+                emit(static_cast<int>(l * l + l - m), k * (q * sm));
+            }
+            q2 = q1;
+            q1 = q;
+        });
+    });
+}
+
 template <int L, typename N>
 __device__ __forceinline__ void sh_unit(const N &x, const N &y, const N &z, N *Y)
 {
-    N Cm[L + 1], Sm[L + 1];
-    Cm[0] = num_const(1.f, x);
-    Sm[0] = num_const(0.f, x);
-    static_range<0, L>([&](auto m) {
-        Cm[m + 1] = Cm[m] * x - Sm[m] * y;
-        Sm[m + 1] = Sm[m] * x + Cm[m] * y;
-    });
-    N Q[L + 1][L + 1];
-    static_range<0, L + 1>([&](auto m) {
-        Q[m][m] = num_const(static_cast<float>(dfact_odd(m)), x);
-        if constexpr (m + 1 <= L)
-            Q[m + 1][m] = static_cast<float>(2 * m + 1) * (z * Q[m][m]);
-        static_range<m + 2, L + 1>([&](auto l) {
-            constexpr float a = static_cast<float>((2.0 * l - 1.0) / (l - m));
-            constexpr float b = static_cast<float>((l + m - 1.0) / (l - m));
-            Q[l][m] = a * (z * Q[l - 1][m]) - b * Q[l - 2][m];
-        });
-    });
-    static_range<0, L + 1>([&](auto l) {
-        static_range<0, 2 * l + 1>([&](auto mi) {
-            constexpr int m = mi - l;
-            constexpr int am = m < 0 ? -m : m;
-            constexpr double k0 = cx_sqrt((2.0 * l + 1.0) * cx_fact(l - am) / cx_fact(l + am));
-            if constexpr (m == 0) {
-                Y[l * l + l] = static_cast<float>(k0) * Q[l][0];
-            } else if constexpr (m > 0) {
-                constexpr float k = static_cast<float>(k0 * 1.41421356237309504880);
-                Y[l * l + l + m] = k * (Q[l][am] * Cm[am]);
-            } else {
-                constexpr float k = static_cast<float>(k0 * 1.41421356237309504880);
-                Y[l * l + l + m] = k * (Q[l][am] * Sm[am]);
-            }
-        });
-    });
+    sh_unit_emit<L>(x, y, z, [&](int b, const N &v) { Y[b] = v; });
 }
 
 // Y at the bond vector r (any length > 0). A zero vector gives Y = (1, 0, ...).
@@ -159,23 +164,30 @@ __device__ __forceinline__ void sh_value(float rx, float ry, float rz, float *Y)
     }
 }
 
-// Y and dY/dr (gradient with respect to the unnormalised r).
-template <int L>
-__device__ __forceinline__ void sh_grad(float rx, float ry, float rz, D3 *Y)
+// Y and dY/dr (gradient with respect to the unnormalised r), emitted per
+// component as D3 numbers.
+template <int L, typename F>
+__device__ __forceinline__ void sh_grad_emit(float rx, float ry, float rz, F &&emit)
 {
     D3 X{rx, 1.f, 0.f, 0.f}, Yv{ry, 0.f, 1.f, 0.f}, Z{rz, 0.f, 0.f, 1.f};
     D3 r2 = X * X + Yv * Yv + Z * Z;
     if (r2.v > 0.f) {
         D3 inv = num_rsqrt(r2);
-        sh_unit<L>(X * inv, Yv * inv, Z * inv, Y);
+        sh_unit_emit<L>(X * inv, Yv * inv, Z * inv, emit);
     } else {
-        static_range<0, (L + 1) * (L + 1)>([&](auto b) { Y[b] = d3_const(b == 0 ? 1.f : 0.f); });
+        static_range<0, (L + 1) * (L + 1)>([&](auto b) { emit(static_cast<int>(b), d3_const(b == 0 ? 1.f : 0.f)); });
     }
 }
-
-// Y, grad Y, Ydot = grad Y . rho and H rho = grad(grad Y . rho).
 template <int L>
-__device__ __forceinline__ void sh_jet(float rx, float ry, float rz, float px, float py, float pz, Jet *Y)
+__device__ __forceinline__ void sh_grad(float rx, float ry, float rz, D3 *Y)
+{
+    sh_grad_emit<L>(rx, ry, rz, [&](int b, const D3 &v) { Y[b] = v; });
+}
+
+// Y, grad Y, Ydot = grad Y . rho and H rho = grad(grad Y . rho), emitted per
+// component as Jet numbers.
+template <int L, typename F>
+__device__ __forceinline__ void sh_jet_emit(float rx, float ry, float rz, float px, float py, float pz, F &&emit)
 {
     Jet X{rx, 1.f, 0.f, 0.f, px, 0.f, 0.f, 0.f};
     Jet Yv{ry, 0.f, 1.f, 0.f, py, 0.f, 0.f, 0.f};
@@ -183,10 +195,15 @@ __device__ __forceinline__ void sh_jet(float rx, float ry, float rz, float px, f
     Jet r2 = X * X + Yv * Yv + Z * Z;
     if (r2.a > 0.f) {
         Jet inv = num_rsqrt(r2);
-        sh_unit<L>(X * inv, Yv * inv, Z * inv, Y);
+        sh_unit_emit<L>(X * inv, Yv * inv, Z * inv, emit);
     } else {
-        static_range<0, (L + 1) * (L + 1)>([&](auto b) { Y[b] = jet_const(b == 0 ? 1.f : 0.f); });
+        static_range<0, (L + 1) * (L + 1)>([&](auto b) { emit(static_cast<int>(b), jet_const(b == 0 ? 1.f : 0.f)); });
     }
+}
+template <int L>
+__device__ __forceinline__ void sh_jet(float rx, float ry, float rz, float px, float py, float pz, Jet *Y)
+{
+    sh_jet_emit<L>(rx, ry, rz, px, py, pz, [&](int b, const Jet &v) { Y[b] = v; });
 }
 
 // ------------------------------------------------------ wave-level helpers
@@ -221,6 +238,11 @@ __device__ __forceinline__ void wave_sync_lds()
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+
+// Ends the wait for the load that produced v here: an empty asm that reads
+// and writes v. A value loaded before a loop and read inside it otherwise
+// keeps a loop-carried wait whose count also drains the loop's prefetches.
+__device__ __forceinline__ void settle(float &v) { asm volatile("" : "+v"(v)); }
 
 // Blocks are dispatched to the 8 XCDs round robin; this bijection gives each
 // XCD a contiguous range of logical block indices (so neighbouring nodes of

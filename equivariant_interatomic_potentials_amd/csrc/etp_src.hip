@@ -37,23 +37,44 @@
 
 namespace etp {
 
-// Launch shape of the source pass: B edges per SH batch, MAXCOST bounds the
-// registers of one path group (see make_src_groups). The ETP_SRC_* macros
-// override the defaults for tuning builds.
-#ifndef ETP_SRC_B2
-#define ETP_SRC_B2 64
+// Launch shape of the source pass. Per edge a wave keeps in LDS the SH
+// values (and for the VJP-of-VJP the directional derivative Yd) and the
+// coefficients that turn the Z sums into gr / dr (3 or 6 per SH component);
+// B edges per SH batch is the largest power of two up to 64 whose batch fits
+// in 8 KiB, so four waves per SIMD fit the CU's LDS. MAXCOST bounds the
+// registers of one path group (see make_src_groups) and WPE is the waves per
+// SIMD the register allocation must allow: four where the group fits in 128
+// VGPRs, fewer where the batch's SH (second-order jets at high l_max) need
+// more. The ETP_SRC_* macros override the defaults for tuning builds.
+#ifndef ETP_SRC_COST_VJP
+#define ETP_SRC_COST_VJP 60
 #endif
-#ifndef ETP_SRC_COST2
-#define ETP_SRC_COST2 60
+#ifndef ETP_SRC_COST_VJP2
+#define ETP_SRC_COST_VJP2 40
 #endif
 #ifndef ETP_SRC_WPE
-#define ETP_SRC_WPE 2
+#define ETP_SRC_WPE 0
+#endif
+#ifndef ETP_SRC_LDS_BATCH
+#define ETP_SRC_LDS_BATCH 8192
 #endif
 template <int L, int MODE>
 struct SrcCfg {
-    static constexpr int B = L <= 2 ? ETP_SRC_B2 : 32;
+    static constexpr int NV = MODE == SRC_VJP2 ? 2 : 1;             // Y (, Yd) and Z (, Z2) copies
+    static constexpr int DSH = (L + 1) * (L + 1), DSHP = (DSH + 3) & ~3;
+    static constexpr int GQ = 4 * NV * DSH;                         // gr coefficients, a float4 per (b, copy)
+    static constexpr int ES = NV * DSHP + GQ;                       // floats per edge in the batch
+    static constexpr int ESP = ES + 8;                              // + two park slots (3, padded)
+    static constexpr int B = [] {
+        int b = 64;
+        while (b > 8 && b * ESP * 4 > ETP_SRC_LDS_BATCH)
+            b >>= 1;
+        return b;
+    }();
     static constexpr int WMUL = MODE == SRC_VJP2 ? 2 : 1;
-    static constexpr int MAXCOST = L <= 2 ? ETP_SRC_COST2 : (L == 3 ? 32 : 40);
+    static constexpr int MAXCOST =
+        L <= 2 ? (MODE == SRC_VJP2 ? ETP_SRC_COST_VJP2 : ETP_SRC_COST_VJP) : (L == 3 ? 32 : 40);
+    static constexpr int WPE = ETP_SRC_WPE > 0 ? ETP_SRC_WPE : (MODE == SRC_VJP2 && L == 4 ? 3 : 4);
 };
 
 // Edge splits per channel chunk: four waves per workgroup in total.
@@ -62,10 +83,10 @@ constexpr int src_splits(int nch) { return nch >= 4 ? 1 : 4 / nch; }
 template <int L, int MODE>
 constexpr int src_lds_floats(int nch)
 {
-    constexpr int DSH = kTab<L>.dsh, DSHP = (DSH + 3) & ~3;
-    constexpr int NV = MODE == SRC_VJP2 ? 2 : 1;
+    using Cfg = SrcCfg<L, MODE>;
     const int nw = nch * src_splits(nch);
-    const int batch = nw * NV * SrcCfg<L, MODE>::B * (DSHP + DSH);
+    // per wave: the batch (B x ES) and two alternating park slots (B x 4)
+    const int batch = nw * Cfg::B * (Cfg::ES + 8);
     const int reduce = (src_splits(nch) - 1) * nch * kTab<L>.din_rows * 64;  // node rows of the splits
     return batch > reduce ? batch : reduce;
 }
@@ -81,15 +102,13 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                                           const uint32_t flags, float *lds)
 {
     using Cfg = SrcCfg<L, MODE>;
-    constexpr int B = Cfg::B;
+    constexpr int B = Cfg::B, ES = Cfg::ES, NV = Cfg::NV, DSHP = Cfg::DSHP;
     constexpr bool V2 = MODE == SRC_VJP2;
     constexpr Groups GR = make_src_groups(kTab<L>, Cfg::MAXCOST, Cfg::WMUL);
     constexpr SrcGroupInfo GI = src_group_info(kTab<L>, GR, SG);
     constexpr int P = kTab<L>.P, DIN = kTab<L>.din_rows, DOUT = kTab<L>.dout_rows, DSH = kTab<L>.dsh;
     constexpr int NP = GI.np, NXR = GI.nxr, NGR = GI.ngr;
     constexpr int BLO = sh_lo(kTab<L>, GI.p0, GI.p1), BHI = sh_hi(kTab<L>, GI.p0, GI.p1);
-    constexpr int DSHP = (DSH + 3) & ~3;
-    constexpr int NV = V2 ? 2 : 1;  // SH copies (Y, Yd) and Z copies (Z1, Z2)
 
     const int lane = threadIdx.x & 63, wv = wave_id();
     const int nch = (C + 63) >> 6, nsp = src_splits(nch);
@@ -103,13 +122,13 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
     const uint32_t offx = active ? static_cast<uint32_t>(u) * static_cast<uint32_t>(sizeof(XT)) : kOOB;
     const bool want_vec = ovec != nullptr;
     const bool has_xp = V2 && ggx != nullptr, has_wp = V2 && ggw != nullptr, has_rp = V2 && ggvec != nullptr;
-    const uint32_t rowb = static_cast<uint32_t>(C) * 4u;  // bytes per f32 row
+    const uint32_t rowb = static_cast<uint32_t>(C) * 4u;
 
-    // LDS: per wave Y[B][DSHP] (+ Yd[B][DSHP]); then per wave Z[B][DSH] (+ Z2[B][DSH])
+    // LDS: per wave the batch [B][ES] and two park slots [2][B][4]
     const int nw = nch * nsp;
-    float *ylds = lds + wv * (NV * B * DSHP);
-    float *zall = lds + nw * (NV * B * DSHP);
-    float *zlds = zall + wv * (NV * B * DSH);
+    float *blds = lds + wv * (B * ES);
+    float *pall = lds + nw * (B * ES);
+    float *plds = pall + wv * (2 * B * 4);
 
     // this wave's split of j's out-edges; every wave runs nbatch batches
     const int len = src_ptr[j + 1] - src_ptr[j];
@@ -130,114 +149,88 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
         });
     }
 
+    // Operands of one edge, per path of the group: the w (and W') row and
+    // the path's own G[i] rows. Rows of different paths are disjoint, so a
+    // path's registers are reloaded with the next edge's rows as soon as the
+    // path is done: one edge of look-ahead without a second register set.
     struct Ops {
         float w[NP], wp[V2 ? NP : 1], g[NGR];
     };
-    auto load = [&](int k, Ops &o) {
+    struct EdgeRsrc {
+        rsrc_t w, wp, g;
+    };
+    auto edge_rsrc = [&](int k, bool valid) {
         const int e = perm[k], i = perm_dst[k];
-        const rsrc_t rw = make_rsrc(w + static_cast<int64_t>(e) * (P * C), P * C * 4u);
-        const rsrc_t rg = make_rsrc(G + static_cast<int64_t>(i) * (DOUT * C), DOUT * C * 4u);
-        static_range<0, NP>([&](auto q) { o.w[q] = bload<float, kNT>(rw, off4, (GI.p0 + q) * rowb); });
-        static_range<0, NGR>([&](auto r) { o.g[r] = bload<float>(rg, off4, (GI.gr0 + r) * rowb); });
-        if constexpr (V2) {
-            const rsrc_t rwp = make_rsrc(has_wp ? ggw + static_cast<int64_t>(e) * (P * C) : nullptr,
-                                         has_wp ? P * C * 4u : 0u);
-            static_range<0, NP>([&](auto q) { o.wp[q] = bload<float, kNT>(rwp, off4, (GI.p0 + q) * rowb); });
-        }
+        EdgeRsrc r;
+        r.w = make_rsrc(w + static_cast<int64_t>(e) * (P * C), valid ? P * C * 4u : 0u);
+        r.g = make_rsrc(G + static_cast<int64_t>(i) * (DOUT * C), valid ? DOUT * C * 4u : 0u);
+        r.wp = make_rsrc(has_wp ? ggw + static_cast<int64_t>(e) * (P * C) : nullptr,
+                         has_wp && valid ? P * C * 4u : 0u);
+        return r;
+    };
+    Ops o;
+    auto load_path = [&](auto p, const EdgeRsrc &r) {
+        constexpr Path pa = kTab<L>.path[p];
+        constexpr int GO = pa.out_row - GI.gr0, WQ = p - GI.p0;
+        o.w[WQ] = bload<float, kNT>(r.w, off4, p * rowb);
+        if constexpr (V2)
+            o.wp[WQ] = bload<float, kNT>(r.wp, off4, p * rowb);
+        static_range<0, 2 * pa.l3 + 1>([&](auto m) { o.g[GO + m] = bload<float>(r.g, off4, (pa.out_row + m) * rowb); });
     };
 
+    // Per batch, lane = edge: Y (, Yd) and the coefficients of the gr / dr
+    // contraction, dY_b/dr (VJP) or the two Hessian-vector terms (VJP2).
     auto prologue = [&](int kb, int nb) {
         wave_sync_lds();
         if (lane < nb) {
             const int e = perm[kb + lane];
             const float rx = vec[3 * e], ry = vec[3 * e + 1], rz = vec[3 * e + 2];
-            float *yp = ylds + lane * DSHP;
-            float yv[DSHP], ydv[DSHP];
+            float *ep = blds + lane * ES;
+            float4 *cp = reinterpret_cast<float4 *>(ep + NV * DSHP);
+            // padding of the SH rows (the edge loop reads them as float4)
+            static_range<DSH, DSHP>([&](auto b) {
+                ep[b] = 0.f;
+                if constexpr (V2)
+                    ep[DSHP + b] = 0.f;
+            });
             if constexpr (!V2) {
-                float Y[DSH];
-                sh_value<L>(rx, ry, rz, Y);
-                static_range<0, DSHP>([&](auto b) {
-                    if constexpr (b < DSH)
-                        yv[b] = Y[b];
-                    else
-                        yv[b] = 0.f;
+                sh_grad_emit<L>(rx, ry, rz, [&](int b, const D3 &y) {
+                    ep[b] = y.v;
+                    cp[b] = make_float4(y.g0, y.g1, y.g2, 0.f);
                 });
             } else {
-                D3 Y[DSH];
-                sh_grad<L>(rx, ry, rz, Y);
                 float px = 0.f, py = 0.f, pz = 0.f;
                 if (has_rp) {
                     px = ggvec[3 * e];
                     py = ggvec[3 * e + 1];
                     pz = ggvec[3 * e + 2];
                 }
-                static_range<0, DSHP>([&](auto b) {
-                    if constexpr (b < DSH) {
-                        yv[b] = Y[b].v;
-                        ydv[b] = Y[b].g0 * px + Y[b].g1 * py + Y[b].g2 * pz;
-                    } else {
-                        yv[b] = 0.f;
-                        ydv[b] = 0.f;
-                    }
+                sh_jet_emit<L>(rx, ry, rz, px, py, pz, [&](int b, const Jet &y) {
+                    ep[b] = y.a;
+                    ep[DSHP + b] = y.c;
+                    cp[2 * b] = make_float4(y.b0, y.b1, y.b2, 0.f);
+                    cp[2 * b + 1] = make_float4(y.d0, y.d1, y.d2, 0.f);
                 });
             }
-            static_range<0, DSHP / 4>([&](auto q) {
-                *reinterpret_cast<float4 *>(yp + 4 * q) =
-                    make_float4(yv[4 * q], yv[4 * q + 1], yv[4 * q + 2], yv[4 * q + 3]);
-                if constexpr (V2)
-                    *reinterpret_cast<float4 *>(yp + B * DSHP + 4 * q) =
-                        make_float4(ydv[4 * q], ydv[4 * q + 1], ydv[4 * q + 2], ydv[4 * q + 3]);
-            });
         }
         wave_sync_lds();
     };
 
-    // gr / dr of the batch's edges from the parked per-chunk Z sums (lane =
-    // edge of the batch, wave 0 only; chunks summed in order).
-    auto epilogue = [&](int kb, int nb) {
+    // gr / dr of a finished batch from the parked per-chunk partial sums
+    // (several chunks only): lane = edge of the batch, chunk 0's wave of the
+    // split adds the chunks in order. The park slots alternate by batch, so
+    // one barrier per batch keeps writers and the reader apart.
+    auto epilogue = [&](int kb, int nb, int slot) {
         __syncthreads();
         if (want_vec && ch == 0 && lane < nb) {
-            const int e = perm[kb + lane];
-            const float rx = vec[3 * e], ry = vec[3 * e + 1], rz = vec[3 * e + 2];
-            float z1[DSH], z2[V2 ? DSH : 1];
-            static_range<BLO, BHI>([&](auto b) {
-                z1[b] = 0.f;
-                if constexpr (V2)
-                    z2[b] = 0.f;
-            });
-            for (int c = 0; c < nch; ++c) {
-                const float *zp = zall + (sp * nch + c) * (NV * B * DSH) + lane * DSH;
-                static_range<BLO, BHI>([&](auto b) {
-                    z1[b] += zp[b];
-                    if constexpr (V2)
-                        z2[b] += zp[B * DSH + b];
-                });
-            }
             float g0 = 0.f, g1 = 0.f, g2 = 0.f;
-            if constexpr (!V2) {
-                D3 Y[DSH];
-                sh_grad<L>(rx, ry, rz, Y);
-                static_range<BLO, BHI>([&](auto b) {
-                    g0 = fmaf(z1[b], Y[b].g0, g0);
-                    g1 = fmaf(z1[b], Y[b].g1, g1);
-                    g2 = fmaf(z1[b], Y[b].g2, g2);
-                });
-            } else {
-                float px = 0.f, py = 0.f, pz = 0.f;
-                if (has_rp) {
-                    px = ggvec[3 * e];
-                    py = ggvec[3 * e + 1];
-                    pz = ggvec[3 * e + 2];
-                }
-                Jet Y[DSH];
-                sh_jet<L>(rx, ry, rz, px, py, pz, Y);
-                static_range<BLO, BHI>([&](auto b) {
-                    g0 = fmaf(z1[b], Y[b].b0, fmaf(z2[b], Y[b].d0, g0));
-                    g1 = fmaf(z1[b], Y[b].b1, fmaf(z2[b], Y[b].d1, g1));
-                    g2 = fmaf(z1[b], Y[b].b2, fmaf(z2[b], Y[b].d2, g2));
-                });
+            for (int c = 0; c < nch; ++c) {
+                const float *pp = pall + (sp * nch + c) * (2 * B * 4) + (slot * B + lane) * 4;
+                g0 += pp[0];
+                g1 += pp[1];
+                g2 += pp[2];
             }
-            float *gp = ovec + 3 * static_cast<int64_t>(e);
+            float *gp = ovec + 3 * static_cast<int64_t>(perm[kb + lane]);
             if (SG > 0) {  // later source groups add to the earlier groups' result
                 g0 += gp[0];
                 g1 += gp[1];
@@ -247,27 +240,27 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
             gp[1] = g1;
             gp[2] = g2;
         }
-        __syncthreads();
     };
 
-    // One edge: per path, the K contraction of the gathered G rows, the node
-    // accumulators, the weight cotangent (stored) and the Z partial sums.
+    // One edge, path by path: the K contraction of the gathered G rows, the
+    // node accumulators, the weight cotangent (stored) and the Z partial
+    // sums; then the path's registers take the next edge's rows.
     float Z[DSH], Z2[V2 ? DSH : 1];
     static_range<0, DSH>([&](auto b) {
         Z[b] = 0.f;
         if constexpr (V2)
             Z2[b] = 0.f;
     });
-    auto compute = [&](const Ops &o, const float *yk, int e) {
+    auto compute = [&](const float *ep, int e, const EdgeRsrc &nx) {
         float Yb[DSHP], Ydb[V2 ? DSHP : 1];
         static_range<0, DSHP / 4>([&](auto q) {
-            const float4 v = *reinterpret_cast<const float4 *>(yk + 4 * q);
+            const float4 v = *reinterpret_cast<const float4 *>(ep + 4 * q);
             Yb[4 * q] = v.x;
             Yb[4 * q + 1] = v.y;
             Yb[4 * q + 2] = v.z;
             Yb[4 * q + 3] = v.w;
             if constexpr (V2) {
-                const float4 d = *reinterpret_cast<const float4 *>(yk + B * DSHP + 4 * q);
+                const float4 d = *reinterpret_cast<const float4 *>(ep + DSHP + 4 * q);
                 Ydb[4 * q] = d.x;
                 Ydb[4 * q + 1] = d.y;
                 Ydb[4 * q + 2] = d.z;
@@ -276,6 +269,9 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
         });
         const rsrc_t rgw = make_rsrc(ow ? ow + static_cast<int64_t>(e) * (P * C) : nullptr, ow ? P * C * 4u : 0u);
         static_range<GI.p0, GI.p1>([&](auto p) {
+#ifdef ETP_SRC_SCHED_FENCE
+            __builtin_amdgcn_sched_barrier(0);
+#endif
             constexpr Path pa = kTab<L>.path[p];
             constexpr int d1 = 2 * pa.l1 + 1;
             constexpr int XO = pa.x_row - GI.xr0, GO = pa.out_row - GI.gr0, WQ = p - GI.p0;
@@ -325,6 +321,7 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                     }
                 }
             });
+            load_path(p, nx);
             float gwv;
             static_range<0, d1>([&](auto a) {
                 if constexpr (!V2) {
@@ -345,64 +342,88 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
         });
     };
 
-    // the batch's Z sums: fixed-order DPP wave sum, lane 63 parks them
-    auto park_z = [&](int kb) {
-        float *zk = zlds + kb * DSH;
+    // The edge's gr / dr partial over this wave's channels: Z contracted
+    // with the edge's coefficients per lane, then a fixed-order DPP sum of
+    // the three components (the sum is exact in lane 63).
+    auto fold = [&](const float *ep, float &g0, float &g1, float &g2) {
+        const float4 *cp = reinterpret_cast<const float4 *>(ep + NV * DSHP);
+        g0 = 0.f;
+        g1 = 0.f;
+        g2 = 0.f;
         static_range<BLO, BHI>([&](auto b) {
-            const float z = wave_sum_to_lane63(Z[b]);
-            if (lane == 63)
-                zk[b] = z;
+            const float4 c = cp[NV * b];
+            g0 = fmaf(Z[b], c.x, g0);
+            g1 = fmaf(Z[b], c.y, g1);
+            g2 = fmaf(Z[b], c.z, g2);
             if constexpr (V2) {
-                const float z2 = wave_sum_to_lane63(Z2[b]);
-                if (lane == 63)
-                    zk[B * DSH + b] = z2;
+                const float4 d = cp[2 * b + 1];
+                g0 = fmaf(Z2[b], d.x, g0);
+                g1 = fmaf(Z2[b], d.y, g1);
+                g2 = fmaf(Z2[b], d.z, g2);
             }
         });
+        g0 = wave_sum_to_lane63(g0);
+        g1 = wave_sum_to_lane63(g1);
+        g2 = wave_sum_to_lane63(g2);
     };
 
-    Ops opA, opB;
     int kb = 0, done = 0;
-    if (kb0 < kb1)
-        load(kb0, opA);
-    for (int k = kb0; k < kb1; k += 2) {
-        // edge k uses opA, edge k + 1 uses opB
-        {
-            const int batch0 = k - kb, nb = min(B, kb1 - batch0);
-            if (kb == 0)
-                prologue(k, nb);
-            if (k + 1 < kb1)
-                load(k + 1, opB);
-            compute(opA, ylds + kb * DSHP, perm[k]);
-            if (want_vec)
-                park_z(kb);
-            if (++kb == nb) {
-                epilogue(batch0, nb);
-                kb = 0;
-                ++done;
+    static_range<0, NXR>([&](auto q) {
+        settle(xr[q]);
+        if constexpr (V2)
+            settle(xpr[q]);
+    });
+    for (int k = kb0; k < kb1; ++k) {
+        const int batch0 = k - kb, nb = min(B, kb1 - batch0);
+        if (kb == 0) {
+            // the look-ahead stops at batch ends, so no operand registers
+            // are live while the batch's SH are evaluated
+            prologue(k, nb);
+            const EdgeRsrc r0 = edge_rsrc(k, true);
+            static_range<GI.p0, GI.p1>([&](auto p) { load_path(p, r0); });
+        }
+        const bool more = kb + 1 < nb;
+        const EdgeRsrc nx = edge_rsrc(more ? k + 1 : k, more);
+        const int e = perm[k];
+        const float *ep = blds + kb * ES;
+        compute(ep, e, nx);
+        // the fold runs whether or not gr / dr is wanted: guarding it lets the
+        // compiler sink the Z sums into the branch and keep every K alive
+        float g0, g1, g2;
+        fold(ep, g0, g1, g2);
+        if (want_vec) {
+            if (nch == 1) {
+                // one chunk: lane 63 holds the edge's whole sum
+                if (lane == 63) {
+                    float *gp = ovec + 3 * static_cast<int64_t>(e);
+                    if (SG > 0) {
+                        g0 += gp[0];
+                        g1 += gp[1];
+                        g2 += gp[2];
+                    }
+                    gp[0] = g0;
+                    gp[1] = g1;
+                    gp[2] = g2;
+                }
+            } else if (lane == 63) {
+                float *pp = plds + ((done & 1) * B + kb) * 4;
+                pp[0] = g0;
+                pp[1] = g1;
+                pp[2] = g2;
             }
         }
-        if (k + 1 >= kb1)
-            break;
-        {
-            const int batch0 = k + 1 - kb, nb = min(B, kb1 - batch0);
-            if (kb == 0)
-                prologue(k + 1, nb);
-            if (k + 2 < kb1)
-                load(k + 2, opA);
-            compute(opB, ylds + kb * DSHP, perm[k + 1]);
-            if (want_vec)
-                park_z(kb);
-            if (++kb == nb) {
-                epilogue(batch0, nb);
-                kb = 0;
-                ++done;
-            }
+        if (++kb == nb) {
+            if (nch > 1)
+                epilogue(batch0, nb, done & 1);
+            kb = 0;
+            ++done;
         }
     }
 
     // splits with fewer edges still meet every batch barrier
-    for (; done < nbatch; ++done)
-        epilogue(kb1, 0);
+    if (nch > 1)
+        for (; done < nbatch; ++done)
+            epilogue(kb1, 0, done & 1);
 
     // the splits' node accumulators meet in wave sp = 0 of each chunk, in order
     if (nsp > 1) {
@@ -432,7 +453,7 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
 }
 
 template <int L, typename XT, int MODE, int SG>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ETP_SRC_WPE)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SrcCfg<L, MODE>::WPE)))
     src_kernel(const int n_src, const int C, const int *__restrict__ src_ptr, const int *__restrict__ perm,
                const int *__restrict__ perm_dst, const float *__restrict__ vec, const XT *__restrict__ x,
                const float *__restrict__ w, const float *__restrict__ G, const float *__restrict__ ggx,
