@@ -21,7 +21,7 @@ template <int B, int E, typename F>
 __host__ __device__ __forceinline__ void static_range(F &&f)
 {
     if constexpr (B < E) {
-        [&]<int... I>(std::integer_sequence<int, I...>) {
+        [&]<int... I>(std::integer_sequence<int, I...>) __attribute__((always_inline)) {
             (f(ic<B + I>{}), ...);
         }(std::make_integer_sequence<int, E - B>{});
     }
@@ -108,7 +108,8 @@ constexpr double dfact_odd(int m)  // (2m-1)!!
 // of the Condon-Shortley phase (Q_m^m = (2m-1)!!, Q_{m+1}^m = (2m+1) z Q_m^m,
 // (l-m) Q_l^m = (2l-1) z Q_{l-1}^m - (l+m-1) Q_{l-2}^m).
 // The components are produced one column m at a time, emit(b, value) with
-// b = l*l + l + m, so only one column of Q and one power of (x + iy) are live.
+// b = l*l + l + m (a std::integral_constant), so only one column of Q and one
+// power of (x + iy) are live.
 template <int L, typename N, typename F>
 __device__ __forceinline__ void sh_unit_emit(const N &x, const N &y, const N &z, F &&emit)
 {
@@ -133,11 +134,11 @@ __device__ __forceinline__ void sh_unit_emit(const N &x, const N &y, const N &z,
             }
             constexpr double k0 = cx_sqrt((2.0 * l + 1.0) * cx_fact(l - m) / cx_fact(l + m));
             if constexpr (m == 0) {
-                emit(static_cast<int>(l * l + l), static_cast<float>(k0) * q);
+                emit(std::integral_constant<int, l * l + l>{}, static_cast<float>(k0) * q);
             } else {
                 constexpr float k = static_cast<float>(k0 * 1.41421356237309504880);
-                emit(static_cast<int>(l * l + l + m), k * (q * cm));
-                emit(static_cast<int>(l * l + l - m), k * (q * sm));
+                emit(std::integral_constant<int, l * l + l + m>{}, k * (q * cm));
+                emit(std::integral_constant<int, l * l + l - m>{}, k * (q * sm));
             }
             q2 = q1;
             q1 = q;
@@ -148,7 +149,7 @@ __device__ __forceinline__ void sh_unit_emit(const N &x, const N &y, const N &z,
 template <int L, typename N>
 __device__ __forceinline__ void sh_unit(const N &x, const N &y, const N &z, N *Y)
 {
-    sh_unit_emit<L>(x, y, z, [&](int b, const N &v) { Y[b] = v; });
+    sh_unit_emit<L>(x, y, z, [&](auto b, const N &v) { Y[b] = v; });
 }
 
 // Y at the bond vector r (any length > 0). A zero vector gives Y = (1, 0, ...).
@@ -175,13 +176,13 @@ __device__ __forceinline__ void sh_grad_emit(float rx, float ry, float rz, F &&e
         D3 inv = num_rsqrt(r2);
         sh_unit_emit<L>(X * inv, Yv * inv, Z * inv, emit);
     } else {
-        static_range<0, (L + 1) * (L + 1)>([&](auto b) { emit(static_cast<int>(b), d3_const(b == 0 ? 1.f : 0.f)); });
+        static_range<0, (L + 1) * (L + 1)>([&](auto b) { emit(b, d3_const(b == 0 ? 1.f : 0.f)); });
     }
 }
 template <int L>
 __device__ __forceinline__ void sh_grad(float rx, float ry, float rz, D3 *Y)
 {
-    sh_grad_emit<L>(rx, ry, rz, [&](int b, const D3 &v) { Y[b] = v; });
+    sh_grad_emit<L>(rx, ry, rz, [&](auto b, const D3 &v) { Y[b] = v; });
 }
 
 // Y, grad Y, Ydot = grad Y . rho and H rho = grad(grad Y . rho), emitted per
@@ -197,13 +198,13 @@ __device__ __forceinline__ void sh_jet_emit(float rx, float ry, float rz, float 
         Jet inv = num_rsqrt(r2);
         sh_unit_emit<L>(X * inv, Yv * inv, Z * inv, emit);
     } else {
-        static_range<0, (L + 1) * (L + 1)>([&](auto b) { emit(static_cast<int>(b), jet_const(b == 0 ? 1.f : 0.f)); });
+        static_range<0, (L + 1) * (L + 1)>([&](auto b) { emit(b, jet_const(b == 0 ? 1.f : 0.f)); });
     }
 }
 template <int L>
 __device__ __forceinline__ void sh_jet(float rx, float ry, float rz, float px, float py, float pz, Jet *Y)
 {
-    sh_jet_emit<L>(rx, ry, rz, px, py, pz, [&](int b, const Jet &v) { Y[b] = v; });
+    sh_jet_emit<L>(rx, ry, rz, px, py, pz, [&](auto b, const Jet &v) { Y[b] = v; });
 }
 
 // ------------------------------------------------------ wave-level helpers

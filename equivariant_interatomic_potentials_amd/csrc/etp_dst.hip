@@ -49,11 +49,25 @@ namespace etp {
 #ifndef ETP_DST_ROWS_DG
 #define ETP_DST_ROWS_DG 40
 #endif
+#ifndef ETP_DST_ROWS_FWD3
+#define ETP_DST_ROWS_FWD3 ETP_DST_ROWS_FWD
+#endif
+#ifndef ETP_DST_ROWS_FWD4
+#define ETP_DST_ROWS_FWD4 ETP_DST_ROWS_FWD
+#endif
+#ifndef ETP_DST_ROWS_DG3
+#define ETP_DST_ROWS_DG3 ETP_DST_ROWS_DG
+#endif
+#ifndef ETP_DST_ROWS_DG4
+#define ETP_DST_ROWS_DG4 24
+#endif
 template <int L, int CPL, int MODE>
 struct DstCfg {
     static constexpr int S = ETP_DST_S;
     static constexpr int B = L <= 2 ? ETP_DST_B2 : (L == 3 ? 16 : 8);
-    static constexpr int MAXROWS = MODE == DST_FWD ? ETP_DST_ROWS_FWD / CPL : (L >= 4 ? 24 : ETP_DST_ROWS_DG / CPL);
+    static constexpr int ROWS = MODE == DST_FWD ? (L <= 2 ? ETP_DST_ROWS_FWD : L == 3 ? ETP_DST_ROWS_FWD3 : ETP_DST_ROWS_FWD4)
+                                                : (L <= 2 ? ETP_DST_ROWS_DG : L == 3 ? ETP_DST_ROWS_DG3 : ETP_DST_ROWS_DG4);
+    static constexpr int MAXROWS = (ROWS + CPL - 1) / CPL;
     static constexpr int TCOPIES = MODE == DST_FWD ? 1 : 2;  // T (and Td) per edge
 };
 
@@ -131,8 +145,6 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
                 sh_value<L>(rx, ry, rz, Y);
                 write_T<L, GI.pr0, GI.npr, STRIDE>(Y, tl + lane * STRIDE);
             } else {
-                D3 Yg[DSH];
-                sh_grad<L>(rx, ry, rz, Yg);
                 float px = 0.f, py = 0.f, pz = 0.f;
                 if (has_rp) {
                     px = ggvec[3 * e];
@@ -140,9 +152,9 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
                     pz = ggvec[3 * e + 2];
                 }
                 float Y[DSH], Yd[DSH];
-                static_range<0, DSH>([&](auto b) {
-                    Y[b] = Yg[b].v;
-                    Yd[b] = Yg[b].g0 * px + Yg[b].g1 * py + Yg[b].g2 * pz;
+                sh_grad_emit<L>(rx, ry, rz, [&](auto b, const D3 &y) {
+                    Y[b] = y.v;
+                    Yd[b] = y.g0 * px + y.g1 * py + y.g2 * pz;
                 });
                 write_T<L, GI.pr0, GI.npr, STRIDE>(Y, tl + lane * STRIDE);
                 write_T<L, GI.pr0, GI.npr, STRIDE>(Yd, tl + B * STRIDE + lane * STRIDE);
@@ -193,27 +205,35 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
         });
     };
 
+    // Edges in batches of B: the batch's SH / T are evaluated first, then
+    // its edges run with one edge of look-ahead (opA / opB alternate). The
+    // look-ahead stops at the batch end, so no operand registers are live
+    // while the next batch's SH are evaluated.
     Ops opA, opB;
-    int e = e_begin, kb = 0;
-    if (e < e_end)
-        load(e, opA);
+    int e = e_begin, kb = 0, nb = 0;
     while (e < e_end) {
-        if (kb == 0)
-            prologue(e, min(B, e_end - e));
-        if (e + 1 < e_end)
+        if (kb == 0) {
+            nb = min(B, e_end - e);
+            prologue(e, nb);
+            load(e, opA);
+        }
+        if (kb + 1 < nb)
             load(e + 1, opB);
         compute(opA, tl + kb * STRIDE);
         ++e;
-        kb = (kb + 1 == B) ? 0 : kb + 1;
+        kb = (kb + 1 == nb) ? 0 : kb + 1;
         if (e >= e_end)
             break;
-        if (kb == 0)
-            prologue(e, min(B, e_end - e));
-        if (e + 1 < e_end)
+        if (kb == 0) {
+            nb = min(B, e_end - e);
+            prologue(e, nb);
+            load(e, opB);
+        }
+        if (kb + 1 < nb)
             load(e + 1, opA);
         compute(opB, tl + kb * STRIDE);
         ++e;
-        kb = (kb + 1 == B) ? 0 : kb + 1;
+        kb = (kb + 1 == nb) ? 0 : kb + 1;
     }
 
     reduce_waves<S, NROW, V, LDS_FLOATS>(acc, lds, lane, wv);
@@ -241,7 +261,7 @@ __global__ void __launch_bounds__((64 * DstCfg<L, CPL, MODE>::S))
     extern __shared__ float lds[];
     constexpr Groups GR = make_groups(kTab<L>, DstCfg<L, CPL, MODE>::MAXROWS);
     const int g = blockIdx.y;
-    static_range<0, GR.n>([&](auto G) {
+    static_range<0, GR.n>([&](auto G) __attribute__((always_inline)) {
         if (g == G)
             dst_group<L, CPL, XT, MODE, G>(n_dst, C, nchunk, row_ptr, src, vec, x, w, ggx, ggw, ggvec, out, flags,
                                            lds);

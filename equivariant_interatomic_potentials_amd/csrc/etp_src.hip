@@ -194,7 +194,7 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                     ep[DSHP + b] = 0.f;
             });
             if constexpr (!V2) {
-                sh_grad_emit<L>(rx, ry, rz, [&](int b, const D3 &y) {
+                sh_grad_emit<L>(rx, ry, rz, [&](auto b, const D3 &y) {
                     ep[b] = y.v;
                     cp[b] = make_float4(y.g0, y.g1, y.g2, 0.f);
                 });
@@ -205,7 +205,7 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                     py = ggvec[3 * e + 1];
                     pz = ggvec[3 * e + 2];
                 }
-                sh_jet_emit<L>(rx, ry, rz, px, py, pz, [&](int b, const Jet &y) {
+                sh_jet_emit<L>(rx, ry, rz, px, py, pz, [&](auto b, const Jet &y) {
                     ep[b] = y.a;
                     ep[DSHP + b] = y.c;
                     cp[2 * b] = make_float4(y.b0, y.b1, y.b2, 0.f);
