@@ -16,11 +16,12 @@
 //
 // Mapping (gfx950, wave64):
 //   * one workgroup per source node j with one wave per (64-channel chunk,
-//     edge split): the splits divide j's out-edges (the stable transpose of
-//     the destination-sorted CSR) into contiguous parts; a wave's gx / dx
-//     rows stay in registers and the splits meet in a fixed-order LDS sum at
-//     the end; every wave runs the same number of SH batches so workgroup
-//     barriers stay aligned;
+//     edge split): split s of n takes every n-th of j's out-edges from the
+//     s-th on (the out-edges come from the stable transpose of the
+//     destination-sorted CSR, so all splits walk the same window of
+//     destination rows); a wave's gx / dx rows stay in registers and the
+//     splits meet in a fixed-order LDS sum at the end; every wave runs the
+//     same number of SH batches so workgroup barriers stay aligned;
 //   * x[j] (and X'[j]) rows stay in registers; per edge the wave streams the
 //     w (and W') rows of its path group and gathers the group's G[i] rows
 //     with raw buffer loads (lanes past C read 0 and their stores are
@@ -130,11 +131,13 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
     float *pall = lds + nw * (B * ES);
     float *plds = pall + wv * (2 * B * 4);
 
-    // this wave's split of j's out-edges; every wave runs nbatch batches
-    const int len = src_ptr[j + 1] - src_ptr[j];
-    const int part = (len + nsp - 1) / nsp;
-    const int kb0 = src_ptr[j] + min(len, sp * part), kb1 = src_ptr[j] + min(len, (sp + 1) * part);
-    const int nbatch = (part + B - 1) / B;
+    // this wave's split of j's out-edges: every nsp-th edge from sp on, so
+    // that the splits walk the same (destination-ordered) window of G rows;
+    // every wave runs nbatch batches
+    const int kbase = src_ptr[j] + sp, len = src_ptr[j + 1] - src_ptr[j];
+    const int cnt = len > sp ? (len - sp + nsp - 1) / nsp : 0;
+    const int nbatch = ((len + nsp - 1) / nsp + B - 1) / B;
+    auto kpos = [&](int i) { return kbase + i * nsp; };  // position of the split's i-th edge
 
     // node-resident rows of x[j] (and X'[j]) for this group's l1 values
     float xr[NXR], xpr[NXR], acc[NXR];
@@ -180,10 +183,10 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
 
     // Per batch, lane = edge: Y (, Yd) and the coefficients of the gr / dr
     // contraction, dY_b/dr (VJP) or the two Hessian-vector terms (VJP2).
-    auto prologue = [&](int kb, int nb) {
+    auto prologue = [&](int i0, int nb) {
         wave_sync_lds();
         if (lane < nb) {
-            const int e = perm[kb + lane];
+            const int e = perm[kpos(i0 + lane)];
             const float rx = vec[3 * e], ry = vec[3 * e + 1], rz = vec[3 * e + 2];
             float *ep = blds + lane * ES;
             float4 *cp = reinterpret_cast<float4 *>(ep + NV * DSHP);
@@ -220,7 +223,7 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
     // (several chunks only): lane = edge of the batch, chunk 0's wave of the
     // split adds the chunks in order. The park slots alternate by batch, so
     // one barrier per batch keeps writers and the reader apart.
-    auto epilogue = [&](int kb, int nb, int slot) {
+    auto epilogue = [&](int i0, int nb, int slot) {
         __syncthreads();
         if (want_vec && ch == 0 && lane < nb) {
             float g0 = 0.f, g1 = 0.f, g2 = 0.f;
@@ -230,7 +233,7 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                 g1 += pp[1];
                 g2 += pp[2];
             }
-            float *gp = ovec + 3 * static_cast<int64_t>(perm[kb + lane]);
+            float *gp = ovec + 3 * static_cast<int64_t>(perm[kpos(i0 + lane)]);
             if (SG > 0) {  // later source groups add to the earlier groups' result
                 g0 += gp[0];
                 g1 += gp[1];
@@ -373,17 +376,17 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
         if constexpr (V2)
             settle(xpr[q]);
     });
-    for (int k = kb0; k < kb1; ++k) {
-        const int batch0 = k - kb, nb = min(B, kb1 - batch0);
+    for (int i = 0; i < cnt; ++i) {
+        const int batch0 = i - kb, nb = min(B, cnt - batch0), k = kpos(i);
         if (kb == 0) {
             // the look-ahead stops at batch ends, so no operand registers
             // are live while the batch's SH are evaluated
-            prologue(k, nb);
+            prologue(i, nb);
             const EdgeRsrc r0 = edge_rsrc(k, true);
             static_range<GI.p0, GI.p1>([&](auto p) { load_path(p, r0); });
         }
         const bool more = kb + 1 < nb;
-        const EdgeRsrc nx = edge_rsrc(more ? k + 1 : k, more);
+        const EdgeRsrc nx = edge_rsrc(more ? k + nsp : k, more);
         const int e = perm[k];
         const float *ep = blds + kb * ES;
         compute(ep, e, nx);
@@ -423,7 +426,7 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
     // splits with fewer edges still meet every batch barrier
     if (nch > 1)
         for (; done < nbatch; ++done)
-            epilogue(kb1, 0, done & 1);
+            epilogue(cnt, 0, done & 1);
 
     // the splits' node accumulators meet in wave sp = 0 of each chunk, in order
     if (nsp > 1) {
