@@ -77,8 +77,9 @@ SMALL = [
     (4, 128, "ragged"),
     # long destination segments (several T batches per wave) and long source segments
     (2, 128, "fan_in"), (2, 64, "fan_out"), (3, 128, "fan_in"), (4, 64, "fan_out"), (1, 8, "fan_out"),
-    # several channel chunks per node, the last one partly filled
-    (2, 200, "ragged"), (1, 256, "fan_out"),
+    # several channel chunks per node, the last one partly filled; one channel;
+    # the widest source pass (256 channels)
+    (2, 200, "ragged"), (1, 256, "fan_out"), (2, 1, "ragged"), (4, 1, "ragged"), (3, 256, "ragged"),
 ]
 
 
@@ -121,6 +122,33 @@ def test_vjp2_small(L, C, kind):
     r = oracle.vjp2(L, wl.row_ptr, wl.src, wl.vec, wl.x, wl.w, wl.G, wl.ggx, wl.ggw, wl.ggvec)
     for name, got, ref in zip(("dx", "dw", "dr", "dG"), (dx, dw, dr, dG), r):
         assert rel_err(got, ref) < FP32_TOL, (name, rel_err(got, ref))
+
+
+@pytest.mark.parametrize("L,C", [(1, 512), (2, 1024), (2, 300)])
+def test_fwd_wide_channels(L, C):
+    """The forward takes up to 1024 channels (several 128-channel chunks)."""
+    say("fwd-wide", L, C)
+    wl = workloads.small(L, C, 11, 6, seed=C + L)
+    p = DeviceProblem(wl)
+    out = np_(p.fwd())
+    ref = oracle.fwd(L, wl.row_ptr, wl.src, wl.vec, wl.x, wl.w)
+    assert rel_err(out, ref) < FP32_TOL, rel_err(out, ref)
+
+
+def test_empty_graph_zeroes_node_outputs():
+    """No edges at all: every node output is overwritten with zeros."""
+    import torch
+    say("empty-graph")
+    wl = workloads.small(2, 64, 7, 0, seed=5)
+    assert wl.E == 0
+    p = DeviceProblem(wl)
+    out = torch.full((wl.n_dst, wl.Dout, wl.C), 7.0, device="cuda")
+    p.fwd(out=out)
+    assert float(out.abs().max()) == 0.0
+    gx, gw, gr = p.vjp()
+    assert float(gx.abs().max()) == 0.0 and gw.numel() == 0 and gr.numel() == 0
+    dx, dw, dr, dG = p.vjp2()
+    assert float(dx.abs().max()) == 0.0 and float(dG.abs().max()) == 0.0
 
 
 @pytest.mark.parametrize("cot", [("ggx",), ("ggw",), ("ggvec",), ("ggx", "ggw"), ()])
