@@ -166,7 +166,8 @@ class Plan:
         self.dout_rows = info["dout_rows"]
 
     def __del__(self):
-        if getattr(self, "handle", None):
+        # at interpreter exit the module's globals may already be gone
+        if getattr(self, "handle", None) and lib is not None:
             lib.etp_plan_destroy(self.handle)
             self.handle = None
 
