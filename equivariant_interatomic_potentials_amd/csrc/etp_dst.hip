@@ -27,8 +27,9 @@
 //     fixed-order register sum and the S waves meet in a fixed-order LDS
 //     tree, so results are deterministic without atomics;
 //   * w / W' are streamed with non-temporal loads, x / X' rows gathered
-//     cached; the forward issues the next edge's loads before the current
-//     edge's FMAs.
+//     cached; each path's w row (and each l1 block's x rows) is reloaded
+//     with the next edge's as soon as its last use in the current edge is
+//     done, one edge of look-ahead in one register set.
 #include "etp_conv_common.hpp"
 
 namespace etp {
@@ -61,6 +62,9 @@ namespace etp {
 #ifndef ETP_DST_ROWS_DG4
 #define ETP_DST_ROWS_DG4 24
 #endif
+#ifndef ETP_DST_WPE
+#define ETP_DST_WPE 0
+#endif
 template <int L, int CPL, int MODE>
 struct DstCfg {
     static constexpr int S = ETP_DST_S;
@@ -69,6 +73,8 @@ struct DstCfg {
                                                 : (L <= 2 ? ETP_DST_ROWS_DG : L == 3 ? ETP_DST_ROWS_DG3 : ETP_DST_ROWS_DG4);
     static constexpr int MAXROWS = (ROWS + CPL - 1) / CPL;
     static constexpr int TCOPIES = MODE == DST_FWD ? 1 : 2;  // T (and Td) per edge
+    // waves per SIMD the registers must allow: 3 at l=3 (169 VGPRs otherwise)
+    static constexpr int WPE = ETP_DST_WPE > 0 ? ETP_DST_WPE : (L == 3 ? 3 : 1);
 };
 
 template <int L, int CPL, typename XT, int MODE, int G>
@@ -112,26 +118,41 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
     V acc[NROW];
     static_range<0, NROW>([&](auto r) { acc[r] = vzero<V>(); });
 
-    // per-edge operands: w (and W') rows of the group's paths, x (and X')
-    // rows of the group's l1 values
+    // Per-edge operands: w (and W') rows of the group's paths, x (and X')
+    // rows of the group's l1 values. One register set: a path's w row is
+    // reloaded with the next edge's as soon as the path is done, an l1
+    // block's x rows as soon as the last path with that l1 is done (paths
+    // are in l1-major order), which gives one edge of look-ahead.
     struct Ops {
         V w[NP], x[NXR], wp[DG ? NP : 1], xp[DG ? NXR : 1];
     };
-    auto load = [&](int e, Ops &o) {
+    struct EdgeRsrc {
+        rsrc_t w, x, wp, xp;
+    };
+    auto edge_rsrc = [&](int e, bool valid) {
         const int j = src[e];
-        const rsrc_t rw = make_rsrc(w + static_cast<int64_t>(e) * (P * C), P * C * 4u);
-        const rsrc_t rx = make_rsrc(x + static_cast<int64_t>(j) * (DIN * C), DIN * C * sizeof(XT));
-        static_range<0, NP>([&](auto q) { o.w[q] = bload<V, kNT>(rw, off4, (GI.p0 + q) * rowb); });
-        static_range<0, NXR>([&](auto q) { o.x[q] = bload_x<V, XT>(rx, offx, (GI.xr0 + q) * rowx); });
-        if constexpr (DG) {
-            // a missing cotangent is a zero-length block: its loads read 0
-            const rsrc_t rwp = make_rsrc(has_wp ? ggw + static_cast<int64_t>(e) * (P * C) : nullptr,
-                                         has_wp ? P * C * 4u : 0u);
-            const rsrc_t rxp = make_rsrc(has_xp ? ggx + static_cast<int64_t>(j) * (DIN * C) : nullptr,
-                                         has_xp ? DIN * C * 4u : 0u);
-            static_range<0, NP>([&](auto q) { o.wp[q] = bload<V, kNT>(rwp, off4, (GI.p0 + q) * rowb); });
-            static_range<0, NXR>([&](auto q) { o.xp[q] = bload<V>(rxp, off4, (GI.xr0 + q) * rowb); });
-        }
+        EdgeRsrc r;
+        r.w = make_rsrc(w + static_cast<int64_t>(e) * (P * C), valid ? P * C * 4u : 0u);
+        r.x = make_rsrc(x + static_cast<int64_t>(j) * (DIN * C), valid ? DIN * C * static_cast<uint32_t>(sizeof(XT)) : 0u);
+        // a missing cotangent is a zero-length block: its loads read 0
+        r.wp = make_rsrc(has_wp ? ggw + static_cast<int64_t>(e) * (P * C) : nullptr, has_wp && valid ? P * C * 4u : 0u);
+        r.xp = make_rsrc(has_xp ? ggx + static_cast<int64_t>(j) * (DIN * C) : nullptr, has_xp && valid ? DIN * C * 4u : 0u);
+        return r;
+    };
+    Ops o;
+    auto load_w = [&](auto q, const EdgeRsrc &r) {  // q: path index within the group
+        o.w[q] = bload<V, kNT>(r.w, off4, (GI.p0 + q) * rowb);
+        if constexpr (DG)
+            o.wp[q] = bload<V, kNT>(r.wp, off4, (GI.p0 + q) * rowb);
+    };
+    auto load_x = [&](auto q, const EdgeRsrc &r) {  // q: x row within the group
+        o.x[q] = bload_x<V, XT>(r.x, offx, (GI.xr0 + q) * rowx);
+        if constexpr (DG)
+            o.xp[q] = bload<V>(r.xp, off4, (GI.xr0 + q) * rowb);
+    };
+    auto load_all = [&](const EdgeRsrc &r) {
+        static_range<0, NP>([&](auto q) { load_w(q, r); });
+        static_range<0, NXR>([&](auto q) { load_x(q, r); });
     };
 
     // SH (and Yd) and the T (and Td) coefficients of edges [eb, eb + nb)
@@ -167,7 +188,7 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
     // inputs pre-scaled by w, or y[m3] += T x[m1] followed by
     // acc[p, m3] += w y[m3], whichever form needs fewer multiplies.
     // dG: acc[p, m3] += T (w X' + W' x)[m1] + Td (w x)[m1].
-    auto compute = [&](const Ops &o, const float *tk) {
+    auto compute = [&](const float *tk, const EdgeRsrc &nx) {
         float4 tq = make_float4(0.f, 0.f, 0.f, 0.f), tdq = tq;
         V xw[9], y[9], xx[DG ? 9 : 1];
         static_range<GI.pr0, GI.pr1>([&](auto q) {
@@ -202,37 +223,29 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
             }
             if constexpr (!XW && q == pa.pr1 - 1)
                 static_range<0, d3>([&](auto m) { acc[OO + m] = vfma(o.w[WQ], y[m], acc[OO + m]); });
+            if constexpr (q == pa.pr1 - 1) {
+                // the path is done: its w row, and the x rows of its l1 when no
+                // later path of the group uses them, take the next edge's
+                load_w(ic<WQ>{}, nx);
+                if constexpr (pr.path + 1 == GI.p1 || kTab<L>.path[pr.path + 1].l1 != pa.l1)
+                    static_range<0, d1>([&](auto k) { load_x(ic<XO + k>{}, nx); });
+            }
         });
     };
 
     // Edges in batches of B: the batch's SH / T are evaluated first, then
-    // its edges run with one edge of look-ahead (opA / opB alternate). The
-    // look-ahead stops at the batch end, so no operand registers are live
-    // while the next batch's SH are evaluated.
-    Ops opA, opB;
-    int e = e_begin, kb = 0, nb = 0;
-    while (e < e_end) {
+    // its edges run with one edge of look-ahead. The look-ahead stops at the
+    // batch end, so no operand registers are live while the next batch's SH
+    // are evaluated.
+    int kb = 0, nb = 0;
+    for (int e = e_begin; e < e_end; ++e) {
         if (kb == 0) {
             nb = min(B, e_end - e);
             prologue(e, nb);
-            load(e, opA);
+            load_all(edge_rsrc(e, true));
         }
-        if (kb + 1 < nb)
-            load(e + 1, opB);
-        compute(opA, tl + kb * STRIDE);
-        ++e;
-        kb = (kb + 1 == nb) ? 0 : kb + 1;
-        if (e >= e_end)
-            break;
-        if (kb == 0) {
-            nb = min(B, e_end - e);
-            prologue(e, nb);
-            load(e, opB);
-        }
-        if (kb + 1 < nb)
-            load(e + 1, opA);
-        compute(opB, tl + kb * STRIDE);
-        ++e;
+        const bool more = kb + 1 < nb;
+        compute(tl + kb * STRIDE, edge_rsrc(more ? e + 1 : e, more));
         kb = (kb + 1 == nb) ? 0 : kb + 1;
     }
 
@@ -252,7 +265,7 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
 }
 
 template <int L, int CPL, typename XT, int MODE>
-__global__ void __launch_bounds__((64 * DstCfg<L, CPL, MODE>::S))
+__global__ void __launch_bounds__((64 * DstCfg<L, CPL, MODE>::S)) __attribute__((amdgpu_waves_per_eu(DstCfg<L, CPL, MODE>::WPE)))
     dst_kernel(const int n_dst, const int C, const int nchunk, const int *__restrict__ row_ptr,
                const int *__restrict__ src, const float *__restrict__ vec, const XT *__restrict__ x,
                const float *__restrict__ w, const float *__restrict__ ggx, const float *__restrict__ ggw,
