@@ -54,7 +54,7 @@ namespace etp {
 #define ETP_DST_ROWS_FWD3 ETP_DST_ROWS_FWD
 #endif
 #ifndef ETP_DST_ROWS_FWD4
-#define ETP_DST_ROWS_FWD4 ETP_DST_ROWS_FWD
+#define ETP_DST_ROWS_FWD4 80
 #endif
 #ifndef ETP_DST_ROWS_DG3
 #define ETP_DST_ROWS_DG3 ETP_DST_ROWS_DG

@@ -97,8 +97,8 @@ constexpr bool first_m1_in_path(const Table &T, int q)
 
 // Source-side passes: contiguous path groups sized so that one edge's
 // streamed operands (wmul weight rows per path + the G rows of the group's
-// paths), double buffered, plus the resident x rows fit the VGPR budget:
-// cost = wmul * paths + G rows + 2 * x rows <= max_cost. A group may start
+// paths) plus the resident x rows and their accumulators fit the VGPR
+// budget: cost = wmul * paths + G rows + 2 * x rows <= max_cost. A group may start
 // inside an l1 block; the node rows of that l1 are then added to the rows
 // the previous group stored.
 struct SrcGroupInfo {
