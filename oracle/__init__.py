@@ -74,6 +74,8 @@ def _load():
         lib.oracle_vjp.argtypes = [ctypes.c_int] * 6 + [_i32p, _i32p] + [_f64p] * 7
         lib.oracle_vjp2.restype = ctypes.c_int
         lib.oracle_vjp2.argtypes = [ctypes.c_int] * 6 + [_i32p, _i32p] + [_f64p] * 11
+        lib.oracle_channel_mix.restype = ctypes.c_int
+        lib.oracle_channel_mix.argtypes = [ctypes.c_int] * 5 + [_f64p] * 3
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -204,6 +206,30 @@ def fwd(L, row_ptr, src, vec, x, w):
     if rc:
         raise ValueError("oracle_fwd failed")
     return out
+
+
+def mix_rows(L) -> list:
+    """Number of paths per output order l3 = 0..l_max_out: W_l has n_l * C rows."""
+    lout = _lmax(L)[2]
+    p = paths(L)
+    return [int((p[:, 2] == l).sum()) for l in range(lout + 1)]
+
+
+def channel_mix(L, out, W):
+    """y[n, (l_max_out+1)^2, C] from the convolution output out[n, Dout, C] and
+    W = W_0, W_1, ... back to back (W_l: [n_l * C, C] row-major)."""
+    lin, lsh, lout = _lmax(L)
+    out = _f64(out)
+    n, _, C = out.shape
+    W = _f64(W).reshape(-1)
+    need = sum(mix_rows(L)) * C * C
+    if W.size != need:
+        raise ValueError(f"W has {W.size} values, expected {need}")
+    y = np.zeros((n, (lout + 1) ** 2, C))
+    if _load().oracle_channel_mix(lin, lsh, lout, C, n, _p(_nz(out.reshape(-1)), _f64p), _p(W, _f64p),
+                                  _p(_nz(y.reshape(-1)), _f64p)):
+        raise ValueError("oracle_channel_mix failed")
+    return y
 
 
 def _nz(a):

@@ -654,6 +654,59 @@ int oracle_vjp2(int lin, int lsh, int lout, int C, int n_dst, int n_src, const i
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Channel mixing after the convolution                                      */
+/* ------------------------------------------------------------------------ */
+
+/* A per-irrep linear layer on the convolution output: for every output
+ * order l, the channels of all paths with l3 = l (in path order) are mixed
+ * by one dense matrix W_l of (n_l * C) rows and C columns, the same for every
+ * component m (so the map commutes with rotations):
+ *   y[i][l*l + l + m][v] = sum_{p: l3_p = l} sum_u W_l[(q_p*C + u)*C + v] * out[i][off_p + l + m][u]
+ * with q_p the rank of p among the paths of order l. W holds W_0, W_1, ...,
+ * W_lout back to back. The pages name the dense channel contraction that
+ * follows the tensor product ("Scaling the leading accuracy of deep
+ * equivariant models to biomolecular simulations of realistic size",
+ * section "Proposed method") but not its form; this is the plainest
+ * equivariant reading (one matrix per output order, shared by its
+ * components). */
+int oracle_channel_mix(int lin, int lsh, int lout, int C, int n, const double *out, const double *W, double *y)
+{
+    table t;
+    if (table_make(lin, lsh, lout, &t))
+        return -1;
+    const int Dout = t.Dout, Dy = (lout + 1) * (lout + 1);
+    /* start of W_l and the rank of every path among those of its order */
+    int64_t wofs[OR_LMAX + 2];
+    int rank[128], count[OR_LMAX + 1] = {0};
+    for (int p = 0; p < t.P; ++p) {
+        const int l3 = t.path[3 * p + 2];
+        rank[p] = count[l3]++;
+    }
+    wofs[0] = 0;
+    for (int l = 0; l <= lout; ++l)
+        wofs[l + 1] = wofs[l] + (int64_t)count[l] * C * C;
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < n; ++i) {
+        double *yi = y + (int64_t)i * Dy * C;
+        for (int q = 0; q < Dy * C; ++q)
+            yi[q] = 0.0;
+        for (int p = 0; p < t.P; ++p) {
+            const int l = t.path[3 * p + 2];
+            const double *Wl = W + wofs[l] + (int64_t)rank[p] * C * C;
+            for (int mi = 0; mi < 2 * l + 1; ++mi) {
+                const double *o = out + ((int64_t)i * Dout + t.off[p] + mi) * C;
+                double *yr = yi + (int64_t)(l * l + mi) * C;
+                for (int u = 0; u < C; ++u)
+                    for (int v = 0; v < C; ++v)
+                        yr[v] += Wl[(int64_t)u * C + v] * o[u];
+            }
+        }
+    }
+    table_free(&t);
+    return 0;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP
