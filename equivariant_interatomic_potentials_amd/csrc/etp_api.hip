@@ -13,6 +13,8 @@
 namespace etp {
 
 hipError_t launch_sh(int L, int64_t n, const float *vec, float *Y, float *dY, hipStream_t stream);
+hipError_t launch_mix(int L, int C, int n, const float *in, const float *W, float *y, bool accumulate,
+                      hipStream_t stream);
 size_t transpose_workspace_bytes(int n_src);
 hipError_t launch_transpose(int n_dst, int n_src, int64_t E, const int *row_ptr, const int *src, int *src_ptr,
                             int *perm, int *perm_dst, void *ws, hipStream_t stream);
@@ -386,6 +388,21 @@ etp_status etp_edge_conv_vjp2(etp_plan_t plan, const etp_graph *g, const float *
     if (d_x || d_w || d_vec)
         return hip_status(run_src(plan->L, bf16, etp::SRC_VJP2, a));
     return ETP_OK;
+}
+
+etp_status etp_channel_mix(etp_plan_t plan, int32_t n_nodes, const float *in, const float *W, float *out,
+                           uint32_t flags, void *stream)
+{
+    if (!plan || n_nodes < 0)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (flags & ~static_cast<uint32_t>(ETP_FLAG_ACCUMULATE))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (n_nodes == 0)
+        return ETP_OK;
+    if (!in || !W || !out)
+        return ETP_ERR_INVALID_ARGUMENT;
+    return hip_status(etp::launch_mix(plan->L, plan->C, n_nodes, in, W, out, flags & ETP_FLAG_ACCUMULATE,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 const char *etp_status_string(etp_status s)

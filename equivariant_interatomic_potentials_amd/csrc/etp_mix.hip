@@ -1,0 +1,155 @@
+// etp_mix.hip -- the per-irrep channel-mixing linear layer that follows the
+// convolution, on the matrix cores.
+//
+//   y[i, l, m, v] = sum_{p: l3_p = l} sum_u W_l[(q_p C + u), v] out[i, off_p + m, u]
+//
+// (q_p = rank of path p among the paths of output order l, in path order;
+// W = W_0, W_1, ... back to back, W_l of n_l * C rows and C columns; y has
+// the node-feature layout [n][(l_max + 1)^2][C], so it can feed the next
+// convolution.) The pages name a single dense channel contraction after the
+// tensor product ("Scaling the leading accuracy of deep equivariant models
+// to biomolecular simulations of realistic size", section "Proposed
+// method") without fixing its form; one matrix per output order, shared by
+// its 2l + 1 components, is the plainest equivariant reading.
+//
+// Per order l it is one dense product [n (2l+1)] x [n_l C] times [n_l C] x C.
+// Mapping (gfx950, wave64, v_mfma_f32_16x16x4f32):
+//   * a workgroup of 4 waves owns 64 rows (node, m) of one order and 128
+//     output channels; each wave owns 16 rows and holds eight 16 x 16 fp32
+//     accumulator tiles;
+//   * K runs over (path of order l, input channel) in chunks of 32 input
+//     channels: the chunk of W_l (32 x 128) is staged in LDS once per
+//     workgroup; each wave reads its A operand straight from the
+//     convolution output (lane l: row l % 16, k = l / 16 + 4 s), 4
+//     consecutive floats per row and step, the rest of the 128-byte line
+//     served by L1 on the next steps;
+//   * fp32 in, fp32 accumulate, no atomics; rows, output channels and input
+//     channels past the problem are zero-filled or dropped.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "etp_tables.hpp"
+
+namespace etp {
+
+constexpr int kMixMaxPaths = 17;  // most paths of one output order (l_max 4, l3 = 3)
+
+struct MixTab {
+    int lout, C, n, Dout, Dy;
+    int nl[5];                   // paths per output order
+    int tiles0[6];               // prefix of 64-row tiles over the orders
+    int off[5][kMixMaxPaths];    // first output row of each path of order l
+    int64_t wofs[6];             // start of W_l (floats)
+};
+
+typedef float mix_f4 __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(256) mix_kernel(const MixTab tb, const float *__restrict__ in,
+                                                  const float *__restrict__ W, float *__restrict__ y,
+                                                  const int accumulate)
+{
+    __shared__ float Bs[32][128 + 4];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int l = 0;
+    while (l < tb.lout && static_cast<int>(blockIdx.x) >= tb.tiles0[l + 1])
+        ++l;
+    const int tile = blockIdx.x - tb.tiles0[l];
+    const int d = 2 * l + 1, M = tb.n * d, C = tb.C;
+    const int c0 = blockIdx.y * 128;
+    const int kq = lane >> 4, col = lane & 15;
+
+    // this lane's A row
+    const int ra = tile * 64 + wv * 16 + col;
+    const bool rok = ra < M;
+    const int ia = rok ? ra / d : 0, ma = rok ? ra - ia * d : 0;
+    const float *abase = in + (static_cast<int64_t>(ia) * tb.Dout + ma) * C;
+
+    mix_f4 acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+        acc[t] = mix_f4{0.f, 0.f, 0.f, 0.f};
+
+    for (int q = 0; q < tb.nl[l]; ++q) {
+        const float *arow = abase + static_cast<int64_t>(tb.off[l][q]) * C;
+        const float *Wq = W + tb.wofs[l] + static_cast<int64_t>(q) * C * C;
+        for (int u0 = 0; u0 < C; u0 += 32) {
+            __syncthreads();  // the previous chunk's B reads are done
+            for (int t = threadIdx.x; t < 32 * 128; t += 256) {
+                const int kr = t >> 7, cc = t & 127;
+                const int u = u0 + kr, c = c0 + cc;
+                Bs[kr][cc] = (u < C && c < C) ? Wq[static_cast<int64_t>(u) * C + c] : 0.f;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int u = u0 + 4 * s + kq;
+                const float a = (rok && u < C) ? arow[u] : 0.f;
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Bs[4 * s + kq][16 * t + col], acc[t], 0, 0, 0);
+            }
+        }
+    }
+
+    // lane l holds rows 4 (l / 16) + rr, column 16 t + l % 16 of each tile
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int c = c0 + 16 * t + col;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int r = tile * 64 + wv * 16 + 4 * kq + rr;
+            if (r < M && c < C) {
+                const int i = r / d, m = r - (r / d) * d;
+                float *dst = y + (static_cast<int64_t>(i) * tb.Dy + l * l + m) * C + c;
+                *dst = accumulate ? *dst + acc[t][rr] : acc[t][rr];
+            }
+        }
+    }
+}
+
+// Path layout of one l_max for the mixing (from the compile-time table).
+template <int L>
+static MixTab mix_table(int C, int n)
+{
+    const Table &T = kTab<L>;
+    MixTab tb{};
+    tb.lout = L;
+    tb.C = C;
+    tb.n = n;
+    tb.Dout = T.dout_rows;
+    tb.Dy = (L + 1) * (L + 1);
+    for (int p = 0; p < T.P; ++p) {
+        const int l3 = T.path[p].l3;
+        tb.off[l3][tb.nl[l3]++] = T.path[p].out_row;
+    }
+    tb.tiles0[0] = 0;
+    tb.wofs[0] = 0;
+    for (int l = 0; l <= L; ++l) {
+        const int64_t rows = static_cast<int64_t>(n) * (2 * l + 1);
+        tb.tiles0[l + 1] = tb.tiles0[l] + static_cast<int>((rows + 63) / 64);
+        tb.wofs[l + 1] = tb.wofs[l] + static_cast<int64_t>(tb.nl[l]) * C * C;
+    }
+    return tb;
+}
+
+hipError_t launch_mix(int L, int C, int n, const float *in, const float *W, float *y, bool accumulate,
+                      hipStream_t stream)
+{
+    if (n == 0)
+        return hipSuccess;
+    MixTab tb;
+    switch (L) {
+    case 0: tb = mix_table<0>(C, n); break;
+    case 1: tb = mix_table<1>(C, n); break;
+    case 2: tb = mix_table<2>(C, n); break;
+    case 3: tb = mix_table<3>(C, n); break;
+    case 4: tb = mix_table<4>(C, n); break;
+    default: return hipErrorInvalidValue;
+    }
+    const dim3 grid(tb.tiles0[L + 1], (C + 127) / 128);
+    hipLaunchKernelGGL(mix_kernel, grid, dim3(256), 0, stream, tb, in, W, y, accumulate ? 1 : 0);
+    return hipGetLastError();
+}
+
+}  // namespace etp

@@ -30,7 +30,8 @@ ETP_FLAG_VALIDATE = 2
 # every symbol include/etp.h declares
 ABI_SYMBOLS = ("etp_plan_create", "etp_plan_destroy", "etp_plan_info", "etp_plan_tables",
                "etp_csr_transpose_workspace", "etp_csr_transpose", "etp_sh", "etp_edge_conv_fwd",
-               "etp_edge_conv_vjp", "etp_edge_conv_vjp2", "etp_status_string", "etp_version")
+               "etp_edge_conv_vjp", "etp_edge_conv_vjp2", "etp_channel_mix", "etp_status_string",
+               "etp_version")
 
 
 class EtpError(RuntimeError):
@@ -96,6 +97,7 @@ def _load():
         "etp_edge_conv_vjp": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, vp, vp, vp, u32, vp]),
         "etp_edge_conv_vjp2": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                     vp, u32, vp]),
+        "etp_channel_mix": (st, [vp, i32, vp, vp, vp, u32, vp]),
         "etp_status_string": (ctypes.c_char_p, [st]),
         "etp_version": (i32, []),
     }
@@ -310,3 +312,23 @@ def etp_edge_conv_vjp2(plan: Plan, graph: Graph, vec, x, w, grad_out, gg_x=None,
                                   _ptr(d_vec, "d_vec", f32, 3 * E, optional=True),
                                   _ptr(d_grad_out, "d_grad_out", f32, no, optional=True),
                                   flags, _stream(stream)), "etp_edge_conv_vjp2")
+
+
+def mix_rows(plan: Plan):
+    """Paths per output order l = 0..l_max (W_l has mix_rows[l] * C rows), from the plan's table."""
+    t = etp_plan_tables(plan)
+    l3 = t["paths"][:, 2]
+    return [int((l3 == l).sum()) for l in range(plan.L + 1)]
+
+
+def etp_channel_mix(plan: Plan, inp, W, out, flags: int = 0, stream=None):
+    """out[n, (l_max+1)^2, C] = per-order channel mixing of the convolution output inp[n, dout_rows, C];
+    W = W_0, W_1, ... back to back (W_l: [mix_rows[l] * C, C])."""
+    import torch
+    C = plan.C
+    n = inp.shape[0] if inp is not None else 0
+    nw = sum(mix_rows(plan)) * C * C
+    _check(lib.etp_channel_mix(plan.handle, n, _ptr(inp, "in", torch.float32, n * plan.dout_rows * C, optional=True),
+                               _ptr(W, "W", torch.float32, nw, optional=True),
+                               _ptr(out, "out", torch.float32, n * (plan.L + 1) ** 2 * C, optional=True),
+                               flags, _stream(stream)), "etp_channel_mix")

@@ -182,6 +182,25 @@ ETP_API etp_status etp_edge_conv_vjp2(etp_plan_t plan, const etp_graph *g, const
                               float *d_x, float *d_w, float *d_vec, float *d_grad_out, uint32_t flags,
                               void *stream);
 
+/* Per-irrep channel mixing after the convolution (the dense channel
+ * contraction that follows the tensor product: "Scaling the leading accuracy
+ * of deep equivariant models to biomolecular simulations of realistic size",
+ * section "Proposed method"; the pages do not fix its form, and this is one
+ * matrix per output order shared by that order's components):
+ *   out[i][l*l + m][v] = sum_{p: l3_p = l} sum_u W_l[(q_p*C + u)*C + v] * in[i][off_p + m][u]
+ * for i < n_nodes, l = 0..l_max, m < 2l + 1, v < C; q_p is the rank of path p
+ * among the paths of order l (path order) and off_p its first output row.
+ * in:  DEVICE float [n_nodes][dout_rows][C] (a convolution output);
+ * W:   DEVICE float W_0, W_1, ..., W_lmax back to back, W_l of n_l*C rows
+ *      and C columns (row-major), n_l = number of paths with l3 = l;
+ * out: DEVICE float [n_nodes][(l_max+1)^2][C] (the node-feature layout).
+ * fp32 in and out, fp32 matrix-core accumulation. flags: ETP_FLAG_ACCUMULATE
+ * adds into out. The caller owns every buffer; nothing is allocated. Errors:
+ * INVALID_ARGUMENT (null plan or pointers with n_nodes > 0, negative
+ * n_nodes, other flags), HIP (launch failure). */
+ETP_API etp_status etp_channel_mix(etp_plan_t plan, int32_t n_nodes, const float *in, const float *W, float *out,
+                                   uint32_t flags, void *stream);
+
 ETP_API const char *etp_status_string(etp_status s);
 
 /* Version of this ABI (major * 10000 + minor * 100 + patch). */
