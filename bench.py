@@ -116,6 +116,36 @@ def measured_traffic(op):
     return d.get("bytes_per_launch", {}).get(op)
 
 
+MFMA_F32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix-core peak
+
+
+def time_channel_mix(etp, plan, out, L, C, N, reps):
+    """The per-irrep channel mixing after the convolution (outside the step):
+    ms per call with HIP events, algorithmic bytes (conv output, W, result,
+    each once) and FLOPs (2 per multiply-add of the per-order products)."""
+    import torch
+    rows = etp.mix_rows(plan)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12345)
+    W = torch.randn(sum(rows) * C * C, generator=g, device="cuda") / float(np.sqrt(C))
+    y = torch.empty(N, (L + 1) ** 2, C, device="cuda")
+    for _ in range(3):
+        etp.etp_channel_mix(plan, out, W, y)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        etp.etp_channel_mix(plan, out, W, y)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / reps * 1e-3
+    byts = 4.0 * (out.numel() + W.numel() + y.numel())
+    flops = 2.0 * sum(N * (2 * l + 1) * rows[l] * C * C for l in range(L + 1))
+    return {"ms": round(t * 1e3, 4), "algo_GBps": byts / t / 1e9, "algo_TFLOPs": flops / t / 1e12,
+            "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS, "mfma_frac": flops / t / 1e12 / MFMA_F32_PEAK_TFLOPS,
+            "bound": "mfma" if flops / (MFMA_F32_PEAK_TFLOPS * 1e12) > byts / (HBM_PEAK_GBS * 1e9) else "hbm"}
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """The oracle, as it is, on the first R destination rows of the graph
     (R sized to about budget_s of host time); edges/s of fwd + VJP + VJP2."""
@@ -267,6 +297,7 @@ def main(argv=None):
         "ops": op_report,
         "roofline": roof,
     }
+    line["next_ops"] = {"channel_mix": time_channel_mix(etp, plan, out, L, C, N, a.steps)}
     if not a.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)

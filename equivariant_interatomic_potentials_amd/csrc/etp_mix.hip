@@ -14,15 +14,15 @@
 //
 // Per order l it is one dense product [n (2l+1)] x [n_l C] times [n_l C] x C.
 // Mapping (gfx950, wave64, v_mfma_f32_16x16x4f32):
-//   * a workgroup of 4 waves owns 64 rows (node, m) of one order and 128
-//     output channels; each wave owns 16 rows and holds eight 16 x 16 fp32
+//   * a workgroup of 4 waves owns 64 rows (node, m) of one order and 64
+//     output channels; each wave owns 16 rows and holds four 16 x 16 fp32
 //     accumulator tiles;
 //   * K runs over (path of order l, input channel) in chunks of 32 input
-//     channels: the chunk of W_l (32 x 128) is staged in LDS once per
-//     workgroup; each wave reads its A operand straight from the
-//     convolution output (lane l: row l % 16, k = l / 16 + 4 s), 4
-//     consecutive floats per row and step, the rest of the 128-byte line
-//     served by L1 on the next steps;
+//     channels: the chunk of W_l (32 x 64) is staged in a double-buffered
+//     LDS tile once per workgroup; each wave reads its A operand straight
+//     from the convolution output (lane l: row l % 16, k = l / 16 + 4 s);
+//     the next chunk's A and W values are loaded into registers while the
+//     current chunk's MFMAs run (one barrier per chunk);
 //   * fp32 in, fp32 accumulate, no atomics; rows, output channels and input
 //     channels past the problem are zero-filled or dropped.
 #include <hip/hip_runtime.h>
@@ -45,18 +45,20 @@ struct MixTab {
 
 typedef float mix_f4 __attribute__((ext_vector_type(4)));
 
+constexpr int kMixCols = 64;  // output channels per workgroup
+
 __global__ void __launch_bounds__(256) mix_kernel(const MixTab tb, const float *__restrict__ in,
                                                   const float *__restrict__ W, float *__restrict__ y,
                                                   const int accumulate)
 {
-    __shared__ float Bs[32][128 + 4];
+    __shared__ float Bs[2][32][kMixCols + 4];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     int l = 0;
     while (l < tb.lout && static_cast<int>(blockIdx.x) >= tb.tiles0[l + 1])
         ++l;
     const int tile = blockIdx.x - tb.tiles0[l];
     const int d = 2 * l + 1, M = tb.n * d, C = tb.C;
-    const int c0 = blockIdx.y * 128;
+    const int c0 = blockIdx.y * kMixCols;
     const int kq = lane >> 4, col = lane & 15;
 
     // this lane's A row
@@ -65,36 +67,63 @@ __global__ void __launch_bounds__(256) mix_kernel(const MixTab tb, const float *
     const int ia = rok ? ra / d : 0, ma = rok ? ra - ia * d : 0;
     const float *abase = in + (static_cast<int64_t>(ia) * tb.Dout + ma) * C;
 
-    mix_f4 acc[8];
+    mix_f4 acc[4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < 4; ++t)
         acc[t] = mix_f4{0.f, 0.f, 0.f, 0.f};
 
-    for (int q = 0; q < tb.nl[l]; ++q) {
+    // K in chunks of 32 input channels of one path: chunk ci = (q, u0).
+    // The next chunk's A and W values are loaded into registers while the
+    // current chunk's MFMAs run; W goes through a double-buffered LDS tile.
+    const int ncu = (C + 31) / 32, nchunk = tb.nl[l] * ncu;
+    constexpr int BPT = 32 * kMixCols / 256;  // W values staged per thread
+    float a_nx[8], b_nx[BPT];
+    auto fetch = [&](int ci) {
+        const int q = ci / ncu, u0 = (ci - q * ncu) * 32;
         const float *arow = abase + static_cast<int64_t>(tb.off[l][q]) * C;
         const float *Wq = W + tb.wofs[l] + static_cast<int64_t>(q) * C * C;
-        for (int u0 = 0; u0 < C; u0 += 32) {
-            __syncthreads();  // the previous chunk's B reads are done
-            for (int t = threadIdx.x; t < 32 * 128; t += 256) {
-                const int kr = t >> 7, cc = t & 127;
-                const int u = u0 + kr, c = c0 + cc;
-                Bs[kr][cc] = (u < C && c < C) ? Wq[static_cast<int64_t>(u) * C + c] : 0.f;
-            }
-            __syncthreads();
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const int u = u0 + 4 * s + kq;
-                const float a = (rok && u < C) ? arow[u] : 0.f;
+        for (int s = 0; s < 8; ++s) {
+            const int u = u0 + 4 * s + kq;
+            a_nx[s] = (rok && u < C) ? arow[u] : 0.f;
+        }
 #pragma unroll
-                for (int t = 0; t < 8; ++t)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Bs[4 * s + kq][16 * t + col], acc[t], 0, 0, 0);
-            }
+        for (int k = 0; k < BPT; ++k) {
+            const int t = threadIdx.x + 256 * k;
+            const int kr = t / kMixCols, cc = t % kMixCols;
+            const int u = u0 + kr, c = c0 + cc;
+            b_nx[k] = (u < C && c < C) ? Wq[static_cast<int64_t>(u) * C + c] : 0.f;
+        }
+    };
+    fetch(0);
+    for (int ci = 0; ci < nchunk; ++ci) {
+        const int buf = ci & 1;
+#pragma unroll
+        for (int k = 0; k < BPT; ++k) {
+            const int t = threadIdx.x + 256 * k;
+            Bs[buf][t / kMixCols][t % kMixCols] = b_nx[k];
+        }
+        float a[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            a[s] = a_nx[s];
+        // one barrier per chunk: the stores above are seen by every wave,
+        // and the buffer written next (buf ^ 1) was last read before it
+        __syncthreads();
+        if (ci + 1 < nchunk)
+            fetch(ci + 1);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], Bs[buf][4 * s + kq][16 * t + col], acc[t], 0,
+                                                              0, 0);
         }
     }
 
     // lane l holds rows 4 (l / 16) + rr, column 16 t + l % 16 of each tile
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < 4; ++t) {
         const int c = c0 + 16 * t + col;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -147,7 +176,7 @@ hipError_t launch_mix(int L, int C, int n, const float *in, const float *W, floa
     case 4: tb = mix_table<4>(C, n); break;
     default: return hipErrorInvalidValue;
     }
-    const dim3 grid(tb.tiles0[L + 1], (C + 127) / 128);
+    const dim3 grid(tb.tiles0[L + 1], (C + kMixCols - 1) / kMixCols);
     hipLaunchKernelGGL(mix_kernel, grid, dim3(256), 0, stream, tb, in, W, y, accumulate ? 1 : 0);
     return hipGetLastError();
 }
