@@ -76,6 +76,8 @@ def _load():
         lib.oracle_vjp2.argtypes = [ctypes.c_int] * 6 + [_i32p, _i32p] + [_f64p] * 11
         lib.oracle_channel_mix.restype = ctypes.c_int
         lib.oracle_channel_mix.argtypes = [ctypes.c_int] * 5 + [_f64p] * 3
+        lib.oracle_edge_forces.restype = None
+        lib.oracle_edge_forces.argtypes = [ctypes.c_int, ctypes.c_int, _i32p, _i32p, _f64p, _f64p]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -230,6 +232,17 @@ def channel_mix(L, out, W):
                                   _p(_nz(y.reshape(-1)), _f64p)):
         raise ValueError("oracle_channel_mix failed")
     return y
+
+
+def edge_forces(row_ptr, src, n_src, gr):
+    """F[max(n_dst, n_src), 3] = sum over in-edges of gr - sum over out-edges of gr
+    (forces when gr = dE/dvec and vec_e = pos[src_e] - pos[dst_e])."""
+    row_ptr, srcv, n_dst = _graph(row_ptr, src)
+    gr = _f64(gr).reshape(-1)
+    F = np.zeros((max(n_dst, n_src), 3))
+    _load().oracle_edge_forces(n_dst, n_src, _p(row_ptr, _i32p), _p(srcv, _i32p), _p(_nz(gr), _f64p),
+                               _p(_nz(F.reshape(-1)), _f64p))
+    return F
 
 
 def _nz(a):

@@ -707,6 +707,31 @@ int oracle_channel_mix(int lin, int lsh, int lout, int C, int n, const double *o
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Forces on the atoms                                                       */
+/* ------------------------------------------------------------------------ */
+
+/* With vec_e = pos[src_e] - pos[dst_e] (from the receiving atom to its
+ * neighbour) and gr_e = dE/dvec_e, the chain rule gives
+ * dE/dpos[k] = sum_{e: src_e = k} gr_e - sum_{e: dst_e = k} gr_e, and the
+ * force F = -dE/dpos (energy and forces from one model: "How does FlashCart
+ * make equivariant interatomic potentials faster and more accurate?",
+ * section on the SPICE-MACE-OFF model). F has max(n_dst, n_src) rows; edge
+ * by edge, in edge order. */
+void oracle_edge_forces(int n_dst, int n_src, const int32_t *row_ptr, const int32_t *src, const double *gr,
+                        double *F)
+{
+    const int n = n_dst > n_src ? n_dst : n_src;
+    for (int k = 0; k < 3 * n; ++k)
+        F[k] = 0.0;
+    for (int i = 0; i < n_dst; ++i)
+        for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e)
+            for (int c = 0; c < 3; ++c) {
+                F[3 * i + c] += gr[3 * e + c];
+                F[3 * (int64_t)src[e] + c] -= gr[3 * e + c];
+            }
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP
