@@ -15,6 +15,8 @@ namespace etp {
 hipError_t launch_sh(int L, int64_t n, const float *vec, float *Y, float *dY, hipStream_t stream);
 hipError_t launch_mix(int L, int C, int n, const float *in, const float *W, float *y, bool accumulate,
                       hipStream_t stream);
+hipError_t launch_forces(int n_dst, int n_src, const int *row_ptr, const int *src_ptr, const int *perm,
+                         const float *gr, float *F, bool accumulate, hipStream_t stream);
 size_t transpose_workspace_bytes(int n_src);
 hipError_t launch_transpose(int n_dst, int n_src, int64_t E, const int *row_ptr, const int *src, int *src_ptr,
                             int *perm, int *perm_dst, void *ws, hipStream_t stream);
@@ -403,6 +405,28 @@ etp_status etp_channel_mix(etp_plan_t plan, int32_t n_nodes, const float *in, co
         return ETP_ERR_INVALID_ARGUMENT;
     return hip_status(etp::launch_mix(plan->L, plan->C, n_nodes, in, W, out, flags & ETP_FLAG_ACCUMULATE,
                                       static_cast<hipStream_t>(stream)));
+}
+
+etp_status etp_edge_forces(const etp_graph *g, const float *grad_vec, float *forces, uint32_t flags, void *stream)
+{
+    etp_status st = check_graph(g, true);
+    if (st != ETP_OK)
+        return st;
+    if (flags & ~3u)
+        return ETP_ERR_INVALID_ARGUMENT;
+    const int n = g->n_dst > g->n_src ? g->n_dst : g->n_src;
+    if (n > 0 && !forces)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (g->n_edges > 0 && !grad_vec)
+        return ETP_ERR_INVALID_ARGUMENT;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (flags & ETP_FLAG_VALIDATE) {
+        st = validate_graph(g, s);
+        if (st != ETP_OK)
+            return st;
+    }
+    return hip_status(etp::launch_forces(g->n_dst, g->n_src, g->row_ptr, g->src_ptr, g->perm, grad_vec, forces,
+                                         flags & ETP_FLAG_ACCUMULATE, s));
 }
 
 const char *etp_status_string(etp_status s)

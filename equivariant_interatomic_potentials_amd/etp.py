@@ -30,8 +30,8 @@ ETP_FLAG_VALIDATE = 2
 # every symbol include/etp.h declares
 ABI_SYMBOLS = ("etp_plan_create", "etp_plan_destroy", "etp_plan_info", "etp_plan_tables",
                "etp_csr_transpose_workspace", "etp_csr_transpose", "etp_sh", "etp_edge_conv_fwd",
-               "etp_edge_conv_vjp", "etp_edge_conv_vjp2", "etp_channel_mix", "etp_status_string",
-               "etp_version")
+               "etp_edge_conv_vjp", "etp_edge_conv_vjp2", "etp_channel_mix", "etp_edge_forces",
+               "etp_status_string", "etp_version")
 
 
 class EtpError(RuntimeError):
@@ -98,6 +98,7 @@ def _load():
         "etp_edge_conv_vjp2": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                     vp, u32, vp]),
         "etp_channel_mix": (st, [vp, i32, vp, vp, vp, u32, vp]),
+        "etp_edge_forces": (st, [ctypes.POINTER(etp_graph), vp, vp, u32, vp]),
         "etp_status_string": (ctypes.c_char_p, [st]),
         "etp_version": (i32, []),
     }
@@ -332,3 +333,14 @@ def etp_channel_mix(plan: Plan, inp, W, out, flags: int = 0, stream=None):
                                _ptr(W, "W", torch.float32, nw, optional=True),
                                _ptr(out, "out", torch.float32, n * (plan.L + 1) ** 2 * C, optional=True),
                                flags, _stream(stream)), "etp_channel_mix")
+
+
+def etp_edge_forces(graph: Graph, grad_vec, forces, flags: int = 0, stream=None):
+    """forces[max(n_dst, n_src), 3] = sum over in-edges of grad_vec - sum over out-edges (needs the transpose)."""
+    import torch
+    E = graph.n_edges
+    n = max(graph.n_dst, graph.n_src)
+    g = graph.struct()
+    _check(lib.etp_edge_forces(ctypes.byref(g), _ptr(grad_vec, "grad_vec", torch.float32, 3 * E, optional=True),
+                               _ptr(forces, "forces", torch.float32, 3 * n, optional=True), flags, _stream(stream)),
+           "etp_edge_forces")

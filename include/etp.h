@@ -201,6 +201,21 @@ ETP_API etp_status etp_edge_conv_vjp2(etp_plan_t plan, const etp_graph *g, const
 ETP_API etp_status etp_channel_mix(etp_plan_t plan, int32_t n_nodes, const float *in, const float *W, float *out,
                                    uint32_t flags, void *stream);
 
+/* Forces on the atoms from the per-edge energy gradient grad_vec = dE/dvec
+ * (the VJP's grad_vec), with vec_e = pos[src_e] - pos[dst_e]:
+ *   forces[k] = sum_{e in in(k)} grad_vec[e] - sum_{e in out(k)} grad_vec[e]
+ * for k < max(n_dst, n_src) (energy and forces from one model: "How does
+ * FlashCart make equivariant interatomic potentials faster and more
+ * accurate?", section on the SPICE-MACE-OFF model). g needs the transpose
+ * (src_ptr, perm). grad_vec: DEVICE float [n_edges][3]; forces: DEVICE float
+ * [max(n_dst, n_src)][3]. Fixed-order sums, no atomics. flags:
+ * ETP_FLAG_ACCUMULATE adds into forces, ETP_FLAG_VALIDATE checks the CSR
+ * first. The caller owns every buffer. Errors: INVALID_ARGUMENT (null graph,
+ * missing transpose, null pointers, other flags), UNSUPPORTED (n_edges >=
+ * 2^31), INTERNAL (malformed graph under VALIDATE), HIP (launch failure). */
+ETP_API etp_status etp_edge_forces(const etp_graph *g, const float *grad_vec, float *forces, uint32_t flags,
+                                   void *stream);
+
 ETP_API const char *etp_status_string(etp_status s);
 
 /* Version of this ABI (major * 10000 + minor * 100 + patch). */
