@@ -146,6 +146,28 @@ def time_channel_mix(etp, plan, out, L, C, N, reps):
             "bound": "mfma" if flops / (MFMA_F32_PEAK_TFLOPS * 1e12) > byts / (HBM_PEAK_GBS * 1e9) else "hbm"}
 
 
+def time_edge_forces(etp, g, gr, N, n_src, E, reps):
+    """Edge-to-atom force assembly from the VJP's grad_vec (outside the step):
+    ms per call; algorithmic bytes = grad_vec, perm, both offset arrays and the
+    forces, each once."""
+    import torch
+    n = max(N, n_src)
+    F = torch.empty(n, 3, device="cuda")
+    for _ in range(3):
+        etp.etp_edge_forces(g, gr, F)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        etp.etp_edge_forces(g, gr, F)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / reps * 1e-3
+    byts = 12.0 * E + 4.0 * E + 4.0 * (N + 1) + 4.0 * (n_src + 1) + 12.0 * n
+    return {"ms": round(t * 1e3, 4), "algo_GBps": byts / t / 1e9, "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS,
+            "bound": "hbm"}
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """The oracle, as it is, on the first R destination rows of the graph
     (R sized to about budget_s of host time); edges/s of fwd + VJP + VJP2."""
@@ -297,7 +319,8 @@ def main(argv=None):
         "ops": op_report,
         "roofline": roof,
     }
-    line["next_ops"] = {"channel_mix": time_channel_mix(etp, plan, out, L, C, N, a.steps)}
+    line["next_ops"] = {"channel_mix": time_channel_mix(etp, plan, out, L, C, N, a.steps),
+                        "edge_forces": time_edge_forces(etp, g, gr, N, n_src, E, a.steps)}
     if not a.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)
