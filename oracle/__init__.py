@@ -78,6 +78,9 @@ def _load():
         lib.oracle_channel_mix.argtypes = [ctypes.c_int] * 5 + [_f64p] * 3
         lib.oracle_edge_forces.restype = None
         lib.oracle_edge_forces.argtypes = [ctypes.c_int, ctypes.c_int, _i32p, _i32p, _f64p, _f64p]
+        _f32p = ctypes.POINTER(ctypes.c_float)
+        lib.oracle_neighbors.restype = ctypes.c_int64
+        lib.oracle_neighbors.argtypes = [ctypes.c_int, _f32p, _f32p, ctypes.c_float, _i32p, _i32p, _f32p]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -243,6 +246,23 @@ def edge_forces(row_ptr, src, n_src, gr):
     _load().oracle_edge_forces(n_dst, n_src, _p(row_ptr, _i32p), _p(srcv, _i32p), _p(_nz(gr), _f64p),
                                _p(_nz(F.reshape(-1)), _f64p))
     return F
+
+
+def neighbors(pos, box, rc):
+    """Periodic neighbour list (row_ptr[n+1], src[E], vec[E, 3] float32): j != i with the
+    float32 minimum-image distance strictly below rc, rows sorted by src."""
+    f32p = ctypes.POINTER(ctypes.c_float)
+    pos = np.ascontiguousarray(pos, np.float32)
+    n = pos.shape[0]
+    box = np.ascontiguousarray(np.broadcast_to(np.asarray(box, np.float32), (3,)))
+    lib = _load()
+    row_ptr = np.zeros(n + 1, np.int32)
+    E = lib.oracle_neighbors(n, _p(pos, f32p), _p(box, f32p), float(rc), _p(row_ptr, _i32p), None, None)
+    src = np.zeros(max(E, 1), np.int32)
+    vec = np.zeros((max(E, 1), 3), np.float32)
+    lib.oracle_neighbors(n, _p(pos, f32p), _p(box, f32p), float(rc), _p(row_ptr, _i32p), _p(src, _i32p),
+                         _p(vec, f32p))
+    return row_ptr, src[:E], vec[:E]
 
 
 def _nz(a):

@@ -732,6 +732,59 @@ void oracle_edge_forces(int n_dst, int n_src, const int32_t *row_ptr, const int3
             }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Neighbour list                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* Periodic neighbour list of n atoms in an orthorhombic box (each side at
+ * least twice the cutoff): edge (i <- j) for every j != i whose minimum-image
+ * distance is strictly below rc, rows sorted by j; vec = the minimum-image
+ * displacement pos[j] - pos[i] (the graph the convolution walks: "edges per
+ * atom" in "How does FlashCart make equivariant interatomic potentials faster
+ * and more accurate?", section on the SPICE-MACE-OFF model). The cutoff test
+ * decides an integer from floating point, so it is taken in float32 with the
+ * operations spelled out (wrap q = p - L floor(p / L), d = q_j - q_i,
+ * d -= L rint(d / L), r2 = dx dx + dy dy + dz dz as fused multiply-adds),
+ * which any implementation of this contract reproduces bit for bit. Brute
+ * force over all pairs. Returns the number of edges; src / vec are written
+ * only when not NULL (then they must hold that many). */
+static float or_wrap(float p, float L) { return fmaf(-L, floorf(p / L), p); }
+
+int64_t oracle_neighbors(int n, const float *pos, const float *box, float rc, int32_t *row_ptr, int32_t *src,
+                         float *vec)
+{
+    const float rc2 = rc * rc;
+    int64_t e = 0;
+    if (row_ptr)
+        row_ptr[0] = 0;
+    for (int i = 0; i < n; ++i) {
+        float qi[3];
+        for (int c = 0; c < 3; ++c)
+            qi[c] = or_wrap(pos[3 * i + c], box[c]);
+        for (int j = 0; j < n; ++j) {
+            if (j == i)
+                continue;
+            float d[3];
+            for (int c = 0; c < 3; ++c) {
+                const float dc = or_wrap(pos[3 * j + c], box[c]) - qi[c];
+                d[c] = fmaf(-box[c], rintf(dc / box[c]), dc);
+            }
+            const float r2 = fmaf(d[2], d[2], fmaf(d[1], d[1], d[0] * d[0]));
+            if (r2 < rc2) {
+                if (src)
+                    src[e] = j;
+                if (vec)
+                    for (int c = 0; c < 3; ++c)
+                        vec[3 * e + c] = d[c];
+                ++e;
+            }
+        }
+        if (row_ptr)
+            row_ptr[i + 1] = (int32_t)e;
+    }
+    return e;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -16,6 +16,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "etp_oracle.c")
 PINS = [os.path.join(ROOT, "tests", "test_oracle_sh_cg.py"),
         os.path.join(ROOT, "tests", "test_oracle_conv.py")]
+# the pin files of the layers outside the convolution, by mutant name prefix
+EXTRA_PINS = {"mix_": "test_oracle_mix.py", "forces_": "test_oracle_forces.py",
+              "nl_": "test_oracle_neighbors.py"}
 
 # (name, exact text in the oracle, replacement)
 MUTANTS = [
@@ -41,6 +44,18 @@ MUTANTS = [
     ("vjp2_dx_swap", "dxj[en.a * C + u] += en.C * g * (Y[en.b] * Wv + Yd[en.b] * wv);",
      "dxj[en.a * C + u] += en.C * g * (Y[en.b] * wv + Yd[en.b] * Wv);"),
     ("hyperdual_mixed", "x.a * y.d + x.b * y.c + x.c * y.b + x.d * y.a};", "x.a * y.d + x.b * y.c + x.d * y.a};"),
+    ("mix_rank", "rank[p] = count[l3]++;", "rank[p] = count[l3];"),
+    ("mix_transposed_W", "yr[v] += Wl[(int64_t)u * C + v] * o[u];", "yr[v] += Wl[(int64_t)v * C + u] * o[u];"),
+    ("forces_sign", "F[3 * (int64_t)src[e] + c] -= gr[3 * e + c];", "F[3 * (int64_t)src[e] + c] += gr[3 * e + c];"),
+    ("forces_dst_index", "F[3 * i + c] += gr[3 * e + c];", "F[3 * (int64_t)src[e] + c] += gr[3 * e + c];"),
+    ("nl_not_strict", "if (r2 < rc2) {", "if (r2 <= rc2) {"),
+    ("nl_no_min_image", "d[c] = fmaf(-box[c], rintf(dc / box[c]), dc);", "d[c] = dc;"),
+    ("nl_floor_image", "d[c] = fmaf(-box[c], rintf(dc / box[c]), dc);",
+     "d[c] = fmaf(-box[c], floorf(dc / box[c]), dc);"),
+    ("nl_vec_sign", "const float dc = or_wrap(pos[3 * j + c], box[c]) - qi[c];",
+     "const float dc = qi[c] - or_wrap(pos[3 * j + c], box[c]);"),
+    ("nl_self", "if (j == i)\n                continue;", "if (j == i && i < 0)\n                continue;"),
+    ("nl_no_wrap", "qi[c] = or_wrap(pos[3 * i + c], box[c]);", "qi[c] = pos[3 * i + c];"),
     ("transpose_unstable", "int64_t k = cursor[src[e]]++;", "int64_t k = src_ptr[src[e] + 1] - 1 - (cursor[src[e]]++ - src_ptr[src[e]]);"),
 ]
 
@@ -56,6 +71,7 @@ def test_pins_catch_mutant(name, old, new, tmp_path):
     subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC",
                            str(mutated), "-o", str(lib), "-lm"])
     env = dict(os.environ, ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    pins = [os.path.join(ROOT, "tests", f) for k, f in EXTRA_PINS.items() if name.startswith(k)] or PINS
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        *PINS], cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+                        *pins], cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pin suite:\n{r.stdout[-2000:]}"
