@@ -3,6 +3,7 @@
 // per-l_max kernel launchers.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -20,6 +21,11 @@ hipError_t launch_forces(int n_dst, int n_src, const int *row_ptr, const int *sr
 size_t transpose_workspace_bytes(int n_src);
 hipError_t launch_transpose(int n_dst, int n_src, int64_t E, const int *row_ptr, const int *src, int *src_ptr,
                             int *perm, int *perm_dst, void *ws, hipStream_t stream);
+size_t neighbor_workspace_bytes(int n, const float *box, float rc);
+hipError_t launch_neighbor_count(int n, const float *pos, const float *box, float rc, int *row_ptr, void *ws,
+                                 hipStream_t stream);
+hipError_t launch_neighbor_fill(int n, const float *pos, const float *box, float rc, const int *row_ptr,
+                                int64_t n_edges, int *src, float *vec, void *ws, int **bad, hipStream_t stream);
 hipError_t launch_validate(int n_dst, int n_src, int64_t E, const int *row_ptr, const int *src, int *bad,
                            hipStream_t stream);
 
@@ -113,6 +119,20 @@ hipError_t run_src(int L, bool bf16, int mode, const etp::ConvArgs &a)
         ETP_RUN_CASES(src, 4, 0) ETP_RUN_CASES(src, 4, 1)
     default: return hipErrorInvalidValue;
     }
+}
+
+// box: three finite sides, each at least twice the finite, positive cutoff
+etp_status check_neighbor_args(int32_t n, const float *box, float cutoff)
+{
+    if (n < 0 || !box || !(cutoff > 0.f) || !std::isfinite(cutoff))
+        return ETP_ERR_INVALID_ARGUMENT;
+    for (int a = 0; a < 3; ++a)
+        if (!std::isfinite(box[a]) || !(box[a] > 0.f))
+            return ETP_ERR_INVALID_ARGUMENT;
+    for (int a = 0; a < 3; ++a)
+        if (!(box[a] >= 2.f * cutoff))
+            return ETP_ERR_UNSUPPORTED;
+    return ETP_OK;
 }
 
 }  // namespace
@@ -427,6 +447,69 @@ etp_status etp_edge_forces(const etp_graph *g, const float *grad_vec, float *for
     }
     return hip_status(etp::launch_forces(g->n_dst, g->n_src, g->row_ptr, g->src_ptr, g->perm, grad_vec, forces,
                                          flags & ETP_FLAG_ACCUMULATE, s));
+}
+
+etp_status etp_neighbor_workspace(int32_t n_atoms, const float *box, float cutoff, size_t *bytes)
+{
+    etp_status st = check_neighbor_args(n_atoms, box, cutoff);
+    if (st != ETP_OK)
+        return st;
+    if (!bytes)
+        return ETP_ERR_INVALID_ARGUMENT;
+    *bytes = etp::neighbor_workspace_bytes(n_atoms, box, cutoff);
+    return ETP_OK;
+}
+
+etp_status etp_neighbor_count(int32_t n_atoms, const float *pos, const float *box, float cutoff, int32_t *row_ptr,
+                              void *ws, size_t ws_bytes, void *stream)
+{
+    etp_status st = check_neighbor_args(n_atoms, box, cutoff);
+    if (st != ETP_OK)
+        return st;
+    if (!row_ptr || (n_atoms > 0 && !pos))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (!ws || ws_bytes < etp::neighbor_workspace_bytes(n_atoms, box, cutoff))
+        return ETP_ERR_WORKSPACE;
+    return hip_status(
+        etp::launch_neighbor_count(n_atoms, pos, box, cutoff, row_ptr, ws, static_cast<hipStream_t>(stream)));
+}
+
+etp_status etp_neighbor_fill(int32_t n_atoms, const float *pos, const float *box, float cutoff, const int32_t *row_ptr,
+                             int64_t n_edges, int32_t *src, float *vec, uint32_t flags, void *ws, size_t ws_bytes,
+                             void *stream)
+{
+    etp_status st = check_neighbor_args(n_atoms, box, cutoff);
+    if (st != ETP_OK)
+        return st;
+    if (n_edges < 0 || flags & ~static_cast<uint32_t>(ETP_FLAG_VALIDATE))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (n_edges >= kMaxEdges)
+        return ETP_ERR_UNSUPPORTED;
+    if (!row_ptr || (n_atoms > 0 && !pos) || (n_edges > 0 && (!src || !vec)))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (!ws || ws_bytes < etp::neighbor_workspace_bytes(n_atoms, box, cutoff))
+        return ETP_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (flags & ETP_FLAG_VALIDATE) {
+        // row_ptr must be a CSR of n_edges entries before anything is written
+        etp_graph g{n_atoms, n_atoms, n_edges, row_ptr, nullptr, nullptr, nullptr, nullptr};
+        if (n_atoms > 0 && (st = validate_graph(&g, s)) != ETP_OK)
+            return st;
+        if (n_atoms == 0 && n_edges != 0)
+            return ETP_ERR_INTERNAL;
+    }
+    int *bad = nullptr;
+    if (etp::launch_neighbor_fill(n_atoms, pos, box, cutoff, row_ptr, n_edges, src, vec, ws, &bad, s) != hipSuccess)
+        return ETP_ERR_HIP;
+    if (flags & ETP_FLAG_VALIDATE) {
+        int host = 0;
+        if (hipMemcpyAsync(&host, bad, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess)
+            return ETP_ERR_HIP;
+        if (host != 0)
+            return ETP_ERR_INTERNAL;
+    }
+    return ETP_OK;
 }
 
 const char *etp_status_string(etp_status s)

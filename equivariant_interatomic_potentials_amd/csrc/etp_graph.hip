@@ -203,7 +203,7 @@ __global__ void __launch_bounds__(256) dst_lookup_kernel(int64_t E, int n_dst, c
 }
 
 // Counts violations of: row_ptr[0] == 0, row_ptr non-decreasing,
-// row_ptr[n_dst] == E, 0 <= src[e] < n_src.
+// row_ptr[n_dst] == E, 0 <= src[e] < n_src (src may be null: not checked).
 __global__ void __launch_bounds__(256) validate_kernel(int n_dst, int n_src, int64_t E, const int *__restrict__ row_ptr,
                                                        const int *__restrict__ src, int *__restrict__ bad)
 {
@@ -212,8 +212,9 @@ __global__ void __launch_bounds__(256) validate_kernel(int n_dst, int n_src, int
     int nbad = 0;
     for (int64_t i = t0; i < n_dst; i += stride)
         nbad += row_ptr[i] > row_ptr[i + 1];
-    for (int64_t e = t0; e < E; e += stride)
-        nbad += (src[e] < 0 || src[e] >= n_src);
+    if (src)
+        for (int64_t e = t0; e < E; e += stride)
+            nbad += (src[e] < 0 || src[e] >= n_src);
     if (t0 == 0)
         nbad += (row_ptr[0] != 0) + (static_cast<int64_t>(row_ptr[n_dst]) != E);
     if (nbad)
@@ -224,6 +225,33 @@ static unsigned grid_for(int64_t n)
 {
     const int64_t b = (n + 255) / 256;
     return static_cast<unsigned>(b < 1 ? 1 : (b > 16384 ? 16384 : b));
+}
+
+int64_t scan_bsum_ints(int64_t n) { return (n + kScanTile - 1) / kScanTile + 1; }
+
+hipError_t launch_fill_int(int *p, int64_t n, int v, hipStream_t stream)
+{
+    if (n > 0)
+        hipLaunchKernelGGL(fill_kernel, dim3(grid_for(n)), dim3(256), 0, stream, p, n, v);
+    return hipGetLastError();
+}
+
+// ptr[1..n] hold counts; on return ptr[k] = the sum of counts 1..k, i.e.
+// the offsets of a CSR when ptr[0] = 0 (ptr[0] is not touched). bsum holds
+// scan_bsum_ints(n) ints.
+hipError_t launch_counts_to_offsets(int *ptr, int64_t n, int *bsum, hipStream_t stream)
+{
+    if (n <= 0)
+        return hipGetLastError();
+    const int64_t ntile = (n + kScanTile - 1) / kScanTile;
+    hipLaunchKernelGGL(scan_tiles_kernel, dim3(static_cast<unsigned>(ntile)), dim3(kScanThreads), 0, stream, ptr + 1,
+                       n, bsum);
+    if (ntile > 1) {
+        hipLaunchKernelGGL(scan_single_kernel, dim3(1), dim3(kScanThreads), 0, stream, bsum, ntile);
+        hipLaunchKernelGGL(add_offsets_kernel, dim3(static_cast<unsigned>(ntile)), dim3(kScanThreads), 0, stream,
+                           ptr + 1, n, bsum);
+    }
+    return hipGetLastError();
 }
 
 size_t transpose_workspace_bytes(int n_src)
@@ -243,13 +271,7 @@ hipError_t launch_transpose(int n_dst, int n_src, int64_t E, const int *row_ptr,
     if (E > 0)
         hipLaunchKernelGGL(hist_kernel, dim3(grid_for(E)), dim3(256), 0, stream, E, src, src_ptr + 1);
     if (n_src > 0) {
-        hipLaunchKernelGGL(scan_tiles_kernel, dim3(static_cast<unsigned>(ntile)), dim3(kScanThreads), 0, stream,
-                           src_ptr + 1, static_cast<int64_t>(n_src), bsum);
-        if (ntile > 1) {
-            hipLaunchKernelGGL(scan_single_kernel, dim3(1), dim3(kScanThreads), 0, stream, bsum, ntile);
-            hipLaunchKernelGGL(add_offsets_kernel, dim3(static_cast<unsigned>(ntile)), dim3(kScanThreads), 0, stream,
-                               src_ptr + 1, static_cast<int64_t>(n_src), bsum);
-        }
+        launch_counts_to_offsets(src_ptr, n_src, bsum, stream);
         hipLaunchKernelGGL(copy_kernel, dim3(grid_for(n_src)), dim3(256), 0, stream, cursor, src_ptr,
                            static_cast<int64_t>(n_src));
     }

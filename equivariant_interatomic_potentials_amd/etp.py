@@ -31,6 +31,7 @@ ETP_FLAG_VALIDATE = 2
 ABI_SYMBOLS = ("etp_plan_create", "etp_plan_destroy", "etp_plan_info", "etp_plan_tables",
                "etp_csr_transpose_workspace", "etp_csr_transpose", "etp_sh", "etp_edge_conv_fwd",
                "etp_edge_conv_vjp", "etp_edge_conv_vjp2", "etp_channel_mix", "etp_edge_forces",
+               "etp_neighbor_workspace", "etp_neighbor_count", "etp_neighbor_fill",
                "etp_status_string", "etp_version")
 
 
@@ -99,6 +100,9 @@ def _load():
                                     vp, u32, vp]),
         "etp_channel_mix": (st, [vp, i32, vp, vp, vp, u32, vp]),
         "etp_edge_forces": (st, [ctypes.POINTER(etp_graph), vp, vp, u32, vp]),
+        "etp_neighbor_workspace": (st, [i32, vp, ctypes.c_float, ctypes.POINTER(ctypes.c_size_t)]),
+        "etp_neighbor_count": (st, [i32, vp, vp, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]),
+        "etp_neighbor_fill": (st, [i32, vp, vp, ctypes.c_float, vp, i64, vp, vp, u32, vp, ctypes.c_size_t, vp]),
         "etp_status_string": (ctypes.c_char_p, [st]),
         "etp_version": (i32, []),
     }
@@ -344,3 +348,58 @@ def etp_edge_forces(graph: Graph, grad_vec, forces, flags: int = 0, stream=None)
     _check(lib.etp_edge_forces(ctypes.byref(g), _ptr(grad_vec, "grad_vec", torch.float32, 3 * E, optional=True),
                                _ptr(forces, "forces", torch.float32, 3 * n, optional=True), flags, _stream(stream)),
            "etp_edge_forces")
+
+
+def _box3(box):
+    """Box sides as a HOST float[3] (kept alive by the caller)."""
+    import numpy as np
+    return np.ascontiguousarray(np.broadcast_to(np.asarray(box, np.float32), (3,)))
+
+
+def etp_neighbor_workspace(n_atoms: int, box, cutoff: float) -> int:
+    b = ctypes.c_size_t()
+    bx = _box3(box)
+    _check(lib.etp_neighbor_workspace(n_atoms, bx.ctypes.data, float(cutoff), ctypes.byref(b)),
+           "etp_neighbor_workspace")
+    return b.value
+
+
+def etp_neighbor_count(pos, box, cutoff: float, row_ptr, ws, stream=None):
+    """row_ptr[n+1] of the periodic neighbour list of pos[n, 3] (float32 cutoff decision)."""
+    import torch
+    n = pos.shape[0]
+    bx = _box3(box)
+    _check(lib.etp_neighbor_count(n, _ptr(pos, "pos", torch.float32, 3 * n, optional=True), bx.ctypes.data,
+                                  float(cutoff), _ptr(row_ptr, "row_ptr", torch.int32, n + 1),
+                                  _ptr(ws, "ws", optional=True), ws.numel() * ws.element_size(), _stream(stream)),
+           "etp_neighbor_count")
+
+
+def etp_neighbor_fill(pos, box, cutoff: float, row_ptr, n_edges: int, src, vec, ws, flags: int = 0,
+                      stream=None):
+    """src[E] (ascending within each row) and vec[E, 3] (minimum image of pos[src] - pos[dst])."""
+    import torch
+    n = pos.shape[0]
+    bx = _box3(box)
+    _check(lib.etp_neighbor_fill(n, _ptr(pos, "pos", torch.float32, 3 * n, optional=True), bx.ctypes.data,
+                                 float(cutoff), _ptr(row_ptr, "row_ptr", torch.int32, n + 1), n_edges,
+                                 _ptr(src, "src", torch.int32, n_edges, optional=True),
+                                 _ptr(vec, "vec", torch.float32, 3 * n_edges, optional=True), flags,
+                                 _ptr(ws, "ws", optional=True), ws.numel() * ws.element_size(), _stream(stream)),
+           "etp_neighbor_fill")
+
+
+def neighbor_list(pos, box, cutoff: float, flags: int = 0, stream=None):
+    """Both calls with torch-allocated outputs: (row_ptr, src, vec) on pos's device.
+    Reads the edge count back to the host in between (synchronises the stream)."""
+    import torch
+    n = pos.shape[0]
+    dev = pos.device
+    ws = torch.empty(etp_neighbor_workspace(n, box, cutoff), dtype=torch.uint8, device=dev)
+    row_ptr = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    etp_neighbor_count(pos, box, cutoff, row_ptr, ws, stream)
+    E = int(row_ptr[n].item())
+    src = torch.empty(E, dtype=torch.int32, device=dev)
+    vec = torch.empty(E, 3, dtype=torch.float32, device=dev)
+    etp_neighbor_fill(pos, box, cutoff, row_ptr, E, src, vec, ws, flags, stream)
+    return row_ptr, src, vec

@@ -216,6 +216,43 @@ ETP_API etp_status etp_channel_mix(etp_plan_t plan, int32_t n_nodes, const float
 ETP_API etp_status etp_edge_forces(const etp_graph *g, const float *grad_vec, float *forces, uint32_t flags,
                                    void *stream);
 
+/* Periodic neighbour list: the destination-sorted CSR graph and bond vectors
+ * the convolution walks ("edges per atom" in "How does FlashCart make
+ * equivariant interatomic potentials faster and more accurate?", section on
+ * the SPICE-MACE-OFF model). For n_atoms atoms at pos (DEVICE float
+ * [n_atoms][3]) in an orthorhombic periodic box (box: HOST float[3], every
+ * side at least 2 * cutoff), row i lists every j != i with
+ *   q = p - L floor(p / L),  d = q_j - q_i,  d = d - L rint(d / L)   (per axis)
+ *   fma(dz, dz, fma(dy, dy, dx * dx)) < cutoff * cutoff
+ * evaluated in float32 exactly as written (correctly rounded division,
+ * round-half-even rint), sources ascending; vec of that edge = d (the
+ * minimum image of pos[j] - pos[i]). The edges are therefore bit-exact and
+ * deterministic. Two calls, because the edge count is known only on the
+ * device:
+ *   1. etp_neighbor_count writes row_ptr (DEVICE int32 [n_atoms + 1]); the
+ *      caller reads n_edges = row_ptr[n_atoms] (this needs the stream to
+ *      finish) and sizes src and vec;
+ *   2. etp_neighbor_fill, with the same pos, box and cutoff, writes src
+ *      (DEVICE int32 [n_edges]) and vec (DEVICE float [n_edges][3]); vec also
+ *      serves as scratch during the call.
+ * ws: DEVICE workspace of at least etp_neighbor_workspace() bytes (contents
+ * need not survive between the calls). Nothing is allocated, except that
+ * ETP_FLAG_VALIDATE (the only flag of the fill) checks row_ptr before the
+ * fill and, after it, that every row got exactly its count (positions that
+ * changed between the calls fail it), synchronising the stream; without it
+ * such rows hold -1 padding or are cut short, and their vec is NaN where the
+ * source is -1. Errors: INVALID_ARGUMENT (negative n_atoms or n_edges, null
+ * pointers, cutoff not positive and finite, box sides not positive and
+ * finite, other flags), UNSUPPORTED (a box side below 2 * cutoff, n_edges >=
+ * 2^31), WORKSPACE, INTERNAL (VALIDATE found a mismatch), HIP. The total
+ * edge count must stay below 2^31 (row_ptr is int32). */
+ETP_API etp_status etp_neighbor_workspace(int32_t n_atoms, const float *box, float cutoff, size_t *bytes);
+ETP_API etp_status etp_neighbor_count(int32_t n_atoms, const float *pos, const float *box, float cutoff,
+                                      int32_t *row_ptr, void *ws, size_t ws_bytes, void *stream);
+ETP_API etp_status etp_neighbor_fill(int32_t n_atoms, const float *pos, const float *box, float cutoff,
+                                     const int32_t *row_ptr, int64_t n_edges, int32_t *src, float *vec,
+                                     uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+
 ETP_API const char *etp_status_string(etp_status s);
 
 /* Version of this ABI (major * 10000 + minor * 100 + patch). */

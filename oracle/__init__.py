@@ -81,6 +81,8 @@ def _load():
         _f32p = ctypes.POINTER(ctypes.c_float)
         lib.oracle_neighbors.restype = ctypes.c_int64
         lib.oracle_neighbors.argtypes = [ctypes.c_int, _f32p, _f32p, ctypes.c_float, _i32p, _i32p, _f32p]
+        lib.oracle_neighbor_row.restype = ctypes.c_int
+        lib.oracle_neighbor_row.argtypes = [ctypes.c_int, _f32p, _f32p, ctypes.c_float, ctypes.c_int, _i32p, _f32p]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -263,6 +265,19 @@ def neighbors(pos, box, rc):
     lib.oracle_neighbors(n, _p(pos, f32p), _p(box, f32p), float(rc), _p(row_ptr, _i32p), _p(src, _i32p),
                          _p(vec, f32p))
     return row_ptr, src[:E], vec[:E]
+
+
+def neighbor_row(pos, box, rc, i):
+    """Row i of the periodic neighbour list: (src ascending, vec[k, 3])."""
+    f32p = ctypes.POINTER(ctypes.c_float)
+    pos = np.ascontiguousarray(pos, np.float32)
+    box = np.ascontiguousarray(np.broadcast_to(np.asarray(box, np.float32), (3,)))
+    n = pos.shape[0]
+    src = np.zeros(max(n, 1), np.int32)
+    vec = np.zeros((max(n, 1), 3), np.float32)
+    k = _load().oracle_neighbor_row(n, _p(pos, f32p), _p(box, f32p), float(rc), int(i), _p(src, _i32p),
+                                    _p(vec, f32p))
+    return src[:k], vec[:k]
 
 
 def _nz(a):

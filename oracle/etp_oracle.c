@@ -750,35 +750,44 @@ void oracle_edge_forces(int n_dst, int n_src, const int32_t *row_ptr, const int3
  * only when not NULL (then they must hold that many). */
 static float or_wrap(float p, float L) { return fmaf(-L, floorf(p / L), p); }
 
+/* Row i of the list: writes (when not NULL) its sources, ascending, and
+ * their vectors; returns the row length. */
+int oracle_neighbor_row(int n, const float *pos, const float *box, float rc, int i, int32_t *src, float *vec)
+{
+    const float rc2 = rc * rc;
+    float qi[3];
+    int k = 0;
+    for (int c = 0; c < 3; ++c)
+        qi[c] = or_wrap(pos[3 * i + c], box[c]);
+    for (int j = 0; j < n; ++j) {
+        if (j == i)
+            continue;
+        float d[3];
+        for (int c = 0; c < 3; ++c) {
+            const float dc = or_wrap(pos[3 * j + c], box[c]) - qi[c];
+            d[c] = fmaf(-box[c], rintf(dc / box[c]), dc);
+        }
+        const float r2 = fmaf(d[2], d[2], fmaf(d[1], d[1], d[0] * d[0]));
+        if (r2 < rc2) {
+            if (src)
+                src[k] = j;
+            if (vec)
+                for (int c = 0; c < 3; ++c)
+                    vec[3 * k + c] = d[c];
+            ++k;
+        }
+    }
+    return k;
+}
+
 int64_t oracle_neighbors(int n, const float *pos, const float *box, float rc, int32_t *row_ptr, int32_t *src,
                          float *vec)
 {
-    const float rc2 = rc * rc;
     int64_t e = 0;
     if (row_ptr)
         row_ptr[0] = 0;
     for (int i = 0; i < n; ++i) {
-        float qi[3];
-        for (int c = 0; c < 3; ++c)
-            qi[c] = or_wrap(pos[3 * i + c], box[c]);
-        for (int j = 0; j < n; ++j) {
-            if (j == i)
-                continue;
-            float d[3];
-            for (int c = 0; c < 3; ++c) {
-                const float dc = or_wrap(pos[3 * j + c], box[c]) - qi[c];
-                d[c] = fmaf(-box[c], rintf(dc / box[c]), dc);
-            }
-            const float r2 = fmaf(d[2], d[2], fmaf(d[1], d[1], d[0] * d[0]));
-            if (r2 < rc2) {
-                if (src)
-                    src[e] = j;
-                if (vec)
-                    for (int c = 0; c < 3; ++c)
-                        vec[3 * e + c] = d[c];
-                ++e;
-            }
-        }
+        e += oracle_neighbor_row(n, pos, box, rc, i, src ? src + e : NULL, vec ? vec + 3 * e : NULL);
         if (row_ptr)
             row_ptr[i + 1] = (int32_t)e;
     }

@@ -32,7 +32,7 @@ def header_symbols():
 
 def test_header_symbols_exported():
     names = header_symbols()
-    assert len(names) == 14
+    assert len(names) == 17
     assert sorted(etp.ABI_SYMBOLS) == names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (etp_\w+)$", out, flags=re.M))
@@ -145,6 +145,32 @@ def test_call_validation_without_device():
     assert lib.etp_edge_forces(ctypes.byref(g4), 8, 8, 0, None) == INV                 # no transpose
     assert lib.etp_edge_forces(ctypes.byref(g5), None, 8, 0, None) == INV
     assert lib.etp_edge_forces(ctypes.byref(g5), 8, 8, 4, None) == INV
+    box = np.array([20.0, 20.0, 30.0], np.float32)
+    bp = box.ctypes.data
+    nb = ctypes.c_size_t()
+    assert lib.etp_neighbor_workspace(1000, bp, 5.0, ctypes.byref(nb)) == 0 and nb.value >= 36 * 1000
+    nb2 = ctypes.c_size_t()
+    assert lib.etp_neighbor_workspace(2000, bp, 5.0, ctypes.byref(nb2)) == 0 and nb2.value > nb.value
+    assert lib.etp_neighbor_workspace(1000, bp, 10.5, ctypes.byref(nb2)) == UNS       # box < 2 rc
+    assert lib.etp_neighbor_workspace(1000, bp, 0.0, ctypes.byref(nb2)) == INV
+    assert lib.etp_neighbor_workspace(1000, bp, float("nan"), ctypes.byref(nb2)) == INV
+    assert lib.etp_neighbor_workspace(-1, bp, 5.0, ctypes.byref(nb2)) == INV
+    assert lib.etp_neighbor_workspace(1000, None, 5.0, ctypes.byref(nb2)) == INV
+    assert lib.etp_neighbor_workspace(1000, bp, 5.0, None) == INV
+    nanbox = np.array([20.0, np.nan, 30.0], np.float32)
+    assert lib.etp_neighbor_workspace(1000, nanbox.ctypes.data, 5.0, ctypes.byref(nb2)) == INV
+    assert lib.etp_neighbor_count(1000, 8, bp, 5.0, 8, 8, nb.value - 1, None) == WS
+    assert lib.etp_neighbor_count(1000, 8, bp, 5.0, 8, None, nb.value, None) == WS
+    assert lib.etp_neighbor_count(1000, None, bp, 5.0, 8, 8, nb.value, None) == INV
+    assert lib.etp_neighbor_count(1000, 8, bp, 5.0, None, 8, nb.value, None) == INV
+    assert lib.etp_neighbor_fill(1000, 8, bp, 5.0, 8, 100, 8, 8, 1, 8, nb.value, None) == INV   # ACCUMULATE
+    assert lib.etp_neighbor_fill(1000, 8, bp, 5.0, 8, -1, 8, 8, 0, 8, nb.value, None) == INV
+    assert lib.etp_neighbor_fill(1000, 8, bp, 5.0, 8, 2 ** 31, 8, 8, 0, 8, nb.value, None) == UNS
+    assert lib.etp_neighbor_fill(1000, 8, bp, 5.0, 8, 100, None, 8, 0, 8, nb.value, None) == INV
+    assert lib.etp_neighbor_fill(1000, 8, bp, 5.0, 8, 100, 8, None, 0, 8, nb.value, None) == INV
+    assert lib.etp_neighbor_fill(1000, 8, bp, 5.0, None, 100, 8, 8, 0, 8, nb.value, None) == INV
+    assert lib.etp_neighbor_fill(1000, 8, bp, 5.0, 8, 100, 8, 8, 0, 8, 16, None) == WS
+    assert lib.etp_neighbor_fill(1000, 8, bp, 12.0, 8, 100, 8, 8, 0, 8, nb.value, None) == UNS
     b = ctypes.c_size_t()
     assert lib.etp_csr_transpose_workspace(1000, ctypes.byref(b)) == 0 and b.value >= 4000
     assert lib.etp_csr_transpose_workspace(-1, ctypes.byref(b)) == INV

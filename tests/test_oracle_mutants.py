@@ -54,7 +54,7 @@ MUTANTS = [
      "d[c] = fmaf(-box[c], floorf(dc / box[c]), dc);"),
     ("nl_vec_sign", "const float dc = or_wrap(pos[3 * j + c], box[c]) - qi[c];",
      "const float dc = qi[c] - or_wrap(pos[3 * j + c], box[c]);"),
-    ("nl_self", "if (j == i)\n                continue;", "if (j == i && i < 0)\n                continue;"),
+    ("nl_self", "if (j == i)\n            continue;", "if (j == i && i < 0)\n            continue;"),
     ("nl_no_wrap", "qi[c] = or_wrap(pos[3 * i + c], box[c]);", "qi[c] = pos[3 * i + c];"),
     ("transpose_unstable", "int64_t k = cursor[src[e]]++;", "int64_t k = src_ptr[src[e] + 1] - 1 - (cursor[src[e]]++ - src_ptr[src[e]]);"),
 ]

@@ -108,6 +108,25 @@ def water_positions(seed: int, n_side: int = 12):
     return pos, box
 
 
+def gas_positions(n: int, box, seed: int, images: int = 1):
+    """n atoms uniform over [-images L, (1 + images) L) per axis (so most sit
+    outside the primary box), float32; box: one side or three."""
+    L = np.broadcast_to(np.asarray(box, np.float64), (3,))
+    u = rng(seed, "pos").random((n, 3))
+    return ((u * (2 * images + 1) - images) * L).astype(np.float32)
+
+
+def lattice_positions(n: int, box_units: int, seed: int, dup: int = 0):
+    """n atoms on a grid of spacing 1/8 (exact in float32) over three boxes of
+    box_units / 8 per axis, the last dup of them copies of earlier atoms
+    (coincident pairs)."""
+    g = rng(seed, "pos")
+    ip = g.integers(-box_units, 2 * box_units, size=(n, 3))
+    if dup:
+        ip[n - dup:] = ip[g.integers(0, n - dup, size=dup)]
+    return ip.astype(np.float32) / 8.0
+
+
 def diamond_positions(seed: int, n_side: int = 16, a: float = 3.567, sigma: float = 0.05):
     basis = np.array([[0, 0, 0], [0, .5, .5], [.5, 0, .5], [.5, .5, 0],
                       [.25, .25, .25], [.25, .75, .75], [.75, .25, .75], [.75, .75, .25]])
