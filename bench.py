@@ -168,6 +168,43 @@ def time_edge_forces(etp, g, gr, N, n_src, E, reps):
             "bound": "hbm"}
 
 
+def time_neighbor_list(etp, pos_np, box, rc, reps):
+    """Periodic neighbour list (outside the step): ms of the count call and of
+    the fill call; algorithmic bytes = positions in, row_ptr out (count) and
+    positions + row_ptr in, src + vec out (fill)."""
+    import torch
+    n = pos_np.shape[0]
+    pos = torch.from_numpy(np.ascontiguousarray(pos_np, np.float32)).cuda()
+    ws = torch.empty(etp.etp_neighbor_workspace(n, box, rc), dtype=torch.uint8, device="cuda")
+    rp = torch.empty(n + 1, dtype=torch.int32, device="cuda")
+    etp.etp_neighbor_count(pos, box, rc, rp, ws)
+    E = int(rp[n].item())
+    src = torch.empty(E, dtype=torch.int32, device="cuda")
+    vec = torch.empty(E, 3, device="cuda")
+    for _ in range(3):
+        etp.etp_neighbor_count(pos, box, rc, rp, ws)
+        etp.etp_neighbor_fill(pos, box, rc, rp, E, src, vec, ws)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tc = tf = 0.0
+    for _ in range(reps):
+        ev[0].record()
+        etp.etp_neighbor_count(pos, box, rc, rp, ws)
+        ev[1].record()
+        etp.etp_neighbor_fill(pos, box, rc, rp, E, src, vec, ws)
+        ev[2].record()
+        torch.cuda.synchronize()
+        tc += ev[0].elapsed_time(ev[1])
+        tf += ev[1].elapsed_time(ev[2])
+    tc, tf = tc / reps * 1e-3, tf / reps * 1e-3
+    bc = 12.0 * n + 4.0 * (n + 1)
+    bf = 12.0 * n + 4.0 * (n + 1) + 16.0 * E
+    return {"atoms": n, "edges": E, "cutoff": rc, "count_ms": round(tc * 1e3, 4), "fill_ms": round(tf * 1e3, 4),
+            "edges_per_s": E / (tc + tf), "fill_algo_GBps": bf / tf / 1e9,
+            "algo_GBps": (bc + bf) / (tc + tf) / 1e9, "hbm_frac": (bc + bf) / (tc + tf) / 1e9 / HBM_PEAK_GBS,
+            "bound": "alu"}
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """The oracle, as it is, on the first R destination rows of the graph
     (R sized to about budget_s of host time); edges/s of fwd + VJP + VJP2."""
@@ -321,6 +358,9 @@ def main(argv=None):
     }
     line["next_ops"] = {"channel_mix": time_channel_mix(etp, plan, out, L, C, N, a.steps),
                         "edge_forces": time_edge_forces(etp, g, gr, N, n_src, E, a.steps)}
+    for name, (pos_np, box) in (("neighbor_list_water", workloads.water_positions(0)),
+                                ("neighbor_list_diamond", workloads.diamond_positions(0))):
+        line["next_ops"][name] = time_neighbor_list(etp, pos_np, box, 6.0, a.steps)
     if not a.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)

@@ -28,6 +28,12 @@ namespace etp {
 constexpr int kScanThreads = 256, kScanItems = 8, kScanTile = kScanThreads * kScanItems;
 constexpr int kSortCap = 2048;
 
+// The fill and scan kernels serve several callers; TAG (kTagTranspose,
+// kTagNeighbors) only gives each caller its own kernel names, so that a
+// kernel trace attributes their time to the right step.
+constexpr int kTagTranspose = 0, kTagNeighbors = 1;
+
+template <int TAG>
 __global__ void __launch_bounds__(256) fill_kernel(int *__restrict__ p, int64_t n, int v)
 {
     for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
@@ -68,6 +74,7 @@ __device__ int block_inclusive_scan(int v, int *total)
 }
 
 // In-place inclusive scan of each tile of a[0, n); tile totals to bsum.
+template <int TAG>
 __global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(int *__restrict__ a, int64_t n, int *__restrict__ bsum)
 {
     const int64_t base = blockIdx.x * static_cast<int64_t>(kScanTile) + threadIdx.x * kScanItems;
@@ -89,6 +96,7 @@ __global__ void __launch_bounds__(kScanThreads) scan_tiles_kernel(int *__restric
 }
 
 // Single-block inclusive scan of b[0, n) in place.
+template <int TAG>
 __global__ void __launch_bounds__(kScanThreads) scan_single_kernel(int *__restrict__ b, int64_t n)
 {
     int carry = 0;
@@ -103,6 +111,7 @@ __global__ void __launch_bounds__(kScanThreads) scan_single_kernel(int *__restri
     }
 }
 
+template <int TAG>
 __global__ void __launch_bounds__(kScanThreads) add_offsets_kernel(int *__restrict__ a, int64_t n,
                                                                    const int *__restrict__ bsum)
 {
@@ -229,29 +238,41 @@ static unsigned grid_for(int64_t n)
 
 int64_t scan_bsum_ints(int64_t n) { return (n + kScanTile - 1) / kScanTile + 1; }
 
-hipError_t launch_fill_int(int *p, int64_t n, int v, hipStream_t stream)
+template <int TAG>
+static hipError_t fill_int(int *p, int64_t n, int v, hipStream_t stream)
 {
     if (n > 0)
-        hipLaunchKernelGGL(fill_kernel, dim3(grid_for(n)), dim3(256), 0, stream, p, n, v);
+        hipLaunchKernelGGL(fill_kernel<TAG>, dim3(grid_for(n)), dim3(256), 0, stream, p, n, v);
     return hipGetLastError();
+}
+
+hipError_t launch_nl_fill_int(int *p, int64_t n, int v, hipStream_t stream)
+{
+    return fill_int<kTagNeighbors>(p, n, v, stream);
 }
 
 // ptr[1..n] hold counts; on return ptr[k] = the sum of counts 1..k, i.e.
 // the offsets of a CSR when ptr[0] = 0 (ptr[0] is not touched). bsum holds
 // scan_bsum_ints(n) ints.
-hipError_t launch_counts_to_offsets(int *ptr, int64_t n, int *bsum, hipStream_t stream)
+template <int TAG>
+static hipError_t counts_to_offsets(int *ptr, int64_t n, int *bsum, hipStream_t stream)
 {
     if (n <= 0)
         return hipGetLastError();
     const int64_t ntile = (n + kScanTile - 1) / kScanTile;
-    hipLaunchKernelGGL(scan_tiles_kernel, dim3(static_cast<unsigned>(ntile)), dim3(kScanThreads), 0, stream, ptr + 1,
-                       n, bsum);
+    hipLaunchKernelGGL(scan_tiles_kernel<TAG>, dim3(static_cast<unsigned>(ntile)), dim3(kScanThreads), 0, stream,
+                       ptr + 1, n, bsum);
     if (ntile > 1) {
-        hipLaunchKernelGGL(scan_single_kernel, dim3(1), dim3(kScanThreads), 0, stream, bsum, ntile);
-        hipLaunchKernelGGL(add_offsets_kernel, dim3(static_cast<unsigned>(ntile)), dim3(kScanThreads), 0, stream,
-                           ptr + 1, n, bsum);
+        hipLaunchKernelGGL(scan_single_kernel<TAG>, dim3(1), dim3(kScanThreads), 0, stream, bsum, ntile);
+        hipLaunchKernelGGL(add_offsets_kernel<TAG>, dim3(static_cast<unsigned>(ntile)), dim3(kScanThreads), 0,
+                           stream, ptr + 1, n, bsum);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_nl_counts_to_offsets(int *ptr, int64_t n, int *bsum, hipStream_t stream)
+{
+    return counts_to_offsets<kTagNeighbors>(ptr, n, bsum, stream);
 }
 
 size_t transpose_workspace_bytes(int n_src)
@@ -266,12 +287,11 @@ hipError_t launch_transpose(int n_dst, int n_src, int64_t E, const int *row_ptr,
     int *cursor = static_cast<int *>(ws);
     const int64_t ntile = (static_cast<int64_t>(n_src) + kScanTile - 1) / kScanTile;
     int *bsum = cursor + n_src;
-    hipLaunchKernelGGL(fill_kernel, dim3(grid_for(n_src + 1)), dim3(256), 0, stream, src_ptr,
-                       static_cast<int64_t>(n_src) + 1, 0);
+    fill_int<kTagTranspose>(src_ptr, static_cast<int64_t>(n_src) + 1, 0, stream);
     if (E > 0)
         hipLaunchKernelGGL(hist_kernel, dim3(grid_for(E)), dim3(256), 0, stream, E, src, src_ptr + 1);
     if (n_src > 0) {
-        launch_counts_to_offsets(src_ptr, n_src, bsum, stream);
+        counts_to_offsets<kTagTranspose>(src_ptr, n_src, bsum, stream);
         hipLaunchKernelGGL(copy_kernel, dim3(grid_for(n_src)), dim3(256), 0, stream, cursor, src_ptr,
                            static_cast<int64_t>(n_src));
     }

@@ -45,8 +45,8 @@
 
 namespace etp {
 
-hipError_t launch_fill_int(int *p, int64_t n, int v, hipStream_t stream);
-hipError_t launch_counts_to_offsets(int *ptr, int64_t n, int *bsum, hipStream_t stream);
+hipError_t launch_nl_fill_int(int *p, int64_t n, int v, hipStream_t stream);
+hipError_t launch_nl_counts_to_offsets(int *ptr, int64_t n, int *bsum, hipStream_t stream);
 int64_t scan_bsum_ints(int64_t n);
 
 constexpr int kNlMaxCellsAxis = 128;
@@ -305,11 +305,11 @@ static NlWork nl_carve(void *ws, int n, const NlGeom &g)
 // steps 1-2
 static hipError_t nl_bin(int n, const float *pos, const NlGeom &g, const NlWork &w, hipStream_t stream)
 {
-    hipError_t e = launch_fill_int(w.cell_start, g.ncell + 1, 0, stream);
+    hipError_t e = launch_nl_fill_int(w.cell_start, g.ncell + 1, 0, stream);
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(nl_bin_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, n, pos, g, w);
-    if ((e = launch_counts_to_offsets(w.cell_start, g.ncell, w.bsum, stream)) != hipSuccess)
+    if ((e = launch_nl_counts_to_offsets(w.cell_start, g.ncell, w.bsum, stream)) != hipSuccess)
         return e;
     hipLaunchKernelGGL(nl_scatter_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, n, w);
     return hipGetLastError();
@@ -318,7 +318,7 @@ static hipError_t nl_bin(int n, const float *pos, const NlGeom &g, const NlWork 
 hipError_t launch_neighbor_count(int n, const float *pos, const float *box, float rc, int *row_ptr, void *ws,
                                  hipStream_t stream)
 {
-    hipError_t e = launch_fill_int(row_ptr, 1, 0, stream);
+    hipError_t e = launch_nl_fill_int(row_ptr, 1, 0, stream);
     if (e != hipSuccess || n == 0)
         return e;
     const NlGeom g = nl_geom(box, rc);
@@ -329,7 +329,7 @@ hipError_t launch_neighbor_count(int n, const float *pos, const float *box, floa
                        static_cast<int *>(nullptr));
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    return launch_counts_to_offsets(row_ptr, n, w.bsum, stream);
+    return launch_nl_counts_to_offsets(row_ptr, n, w.bsum, stream);
 }
 
 hipError_t launch_neighbor_fill(int n, const float *pos, const float *box, float rc, const int *row_ptr,
@@ -338,7 +338,7 @@ hipError_t launch_neighbor_fill(int n, const float *pos, const float *box, float
     const NlGeom g = nl_geom(box, rc);
     const NlWork w = nl_carve(ws, n, g);
     *bad = w.bad;
-    hipError_t e = launch_fill_int(w.bad, 1, 0, stream);
+    hipError_t e = launch_nl_fill_int(w.bad, 1, 0, stream);
     if (e != hipSuccess || n == 0)
         return e;
     if ((e = nl_bin(n, pos, g, w, stream)) != hipSuccess)
