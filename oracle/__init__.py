@@ -83,6 +83,8 @@ def _load():
         lib.oracle_neighbors.argtypes = [ctypes.c_int, _f32p, _f32p, ctypes.c_float, _i32p, _i32p, _f32p]
         lib.oracle_neighbor_row.restype = ctypes.c_int
         lib.oracle_neighbor_row.argtypes = [ctypes.c_int, _f32p, _f32p, ctypes.c_float, ctypes.c_int, _i32p, _f32p]
+        lib.oracle_node_product.restype = ctypes.c_int
+        lib.oracle_node_product.argtypes = [ctypes.c_int] * 4 + [_f64p, _f64p, _f64p]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -265,6 +267,19 @@ def neighbors(pos, box, rc):
     lib.oracle_neighbors(n, _p(pos, f32p), _p(box, f32p), float(rc), _p(row_ptr, _i32p), _p(src, _i32p),
                          _p(vec, f32p))
     return row_ptr, src[:E], vec[:E]
+
+
+def node_product(L, A, W, nu):
+    """Node-local correlation product: out[n, (L+1)^2, C] = B_1 + ... + B_nu with
+    B_1 = A and B_{k+1} = sum_p W[k-1, p] * CG_p(B_k, A), channel-wise."""
+    A = np.ascontiguousarray(A, np.float64)
+    n, D, C = A.shape
+    assert D == (L + 1) ** 2
+    W = np.ascontiguousarray(np.zeros((1,)) if W is None else W, np.float64)
+    out = np.zeros_like(A)
+    if _load().oracle_node_product(L, C, n, nu, _p(A, _f64p), _p(W, _f64p), _p(out, _f64p)):
+        raise ValueError("bad arguments")
+    return out
 
 
 def neighbor_row(pos, box, rc, i):

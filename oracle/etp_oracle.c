@@ -733,6 +733,62 @@ void oracle_edge_forces(int n_dst, int n_src, const int32_t *row_ptr, const int3
 }
 
 /* ------------------------------------------------------------------------ */
+/* Node-local correlation product                                            */
+/* ------------------------------------------------------------------------ */
+
+/* The node-local product ladder of "How does FlashCart make equivariant
+ * interatomic potentials faster and more accurate?" (section "Generated
+ * kernels beat SH baselines at high order"): weighted products applied step
+ * by step, each result truncated to orders <= L. The page gives no formula;
+ * the reading here, channel by channel (channel u only meets channel u):
+ *   B_1 = A
+ *   B_{k+1}[l3, m3, u] = sum over paths p = (l1, l2, l3) of W[k-1][p][u]
+ *                        sum_{(m1, m2, m3)} C_p[m1, m2, m3] B_k[l1, m1, u] A[l2, m2, u]
+ *   out = B_1 + B_2 + ... + B_nu
+ * with the convolution's path list and real CG (l1, l2, l3 <= L). A and out
+ * have the node-feature layout [n][(L+1)^2][C]; W is [nu-1][P][C]. */
+int oracle_node_product(int L, int C, int n, int nu, const double *A, const double *W, double *out)
+{
+    table t;
+    if (nu < 1 || table_make(L, L, L, &t))
+        return -1;
+    const int D = (L + 1) * (L + 1), P = t.P;
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < n; ++i) {
+        double *B = (double *)malloc(sizeof(double) * D * C);
+        double *NB = (double *)malloc(sizeof(double) * D * C);
+        const double *Ai = A + (int64_t)i * D * C;
+        double *oi = out + (int64_t)i * D * C;
+        for (int q = 0; q < D * C; ++q) {
+            B[q] = Ai[q];
+            oi[q] = Ai[q];
+        }
+        for (int k = 1; k < nu; ++k) {
+            for (int q = 0; q < D * C; ++q)
+                NB[q] = 0.0;
+            for (int p = 0; p < P; ++p) {
+                const int l1 = t.path[3 * p], l2 = t.path[3 * p + 1], l3 = t.path[3 * p + 2];
+                const double *Wp = W + ((int64_t)(k - 1) * P + p) * C;
+                for (int q = t.ptr[p]; q < t.ptr[p + 1]; ++q) {
+                    const int r1 = l1 * l1 + l1 + t.m[3 * q], r2 = l2 * l2 + l2 + t.m[3 * q + 1];
+                    const int r3 = l3 * l3 + l3 + t.m[3 * q + 2];
+                    for (int u = 0; u < C; ++u)
+                        NB[r3 * C + u] += Wp[u] * t.val[q] * B[r1 * C + u] * Ai[r2 * C + u];
+                }
+            }
+            for (int q = 0; q < D * C; ++q) {
+                B[q] = NB[q];
+                oi[q] += NB[q];
+            }
+        }
+        free(B);
+        free(NB);
+    }
+    table_free(&t);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Neighbour list                                                            */
 /* ------------------------------------------------------------------------ */
 

@@ -18,7 +18,7 @@ PINS = [os.path.join(ROOT, "tests", "test_oracle_sh_cg.py"),
         os.path.join(ROOT, "tests", "test_oracle_conv.py")]
 # the pin files of the layers outside the convolution, by mutant name prefix
 EXTRA_PINS = {"mix_": "test_oracle_mix.py", "forces_": "test_oracle_forces.py",
-              "nl_": "test_oracle_neighbors.py"}
+              "nl_": "test_oracle_neighbors.py", "np_": "test_oracle_node_product.py"}
 
 # (name, exact text in the oracle, replacement)
 MUTANTS = [
@@ -56,6 +56,14 @@ MUTANTS = [
      "const float dc = qi[c] - or_wrap(pos[3 * j + c], box[c]);"),
     ("nl_self", "if (j == i)\n            continue;", "if (j == i && i < 0)\n            continue;"),
     ("nl_no_wrap", "qi[c] = or_wrap(pos[3 * i + c], box[c]);", "qi[c] = pos[3 * i + c];"),
+    ("np_weight_step", "const double *Wp = W + ((int64_t)(k - 1) * P + p) * C;",
+     "const double *Wp = W + ((int64_t)(nu - 1 - k) * P + p) * C;"),
+    ("np_operands_swapped", "NB[r3 * C + u] += Wp[u] * t.val[q] * B[r1 * C + u] * Ai[r2 * C + u];",
+     "NB[r3 * C + u] += Wp[u] * t.val[q] * Ai[r1 * C + u] * B[r2 * C + u];"),
+    ("np_square_of_B", "NB[r3 * C + u] += Wp[u] * t.val[q] * B[r1 * C + u] * Ai[r2 * C + u];",
+     "NB[r3 * C + u] += Wp[u] * t.val[q] * B[r1 * C + u] * B[r2 * C + u];"),
+    ("np_last_only", "                oi[q] += NB[q];", "                oi[q] = NB[q];"),
+    ("np_m3_sign", "const int r3 = l3 * l3 + l3 + t.m[3 * q + 2];", "const int r3 = l3 * l3 + l3 - t.m[3 * q + 2];"),
     ("transpose_unstable", "int64_t k = cursor[src[e]]++;", "int64_t k = src_ptr[src[e] + 1] - 1 - (cursor[src[e]]++ - src_ptr[src[e]]);"),
 ]
 

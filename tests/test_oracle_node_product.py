@@ -1,0 +1,115 @@
+"""Pins for the oracle's node-local correlation product (the weighted product
+ladder B_{k+1} = sum_p W_k[p] CG_p(B_k, A), out = B_1 + ... + B_nu):
+
+  * nu = 1 is the identity;
+  * l_max = 0 and inputs with only l = 0 are scalar polynomials in closed form;
+  * a pure vector input at nu = 2: the l = 0 block is -W |a|^2 / sqrt3, the
+    l = 1 block keeps only a (a x a = 0), and the l = 2 block carries the rest
+    of |a|^4 (the coupling is orthogonal);
+  * the whole ladder against a dense recursion whose CG comes from sympy;
+  * rotation equivariance.
+"""
+import math
+
+import numpy as np
+import pytest
+from scipy.spatial.transform import Rotation
+
+import oracle
+from test_oracle_conv import _library_dense_cg, _wigner_D
+
+
+def paths(L):
+    return [tuple(int(v) for v in p) for p in oracle.paths(L)]
+
+
+def test_order_one_is_identity():
+    A = np.random.default_rng(0).standard_normal((4, 16, 3))
+    assert np.array_equal(oracle.node_product(3, A, None, 1), A)
+
+
+@pytest.mark.parametrize("nu", [2, 3, 5])
+def test_scalar_closed_form(nu):
+    """l_max = 0: B_{k+1} = W_k B_k a, so out = sum_k (prod_{j<k} W_j) a^k."""
+    g = np.random.default_rng(nu)
+    A = g.standard_normal((6, 1, 4))
+    W = g.standard_normal((nu - 1, 1, 4))
+    out = oracle.node_product(0, A, W, nu)
+    a = A[:, 0, :]
+    want, term = a.copy(), a.copy()
+    for k in range(nu - 1):
+        term = W[k, 0] * term * a
+        want += term
+    np.testing.assert_allclose(out[:, 0, :], want, rtol=1e-13, atol=1e-13)
+
+
+def test_scalar_input_stays_scalar():
+    """Only l = 0 populated at l_max = 2: the ladder only uses the (0, 0, 0) path."""
+    g = np.random.default_rng(1)
+    A = np.zeros((5, 9, 3))
+    A[:, 0, :] = g.standard_normal((5, 3))
+    W = g.standard_normal((3, 15, 3))
+    out = oracle.node_product(2, A, W, 4)
+    p000 = paths(2).index((0, 0, 0))
+    a = A[:, 0, :]
+    want, term = a.copy(), a.copy()
+    for k in range(3):
+        term = W[k, p000] * term * a
+        want += term
+    np.testing.assert_allclose(out[:, 0, :], want, rtol=1e-13, atol=1e-13)
+    assert np.abs(out[:, 1:, :]).max() == 0.0
+
+
+def test_pure_vector_order_two():
+    g = np.random.default_rng(2)
+    n, C = 6, 3
+    A = np.zeros((n, 9, C))
+    A[:, 1:4, :] = g.standard_normal((n, 3, C))
+    W = g.standard_normal((1, 15, C))
+    out = oracle.node_product(2, A, W, 2)
+    P = paths(2)
+    a2 = (A[:, 1:4, :] ** 2).sum(axis=1)                       # |a|^2 per (node, channel)
+    np.testing.assert_allclose(out[:, 0, :], -W[0, P.index((1, 1, 0))] * a2 / math.sqrt(3), atol=1e-13)
+    np.testing.assert_allclose(out[:, 1:4, :], A[:, 1:4, :], atol=1e-13)   # a x a = 0
+    l2 = out[:, 4:9, :] / W[0, P.index((1, 1, 2))]
+    np.testing.assert_allclose((l2 ** 2).sum(axis=1), 2.0 / 3.0 * a2 ** 2, rtol=1e-12)
+
+
+@pytest.mark.parametrize("L,nu", [(1, 4), (2, 3)])
+def test_ladder_against_sympy_recursion(L, nu):
+    g = np.random.default_rng(10 + L)
+    n, C = 3, 2
+    D = (L + 1) ** 2
+    A = g.standard_normal((n, D, C))
+    W = g.standard_normal((nu - 1, len(paths(L)), C))
+    out = oracle.node_product(L, A, W, nu)
+    T = {p: _library_dense_cg(*p) for p in paths(L)}
+    B, want = A.copy(), A.copy()
+    for k in range(nu - 1):
+        nb = np.zeros_like(A)
+        for q, (l1, l2, l3) in enumerate(paths(L)):
+            nb[:, l3 * l3:(l3 + 1) ** 2] += W[k, q] * np.einsum(
+                "abc,nau,nbu->ncu", T[(l1, l2, l3)], B[:, l1 * l1:(l1 + 1) ** 2], A[:, l2 * l2:(l2 + 1) ** 2])
+        B = nb
+        want += B
+    np.testing.assert_allclose(out, want, rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("L", [2, 3])
+def test_rotation_equivariance(L):
+    g = np.random.default_rng(20 + L)
+    n, C, nu = 4, 3, 4
+    D = (L + 1) ** 2
+    A = g.standard_normal((n, D, C)) * 0.5
+    W = g.standard_normal((nu - 1, len(paths(L)), C))
+    R = Rotation.random(random_state=30 + L).as_matrix()
+
+    def rot(x):
+        y = np.empty_like(x)
+        for l in range(L + 1):
+            y[:, l * l:(l + 1) ** 2] = np.einsum("ab,nbu->nau", _wigner_D(l, R), x[:, l * l:(l + 1) ** 2])
+        return y
+
+    lhs = oracle.node_product(L, rot(A), W, nu)
+    rhs = rot(oracle.node_product(L, A, W, nu))
+    np.testing.assert_allclose(lhs, rhs, atol=1e-9 * np.abs(rhs).max())
