@@ -205,6 +205,43 @@ def time_neighbor_list(etp, pos_np, box, rc, reps):
             "bound": "alu"}
 
 
+def time_node_product(etp, L, nu, reps, n=4096, C=128):
+    """Node-local correlation product (outside the step) at the FlashCart
+    page's node-local benchmark size: ms per call and VALU FLOPs per call =
+    n C (nu - 1) (n_prod + 2 nnz + 2 Dout + D): one product B[l1, m1] A[l2, m2]
+    per distinct (l1, m1, l2, m2) of the CG table (shared by the paths that
+    differ only in l3), one FMA per CG entry, one FMA per output row of a path
+    for its weight, one add per row of the running sum."""
+    import torch
+    import workloads
+    plan = etp.etp_plan_create(L, C)
+    tb = etp.etp_plan_tables(plan)
+    prods = set()
+    for p, (l1, l2, _) in enumerate(tb["paths"]):
+        for m1, m2, _ in tb["cg_m"][tb["cg_ptr"][p]:tb["cg_ptr"][p + 1]]:
+            prods.add((int(l1), int(m1), int(l2), int(m2)))
+    nnz, dout, D = len(tb["cg_val"]), int(tb["out_off"][-1]), (L + 1) ** 2
+    A_np, W_np = workloads.node_features(n, L, C, nu, seed=0)
+    A = torch.from_numpy(A_np).cuda()
+    W = torch.from_numpy(W_np).cuda()
+    out = torch.empty_like(A)
+    for _ in range(3):
+        etp.etp_node_product(plan, A, W, out, nu)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        etp.etp_node_product(plan, A, W, out, nu)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / reps * 1e-3
+    flops = float(n) * C * (nu - 1) * (len(prods) + 2 * nnz + 2 * dout + D)
+    byts = 4.0 * (2 * n * D * C + (nu - 1) * len(tb["paths"]) * C)
+    return {"nodes": n, "channels": C, "l_max": L, "corr_order": nu, "ms": round(t * 1e3, 4),
+            "algo_TFLOPs": flops / t / 1e12, "valu_frac": flops / t / 1e12 / VALU_PEAK_TFLOPS,
+            "algo_GBps": byts / t / 1e9, "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS, "bound": "alu"}
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """The oracle, as it is, on the first R destination rows of the graph
     (R sized to about budget_s of host time); edges/s of fwd + VJP + VJP2."""
@@ -361,6 +398,8 @@ def main(argv=None):
     for name, (pos_np, box) in (("neighbor_list_water", workloads.water_positions(0)),
                                 ("neighbor_list_diamond", workloads.diamond_positions(0))):
         line["next_ops"][name] = time_neighbor_list(etp, pos_np, box, 6.0, a.steps)
+    for Lp, nu in ((3, 4), (4, 6)):
+        line["next_ops"][f"node_product_l{Lp}_nu{nu}"] = time_node_product(etp, Lp, nu, a.steps)
     if not a.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)

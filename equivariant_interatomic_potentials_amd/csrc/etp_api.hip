@@ -16,6 +16,8 @@ namespace etp {
 hipError_t launch_sh(int L, int64_t n, const float *vec, float *Y, float *dY, hipStream_t stream);
 hipError_t launch_mix(int L, int C, int n, const float *in, const float *W, float *y, bool accumulate,
                       hipStream_t stream);
+hipError_t launch_node_product(int L, int C, int n, int nu, const float *A, const float *W, float *out,
+                               bool accumulate, hipStream_t stream);
 hipError_t launch_forces(int n_dst, int n_src, const int *row_ptr, const int *src_ptr, const int *perm,
                          const float *gr, float *F, bool accumulate, hipStream_t stream);
 size_t transpose_workspace_bytes(int n_src);
@@ -425,6 +427,23 @@ etp_status etp_channel_mix(etp_plan_t plan, int32_t n_nodes, const float *in, co
         return ETP_ERR_INVALID_ARGUMENT;
     return hip_status(etp::launch_mix(plan->L, plan->C, n_nodes, in, W, out, flags & ETP_FLAG_ACCUMULATE,
                                       static_cast<hipStream_t>(stream)));
+}
+
+etp_status etp_node_product(etp_plan_t plan, int32_t n_nodes, int32_t corr_order, const float *A, const float *W,
+                            float *out, uint32_t flags, void *stream)
+{
+    if (!plan || n_nodes < 0 || corr_order < 1 || corr_order > 8)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (flags & ~static_cast<uint32_t>(ETP_FLAG_ACCUMULATE))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (plan->dtype != ETP_F32)
+        return ETP_ERR_UNSUPPORTED;
+    if (n_nodes == 0)
+        return ETP_OK;
+    if (!A || !out || (corr_order > 1 && !W))
+        return ETP_ERR_INVALID_ARGUMENT;
+    return hip_status(etp::launch_node_product(plan->L, plan->C, n_nodes, corr_order, A, W, out,
+                                               flags & ETP_FLAG_ACCUMULATE, static_cast<hipStream_t>(stream)));
 }
 
 etp_status etp_edge_forces(const etp_graph *g, const float *grad_vec, float *forces, uint32_t flags, void *stream)

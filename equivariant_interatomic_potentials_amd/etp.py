@@ -31,7 +31,7 @@ ETP_FLAG_VALIDATE = 2
 ABI_SYMBOLS = ("etp_plan_create", "etp_plan_destroy", "etp_plan_info", "etp_plan_tables",
                "etp_csr_transpose_workspace", "etp_csr_transpose", "etp_sh", "etp_edge_conv_fwd",
                "etp_edge_conv_vjp", "etp_edge_conv_vjp2", "etp_channel_mix", "etp_edge_forces",
-               "etp_neighbor_workspace", "etp_neighbor_count", "etp_neighbor_fill",
+               "etp_neighbor_workspace", "etp_neighbor_count", "etp_neighbor_fill", "etp_node_product",
                "etp_status_string", "etp_version")
 
 
@@ -100,6 +100,7 @@ def _load():
                                     vp, u32, vp]),
         "etp_channel_mix": (st, [vp, i32, vp, vp, vp, u32, vp]),
         "etp_edge_forces": (st, [ctypes.POINTER(etp_graph), vp, vp, u32, vp]),
+        "etp_node_product": (st, [vp, i32, i32, vp, vp, vp, u32, vp]),
         "etp_neighbor_workspace": (st, [i32, vp, ctypes.c_float, ctypes.POINTER(ctypes.c_size_t)]),
         "etp_neighbor_count": (st, [i32, vp, vp, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]),
         "etp_neighbor_fill": (st, [i32, vp, vp, ctypes.c_float, vp, i64, vp, vp, u32, vp, ctypes.c_size_t, vp]),
@@ -348,6 +349,17 @@ def etp_edge_forces(graph: Graph, grad_vec, forces, flags: int = 0, stream=None)
     _check(lib.etp_edge_forces(ctypes.byref(g), _ptr(grad_vec, "grad_vec", torch.float32, 3 * E, optional=True),
                                _ptr(forces, "forces", torch.float32, 3 * n, optional=True), flags, _stream(stream)),
            "etp_edge_forces")
+
+
+def etp_node_product(plan: Plan, A, W, out, corr_order: int, flags: int = 0, stream=None):
+    """out[n, (L+1)^2, C] = B_1 + ... + B_nu, B_1 = A, B_{k+1} = sum_p W[k-1, p] * CG_p(B_k, A)."""
+    import torch
+    n = A.shape[0]
+    D, C = plan.din_rows, plan.C
+    _check(lib.etp_node_product(plan.handle, n, corr_order, _ptr(A, "A", torch.float32, n * D * C, optional=True),
+                                _ptr(W, "W", torch.float32, (corr_order - 1) * plan.P * C, optional=True),
+                                _ptr(out, "out", torch.float32, n * D * C, optional=True), flags,
+                                _stream(stream)), "etp_node_product")
 
 
 def _box3(box):

@@ -201,6 +201,26 @@ ETP_API etp_status etp_edge_conv_vjp2(etp_plan_t plan, const etp_graph *g, const
 ETP_API etp_status etp_channel_mix(etp_plan_t plan, int32_t n_nodes, const float *in, const float *W, float *out,
                                    uint32_t flags, void *stream);
 
+/* Node-local correlation product: weighted products of each node's irreps
+ * with themselves, applied step by step and truncated to orders <= l_max
+ * after every step (the node-local product ladder of "How does FlashCart
+ * make equivariant interatomic potentials faster and more accurate?",
+ * section "Generated kernels beat SH baselines at high order"; the page
+ * gives no formula, this is the channel-wise reading):
+ *   B_1 = A,
+ *   B_{k+1}[i][l3*l3 + l3 + m3][u] = sum_{p = (l1, l2, l3)} W[k-1][p][u]
+ *        sum_{(m1, m2, m3)} C_p[m1, m2, m3] B_k[i][l1 row, m1][u] A[i][l2 row, m2][u],
+ *   out = B_1 + ... + B_nu                    (nu = corr_order, in [1, 8])
+ * over the plan's paths and real CG table (l1, l2, l3 <= l_max).
+ * A, out: DEVICE float [n_nodes][(l_max+1)^2][C]; W: DEVICE float
+ * [corr_order-1][P][C] (may be NULL when corr_order is 1). fp32 throughout;
+ * the plan must be ETP_F32. flags: ETP_FLAG_ACCUMULATE adds into out. Nothing
+ * is allocated. Errors: INVALID_ARGUMENT (null plan or pointers, negative
+ * n_nodes, corr_order outside [1, 8], other flags), UNSUPPORTED (a bf16
+ * plan), HIP. */
+ETP_API etp_status etp_node_product(etp_plan_t plan, int32_t n_nodes, int32_t corr_order, const float *A,
+                                    const float *W, float *out, uint32_t flags, void *stream);
+
 /* Forces on the atoms from the per-edge energy gradient grad_vec = dE/dvec
  * (the VJP's grad_vec), with vec_e = pos[src_e] - pos[dst_e]:
  *   forces[k] = sum_{e in in(k)} grad_vec[e] - sum_{e in out(k)} grad_vec[e]

@@ -108,6 +108,15 @@ def water_positions(seed: int, n_side: int = 12):
     return pos, box
 
 
+def node_features(n: int, L: int, C: int, nu: int, seed: int = 0):
+    """Inputs of the node-local product: A[n, (L+1)^2, C] ~ N(0, 0.5^2) and
+    W[nu-1, P, C] ~ N(0, 1/P) (float32)."""
+    A = (0.5 * rng(seed, "x").standard_normal((n, (L + 1) ** 2, C))).astype(np.float32)
+    P = _n_paths(L)
+    W = (rng(seed, "w").standard_normal((max(nu - 1, 0), P, C)) / np.sqrt(P)).astype(np.float32)
+    return A, W
+
+
 def gas_positions(n: int, box, seed: int, images: int = 1):
     """n atoms uniform over [-images L, (1 + images) L) per axis (so most sit
     outside the primary box), float32; box: one side or three."""
