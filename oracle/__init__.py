@@ -269,6 +269,21 @@ def neighbors(pos, box, rc):
     return row_ptr, src[:E], vec[:E]
 
 
+def edge_tp_fwd(L, vec, V, w):
+    """Edge-local tensor product: the convolution with every edge its own
+    destination and source (out[E, Dout, C], no destination sum)."""
+    E = np.asarray(vec).reshape(-1, 3).shape[0]
+    ar = np.arange(E + 1, dtype=np.int32)
+    return fwd(L, ar, ar[:E], vec, V, w)
+
+
+def edge_tp_vjp(L, vec, V, w, G):
+    """(gV, gw, gr) of the edge-local tensor product."""
+    E = np.asarray(vec).reshape(-1, 3).shape[0]
+    ar = np.arange(E + 1, dtype=np.int32)
+    return vjp(L, ar, ar[:E], vec, V, w, G)
+
+
 def node_product(L, A, W, nu):
     """Node-local correlation product: out[n, (L+1)^2, C] = B_1 + ... + B_nu with
     B_1 = A and B_{k+1} = sum_p W[k-1, p] * CG_p(B_k, A), channel-wise."""
