@@ -205,6 +205,40 @@ def time_neighbor_list(etp, pos_np, box, rc, reps):
             "bound": "alu"}
 
 
+def time_edge_tp(etp, plan, L, C, E, Din, P, Dout, vec, w, reps):
+    """Edge-local tensor product on the step's edges (outside the step): ms of
+    the forward and of the VJP (gV, gw, gr); algorithmic bytes = every input
+    and output once (fwd: vec, V, w, out; VJP: vec, V, w, G, gV, gw, gr)."""
+    import torch
+    import workloads
+    V = workloads.device_normal((E, Din, C), 3, "x", 8192)
+    G = workloads.device_normal((E, Dout, C), 4, "G", 8192)
+    out = torch.empty(E, Dout, C, device="cuda")
+    gV, gw, gr = torch.empty_like(V), torch.empty_like(w), torch.empty(E, 3, device="cuda")
+    res = {}
+    for name, f, byts in (
+            ("fwd", lambda: etp.etp_edge_tp_fwd(plan, vec, V, w, out), 4.0 * E * (3 + Din * C + P * C + Dout * C)),
+            ("vjp", lambda: etp.etp_edge_tp_vjp(plan, vec, V, w, G, gV, gw, gr),
+             4.0 * E * (6 + 2 * Din * C + 2 * P * C + Dout * C))):
+        for _ in range(2):
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) / reps * 1e-3
+        res[name + "_ms"] = round(t * 1e3, 4)
+        res[name + "_algo_GBps"] = byts / t / 1e9
+        res[name + "_hbm_frac"] = byts / t / 1e9 / HBM_PEAK_GBS
+    res.update({"edges": E, "l_max": L, "channels": C, "bound": "hbm"})
+    del V, G, out, gV, gw, gr
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_node_product(etp, L, nu, reps, n=4096, C=128):
     """Node-local correlation product (outside the step) at the FlashCart
     page's node-local benchmark size: ms per call and VALU FLOPs per call =
@@ -398,6 +432,7 @@ def main(argv=None):
     for name, (pos_np, box) in (("neighbor_list_water", workloads.water_positions(0)),
                                 ("neighbor_list_diamond", workloads.diamond_positions(0))):
         line["next_ops"][name] = time_neighbor_list(etp, pos_np, box, 6.0, a.steps)
+    line["next_ops"]["edge_tp"] = time_edge_tp(etp, plan, L, C, E, (L + 1) ** 2, wl.P, wl.Dout, vec, w, a.steps)
     for Lp, nu in ((3, 4), (4, 6)):
         line["next_ops"][f"node_product_l{Lp}_nu{nu}"] = time_node_product(etp, Lp, nu, a.steps)
     if not a.no_cpu:

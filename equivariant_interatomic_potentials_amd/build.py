@@ -37,7 +37,7 @@ CFLAGS = [
 def units():
     """(source, object, extra flags) for every translation unit."""
     out = []
-    for name in ("etp_api", "etp_sh", "etp_graph", "etp_mix", "etp_forces", "etp_neighbors", "etp_node_product"):
+    for name in ("etp_api", "etp_sh", "etp_graph", "etp_mix", "etp_forces", "etp_neighbors", "etp_node_product", "etp_edge_tp"):
         out.append((os.path.join(CSRC, name + ".hip"), os.path.join(BUILD, name + ".o"), []))
     for name in ("etp_dst", "etp_src"):
         for L in range(5):

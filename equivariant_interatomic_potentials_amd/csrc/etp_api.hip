@@ -18,6 +18,10 @@ hipError_t launch_mix(int L, int C, int n, const float *in, const float *W, floa
                       hipStream_t stream);
 hipError_t launch_node_product(int L, int C, int n, int nu, const float *A, const float *W, float *out,
                                bool accumulate, hipStream_t stream);
+hipError_t launch_edge_tp_fwd(int L, int C, int64_t E, const float *vec, const float *V, const float *w, float *out,
+                              bool accumulate, hipStream_t stream);
+hipError_t launch_edge_tp_vjp(int L, int C, int64_t E, const float *vec, const float *V, const float *w,
+                              const float *G, float *gV, float *gw, float *gr, bool accumulate, hipStream_t stream);
 hipError_t launch_forces(int n_dst, int n_src, const int *row_ptr, const int *src_ptr, const int *perm,
                          const float *gr, float *F, bool accumulate, hipStream_t stream);
 size_t transpose_workspace_bytes(int n_src);
@@ -427,6 +431,42 @@ etp_status etp_channel_mix(etp_plan_t plan, int32_t n_nodes, const float *in, co
         return ETP_ERR_INVALID_ARGUMENT;
     return hip_status(etp::launch_mix(plan->L, plan->C, n_nodes, in, W, out, flags & ETP_FLAG_ACCUMULATE,
                                       static_cast<hipStream_t>(stream)));
+}
+
+etp_status etp_edge_tp_fwd(etp_plan_t plan, int64_t n_edges, const float *vec, const float *V, const float *w,
+                           float *out, uint32_t flags, void *stream)
+{
+    if (!plan || n_edges < 0 || (flags & ~static_cast<uint32_t>(ETP_FLAG_ACCUMULATE)))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (n_edges >= kMaxEdges)
+        return ETP_ERR_UNSUPPORTED;
+    if (plan->dtype != ETP_F32)
+        return ETP_ERR_UNSUPPORTED;
+    if (n_edges == 0)
+        return ETP_OK;
+    if (!vec || !V || !w || !out)
+        return ETP_ERR_INVALID_ARGUMENT;
+    return hip_status(etp::launch_edge_tp_fwd(plan->L, plan->C, n_edges, vec, V, w, out,
+                                              flags & ETP_FLAG_ACCUMULATE, static_cast<hipStream_t>(stream)));
+}
+
+etp_status etp_edge_tp_vjp(etp_plan_t plan, int64_t n_edges, const float *vec, const float *V, const float *w,
+                           const float *grad_out, float *grad_V, float *grad_w, float *grad_vec, uint32_t flags,
+                           void *stream)
+{
+    if (!plan || n_edges < 0 || (flags & ~static_cast<uint32_t>(ETP_FLAG_ACCUMULATE)))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (n_edges >= kMaxEdges)
+        return ETP_ERR_UNSUPPORTED;
+    if (plan->dtype != ETP_F32)
+        return ETP_ERR_UNSUPPORTED;
+    if (n_edges == 0 || (!grad_V && !grad_w && !grad_vec))
+        return ETP_OK;
+    if (!vec || !V || !w || !grad_out)
+        return ETP_ERR_INVALID_ARGUMENT;
+    return hip_status(etp::launch_edge_tp_vjp(plan->L, plan->C, n_edges, vec, V, w, grad_out, grad_V, grad_w,
+                                              grad_vec, flags & ETP_FLAG_ACCUMULATE,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 etp_status etp_node_product(etp_plan_t plan, int32_t n_nodes, int32_t corr_order, const float *A, const float *W,

@@ -32,6 +32,7 @@ ABI_SYMBOLS = ("etp_plan_create", "etp_plan_destroy", "etp_plan_info", "etp_plan
                "etp_csr_transpose_workspace", "etp_csr_transpose", "etp_sh", "etp_edge_conv_fwd",
                "etp_edge_conv_vjp", "etp_edge_conv_vjp2", "etp_channel_mix", "etp_edge_forces",
                "etp_neighbor_workspace", "etp_neighbor_count", "etp_neighbor_fill", "etp_node_product",
+               "etp_edge_tp_fwd", "etp_edge_tp_vjp",
                "etp_status_string", "etp_version")
 
 
@@ -101,6 +102,8 @@ def _load():
         "etp_channel_mix": (st, [vp, i32, vp, vp, vp, u32, vp]),
         "etp_edge_forces": (st, [ctypes.POINTER(etp_graph), vp, vp, u32, vp]),
         "etp_node_product": (st, [vp, i32, i32, vp, vp, vp, u32, vp]),
+        "etp_edge_tp_fwd": (st, [vp, i64, vp, vp, vp, vp, u32, vp]),
+        "etp_edge_tp_vjp": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, u32, vp]),
         "etp_neighbor_workspace": (st, [i32, vp, ctypes.c_float, ctypes.POINTER(ctypes.c_size_t)]),
         "etp_neighbor_count": (st, [i32, vp, vp, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]),
         "etp_neighbor_fill": (st, [i32, vp, vp, ctypes.c_float, vp, i64, vp, vp, u32, vp, ctypes.c_size_t, vp]),
@@ -360,6 +363,32 @@ def etp_node_product(plan: Plan, A, W, out, corr_order: int, flags: int = 0, str
                                 _ptr(W, "W", torch.float32, (corr_order - 1) * plan.P * C, optional=True),
                                 _ptr(out, "out", torch.float32, n * D * C, optional=True), flags,
                                 _stream(stream)), "etp_node_product")
+
+
+def etp_edge_tp_fwd(plan: Plan, vec, V, w, out, flags: int = 0, stream=None):
+    """Edge-local tensor product: out[E, Dout, C] (no destination sum)."""
+    import torch
+    E, C = vec.numel() // 3, plan.C
+    _check(lib.etp_edge_tp_fwd(plan.handle, E, _ptr(vec, "vec", torch.float32, 3 * E, optional=True),
+                               _ptr(V, "V", torch.float32, E * plan.din_rows * C, optional=True),
+                               _ptr(w, "w", torch.float32, E * plan.P * C, optional=True),
+                               _ptr(out, "out", torch.float32, E * plan.dout_rows * C, optional=True), flags,
+                               _stream(stream)), "etp_edge_tp_fwd")
+
+
+def etp_edge_tp_vjp(plan: Plan, vec, V, w, grad_out, grad_V=None, grad_w=None, grad_vec=None, flags: int = 0,
+                    stream=None):
+    import torch
+    E, C = vec.numel() // 3, plan.C
+    f32 = torch.float32
+    _check(lib.etp_edge_tp_vjp(plan.handle, E, _ptr(vec, "vec", f32, 3 * E, optional=True),
+                               _ptr(V, "V", f32, E * plan.din_rows * C, optional=True),
+                               _ptr(w, "w", f32, E * plan.P * C, optional=True),
+                               _ptr(grad_out, "grad_out", f32, E * plan.dout_rows * C, optional=True),
+                               _ptr(grad_V, "grad_V", f32, E * plan.din_rows * C, optional=True),
+                               _ptr(grad_w, "grad_w", f32, E * plan.P * C, optional=True),
+                               _ptr(grad_vec, "grad_vec", f32, 3 * E, optional=True), flags, _stream(stream)),
+           "etp_edge_tp_vjp")
 
 
 def _box3(box):

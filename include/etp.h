@@ -201,6 +201,27 @@ ETP_API etp_status etp_edge_conv_vjp2(etp_plan_t plan, const etp_graph *g, const
 ETP_API etp_status etp_channel_mix(etp_plan_t plan, int32_t n_nodes, const float *in, const float *W, float *out,
                                    uint32_t flags, void *stream);
 
+/* Edge-local tensor product: the convolution's message without the
+ * destination sum, one output block per edge (the pair-wise tensor product of
+ * Allegro, whose energy is a sum of per-pair terms: "Scaling the leading
+ * accuracy of deep equivariant models to biomolecular simulations of
+ * realistic size", section "Proposed method"):
+ *   out[e][off_p + l3 + m3][u] = w[e][p][u]
+ *        sum_{(m1, m2, m3) in p} C[m1, m2, m3] Y_{l2, m2}(vec_e) V[e][l1*l1 + l1 + m1][u]
+ * (the forward of the convolution on a graph where every edge is its own
+ * destination and source). V: DEVICE float [n_edges][(l_max+1)^2][C];
+ * w: [n_edges][P][C]; vec: [n_edges][3]; out, grad_out: [n_edges][dout_rows][C].
+ * The VJP gives grad_V, grad_w and grad_vec (each may be NULL: not computed).
+ * fp32 only (the plan must be ETP_F32). flags: ETP_FLAG_ACCUMULATE adds into
+ * every output. Nothing is allocated; no atomics (deterministic). Errors:
+ * INVALID_ARGUMENT (null plan or pointers, negative n_edges, other flags),
+ * UNSUPPORTED (bf16 plan, n_edges >= 2^31), HIP. */
+ETP_API etp_status etp_edge_tp_fwd(etp_plan_t plan, int64_t n_edges, const float *vec, const float *V, const float *w,
+                                   float *out, uint32_t flags, void *stream);
+ETP_API etp_status etp_edge_tp_vjp(etp_plan_t plan, int64_t n_edges, const float *vec, const float *V, const float *w,
+                                   const float *grad_out, float *grad_V, float *grad_w, float *grad_vec,
+                                   uint32_t flags, void *stream);
+
 /* Node-local correlation product: weighted products of each node's irreps
  * with themselves, applied step by step and truncated to orders <= l_max
  * after every step (the node-local product ladder of "How does FlashCart

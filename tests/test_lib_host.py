@@ -32,7 +32,7 @@ def header_symbols():
 
 def test_header_symbols_exported():
     names = header_symbols()
-    assert len(names) == 18
+    assert len(names) == 20
     assert sorted(etp.ABI_SYMBOLS) == names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (etp_\w+)$", out, flags=re.M))
@@ -145,6 +145,14 @@ def test_call_validation_without_device():
     assert lib.etp_edge_forces(ctypes.byref(g4), 8, 8, 0, None) == INV                 # no transpose
     assert lib.etp_edge_forces(ctypes.byref(g5), None, 8, 0, None) == INV
     assert lib.etp_edge_forces(ctypes.byref(g5), 8, 8, 4, None) == INV
+    assert lib.etp_edge_tp_fwd(None, 4, 8, 8, 8, 8, 0, None) == INV
+    assert lib.etp_edge_tp_fwd(plan.handle, -1, 8, 8, 8, 8, 0, None) == INV
+    assert lib.etp_edge_tp_fwd(plan.handle, 4, 8, None, 8, 8, 0, None) == INV
+    assert lib.etp_edge_tp_fwd(plan.handle, 4, 8, 8, 8, 8, 2, None) == INV
+    assert lib.etp_edge_tp_fwd(plan.handle, 2 ** 31, 8, 8, 8, 8, 0, None) == UNS
+    assert lib.etp_edge_tp_fwd(plan.handle, 0, None, None, None, None, 0, None) == 0
+    assert lib.etp_edge_tp_vjp(plan.handle, 4, 8, 8, 8, None, 8, 8, 8, 0, None) == INV   # grad_out needed
+    assert lib.etp_edge_tp_vjp(plan.handle, 4, 8, 8, 8, 8, None, None, None, 0, None) == 0  # nothing asked
     assert lib.etp_node_product(None, 4, 2, 8, 8, 8, 0, None) == INV
     assert lib.etp_node_product(plan.handle, -1, 2, 8, 8, 8, 0, None) == INV
     assert lib.etp_node_product(plan.handle, 4, 0, 8, 8, 8, 0, None) == INV
@@ -155,6 +163,7 @@ def test_call_validation_without_device():
     assert lib.etp_node_product(plan.handle, 0, 3, None, None, None, 0, None) == 0
     bfp = etp.etp_plan_create(2, 8, etp.ETP_BF16)
     assert lib.etp_node_product(bfp.handle, 4, 2, 8, 8, 8, 0, None) == UNS
+    assert lib.etp_edge_tp_fwd(bfp.handle, 4, 8, 8, 8, 8, 0, None) == UNS
     box = np.array([20.0, 20.0, 30.0], np.float32)
     bp = box.ctypes.data
     nb = ctypes.c_size_t()
