@@ -254,6 +254,27 @@ etp_status etp_csr_transpose_workspace(int32_t n_src, size_t *bytes)
     return ETP_OK;
 }
 
+etp_status etp_workspace_size(etp_plan_t plan, int32_t op, const etp_graph *g, size_t *bytes)
+{
+    if (!plan || !g || !bytes)
+        return ETP_ERR_INVALID_ARGUMENT;
+    etp_status st = check_graph(g, false);
+    if (st != ETP_OK)
+        return st;
+    switch (op) {
+    case ETP_OP_FWD:
+    case ETP_OP_VJP:
+    case ETP_OP_VJP2:
+        *bytes = 0;  // the convolution keeps everything in registers and LDS
+        return ETP_OK;
+    case ETP_OP_TRANSPOSE:
+        *bytes = etp::transpose_workspace_bytes(g->n_src);
+        return ETP_OK;
+    default:
+        return ETP_ERR_INVALID_ARGUMENT;
+    }
+}
+
 etp_status etp_csr_transpose(const etp_graph *g, int32_t *src_ptr, int32_t *perm, int32_t *perm_dst, void *ws,
                              size_t ws_bytes, void *stream)
 {

@@ -29,7 +29,7 @@ ETP_FLAG_VALIDATE = 2
 
 # every symbol include/etp.h declares
 ABI_SYMBOLS = ("etp_plan_create", "etp_plan_destroy", "etp_plan_info", "etp_plan_tables",
-               "etp_csr_transpose_workspace", "etp_csr_transpose", "etp_sh", "etp_edge_conv_fwd",
+               "etp_csr_transpose_workspace", "etp_csr_transpose", "etp_workspace_size", "etp_sh", "etp_edge_conv_fwd",
                "etp_edge_conv_vjp", "etp_edge_conv_vjp2", "etp_channel_mix", "etp_edge_forces",
                "etp_neighbor_workspace", "etp_neighbor_count", "etp_neighbor_fill", "etp_node_product",
                "etp_edge_tp_fwd", "etp_edge_tp_vjp",
@@ -94,6 +94,7 @@ def _load():
         "etp_plan_tables": (st, [vp, vp, vp, vp, vp, vp]),
         "etp_csr_transpose_workspace": (st, [i32, ctypes.POINTER(ctypes.c_size_t)]),
         "etp_csr_transpose": (st, [ctypes.POINTER(etp_graph), vp, vp, vp, vp, ctypes.c_size_t, vp]),
+        "etp_workspace_size": (st, [vp, i32, ctypes.POINTER(etp_graph), ctypes.POINTER(ctypes.c_size_t)]),
         "etp_sh": (st, [vp, i64, vp, vp, vp, vp]),
         "etp_edge_conv_fwd": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, u32, vp]),
         "etp_edge_conv_vjp": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, vp, vp, vp, u32, vp]),
@@ -246,6 +247,16 @@ class Graph:
 def etp_csr_transpose_workspace(n_src: int) -> int:
     b = ctypes.c_size_t()
     _check(lib.etp_csr_transpose_workspace(n_src, ctypes.byref(b)), "etp_csr_transpose_workspace")
+    return b.value
+
+
+ETP_OP_FWD, ETP_OP_VJP, ETP_OP_VJP2, ETP_OP_TRANSPOSE = 0, 1, 2, 3
+
+
+def etp_workspace_size(plan: Plan, op: int, graph: Graph) -> int:
+    b = ctypes.c_size_t()
+    g = graph.struct()
+    _check(lib.etp_workspace_size(plan.handle, op, ctypes.byref(g), ctypes.byref(b)), "etp_workspace_size")
     return b.value
 
 

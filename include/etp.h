@@ -157,6 +157,15 @@ ETP_API etp_status etp_csr_transpose_workspace(int32_t n_src, size_t *bytes);
 ETP_API etp_status etp_csr_transpose(const etp_graph *g, int32_t *src_ptr, int32_t *perm, int32_t *perm_dst, void *ws,
                              size_t ws_bytes, void *stream);
 
+/* Device workspace (bytes) that an operation needs on graph g: ETP_OP_FWD,
+ * ETP_OP_VJP and ETP_OP_VJP2 need none (0: the convolution keeps its
+ * intermediates in registers and LDS and takes no workspace argument);
+ * ETP_OP_TRANSPOSE needs etp_csr_transpose_workspace(g->n_src). Host only.
+ * Errors: INVALID_ARGUMENT (null pointers, a malformed graph descriptor, an
+ * unknown op), UNSUPPORTED (n_edges >= 2^31). */
+enum { ETP_OP_FWD = 0, ETP_OP_VJP = 1, ETP_OP_VJP2 = 2, ETP_OP_TRANSPOSE = 3 };
+ETP_API etp_status etp_workspace_size(etp_plan_t plan, int32_t op, const etp_graph *g, size_t *bytes);
+
 /* Spherical harmonics of n_edges bond vectors: Y[n][dsh] and, if dY is not
  * NULL, dY[n][3][dsh] = dY/dr (with respect to the unnormalised vector). */
 ETP_API etp_status etp_sh(etp_plan_t plan, int64_t n_edges, const float *vec, float *Y, float *dY, void *stream);

@@ -32,7 +32,7 @@ def header_symbols():
 
 def test_header_symbols_exported():
     names = header_symbols()
-    assert len(names) == 20
+    assert len(names) == 21
     assert sorted(etp.ABI_SYMBOLS) == names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (etp_\w+)$", out, flags=re.M))
@@ -192,4 +192,13 @@ def test_call_validation_without_device():
     assert lib.etp_neighbor_fill(1000, 8, bp, 12.0, 8, 100, 8, 8, 0, 8, nb.value, None) == UNS
     b = ctypes.c_size_t()
     assert lib.etp_csr_transpose_workspace(1000, ctypes.byref(b)) == 0 and b.value >= 4000
+    g6 = etp.etp_graph(4, 1000, 8, 8, 8, None, None, None)
+    wsb = ctypes.c_size_t(7)
+    for op in (etp.ETP_OP_FWD, etp.ETP_OP_VJP, etp.ETP_OP_VJP2):
+        assert lib.etp_workspace_size(plan.handle, op, ctypes.byref(g6), ctypes.byref(wsb)) == 0 and wsb.value == 0
+    assert lib.etp_workspace_size(plan.handle, etp.ETP_OP_TRANSPOSE, ctypes.byref(g6), ctypes.byref(wsb)) == 0
+    assert wsb.value == b.value
+    assert lib.etp_workspace_size(plan.handle, 9, ctypes.byref(g6), ctypes.byref(wsb)) == INV
+    assert lib.etp_workspace_size(None, 0, ctypes.byref(g6), ctypes.byref(wsb)) == INV
+    assert lib.etp_workspace_size(plan.handle, 0, ctypes.byref(g2), ctypes.byref(wsb)) == UNS
     assert lib.etp_csr_transpose_workspace(-1, ctypes.byref(b)) == INV
