@@ -25,13 +25,13 @@
 //      3 cells) neighbouring cells are flattened into one candidate range,
 //      64 candidates per step, and every hit is counted with a ballot;
 //   4. scan the counts into row_ptr;                  (end of the count call)
-//   5. fill: the same sweep writes each row's sources, unordered, at slots
-//      from ballot prefix counts;
-//   6. sort every row by source id (rank by counting: the ids in a row are
-//      distinct), in LDS for rows up to kNlRowCap, else through the vec
-//      buffer, which is free until step 7;
+//   5. fill: the same sweep gathers each row's sources at slots from ballot
+//      prefix counts (in LDS for rows up to kNlRowCap, else unordered in src);
+//   6. sort the row by source id (rank by counting: the ids in a row are
+//      distinct) -- in the fill for rows in LDS, else in nl_sort_kernel
+//      through the row's own part of the vec buffer, free until step 7;
 //   7. vec of every edge from the wrapped positions, in the contract's
-//      arithmetic.
+//      arithmetic (in the fill, or in nl_vec_kernel for long rows).
 // Cells have side >= rc (1 + 2^-10), so two atoms closer than the cutoff sit
 // in the same or adjacent cells even after the float32 rounding of the cell
 // index (an error of a few 1e-5 cell sides for up to kNlMaxCellsAxis cells
@@ -73,7 +73,25 @@ struct NlWork {
 
 __device__ __forceinline__ float nl_wrap(float p, float L) { return __builtin_fmaf(-L, floorf(p / L), p); }
 
-__device__ __forceinline__ float nl_image(float d, float L) { return __builtin_fmaf(-L, rintf(d / L), d); }
+// d - L rint(d / L) for d = q_j - q_i of wrapped positions (|d| <= L). The
+// division is taken only where its rounding can matter: for |d| <= L/4 the
+// correctly rounded quotient lies in [-1/4, 1/4] and rint gives 0; for |d| >=
+// fl(3L/4) it lies in (1/2, 1] and rint gives sign(d); in between the
+// quotient is formed. The result is bit-identical to the formula as written
+// (also for d = 0: both give +0), and most candidates of a cell list take the
+// first branch.
+__device__ __forceinline__ float nl_image(float d, float L)
+{
+    const float a = fabsf(d);
+    float k;
+    if (a <= 0.25f * L)
+        k = 0.f;
+    else if (a >= 0.75f * L)
+        k = copysignf(1.f, d);
+    else
+        k = rintf(d / L);
+    return __builtin_fmaf(-L, k, d);
+}
 
 __device__ __forceinline__ int nl_axis_cell(float q, float f, int nc)
 {
@@ -112,13 +130,17 @@ __global__ void __launch_bounds__(256) nl_scatter_kernel(int n, NlWork w)
     w.cq[w.cell_start[w.cell_of[i]] + w.cell_rank[i]] = make_float4(q.x, q.y, q.z, __int_as_float(i));
 }
 
-// steps 3 and 5: one wave per atom, atoms taken in cell order.
+// steps 3 and 5: one wave per atom, atoms taken in cell order. The fill
+// keeps a row of up to kNlRowCap sources in LDS, ranks it there and writes
+// src and vec in order (steps 5-7 in one pass); a longer row is written
+// unordered and left to nl_sort_kernel / nl_vec_kernel.
 template <bool FILL>
 __global__ void __launch_bounds__(256) nl_sweep_kernel(int n, const NlGeom g, NlWork w, int *__restrict__ row_ptr,
-                                                       int *__restrict__ src)
+                                                       int *__restrict__ src, float *__restrict__ vec)
 {
     __shared__ int cstart_s[4][32];
     __shared__ int cpre_s[4][32];
+    __shared__ int4 buf_s[FILL ? 4 : 1][FILL ? kNlRowCap / 4 + 1 : 1];
     const int lane = threadIdx.x & 63, wv = wave_id();
     const int slot = blockIdx.x * 4 + wv;
     if (slot >= n)
@@ -159,6 +181,8 @@ __global__ void __launch_bounds__(256) nl_sweep_kernel(int n, const NlGeom g, Nl
         base = row_ptr[i];
         lim = row_ptr[i + 1] - base;
     }
+    const bool inl = FILL && lim <= kNlRowCap;  // this row is ordered in LDS
+    int *buf = reinterpret_cast<int *>(buf_s[FILL ? wv : 0]);
     int t = 0, found = 0;
     for (int v0 = 0; v0 < total; v0 += 64) {
         const int v = v0 + lane;
@@ -181,15 +205,48 @@ __global__ void __launch_bounds__(256) nl_sweep_kernel(int n, const NlGeom g, Nl
             const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
                                                         __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
             const int k = found + below;
-            if (hit && k < lim)
-                src[base + k] = j;
+            if (hit && k < lim) {
+                if (inl)
+                    buf[k] = j;
+                else
+                    src[base + k] = j;
+            }
         }
         found += __popcll(m);
     }
     if constexpr (FILL) {
+        const int have = found < lim ? found : lim;
+        if (inl) {
+            // rank by counting (the ids of a row are distinct), four ids per
+            // LDS read; the padding after the row never counts
+            if (lane < 4)
+                buf[have + lane] = 0x7FFFFFFF;
+            wave_sync_lds();
+            const int4 *b4 = buf_s[wv];
+            const int nq = (have + 3) >> 2;
+            for (int k = lane; k < have; k += 64) {
+                const int v = buf[k];
+                int r = 0;
+                for (int q = 0; q < nq; ++q) {
+                    const int4 b = b4[q];
+                    r += (b.x < v) + (b.y < v) + (b.z < v) + (b.w < v);
+                }
+                const float4 o = w.qa[v];
+                float *ve = vec + 3 * (static_cast<int64_t>(base) + r);
+                src[base + r] = v;
+                ve[0] = nl_image(o.x - me.x, g.L[0]);
+                ve[1] = nl_image(o.y - me.y, g.L[1]);
+                ve[2] = nl_image(o.z - me.z, g.L[2]);
+            }
+        }
         // positions changed since the count: pad the row and flag it
-        for (int k = found + lane; k < lim; k += 64)
+        for (int k = have + lane; k < lim; k += 64) {
             src[base + k] = -1;
+            if (inl) {
+                float *ve = vec + 3 * (static_cast<int64_t>(base) + k);
+                ve[0] = ve[1] = ve[2] = __builtin_nanf("");
+            }
+        }
         if (lane == 0 && found != lim)
             atomicAdd(w.bad, 1);
     } else {
@@ -198,27 +255,23 @@ __global__ void __launch_bounds__(256) nl_sweep_kernel(int n, const NlGeom g, Nl
     }
 }
 
-// step 6: sort each row by source id; one wave per row. Rows up to
-// kNlRowCap are ranked in LDS, longer ones through scratch (the vec buffer,
-// reinterpreted, row for row at the same offsets as src).
+// step 6 for rows longer than kNlRowCap: sort by source id, one wave per
+// row, rank by counting through scratch in the row's own part of the vec
+// buffer (3 len floats, not yet written; other rows' vec is never touched).
 __global__ void __launch_bounds__(256) nl_sort_kernel(int n, const int *__restrict__ row_ptr, int *__restrict__ src,
                                                       int *__restrict__ scratch)
 {
-    __shared__ int buf_s[4][kNlRowCap];
-    const int lane = threadIdx.x & 63, wv = wave_id();
-    const int i = blockIdx.x * 4 + wv;
+    const int lane = threadIdx.x & 63;
+    const int i = blockIdx.x * 4 + wave_id();
     if (i >= n)
         return;
     const int s = row_ptr[i], len = row_ptr[i + 1] - s;
-    if (len <= 1)
-        return;
-    int *buf = len <= kNlRowCap ? buf_s[wv] : scratch + s;
+    if (len <= kNlRowCap)
+        return;  // ordered by the fill
+    int *buf = scratch + 3 * static_cast<int64_t>(s);
     for (int k = lane; k < len; k += 64)
         buf[k] = src[s + k];
-    if (len <= kNlRowCap)
-        wave_sync_lds();
-    else
-        __threadfence();  // the wave's stores complete before its loads, which miss L1
+    __threadfence();  // the wave's stores complete before its loads, which miss L1
     for (int k = lane; k < len; k += 64) {
         const int v = buf[k];
         int r = 0;
@@ -228,7 +281,7 @@ __global__ void __launch_bounds__(256) nl_sort_kernel(int n, const int *__restri
     }
 }
 
-// step 7: vec of every edge; one wave per row.
+// step 7 for rows longer than kNlRowCap: vec of every edge; one wave per row.
 __global__ void __launch_bounds__(256) nl_vec_kernel(int n, const NlGeom g, const float4 *__restrict__ qa,
                                                      const int *__restrict__ row_ptr, const int *__restrict__ src,
                                                      float *__restrict__ vec)
@@ -237,8 +290,10 @@ __global__ void __launch_bounds__(256) nl_vec_kernel(int n, const NlGeom g, cons
     const int i = blockIdx.x * 4 + wave_id();
     if (i >= n)
         return;
-    const float4 me = qa[i];
     const int s = row_ptr[i], e1 = row_ptr[i + 1];
+    if (e1 - s <= kNlRowCap)
+        return;  // written by the fill
+    const float4 me = qa[i];
     for (int e = s + lane; e < e1; e += 64) {
         const int j = src[e];
         float dx = __builtin_nanf(""), dy = dx, dz = dx;
@@ -326,7 +381,7 @@ hipError_t launch_neighbor_count(int n, const float *pos, const float *box, floa
     if ((e = nl_bin(n, pos, g, w, stream)) != hipSuccess)
         return e;
     hipLaunchKernelGGL(nl_sweep_kernel<false>, dim3((n + 3) / 4), dim3(256), 0, stream, n, g, w, row_ptr,
-                       static_cast<int *>(nullptr));
+                       static_cast<int *>(nullptr), static_cast<float *>(nullptr));
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     return launch_nl_counts_to_offsets(row_ptr, n, w.bsum, stream);
@@ -346,7 +401,7 @@ hipError_t launch_neighbor_fill(int n, const float *pos, const float *box, float
     if (n_edges == 0)
         return hipSuccess;
     int *rp = const_cast<int *>(row_ptr);  // read only in the fill sweep
-    hipLaunchKernelGGL(nl_sweep_kernel<true>, dim3((n + 3) / 4), dim3(256), 0, stream, n, g, w, rp, src);
+    hipLaunchKernelGGL(nl_sweep_kernel<true>, dim3((n + 3) / 4), dim3(256), 0, stream, n, g, w, rp, src, vec);
     hipLaunchKernelGGL(nl_sort_kernel, dim3((n + 3) / 4), dim3(256), 0, stream, n, row_ptr, src,
                        reinterpret_cast<int *>(vec));
     hipLaunchKernelGGL(nl_vec_kernel, dim3((n + 3) / 4), dim3(256), 0, stream, n, g, w.qa, row_ptr, src, vec);
