@@ -85,6 +85,8 @@ def _load():
         lib.oracle_neighbor_row.argtypes = [ctypes.c_int, _f32p, _f32p, ctypes.c_float, ctypes.c_int, _i32p, _f32p]
         lib.oracle_node_product.restype = ctypes.c_int
         lib.oracle_node_product.argtypes = [ctypes.c_int] * 4 + [_f64p, _f64p, _f64p]
+        lib.oracle_node_product_vjp.restype = ctypes.c_int
+        lib.oracle_node_product_vjp.argtypes = [ctypes.c_int] * 4 + [_f64p, _f64p, _f64p, _f64p]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -295,6 +297,18 @@ def node_product(L, A, W, nu):
     if _load().oracle_node_product(L, C, n, nu, _p(A, _f64p), _p(W, _f64p), _p(out, _f64p)):
         raise ValueError("bad arguments")
     return out
+
+
+def node_product_vjp(L, A, W, G, nu):
+    """gA[n, (L+1)^2, C] = d<G, node_product(L, A, W, nu)>/dA."""
+    A = np.ascontiguousarray(A, np.float64)
+    n, D, C = A.shape
+    G = np.ascontiguousarray(G, np.float64)
+    W = np.ascontiguousarray(np.zeros((1,)) if W is None else W, np.float64)
+    gA = np.zeros_like(A)
+    if _load().oracle_node_product_vjp(L, C, n, nu, _p(A, _f64p), _p(W, _f64p), _p(G, _f64p), _p(gA, _f64p)):
+        raise ValueError("bad arguments")
+    return gA
 
 
 def neighbor_row(pos, box, rc, i):

@@ -788,6 +788,77 @@ int oracle_node_product(int L, int C, int n, int nu, const double *A, const doub
     return 0;
 }
 
+/* VJP of the node-local product with respect to A (what forces need: A is
+ * built from the positions): gA = d<G, out>/dA by reverse mode over the
+ * ladder, every B_k kept. With Bbar_nu = G:
+ *   Bbar_k = G + sum_p W[k-1][p] sum C A[l2,m2] Bbar_{k+1}[l3,m3]   (into [l1,m1])
+ *   gA    += sum_p W[k-1][p] sum C B_k[l1,m1] Bbar_{k+1}[l3,m3]     (into [l2,m2])
+ * for k = nu-1 .. 1, then gA += Bbar_1 (B_1 = A). */
+int oracle_node_product_vjp(int L, int C, int n, int nu, const double *A, const double *W, const double *G,
+                            double *gA)
+{
+    table t;
+    if (nu < 1 || table_make(L, L, L, &t))
+        return -1;
+    const int D = (L + 1) * (L + 1), P = t.P;
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < n; ++i) {
+        const double *Ai = A + (int64_t)i * D * C, *Gi = G + (int64_t)i * D * C;
+        double *gi = gA + (int64_t)i * D * C;
+        double *B = (double *)malloc(sizeof(double) * (size_t)nu * D * C); /* B_1 .. B_nu */
+        double *bb = (double *)malloc(sizeof(double) * D * C);
+        double *nbb = (double *)malloc(sizeof(double) * D * C);
+        for (int q = 0; q < D * C; ++q)
+            B[q] = Ai[q];
+        for (int k = 1; k < nu; ++k) {
+            double *Bk = B + (int64_t)(k - 1) * D * C, *Bn = B + (int64_t)k * D * C;
+            for (int q = 0; q < D * C; ++q)
+                Bn[q] = 0.0;
+            for (int p = 0; p < P; ++p) {
+                const int l1 = t.path[3 * p], l2 = t.path[3 * p + 1], l3 = t.path[3 * p + 2];
+                const double *Wp = W + ((int64_t)(k - 1) * P + p) * C;
+                for (int q = t.ptr[p]; q < t.ptr[p + 1]; ++q) {
+                    const int r1 = l1 * l1 + l1 + t.m[3 * q], r2 = l2 * l2 + l2 + t.m[3 * q + 1];
+                    const int r3 = l3 * l3 + l3 + t.m[3 * q + 2];
+                    for (int u = 0; u < C; ++u)
+                        Bn[r3 * C + u] += Wp[u] * t.val[q] * Bk[r1 * C + u] * Ai[r2 * C + u];
+                }
+            }
+        }
+        for (int q = 0; q < D * C; ++q) {
+            bb[q] = Gi[q];
+            gi[q] = 0.0;
+        }
+        for (int k = nu - 1; k >= 1; --k) {
+            const double *Bk = B + (int64_t)(k - 1) * D * C;
+            for (int q = 0; q < D * C; ++q)
+                nbb[q] = Gi[q];
+            for (int p = 0; p < P; ++p) {
+                const int l1 = t.path[3 * p], l2 = t.path[3 * p + 1], l3 = t.path[3 * p + 2];
+                const double *Wp = W + ((int64_t)(k - 1) * P + p) * C;
+                for (int q = t.ptr[p]; q < t.ptr[p + 1]; ++q) {
+                    const int r1 = l1 * l1 + l1 + t.m[3 * q], r2 = l2 * l2 + l2 + t.m[3 * q + 1];
+                    const int r3 = l3 * l3 + l3 + t.m[3 * q + 2];
+                    for (int u = 0; u < C; ++u) {
+                        const double s = Wp[u] * t.val[q] * bb[r3 * C + u];
+                        nbb[r1 * C + u] += s * Ai[r2 * C + u];
+                        gi[r2 * C + u] += s * Bk[r1 * C + u];
+                    }
+                }
+            }
+            for (int q = 0; q < D * C; ++q)
+                bb[q] = nbb[q];
+        }
+        for (int q = 0; q < D * C; ++q)
+            gi[q] += bb[q];
+        free(B);
+        free(bb);
+        free(nbb);
+    }
+    table_free(&t);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Neighbour list                                                            */
 /* ------------------------------------------------------------------------ */

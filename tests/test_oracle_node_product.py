@@ -7,7 +7,9 @@ ladder B_{k+1} = sum_p W_k[p] CG_p(B_k, A), out = B_1 + ... + B_nu):
     l = 1 block keeps only a (a x a = 0), and the l = 2 block carries the rest
     of |a|^4 (the coupling is orthogonal);
   * the whole ladder against a dense recursion whose CG comes from sympy;
-  * rotation equivariance.
+  * rotation equivariance;
+  * the VJP with respect to A: central differences of <G, out>, the
+    derivative of the l_max = 0 polynomial, and rotation covariance.
 """
 import math
 
@@ -113,3 +115,56 @@ def test_rotation_equivariance(L):
     lhs = oracle.node_product(L, rot(A), W, nu)
     rhs = rot(oracle.node_product(L, A, W, nu))
     np.testing.assert_allclose(lhs, rhs, atol=1e-9 * np.abs(rhs).max())
+
+
+@pytest.mark.parametrize("L,nu", [(1, 3), (2, 4), (3, 2)])
+def test_vjp_finite_differences(L, nu):
+    g = np.random.default_rng(40 + L)
+    n, C = 3, 2
+    D = (L + 1) ** 2
+    A = g.standard_normal((n, D, C)) * 0.7
+    W = g.standard_normal((nu - 1, len(paths(L)), C))
+    G = g.standard_normal((n, D, C))
+    gA = oracle.node_product_vjp(L, A, W, G, nu)
+    h = 1e-6
+    for idx in [(0, 0, 0), (1, D - 1, 1), (2, D // 2, 0), (0, 1, 1)]:
+        d = np.zeros_like(A)
+        d[idx] = h
+        fd = ((G * oracle.node_product(L, A + d, W, nu)).sum() - (G * oracle.node_product(L, A - d, W, nu)).sum()) / (2 * h)
+        assert abs(fd - gA[idx]) < 1e-6 * max(1.0, abs(fd)), (idx, fd, gA[idx])
+
+
+def test_vjp_scalar_polynomial():
+    """l_max = 0: out = sum_k c_k a^k with c_k = prod_{j<k-1} W_j, so gA = G sum_k k c_k a^(k-1)."""
+    g = np.random.default_rng(50)
+    nu = 4
+    A = g.standard_normal((5, 1, 3))
+    W = g.standard_normal((nu - 1, 1, 3))
+    G = g.standard_normal((5, 1, 3))
+    gA = oracle.node_product_vjp(0, A, W, G, nu)
+    a = A[:, 0, :]
+    c, want = np.ones_like(a), np.zeros_like(a)
+    for k in range(1, nu + 1):
+        want += k * c * a ** (k - 1)
+        if k < nu:
+            c = c * W[k - 1, 0]
+    np.testing.assert_allclose(gA[:, 0, :], G[:, 0, :] * want, rtol=1e-12, atol=1e-12)
+
+
+def test_vjp_rotation_covariance():
+    L, nu = 2, 3
+    g = np.random.default_rng(60)
+    n, C = 3, 2
+    A = g.standard_normal((n, 9, C)) * 0.6
+    W = g.standard_normal((nu - 1, 15, C))
+    G = g.standard_normal((n, 9, C))
+    R = Rotation.random(random_state=61).as_matrix()
+
+    def rot(x):
+        y = np.empty_like(x)
+        for l in range(L + 1):
+            y[:, l * l:(l + 1) ** 2] = np.einsum("ab,nbu->nau", _wigner_D(l, R), x[:, l * l:(l + 1) ** 2])
+        return y
+
+    lhs = oracle.node_product_vjp(L, rot(A), W, rot(G), nu)
+    np.testing.assert_allclose(lhs, rot(oracle.node_product_vjp(L, A, W, G, nu)), atol=1e-9)
