@@ -816,12 +816,12 @@ int oracle_node_product_vjp(int L, int C, int n, int nu, const double *A, const 
                 Bn[q] = 0.0;
             for (int p = 0; p < P; ++p) {
                 const int l1 = t.path[3 * p], l2 = t.path[3 * p + 1], l3 = t.path[3 * p + 2];
-                const double *Wp = W + ((int64_t)(k - 1) * P + p) * C;
+                const double *Wv = W + ((int64_t)(k - 1) * P + p) * C;
                 for (int q = t.ptr[p]; q < t.ptr[p + 1]; ++q) {
-                    const int r1 = l1 * l1 + l1 + t.m[3 * q], r2 = l2 * l2 + l2 + t.m[3 * q + 1];
-                    const int r3 = l3 * l3 + l3 + t.m[3 * q + 2];
+                    const int s1 = l1 * l1 + l1 + t.m[3 * q], s2 = l2 * l2 + l2 + t.m[3 * q + 1];
+                    const int s3 = l3 * l3 + l3 + t.m[3 * q + 2];
                     for (int u = 0; u < C; ++u)
-                        Bn[r3 * C + u] += Wp[u] * t.val[q] * Bk[r1 * C + u] * Ai[r2 * C + u];
+                        Bn[s3 * C + u] += Wv[u] * t.val[q] * Bk[s1 * C + u] * Ai[s2 * C + u];
                 }
             }
         }
@@ -835,14 +835,14 @@ int oracle_node_product_vjp(int L, int C, int n, int nu, const double *A, const 
                 nbb[q] = Gi[q];
             for (int p = 0; p < P; ++p) {
                 const int l1 = t.path[3 * p], l2 = t.path[3 * p + 1], l3 = t.path[3 * p + 2];
-                const double *Wp = W + ((int64_t)(k - 1) * P + p) * C;
+                const double *Wv = W + ((int64_t)(k - 1) * P + p) * C;
                 for (int q = t.ptr[p]; q < t.ptr[p + 1]; ++q) {
-                    const int r1 = l1 * l1 + l1 + t.m[3 * q], r2 = l2 * l2 + l2 + t.m[3 * q + 1];
-                    const int r3 = l3 * l3 + l3 + t.m[3 * q + 2];
+                    const int s1 = l1 * l1 + l1 + t.m[3 * q], s2 = l2 * l2 + l2 + t.m[3 * q + 1];
+                    const int s3 = l3 * l3 + l3 + t.m[3 * q + 2];
                     for (int u = 0; u < C; ++u) {
-                        const double s = Wp[u] * t.val[q] * bb[r3 * C + u];
-                        nbb[r1 * C + u] += s * Ai[r2 * C + u];
-                        gi[r2 * C + u] += s * Bk[r1 * C + u];
+                        const double s = Wv[u] * t.val[q] * bb[s3 * C + u];
+                        nbb[s1 * C + u] += s * Ai[s2 * C + u];
+                        gi[s2 * C + u] += s * Bk[s1 * C + u];
                     }
                 }
             }

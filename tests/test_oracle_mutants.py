@@ -65,8 +65,8 @@ MUTANTS = [
     ("np_last_only", "                oi[q] += NB[q];", "                oi[q] = NB[q];"),
     ("np_m3_sign", "const int r3 = l3 * l3 + l3 + t.m[3 * q + 2];", "const int r3 = l3 * l3 + l3 - t.m[3 * q + 2];"),
     ("np_vjp_no_out_term", "                nbb[q] = Gi[q];", "                nbb[q] = 0.0;"),
-    ("np_vjp_gA_operand", "                        gi[r2 * C + u] += s * Bk[r1 * C + u];",
-     "                        gi[r2 * C + u] += s * Ai[r1 * C + u];"),
+    ("np_vjp_gA_operand", "                        gi[s2 * C + u] += s * Bk[s1 * C + u];",
+     "                        gi[s2 * C + u] += s * Ai[s1 * C + u];"),
     ("np_vjp_no_identity", "            gi[q] += bb[q];", "            gi[q] += 0.0 * bb[q];"),
     ("transpose_unstable", "int64_t k = cursor[src[e]]++;", "int64_t k = src_ptr[src[e] + 1] - 1 - (cursor[src[e]]++ - src_ptr[src[e]]);"),
 ]
