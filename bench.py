@@ -273,11 +273,32 @@ def time_node_product(etp, L, nu, reps, n=4096, C=128):
     b.record()
     torch.cuda.synchronize()
     t = a.elapsed_time(b) / reps * 1e-3
-    flops = float(n) * C * (nu - 1) * (len(prods) + 2 * nnz + 2 * dout + D)
+    f_step = len(prods) + 2 * nnz + 2 * dout + D
+    flops = float(n) * C * (nu - 1) * f_step
     byts = 4.0 * (2 * n * D * C + (nu - 1) * len(tb["paths"]) * C)
-    return {"nodes": n, "channels": C, "l_max": L, "corr_order": nu, "ms": round(t * 1e3, 4),
-            "algo_TFLOPs": flops / t / 1e12, "valu_frac": flops / t / 1e12 / VALU_PEAK_TFLOPS,
-            "algo_GBps": byts / t / 1e9, "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS, "bound": "alu"}
+    res = {"nodes": n, "channels": C, "l_max": L, "corr_order": nu, "ms": round(t * 1e3, 4),
+           "algo_TFLOPs": flops / t / 1e12, "valu_frac": flops / t / 1e12 / VALU_PEAK_TFLOPS,
+           "algo_GBps": byts / t / 1e9, "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS, "bound": "alu"}
+    # VJP with respect to A: (nu-1)(nu-2)/2 recomputed forward steps plus nu-1
+    # reverse steps (per step: Dout weight products, one FMA per CG entry,
+    # two FMAs per (path, m1, m2) group)
+    groups = sum(len({(int(a_), int(b_)) for a_, b_, _ in tb["cg_m"][tb["cg_ptr"][p]:tb["cg_ptr"][p + 1]]})
+                 for p in range(len(tb["paths"])))
+    G = torch.randn_like(A)
+    gA = torch.empty_like(A)
+    for _ in range(2):
+        etp.etp_node_product_vjp(plan, A, W, G, gA, nu)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        etp.etp_node_product_vjp(plan, A, W, G, gA, nu)
+    b.record()
+    torch.cuda.synchronize()
+    tv = a.elapsed_time(b) / reps * 1e-3
+    fv = float(n) * C * ((nu - 1) * (nu - 2) // 2 * f_step + (nu - 1) * (dout + 2 * nnz + 4 * groups))
+    res.update({"vjp_ms": round(tv * 1e3, 4), "vjp_algo_TFLOPs": fv / tv / 1e12,
+                "vjp_valu_frac": fv / tv / 1e12 / VALU_PEAK_TFLOPS})
+    return res
 
 
 def cpu_baseline(wl, budget_s=12.0):

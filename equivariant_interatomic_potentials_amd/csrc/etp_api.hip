@@ -22,6 +22,8 @@ hipError_t launch_edge_tp_fwd(int L, int C, int64_t E, const float *vec, const f
                               bool accumulate, hipStream_t stream);
 hipError_t launch_edge_tp_vjp(int L, int C, int64_t E, const float *vec, const float *V, const float *w,
                               const float *G, float *gV, float *gw, float *gr, bool accumulate, hipStream_t stream);
+hipError_t launch_node_product_vjp(int L, int C, int n, int nu, const float *A, const float *W, const float *G,
+                                   float *gA, bool accumulate, hipStream_t stream);
 hipError_t launch_forces(int n_dst, int n_src, const int *row_ptr, const int *src_ptr, const int *perm,
                          const float *gr, float *F, bool accumulate, hipStream_t stream);
 size_t transpose_workspace_bytes(int n_src);
@@ -505,6 +507,23 @@ etp_status etp_node_product(etp_plan_t plan, int32_t n_nodes, int32_t corr_order
         return ETP_ERR_INVALID_ARGUMENT;
     return hip_status(etp::launch_node_product(plan->L, plan->C, n_nodes, corr_order, A, W, out,
                                                flags & ETP_FLAG_ACCUMULATE, static_cast<hipStream_t>(stream)));
+}
+
+etp_status etp_node_product_vjp(etp_plan_t plan, int32_t n_nodes, int32_t corr_order, const float *A, const float *W,
+                                const float *grad_out, float *grad_A, uint32_t flags, void *stream)
+{
+    if (!plan || n_nodes < 0 || corr_order < 1 || corr_order > 8)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (flags & ~static_cast<uint32_t>(ETP_FLAG_ACCUMULATE))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (plan->dtype != ETP_F32)
+        return ETP_ERR_UNSUPPORTED;
+    if (n_nodes == 0)
+        return ETP_OK;
+    if (!A || !grad_out || !grad_A || (corr_order > 1 && !W))
+        return ETP_ERR_INVALID_ARGUMENT;
+    return hip_status(etp::launch_node_product_vjp(plan->L, plan->C, n_nodes, corr_order, A, W, grad_out, grad_A,
+                                                   flags & ETP_FLAG_ACCUMULATE, static_cast<hipStream_t>(stream)));
 }
 
 etp_status etp_edge_forces(const etp_graph *g, const float *grad_vec, float *forces, uint32_t flags, void *stream)

@@ -112,6 +112,144 @@ node_product_kernel(const int n, const int C, const int nu, const float *__restr
     }
 }
 
+// ---------------------------------------------------------------- VJP (A)
+// gA = d<G, out>/dA by reverse mode over the ladder (see the header of the
+// oracle's version for the recursion). Each reverse step k needs B_{k+1},
+// which is recomputed from A in registers (k forward steps) rather than kept
+// for every step: (nu - 1)(nu - 2) / 2 extra forward steps, no memory.
+
+// One forward step nb = sum_p W[k][p] CG_p(b, a), with its own weight ring.
+template <int L, typename WL>
+__device__ __forceinline__ void np_step(const float *a, const float *b, float *nb, int k, WL &&wload)
+{
+    constexpr int D = (L + 1) * (L + 1), P = kTab<L>.P, PF = kNpPrefetch;
+    float wr[PF];
+    static_range<0, PF>([&](auto q) { wr[q] = q < P ? wload(k, q) : 0.f; });
+    static_range<0, D>([&](auto r) { nb[r] = 0.f; });
+    static_range<0, P>([&](auto pc) {
+        constexpr int p = pc;
+        constexpr Path pa = kTab<L>.path[p];
+        const float w = wr[p % PF];
+        if constexpr (p + PF < P)
+            wr[p % PF] = wload(k, p + PF);
+        float acc[2 * pa.l3 + 1];
+        static_range<0, 2 * pa.l3 + 1>([&](auto m) { acc[m] = 0.f; });
+        static_range<kTab<L>.path_ab0[p], kTab<L>.path_ab0[p + 1]>([&](auto gc) {
+            constexpr ABGroup g = kTab<L>.ab[gc];
+            const float t = b[pa.l1 * pa.l1 + pa.l1 + g.m1] * a[pa.l2 * pa.l2 + pa.l2 + g.m2];
+            static_range<g.t0, g.t1>([&](auto ec) {
+                constexpr Entry e = kTab<L>.nz[kTab<L>.ab_entries[ec]];
+                acc[e.m3 + pa.l3] = __builtin_fmaf(e.fval, t, acc[e.m3 + pa.l3]);
+            });
+        });
+        static_range<0, 2 * pa.l3 + 1>(
+            [&](auto m) { nb[pa.l3 * pa.l3 + m] = __builtin_fmaf(w, acc[m], nb[pa.l3 * pa.l3 + m]); });
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+template <int L>
+constexpr int np_vjp_waves_per_eu()
+{
+    return L <= 2 ? 4 : (L == 3 ? 3 : 2);
+}
+
+template <int L, bool ACC>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(np_vjp_waves_per_eu<L>())))
+node_product_vjp_kernel(const int n, const int C, const int nu, const float *__restrict__ A,
+                        const float *__restrict__ W, const float *__restrict__ G, float *__restrict__ gA)
+{
+    constexpr int D = (L + 1) * (L + 1), P = kTab<L>.P, PF = kNpPrefetch;
+    const int lane = threadIdx.x & 63;
+    const int cw = (C + 63) >> 6;
+    const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + wave_id();
+    if (wid >= static_cast<int64_t>(n) * cw)
+        return;
+    const int i = static_cast<int>(wid / cw);
+    const int u = static_cast<int>(wid - static_cast<int64_t>(i) * cw) * 64 + lane;
+    const bool ok = u < C;
+    const uint32_t vo = ok ? static_cast<uint32_t>(u) * 4u : kOOB, rowb = static_cast<uint32_t>(C) * 4u;
+    const rsrc_t ra = make_rsrc(A + static_cast<int64_t>(i) * D * C, D * rowb);
+    const rsrc_t rg = make_rsrc(G + static_cast<int64_t>(i) * D * C, D * rowb);
+    const rsrc_t rw = make_rsrc(W, static_cast<uint32_t>((nu - 1) * P * C * 4));
+    auto wload = [&](int k, int q) { return bload<float>(rw, vo, static_cast<uint32_t>((k * P + q) * C * 4)); };
+
+    float a[D], ga[D], bb[D];
+    static_range<0, D>([&](auto r) {
+        a[r] = bload<float>(ra, vo, r * rowb);
+        bb[r] = bload<float>(rg, vo, r * rowb);  // dL/dB_nu = G
+        ga[r] = 0.f;
+    });
+    for (int k = nu - 2; k >= 0; --k) {
+        // B after k forward steps
+        float b[D];
+        static_range<0, D>([&](auto r) { b[r] = a[r]; });
+        for (int j = 0; j < k; ++j) {
+            float nb[D];
+            np_step<L>(a, b, nb, j, wload);
+            static_range<0, D>([&](auto r) { b[r] = nb[r]; });
+        }
+        // reverse of forward step k: dL/dB (before it) = G + J_b^T bb, gA += J_a^T bb
+        float nbb[D];
+        static_range<0, D>([&](auto r) { nbb[r] = bload<float>(rg, vo, r * rowb); });
+        float wr[PF];
+        static_range<0, PF>([&](auto q) { wr[q] = q < P ? wload(k, q) : 0.f; });
+        static_range<0, P>([&](auto pc) {
+            constexpr int p = pc;
+            constexpr Path pa = kTab<L>.path[p];
+            const float w = wr[p % PF];
+            if constexpr (p + PF < P)
+                wr[p % PF] = wload(k, p + PF);
+            float wb[2 * pa.l3 + 1];
+            static_range<0, 2 * pa.l3 + 1>([&](auto m) { wb[m] = w * bb[pa.l3 * pa.l3 + m]; });
+            static_range<kTab<L>.path_ab0[p], kTab<L>.path_ab0[p + 1]>([&](auto gc) {
+                constexpr ABGroup g = kTab<L>.ab[gc];
+                constexpr int r1 = pa.l1 * pa.l1 + pa.l1 + g.m1, r2 = pa.l2 * pa.l2 + pa.l2 + g.m2;
+                float c = 0.f;
+                static_range<g.t0, g.t1>([&](auto ec) {
+                    constexpr Entry e = kTab<L>.nz[kTab<L>.ab_entries[ec]];
+                    c = __builtin_fmaf(e.fval, wb[e.m3 + pa.l3], c);
+                });
+                nbb[r1] = __builtin_fmaf(c, a[r2], nbb[r1]);
+                ga[r2] = __builtin_fmaf(c, b[r1], ga[r2]);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        static_range<0, D>([&](auto r) { bb[r] = nbb[r]; });
+    }
+    const rsrc_t ro = make_rsrc(gA + static_cast<int64_t>(i) * D * C, D * rowb);
+    static_range<0, D>([&](auto r) {
+        float v = ga[r] + bb[r];  // B_1 = A
+        if constexpr (ACC)
+            v += bload<float>(ro, vo, r * rowb);
+        bstore<float>(v, ro, vo, r * rowb);
+    });
+}
+
+hipError_t launch_node_product_vjp(int L, int C, int n, int nu, const float *A, const float *W, const float *G,
+                                   float *gA, bool accumulate, hipStream_t stream)
+{
+    if (n == 0)
+        return hipSuccess;
+    const int64_t waves = static_cast<int64_t>(n) * ((C + 63) / 64);
+    const dim3 grid(static_cast<unsigned>((waves + 3) / 4)), block(256);
+#define ETP_NPV_CASE(LL)                                                                                      \
+    case LL:                                                                                                  \
+        if (accumulate)                                                                                       \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(node_product_vjp_kernel<LL, true>), grid, block, 0, stream, n, \
+                               C, nu, A, W, G, gA);                                                           \
+        else                                                                                                  \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(node_product_vjp_kernel<LL, false>), grid, block, 0, stream,   \
+                               n, C, nu, A, W, G, gA);                                                        \
+        break;
+    switch (L) {
+        ETP_NPV_CASE(0) ETP_NPV_CASE(1) ETP_NPV_CASE(2) ETP_NPV_CASE(3) ETP_NPV_CASE(4)
+    default: return hipErrorInvalidValue;
+    }
+#undef ETP_NPV_CASE
+    return hipGetLastError();
+}
+
 hipError_t launch_node_product(int L, int C, int n, int nu, const float *A, const float *W, float *out,
                                bool accumulate, hipStream_t stream)
 {

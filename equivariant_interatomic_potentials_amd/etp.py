@@ -31,7 +31,7 @@ ETP_FLAG_VALIDATE = 2
 ABI_SYMBOLS = ("etp_plan_create", "etp_plan_destroy", "etp_plan_info", "etp_plan_tables",
                "etp_csr_transpose_workspace", "etp_csr_transpose", "etp_workspace_size", "etp_sh", "etp_edge_conv_fwd",
                "etp_edge_conv_vjp", "etp_edge_conv_vjp2", "etp_channel_mix", "etp_edge_forces",
-               "etp_neighbor_workspace", "etp_neighbor_count", "etp_neighbor_fill", "etp_node_product",
+               "etp_neighbor_workspace", "etp_neighbor_count", "etp_neighbor_fill", "etp_node_product", "etp_node_product_vjp",
                "etp_edge_tp_fwd", "etp_edge_tp_vjp",
                "etp_status_string", "etp_version")
 
@@ -103,6 +103,7 @@ def _load():
         "etp_channel_mix": (st, [vp, i32, vp, vp, vp, u32, vp]),
         "etp_edge_forces": (st, [ctypes.POINTER(etp_graph), vp, vp, u32, vp]),
         "etp_node_product": (st, [vp, i32, i32, vp, vp, vp, u32, vp]),
+        "etp_node_product_vjp": (st, [vp, i32, i32, vp, vp, vp, vp, u32, vp]),
         "etp_edge_tp_fwd": (st, [vp, i64, vp, vp, vp, vp, u32, vp]),
         "etp_edge_tp_vjp": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, u32, vp]),
         "etp_neighbor_workspace": (st, [i32, vp, ctypes.c_float, ctypes.POINTER(ctypes.c_size_t)]),
@@ -374,6 +375,19 @@ def etp_node_product(plan: Plan, A, W, out, corr_order: int, flags: int = 0, str
                                 _ptr(W, "W", torch.float32, (corr_order - 1) * plan.P * C, optional=True),
                                 _ptr(out, "out", torch.float32, n * D * C, optional=True), flags,
                                 _stream(stream)), "etp_node_product")
+
+
+def etp_node_product_vjp(plan: Plan, A, W, grad_out, grad_A, corr_order: int, flags: int = 0, stream=None):
+    """grad_A = d<grad_out, node_product(A)>/dA."""
+    import torch
+    n = A.shape[0]
+    D, C = plan.din_rows, plan.C
+    f32 = torch.float32
+    _check(lib.etp_node_product_vjp(plan.handle, n, corr_order, _ptr(A, "A", f32, n * D * C, optional=True),
+                                    _ptr(W, "W", f32, (corr_order - 1) * plan.P * C, optional=True),
+                                    _ptr(grad_out, "grad_out", f32, n * D * C, optional=True),
+                                    _ptr(grad_A, "grad_A", f32, n * D * C, optional=True), flags, _stream(stream)),
+           "etp_node_product_vjp")
 
 
 def etp_edge_tp_fwd(plan: Plan, vec, V, w, out, flags: int = 0, stream=None):

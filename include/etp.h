@@ -251,6 +251,17 @@ ETP_API etp_status etp_edge_tp_vjp(etp_plan_t plan, int64_t n_edges, const float
 ETP_API etp_status etp_node_product(etp_plan_t plan, int32_t n_nodes, int32_t corr_order, const float *A,
                                     const float *W, float *out, uint32_t flags, void *stream);
 
+/* VJP of etp_node_product with respect to A (what forces need, A being
+ * built from the positions): grad_A = d<grad_out, out>/dA, by reverse mode
+ * over the ladder with each B_k recomputed from A in registers. grad_out,
+ * grad_A: DEVICE float [n_nodes][(l_max+1)^2][C]; the other arguments as in
+ * etp_node_product. The weight gradient (a sum over all nodes) is not
+ * computed. flags: ETP_FLAG_ACCUMULATE adds into grad_A. Errors as for
+ * etp_node_product. */
+ETP_API etp_status etp_node_product_vjp(etp_plan_t plan, int32_t n_nodes, int32_t corr_order, const float *A,
+                                        const float *W, const float *grad_out, float *grad_A, uint32_t flags,
+                                        void *stream);
+
 /* Forces on the atoms from the per-edge energy gradient grad_vec = dE/dvec
  * (the VJP's grad_vec), with vec_e = pos[src_e] - pos[dst_e]:
  *   forces[k] = sum_{e in in(k)} grad_vec[e] - sum_{e in out(k)} grad_vec[e]

@@ -104,3 +104,22 @@ def test_edge_tp_micro_size_sampled():
     assert rel_err(np_(gV[ti]), rV) < FP32_TOL
     assert rel_err(np_(gw[ti]), rw) < FP32_TOL
     assert rel_err(np_(gr[ti]), rr) < FP32_TOL
+
+
+@pytest.mark.parametrize("L,C", [(1, 16), (2, 64), (3, 32)])
+def test_edge_tp_vjp2_through_identity_graph(L, C):
+    """The edge-local product's VJP-of-VJP is the convolution's on the graph
+    where every edge is its own destination and source."""
+    from gpu_common import DeviceProblem
+    say("edge_tp vjp2", L, C)
+    E = 37
+    ar = np.arange(E + 1, dtype=np.int32)
+    vec = workloads.random_vectors(E, 0.8, 5.0, seed=L)
+    wl = workloads.Workload(f"identity_L{L}", L, C, E, ar, ar[:E].copy(), vec, seed=L)
+    p = DeviceProblem(wl)
+    got = [np_(t) for t in p.vjp2()]
+    ref = oracle.vjp2(L, wl.row_ptr, wl.src, wl.vec, wl.x, wl.w, wl.G, wl.ggx, wl.ggw, wl.ggvec)
+    for name, g, r in zip(("dV", "dw", "dr", "dG"), got, ref):
+        assert rel_err(g, r) < FP32_TOL, (name, rel_err(g, r))
+    # and its forward is the edge-local product
+    assert rel_err(np_(p.fwd()), oracle.edge_tp_fwd(L, wl.vec, wl.x, wl.w)) < FP32_TOL

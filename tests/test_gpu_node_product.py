@@ -71,3 +71,43 @@ def test_node_product_full_size_sampled(L, nu):
     ref = oracle.node_product(L, A[rows], W, nu)
     assert rel_err(out[rows], ref) < FP32_TOL, rel_err(out[rows], ref)
     assert np.isfinite(out).all()
+
+
+VJP_CASES = [(0, 8, 5, 4), (1, 5, 7, 3), (2, 128, 6, 5), (2, 100, 4, 1), (3, 64, 5, 4), (3, 130, 3, 2),
+             (4, 16, 4, 6), (4, 128, 3, 3)]
+
+
+@pytest.mark.parametrize("L,C,n,nu", VJP_CASES)
+def test_node_product_vjp_small(L, C, n, nu):
+    import torch
+    from equivariant_interatomic_potentials_amd import etp
+    say("node_product vjp", L, C, n, nu)
+    A, W = workloads.node_features(n, L, C, nu, seed=L * 5 + nu)
+    G = workloads.rng(L + 17, "G").standard_normal(A.shape).astype(np.float32)
+    plan = etp.etp_plan_create(L, C)
+    gA = torch.full(A.shape, float("nan"), device="cuda")
+    etp.etp_node_product_vjp(plan, dev(A), dev(W) if nu > 1 else None, dev(G), gA, nu)
+    ref = oracle.node_product_vjp(L, A, W if nu > 1 else None, G, nu)
+    assert rel_err(np_(gA), ref) < FP32_TOL, rel_err(np_(gA), ref)
+    base = np.random.default_rng(1).standard_normal(A.shape).astype(np.float32)
+    acc = dev(base)
+    etp.etp_node_product_vjp(plan, dev(A), dev(W) if nu > 1 else None, dev(G), acc, nu, etp.ETP_FLAG_ACCUMULATE)
+    assert rel_err(np_(acc), ref + base) < FP32_TOL
+
+
+@pytest.mark.parametrize("L,nu", [(3, 4), (4, 6)])
+def test_node_product_vjp_full_size_sampled(L, nu):
+    import torch
+    from equivariant_interatomic_potentials_amd import etp
+    say("node_product vjp full", L, nu)
+    n, C = 4096, 128
+    A, W = workloads.node_features(n, L, C, nu, seed=11)
+    G = workloads.rng(3, "G").standard_normal(A.shape).astype(np.float32)
+    plan = etp.etp_plan_create(L, C)
+    gA = torch.empty(A.shape, device="cuda")
+    etp.etp_node_product_vjp(plan, dev(A), dev(W), dev(G), gA, nu)
+    rows = np.concatenate([[0], np.sort(np.random.default_rng(L + 1).choice(n, size=32, replace=False)), [n - 1]])
+    got = np_(gA)
+    ref = oracle.node_product_vjp(L, A[rows], W, G[rows], nu)
+    assert rel_err(got[rows], ref) < FP32_TOL, rel_err(got[rows], ref)
+    assert np.isfinite(got).all()

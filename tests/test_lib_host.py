@@ -32,7 +32,7 @@ def header_symbols():
 
 def test_header_symbols_exported():
     names = header_symbols()
-    assert len(names) == 21
+    assert len(names) == 22
     assert sorted(etp.ABI_SYMBOLS) == names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (etp_\w+)$", out, flags=re.M))
@@ -161,7 +161,12 @@ def test_call_validation_without_device():
     assert lib.etp_node_product(plan.handle, 4, 2, None, 8, 8, 0, None) == INV
     assert lib.etp_node_product(plan.handle, 4, 2, 8, 8, 8, 2, None) == INV          # only ACCUMULATE
     assert lib.etp_node_product(plan.handle, 0, 3, None, None, None, 0, None) == 0
+    assert lib.etp_node_product_vjp(plan.handle, 4, 2, 8, 8, None, 8, 0, None) == INV   # grad_out needed
+    assert lib.etp_node_product_vjp(plan.handle, 4, 2, 8, None, 8, 8, 0, None) == INV
+    assert lib.etp_node_product_vjp(plan.handle, 4, 9, 8, 8, 8, 8, 0, None) == INV
+    assert lib.etp_node_product_vjp(plan.handle, 0, 2, None, None, None, None, 0, None) == 0
     bfp = etp.etp_plan_create(2, 8, etp.ETP_BF16)
+    assert lib.etp_node_product_vjp(bfp.handle, 4, 2, 8, 8, 8, 8, 0, None) == UNS
     assert lib.etp_node_product(bfp.handle, 4, 2, 8, 8, 8, 0, None) == UNS
     assert lib.etp_edge_tp_fwd(bfp.handle, 4, 8, 8, 8, 8, 0, None) == UNS
     box = np.array([20.0, 20.0, 30.0], np.float32)
