@@ -87,6 +87,8 @@ def _load():
         lib.oracle_node_product.argtypes = [ctypes.c_int] * 4 + [_f64p, _f64p, _f64p]
         lib.oracle_node_product_vjp.restype = ctypes.c_int
         lib.oracle_node_product_vjp.argtypes = [ctypes.c_int] * 4 + [_f64p, _f64p, _f64p, _f64p]
+        lib.oracle_channel_mix_vjp.restype = ctypes.c_int
+        lib.oracle_channel_mix_vjp.argtypes = [ctypes.c_int] * 5 + [_f64p, _f64p, _f64p]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -241,6 +243,20 @@ def channel_mix(L, out, W):
                                   _p(_nz(y.reshape(-1)), _f64p)):
         raise ValueError("oracle_channel_mix failed")
     return y
+
+
+def channel_mix_vjp(L, gy, W):
+    """gin[n, Dout, C]: the transposed mixing of the cotangent gy[n, (l_max_out+1)^2, C]."""
+    lin, lsh, lout = _lmax(L)
+    gy = _f64(gy)
+    n, _, C = gy.shape
+    W = _f64(W).reshape(-1)
+    Dout = int(sum(2 * p[2] + 1 for p in paths(L)))
+    gin = np.zeros((n, Dout, C))
+    if _load().oracle_channel_mix_vjp(lin, lsh, lout, C, n, _p(_nz(gy.reshape(-1)), _f64p), _p(W, _f64p),
+                                      _p(_nz(gin.reshape(-1)), _f64p)):
+        raise ValueError("oracle_channel_mix_vjp failed")
+    return gin
 
 
 def edge_forces(row_ptr, src, n_src, gr):

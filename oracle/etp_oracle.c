@@ -707,6 +707,45 @@ int oracle_channel_mix(int lin, int lsh, int lout, int C, int n, const double *o
     return 0;
 }
 
+/* VJP of the channel mixing with respect to its input (the mixing is linear,
+ * so this is the transposed map): gin[i][off_p + m][u] = sum_v W_l[(q_p C + u)
+ * C + v] gy[i][l*l + m][v] for every path p of order l = l3_p. */
+int oracle_channel_mix_vjp(int lin, int lsh, int lout, int C, int n, const double *gy, const double *W, double *gin)
+{
+    table t;
+    if (table_make(lin, lsh, lout, &t))
+        return -1;
+    const int Dout = t.Dout, Dy = (lout + 1) * (lout + 1);
+    int64_t wofs[OR_LMAX + 2];
+    int prank[128], pcount[OR_LMAX + 1] = {0};
+    for (int p = 0; p < t.P; ++p) {
+        const int l3 = t.path[3 * p + 2];
+        prank[p] = pcount[l3]++;
+    }
+    wofs[0] = 0;
+    for (int l = 0; l <= lout; ++l)
+        wofs[l + 1] = wofs[l] + (int64_t)pcount[l] * C * C;
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < n; ++i) {
+        for (int p = 0; p < t.P; ++p) {
+            const int l = t.path[3 * p + 2];
+            const double *Wl = W + wofs[l] + (int64_t)prank[p] * C * C;
+            for (int mi = 0; mi < 2 * l + 1; ++mi) {
+                const double *gr = gy + ((int64_t)i * Dy + l * l + mi) * C;
+                double *o = gin + ((int64_t)i * Dout + t.off[p] + mi) * C;
+                for (int u = 0; u < C; ++u) {
+                    double acc = 0.0;
+                    for (int v = 0; v < C; ++v)
+                        acc += Wl[(int64_t)u * C + v] * gr[v];
+                    o[u] = acc;
+                }
+            }
+        }
+    }
+    table_free(&t);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Forces on the atoms                                                       */
 /* ------------------------------------------------------------------------ */

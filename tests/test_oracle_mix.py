@@ -80,3 +80,29 @@ def test_commutes_with_maps_on_components():
     for l in range(L + 1):
         sl = slice(l * l, (l + 1) * (l + 1))
         assert np.abs(y_moved[:, sl] - np.einsum("ab,nbc->nac", A[l], y[:, sl])).max() < 1e-10
+
+
+@pytest.mark.parametrize("L,C", [(1, 3), (2, 4), (3, 2), (4, 1)])
+def test_vjp_is_the_adjoint(L, C):
+    """<gy, mix(in)> = <mix_vjp(gy), in> for random in, gy, W (the map is linear)."""
+    g = np.random.default_rng(30 + L)
+    p, off = offsets(L)
+    n = 4
+    inp = g.standard_normal((n, off[-1], C))
+    gy = g.standard_normal((n, (L + 1) ** 2, C))
+    W = g.standard_normal(sum(oracle.mix_rows(L)) * C * C)
+    lhs = (gy * oracle.channel_mix(L, inp, W)).sum()
+    rhs = (oracle.channel_mix_vjp(L, gy, W) * inp).sum()
+    assert abs(lhs - rhs) < 1e-10 * max(1.0, abs(lhs))
+
+
+def test_vjp_identity_blocks_copy_cotangent():
+    """W_l = stacked identities: every path block of order l receives gy's block of order l."""
+    L, C = 2, 3
+    g = np.random.default_rng(9)
+    p, off = offsets(L)
+    gy = g.standard_normal((5, 9, C))
+    W = np.concatenate([np.tile(np.eye(C), (k, 1)).reshape(-1) for k in oracle.mix_rows(L)])
+    gin = oracle.channel_mix_vjp(L, gy, W)
+    for q, (l1, l2, l3) in enumerate(p):
+        np.testing.assert_allclose(gin[:, off[q]:off[q + 1]], gy[:, l3 * l3:(l3 + 1) ** 2], atol=1e-14)

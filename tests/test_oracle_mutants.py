@@ -68,6 +68,7 @@ MUTANTS = [
     ("np_vjp_gA_operand", "                        gi[s2 * C + u] += s * Bk[s1 * C + u];",
      "                        gi[s2 * C + u] += s * Ai[s1 * C + u];"),
     ("np_vjp_no_identity", "            gi[q] += bb[q];", "            gi[q] += 0.0 * bb[q];"),
+    ("mix_vjp_transposed", "acc += Wl[(int64_t)u * C + v] * gr[v];", "acc += Wl[(int64_t)v * C + u] * gr[v];"),
     ("transpose_unstable", "int64_t k = cursor[src[e]]++;", "int64_t k = src_ptr[src[e] + 1] - 1 - (cursor[src[e]]++ - src_ptr[src[e]]);"),
 ]
 
