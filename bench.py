@@ -145,9 +145,22 @@ def time_channel_mix(etp, plan, out, L, C, N, reps):
     t = a.elapsed_time(b) / reps * 1e-3
     byts = 4.0 * (out.numel() + W.numel() + y.numel())
     flops = 2.0 * sum(N * (2 * l + 1) * rows[l] * C * C for l in range(L + 1))
-    return {"ms": round(t * 1e3, 4), "algo_GBps": byts / t / 1e9, "algo_TFLOPs": flops / t / 1e12,
-            "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS, "mfma_frac": flops / t / 1e12 / MFMA_F32_PEAK_TFLOPS,
-            "bound": "mfma" if flops / (MFMA_F32_PEAK_TFLOPS * 1e12) > byts / (HBM_PEAK_GBS * 1e9) else "hbm"}
+    res = {"ms": round(t * 1e3, 4), "algo_GBps": byts / t / 1e9, "algo_TFLOPs": flops / t / 1e12,
+           "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS, "mfma_frac": flops / t / 1e12 / MFMA_F32_PEAK_TFLOPS,
+           "bound": "mfma" if flops / (MFMA_F32_PEAK_TFLOPS * 1e12) > byts / (HBM_PEAK_GBS * 1e9) else "hbm"}
+    # the VJP (transposed map, same bytes and FLOPs)
+    gin = torch.empty_like(out)
+    for _ in range(2):
+        etp.etp_channel_mix_vjp(plan, y, W, gin)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        etp.etp_channel_mix_vjp(plan, y, W, gin)
+    b.record()
+    torch.cuda.synchronize()
+    tv = a.elapsed_time(b) / reps * 1e-3
+    res.update({"vjp_ms": round(tv * 1e3, 4), "vjp_mfma_frac": flops / tv / 1e12 / MFMA_F32_PEAK_TFLOPS})
+    return res
 
 
 def time_edge_forces(etp, g, gr, N, n_src, E, reps):

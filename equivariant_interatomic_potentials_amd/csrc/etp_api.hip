@@ -16,6 +16,8 @@ namespace etp {
 hipError_t launch_sh(int L, int64_t n, const float *vec, float *Y, float *dY, hipStream_t stream);
 hipError_t launch_mix(int L, int C, int n, const float *in, const float *W, float *y, bool accumulate,
                       hipStream_t stream);
+hipError_t launch_mix_vjp(int L, int C, int n, const float *gy, const float *W, float *gin, bool accumulate,
+                          hipStream_t stream);
 hipError_t launch_node_product(int L, int C, int n, int nu, const float *A, const float *W, float *out,
                                bool accumulate, hipStream_t stream);
 hipError_t launch_edge_tp_fwd(int L, int C, int64_t E, const float *vec, const float *V, const float *w, float *out,
@@ -454,6 +456,21 @@ etp_status etp_channel_mix(etp_plan_t plan, int32_t n_nodes, const float *in, co
         return ETP_ERR_INVALID_ARGUMENT;
     return hip_status(etp::launch_mix(plan->L, plan->C, n_nodes, in, W, out, flags & ETP_FLAG_ACCUMULATE,
                                       static_cast<hipStream_t>(stream)));
+}
+
+etp_status etp_channel_mix_vjp(etp_plan_t plan, int32_t n_nodes, const float *grad_y, const float *W, float *grad_in,
+                               uint32_t flags, void *stream)
+{
+    if (!plan || n_nodes < 0)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (flags & ~static_cast<uint32_t>(ETP_FLAG_ACCUMULATE))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (n_nodes == 0)
+        return ETP_OK;
+    if (!grad_y || !W || !grad_in)
+        return ETP_ERR_INVALID_ARGUMENT;
+    return hip_status(etp::launch_mix_vjp(plan->L, plan->C, n_nodes, grad_y, W, grad_in, flags & ETP_FLAG_ACCUMULATE,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 etp_status etp_edge_tp_fwd(etp_plan_t plan, int64_t n_edges, const float *vec, const float *V, const float *w,

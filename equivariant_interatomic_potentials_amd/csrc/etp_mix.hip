@@ -137,6 +137,97 @@ __global__ void __launch_bounds__(256) mix_kernel(const MixTab tb, const float *
     }
 }
 
+// VJP with respect to the input (the mixing is linear: the transposed map):
+//   gin[i, off_p + m, u] = sum_v W_l[(q_p C + u), v] gy[i, l*l + m, v]
+// per order l and path q one product [n (2l+1)] x C times C x C (W_{l,q}
+// transposed). Same tiling as the forward; blockIdx.y = (path q of order l,
+// 64-column tile); the W chunk is read along v (contiguous) and transposed
+// into the LDS tile.
+__global__ void __launch_bounds__(256) mix_vjp_kernel(const MixTab tb, const float *__restrict__ gy,
+                                                      const float *__restrict__ W, float *__restrict__ gin,
+                                                      const int accumulate)
+{
+    __shared__ float Bs[2][32][kMixCols + 4];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int l = 0;
+    while (l < tb.lout && static_cast<int>(blockIdx.x) >= tb.tiles0[l + 1])
+        ++l;
+    const int C = tb.C, ntc = (C + kMixCols - 1) / kMixCols;
+    const int q = blockIdx.y / ntc, c0 = (blockIdx.y - q * ntc) * kMixCols;
+    if (q >= tb.nl[l])
+        return;  // the whole workgroup: this order has fewer paths
+    const int tile = blockIdx.x - tb.tiles0[l];
+    const int d = 2 * l + 1, M = tb.n * d;
+    const int kq = lane >> 4, col = lane & 15;
+
+    const int ra = tile * 64 + wv * 16 + col;
+    const bool rok = ra < M;
+    const int ia = rok ? ra / d : 0, ma = rok ? ra - ia * d : 0;
+    const float *arow = gy + (static_cast<int64_t>(ia) * tb.Dy + l * l + ma) * C;
+    const float *Wq = W + tb.wofs[l] + static_cast<int64_t>(q) * C * C;
+
+    mix_f4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        acc[t] = mix_f4{0.f, 0.f, 0.f, 0.f};
+
+    const int nchunk = (C + 31) / 32;
+    constexpr int BPT = 32 * kMixCols / 256;
+    float a_nx[8], b_nx[BPT];
+    auto fetch = [&](int ci) {
+        const int v0 = ci * 32;
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) {
+            const int v = v0 + 4 * s8 + kq;
+            a_nx[s8] = (rok && v < C) ? arow[v] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < BPT; ++k) {
+            const int t = threadIdx.x + 256 * k;
+            const int kr = t & 31, cc = t >> 5;  // consecutive threads read consecutive v
+            const int v = v0 + kr, u = c0 + cc;
+            b_nx[k] = (v < C && u < C) ? Wq[static_cast<int64_t>(u) * C + v] : 0.f;
+        }
+    };
+    fetch(0);
+    for (int ci = 0; ci < nchunk; ++ci) {
+        const int buf = ci & 1;
+#pragma unroll
+        for (int k = 0; k < BPT; ++k) {
+            const int t = threadIdx.x + 256 * k;
+            Bs[buf][t & 31][t >> 5] = b_nx[k];
+        }
+        float a[8];
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8)
+            a[s8] = a_nx[s8];
+        __syncthreads();
+        if (ci + 1 < nchunk)
+            fetch(ci + 1);
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s8], Bs[buf][4 * s8 + kq][16 * t + col], acc[t], 0,
+                                                              0, 0);
+        }
+    }
+
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int c = c0 + 16 * t + col;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int r = tile * 64 + wv * 16 + 4 * kq + rr;
+            if (r < M && c < C) {
+                const int i = r / d, m = r - (r / d) * d;
+                float *dst = gin + (static_cast<int64_t>(i) * tb.Dout + tb.off[l][q] + m) * C + c;
+                *dst = accumulate ? *dst + acc[t][rr] : acc[t][rr];
+            }
+        }
+    }
+}
+
 // Path layout of one l_max for the mixing (from the compile-time table).
 template <int L>
 static MixTab mix_table(int C, int n)
@@ -162,22 +253,44 @@ static MixTab mix_table(int C, int n)
     return tb;
 }
 
+static bool mix_table_for(int L, int C, int n, MixTab *tb)
+{
+    switch (L) {
+    case 0: *tb = mix_table<0>(C, n); return true;
+    case 1: *tb = mix_table<1>(C, n); return true;
+    case 2: *tb = mix_table<2>(C, n); return true;
+    case 3: *tb = mix_table<3>(C, n); return true;
+    case 4: *tb = mix_table<4>(C, n); return true;
+    default: return false;
+    }
+}
+
 hipError_t launch_mix(int L, int C, int n, const float *in, const float *W, float *y, bool accumulate,
                       hipStream_t stream)
 {
     if (n == 0)
         return hipSuccess;
     MixTab tb;
-    switch (L) {
-    case 0: tb = mix_table<0>(C, n); break;
-    case 1: tb = mix_table<1>(C, n); break;
-    case 2: tb = mix_table<2>(C, n); break;
-    case 3: tb = mix_table<3>(C, n); break;
-    case 4: tb = mix_table<4>(C, n); break;
-    default: return hipErrorInvalidValue;
-    }
+    if (!mix_table_for(L, C, n, &tb))
+        return hipErrorInvalidValue;
     const dim3 grid(tb.tiles0[L + 1], (C + kMixCols - 1) / kMixCols);
     hipLaunchKernelGGL(mix_kernel, grid, dim3(256), 0, stream, tb, in, W, y, accumulate ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_mix_vjp(int L, int C, int n, const float *gy, const float *W, float *gin, bool accumulate,
+                          hipStream_t stream)
+{
+    if (n == 0)
+        return hipSuccess;
+    MixTab tb;
+    if (!mix_table_for(L, C, n, &tb))
+        return hipErrorInvalidValue;
+    int maxnl = 0;
+    for (int l = 0; l <= L; ++l)
+        maxnl = tb.nl[l] > maxnl ? tb.nl[l] : maxnl;
+    const dim3 grid(tb.tiles0[L + 1], maxnl * ((C + kMixCols - 1) / kMixCols));
+    hipLaunchKernelGGL(mix_vjp_kernel, grid, dim3(256), 0, stream, tb, gy, W, gin, accumulate ? 1 : 0);
     return hipGetLastError();
 }
 

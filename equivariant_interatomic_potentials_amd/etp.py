@@ -31,7 +31,7 @@ ETP_FLAG_VALIDATE = 2
 ABI_SYMBOLS = ("etp_plan_create", "etp_plan_destroy", "etp_plan_info", "etp_plan_tables",
                "etp_csr_transpose_workspace", "etp_csr_transpose", "etp_workspace_size", "etp_sh", "etp_edge_conv_fwd",
                "etp_edge_conv_vjp", "etp_edge_conv_vjp2", "etp_channel_mix", "etp_edge_forces",
-               "etp_neighbor_workspace", "etp_neighbor_count", "etp_neighbor_fill", "etp_node_product", "etp_node_product_vjp",
+               "etp_neighbor_workspace", "etp_neighbor_count", "etp_neighbor_fill", "etp_node_product", "etp_node_product_vjp", "etp_channel_mix_vjp",
                "etp_edge_tp_fwd", "etp_edge_tp_vjp",
                "etp_status_string", "etp_version")
 
@@ -103,6 +103,7 @@ def _load():
         "etp_channel_mix": (st, [vp, i32, vp, vp, vp, u32, vp]),
         "etp_edge_forces": (st, [ctypes.POINTER(etp_graph), vp, vp, u32, vp]),
         "etp_node_product": (st, [vp, i32, i32, vp, vp, vp, u32, vp]),
+        "etp_channel_mix_vjp": (st, [vp, i32, vp, vp, vp, u32, vp]),
         "etp_node_product_vjp": (st, [vp, i32, i32, vp, vp, vp, vp, u32, vp]),
         "etp_edge_tp_fwd": (st, [vp, i64, vp, vp, vp, vp, u32, vp]),
         "etp_edge_tp_vjp": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, u32, vp]),
@@ -353,6 +354,18 @@ def etp_channel_mix(plan: Plan, inp, W, out, flags: int = 0, stream=None):
                                _ptr(W, "W", torch.float32, nw, optional=True),
                                _ptr(out, "out", torch.float32, n * (plan.L + 1) ** 2 * C, optional=True),
                                flags, _stream(stream)), "etp_channel_mix")
+
+
+def etp_channel_mix_vjp(plan: Plan, grad_y, W, grad_in, flags: int = 0, stream=None):
+    """grad_in[n, Dout, C] = the transposed mixing of grad_y[n, (L+1)^2, C]."""
+    import torch
+    n = grad_y.shape[0]
+    C = plan.C
+    _check(lib.etp_channel_mix_vjp(plan.handle, n,
+                                   _ptr(grad_y, "grad_y", torch.float32, n * (plan.L + 1) ** 2 * C, optional=True),
+                                   _ptr(W, "W", torch.float32, sum(mix_rows(plan)) * C * C, optional=True),
+                                   _ptr(grad_in, "grad_in", torch.float32, n * plan.dout_rows * C, optional=True),
+                                   flags, _stream(stream)), "etp_channel_mix_vjp")
 
 
 def etp_edge_forces(graph: Graph, grad_vec, forces, flags: int = 0, stream=None):

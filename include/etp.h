@@ -210,6 +210,17 @@ ETP_API etp_status etp_edge_conv_vjp2(etp_plan_t plan, const etp_graph *g, const
 ETP_API etp_status etp_channel_mix(etp_plan_t plan, int32_t n_nodes, const float *in, const float *W, float *out,
                                    uint32_t flags, void *stream);
 
+/* VJP of etp_channel_mix with respect to its input (the mixing is linear, so
+ * this is the transposed map; forces flow through it):
+ *   grad_in[i][off_p + m][u] = sum_v W_l[(q_p*C + u)*C + v] * grad_y[i][l*l + m][v]
+ * for every path p of order l = l3_p. grad_y: DEVICE float
+ * [n_nodes][(l_max+1)^2][C]; W as for etp_channel_mix; grad_in: DEVICE float
+ * [n_nodes][dout_rows][C]. fp32 matrix-core accumulation. The weight gradient
+ * (a sum over all nodes) is not computed. flags: ETP_FLAG_ACCUMULATE adds into
+ * grad_in. Errors as for etp_channel_mix. */
+ETP_API etp_status etp_channel_mix_vjp(etp_plan_t plan, int32_t n_nodes, const float *grad_y, const float *W,
+                                       float *grad_in, uint32_t flags, void *stream);
+
 /* Edge-local tensor product: the convolution's message without the
  * destination sum, one output block per edge (the pair-wise tensor product of
  * Allegro, whose energy is a sum of per-pair terms: "Scaling the leading

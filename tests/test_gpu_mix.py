@@ -67,3 +67,22 @@ def test_channel_mix_micro_shape():
     etp.etp_channel_mix(plan, dev(inp), dev(W), out)
     ref = oracle.channel_mix(L, inp, W)
     assert rel_err(np_(out), ref) < FP32_TOL
+
+
+@pytest.mark.parametrize("L,C,n", [(0, 8, 5), (1, 5, 7), (2, 64, 33), (2, 128, 70), (3, 40, 11), (4, 16, 9),
+                                   (2, 200, 13), (3, 256, 6)])
+def test_channel_mix_vjp(L, C, n):
+    import torch
+    from equivariant_interatomic_potentials_amd import etp
+    say("mix vjp", L, C, n)
+    _, W = mix_case(L, C, n, seed=L * 1000 + C + n)
+    gy = workloads.rng(L + C + n, "G").standard_normal((n, (L + 1) ** 2, C)).astype(np.float32)
+    plan = etp.etp_plan_create(L, C)
+    gin = torch.full((n, plan.dout_rows, C), float("nan"), device="cuda")
+    etp.etp_channel_mix_vjp(plan, dev(gy), dev(W), gin)
+    ref = oracle.channel_mix_vjp(L, gy, W)
+    assert rel_err(np_(gin), ref) < FP32_TOL, rel_err(np_(gin), ref)
+    base = np.random.default_rng(0).standard_normal(ref.shape).astype(np.float32)
+    acc = dev(base)
+    etp.etp_channel_mix_vjp(plan, dev(gy), dev(W), acc, etp.ETP_FLAG_ACCUMULATE)
+    assert rel_err(np_(acc), ref + base) < FP32_TOL

@@ -32,7 +32,7 @@ def header_symbols():
 
 def test_header_symbols_exported():
     names = header_symbols()
-    assert len(names) == 22
+    assert len(names) == 23
     assert sorted(etp.ABI_SYMBOLS) == names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (etp_\w+)$", out, flags=re.M))
@@ -141,6 +141,10 @@ def test_call_validation_without_device():
     assert lib.etp_channel_mix(plan.handle, 4, None, 8, 8, 0, None) == INV
     assert lib.etp_channel_mix(plan.handle, 4, 8, 8, 8, 2, None) == INV      # only ACCUMULATE
     assert lib.etp_channel_mix(plan.handle, 0, None, None, None, 0, None) == 0
+    assert lib.etp_channel_mix_vjp(None, 4, 8, 8, 8, 0, None) == INV
+    assert lib.etp_channel_mix_vjp(plan.handle, 4, 8, None, 8, 0, None) == INV
+    assert lib.etp_channel_mix_vjp(plan.handle, 4, 8, 8, 8, 2, None) == INV
+    assert lib.etp_channel_mix_vjp(plan.handle, 0, None, None, None, 0, None) == 0
     assert lib.etp_edge_forces(None, 8, 8, 0, None) == INV
     assert lib.etp_edge_forces(ctypes.byref(g4), 8, 8, 0, None) == INV                 # no transpose
     assert lib.etp_edge_forces(ctypes.byref(g5), None, 8, 0, None) == INV
