@@ -250,8 +250,25 @@ def time_edge_tp(etp, plan, L, C, E, Din, P, Dout, vec, w, reps):
         res[name + "_ms"] = round(t * 1e3, 4)
         res[name + "_algo_GBps"] = byts / t / 1e9
         res[name + "_hbm_frac"] = byts / t / 1e9 / HBM_PEAK_GBS
+    # VJP-of-VJP: reads vec, V, w, G and the three cotangents, writes dV, dw, dr, dG
+    ggV, ggw, ggv = torch.randn_like(V), torch.randn_like(w), torch.randn(E, 3, device="cuda")
+    dG = torch.empty_like(G)
+    f = lambda: etp.etp_edge_tp_vjp2(plan, vec, V, w, G, ggV, ggw, ggv, gV, gw, gr, dG)
+    byts = 4.0 * E * (3 + 2 * Din * C + 2 * P * C + Dout * C + 3 + Din * C + P * C + 3 + Dout * C)
+    for _ in range(2):
+        f()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        f()
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / reps * 1e-3
+    res.update({"vjp2_ms": round(t * 1e3, 4), "vjp2_algo_GBps": byts / t / 1e9,
+                "vjp2_hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS})
     res.update({"edges": E, "l_max": L, "channels": C, "bound": "hbm"})
-    del V, G, out, gV, gw, gr
+    del V, G, out, gV, gw, gr, ggV, ggw, ggv, dG
     torch.cuda.empty_cache()
     return res
 

@@ -26,6 +26,9 @@ hipError_t launch_edge_tp_vjp(int L, int C, int64_t E, const float *vec, const f
                               const float *G, float *gV, float *gw, float *gr, bool accumulate, hipStream_t stream);
 hipError_t launch_node_product_vjp(int L, int C, int n, int nu, const float *A, const float *W, const float *G,
                                    float *gA, bool accumulate, hipStream_t stream);
+hipError_t launch_edge_tp_vjp2(int L, int C, int64_t E, const float *vec, const float *V, const float *w,
+                               const float *G, const float *ggV, const float *ggw, const float *ggvec, float *dV,
+                               float *dw, float *dr, float *dG, bool accumulate, hipStream_t stream);
 hipError_t launch_forces(int n_dst, int n_src, const int *row_ptr, const int *src_ptr, const int *perm,
                          const float *gr, float *F, bool accumulate, hipStream_t stream);
 size_t transpose_workspace_bytes(int n_src);
@@ -507,6 +510,25 @@ etp_status etp_edge_tp_vjp(etp_plan_t plan, int64_t n_edges, const float *vec, c
     return hip_status(etp::launch_edge_tp_vjp(plan->L, plan->C, n_edges, vec, V, w, grad_out, grad_V, grad_w,
                                               grad_vec, flags & ETP_FLAG_ACCUMULATE,
                                               static_cast<hipStream_t>(stream)));
+}
+
+etp_status etp_edge_tp_vjp2(etp_plan_t plan, int64_t n_edges, const float *vec, const float *V, const float *w,
+                            const float *grad_out, const float *gg_V, const float *gg_w, const float *gg_vec, float *d_V,
+                            float *d_w, float *d_vec, float *d_grad_out, uint32_t flags, void *stream)
+{
+    if (!plan || n_edges < 0 || (flags & ~static_cast<uint32_t>(ETP_FLAG_ACCUMULATE)))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (n_edges >= kMaxEdges)
+        return ETP_ERR_UNSUPPORTED;
+    if (plan->dtype != ETP_F32)
+        return ETP_ERR_UNSUPPORTED;
+    if (n_edges == 0 || (!d_V && !d_w && !d_vec && !d_grad_out))
+        return ETP_OK;
+    if (!vec || !V || !w || !grad_out)
+        return ETP_ERR_INVALID_ARGUMENT;
+    return hip_status(etp::launch_edge_tp_vjp2(plan->L, plan->C, n_edges, vec, V, w, grad_out, gg_V, gg_w, gg_vec,
+                                               d_V, d_w, d_vec, d_grad_out, flags & ETP_FLAG_ACCUMULATE,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 etp_status etp_node_product(etp_plan_t plan, int32_t n_nodes, int32_t corr_order, const float *A, const float *W,

@@ -204,6 +204,152 @@ __global__ void __launch_bounds__(256) edge_tp_vjp_kernel(const int64_t E, const
     }
 }
 
+// VJP of the VJP: with cotangents (V', W', R') on (gV, gw, gr), the
+// gradients of S = <V', gV> + <W', gw> + <R', gr> with respect to V (dV), w
+// (dw), vec (dr) and G (dG). With Yd = grad Y . R' and, per (m1, m3) pair,
+// K = sum_{m2} C Y_{m2}, Kd = sum_{m2} C Yd_{m2}:
+//   dG[p, m3] += K (w V'[m1] + W' V[m1]) + Kd w V[m1]
+//   dV[m1]    += G[p, m3] (W' K + w Kd)
+//   dw[p]     += G[p, m3] (K V'[m1] + Kd V[m1])
+//   Z1[m2]    += C G (w V' + W' V),  Z2[m2] += C G w V
+//   dr = sum_b (sum over channels of Z1_b) grad Y_b + (sum of Z2_b) H_b R'.
+// One wave per edge, every channel chunk (as the VJP); the SH jets for dr are
+// formed once more at the end instead of being held through the loop.
+template <int L, bool ACC>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(L <= 2 ? 4 : (L == 3 ? 2 : 1))))
+edge_tp_vjp2_kernel(const int64_t E, const int C, const float *__restrict__ vec, const float *__restrict__ V,
+                    const float *__restrict__ w, const float *__restrict__ G, const float *__restrict__ ggV,
+                    const float *__restrict__ ggw, const float *__restrict__ ggvec, float *__restrict__ dV,
+                    float *__restrict__ dw, float *__restrict__ dr, float *__restrict__ dG)
+{
+    constexpr int P = kTab<L>.P, DIN = kTab<L>.din_rows, DOUT = kTab<L>.dout_rows, DSH = kTab<L>.dsh;
+    const int lane = threadIdx.x & 63;
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * 4 + wave_id();
+    if (e >= E)
+        return;
+    const int cw = (C + 63) >> 6;
+    const uint32_t rowb = static_cast<uint32_t>(C) * 4u;
+    // a null array is an empty range: its loads read 0 and its stores drop
+    auto blk = [&](const float *base, int rows) {
+        return make_rsrc(base ? base + e * rows * C : nullptr, base ? rows * rowb : 0u);
+    };
+    const rsrc_t rv = blk(V, DIN), rvp = blk(ggV, DIN), rw = blk(w, P), rwp = blk(ggw, P), rg = blk(G, DOUT);
+    const rsrc_t rdv = blk(dV, DIN), rdw = blk(dw, P), rdg = blk(dG, DOUT);
+
+    const float rx = vec[3 * e], ry = vec[3 * e + 1], rz = vec[3 * e + 2];
+    float px = 0.f, py = 0.f, pz = 0.f;
+    if (ggvec) {
+        px = ggvec[3 * e];
+        py = ggvec[3 * e + 1];
+        pz = ggvec[3 * e + 2];
+    }
+    float Y[DSH], Yd[DSH];
+    sh_grad_emit<L>(rx, ry, rz, [&](auto b, const D3 &y) {
+        Y[b] = y.v;
+        Yd[b] = y.g0 * px + y.g1 * py + y.g2 * pz;
+    });
+    float Z1[DSH], Z2[DSH];
+    static_range<0, DSH>([&](auto b) {
+        Z1[b] = 0.f;
+        Z2[b] = 0.f;
+    });
+
+    for (int chunk = 0; chunk < cw; ++chunk) {
+        static_range<0, DSH>([&](auto b) {
+            settle(Y[b]);
+            settle(Yd[b]);
+        });
+        const int u = chunk * 64 + lane;
+        const uint32_t vo = u < C ? static_cast<uint32_t>(u) * 4u : kOOB;
+        float x[DIN], xp[DIN], gx[DIN];
+        static_range<0, DIN>([&](auto r) {
+            x[r] = bload<float, kNT>(rv, vo, r * rowb);
+            xp[r] = bload<float, kNT>(rvp, vo, r * rowb);
+            gx[r] = 0.f;
+        });
+        float gb[2][2 * L + 1], wb[2], wpb[2];
+        auto fetch = [&](auto pc, auto slot) {
+            constexpr Path pa = kTab<L>.path[pc];
+            wb[slot] = bload<float, kNT>(rw, vo, pc * rowb);
+            wpb[slot] = bload<float, kNT>(rwp, vo, pc * rowb);
+            static_range<0, 2 * pa.l3 + 1>(
+                [&](auto m) { gb[slot][m] = bload<float, kNT>(rg, vo, (pa.out_row + m) * rowb); });
+        };
+        fetch(ic<0>{}, ic<0>{});
+        static_range<0, P>([&](auto pc) {
+            constexpr Path pa = kTab<L>.path[pc];
+            constexpr int cur = pc % 2;
+            if constexpr (pc + 1 < P)
+                fetch(ic<pc + 1>{}, ic<1 - cur>{});
+            const float wv = wb[cur], wpv = wpb[cur];
+            float dg[2 * pa.l3 + 1];
+            static_range<0, 2 * pa.l3 + 1>([&](auto m) { dg[m] = 0.f; });
+            float sw = 0.f;  // dS/dw[e, p, u]
+            static_range<pa.pr0, pa.pr1>([&](auto qc) {
+                constexpr Pair pr = kTab<L>.pair[qc];
+                constexpr int r1 = pa.x_row + pa.l1 + pr.m1, c3 = pr.m3 + pa.l3;
+                const float k = pair_coef<L, qc>(Y), kd = pair_coef<L, qc>(Yd);
+                const float xm = x[r1], xpm = xp[r1], g = gb[cur][c3];
+                const float uy = __builtin_fmaf(wv, xpm, wpv * xm);  // multiplies Y
+                const float vy = wv * xm;                            // multiplies Yd
+                dg[c3] = __builtin_fmaf(k, uy, __builtin_fmaf(kd, vy, dg[c3]));
+                gx[r1] = __builtin_fmaf(g, __builtin_fmaf(wpv, k, wv * kd), gx[r1]);
+                sw = __builtin_fmaf(g, __builtin_fmaf(k, xpm, kd * xm), sw);
+                const float gu = g * uy, gv = g * vy;
+                static_range<pr.t0, pr.t1>([&](auto tc) {
+                    constexpr Entry en = kTab<L>.nz[kTab<L>.pair_entries[tc]];
+                    constexpr int b = pa.y_row + pa.l2 + en.m2;
+                    Z1[b] = __builtin_fmaf(en.fval, gu, Z1[b]);
+                    Z2[b] = __builtin_fmaf(en.fval, gv, Z2[b]);
+                });
+            });
+            static_range<0, 2 * pa.l3 + 1>([&](auto m) {
+                const uint32_t so = (pa.out_row + m) * rowb;
+                float v = dg[m];
+                if constexpr (ACC)
+                    v += bload<float>(rdg, vo, so);
+                bstore<float, kNT>(v, rdg, vo, so);
+            });
+            {
+                float v = sw;
+                if constexpr (ACC)
+                    v += bload<float>(rdw, vo, pc * rowb);
+                bstore<float, kNT>(v, rdw, vo, pc * rowb);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        static_range<0, DIN>([&](auto r) {
+            float v = gx[r];
+            if constexpr (ACC)
+                v += bload<float>(rdv, vo, r * rowb);
+            bstore<float, kNT>(v, rdv, vo, r * rowb);
+        });
+    }
+    if (dr) {
+        float g0 = 0.f, g1 = 0.f, g2 = 0.f;
+        static_range<0, DSH>([&](auto b) {
+            Z1[b] = wave_sum_to_lane63(Z1[b]);
+            Z2[b] = wave_sum_to_lane63(Z2[b]);
+        });
+        sh_jet_emit<L>(rx, ry, rz, px, py, pz, [&](auto b, const Jet &y) {
+            g0 = __builtin_fmaf(Z1[b], y.b0, __builtin_fmaf(Z2[b], y.d0, g0));
+            g1 = __builtin_fmaf(Z1[b], y.b1, __builtin_fmaf(Z2[b], y.d1, g1));
+            g2 = __builtin_fmaf(Z1[b], y.b2, __builtin_fmaf(Z2[b], y.d2, g2));
+        });
+        if (lane == 63) {
+            float *ge = dr + 3 * e;
+            if constexpr (ACC) {
+                g0 += ge[0];
+                g1 += ge[1];
+                g2 += ge[2];
+            }
+            ge[0] = g0;
+            ge[1] = g1;
+            ge[2] = g2;
+        }
+    }
+}
+
 #define ETP_EDGE_TP_CASE(F, LL, ...)                                                        \
     case LL:                                                                                \
         if (accumulate)                                                                     \
@@ -237,6 +383,18 @@ hipError_t launch_edge_tp_vjp(int L, int C, int64_t E, const float *vec, const f
         return hipSuccess;
     const dim3 grid(static_cast<unsigned>((E + 3) / 4)), block(256);
     ETP_EDGE_TP_CASES(edge_tp_vjp_kernel, grid, block, 0, stream, E, C, vec, V, w, G, gV, gw, gr)
+    return hipGetLastError();
+}
+
+hipError_t launch_edge_tp_vjp2(int L, int C, int64_t E, const float *vec, const float *V, const float *w,
+                               const float *G, const float *ggV, const float *ggw, const float *ggvec, float *dV,
+                               float *dw, float *dr, float *dG, bool accumulate, hipStream_t stream)
+{
+    if (E == 0)
+        return hipSuccess;
+    const dim3 grid(static_cast<unsigned>((E + 3) / 4)), block(256);
+    ETP_EDGE_TP_CASES(edge_tp_vjp2_kernel, grid, block, 0, stream, E, C, vec, V, w, G, ggV, ggw, ggvec, dV, dw, dr,
+                      dG)
     return hipGetLastError();
 }
 

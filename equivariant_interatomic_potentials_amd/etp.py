@@ -32,7 +32,7 @@ ABI_SYMBOLS = ("etp_plan_create", "etp_plan_destroy", "etp_plan_info", "etp_plan
                "etp_csr_transpose_workspace", "etp_csr_transpose", "etp_workspace_size", "etp_sh", "etp_edge_conv_fwd",
                "etp_edge_conv_vjp", "etp_edge_conv_vjp2", "etp_channel_mix", "etp_edge_forces",
                "etp_neighbor_workspace", "etp_neighbor_count", "etp_neighbor_fill", "etp_node_product", "etp_node_product_vjp", "etp_channel_mix_vjp",
-               "etp_edge_tp_fwd", "etp_edge_tp_vjp",
+               "etp_edge_tp_fwd", "etp_edge_tp_vjp", "etp_edge_tp_vjp2",
                "etp_status_string", "etp_version")
 
 
@@ -107,6 +107,7 @@ def _load():
         "etp_node_product_vjp": (st, [vp, i32, i32, vp, vp, vp, vp, u32, vp]),
         "etp_edge_tp_fwd": (st, [vp, i64, vp, vp, vp, vp, u32, vp]),
         "etp_edge_tp_vjp": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, u32, vp]),
+        "etp_edge_tp_vjp2": (st, [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, u32, vp]),
         "etp_neighbor_workspace": (st, [i32, vp, ctypes.c_float, ctypes.POINTER(ctypes.c_size_t)]),
         "etp_neighbor_count": (st, [i32, vp, vp, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]),
         "etp_neighbor_fill": (st, [i32, vp, vp, ctypes.c_float, vp, i64, vp, vp, u32, vp, ctypes.c_size_t, vp]),
@@ -427,6 +428,23 @@ def etp_edge_tp_vjp(plan: Plan, vec, V, w, grad_out, grad_V=None, grad_w=None, g
                                _ptr(grad_w, "grad_w", f32, E * plan.P * C, optional=True),
                                _ptr(grad_vec, "grad_vec", f32, 3 * E, optional=True), flags, _stream(stream)),
            "etp_edge_tp_vjp")
+
+
+def etp_edge_tp_vjp2(plan: Plan, vec, V, w, grad_out, gg_V=None, gg_w=None, gg_vec=None, d_V=None, d_w=None,
+                     d_vec=None, d_grad_out=None, flags: int = 0, stream=None):
+    import torch
+    E, C = vec.numel() // 3, plan.C
+    f32 = torch.float32
+    nv, nw, no = E * plan.din_rows * C, E * plan.P * C, E * plan.dout_rows * C
+    _check(lib.etp_edge_tp_vjp2(plan.handle, E, _ptr(vec, "vec", f32, 3 * E, optional=True),
+                                _ptr(V, "V", f32, nv, optional=True), _ptr(w, "w", f32, nw, optional=True),
+                                _ptr(grad_out, "grad_out", f32, no, optional=True),
+                                _ptr(gg_V, "gg_V", f32, nv, optional=True), _ptr(gg_w, "gg_w", f32, nw, optional=True),
+                                _ptr(gg_vec, "gg_vec", f32, 3 * E, optional=True),
+                                _ptr(d_V, "d_V", f32, nv, optional=True), _ptr(d_w, "d_w", f32, nw, optional=True),
+                                _ptr(d_vec, "d_vec", f32, 3 * E, optional=True),
+                                _ptr(d_grad_out, "d_grad_out", f32, no, optional=True), flags, _stream(stream)),
+           "etp_edge_tp_vjp2")
 
 
 def _box3(box):

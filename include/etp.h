@@ -241,6 +241,17 @@ ETP_API etp_status etp_edge_tp_fwd(etp_plan_t plan, int64_t n_edges, const float
 ETP_API etp_status etp_edge_tp_vjp(etp_plan_t plan, int64_t n_edges, const float *vec, const float *V, const float *w,
                                    const float *grad_out, float *grad_V, float *grad_w, float *grad_vec,
                                    uint32_t flags, void *stream);
+/* VJP of the edge-local VJP (force training): with cotangents (gg_V, gg_w,
+ * gg_vec) on (grad_V, grad_w, grad_vec), the gradients of
+ * S = <gg_V, grad_V> + <gg_w, grad_w> + <gg_vec, grad_vec> with respect to V
+ * (d_V), w (d_w), vec (d_vec) and grad_out (d_grad_out); the same as
+ * etp_edge_conv_vjp2 on the graph where every edge is its own destination
+ * and source. Cotangents may be NULL (zero); outputs may be NULL. Shapes and
+ * flags as for etp_edge_tp_vjp. */
+ETP_API etp_status etp_edge_tp_vjp2(etp_plan_t plan, int64_t n_edges, const float *vec, const float *V,
+                                    const float *w, const float *grad_out, const float *gg_V, const float *gg_w,
+                                    const float *gg_vec, float *d_V, float *d_w, float *d_vec, float *d_grad_out,
+                                    uint32_t flags, void *stream);
 
 /* Node-local correlation product: weighted products of each node's irreps
  * with themselves, applied step by step and truncated to orders <= l_max

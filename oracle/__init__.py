@@ -302,6 +302,13 @@ def edge_tp_vjp(L, vec, V, w, G):
     return vjp(L, ar, ar[:E], vec, V, w, G)
 
 
+def edge_tp_vjp2(L, vec, V, w, G, ggV=None, ggw=None, ggvec=None):
+    """(dV, dw, dr, dG) of the edge-local tensor product's VJP-of-VJP."""
+    E = np.asarray(vec).reshape(-1, 3).shape[0]
+    ar = np.arange(E + 1, dtype=np.int32)
+    return vjp2(L, ar, ar[:E], vec, V, w, G, ggV, ggw, ggvec)
+
+
 def node_product(L, A, W, nu):
     """Node-local correlation product: out[n, (L+1)^2, C] = B_1 + ... + B_nu with
     B_1 = A and B_{k+1} = sum_p W[k-1, p] * CG_p(B_k, A), channel-wise."""

@@ -123,3 +123,52 @@ def test_edge_tp_vjp2_through_identity_graph(L, C):
         assert rel_err(g, r) < FP32_TOL, (name, rel_err(g, r))
     # and its forward is the edge-local product
     assert rel_err(np_(p.fwd()), oracle.edge_tp_fwd(L, wl.vec, wl.x, wl.w)) < FP32_TOL
+
+
+@pytest.mark.parametrize("L,C,E", [(0, 8, 21), (1, 5, 19), (2, 64, 23), (2, 130, 9), (3, 64, 13), (4, 32, 7)])
+def test_edge_tp_vjp2_small(L, C, E):
+    import torch
+    from equivariant_interatomic_potentials_amd import etp
+    say("edge_tp vjp2", L, C, E)
+    vec, V, w, G = inputs(L, C, E, seed=L * 29 + C)
+    g = np.random.default_rng(L + C)
+    ggV = g.standard_normal(V.shape).astype(np.float32)
+    ggw = g.standard_normal(w.shape).astype(np.float32)
+    ggv = g.standard_normal(vec.shape).astype(np.float32)
+    plan = etp.etp_plan_create(L, C)
+    outs = [torch.full(a.shape, float("nan"), device="cuda") for a in (V, w, vec, G)]
+    etp.etp_edge_tp_vjp2(plan, dev(vec), dev(V), dev(w), dev(G), dev(ggV), dev(ggw), dev(ggv), *outs)
+    ref = oracle.edge_tp_vjp2(L, vec, V, w, G, ggV, ggw, ggv)
+    for name, got, r in zip(("dV", "dw", "dr", "dG"), outs, ref):
+        assert rel_err(np_(got), r) < FP32_TOL, (name, rel_err(np_(got), r))
+    # one cotangent at a time (the others null), accumulating into dr
+    base = np.random.default_rng(3).standard_normal(vec.shape).astype(np.float32)
+    dr = dev(base)
+    etp.etp_edge_tp_vjp2(plan, dev(vec), dev(V), dev(w), dev(G), None, None, dev(ggv), d_vec=dr,
+                         flags=etp.ETP_FLAG_ACCUMULATE)
+    ref_r = oracle.edge_tp_vjp2(L, vec, V, w, G, None, None, ggv)[2]
+    assert rel_err(np_(dr), ref_r + base) < FP32_TOL
+
+
+def test_edge_tp_vjp2_micro_size_sampled():
+    import torch
+    from equivariant_interatomic_potentials_amd import etp
+    say("edge_tp vjp2 micro")
+    L, C = 2, 128
+    wl = workloads.get("micro")
+    E = wl.E
+    V = workloads.device_normal((E, 9, C), 3, "x", 8192)
+    w = dev(wl.w)
+    G = workloads.device_normal((E, 51, C), 4, "G", 8192)
+    ggV = workloads.device_normal((E, 9, C), 5, "ggx", 8192)
+    ggw = workloads.device_normal((E, 15, C), 6, "ggw", 8192)
+    ggv = dev(wl.ggvec)
+    plan = etp.etp_plan_create(L, C)
+    dV, dw, dr, dG = torch.empty_like(V), torch.empty_like(w), torch.empty(E, 3, device="cuda"), torch.empty_like(G)
+    etp.etp_edge_tp_vjp2(plan, dev(wl.vec), V, w, G, ggV, ggw, ggv, dV, dw, dr, dG)
+    idx = np.concatenate([[0], np.sort(np.random.default_rng(1).choice(E, size=48, replace=False)), [E - 1]])
+    ti = torch.from_numpy(idx).cuda()
+    ref = oracle.edge_tp_vjp2(L, wl.vec[idx], np_(V[ti]), np_(w[ti]), np_(G[ti]), np_(ggV[ti]), np_(ggw[ti]),
+                              wl.ggvec[idx])
+    for name, got, r in zip(("dV", "dw", "dr", "dG"), (dV, dw, dr, dG), ref):
+        assert rel_err(np_(got[ti]), r) < FP32_TOL, (name, rel_err(np_(got[ti]), r))

@@ -32,7 +32,7 @@ def header_symbols():
 
 def test_header_symbols_exported():
     names = header_symbols()
-    assert len(names) == 23
+    assert len(names) == 24
     assert sorted(etp.ABI_SYMBOLS) == names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (etp_\w+)$", out, flags=re.M))
@@ -157,6 +157,9 @@ def test_call_validation_without_device():
     assert lib.etp_edge_tp_fwd(plan.handle, 0, None, None, None, None, 0, None) == 0
     assert lib.etp_edge_tp_vjp(plan.handle, 4, 8, 8, 8, None, 8, 8, 8, 0, None) == INV   # grad_out needed
     assert lib.etp_edge_tp_vjp(plan.handle, 4, 8, 8, 8, 8, None, None, None, 0, None) == 0  # nothing asked
+    assert lib.etp_edge_tp_vjp2(plan.handle, 4, 8, 8, 8, None, None, None, None, 8, 8, 8, 8, 0, None) == INV
+    assert lib.etp_edge_tp_vjp2(plan.handle, 4, 8, 8, 8, 8, None, None, None, None, None, None, None, 0, None) == 0
+    assert lib.etp_edge_tp_vjp2(plan.handle, 4, 8, 8, 8, 8, None, None, None, 8, 8, 8, 8, 4, None) == INV
     assert lib.etp_node_product(None, 4, 2, 8, 8, 8, 0, None) == INV
     assert lib.etp_node_product(plan.handle, -1, 2, 8, 8, 8, 0, None) == INV
     assert lib.etp_node_product(plan.handle, 4, 0, 8, 8, 8, 0, None) == INV
