@@ -37,8 +37,11 @@ CFLAGS = [
 def units():
     """(source, object, extra flags) for every translation unit."""
     out = []
-    for name in ("etp_api", "etp_sh", "etp_graph", "etp_mix", "etp_forces", "etp_neighbors", "etp_node_product", "etp_edge_tp"):
+    for name in ("etp_api", "etp_sh", "etp_graph", "etp_mix", "etp_forces", "etp_neighbors", "etp_node_product"):
         out.append((os.path.join(CSRC, name + ".hip"), os.path.join(BUILD, name + ".o"), []))
+    for L in range(5):
+        out.append((os.path.join(CSRC, "etp_edge_tp.hip"), os.path.join(BUILD, f"etp_edge_tp_L{L}.o"),
+                    [f"-DETP_L={L}"]))
     for name in ("etp_dst", "etp_src"):
         for L in range(5):
             for xt in (0, 1):

@@ -20,15 +20,47 @@ hipError_t launch_mix_vjp(int L, int C, int n, const float *gy, const float *W, 
                           hipStream_t stream);
 hipError_t launch_node_product(int L, int C, int n, int nu, const float *A, const float *W, float *out,
                                bool accumulate, hipStream_t stream);
+// the edge-local product, one translation unit per l_max
+template <int L>
+hipError_t edge_tp_fwd_l(int C, int64_t E, const float *vec, const float *V, const float *w, float *out,
+                         bool accumulate, hipStream_t stream);
+template <int L>
+hipError_t edge_tp_vjp_l(int C, int64_t E, const float *vec, const float *V, const float *w, const float *G,
+                         float *gV, float *gw, float *gr, bool accumulate, hipStream_t stream);
+template <int L>
+hipError_t edge_tp_vjp2_l(int C, int64_t E, const float *vec, const float *V, const float *w, const float *G,
+                          const float *ggV, const float *ggw, const float *ggvec, float *dV, float *dw, float *dr,
+                          float *dG, bool accumulate, hipStream_t stream);
+
+#define ETP_BY_L(F, ...)                              \
+    switch (L) {                                      \
+    case 0: return F<0>(__VA_ARGS__);                 \
+    case 1: return F<1>(__VA_ARGS__);                 \
+    case 2: return F<2>(__VA_ARGS__);                 \
+    case 3: return F<3>(__VA_ARGS__);                 \
+    case 4: return F<4>(__VA_ARGS__);                 \
+    default: return hipErrorInvalidValue;             \
+    }
+
 hipError_t launch_edge_tp_fwd(int L, int C, int64_t E, const float *vec, const float *V, const float *w, float *out,
-                              bool accumulate, hipStream_t stream);
+                              bool accumulate, hipStream_t stream)
+{
+    ETP_BY_L(edge_tp_fwd_l, C, E, vec, V, w, out, accumulate, stream)
+}
+
 hipError_t launch_edge_tp_vjp(int L, int C, int64_t E, const float *vec, const float *V, const float *w,
-                              const float *G, float *gV, float *gw, float *gr, bool accumulate, hipStream_t stream);
+                              const float *G, float *gV, float *gw, float *gr, bool accumulate, hipStream_t stream)
+{
+    ETP_BY_L(edge_tp_vjp_l, C, E, vec, V, w, G, gV, gw, gr, accumulate, stream)
+}
 hipError_t launch_node_product_vjp(int L, int C, int n, int nu, const float *A, const float *W, const float *G,
                                    float *gA, bool accumulate, hipStream_t stream);
 hipError_t launch_edge_tp_vjp2(int L, int C, int64_t E, const float *vec, const float *V, const float *w,
                                const float *G, const float *ggV, const float *ggw, const float *ggvec, float *dV,
-                               float *dw, float *dr, float *dG, bool accumulate, hipStream_t stream);
+                               float *dw, float *dr, float *dG, bool accumulate, hipStream_t stream)
+{
+    ETP_BY_L(edge_tp_vjp2_l, C, E, vec, V, w, G, ggV, ggw, ggvec, dV, dw, dr, dG, accumulate, stream)
+}
 hipError_t launch_forces(int n_dst, int n_src, const int *row_ptr, const int *src_ptr, const int *perm,
                          const float *gr, float *F, bool accumulate, hipStream_t stream);
 size_t transpose_workspace_bytes(int n_src);

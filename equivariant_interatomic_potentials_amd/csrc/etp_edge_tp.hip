@@ -350,52 +350,59 @@ edge_tp_vjp2_kernel(const int64_t E, const int C, const float *__restrict__ vec,
     }
 }
 
-#define ETP_EDGE_TP_CASE(F, LL, ...)                                                        \
-    case LL:                                                                                \
-        if (accumulate)                                                                     \
-            hipLaunchKernelGGL(HIP_KERNEL_NAME(F<LL, true>), __VA_ARGS__);                  \
-        else                                                                                \
-            hipLaunchKernelGGL(HIP_KERNEL_NAME(F<LL, false>), __VA_ARGS__);                 \
-        break;
-#define ETP_EDGE_TP_CASES(F, ...)                                                           \
-    switch (L) {                                                                            \
-        ETP_EDGE_TP_CASE(F, 0, __VA_ARGS__) ETP_EDGE_TP_CASE(F, 1, __VA_ARGS__)             \
-        ETP_EDGE_TP_CASE(F, 2, __VA_ARGS__) ETP_EDGE_TP_CASE(F, 3, __VA_ARGS__)             \
-        ETP_EDGE_TP_CASE(F, 4, __VA_ARGS__)                                                 \
-    default: return hipErrorInvalidValue;                                                   \
-    }
+// This file is compiled once per l_max (-DETP_L=0..4, in parallel); the
+// C-ABI layer dispatches on l_max to the instantiation of that unit.
+#define ETP_EDGE_TP_LAUNCH(F, ...)                                              \
+    if (accumulate)                                                             \
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(F<L, true>), __VA_ARGS__);           \
+    else                                                                        \
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(F<L, false>), __VA_ARGS__);
 
-hipError_t launch_edge_tp_fwd(int L, int C, int64_t E, const float *vec, const float *V, const float *w, float *out,
-                              bool accumulate, hipStream_t stream)
+template <int L>
+hipError_t edge_tp_fwd_l(int C, int64_t E, const float *vec, const float *V, const float *w, float *out,
+                         bool accumulate, hipStream_t stream)
 {
     if (E == 0)
         return hipSuccess;
     const int64_t waves = (E + kEdgeTpRun - 1) / kEdgeTpRun * ((C + 63) / 64);
     const dim3 grid(static_cast<unsigned>((waves + 3) / 4)), block(256);
-    ETP_EDGE_TP_CASES(edge_tp_fwd_kernel, grid, block, 0, stream, E, C, vec, V, w, out)
+    ETP_EDGE_TP_LAUNCH(edge_tp_fwd_kernel, grid, block, 0, stream, E, C, vec, V, w, out)
     return hipGetLastError();
 }
 
-hipError_t launch_edge_tp_vjp(int L, int C, int64_t E, const float *vec, const float *V, const float *w,
-                              const float *G, float *gV, float *gw, float *gr, bool accumulate, hipStream_t stream)
+template <int L>
+hipError_t edge_tp_vjp_l(int C, int64_t E, const float *vec, const float *V, const float *w, const float *G,
+                         float *gV, float *gw, float *gr, bool accumulate, hipStream_t stream)
 {
     if (E == 0)
         return hipSuccess;
     const dim3 grid(static_cast<unsigned>((E + 3) / 4)), block(256);
-    ETP_EDGE_TP_CASES(edge_tp_vjp_kernel, grid, block, 0, stream, E, C, vec, V, w, G, gV, gw, gr)
+    ETP_EDGE_TP_LAUNCH(edge_tp_vjp_kernel, grid, block, 0, stream, E, C, vec, V, w, G, gV, gw, gr)
     return hipGetLastError();
 }
 
-hipError_t launch_edge_tp_vjp2(int L, int C, int64_t E, const float *vec, const float *V, const float *w,
-                               const float *G, const float *ggV, const float *ggw, const float *ggvec, float *dV,
-                               float *dw, float *dr, float *dG, bool accumulate, hipStream_t stream)
+template <int L>
+hipError_t edge_tp_vjp2_l(int C, int64_t E, const float *vec, const float *V, const float *w, const float *G,
+                          const float *ggV, const float *ggw, const float *ggvec, float *dV, float *dw, float *dr,
+                          float *dG, bool accumulate, hipStream_t stream)
 {
     if (E == 0)
         return hipSuccess;
     const dim3 grid(static_cast<unsigned>((E + 3) / 4)), block(256);
-    ETP_EDGE_TP_CASES(edge_tp_vjp2_kernel, grid, block, 0, stream, E, C, vec, V, w, G, ggV, ggw, ggvec, dV, dw, dr,
-                      dG)
+    ETP_EDGE_TP_LAUNCH(edge_tp_vjp2_kernel, grid, block, 0, stream, E, C, vec, V, w, G, ggV, ggw, ggvec, dV, dw,
+                       dr, dG)
     return hipGetLastError();
 }
+
+#ifndef ETP_L
+#error "etp_edge_tp.hip is compiled once per l_max: -DETP_L=<0..4>"
+#endif
+template hipError_t edge_tp_fwd_l<ETP_L>(int, int64_t, const float *, const float *, const float *, float *, bool,
+                                         hipStream_t);
+template hipError_t edge_tp_vjp_l<ETP_L>(int, int64_t, const float *, const float *, const float *, const float *,
+                                         float *, float *, float *, bool, hipStream_t);
+template hipError_t edge_tp_vjp2_l<ETP_L>(int, int64_t, const float *, const float *, const float *,
+                                          const float *, const float *, const float *, const float *, float *,
+                                          float *, float *, float *, bool, hipStream_t);
 
 }  // namespace etp
