@@ -183,16 +183,27 @@ __global__ void __launch_bounds__(256) nl_sweep_kernel(int n, const NlGeom g, Nl
     }
     const bool inl = FILL && lim <= kNlRowCap;  // this row is ordered in LDS
     int *buf = reinterpret_cast<int *>(buf_s[FILL ? wv : 0]);
+    // this lane's candidate v in cell order: its cell is the last t with
+    // cpre[t] <= v (cells may be empty); t only moves forward
     int t = 0, found = 0;
+    auto locate = [&](int v) {
+        while (t + 1 < K && cpre[t + 1] <= v)
+            ++t;
+        return cstart[t] + (v - cpre[t]);
+    };
+    // one step of look-ahead: the next step's candidate is loaded before this
+    // step's test
+    float4 nxt = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane < total)
+        nxt = w.cq[locate(lane)];
     for (int v0 = 0; v0 < total; v0 += 64) {
         const int v = v0 + lane;
+        const float4 o = nxt;
+        if (v + 64 < total)
+            nxt = w.cq[locate(v + 64)];
         bool hit = false;
         int j = 0;
         if (v < total) {
-            // this lane's cell: the last t with cpre[t] <= v (cells may be empty)
-            while (t + 1 < K && cpre[t + 1] <= v)
-                ++t;
-            const float4 o = w.cq[cstart[t] + (v - cpre[t])];
             j = __float_as_int(o.w);
             const float dx = nl_image(o.x - me.x, g.L[0]);
             const float dy = nl_image(o.y - me.y, g.L[1]);
