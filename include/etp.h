@@ -35,6 +35,15 @@
  *   - no path normalisation; one output block per path (block order = path
  *     order).
  *
+ * Around the convolution the library provides the other steps of a force
+ * call, each declared below with its own contract: the periodic neighbour
+ * list that builds the graph (etp_neighbor_*), the stable transpose
+ * (etp_csr_transpose), the per-irrep channel mixing and its VJP
+ * (etp_channel_mix*), the node-local correlation product and its VJP
+ * (etp_node_product*), the edge-local tensor product with its VJP and
+ * VJP-of-VJP (etp_edge_tp_*), and the edge-to-atom force assembly
+ * (etp_edge_forces).
+ *
  * Layouts (row-major, contiguous, channel fastest):
  *   x[n_src][(l_max+1)^2][C]           row l*l + l + m           (f32 or bf16)
  *   w[n_edges][P][C]                   f32
