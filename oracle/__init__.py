@@ -287,6 +287,19 @@ def neighbors(pos, box, rc):
     return row_ptr, src[:E], vec[:E]
 
 
+def radial_weights(h, Wr):
+    """w[e, p, u] = sum_k h[e, k] Wr[k, p, u]: the last layer of a radial network
+    (h: [E, K] per-edge radial features, Wr: [K, P, C])."""
+    h = np.asarray(h, np.float64)
+    Wr = np.asarray(Wr, np.float64)
+    return np.einsum("ek,kpu->epu", h, Wr)
+
+
+def fwd_radial(L, row_ptr, src, vec, x, h, Wr):
+    """The forward with the per-edge weights formed from (h, Wr) first."""
+    return fwd(L, row_ptr, src, vec, x, radial_weights(h, Wr))
+
+
 def edge_tp_fwd(L, vec, V, w):
     """Edge-local tensor product: the convolution with every edge its own
     destination and source (out[E, Dout, C], no destination sum)."""
