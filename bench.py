@@ -123,6 +123,37 @@ def measured_traffic(op):
 MFMA_F32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix-core peak
 
 
+def time_fwd_radial(etp, plan, g, vec, x, out, L, C, N, E, n_src, fwd_ms, reps, K=8):
+    """The forward with radial weights formed in the kernel (w = h Wr, K basis
+    functions) on the same graph and features as the step: ms per call with
+    HIP events, against the plain forward that reads w. Algorithmic bytes:
+    h, Wr, x, out, vec, src, row_ptr once each; FLOPs: the forward's plus
+    2 K per (edge, path, channel) for the weights."""
+    import torch
+    import workloads
+    h, Wr = workloads.radial_inputs(E, K, L, C, seed=0)
+    h, Wr = torch.from_numpy(h).cuda(), torch.from_numpy(Wr).cuda()
+    y = torch.empty_like(out)
+    for _ in range(3):
+        etp.etp_edge_conv_fwd_radial(plan, g, vec, x, h, Wr, y)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        etp.etp_edge_conv_fwd_radial(plan, g, vec, x, h, Wr, y)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / reps * 1e-3
+    by, fl = algorithmic(L, C, N, E, n_src)
+    P = plan.P
+    byts = by["fwd"] - 4.0 * E * P * C + 4.0 * (E * K + K * P * C)
+    flops = fl["fwd"] + 2.0 * K * P * C * E
+    return {"ms": round(t * 1e3, 4), "edges_per_s": E / t, "n_basis": K,
+            "speedup_vs_fwd": round(fwd_ms * 1e-3 / t, 3), "algo_GBps": byts / t / 1e9,
+            "algo_TFLOPs": flops / t / 1e12, "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS,
+            "valu_frac": flops / t / 1e12 / VALU_PEAK_TFLOPS}
+
+
 def time_channel_mix(etp, plan, out, L, C, N, reps):
     """The per-irrep channel mixing after the convolution (outside the step):
     ms per call with HIP events, algorithmic bytes (conv output, W, result,
@@ -482,7 +513,9 @@ def main(argv=None):
         "ops": op_report,
         "roofline": roof,
     }
-    line["next_ops"] = {"channel_mix": time_channel_mix(etp, plan, out, L, C, N, a.steps),
+    line["next_ops"] = {"fwd_radial": time_fwd_radial(etp, plan, g, vec, x, out, L, C, N, E, n_src,
+                                                      per_op_ms["fwd"], a.steps),
+                        "channel_mix": time_channel_mix(etp, plan, out, L, C, N, a.steps),
                         "edge_forces": time_edge_forces(etp, g, gr, N, n_src, E, a.steps)}
     for name, (pos_np, box) in (("neighbor_list_water", workloads.water_positions(0)),
                                 ("neighbor_list_diamond", workloads.diamond_positions(0))):

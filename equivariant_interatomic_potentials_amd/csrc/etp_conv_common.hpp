@@ -21,11 +21,14 @@ struct ConvArgs {
     const void *x;
     const float *w, *G, *ggx, *ggw, *ggvec;
     float *out, *ox, *ow, *ovec;
+    const float *h, *wr;  // radial features [E][nbasis] and last-layer matrix [nbasis][P][C]
+    int nbasis;
     uint32_t flags;
     hipStream_t stream;
 };
 
-enum { DST_FWD = 0, DST_DG = 1 };
+enum { DST_FWD = 0, DST_DG = 1, DST_FWD_RADIAL = 2 };
+constexpr int kRadialMax = 8;  // radial basis functions per edge (padded to this in LDS)
 enum { SRC_VJP = 0, SRC_VJP2 = 1 };
 
 // Each kernel source is compiled once per (l_max, x dtype, mode) with
@@ -38,6 +41,9 @@ enum { SRC_VJP = 0, SRC_VJP2 = 1 };
 #define ETP_DECLARE_RUN(kind, L, XT, MODE) hipError_t ETP_RUN_NAME(kind, L, XT, MODE)(const ConvArgs &a);
 #define ETP_DECLARE_RUN_L(kind, L) \
     ETP_DECLARE_RUN(kind, L, 0, 0) ETP_DECLARE_RUN(kind, L, 0, 1) ETP_DECLARE_RUN(kind, L, 1, 0) ETP_DECLARE_RUN(kind, L, 1, 1)
+#define ETP_DECLARE_RUN_RADIAL(L) ETP_DECLARE_RUN(dst, L, 0, 2) ETP_DECLARE_RUN(dst, L, 1, 2)
+ETP_DECLARE_RUN_RADIAL(0) ETP_DECLARE_RUN_RADIAL(1) ETP_DECLARE_RUN_RADIAL(2) ETP_DECLARE_RUN_RADIAL(3)
+ETP_DECLARE_RUN_RADIAL(4)
 ETP_DECLARE_RUN_L(dst, 0) ETP_DECLARE_RUN_L(dst, 1) ETP_DECLARE_RUN_L(dst, 2) ETP_DECLARE_RUN_L(dst, 3) ETP_DECLARE_RUN_L(dst, 4)
 ETP_DECLARE_RUN_L(src, 0) ETP_DECLARE_RUN_L(src, 1) ETP_DECLARE_RUN_L(src, 2) ETP_DECLARE_RUN_L(src, 3) ETP_DECLARE_RUN_L(src, 4)
 

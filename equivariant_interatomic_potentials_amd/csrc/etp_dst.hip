@@ -29,7 +29,13 @@
 //   * w / W' are streamed with non-temporal loads, x / X' rows gathered
 //     cached; each path's w row (and each l1 block's x rows) is reloaded
 //     with the next edge's as soon as its last use in the current edge is
-//     done, one edge of look-ahead in one register set.
+//     done, one edge of look-ahead in one register set;
+//   * radial mode (forward only): instead of a w stream, each path's weight
+//     is formed in registers as w[e, p, u] = sum_k h[e, k] Wr[k, p, u] (the
+//     last layer of a radial network) at the path's first use: the lane's
+//     Wr entries of the group's paths stay in registers for the whole
+//     workgroup, and the edge's h row is written to LDS with its SH and read
+//     back once per edge (a broadcast).
 #include "etp_conv_common.hpp"
 
 namespace etp {
@@ -62,6 +68,9 @@ namespace etp {
 #ifndef ETP_DST_ROWS_DG4
 #define ETP_DST_ROWS_DG4 24
 #endif
+#ifndef ETP_DST_ROWS_RAD
+#define ETP_DST_ROWS_RAD 40  // radial mode at l >= 3: a group's Wr entries live in registers
+#endif
 #ifndef ETP_DST_WPE
 #define ETP_DST_WPE 0
 #endif
@@ -69,12 +78,14 @@ template <int L, int CPL, int MODE>
 struct DstCfg {
     static constexpr int S = ETP_DST_S;
     static constexpr int B = L <= 2 ? ETP_DST_B2 : (L == 3 ? 16 : 8);
-    static constexpr int ROWS = MODE == DST_FWD ? (L <= 2 ? ETP_DST_ROWS_FWD : L == 3 ? ETP_DST_ROWS_FWD3 : ETP_DST_ROWS_FWD4)
+    static constexpr int ROWS = MODE == DST_FWD_RADIAL ? (L <= 2 ? ETP_DST_ROWS_FWD : ETP_DST_ROWS_RAD)
+                              : MODE == DST_FWD ? (L <= 2 ? ETP_DST_ROWS_FWD : L == 3 ? ETP_DST_ROWS_FWD3 : ETP_DST_ROWS_FWD4)
                                                 : (L <= 2 ? ETP_DST_ROWS_DG : L == 3 ? ETP_DST_ROWS_DG3 : ETP_DST_ROWS_DG4);
     static constexpr int MAXROWS = (ROWS + CPL - 1) / CPL;
-    static constexpr int TCOPIES = MODE == DST_FWD ? 1 : 2;  // T (and Td) per edge
-    // waves per SIMD the registers must allow: 3 at l=3 (169 VGPRs otherwise)
-    static constexpr int WPE = ETP_DST_WPE > 0 ? ETP_DST_WPE : (L == 3 ? 3 : 1);
+    static constexpr int TCOPIES = MODE == DST_DG ? 2 : 1;  // T (and Td) per edge
+    // waves per SIMD the registers must allow: 3 at l=3 (169 VGPRs otherwise);
+    // 2 in the radial mode, whose Wr entries take 8 registers per path
+    static constexpr int WPE = ETP_DST_WPE > 0 ? ETP_DST_WPE : MODE == DST_FWD_RADIAL ? 2 : (L == 3 ? 3 : 1);
 };
 
 template <int L, int CPL, typename XT, int MODE, int G>
@@ -83,12 +94,15 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
                                           const float *__restrict__ vec, const XT *__restrict__ x,
                                           const float *__restrict__ w, const float *__restrict__ ggx,
                                           const float *__restrict__ ggw, const float *__restrict__ ggvec,
-                                          float *__restrict__ out, const uint32_t flags, float *lds)
+                                          float *__restrict__ out, const uint32_t flags, float *lds,
+                                          const float *__restrict__ hrad, const float *__restrict__ wrad,
+                                          const int nbasis)
 {
     using V = chv_t<CPL>;
     using Cfg = DstCfg<L, CPL, MODE>;
     constexpr int S = Cfg::S, B = Cfg::B, TC = Cfg::TCOPIES;
-    constexpr bool DG = MODE == DST_DG;
+    constexpr bool DG = MODE == DST_DG, RAD = MODE == DST_FWD_RADIAL;
+    constexpr int RK = kRadialMax;
     constexpr Groups GR = make_groups(kTab<L>, Cfg::MAXROWS);
     constexpr GroupInfo GI = group_info(kTab<L>, GR, G);
     constexpr int P = kTab<L>.P, DIN = kTab<L>.din_rows, DOUT = kTab<L>.dout_rows, DSH = kTab<L>.dsh;
@@ -114,6 +128,19 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
     const int e_begin = rb + static_cast<int>((static_cast<int64_t>(len) * wv) / S);
     const int e_end = rb + static_cast<int>((static_cast<int64_t>(len) * (wv + 1)) / S);
     float *tl = lds + wv * (TC * B * STRIDE);  // T[B][STRIDE] (then Td[B][STRIDE])
+    // radial mode: after the T slices, per wave the batch's h rows [B][RK]
+    // (zero past nbasis); the lane's Wr[k, p, u] of the group's paths in
+    // registers (zero past nbasis and C)
+    float *hl = lds + S * TC * B * max_stride(kTab<L>, GR) + wv * (B * RK);
+    float wr[RAD ? NP : 1][RK];
+    if constexpr (RAD) {
+        static_assert(CPL == 1, "the radial mode keeps one channel per lane");
+        static_range<0, NP>([&](auto q) {
+            static_range<0, RK>([&](auto k) {
+                wr[q][k] = (active && k < nbasis) ? wrad[(static_cast<int64_t>(k) * P + GI.p0 + q) * C + u0] : 0.f;
+            });
+        });
+    }
 
     V acc[NROW];
     static_range<0, NROW>([&](auto r) { acc[r] = vzero<V>(); });
@@ -132,7 +159,7 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
     auto edge_rsrc = [&](int e, bool valid) {
         const int j = src[e];
         EdgeRsrc r;
-        r.w = make_rsrc(w + static_cast<int64_t>(e) * (P * C), valid ? P * C * 4u : 0u);
+        r.w = make_rsrc(RAD ? nullptr : w + static_cast<int64_t>(e) * (P * C), (!RAD && valid) ? P * C * 4u : 0u);
         r.x = make_rsrc(x + static_cast<int64_t>(j) * (DIN * C), valid ? DIN * C * static_cast<uint32_t>(sizeof(XT)) : 0u);
         // a missing cotangent is a zero-length block: its loads read 0
         r.wp = make_rsrc(has_wp ? ggw + static_cast<int64_t>(e) * (P * C) : nullptr, has_wp && valid ? P * C * 4u : 0u);
@@ -141,7 +168,8 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
     };
     Ops o;
     auto load_w = [&](auto q, const EdgeRsrc &r) {  // q: path index within the group
-        o.w[q] = bload<V, kNT>(r.w, off4, (GI.p0 + q) * rowb);
+        if constexpr (!RAD)  // (the radial mode forms w at the path's first use)
+            o.w[q] = bload<V, kNT>(r.w, off4, (GI.p0 + q) * rowb);
         if constexpr (DG)
             o.wp[q] = bload<V, kNT>(r.wp, off4, (GI.p0 + q) * rowb);
     };
@@ -165,6 +193,10 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
                 float Y[DSH];
                 sh_value<L>(rx, ry, rz, Y);
                 write_T<L, GI.pr0, GI.npr, STRIDE>(Y, tl + lane * STRIDE);
+                if constexpr (RAD)
+                    static_range<0, RK>([&](auto k) {
+                        hl[lane * RK + k] = k < nbasis ? hrad[static_cast<int64_t>(e) * nbasis + k] : 0.f;
+                    });
             } else {
                 float px = 0.f, py = 0.f, pz = 0.f;
                 if (has_rp) {
@@ -188,9 +220,14 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
     // inputs pre-scaled by w, or y[m3] += T x[m1] followed by
     // acc[p, m3] += w y[m3], whichever form needs fewer multiplies.
     // dG: acc[p, m3] += T (w X' + W' x)[m1] + Td (w x)[m1].
-    auto compute = [&](const float *tk, const EdgeRsrc &nx) {
+    auto compute = [&](const float *tk, const float *hk, const EdgeRsrc &nx) {
         float4 tq = make_float4(0.f, 0.f, 0.f, 0.f), tdq = tq;
         V xw[9], y[9], xx[DG ? 9 : 1];
+        float4 h0, h1;
+        if constexpr (RAD) {
+            h0 = *reinterpret_cast<const float4 *>(hk);
+            h1 = *reinterpret_cast<const float4 *>(hk + 4);
+        }
         static_range<GI.pr0, GI.pr1>([&](auto q) {
             constexpr Pair pr = kTab<L>.pair[q];
             constexpr Path pa = kTab<L>.path[pr.path];
@@ -198,6 +235,16 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
             constexpr int XO = pa.x_row - GI.xr0, OO = pa.out_row - GI.row0, WQ = pr.path - GI.p0;
             constexpr bool XW = DG || d1 <= d3;
             constexpr int a = pr.m1 + pa.l1, c3 = pr.m3 + pa.l3, ql = q - GI.pr0;
+            if constexpr (RAD && q == pa.pr0) {  // w[e, p, u] = sum_k h[e, k] Wr[k, p, u], k in order
+                float t = h0.x * wr[WQ][0];
+                t = fmaf(h0.y, wr[WQ][1], t);
+                t = fmaf(h0.z, wr[WQ][2], t);
+                t = fmaf(h0.w, wr[WQ][3], t);
+                t = fmaf(h1.x, wr[WQ][4], t);
+                t = fmaf(h1.y, wr[WQ][5], t);
+                t = fmaf(h1.z, wr[WQ][6], t);
+                o.w[WQ] = fmaf(h1.w, wr[WQ][7], t);
+            }
             if constexpr (XW && q == pa.pr0) {
                 static_range<0, d1>([&](auto k) {
                     xw[k] = o.w[WQ] * o.x[XO + k];
@@ -245,7 +292,7 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
             load_all(edge_rsrc(e, true));
         }
         const bool more = kb + 1 < nb;
-        compute(tl + kb * STRIDE, edge_rsrc(more ? e + 1 : e, more));
+        compute(tl + kb * STRIDE, hl + kb * RK, edge_rsrc(more ? e + 1 : e, more));
         kb = (kb + 1 == nb) ? 0 : kb + 1;
     }
 
@@ -269,7 +316,8 @@ __global__ void __launch_bounds__((64 * DstCfg<L, CPL, MODE>::S)) __attribute__(
     dst_kernel(const int n_dst, const int C, const int nchunk, const int *__restrict__ row_ptr,
                const int *__restrict__ src, const float *__restrict__ vec, const XT *__restrict__ x,
                const float *__restrict__ w, const float *__restrict__ ggx, const float *__restrict__ ggw,
-               const float *__restrict__ ggvec, float *__restrict__ out, const uint32_t flags)
+               const float *__restrict__ ggvec, float *__restrict__ out, const uint32_t flags,
+               const float *__restrict__ hrad, const float *__restrict__ wrad, const int nbasis)
 {
     extern __shared__ float lds[];
     constexpr Groups GR = make_groups(kTab<L>, DstCfg<L, CPL, MODE>::MAXROWS);
@@ -277,7 +325,7 @@ __global__ void __launch_bounds__((64 * DstCfg<L, CPL, MODE>::S)) __attribute__(
     static_range<0, GR.n>([&](auto G) __attribute__((always_inline)) {
         if (g == G)
             dst_group<L, CPL, XT, MODE, G>(n_dst, C, nchunk, row_ptr, src, vec, x, w, ggx, ggw, ggvec, out, flags,
-                                           lds);
+                                           lds, hrad, wrad, nbasis);
     });
 }
 
@@ -286,7 +334,8 @@ static hipError_t launch_dst_t(const ConvArgs &a)
 {
     using Cfg = DstCfg<L, CPL, MODE>;
     constexpr Groups GR = make_groups(kTab<L>, Cfg::MAXROWS);
-    constexpr int LDS_FLOATS = Cfg::S * Cfg::TCOPIES * Cfg::B * max_stride(kTab<L>, GR);
+    constexpr int LDS_FLOATS = Cfg::S * Cfg::TCOPIES * Cfg::B * max_stride(kTab<L>, GR) +
+                               (MODE == DST_FWD_RADIAL ? Cfg::S * Cfg::B * kRadialMax : 0);
     const int nchunk = (a.C + 64 * CPL - 1) / (64 * CPL);
     const int64_t nblk = static_cast<int64_t>(a.n_dst) * nchunk;
     if (nblk == 0)
@@ -296,12 +345,12 @@ static hipError_t launch_dst_t(const ConvArgs &a)
     dim3 grid(static_cast<unsigned>(nblk), GR.n), block(64 * Cfg::S);
     hipLaunchKernelGGL((dst_kernel<L, CPL, XT, MODE>), grid, block, LDS_FLOATS * sizeof(float), a.stream, a.n_dst,
                        a.C, nchunk, a.row_ptr, a.src, a.vec, static_cast<const XT *>(a.x), a.w, a.ggx, a.ggw,
-                       a.ggvec, a.out, a.flags);
+                       a.ggvec, a.out, a.flags, a.h, a.wr, a.nbasis);
     return hipGetLastError();
 }
 
 #if !defined(ETP_L) || !defined(ETP_XT) || !defined(ETP_MODE)
-#error "compile this file once per (l_max, dtype, mode) with -DETP_L=0..4 -DETP_XT=0|1 -DETP_MODE=0|1"
+#error "compile this file once per (l_max, dtype, mode) with -DETP_L=0..4 -DETP_XT=0|1 -DETP_MODE=0|1|2"
 #endif
 
 hipError_t ETP_RUN_NAME(dst, ETP_L, ETP_XT, ETP_MODE)(const ConvArgs &a)
@@ -312,7 +361,8 @@ hipError_t ETP_RUN_NAME(dst, ETP_L, ETP_XT, ETP_MODE)(const ConvArgs &a)
 #ifndef ETP_DST_CPL1
 #define ETP_DST_CPL1 0
 #endif
-    constexpr bool ONE = (ETP_MODE == DST_DG && ETP_L >= 4) || ETP_DST_CPL1;
+    // (and the radial mode: its Wr slice in LDS doubles with the channels)
+    constexpr bool ONE = (ETP_MODE == DST_DG && ETP_L >= 4) || ETP_MODE == DST_FWD_RADIAL || ETP_DST_CPL1;
     if constexpr (ONE)
         return launch_dst_t<ETP_L, 1, XT, ETP_MODE>(a);
     else

@@ -183,6 +183,28 @@ ETP_API etp_status etp_sh(etp_plan_t plan, int64_t n_edges, const float *vec, fl
 ETP_API etp_status etp_edge_conv_fwd(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x, const float *w,
                              float *out, uint32_t flags, void *stream);
 
+/* Forward with the per-edge weights formed inside the kernel from the last
+ * layer of a radial network instead of read from memory:
+ *   w[e, p, u] = sum_{k < n_basis} h[e, k] Wr[(k*P + p)*C + u]
+ * then out as in etp_edge_conv_fwd. The pages' kernels keep intermediates
+ * out of memory ("High-performance training and inference for deep
+ * equivariant interatomic potentials", section "Proposed method") and weight
+ * each path by a learned function of the edge's radial features ("Scaling
+ * the leading accuracy of deep equivariant models to biomolecular
+ * simulations of realistic size", section "Proposed method"); the pages do
+ * not fix the network, and this is its linear last layer, whose E*P*C
+ * weights would otherwise be the largest stream the forward reads.
+ * h:  DEVICE float [n_edges][n_basis] (features after the radial network's
+ *     hidden layers and any envelope), 1 <= n_basis <= ETP_MAX_RADIAL_BASIS;
+ * Wr: DEVICE float [n_basis][P][C], shared by all edges.
+ * Other arguments, layouts and flags as etp_edge_conv_fwd; fp32 sums of
+ * n_basis terms in k order. Errors: UNSUPPORTED (n_basis out of range),
+ * INVALID_ARGUMENT (null pointers, a malformed graph, unknown flags). */
+#define ETP_MAX_RADIAL_BASIS 8
+ETP_API etp_status etp_edge_conv_fwd_radial(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x,
+                                            const float *h, int32_t n_basis, const float *Wr, float *out,
+                                            uint32_t flags, void *stream);
+
 /* VJP: given grad_out = dL/dout, grad_x = dL/dx (source-segmented),
  * grad_w = dL/dw and grad_vec = dL/dvec (forces on the edges). Each output
  * may be NULL. Needs the transpose in g. */

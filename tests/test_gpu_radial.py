@@ -1,0 +1,105 @@
+"""GPU parity of the forward with radial weights formed in the kernel
+(w = h Wr, then the convolution), through the C ABI, against the float64
+oracle: every l_max, ragged channel counts, 1..8 basis functions, bf16
+features, accumulate, an empty graph, the argument checks and the
+benchmarked 1024-node microbenchmark at full size on sampled rows."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+from gpu_common import BF16_TOL, FP32_TOL, DeviceProblem, dev, dst_subgraph, np_, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[radial]", *a, file=sys.stderr, flush=True)
+
+
+def run(p, h, Wr, flags=0, out=None):
+    wl = p.wl
+    if out is None:
+        out = p.empty(wl.n_dst, wl.Dout, wl.C)
+    p.etp.etp_edge_conv_fwd_radial(p.plan, p.graph, p.vec, p.x, dev(h), dev(Wr), out, flags)
+    return out
+
+
+CASES = [(0, 64, 8), (1, 64, 3), (2, 128, 8), (2, 100, 1), (2, 1, 5), (3, 128, 8), (3, 200, 7),
+         (4, 64, 8), (4, 130, 2)]
+
+
+@pytest.mark.parametrize("L,C,K", CASES)
+def test_radial_fwd_small(L, C, K):
+    say("small", L, C, K)
+    wl = workloads.small(L, C, 23, 14, seed=L * 10 + C + K)
+    h, Wr = workloads.radial_inputs(wl.E, K, L, C, seed=K)
+    p = DeviceProblem(wl, need=())
+    out = np_(run(p, h, Wr))
+    ref = oracle.fwd_radial(L, wl.row_ptr, wl.src, wl.vec, wl.x, h, Wr)
+    assert rel_err(out, ref) < FP32_TOL, rel_err(out, ref)
+
+
+@pytest.mark.parametrize("L,C", [(2, 128), (3, 64)])
+def test_radial_fwd_bf16_features(L, C):
+    say("bf16", L, C)
+    wl = workloads.small(L, C, 19, 12, seed=5 + L)
+    h, Wr = workloads.radial_inputs(wl.E, 8, L, C, seed=3)
+    p = DeviceProblem(wl, bf16=True, need=())
+    out = np_(run(p, h, Wr))
+    ref = oracle.fwd_radial(L, wl.row_ptr, wl.src, wl.vec, p.x_seen, h, Wr)
+    assert rel_err(out, ref) < FP32_TOL, rel_err(out, ref)
+    ref32 = oracle.fwd_radial(L, wl.row_ptr, wl.src, wl.vec, wl.x, h, Wr)
+    assert rel_err(out, ref32) < BF16_TOL
+
+
+def test_radial_accumulate_and_empty_rows():
+    """ACCUMULATE adds to out; destinations without edges get 0 (or keep out)."""
+    import torch
+    say("accumulate")
+    wl = workloads.bipartite(2, 64, 40, 30, 0, 5, seed=4)
+    h, Wr = workloads.radial_inputs(wl.E, 4, 2, 64, seed=4)
+    p = DeviceProblem(wl, need=())
+    ref = oracle.fwd_radial(2, wl.row_ptr, wl.src, wl.vec, wl.x, h, Wr)
+    base = torch.randn(wl.n_dst, wl.Dout, wl.C, device="cuda")
+    got = run(p, h, Wr, flags=p.etp.ETP_FLAG_ACCUMULATE, out=base.clone())
+    assert rel_err(np_(got) - np_(base), ref) < FP32_TOL
+    out = run(p, h, Wr, out=torch.full_like(base, 7.0))
+    assert rel_err(np_(out), ref) < FP32_TOL
+    empty = np.diff(wl.row_ptr) == 0
+    assert empty.any() and np.abs(np_(out)[empty]).max() == 0.0
+
+
+def test_radial_argument_checks():
+    import torch
+    say("args")
+    wl = workloads.small(1, 8, 6, 3, seed=2)
+    p = DeviceProblem(wl, need=())
+    out = p.empty(wl.n_dst, wl.Dout, wl.C)
+    for K in (0, 9):
+        h = torch.zeros(wl.E, max(K, 1), device="cuda")
+        Wr = torch.zeros(max(K, 1), p.plan.P, wl.C, device="cuda")
+        with pytest.raises(p.etp.EtpError) as ei:
+            p.etp.etp_edge_conv_fwd_radial(p.plan, p.graph, p.vec, p.x, h if K else None,
+                                           Wr if K else None, out)
+        assert ei.value.status in (p.etp.ETP_ERR_UNSUPPORTED, p.etp.ETP_ERR_INVALID_ARGUMENT)
+
+
+def test_radial_micro_full_size_sampled():
+    """The 1024-node x 128-neighbour microbenchmark with 8 basis functions,
+    in the launch configuration the benchmark times; destination rows
+    sampled and recomputed by the oracle."""
+    say("micro")
+    wl = workloads.get("micro")
+    K = 8
+    h, Wr = workloads.radial_inputs(wl.E, K, wl.L, wl.C, seed=11)
+    p = DeviceProblem(wl, need=())
+    out = np_(run(p, h, Wr))
+    g = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, wl.n_dst - 1], g.choice(wl.n_dst, 6, replace=False)]))
+    rp, eidx = dst_subgraph(wl, rows)
+    ref = oracle.fwd_radial(wl.L, rp, wl.src[eidx], wl.vec[eidx], wl.x, h[eidx], Wr)
+    assert rel_err(out[rows], ref) < FP32_TOL, rel_err(out[rows], ref)

@@ -32,7 +32,7 @@ def header_symbols():
 
 def test_header_symbols_exported():
     names = header_symbols()
-    assert len(names) == 24
+    assert len(names) == 25
     assert sorted(etp.ABI_SYMBOLS) == names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (etp_\w+)$", out, flags=re.M))
@@ -131,6 +131,15 @@ def test_call_validation_without_device():
     g5 = etp.etp_graph(4, 4, 8, 8, 8, 8, 8, 8)
     assert lib.etp_edge_conv_vjp(big.handle, ctypes.byref(g5), 8, 8, 8, 8, 8, 8, 8, 0, None) == UNS
     assert lib.etp_edge_conv_fwd(plan.handle, ctypes.byref(g5), 8, 8, 8, 8, 4, None) == INV   # unknown flag
+    # radial forward: basis count 1..8, h and Wr needed when there are edges
+    fr = lib.etp_edge_conv_fwd_radial
+    assert fr(plan.handle, ctypes.byref(g5), 8, 8, 8, 0, 8, 8, 0, None) == UNS
+    assert fr(plan.handle, ctypes.byref(g5), 8, 8, 8, 9, 8, 8, 0, None) == UNS
+    assert fr(plan.handle, ctypes.byref(g5), 8, 8, None, 4, 8, 8, 0, None) == INV
+    assert fr(plan.handle, ctypes.byref(g5), 8, 8, 8, 4, None, 8, 0, None) == INV
+    assert fr(plan.handle, ctypes.byref(g5), 8, 8, 8, 4, 8, 8, 4, None) == INV
+    assert fr(None, ctypes.byref(g5), 8, 8, 8, 4, 8, 8, 0, None) == INV
+    assert fr(plan.handle, ctypes.byref(g2), 8, 8, 8, 4, 8, 8, 0, None) == UNS
     assert lib.etp_csr_transpose(ctypes.byref(g5), 8, 8, 8, None, 0, None) == WS
     assert lib.etp_csr_transpose(ctypes.byref(g5), 8, 8, 8, 8, 1, None) == WS
     assert lib.etp_sh(None, 4, 8, 8, None, None) == INV

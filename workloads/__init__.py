@@ -34,7 +34,7 @@ import functools
 import numpy as np
 
 STREAMS = ("graph", "dirs", "lens", "x", "w", "G", "ggx", "ggw", "ggvec",
-           "pos", "orient")
+           "pos", "orient", "h", "wr")
 
 
 def _n_paths(L: int) -> int:
@@ -115,6 +115,17 @@ def node_features(n: int, L: int, C: int, nu: int, seed: int = 0):
     P = _n_paths(L)
     W = (rng(seed, "w").standard_normal((max(nu - 1, 0), P, C)) / np.sqrt(P)).astype(np.float32)
     return A, W
+
+
+def radial_inputs(E: int, K: int, L: int, C: int, seed: int = 0):
+    """Inputs of the forward with radial weights: per-edge features
+    h[E, K] ~ N(0, 1) (what a radial network's hidden layers hand on) and the
+    shared last-layer matrix Wr[K, P, C] ~ N(0, 1/(K P)), so that the formed
+    weights have the spread of the plain forward's w (float32)."""
+    P = _n_paths(L)
+    h = rng(seed, "h").standard_normal((E, K), np.float32)
+    Wr = (rng(seed, "wr").standard_normal((K, P, C), np.float32) * np.float32(1.0 / np.sqrt(K * P)))
+    return h, Wr
 
 
 def gas_positions(n: int, box, seed: int, images: int = 1):
