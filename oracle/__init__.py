@@ -300,6 +300,20 @@ def fwd_radial(L, row_ptr, src, vec, x, h, Wr):
     return fwd(L, row_ptr, src, vec, x, radial_weights(h, Wr))
 
 
+def vjp_radial(L, row_ptr, src, vec, x, h, Wr, G):
+    """VJP of the forward with radial weights, by the chain rule through
+    w = h Wr: (gx, gh[E, K], gr, gWr[K, P, C]) with gh[e, k] = sum_{p,u}
+    gw[e, p, u] Wr[k, p, u] and gWr[k, p, u] = sum_e h[e, k] gw[e, p, u]."""
+    h = np.asarray(h, np.float64)
+    Wr = np.asarray(Wr, np.float64)
+    gx, gw, gr = vjp(L, row_ptr, src, vec, x, radial_weights(h, Wr), G)
+    E = h.shape[0]
+    gw = gw[:E]
+    gh = np.einsum("epu,kpu->ek", gw, Wr)
+    gWr = np.einsum("ek,epu->kpu", h, gw)
+    return gx, gh, gr[:E], gWr
+
+
 def edge_tp_fwd(L, vec, V, w):
     """Edge-local tensor product: the convolution with every edge its own
     destination and source (out[E, Dout, C], no destination sum)."""

@@ -3,7 +3,10 @@ features h[E, K] times a shared last-layer matrix Wr[K, P, C]):
 
   * one basis function with h = 1 is the plain forward with w[e] = Wr[0];
   * the forward is linear in h and in Wr;
-  * the weights against an explicit double loop.
+  * the weights against an explicit double loop;
+  * the VJP (gx, gh, gr, gWr) against central differences of <G, out> in
+    x, h, vec and Wr, and the weight gradients against the plain VJP's gw
+    contracted by hand for one basis function.
 """
 import numpy as np
 import pytest
@@ -48,3 +51,40 @@ def test_weights_against_loops():
         for p in range(4):
             for u in range(2):
                 assert abs(w[e, p, u] - sum(h[e, k] * Wr[k, p, u] for k in range(3))) < 1e-12
+
+
+@pytest.mark.parametrize("L,K", [(1, 3), (2, 8)])
+def test_vjp_finite_differences(L, K):
+    wl, h, Wr = case(L, 3, K, 10 + L)
+    g = np.random.default_rng(20 + L)
+    G = g.standard_normal((wl.n_dst, oracle.dims(L)["Dout"], 3))
+    gx, gh, gr, gWr = oracle.vjp_radial(L, wl.row_ptr, wl.src, wl.vec, wl.x, h, Wr, G)
+
+    def f(x=wl.x, hh=h, vec=wl.vec, ww=Wr):
+        return (G * oracle.fwd_radial(L, wl.row_ptr, wl.src, vec, x, hh, ww)).sum()
+
+    eps = 1e-6
+    x = wl.x.astype(np.float64)
+    vec = wl.vec.astype(np.float64)
+    for name, arr, grad, kw in (("x", x, gx, "x"), ("h", h, gh, "hh"), ("vec", vec, gr, "vec"),
+                                ("Wr", Wr, gWr, "ww")):
+        for t in range(4):
+            idx = tuple(int(g.integers(s)) for s in arr.shape)
+            a1, a2 = arr.copy(), arr.copy()
+            a1[idx] += eps
+            a2[idx] -= eps
+            fd = (f(**{kw: a1}) - f(**{kw: a2})) / (2 * eps)
+            assert abs(fd - grad[idx]) < 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+
+
+def test_weight_gradients_single_basis():
+    """K = 1: gh[e] = sum_{p,u} gw[e,p,u] Wr[0,p,u] and gWr[0] = sum_e h[e] gw[e]."""
+    wl, h, Wr = case(2, 2, 1, 7)
+    G = np.random.default_rng(8).standard_normal((wl.n_dst, oracle.dims(2)["Dout"], 2))
+    w = oracle.radial_weights(h, Wr)
+    _, gw, _ = oracle.vjp(2, wl.row_ptr, wl.src, wl.vec, wl.x, w, G)
+    _, gh, _, gWr = oracle.vjp_radial(2, wl.row_ptr, wl.src, wl.vec, wl.x, h, Wr, G)
+    for e in range(wl.E):
+        assert abs(gh[e, 0] - float((gw[e] * Wr[0]).sum())) < 1e-12
+    want = sum(h[e, 0] * gw[e] for e in range(wl.E))
+    np.testing.assert_allclose(gWr[0], want, atol=1e-12)
