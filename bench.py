@@ -123,12 +123,13 @@ def measured_traffic(op):
 MFMA_F32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix-core peak
 
 
-def time_fwd_radial(etp, plan, g, vec, x, out, L, C, N, E, n_src, fwd_ms, reps, K=8):
-    """The forward with radial weights formed in the kernel (w = h Wr, K basis
-    functions) on the same graph and features as the step: ms per call with
-    HIP events, against the plain forward that reads w. Algorithmic bytes:
-    h, Wr, x, out, vec, src, row_ptr once each; FLOPs: the forward's plus
-    2 K per (edge, path, channel) for the weights."""
+def time_radial(etp, plan, g, vec, x, out, G, L, C, N, E, n_src, fwd_ms, vjp_ms, reps, K=8):
+    """The forward and VJP with radial weights formed in the kernel (w = h Wr,
+    K basis functions) on the same graph and features as the step: ms per
+    call with HIP events, against the plain calls that read w (and write gw).
+    Algorithmic bytes: the plain call's with the E P C weight streams
+    replaced by h (and grad_h) and Wr; FLOPs: the plain call's plus 2 K per
+    (edge, path, channel) to form w (and 2 K more for grad_h)."""
     import torch
     import workloads
     h, Wr = workloads.radial_inputs(E, K, L, C, seed=0)
@@ -148,10 +149,25 @@ def time_fwd_radial(etp, plan, g, vec, x, out, L, C, N, E, n_src, fwd_ms, reps, 
     P = plan.P
     byts = by["fwd"] - 4.0 * E * P * C + 4.0 * (E * K + K * P * C)
     flops = fl["fwd"] + 2.0 * K * P * C * E
-    return {"ms": round(t * 1e3, 4), "edges_per_s": E / t, "n_basis": K,
-            "speedup_vs_fwd": round(fwd_ms * 1e-3 / t, 3), "algo_GBps": byts / t / 1e9,
-            "algo_TFLOPs": flops / t / 1e12, "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS,
-            "valu_frac": flops / t / 1e12 / VALU_PEAK_TFLOPS}
+    res = {"ms": round(t * 1e3, 4), "edges_per_s": E / t, "n_basis": K,
+           "speedup_vs_fwd": round(fwd_ms * 1e-3 / t, 3), "algo_GBps": byts / t / 1e9,
+           "algo_TFLOPs": flops / t / 1e12, "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS,
+           "valu_frac": flops / t / 1e12 / VALU_PEAK_TFLOPS}
+    gx, gh, gr = torch.empty_like(x, dtype=torch.float32), torch.empty(E, K, device="cuda"), torch.empty_like(vec)
+    for _ in range(2):
+        etp.etp_edge_conv_vjp_radial(plan, g, vec, x, h, Wr, G, gx, gh, gr)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        etp.etp_edge_conv_vjp_radial(plan, g, vec, x, h, Wr, G, gx, gh, gr)
+    b.record()
+    torch.cuda.synchronize()
+    tv = a.elapsed_time(b) / reps * 1e-3
+    vb = by["vjp"] - 8.0 * E * P * C + 4.0 * (2 * E * K + K * P * C)
+    vf = fl["vjp"] + 4.0 * K * P * C * E
+    res.update({"vjp_ms": round(tv * 1e3, 4), "vjp_speedup_vs_vjp": round(vjp_ms * 1e-3 / tv, 3),
+                "vjp_hbm_frac": vb / tv / 1e9 / HBM_PEAK_GBS, "vjp_valu_frac": vf / tv / 1e12 / VALU_PEAK_TFLOPS})
+    return res
 
 
 def time_channel_mix(etp, plan, out, L, C, N, reps):
@@ -513,8 +529,8 @@ def main(argv=None):
         "ops": op_report,
         "roofline": roof,
     }
-    line["next_ops"] = {"fwd_radial": time_fwd_radial(etp, plan, g, vec, x, out, L, C, N, E, n_src,
-                                                      per_op_ms["fwd"], a.steps),
+    line["next_ops"] = {"radial": time_radial(etp, plan, g, vec, x, out, G, L, C, N, E, n_src,
+                                              per_op_ms["fwd"], per_op_ms["vjp"], a.steps),
                         "channel_mix": time_channel_mix(etp, plan, out, L, C, N, a.steps),
                         "edge_forces": time_edge_forces(etp, g, gr, N, n_src, E, a.steps)}
     for name, (pos_np, box) in (("neighbor_list_water", workloads.water_positions(0)),

@@ -45,7 +45,7 @@ def units():
     for name in ("etp_dst", "etp_src"):
         for L in range(5):
             for xt in (0, 1):
-                for mode in ((0, 1, 2) if name == "etp_dst" else (0, 1)):
+                for mode in (0, 1, 2):
                     out.append((os.path.join(CSRC, name + ".hip"),
                                 os.path.join(BUILD, f"{name}_L{L}_X{xt}_M{mode}.o"),
                                 [f"-DETP_L={L}", f"-DETP_XT={xt}", f"-DETP_MODE={mode}"]))

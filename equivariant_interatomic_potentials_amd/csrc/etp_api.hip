@@ -175,6 +175,23 @@ hipError_t run_dst_radial(int L, bool bf16, const etp::ConvArgs &a)
     }
 }
 
+hipError_t run_src_radial(int L, bool bf16, const etp::ConvArgs &a)
+{
+    switch (L * 2 + (bf16 ? 1 : 0)) {
+    case 0: return etp::ETP_RUN_NAME(src, 0, 0, 2)(a);
+    case 1: return etp::ETP_RUN_NAME(src, 0, 1, 2)(a);
+    case 2: return etp::ETP_RUN_NAME(src, 1, 0, 2)(a);
+    case 3: return etp::ETP_RUN_NAME(src, 1, 1, 2)(a);
+    case 4: return etp::ETP_RUN_NAME(src, 2, 0, 2)(a);
+    case 5: return etp::ETP_RUN_NAME(src, 2, 1, 2)(a);
+    case 6: return etp::ETP_RUN_NAME(src, 3, 0, 2)(a);
+    case 7: return etp::ETP_RUN_NAME(src, 3, 1, 2)(a);
+    case 8: return etp::ETP_RUN_NAME(src, 4, 0, 2)(a);
+    case 9: return etp::ETP_RUN_NAME(src, 4, 1, 2)(a);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t run_src(int L, bool bf16, int mode, const etp::ConvArgs &a)
 {
     switch (L * 4 + (bf16 ? 2 : 0) + mode) {
@@ -477,6 +494,56 @@ etp_status etp_edge_conv_vjp(etp_plan_t plan, const etp_graph *g, const float *v
     a.flags = flags & ETP_FLAG_ACCUMULATE;
     a.stream = s;
     return hip_status(run_src(plan->L, plan->dtype == ETP_BF16, etp::SRC_VJP, a));
+}
+
+etp_status etp_edge_conv_vjp_radial(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x,
+                                    const float *h, int32_t n_basis, const float *Wr, const float *grad_out,
+                                    float *grad_x, float *grad_h, float *grad_vec, uint32_t flags, void *stream)
+{
+    if (!plan)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (n_basis < 1 || n_basis > ETP_MAX_RADIAL_BASIS)
+        return ETP_ERR_UNSUPPORTED;
+    etp_status st = check_graph(g, true);
+    if (st != ETP_OK)
+        return st;
+    if (plan->C > 256)
+        return ETP_ERR_UNSUPPORTED;
+    if (flags & ~3u)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (!grad_x && !grad_h && !grad_vec)
+        return ETP_OK;
+    if (g->n_src > 0 && (!x || !grad_out))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (g->n_edges > 0 && (!vec || !h || !Wr || !grad_out))
+        return ETP_ERR_INVALID_ARGUMENT;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (flags & ETP_FLAG_VALIDATE) {
+        st = validate_graph(g, s);
+        if (st != ETP_OK)
+            return st;
+    }
+    etp::ConvArgs a{};
+    a.C = plan->C;
+    a.n_dst = g->n_dst;
+    a.n_src = g->n_src;
+    a.row_ptr = g->row_ptr;
+    a.src = g->src;
+    a.src_ptr = g->src_ptr;
+    a.perm = g->perm;
+    a.perm_dst = g->perm_dst;
+    a.vec = vec;
+    a.x = x;
+    a.h = h;
+    a.wr = Wr;
+    a.nbasis = n_basis;
+    a.G = grad_out;
+    a.ox = grad_x;
+    a.oh = grad_h;
+    a.ovec = grad_vec;
+    a.flags = flags & ETP_FLAG_ACCUMULATE;
+    a.stream = s;
+    return hip_status(run_src_radial(plan->L, plan->dtype == ETP_BF16, a));
 }
 
 etp_status etp_edge_conv_vjp2(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x, const float *w,

@@ -22,6 +22,7 @@ struct ConvArgs {
     const float *w, *G, *ggx, *ggw, *ggvec;
     float *out, *ox, *ow, *ovec;
     const float *h, *wr;  // radial features [E][nbasis] and last-layer matrix [nbasis][P][C]
+    float *oh;            // radial VJP: grad_h [E][nbasis]
     int nbasis;
     uint32_t flags;
     hipStream_t stream;
@@ -29,7 +30,7 @@ struct ConvArgs {
 
 enum { DST_FWD = 0, DST_DG = 1, DST_FWD_RADIAL = 2 };
 constexpr int kRadialMax = 8;  // radial basis functions per edge (padded to this in LDS)
-enum { SRC_VJP = 0, SRC_VJP2 = 1 };
+enum { SRC_VJP = 0, SRC_VJP2 = 1, SRC_VJP_RADIAL = 2 };
 
 // Each kernel source is compiled once per (l_max, x dtype, mode) with
 // -DETP_L, -DETP_XT (0 = f32, 1 = bf16) and -DETP_MODE, so the translation
@@ -44,6 +45,9 @@ enum { SRC_VJP = 0, SRC_VJP2 = 1 };
 #define ETP_DECLARE_RUN_RADIAL(L) ETP_DECLARE_RUN(dst, L, 0, 2) ETP_DECLARE_RUN(dst, L, 1, 2)
 ETP_DECLARE_RUN_RADIAL(0) ETP_DECLARE_RUN_RADIAL(1) ETP_DECLARE_RUN_RADIAL(2) ETP_DECLARE_RUN_RADIAL(3)
 ETP_DECLARE_RUN_RADIAL(4)
+#define ETP_DECLARE_RUN_SRC_RADIAL(L) ETP_DECLARE_RUN(src, L, 0, 2) ETP_DECLARE_RUN(src, L, 1, 2)
+ETP_DECLARE_RUN_SRC_RADIAL(0) ETP_DECLARE_RUN_SRC_RADIAL(1) ETP_DECLARE_RUN_SRC_RADIAL(2)
+ETP_DECLARE_RUN_SRC_RADIAL(3) ETP_DECLARE_RUN_SRC_RADIAL(4)
 ETP_DECLARE_RUN_L(dst, 0) ETP_DECLARE_RUN_L(dst, 1) ETP_DECLARE_RUN_L(dst, 2) ETP_DECLARE_RUN_L(dst, 3) ETP_DECLARE_RUN_L(dst, 4)
 ETP_DECLARE_RUN_L(src, 0) ETP_DECLARE_RUN_L(src, 1) ETP_DECLARE_RUN_L(src, 2) ETP_DECLARE_RUN_L(src, 3) ETP_DECLARE_RUN_L(src, 4)
 

@@ -33,7 +33,13 @@
 //   * Z is reduced over each wave's lanes with DPP in a fixed order, parked
 //     in LDS per chunk, and at the end of the batch lane k of wave 0 sums the
 //     chunks in order and turns Z into gr / dr of edge k with forward-mode SH
-//     derivatives; no float atomics anywhere.
+//     derivatives; no float atomics anywhere;
+//   * radial mode (VJP with w = h Wr formed in the kernel): the lane's Wr
+//     entries of the group's paths stay in registers, the batch prologue
+//     also stores each edge's h row, w is formed at each path's start, and
+//     instead of storing gw each lane accumulates gh[k] += gw Wr[k, p, u];
+//     the 8 gh sums take the same fixed-order route as gr (wave sum, parked
+//     per chunk, chunks in order, later path groups adding to earlier ones).
 #include "etp_conv_common.hpp"
 
 namespace etp {
@@ -53,6 +59,9 @@ namespace etp {
 #ifndef ETP_SRC_COST_VJP2
 #define ETP_SRC_COST_VJP2 40
 #endif
+#ifndef ETP_SRC_COST_RAD
+#define ETP_SRC_COST_RAD 150
+#endif
 #ifndef ETP_SRC_WPE
 #define ETP_SRC_WPE 0
 #endif
@@ -61,21 +70,27 @@ namespace etp {
 #endif
 template <int L, int MODE>
 struct SrcCfg {
+    static constexpr bool RAD = MODE == SRC_VJP_RADIAL;
     static constexpr int NV = MODE == SRC_VJP2 ? 2 : 1;             // Y (, Yd) and Z (, Z2) copies
     static constexpr int DSH = (L + 1) * (L + 1), DSHP = (DSH + 3) & ~3;
     static constexpr int GQ = 4 * NV * DSH;                         // gr coefficients, a float4 per (b, copy)
-    static constexpr int ES = NV * DSHP + GQ;                       // floats per edge in the batch
-    static constexpr int ESP = ES + 8;                              // + two park slots (3, padded)
+    static constexpr int HR = RAD ? kRadialMax : 0;                 // the edge's h row (radial mode)
+    static constexpr int ES = NV * DSHP + GQ + HR;                  // floats per edge in the batch
+    static constexpr int PK = RAD ? 12 : 4;                         // parked sums per edge: gr (, gh), padded
+    static constexpr int ESP = ES + 2 * PK;                         // + two park slots
     static constexpr int B = [] {
         int b = 64;
         while (b > 8 && b * ESP * 4 > ETP_SRC_LDS_BATCH)
             b >>= 1;
         return b;
     }();
-    static constexpr int WMUL = MODE == SRC_VJP2 ? 2 : 1;
-    static constexpr int MAXCOST =
-        L <= 2 ? (MODE == SRC_VJP2 ? ETP_SRC_COST_VJP2 : ETP_SRC_COST_VJP) : (L == 3 ? 32 : 40);
-    static constexpr int WPE = ETP_SRC_WPE > 0 ? ETP_SRC_WPE : (MODE == SRC_VJP2 && L == 4 ? 3 : 4);
+    // registers per path beyond its G rows: the w row (and W'), or in the
+    // radial mode the 8 Wr entries
+    static constexpr int WMUL = RAD ? kRadialMax : (MODE == SRC_VJP2 ? 2 : 1);
+    static constexpr int MAXCOST = RAD ? (L <= 2 ? ETP_SRC_COST_RAD : L == 3 ? 130 : 100)
+                                   : L <= 2 ? (MODE == SRC_VJP2 ? ETP_SRC_COST_VJP2 : ETP_SRC_COST_VJP)
+                                            : (L == 3 ? 32 : 40);
+    static constexpr int WPE = ETP_SRC_WPE > 0 ? ETP_SRC_WPE : RAD ? 2 : (MODE == SRC_VJP2 && L == 4 ? 3 : 4);
 };
 
 // Edge splits per channel chunk: four waves per workgroup in total.
@@ -86,8 +101,8 @@ constexpr int src_lds_floats(int nch)
 {
     using Cfg = SrcCfg<L, MODE>;
     const int nw = nch * src_splits(nch);
-    // per wave: the batch (B x ES) and two alternating park slots (B x 4)
-    const int batch = nw * Cfg::B * (Cfg::ES + 8);
+    // per wave: the batch (B x ES) and two alternating park slots (B x PK)
+    const int batch = nw * Cfg::B * Cfg::ESP;
     const int reduce = (src_splits(nch) - 1) * nch * kTab<L>.din_rows * 64;  // node rows of the splits
     return batch > reduce ? batch : reduce;
 }
@@ -100,11 +115,14 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                                           const float *__restrict__ ggx, const float *__restrict__ ggw,
                                           const float *__restrict__ ggvec, float *__restrict__ ox,
                                           float *__restrict__ ow, float *__restrict__ ovec,
-                                          const uint32_t flags, float *lds)
+                                          const uint32_t flags, float *lds, const float *__restrict__ hrad,
+                                          const float *__restrict__ wrad, const int nbasis,
+                                          float *__restrict__ oh)
 {
     using Cfg = SrcCfg<L, MODE>;
-    constexpr int B = Cfg::B, ES = Cfg::ES, NV = Cfg::NV, DSHP = Cfg::DSHP;
-    constexpr bool V2 = MODE == SRC_VJP2;
+    constexpr int B = Cfg::B, ES = Cfg::ES, NV = Cfg::NV, DSHP = Cfg::DSHP, PK = Cfg::PK;
+    constexpr bool V2 = MODE == SRC_VJP2, RAD = Cfg::RAD;
+    constexpr int RK = kRadialMax, HO = NV * DSHP + Cfg::GQ;  // h row offset in an edge's batch slot
     constexpr Groups GR = make_src_groups(kTab<L>, Cfg::MAXCOST, Cfg::WMUL);
     constexpr SrcGroupInfo GI = src_group_info(kTab<L>, GR, SG);
     constexpr int P = kTab<L>.P, DIN = kTab<L>.din_rows, DOUT = kTab<L>.dout_rows, DSH = kTab<L>.dsh;
@@ -121,15 +139,15 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
     const bool active = u < C;
     const uint32_t off4 = active ? static_cast<uint32_t>(u) * 4u : kOOB;
     const uint32_t offx = active ? static_cast<uint32_t>(u) * static_cast<uint32_t>(sizeof(XT)) : kOOB;
-    const bool want_vec = ovec != nullptr;
+    const bool want_vec = ovec != nullptr, want_h = RAD && oh != nullptr;
     const bool has_xp = V2 && ggx != nullptr, has_wp = V2 && ggw != nullptr, has_rp = V2 && ggvec != nullptr;
     const uint32_t rowb = static_cast<uint32_t>(C) * 4u;
 
-    // LDS: per wave the batch [B][ES] and two park slots [2][B][4]
+    // LDS: per wave the batch [B][ES] and two park slots [2][B][PK]
     const int nw = nch * nsp;
     float *blds = lds + wv * (B * ES);
     float *pall = lds + nw * (B * ES);
-    float *plds = pall + wv * (2 * B * 4);
+    float *plds = pall + wv * (2 * B * PK);
 
     // this wave's split of j's out-edges: every nsp-th edge from sp on, so
     // that the splits walk the same (destination-ordered) window of G rows;
@@ -138,6 +156,18 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
     const int cnt = len > sp ? (len - sp + nsp - 1) / nsp : 0;
     const int nbatch = ((len + nsp - 1) / nsp + B - 1) / B;
     auto kpos = [&](int i) { return kbase + i * nsp; };  // position of the split's i-th edge
+
+    // radial mode: the lane's Wr[k, p, u] for the group's paths (zero past
+    // nbasis and C)
+    float wr[RAD ? NP : 1][RK];
+    if constexpr (RAD) {
+        static_range<0, NP>([&](auto q) {
+            static_range<0, RK>([&](auto k) {
+                wr[q][k] =
+                    (active && k < nbasis) ? wrad[(static_cast<int64_t>(k) * P + GI.p0 + q) * C + u] : 0.f;
+            });
+        });
+    }
 
     // node-resident rows of x[j] (and X'[j]) for this group's l1 values
     float xr[NXR], xpr[NXR], acc[NXR];
@@ -165,7 +195,7 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
     auto edge_rsrc = [&](int k, bool valid) {
         const int e = perm[k], i = perm_dst[k];
         EdgeRsrc r;
-        r.w = make_rsrc(w + static_cast<int64_t>(e) * (P * C), valid ? P * C * 4u : 0u);
+        r.w = make_rsrc(RAD ? nullptr : w + static_cast<int64_t>(e) * (P * C), (!RAD && valid) ? P * C * 4u : 0u);
         r.g = make_rsrc(G + static_cast<int64_t>(i) * (DOUT * C), valid ? DOUT * C * 4u : 0u);
         r.wp = make_rsrc(has_wp ? ggw + static_cast<int64_t>(e) * (P * C) : nullptr,
                          has_wp && valid ? P * C * 4u : 0u);
@@ -175,7 +205,8 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
     auto load_path = [&](auto p, const EdgeRsrc &r) {
         constexpr Path pa = kTab<L>.path[p];
         constexpr int GO = pa.out_row - GI.gr0, WQ = p - GI.p0;
-        o.w[WQ] = bload<float, kNT>(r.w, off4, p * rowb);
+        if constexpr (!RAD)  // (the radial mode forms w at the path's start)
+            o.w[WQ] = bload<float, kNT>(r.w, off4, p * rowb);
         if constexpr (V2)
             o.wp[WQ] = bload<float, kNT>(r.wp, off4, p * rowb);
         static_range<0, 2 * pa.l3 + 1>([&](auto m) { o.g[GO + m] = bload<float>(r.g, off4, (pa.out_row + m) * rowb); });
@@ -201,6 +232,10 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                     ep[b] = y.v;
                     cp[b] = make_float4(y.g0, y.g1, y.g2, 0.f);
                 });
+                if constexpr (RAD)
+                    static_range<0, RK>([&](auto k) {
+                        ep[HO + k] = k < nbasis ? hrad[static_cast<int64_t>(e) * nbasis + k] : 0.f;
+                    });
             } else {
                 float px = 0.f, py = 0.f, pz = 0.f;
                 if (has_rp) {
@@ -228,7 +263,7 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
         if (want_vec && ch == 0 && lane < nb) {
             float g0 = 0.f, g1 = 0.f, g2 = 0.f;
             for (int c = 0; c < nch; ++c) {
-                const float *pp = pall + (sp * nch + c) * (2 * B * 4) + (slot * B + lane) * 4;
+                const float *pp = pall + (sp * nch + c) * (2 * B * PK) + (slot * B + lane) * PK;
                 g0 += pp[0];
                 g1 += pp[1];
                 g2 += pp[2];
@@ -243,12 +278,27 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
             gp[1] = g1;
             gp[2] = g2;
         }
+        if constexpr (RAD) {
+            if (want_h && ch == 0 && lane < nb) {
+                float gk[RK];
+                static_range<0, RK>([&](auto k) { gk[k] = 0.f; });
+                for (int c = 0; c < nch; ++c) {
+                    const float *pp = pall + (sp * nch + c) * (2 * B * PK) + (slot * B + lane) * PK + 4;
+                    static_range<0, RK>([&](auto k) { gk[k] += pp[k]; });
+                }
+                float *hp = oh + static_cast<int64_t>(perm[kpos(i0 + lane)]) * nbasis;
+                static_range<0, RK>([&](auto k) {
+                    if (k < nbasis)
+                        hp[k] = SG > 0 ? hp[k] + gk[k] : gk[k];
+                });
+            }
+        }
     };
 
     // One edge, path by path: the K contraction of the gathered G rows, the
     // node accumulators, the weight cotangent (stored) and the Z partial
     // sums; then the path's registers take the next edge's rows.
-    float Z[DSH], Z2[V2 ? DSH : 1];
+    float Z[DSH], Z2[V2 ? DSH : 1], ghk[RAD ? RK : 1];
     static_range<0, DSH>([&](auto b) {
         Z[b] = 0.f;
         if constexpr (V2)
@@ -271,6 +321,12 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
             }
         });
         const rsrc_t rgw = make_rsrc(ow ? ow + static_cast<int64_t>(e) * (P * C) : nullptr, ow ? P * C * 4u : 0u);
+        float4 h0, h1;
+        if constexpr (RAD) {
+            h0 = *reinterpret_cast<const float4 *>(ep + HO);
+            h1 = *reinterpret_cast<const float4 *>(ep + HO + 4);
+            static_range<0, RK>([&](auto k) { ghk[k] = 0.f; });
+        }
         static_range<GI.p0, GI.p1>([&](auto p) {
 #ifdef ETP_SRC_SCHED_FENCE
             __builtin_amdgcn_sched_barrier(0);
@@ -278,7 +334,19 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
             constexpr Path pa = kTab<L>.path[p];
             constexpr int d1 = 2 * pa.l1 + 1;
             constexpr int XO = pa.x_row - GI.xr0, GO = pa.out_row - GI.gr0, WQ = p - GI.p0;
-            const float wp = o.w[WQ];
+            float wp;
+            if constexpr (RAD) {  // w[e, p, u] = sum_k h[e, k] Wr[k, p, u], k in order
+                float t = h0.x * wr[WQ][0];
+                t = fmaf(h0.y, wr[WQ][1], t);
+                t = fmaf(h0.z, wr[WQ][2], t);
+                t = fmaf(h0.w, wr[WQ][3], t);
+                t = fmaf(h1.x, wr[WQ][4], t);
+                t = fmaf(h1.y, wr[WQ][5], t);
+                t = fmaf(h1.z, wr[WQ][6], t);
+                wp = fmaf(h1.w, wr[WQ][7], t);
+            } else {
+                wp = o.w[WQ];
+            }
             float wpp = 0.f;
             if constexpr (V2)
                 wpp = o.wp[WQ];
@@ -341,7 +409,10 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                         gwv = fmaf(xpr[XO + a], s[a], fmaf(xr[XO + a], sd[a], gwv));
                 }
             });
-            bstore<float, kNT>(gwv, rgw, off4, p * rowb);
+            if constexpr (RAD)  // gh[e, k] += gw[e, p, u] Wr[k, p, u] (summed over lanes later)
+                static_range<0, RK>([&](auto k) { ghk[k] = fmaf(gwv, wr[WQ][k], ghk[k]); });
+            else
+                bstore<float, kNT>(gwv, rgw, off4, p * rowb);
         });
     };
 
@@ -368,6 +439,8 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
         g0 = wave_sum_to_lane63(g0);
         g1 = wave_sum_to_lane63(g1);
         g2 = wave_sum_to_lane63(g2);
+        if constexpr (RAD)
+            static_range<0, RK>([&](auto k) { ghk[k] = wave_sum_to_lane63(ghk[k]); });
     };
 
     int kb = 0, done = 0;
@@ -409,10 +482,24 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                     gp[2] = g2;
                 }
             } else if (lane == 63) {
-                float *pp = plds + ((done & 1) * B + kb) * 4;
+                float *pp = plds + ((done & 1) * B + kb) * PK;
                 pp[0] = g0;
                 pp[1] = g1;
                 pp[2] = g2;
+            }
+        }
+        if constexpr (RAD) {
+            if (want_h && lane == 63) {
+                if (nch == 1) {
+                    float *hp = oh + static_cast<int64_t>(e) * nbasis;
+                    static_range<0, RK>([&](auto k) {
+                        if (k < nbasis)
+                            hp[k] = SG > 0 ? hp[k] + ghk[k] : ghk[k];
+                    });
+                } else {
+                    float *pp = plds + ((done & 1) * B + kb) * PK + 4;
+                    static_range<0, RK>([&](auto k) { pp[k] = ghk[k]; });
+                }
             }
         }
         if (++kb == nb) {
@@ -461,11 +548,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SrcCfg
                const int *__restrict__ perm_dst, const float *__restrict__ vec, const XT *__restrict__ x,
                const float *__restrict__ w, const float *__restrict__ G, const float *__restrict__ ggx,
                const float *__restrict__ ggw, const float *__restrict__ ggvec, float *__restrict__ ox,
-               float *__restrict__ ow, float *__restrict__ ovec, const uint32_t flags)
+               float *__restrict__ ow, float *__restrict__ ovec, const uint32_t flags,
+               const float *__restrict__ hrad, const float *__restrict__ wrad, const int nbasis,
+               float *__restrict__ oh)
 {
     extern __shared__ float lds[];
     src_group<L, XT, MODE, SG>(n_src, C, src_ptr, perm, perm_dst, vec, x, w, G, ggx, ggw, ggvec, ox, ow, ovec, flags,
-                               lds);
+                               lds, hrad, wrad, nbasis, oh);
 }
 
 template <int L, typename XT, int MODE>
@@ -485,14 +574,14 @@ static hipError_t launch_src_t(const ConvArgs &a)
             return;
         hipLaunchKernelGGL((src_kernel<L, XT, MODE, g>), dim3(a.n_src), dim3(64 * nch * src_splits(nch)), lds_bytes,
                            a.stream, a.n_src, a.C, a.src_ptr, a.perm, a.perm_dst, a.vec, static_cast<const XT *>(a.x), a.w, a.G, a.ggx,
-                           a.ggw, a.ggvec, a.ox, a.ow, a.ovec, a.flags);
+                           a.ggw, a.ggvec, a.ox, a.ow, a.ovec, a.flags, a.h, a.wr, a.nbasis, a.oh);
         err = hipGetLastError();
     });
     return err;
 }
 
 #if !defined(ETP_L) || !defined(ETP_XT) || !defined(ETP_MODE)
-#error "compile this file once per (l_max, dtype, mode) with -DETP_L=0..4 -DETP_XT=0|1 -DETP_MODE=0|1"
+#error "compile this file once per (l_max, dtype, mode) with -DETP_L=0..4 -DETP_XT=0|1 -DETP_MODE=0|1|2"
 #endif
 
 hipError_t ETP_RUN_NAME(src, ETP_L, ETP_XT, ETP_MODE)(const ConvArgs &a)

@@ -30,7 +30,7 @@ ETP_FLAG_VALIDATE = 2
 # every symbol include/etp.h declares
 ABI_SYMBOLS = ("etp_plan_create", "etp_plan_destroy", "etp_plan_info", "etp_plan_tables",
                "etp_csr_transpose_workspace", "etp_csr_transpose", "etp_workspace_size", "etp_sh", "etp_edge_conv_fwd",
-               "etp_edge_conv_fwd_radial",
+               "etp_edge_conv_fwd_radial", "etp_edge_conv_vjp_radial",
                "etp_edge_conv_vjp", "etp_edge_conv_vjp2", "etp_channel_mix", "etp_edge_forces",
                "etp_neighbor_workspace", "etp_neighbor_count", "etp_neighbor_fill", "etp_node_product", "etp_node_product_vjp", "etp_channel_mix_vjp",
                "etp_edge_tp_fwd", "etp_edge_tp_vjp", "etp_edge_tp_vjp2",
@@ -99,6 +99,8 @@ def _load():
         "etp_sh": (st, [vp, i64, vp, vp, vp, vp]),
         "etp_edge_conv_fwd": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, u32, vp]),
         "etp_edge_conv_fwd_radial": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, i32, vp, vp, u32, vp]),
+        "etp_edge_conv_vjp_radial": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, i32, vp, vp, vp, vp, vp, u32,
+                                          vp]),
         "etp_edge_conv_vjp": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, vp, vp, vp, u32, vp]),
         "etp_edge_conv_vjp2": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                     vp, u32, vp]),
@@ -313,6 +315,26 @@ def etp_edge_conv_fwd_radial(plan: Plan, graph: Graph, vec, x, h, Wr, out, flags
                                         _ptr(Wr, "Wr", torch.float32, K * plan.P * C, optional=True),
                                         _ptr(out, "out", torch.float32, graph.n_dst * plan.dout_rows * C, optional=True),
                                         flags, _stream(stream)), "etp_edge_conv_fwd_radial")
+
+
+def etp_edge_conv_vjp_radial(plan: Plan, graph: Graph, vec, x, h, Wr, grad_out, grad_x=None, grad_h=None,
+                             grad_vec=None, flags: int = 0, stream=None):
+    """VJP of etp_edge_conv_fwd_radial: grad_x, grad_h [E, K], grad_vec (each optional)."""
+    import torch
+    E, C = graph.n_edges, plan.C
+    K = int(Wr.shape[0]) if Wr is not None else 0
+    g = graph.struct()
+    _check(lib.etp_edge_conv_vjp_radial(
+        plan.handle, ctypes.byref(g),
+        _ptr(vec, "vec", torch.float32, 3 * E, optional=True),
+        _ptr(x, "x", _xdtype(plan), graph.n_src * plan.din_rows * C, optional=True),
+        _ptr(h, "h", torch.float32, E * K, optional=True), K,
+        _ptr(Wr, "Wr", torch.float32, K * plan.P * C, optional=True),
+        _ptr(grad_out, "grad_out", torch.float32, graph.n_dst * plan.dout_rows * C, optional=True),
+        _ptr(grad_x, "grad_x", torch.float32, graph.n_src * plan.din_rows * C, optional=True),
+        _ptr(grad_h, "grad_h", torch.float32, E * K, optional=True),
+        _ptr(grad_vec, "grad_vec", torch.float32, 3 * E, optional=True),
+        flags, _stream(stream)), "etp_edge_conv_vjp_radial")
 
 
 def etp_edge_conv_vjp(plan: Plan, graph: Graph, vec, x, w, grad_out, grad_x=None, grad_w=None, grad_vec=None,

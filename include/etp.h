@@ -212,6 +212,23 @@ ETP_API etp_status etp_edge_conv_vjp(etp_plan_t plan, const etp_graph *g, const 
                              const float *grad_out, float *grad_x, float *grad_w, float *grad_vec, uint32_t flags,
                              void *stream);
 
+/* VJP of etp_edge_conv_fwd_radial (the force call of a model whose path
+ * weights come from radial features): with w = h Wr formed in the kernel as
+ * in the forward, grad_x and grad_vec as etp_edge_conv_vjp gives them, and
+ * instead of grad_w its contraction with the last layer,
+ *   grad_h[e, k] = sum_{p,u} grad_w[e, p, u] Wr[(k*P + p)*C + u]
+ * (DEVICE float [n_edges][n_basis]; with grad_vec it yields the forces
+ * through h's dependence on |r|). The gradient with respect to Wr (a sum
+ * over all edges, needed only for training) is not formed. Outputs may be
+ * NULL; ETP_FLAG_ACCUMULATE applies to grad_x only. Sums over channels,
+ * paths and channel chunks are in a fixed order (deterministic). Needs the
+ * transpose in g; C <= 256. Errors as etp_edge_conv_fwd_radial, plus
+ * UNSUPPORTED for C > 256. */
+ETP_API etp_status etp_edge_conv_vjp_radial(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x,
+                                            const float *h, int32_t n_basis, const float *Wr,
+                                            const float *grad_out, float *grad_x, float *grad_h, float *grad_vec,
+                                            uint32_t flags, void *stream);
+
 /* VJP of the VJP: with cotangents (gg_x, gg_w, gg_vec) on (grad_x, grad_w,
  * grad_vec), the gradients of S = <gg_x, grad_x> + <gg_w, grad_w> +
  * <gg_vec, grad_vec> with respect to x (d_x), w (d_w), vec (d_vec) and

@@ -1,7 +1,8 @@
 """GPU parity of the forward with radial weights formed in the kernel
-(w = h Wr, then the convolution), through the C ABI, against the float64
-oracle: every l_max, ragged channel counts, 1..8 basis functions, bf16
-features, accumulate, an empty graph, the argument checks and the
+(w = h Wr, then the convolution) and of its VJP (grad_x, grad_h, grad_vec),
+through the C ABI, against the float64 oracle: every l_max, ragged channel
+counts (one to four 64-channel chunks), 1..8 basis functions, bf16 features,
+accumulate, null outputs, empty rows, the argument checks and the
 benchmarked 1024-node microbenchmark at full size on sampled rows."""
 import sys
 
@@ -11,7 +12,7 @@ import pytest
 import oracle
 import workloads
 
-from gpu_common import BF16_TOL, FP32_TOL, DeviceProblem, dev, dst_subgraph, np_, rel_err
+from gpu_common import BF16_TOL, FP32_TOL, DeviceProblem, dev, dst_subgraph, np_, rel_err, src_subgraph
 
 pytestmark = pytest.mark.gpu
 
@@ -103,3 +104,113 @@ def test_radial_micro_full_size_sampled():
     rp, eidx = dst_subgraph(wl, rows)
     ref = oracle.fwd_radial(wl.L, rp, wl.src[eidx], wl.vec[eidx], wl.x, h[eidx], Wr)
     assert rel_err(out[rows], ref) < FP32_TOL, rel_err(out[rows], ref)
+
+
+def run_vjp(p, h, Wr, want=("gx", "gh", "gr"), flags=0, gx=None):
+    wl = p.wl
+    K = h.shape[1]
+    if gx is None and "gx" in want:
+        gx = p.empty(wl.n, wl.Din, wl.C)
+    gh = p.empty(wl.E, K) if "gh" in want else None
+    gr = p.empty(wl.E, 3) if "gr" in want else None
+    p.etp.etp_edge_conv_vjp_radial(p.plan, p.graph, p.vec, p.x, dev(h), dev(Wr), p.G, gx, gh, gr, flags)
+    return gx, gh, gr
+
+
+VJP_CASES = [(0, 64, 8), (1, 1, 3), (1, 64, 4), (2, 128, 8), (2, 100, 1), (2, 200, 6), (2, 256, 8),
+             (3, 128, 8), (3, 64, 5), (4, 64, 8), (4, 130, 2)]
+
+
+@pytest.mark.parametrize("L,C,K", VJP_CASES)
+def test_radial_vjp_small(L, C, K):
+    say("vjp", L, C, K)
+    wl = workloads.small(L, C, 23, 14, seed=L * 7 + C + K)
+    h, Wr = workloads.radial_inputs(wl.E, K, L, C, seed=K + 1)
+    p = DeviceProblem(wl, need=("G",))
+    gx, gh, gr = (np_(t) for t in run_vjp(p, h, Wr))
+    rgx, rgh, rgr, _ = oracle.vjp_radial(L, wl.row_ptr, wl.src, wl.vec, wl.x, h, Wr, wl.G)
+    assert rel_err(gx, rgx) < FP32_TOL, rel_err(gx, rgx)
+    assert rel_err(gh, rgh) < FP32_TOL, rel_err(gh, rgh)
+    assert rel_err(gr, rgr) < FP32_TOL, rel_err(gr, rgr)
+
+
+@pytest.mark.parametrize("want", [("gh",), ("gr",), ("gx",), ("gh", "gr")])
+def test_radial_vjp_null_outputs(want):
+    say("vjp-null", want)
+    L, C, K = 2, 128, 8
+    wl = workloads.small(L, C, 17, 10, seed=31)
+    h, Wr = workloads.radial_inputs(wl.E, K, L, C, seed=2)
+    p = DeviceProblem(wl, need=("G",))
+    got = dict(zip(("gx", "gh", "gr"), run_vjp(p, h, Wr, want=want)))
+    ref = dict(zip(("gx", "gh", "gr"), oracle.vjp_radial(L, wl.row_ptr, wl.src, wl.vec, wl.x, h, Wr, wl.G)))
+    for k in want:
+        assert rel_err(np_(got[k]), ref[k]) < FP32_TOL, (k, rel_err(np_(got[k]), ref[k]))
+
+
+def test_radial_vjp_accumulate_and_fan_out():
+    """ACCUMULATE adds grad_x; few sources with many out-edges each, then many
+    sources per destination."""
+    import torch
+    say("vjp-acc")
+    L, C, K = 2, 64, 4
+    wl = workloads.bipartite(L, C, 300, 6, 1, 6, seed=8)
+    h, Wr = workloads.radial_inputs(wl.E, K, L, C, seed=5)
+    p = DeviceProblem(wl, need=("G",))
+    rgx, rgh, rgr, _ = oracle.vjp_radial(L, wl.row_ptr, wl.src, wl.vec, wl.x, h, Wr, wl.G)
+    base = torch.randn(wl.n, wl.Din, wl.C, device="cuda")
+    gx, gh, gr = run_vjp(p, h, Wr, flags=p.etp.ETP_FLAG_ACCUMULATE, gx=base.clone())
+    assert rel_err(np_(gx) - np_(base), rgx) < FP32_TOL
+    assert rel_err(np_(gh), rgh) < FP32_TOL
+    assert rel_err(np_(gr), rgr) < FP32_TOL
+    wl2 = workloads.bipartite(L, C, 5, 400, 250, 390, seed=9)
+    h2, Wr2 = workloads.radial_inputs(wl2.E, K, L, C, seed=6)
+    p2 = DeviceProblem(wl2, need=("G",))
+    gx2, gh2, gr2 = (np_(t) for t in run_vjp(p2, h2, Wr2))
+    r2 = oracle.vjp_radial(L, wl2.row_ptr, wl2.src, wl2.vec, wl2.x, h2, Wr2, wl2.G)
+    for got, ref in zip((gx2, gh2, gr2), r2[:3]):
+        assert rel_err(got, ref) < FP32_TOL
+
+
+def test_radial_vjp_bf16_features():
+    say("vjp-bf16")
+    L, C, K = 3, 128, 8
+    wl = workloads.small(L, C, 19, 12, seed=41)
+    h, Wr = workloads.radial_inputs(wl.E, K, L, C, seed=7)
+    p = DeviceProblem(wl, bf16=True, need=("G",))
+    gx, gh, gr = (np_(t) for t in run_vjp(p, h, Wr))
+    ref = oracle.vjp_radial(L, wl.row_ptr, wl.src, wl.vec, p.x_seen, h, Wr, wl.G)
+    for name, got, r in zip(("gx", "gh", "gr"), (gx, gh, gr), ref[:3]):
+        assert rel_err(got, r) < FP32_TOL, (name, rel_err(got, r))
+
+
+def test_radial_vjp_argument_checks():
+    import torch
+    say("vjp-args")
+    wl = workloads.small(1, 8, 6, 3, seed=2)
+    p = DeviceProblem(wl, need=("G",))
+    gr = p.empty(wl.E, 3)
+    for K in (0, 9):
+        h = torch.zeros(wl.E, max(K, 1), device="cuda")
+        Wr = torch.zeros(max(K, 1), p.plan.P, wl.C, device="cuda")
+        with pytest.raises(p.etp.EtpError) as ei:
+            p.etp.etp_edge_conv_vjp_radial(p.plan, p.graph, p.vec, p.x, h if K else None, Wr if K else None, p.G,
+                                           grad_vec=gr)
+        assert ei.value.status in (p.etp.ETP_ERR_UNSUPPORTED, p.etp.ETP_ERR_INVALID_ARGUMENT)
+
+
+def test_radial_vjp_micro_full_size_sampled():
+    """The microbenchmark's VJP with 8 basis functions at full size; source
+    nodes sampled, their out-edges recomputed by the oracle."""
+    say("vjp-micro")
+    wl = workloads.get("micro")
+    K = 8
+    h, Wr = workloads.radial_inputs(wl.E, K, wl.L, wl.C, seed=11)
+    p = DeviceProblem(wl, need=("G",))
+    gx, gh, gr = (np_(t) for t in run_vjp(p, h, Wr))
+    g = np.random.default_rng(4)
+    cols = np.unique(np.concatenate([[0, wl.n - 1], g.choice(wl.n, 6, replace=False)]))
+    rp2, eidx2 = src_subgraph(wl, cols)
+    rgx, rgh, rgr, _ = oracle.vjp_radial(wl.L, rp2, wl.src[eidx2], wl.vec[eidx2], wl.x, h[eidx2], Wr, wl.G)
+    assert rel_err(gx[cols], rgx[cols]) < FP32_TOL
+    assert rel_err(gh[eidx2], rgh) < FP32_TOL
+    assert rel_err(gr[eidx2], rgr) < FP32_TOL

@@ -32,7 +32,7 @@ def header_symbols():
 
 def test_header_symbols_exported():
     names = header_symbols()
-    assert len(names) == 25
+    assert len(names) == 26
     assert sorted(etp.ABI_SYMBOLS) == names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (etp_\w+)$", out, flags=re.M))
@@ -140,6 +140,14 @@ def test_call_validation_without_device():
     assert fr(plan.handle, ctypes.byref(g5), 8, 8, 8, 4, 8, 8, 4, None) == INV
     assert fr(None, ctypes.byref(g5), 8, 8, 8, 4, 8, 8, 0, None) == INV
     assert fr(plan.handle, ctypes.byref(g2), 8, 8, 8, 4, 8, 8, 0, None) == UNS
+    vr = lib.etp_edge_conv_vjp_radial
+    assert vr(plan.handle, ctypes.byref(g5), 8, 8, 8, 0, 8, 8, 8, 8, 8, 0, None) == UNS
+    assert vr(plan.handle, ctypes.byref(g5), 8, 8, None, 4, 8, 8, 8, 8, 8, 0, None) == INV
+    assert vr(plan.handle, ctypes.byref(g5), 8, 8, 8, 4, None, 8, 8, 8, 8, 0, None) == INV
+    assert vr(plan.handle, ctypes.byref(g5), 8, 8, 8, 4, 8, 8, 8, 8, 8, 4, None) == INV
+    assert vr(plan.handle, ctypes.byref(g4), 8, 8, 8, 4, 8, 8, 8, 8, 8, 0, None) == INV    # no transpose
+    assert vr(big.handle, ctypes.byref(g5), 8, 8, 8, 4, 8, 8, 8, 8, 8, 0, None) == UNS    # C > 256
+    assert vr(plan.handle, ctypes.byref(g5), 8, 8, 8, 4, 8, 8, None, None, None, 0, None) == 0  # nothing wanted
     assert lib.etp_csr_transpose(ctypes.byref(g5), 8, 8, 8, None, 0, None) == WS
     assert lib.etp_csr_transpose(ctypes.byref(g5), 8, 8, 8, 8, 1, None) == WS
     assert lib.etp_sh(None, 4, 8, 8, None, None) == INV
