@@ -54,7 +54,7 @@ namespace etp {
 #define ETP_DST_ROWS_FWD 112
 #endif
 #ifndef ETP_DST_ROWS_DG
-#define ETP_DST_ROWS_DG 40
+#define ETP_DST_ROWS_DG 64  // two groups at l = 2, C = 128 (40: three, 15% slower)
 #endif
 #ifndef ETP_DST_ROWS_FWD3
 #define ETP_DST_ROWS_FWD3 ETP_DST_ROWS_FWD
@@ -63,7 +63,10 @@ namespace etp {
 #define ETP_DST_ROWS_FWD4 80
 #endif
 #ifndef ETP_DST_ROWS_DG3
-#define ETP_DST_ROWS_DG3 ETP_DST_ROWS_DG
+#define ETP_DST_ROWS_DG3 56
+#endif
+#ifndef ETP_DST_ROWS_DG1
+#define ETP_DST_ROWS_DG1 40
 #endif
 #ifndef ETP_DST_ROWS_DG4
 #define ETP_DST_ROWS_DG4 24
@@ -81,7 +84,10 @@ struct DstCfg {
     static constexpr int ROWS = MODE == DST_FWD_RADIAL ? (L <= 2 ? ETP_DST_ROWS_FWD : ETP_DST_ROWS_RAD)
                               : MODE == DST_FWD ? (L <= 2 ? ETP_DST_ROWS_FWD : L == 3 ? ETP_DST_ROWS_FWD3 : ETP_DST_ROWS_FWD4)
                                                 : (L <= 2 ? ETP_DST_ROWS_DG : L == 3 ? ETP_DST_ROWS_DG3 : ETP_DST_ROWS_DG4);
-    static constexpr int MAXROWS = (ROWS + CPL - 1) / CPL;
+    // (the dG pass with one channel per lane keeps 40-row groups at l <= 3:
+    // one 51-row group at l = 2, C = 64 is 19% slower than two)
+    static constexpr int MAXROWS =
+        (MODE == DST_DG && CPL == 1 && L <= 3) ? ETP_DST_ROWS_DG1 : (ROWS + CPL - 1) / CPL;
     static constexpr int TCOPIES = MODE == DST_DG ? 2 : 1;  // T (and Td) per edge
     // waves per SIMD the registers must allow: 3 at l=3 (169 VGPRs otherwise);
     // 2 in the radial mode, whose Wr entries take 8 registers per path

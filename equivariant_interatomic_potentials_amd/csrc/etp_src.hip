@@ -52,12 +52,22 @@ namespace etp {
 // registers of one path group (see make_src_groups) and WPE is the waves per
 // SIMD the register allocation must allow: four where the group fits in 128
 // VGPRs, fewer where the batch's SH (second-order jets at high l_max) need
-// more. The ETP_SRC_* macros override the defaults for tuning builds.
+// more, and two for the VJP-of-VJP, whose groups then take 256 VGPRs (at
+// l = 2 all paths fit one group: one walk over the edges instead of four
+// beats the lost occupancy, since the pass is VALU-bound and every group
+// repeats the SH jets and the x, X' loads). The ETP_SRC_* macros override
+// the defaults for tuning builds.
 #ifndef ETP_SRC_COST_VJP
 #define ETP_SRC_COST_VJP 60
 #endif
 #ifndef ETP_SRC_COST_VJP2
-#define ETP_SRC_COST_VJP2 40
+#define ETP_SRC_COST_VJP2 100  // one group at l = 2 (two waves per SIMD; 40: four groups, 15% slower)
+#endif
+#ifndef ETP_SRC_COST_VJP2_3
+#define ETP_SRC_COST_VJP2_3 80  // (32 at four waves per SIMD: 13% slower)
+#endif
+#ifndef ETP_SRC_COST_VJP2_4
+#define ETP_SRC_COST_VJP2_4 64  // (40 at three waves per SIMD: 11% slower)
 #endif
 #ifndef ETP_SRC_COST_RAD
 #define ETP_SRC_COST_RAD 150
@@ -88,9 +98,10 @@ struct SrcCfg {
     // radial mode the 8 Wr entries
     static constexpr int WMUL = RAD ? kRadialMax : (MODE == SRC_VJP2 ? 2 : 1);
     static constexpr int MAXCOST = RAD ? (L <= 2 ? ETP_SRC_COST_RAD : L == 3 ? 130 : 100)
-                                   : L <= 2 ? (MODE == SRC_VJP2 ? ETP_SRC_COST_VJP2 : ETP_SRC_COST_VJP)
-                                            : (L == 3 ? 32 : 40);
-    static constexpr int WPE = ETP_SRC_WPE > 0 ? ETP_SRC_WPE : RAD ? 2 : (MODE == SRC_VJP2 && L == 4 ? 3 : 4);
+                                   : MODE == SRC_VJP2 ? (L <= 2 ? ETP_SRC_COST_VJP2 : L == 3 ? ETP_SRC_COST_VJP2_3
+                                                                                         : ETP_SRC_COST_VJP2_4)
+                                                      : (L <= 2 ? ETP_SRC_COST_VJP : L == 3 ? 32 : 40);
+    static constexpr int WPE = ETP_SRC_WPE > 0 ? ETP_SRC_WPE : (RAD || MODE == SRC_VJP2) ? 2 : 4;
 };
 
 // Edge splits per channel chunk: four waves per workgroup in total.
