@@ -63,6 +63,12 @@ namespace etp {
 #ifndef ETP_SRC_COST_VJP2
 #define ETP_SRC_COST_VJP2 100  // one group at l = 2 (two waves per SIMD; 40: four groups, 15% slower)
 #endif
+#ifndef ETP_SRC_COST_VJP_3
+#define ETP_SRC_COST_VJP_3 48  // at three waves per SIMD (32 at four: 5% slower)
+#endif
+#ifndef ETP_SRC_COST_VJP_4
+#define ETP_SRC_COST_VJP_4 40
+#endif
 #ifndef ETP_SRC_COST_VJP2_3
 #define ETP_SRC_COST_VJP2_3 80  // (32 at four waves per SIMD: 13% slower)
 #endif
@@ -100,8 +106,9 @@ struct SrcCfg {
     static constexpr int MAXCOST = RAD ? (L <= 2 ? ETP_SRC_COST_RAD : L == 3 ? 130 : 100)
                                    : MODE == SRC_VJP2 ? (L <= 2 ? ETP_SRC_COST_VJP2 : L == 3 ? ETP_SRC_COST_VJP2_3
                                                                                          : ETP_SRC_COST_VJP2_4)
-                                                      : (L <= 2 ? ETP_SRC_COST_VJP : L == 3 ? 32 : 40);
-    static constexpr int WPE = ETP_SRC_WPE > 0 ? ETP_SRC_WPE : (RAD || MODE == SRC_VJP2) ? 2 : 4;
+                                                      : (L <= 2 ? ETP_SRC_COST_VJP : L == 3 ? ETP_SRC_COST_VJP_3
+                                                                                         : ETP_SRC_COST_VJP_4);
+    static constexpr int WPE = ETP_SRC_WPE > 0 ? ETP_SRC_WPE : (RAD || MODE == SRC_VJP2) ? 2 : (L == 3 ? 3 : 4);
 };
 
 // Edge splits per channel chunk: four waves per workgroup in total.
