@@ -48,7 +48,7 @@ namespace etp {
 // values (and for the VJP-of-VJP the directional derivative Yd) and the
 // coefficients that turn the Z sums into gr / dr (3 or 6 per SH component);
 // B edges per SH batch is the largest power of two up to 64 whose batch fits
-// in 8 KiB, so four waves per SIMD fit the CU's LDS. MAXCOST bounds the
+// in 8 KiB (16 KiB at two waves per SIMD), so the waves of a CU fit its LDS. MAXCOST bounds the
 // registers of one path group (see make_src_groups) and WPE is the waves per
 // SIMD the register allocation must allow: four where the group fits in 128
 // VGPRs, fewer where the batch's SH (second-order jets at high l_max) need
@@ -94,9 +94,12 @@ struct SrcCfg {
     static constexpr int ES = NV * DSHP + GQ + HR;                  // floats per edge in the batch
     static constexpr int PK = RAD ? 12 : 4;                         // parked sums per edge: gr (, gh), padded
     static constexpr int ESP = ES + 2 * PK;                         // + two park slots
+    // at two waves per SIMD (VJP2, radial) a wave may take twice the LDS:
+    // longer batches keep more of the prologue's lanes busy (l=3 VJP2: 5%)
+    static constexpr int LDS_BATCH = (RAD || MODE == SRC_VJP2) ? 2 * ETP_SRC_LDS_BATCH : ETP_SRC_LDS_BATCH;
     static constexpr int B = [] {
         int b = 64;
-        while (b > 8 && b * ESP * 4 > ETP_SRC_LDS_BATCH)
+        while (b > 8 && b * ESP * 4 > LDS_BATCH)
             b >>= 1;
         return b;
     }();
