@@ -7,7 +7,11 @@ scale, as translation invariance requires):
     linear readout (E = <G, out>) -> edge-to-atom force assembly;
   * one MACE-like block: convolution -> channel mixing -> node-local
     product, E = <G, product>; the backward chain runs the product's VJP,
-    the mixing's VJP and the convolution's VJP before the force assembly."""
+    the mixing's VJP and the convolution's VJP before the force assembly;
+  * a model whose path weights come from radial features h(|r|) through the
+    in-kernel last layer: the radial VJP's grad_vec and grad_h, chained
+    through dh/d|r|, give the forces, which also match central differences
+    of the oracle's energy in the atom positions."""
 import numpy as np
 import pytest
 
@@ -109,3 +113,87 @@ def test_forces_through_mixing_and_node_product():
     assert rel_err(np_(y), y_o) < FP32_TOL
     assert rel_err(Fg, F_o) < FP32_TOL, rel_err(Fg, F_o)
     assert np.abs(Fg.sum(axis=0)).max() < 1e-4 * np.abs(Fg).max() * np.sqrt(n)
+
+
+def _radial_basis(vec, K, rc):
+    """Test-side radial features h[E, K] and dh/d|r| (float64): a sine (Bessel)
+    basis times a smooth polynomial cutoff, one common choice; any smooth
+    function of |r| that vanishes at the cutoff would do."""
+    r = np.linalg.norm(np.asarray(vec, np.float64), axis=1)[:, None]
+    k = np.arange(1, K + 1)[None, :]
+    a = k * np.pi / rc
+    c = np.sqrt(2.0 / rc)
+    b = c * np.sin(a * r) / r
+    db = c * (a * np.cos(a * r) * r - np.sin(a * r)) / r ** 2
+    t = r / rc
+    u = 1 - 28 * t ** 6 + 48 * t ** 7 - 21 * t ** 8
+    du = (-168 * t ** 5 + 336 * t ** 6 - 168 * t ** 7) / rc
+    return b * u, db * u + b * du
+
+
+def test_forces_of_a_radial_model():
+    import torch
+    from equivariant_interatomic_potentials_amd import etp
+    print("[case] pipeline radial water 6^3", flush=True)
+    L, C, rc, K = 2, 16, 6.0, 8
+    pos, box = workloads.water_positions(4, n_side=6)
+    pos = pos.astype(np.float32)
+    n = pos.shape[0]
+    x = workloads.rng(4, "x").standard_normal((n, 9, C)).astype(np.float32)
+    Gr = workloads.rng(4, "G").standard_normal((n, 51, C)).astype(np.float32)
+    _, Wr = workloads.radial_inputs(1, K, L, C, seed=4)
+
+    row_ptr, src, vec = etp.neighbor_list(dev(pos), box, rc)
+    E = int(src.numel())
+    vec_np = np_(vec)
+    h64, dh64 = _radial_basis(vec_np, K, rc)
+    h = h64.astype(np.float32)
+    plan = etp.etp_plan_create(L, C)
+    src_ptr = torch.empty(n + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(E, dtype=torch.int32, device="cuda")
+    perm_dst = torch.empty(E, dtype=torch.int32, device="cuda")
+    ws = torch.empty(etp.etp_csr_transpose_workspace(n), dtype=torch.uint8, device="cuda")
+    etp.etp_csr_transpose(etp.Graph(n, n, row_ptr, src), src_ptr, perm, perm_dst, ws)
+    graph = etp.Graph(n, n, row_ptr, src, src_ptr, perm, perm_dst)
+    gr = torch.empty(E, 3, device="cuda")
+    gh = torch.empty(E, K, device="cuda")
+    etp.etp_edge_conv_vjp_radial(plan, graph, vec, dev(x), dev(h), dev(Wr), dev(Gr), None, gh, gr)
+    # dE/dvec = the direct part + sum_k dE/dh_k dh_k/d|r| r/|r| (test-side glue)
+    rhat = vec / vec.norm(dim=1, keepdim=True)
+    g_all = gr + (gh * dev(dh64.astype(np.float32))).sum(dim=1, keepdim=True) * rhat
+    F = torch.empty(n, 3, device="cuda")
+    etp.etp_edge_forces(graph, g_all.contiguous(), F)
+
+    rp_o, src_o, vec_o = oracle.neighbors(pos, box, rc)
+    np.testing.assert_array_equal(np_(src), src_o)
+
+    def oracle_forces(hh, dhh):
+        _, gh_o, gr_o, _ = oracle.vjp_radial(L, rp_o, src_o, vec_o, x, hh, Wr, Gr)
+        v = vec_o.astype(np.float64)
+        g = gr_o + (gh_o * dhh).sum(axis=1, keepdims=True) * v / np.linalg.norm(v, axis=1, keepdims=True)
+        return oracle.edge_forces(rp_o, src_o, n, g)
+
+    F_o = oracle_forces(h, dh64)
+    Fg = np_(F)
+    assert rel_err(Fg, F_o) < FP32_TOL, rel_err(Fg, F_o)
+    assert np.abs(Fg.sum(axis=0)).max() < 1e-4 * np.abs(Fg).max() * np.sqrt(n)
+
+    # the oracle's forces are -dE/dpos: central differences of
+    # E = sum_e <G[dst_e], message_e> over the edges that touch the atom
+    F64 = oracle_forces(h64, dh64)
+    dst_o = np.repeat(np.arange(n), np.diff(rp_o))
+    vec64 = vec_o.astype(np.float64)
+    for i in (0, 17, 300):
+        eidx = np.nonzero((src_o == i) | (dst_o == i))[0]
+        sign = (src_o[eidx] == i).astype(np.float64) - (dst_o[eidx] == i)
+        ar = np.arange(len(eidx) + 1, dtype=np.int32)
+        for d in range(3):
+            def energy(eps):
+                v = vec64[eidx].copy()
+                v[:, d] += sign * eps
+                hh, _ = _radial_basis(v, K, rc)
+                out = oracle.fwd_radial(L, ar, src_o[eidx], v, x, hh, Wr)
+                return float((Gr[dst_o[eidx]] * out).sum())
+            eps = 1e-5
+            fd = -(energy(eps) - energy(-eps)) / (2 * eps)
+            assert abs(fd - F64[i, d]) < 1e-6 * np.abs(F64).max(), (i, d, fd, F64[i, d])
