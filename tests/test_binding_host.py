@@ -60,3 +60,18 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     mod = importlib.util.module_from_spec(spec)
     with pytest.raises(ImportError, match="not built"):
         spec.loader.exec_module(mod)
+
+
+def test_radial_binding_sizes_h_by_Wr():
+    """The radial calls take the basis count from Wr's first dimension and
+    check h against it before the C call (pointer arguments given as ints)."""
+    import torch
+    plan = etp.etp_plan_create(2, 8)
+    g = etp.Graph(4, 4, 8, 8, 8, 8, 8, n_edges=10)
+    Wr = torch.zeros(3, plan.P, 8)
+    with pytest.raises(ValueError, match="h must have 30 elements"):
+        etp.etp_edge_conv_fwd_radial(plan, g, 8, 8, torch.zeros(10, 4), Wr, 8)
+    with pytest.raises(ValueError, match="h must have 30 elements"):
+        etp.etp_edge_conv_vjp_radial(plan, g, 8, 8, torch.zeros(10, 2), Wr, 8, grad_h=8)
+    with pytest.raises(ValueError, match="Wr must be torch.float32"):
+        etp.etp_edge_conv_fwd_radial(plan, g, 8, 8, 8, Wr.double(), 8)
