@@ -57,6 +57,34 @@ def test_radial_fwd_bf16_features(L, C):
     assert rel_err(out, ref32) < BF16_TOL
 
 
+@pytest.mark.parametrize("L,C", [(1, 512), (2, 1024)])
+def test_radial_fwd_wide_channels(L, C):
+    """The forward's channel chunks go up to 1024 channels (16 workgroups per node)."""
+    say("wide", L, C)
+    wl = workloads.small(L, C, 11, 6, seed=C + L)
+    h, Wr = workloads.radial_inputs(wl.E, 8, L, C, seed=9)
+    p = DeviceProblem(wl, need=())
+    out = np_(run(p, h, Wr))
+    ref = oracle.fwd_radial(L, wl.row_ptr, wl.src, wl.vec, wl.x, h, Wr)
+    assert rel_err(out, ref) < FP32_TOL, rel_err(out, ref)
+
+
+def test_radial_empty_graph():
+    """No edges: the forward writes zeros and the VJP zero grad_x."""
+    import torch
+    say("empty")
+    wl = workloads.small(2, 64, 7, 0, seed=5)
+    assert wl.E == 0
+    h, Wr = workloads.radial_inputs(0, 4, 2, 64, seed=1)
+    p = DeviceProblem(wl, need=("G",))
+    out = torch.full((wl.n_dst, wl.Dout, wl.C), 7.0, device="cuda")
+    run(p, h, Wr, out=out)
+    assert float(out.abs().max()) == 0.0
+    gx = torch.full((wl.n, wl.Din, wl.C), 7.0, device="cuda")
+    run_vjp(p, h, Wr, gx=gx)
+    assert float(gx.abs().max()) == 0.0
+
+
 def test_radial_accumulate_and_empty_rows():
     """ACCUMULATE adds to out; destinations without edges get 0 (or keep out)."""
     import torch
