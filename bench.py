@@ -1,22 +1,32 @@
 """Benchmark of the fused edge tensor-product convolution on one MI355X.
 
-One step = one pass of the whole device path over the synthetic
-microbenchmark graph (1024 nodes x 128 random neighbours, C = 128 channels,
-l_max = 2, fp32 -- the edge-convolution microbenchmark shape of "How does
-FlashCart make equivariant interatomic potentials faster and more
-accurate?", section "Generated kernels beat SH baselines at high order"):
+Headline workload: the 32768-atom diamond solid (16^3 conventional cells,
+a = 3.567 A, Gaussian jitter 0.05 A, periodic, 6.0 A cutoff: about 158
+neighbours per atom and 5.17 M edges; C = 128 channels, l_max = 3) -- the
+diamond system of "How does FlashCart make equivariant interatomic potentials
+faster and more accurate?" (SPICE-MACE-OFF section), the largest
+configuration that fits one GPU. The node features are fp32 for the value
+(a second run stores them in bf16, fp32 arithmetic either way).
 
-    CSR transpose -> forward -> VJP (gx, gw, forces) -> VJP-of-VJP
-    (dG destination pass, then dx / dw / dr source pass)
+One step = one pass of the whole device path over that graph:
 
-value = edges per second of the whole step (inputs resident in HBM).
-Per-op times come from HIP events recorded on the launch stream inside the
-timed region; the roofline is reported for the op that takes the most time,
-with its algorithmic bytes (every tensor it must touch, once) and
-algorithmic FLOPs per edge. The float64 oracle is timed on the host on a
-bounded sample of destination rows of the same graph.
+    CSR transpose -> forward -> VJP (gx, gw, forces) -> VJP-of-VJP (dx, dw, dr, dG)
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload micro]
+value = edges per second of forward + VJP, E / (t_fwd + t_vjp), with every
+input resident in HBM; the per-op times come from HIP events recorded on the
+launch stream around each call inside the timed region. Every op is also
+reported against its compulsory bytes (each tensor touched once) and
+algorithmic FLOPs; the roofline object is the op that takes the most time.
+The other workloads (tiny, micro, micro3, micro4, water) are timed the same
+way under "configs". The float64 oracle is timed on the host on a bounded
+sample of destination rows of the diamond graph.
+
+Per-edge arrays too large for the device budget (the VJP-of-VJP cotangent
+on w, 90 GB in fp32 at the diamond) are drawn per destination-row chunk on
+the GPU outside the timed ops; each chunk runs on its own sub-CSR and
+transpose, node gradients accumulating across chunks.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload diamond]
 """
 from __future__ import annotations
 
@@ -24,6 +34,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -35,18 +46,22 @@ sys.path.insert(0, ROOT)
 METRIC = "edges/sec for fused edge TP conv (fwd, fwd+VJP) + % of HBM/VALU roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 VALU_PEAK_TFLOPS = 157.3       # MI355X fp32 vector (packed); 78.6 without packing
+MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix-core peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 WORKLOADS = {
-    "micro": "1024 nodes x 128 random neighbours (131072 edges), C=128, l_max=2, fp32",
-    "micro3": "1024 nodes x 128 random neighbours (131072 edges), C=128, l_max=3, fp32",
-    "micro4": "1024 nodes x 128 random neighbours (131072 edges), C=128, l_max=4, fp32",
-    "water": "5184-atom water box, 6 A cutoff, C=64, l_max=2, fp32",
-    "tiny": "32 nodes x 8 random neighbours (256 edges), C=8, l_max=1, fp32",
+    "diamond": "32768-atom diamond (16^3 cells, a=3.567 A, jitter 0.05 A), 6 A cutoff, C=128, l_max=3",
+    "micro": "1024 nodes x 128 random neighbours (131072 edges), C=128, l_max=2",
+    "micro3": "1024 nodes x 128 random neighbours (131072 edges), C=128, l_max=3",
+    "micro4": "1024 nodes x 128 random neighbours (131072 edges), C=128, l_max=4",
+    "water": "5184-atom water box, 6 A cutoff, C=64, l_max=2",
+    "tiny": "32 nodes x 8 random neighbours (256 edges), C=8, l_max=1",
 }
-OPS = ("transpose", "fwd", "vjp", "vjp2_dst", "vjp2_src")
+CONFIG_ORDER = ("tiny", "micro", "micro3", "micro4", "water", "diamond")
+OPS = ("transpose", "fwd", "vjp", "vjp2")
 
 
 def table_counts(L):
-    """(P, nnz, pairs, Din, Dout) from the library's own tables."""
+    """(P, nnz, pairs, Din, Dout, per-path 2l1+1 and 2l3+1) from the library's own tables."""
     from equivariant_interatomic_potentials_amd import etp
     plan = etp.etp_plan_create(L, 8)
     t = etp.etp_plan_tables(plan)
@@ -64,34 +79,47 @@ def table_counts(L):
                 d1=np.array(d1), d3=np.array(d3))
 
 
-def algorithmic(L, C, N, E, n_src):
-    """Per-op algorithmic bytes (each tensor touched once) and FLOPs (2 per FMA)."""
+def compulsory(L, C, N, E, n_src, xb=4):
+    """Per-op compulsory HBM bytes (every tensor the op must read or write,
+    touched once; x in xb bytes per value) and algorithmic FLOPs (2 per FMA of
+    the sparse contraction, per edge and channel: fwd nnz + sum_p min(2l1+1,
+    2l3+1); VJP 2 nnz + pairs + 3 sum_p (2l1+1); VJP-of-VJP 6 nnz + 2 pairs +
+    9 sum_p (2l1+1)). The VJP-of-VJP is one op: its destination and source
+    halves together must touch w, W' and dw once each."""
     k = table_counts(L)
     P, nnz, pairs, Din, Dout = k["P"], k["nnz"], k["pairs"], k["Din"], k["Dout"]
-    f4 = 4
-    w = E * P * C * f4
-    x = n_src * Din * C * f4
-    out = N * Dout * C * f4
-    vec = E * 3 * f4
-    idx = E * 4
+    w = 4.0 * E * P * C
+    xin = float(n_src) * Din * C * xb
+    x32 = 4.0 * n_src * Din * C
+    out = 4.0 * N * Dout * C
+    vec = 12.0 * E
+    idx = 4.0 * E
+    offs = 4.0 * (N + 1)
+    toffs = 4.0 * (n_src + 1)
     by = {
-        "transpose": idx * 4 + (n_src + 1) * 4 + (N + 1) * 4,
-        "fwd": w + x + out + vec + idx + (N + 1) * 4,
-        "vjp": 2 * w + x + out + 2 * vec + 2 * idx + x + (n_src + 1) * 4,
-        "vjp2_dst": 2 * w + 2 * x + out + 2 * vec + idx + (N + 1) * 4,
-        "vjp2_src": 3 * w + 2 * x + out + 3 * vec + 2 * idx + x + (n_src + 1) * 4,
+        "transpose": 4 * idx + toffs + offs,
+        "fwd": w + xin + out + vec + idx + offs,
+        "vjp": 2 * w + xin + x32 + out + 2 * vec + 2 * idx + offs + toffs,
+        "vjp2": 3 * w + xin + 2 * x32 + 2 * out + 3 * vec + 3 * idx + offs + toffs,
     }
     sum_min = int(np.minimum(k["d1"], k["d3"]).sum())
     s1 = int(k["d1"].sum())
-    fma_ch = {
-        "transpose": 0,
-        "fwd": nnz + sum_min,
-        "vjp": 2 * nnz + pairs + 3 * s1,
-        "vjp2_dst": 2 * nnz + 3 * s1,
-        "vjp2_src": 4 * nnz + 2 * pairs + 6 * s1,
-    }
-    fl = {op: 2 * fma_ch[op] * C * E for op in by}
+    fma_ch = {"transpose": 0, "fwd": nnz + sum_min, "vjp": 2 * nnz + pairs + 3 * s1,
+              "vjp2": 6 * nnz + 2 * pairs + 9 * s1}
+    fl = {op: 2.0 * fma_ch[op] * C * E for op in by}
     return by, fl
+
+
+def roof(byts, flops, t):
+    """Roofline of one op: the larger of its HBM and VALU times at peak over
+    the measured time."""
+    th = byts / (HBM_PEAK_GBS * 1e9)
+    tv = flops / (VALU_PEAK_TFLOPS * 1e12)
+    if th >= tv:
+        return {"bound": "hbm", "achieved": round(byts / t / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(th / t, 4)}
+    return {"bound": "alu", "achieved": round(flops / t / 1e12, 2), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tv / t, 4)}
 
 
 def kernel_source_hash():
@@ -107,9 +135,9 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(op):
-    """HBM bytes per launch of `op` from committed rocprofv3 counter runs, if
-    they were taken on the current kernel sources (else None)."""
+def measured_traffic(workload, op):
+    """HBM bytes per call of `op` on `workload` from committed rocprofv3
+    counter runs, if they were taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
     if not os.path.exists(path):
         return None
@@ -117,52 +145,252 @@ def measured_traffic(op):
         d = json.load(f)
     if d.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return d.get("bytes_per_launch", {}).get(op)
+    return d.get("bytes_per_call", {}).get(workload, {}).get(op)
 
 
-MFMA_F32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix-core peak
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
 
 
-def time_radial(etp, plan, g, vec, x, out, G, L, C, N, E, n_src, fwd_ms, vjp_ms, reps, K=8):
-    """The forward and VJP with radial weights formed in the kernel (w = h Wr,
-    K basis functions) on the same graph and features as the step: ms per
-    call with HIP events, against the plain calls that read w (and write gw).
-    Algorithmic bytes: the plain call's with the E P C weight streams
-    replaced by h (and grad_h) and Wr; FLOPs: the plain call's plus 2 K per
-    (edge, path, channel) to form w (and 2 K more for grad_h)."""
+# ------------------------------------------------------------ the step
+
+class Problem:
+    """One workload resident on the GPU: graph, transpose, features, weights,
+    cotangents and outputs, with the step's ops as closures. Per-edge
+    cotangents that do not fit beside w, gw and dw are drawn per chunk of
+    destination rows (outside the timed ops)."""
+
+    def __init__(self, name, bf16=False, shared=None):
+        import torch
+
+        import workloads
+        from equivariant_interatomic_potentials_amd import etp
+        self.etp, self.torch = etp, torch
+        self.name = name
+        self.bf16 = bf16
+        wl = shared["wl"] if shared else workloads.get(name)
+        self.wl = wl
+        L, C, N, E, n_src, P = wl.L, wl.C, wl.n_dst, wl.E, wl.n, wl.P
+        self.L, self.C, self.N, self.E, self.n_src, self.P = L, C, N, E, n_src, P
+        self.plan = etp.etp_plan_create(L, C, etp.ETP_BF16 if bf16 else etp.ETP_F32)
+        cuda = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        if shared:
+            for k in ("row_ptr", "src", "vec", "ggv", "w", "G", "ggx", "x32", "src_ptr", "perm", "perm_dst", "tws",
+                      "chunks", "out", "gx", "gr", "dx", "dr", "dG", "gw", "ggw_full", "ggw_buf"):
+                setattr(self, k, shared[k])
+        else:
+            self.row_ptr, self.src, self.vec = cuda(wl.row_ptr), cuda(wl.src), cuda(wl.vec)
+            self.ggv = cuda(wl.ggvec)
+            # per-edge weights drawn on the device (the diamond's are 90 GB)
+            self.w = workloads.device_normal((E, P, C), wl.seed, "w", 0, 1.0 / np.sqrt(P))
+            self.G = workloads.device_normal((N, wl.Dout, C), wl.seed, "G", 0)
+            self.ggx = workloads.device_normal((n_src, wl.Din, C), wl.seed, "ggx", 0)
+            self.x32 = cuda(wl.x)
+            self.src_ptr = torch.empty(n_src + 1, dtype=torch.int32, device="cuda")
+            self.perm = torch.empty(E, dtype=torch.int32, device="cuda")
+            self.perm_dst = torch.empty(E, dtype=torch.int32, device="cuda")
+            self.tws = torch.empty(etp.etp_csr_transpose_workspace(n_src) // 4 + 1, dtype=torch.int32,
+                                   device="cuda")
+            self.out = torch.empty(N, wl.Dout, C, device="cuda")
+            self.gx = torch.empty(n_src, wl.Din, C, device="cuda")
+            self.gr = torch.empty(E, 3, device="cuda")
+            self.dx, self.dr, self.dG = torch.empty_like(self.gx), torch.empty_like(self.gr), torch.empty_like(self.out)
+            # gw (VJP output) and dw (VJP-of-VJP output) share one buffer: a
+            # step writes gw, then dw over it
+            self.gw = torch.empty(E, P, C, device="cuda")
+            self._plan_chunks()
+        self.x = self.x32.to(torch.bfloat16) if bf16 else self.x32
+        self.g0 = etp.Graph(N, n_src, self.row_ptr, self.src)
+        self.g = etp.Graph(N, n_src, self.row_ptr, self.src, self.src_ptr, self.perm, self.perm_dst)
+
+    def shared(self):
+        return {k: getattr(self, k) for k in (
+            "wl", "row_ptr", "src", "vec", "ggv", "w", "G", "ggx", "x32", "src_ptr", "perm", "perm_dst", "tws",
+            "chunks", "out", "gx", "gr", "dx", "dr", "dG", "gw", "ggw_full", "ggw_buf")}
+
+    def _plan_chunks(self):
+        """Destination-row chunks for the VJP-of-VJP: one when its per-edge
+        cotangent fits beside everything else, else the fewest that fit."""
+        import torch
+
+        import workloads
+        etp, wl = self.etp, self.wl
+        free, _ = torch.cuda.mem_get_info()
+        per_edge = 4.0 * self.P * self.C
+        margin = 6e9
+        n = 1
+        while n < 64 and per_edge * self.E / n > free - margin:
+            n *= 2
+        self.n_chunks = n
+        bounds = np.linspace(0, self.N, n + 1).astype(int)
+        self.chunks = []
+        for c in range(n):
+            r0, r1 = int(bounds[c]), int(bounds[c + 1])
+            e0, e1 = int(wl.row_ptr[r0]), int(wl.row_ptr[r1])
+            ch = {"r0": r0, "r1": r1, "e0": e0, "e1": e1}
+            if n > 1:
+                rp = torch.from_numpy((wl.row_ptr[r0:r1 + 1] - e0).astype(np.int32)).cuda()
+                src = self.src[e0:e1]
+                sp = torch.empty(self.n_src + 1, dtype=torch.int32, device="cuda")
+                pm = torch.empty(e1 - e0, dtype=torch.int32, device="cuda")
+                pd = torch.empty(e1 - e0, dtype=torch.int32, device="cuda")
+                etp.etp_csr_transpose(etp.Graph(r1 - r0, self.n_src, rp, src), sp, pm, pd, self.tws)
+                ch["g"] = etp.Graph(r1 - r0, self.n_src, rp, src, sp, pm, pd)
+            self.chunks.append(ch)
+        if n == 1:
+            self.ggw_full = workloads.device_normal((self.E, self.P, self.C), wl.seed, "ggw", 0)
+            self.ggw_buf = None
+        else:
+            self.ggw_full = None
+            emax = max(ch["e1"] - ch["e0"] for ch in self.chunks)
+            self.ggw_buf = torch.empty(emax * self.P * self.C, device="cuda")
+        torch.cuda.synchronize()
+
+    def fill_ggw(self, c):
+        """The chunk's cotangent on w, drawn in place on the device."""
+        import workloads
+        ch = self.chunks[c]
+        n = (ch["e1"] - ch["e0"]) * self.P * self.C
+        buf = self.ggw_buf[:n].view(ch["e1"] - ch["e0"], self.P, self.C)
+        workloads.device_normal_(buf, self.wl.seed, "ggw", c)
+        return buf
+
+    def step(self, ev=None, ops=OPS):
+        """One pass of the path; ev[op] is a list of (start, end) event pairs
+        that receive the op's calls."""
+        etp = self.etp
+        plan, g = self.plan, self.g
+
+        def timed(op, f):
+            if ev is None:
+                f()
+                return
+            a, b = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            ev[op].append((a, b))
+
+        if "transpose" in ops:
+            timed("transpose", lambda: etp.etp_csr_transpose(self.g0, self.src_ptr, self.perm, self.perm_dst,
+                                                             self.tws))
+        if "fwd" in ops:
+            timed("fwd", lambda: etp.etp_edge_conv_fwd(plan, g, self.vec, self.x, self.w, self.out))
+        if "vjp" in ops:
+            timed("vjp", lambda: etp.etp_edge_conv_vjp(plan, g, self.vec, self.x, self.w, self.G, self.gx,
+                                                       self.gw, self.gr))
+        if "vjp2" in ops:
+            if len(self.chunks) == 1:
+                timed("vjp2", lambda: etp.etp_edge_conv_vjp2(plan, g, self.vec, self.x, self.w, self.G, self.ggx,
+                                                             self.ggw_full, self.ggv, self.dx, self.gw, self.dr,
+                                                             self.dG))
+            else:
+                for c, ch in enumerate(self.chunks):
+                    ggw = self.fill_ggw(c)
+                    r0, r1, e0, e1 = ch["r0"], ch["r1"], ch["e0"], ch["e1"]
+                    acc = etp.ETP_FLAG_ACCUMULATE if c else 0
+                    timed("vjp2", lambda: etp.etp_edge_conv_vjp2(
+                        plan, ch["g"], self.vec[e0:e1], self.x, self.w[e0:e1], self.G[r0:r1], self.ggx, ggw,
+                        self.ggv[e0:e1], self.dx, self.gw[e0:e1], self.dr[e0:e1], self.dG[r0:r1], acc))
+
+    def run(self, steps, warmup, ops=OPS):
+        """warmup untimed steps, then `steps` timed ones; per-op mean ms over
+        the steps (an op's chunks summed) and wall ms per step."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(None, ops)
+        torch.cuda.synchronize()
+        evs = []
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            ev = {op: [] for op in ops}
+            self.step(ev, ops)
+            evs.append(ev)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per_op = {op: float(np.mean([sum(a.elapsed_time(b) for a, b in ev[op]) for ev in evs])) for op in ops}
+        return per_op, wall / steps * 1e3
+
+    def report(self, per_op):
+        """Per-op ms, edges/s and roofline fraction against compulsory bytes."""
+        xb = 2 if self.bf16 else 4
+        by, fl = compulsory(self.L, self.C, self.N, self.E, self.n_src, xb)
+        rep = {}
+        for op, ms in per_op.items():
+            t = ms * 1e-3
+            r = {"ms": round(ms, 4), "edges_per_s": self.E / t, "algo_GBps": round(by[op] / t / 1e9, 1),
+                 "algo_TFLOPs": round(fl[op] / t / 1e12, 2)}
+            if op != "transpose":
+                rf = roof(by[op], fl[op], t)
+                r.update({"bound": rf["bound"], "frac": rf["frac"],
+                          "compulsory_B_per_edge": round(by[op] / self.E, 1),
+                          "flop_per_edge": round(fl[op] / self.E, 1)})
+            rep[op] = r
+        return rep, by, fl
+
+
+def config_entry(name, steps, warmup):
+    """A non-headline workload: fwd, fwd+VJP and per-op figures."""
     import torch
-    import workloads
-    h, Wr = workloads.radial_inputs(E, K, L, C, seed=0)
-    h, Wr = torch.from_numpy(h).cuda(), torch.from_numpy(Wr).cuda()
-    y = torch.empty_like(out)
-    for _ in range(3):
-        etp.etp_edge_conv_fwd_radial(plan, g, vec, x, h, Wr, y)
+    p = Problem(name)
+    per_op, ms_step = p.run(steps, warmup)
+    rep, _, _ = p.report(per_op)
+    fwd_vjp = p.E / ((per_op["fwd"] + per_op["vjp"]) * 1e-3)
+    d = {"workload": WORKLOADS[name], "n_nodes": p.N, "n_edges": p.E, "channels": p.C, "l_max": p.L,
+         "ms_per_step": round(ms_step, 4), "fwd_edges_per_s": rep["fwd"]["edges_per_s"],
+         "fwd_vjp_edges_per_s": fwd_vjp, "vjp2_chunks": len(p.chunks), "ops": rep}
+    del p
+    torch.cuda.empty_cache()
+    return d
+
+
+# ------------------------------------------------- calls beside the step
+
+def time_calls(f, reps, warm=2):
+    import torch
+    for _ in range(warm):
+        f()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(reps):
-        etp.etp_edge_conv_fwd_radial(plan, g, vec, x, h, Wr, y)
+        f()
     b.record()
     torch.cuda.synchronize()
-    t = a.elapsed_time(b) / reps * 1e-3
-    by, fl = algorithmic(L, C, N, E, n_src)
-    P = plan.P
+    return a.elapsed_time(b) / reps * 1e-3
+
+
+def time_radial(etp, p, fwd_ms, vjp_ms, reps, K=8):
+    """The forward and VJP with radial weights formed in the kernel (w = h Wr,
+    K basis functions) on the same graph and features as the step: ms per
+    call against the plain calls that read w (and write gw). Algorithmic
+    bytes: the plain call's with the E P C weight streams replaced by h (and
+    grad_h) and Wr; FLOPs: the plain call's plus 2 K per (edge, path,
+    channel) to form w (and 2 K more for grad_h)."""
+    import torch
+
+    import workloads
+    L, C, E, P = p.L, p.C, p.E, p.P
+    h, Wr = workloads.radial_inputs(E, K, L, C, seed=0)
+    h, Wr = torch.from_numpy(h).cuda(), torch.from_numpy(Wr).cuda()
+    y = torch.empty_like(p.out)
+    t = time_calls(lambda: etp.etp_edge_conv_fwd_radial(p.plan, p.g, p.vec, p.x, h, Wr, y), reps, 3)
+    by, fl = compulsory(L, C, p.N, E, p.n_src)
     byts = by["fwd"] - 4.0 * E * P * C + 4.0 * (E * K + K * P * C)
     flops = fl["fwd"] + 2.0 * K * P * C * E
     res = {"ms": round(t * 1e3, 4), "edges_per_s": E / t, "n_basis": K,
            "speedup_vs_fwd": round(fwd_ms * 1e-3 / t, 3), "algo_GBps": byts / t / 1e9,
            "algo_TFLOPs": flops / t / 1e12, "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS,
            "valu_frac": flops / t / 1e12 / VALU_PEAK_TFLOPS}
-    gx, gh, gr = torch.empty_like(x, dtype=torch.float32), torch.empty(E, K, device="cuda"), torch.empty_like(vec)
-    for _ in range(2):
-        etp.etp_edge_conv_vjp_radial(plan, g, vec, x, h, Wr, G, gx, gh, gr)
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(reps):
-        etp.etp_edge_conv_vjp_radial(plan, g, vec, x, h, Wr, G, gx, gh, gr)
-    b.record()
-    torch.cuda.synchronize()
-    tv = a.elapsed_time(b) / reps * 1e-3
+    gx, gh, gr = torch.empty_like(p.gx), torch.empty(E, K, device="cuda"), torch.empty_like(p.gr)
+    tv = time_calls(lambda: etp.etp_edge_conv_vjp_radial(p.plan, p.g, p.vec, p.x, h, Wr, p.G, gx, gh, gr), reps)
     vb = by["vjp"] - 8.0 * E * P * C + 4.0 * (2 * E * K + K * P * C)
     vf = fl["vjp"] + 4.0 * K * P * C * E
     res.update({"vjp_ms": round(tv * 1e3, 4), "vjp_speedup_vs_vjp": round(vjp_ms * 1e-3 / tv, 3),
@@ -172,40 +400,22 @@ def time_radial(etp, plan, g, vec, x, out, G, L, C, N, E, n_src, fwd_ms, vjp_ms,
 
 def time_channel_mix(etp, plan, out, L, C, N, reps):
     """The per-irrep channel mixing after the convolution (outside the step):
-    ms per call with HIP events, algorithmic bytes (conv output, W, result,
-    each once) and FLOPs (2 per multiply-add of the per-order products)."""
+    ms per call, algorithmic bytes (conv output, W, result, each once) and
+    FLOPs (2 per multiply-add of the per-order products)."""
     import torch
     rows = etp.mix_rows(plan)
     g = torch.Generator(device="cuda")
     g.manual_seed(12345)
     W = torch.randn(sum(rows) * C * C, generator=g, device="cuda") / float(np.sqrt(C))
     y = torch.empty(N, (L + 1) ** 2, C, device="cuda")
-    for _ in range(3):
-        etp.etp_channel_mix(plan, out, W, y)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        etp.etp_channel_mix(plan, out, W, y)
-    b.record()
-    torch.cuda.synchronize()
-    t = a.elapsed_time(b) / reps * 1e-3
+    t = time_calls(lambda: etp.etp_channel_mix(plan, out, W, y), reps, 3)
     byts = 4.0 * (out.numel() + W.numel() + y.numel())
     flops = 2.0 * sum(N * (2 * l + 1) * rows[l] * C * C for l in range(L + 1))
     res = {"ms": round(t * 1e3, 4), "algo_GBps": byts / t / 1e9, "algo_TFLOPs": flops / t / 1e12,
            "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS, "mfma_frac": flops / t / 1e12 / MFMA_F32_PEAK_TFLOPS,
            "bound": "mfma" if flops / (MFMA_F32_PEAK_TFLOPS * 1e12) > byts / (HBM_PEAK_GBS * 1e9) else "hbm"}
-    # the VJP (transposed map, same bytes and FLOPs)
     gin = torch.empty_like(out)
-    for _ in range(2):
-        etp.etp_channel_mix_vjp(plan, y, W, gin)
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(reps):
-        etp.etp_channel_mix_vjp(plan, y, W, gin)
-    b.record()
-    torch.cuda.synchronize()
-    tv = a.elapsed_time(b) / reps * 1e-3
+    tv = time_calls(lambda: etp.etp_channel_mix_vjp(plan, y, W, gin), reps)
     res.update({"vjp_ms": round(tv * 1e3, 4), "vjp_mfma_frac": flops / tv / 1e12 / MFMA_F32_PEAK_TFLOPS})
     return res
 
@@ -217,16 +427,7 @@ def time_edge_forces(etp, g, gr, N, n_src, E, reps):
     import torch
     n = max(N, n_src)
     F = torch.empty(n, 3, device="cuda")
-    for _ in range(3):
-        etp.etp_edge_forces(g, gr, F)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        etp.etp_edge_forces(g, gr, F)
-    b.record()
-    torch.cuda.synchronize()
-    t = a.elapsed_time(b) / reps * 1e-3
+    t = time_calls(lambda: etp.etp_edge_forces(g, gr, F), reps, 3)
     byts = 12.0 * E + 4.0 * E + 4.0 * (N + 1) + 4.0 * (n_src + 1) + 12.0 * n
     return {"ms": round(t * 1e3, 4), "algo_GBps": byts / t / 1e9, "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS,
             "bound": "hbm"}
@@ -271,49 +472,28 @@ def time_neighbor_list(etp, pos_np, box, rc, reps):
 
 def time_edge_tp(etp, plan, L, C, E, Din, P, Dout, vec, w, reps):
     """Edge-local tensor product on the step's edges (outside the step): ms of
-    the forward and of the VJP (gV, gw, gr); algorithmic bytes = every input
-    and output once (fwd: vec, V, w, out; VJP: vec, V, w, G, gV, gw, gr)."""
+    the forward, the VJP (gV, gw, gr) and the VJP-of-VJP; algorithmic bytes =
+    every input and output once."""
     import torch
+
     import workloads
     V = workloads.device_normal((E, Din, C), 3, "x", 8192)
     G = workloads.device_normal((E, Dout, C), 4, "G", 8192)
     out = torch.empty(E, Dout, C, device="cuda")
     gV, gw, gr = torch.empty_like(V), torch.empty_like(w), torch.empty(E, 3, device="cuda")
+    ggV, ggw, ggv = torch.randn_like(V), torch.randn_like(w), torch.randn(E, 3, device="cuda")
+    dG = torch.empty_like(G)
     res = {}
     for name, f, byts in (
             ("fwd", lambda: etp.etp_edge_tp_fwd(plan, vec, V, w, out), 4.0 * E * (3 + Din * C + P * C + Dout * C)),
             ("vjp", lambda: etp.etp_edge_tp_vjp(plan, vec, V, w, G, gV, gw, gr),
-             4.0 * E * (6 + 2 * Din * C + 2 * P * C + Dout * C))):
-        for _ in range(2):
-            f()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            f()
-        b.record()
-        torch.cuda.synchronize()
-        t = a.elapsed_time(b) / reps * 1e-3
+             4.0 * E * (6 + 2 * Din * C + 2 * P * C + Dout * C)),
+            ("vjp2", lambda: etp.etp_edge_tp_vjp2(plan, vec, V, w, G, ggV, ggw, ggv, gV, gw, gr, dG),
+             4.0 * E * (3 + 2 * Din * C + 2 * P * C + Dout * C + 3 + Din * C + P * C + 3 + Dout * C))):
+        t = time_calls(f, reps)
         res[name + "_ms"] = round(t * 1e3, 4)
         res[name + "_algo_GBps"] = byts / t / 1e9
         res[name + "_hbm_frac"] = byts / t / 1e9 / HBM_PEAK_GBS
-    # VJP-of-VJP: reads vec, V, w, G and the three cotangents, writes dV, dw, dr, dG
-    ggV, ggw, ggv = torch.randn_like(V), torch.randn_like(w), torch.randn(E, 3, device="cuda")
-    dG = torch.empty_like(G)
-    f = lambda: etp.etp_edge_tp_vjp2(plan, vec, V, w, G, ggV, ggw, ggv, gV, gw, gr, dG)
-    byts = 4.0 * E * (3 + 2 * Din * C + 2 * P * C + Dout * C + 3 + Din * C + P * C + 3 + Dout * C)
-    for _ in range(2):
-        f()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        f()
-    b.record()
-    torch.cuda.synchronize()
-    t = a.elapsed_time(b) / reps * 1e-3
-    res.update({"vjp2_ms": round(t * 1e3, 4), "vjp2_algo_GBps": byts / t / 1e9,
-                "vjp2_hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS})
     res.update({"edges": E, "l_max": L, "channels": C, "bound": "hbm"})
     del V, G, out, gV, gw, gr, ggV, ggw, ggv, dG
     torch.cuda.empty_cache()
@@ -328,6 +508,7 @@ def time_node_product(etp, L, nu, reps, n=4096, C=128):
     differ only in l3), one FMA per CG entry, one FMA per output row of a path
     for its weight, one add per row of the running sum."""
     import torch
+
     import workloads
     plan = etp.etp_plan_create(L, C)
     tb = etp.etp_plan_tables(plan)
@@ -340,16 +521,7 @@ def time_node_product(etp, L, nu, reps, n=4096, C=128):
     A = torch.from_numpy(A_np).cuda()
     W = torch.from_numpy(W_np).cuda()
     out = torch.empty_like(A)
-    for _ in range(3):
-        etp.etp_node_product(plan, A, W, out, nu)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        etp.etp_node_product(plan, A, W, out, nu)
-    b.record()
-    torch.cuda.synchronize()
-    t = a.elapsed_time(b) / reps * 1e-3
+    t = time_calls(lambda: etp.etp_node_product(plan, A, W, out, nu), reps, 3)
     f_step = len(prods) + 2 * nnz + 2 * dout + D
     flops = float(n) * C * (nu - 1) * f_step
     byts = 4.0 * (2 * n * D * C + (nu - 1) * len(tb["paths"]) * C)
@@ -363,57 +535,93 @@ def time_node_product(etp, L, nu, reps, n=4096, C=128):
                  for p in range(len(tb["paths"])))
     G = torch.randn_like(A)
     gA = torch.empty_like(A)
-    for _ in range(2):
-        etp.etp_node_product_vjp(plan, A, W, G, gA, nu)
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(reps):
-        etp.etp_node_product_vjp(plan, A, W, G, gA, nu)
-    b.record()
-    torch.cuda.synchronize()
-    tv = a.elapsed_time(b) / reps * 1e-3
+    tv = time_calls(lambda: etp.etp_node_product_vjp(plan, A, W, G, gA, nu), reps)
     fv = float(n) * C * ((nu - 1) * (nu - 2) // 2 * f_step + (nu - 1) * (dout + 2 * nnz + 4 * groups))
     res.update({"vjp_ms": round(tv * 1e3, 4), "vjp_algo_TFLOPs": fv / tv / 1e12,
                 "vjp_valu_frac": fv / tv / 1e12 / VALU_PEAK_TFLOPS})
     return res
 
 
-def cpu_baseline(wl, budget_s=12.0):
-    """The oracle, as it is, on the first R destination rows of the graph
-    (R sized to about budget_s of host time); edges/s of fwd + VJP + VJP2."""
+def next_ops(etp, reps):
+    """The calls around the convolution (the 'next' rows), on the micro
+    workload unless named."""
+    import workloads
+    p = Problem("micro")
+    per_op, _ = p.run(3, 1, ops=("transpose", "fwd", "vjp"))
+    p.step(None, ("transpose", "fwd", "vjp"))
+    d = {"radial": time_radial(etp, p, per_op["fwd"], per_op["vjp"], reps),
+         "channel_mix": time_channel_mix(etp, p.plan, p.out, p.L, p.C, p.N, reps),
+         "edge_forces": time_edge_forces(etp, p.g, p.gr, p.N, p.n_src, p.E, reps)}
+    for name, (pos_np, box) in (("neighbor_list_water", workloads.water_positions(0)),
+                                ("neighbor_list_diamond", workloads.diamond_positions(0))):
+        d[name] = time_neighbor_list(etp, pos_np, box, 6.0, reps)
+    d["edge_tp"] = time_edge_tp(etp, p.plan, p.L, p.C, p.E, (p.L + 1) ** 2, p.P, p.wl.Dout, p.vec, p.w, reps)
+    del p
+    p3 = Problem("micro3")
+    per3, _ = p3.run(3, 1, ops=("transpose", "fwd", "vjp"))
+    p3.step(None, ("transpose", "fwd", "vjp"))
+    d["radial_micro3"] = time_radial(etp, p3, per3["fwd"], per3["vjp"], reps)
+    d["channel_mix_micro3"] = time_channel_mix(etp, p3.plan, p3.out, p3.L, p3.C, p3.N, reps)
+    del p3
+    for Lp, nu in ((3, 4), (4, 6)):
+        d[f"node_product_l{Lp}_nu{nu}"] = time_node_product(etp, Lp, nu, reps)
+    return d
+
+
+# ------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(p, budget_s=12.0):
+    """The oracle, as it is, on the first R destination rows of the headline
+    graph (R sized to about budget_s of host time), on the same inputs as the
+    GPU run (copied back from the device); edges/s of transpose + fwd + VJP +
+    VJP-of-VJP."""
     import oracle
-    L = wl.L
+    wl, L = p.wl, p.L
+    # a few hundred rows at most: repeated passes fill the budget, and the
+    # sample's per-edge arrays (copied to the host, widened to float64 by
+    # the oracle) stay small
+    rmax = min(wl.n_dst, 256)
+    emax = int(wl.row_ptr[rmax])
+    w = p.w[:emax].cpu().numpy()
+    G = p.G[:rmax].cpu().numpy()
+    ggx = p.ggx.cpu().numpy()
+    x = p.x.float().cpu().numpy()
+    if p.ggw_full is not None:
+        ggw = p.ggw_full[:emax].cpu().numpy()
+    else:
+        ch0 = p.chunks[0]
+        ggw = p.fill_ggw(0)[:min(emax, ch0["e1"] - ch0["e0"])].cpu().numpy()
+        rmax = min(rmax, ch0["r1"])
+        emax = int(wl.row_ptr[rmax])
 
     def run(R):
         rp = wl.row_ptr[:R + 1].copy()
         e1 = int(rp[-1])
-        src, vec, w = wl.src[:e1], wl.vec[:e1], wl.w[:e1]
-        G = wl.G[:R]
+        src, vec = wl.src[:e1], wl.vec[:e1]
         t0 = time.perf_counter()
         oracle.transpose(rp, src, wl.n)
-        oracle.fwd(L, rp, src, vec, wl.x, w)
-        oracle.vjp(L, rp, src, vec, wl.x, w, G)
-        oracle.vjp2(L, rp, src, vec, wl.x, w, G, wl.ggx, wl.ggw[:e1], wl.ggvec[:e1])
+        oracle.fwd(L, rp, src, vec, x, w[:e1])
+        oracle.vjp(L, rp, src, vec, x, w[:e1], G[:R])
+        oracle.vjp2(L, rp, src, vec, x, w[:e1], G[:R], ggx, ggw[:e1], wl.ggvec[:e1])
         return e1, time.perf_counter() - t0
 
     # time per edge from two probe sizes (each call also has a fixed cost:
-    # CG tables, the source-side transpose over all nodes)
-    r1, r2 = min(8, wl.n_dst), min(64, wl.n_dst)
+    # CG tables, the source-side work over all nodes)
+    r1, r2 = min(4, rmax), min(32, rmax)
     e_a, t_a = run(r1)
     e_b, t_b = run(r2)
     per_edge = max((t_b - t_a) / max(e_b - e_a, 1), 1e-9) if e_b > e_a else t_b / max(e_b, 1)
     fixed = max(t_a - per_edge * e_a, 0.0)
-    R = int(min(wl.n_dst, max(r1, (budget_s - fixed) / per_edge / max(wl.E / wl.n_dst, 1))))
+    R = int(min(rmax, max(r1, (budget_s - fixed) / per_edge / max(wl.E / wl.n_dst, 1))))
     e1, t = run(R)
-    # a sample much shorter than the budget is repeated until the budget is
-    # spent, so that the rate rests on about budget_s of host time
     passes, e_tot, t_tot = 1, e1, t
     while t_tot < 0.8 * budget_s and passes < 64:
         e_k, t_k = run(R)
         passes, e_tot, t_tot = passes + 1, e_tot + e_k, t_tot + t_k
     return {"value": e_tot / t_tot, "unit": "edges/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"first {R} destination rows ({e1} edges) of the same graph, {passes} pass(es); "
-                      f"transpose + fwd + VJP + VJP2 in float64, {t_tot:.1f} s wall"}
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "sample": f"first {R} destination rows ({e1} edges) of the {p.name} graph, {passes} pass(es); "
+                      f"transpose + fwd + VJP + VJP2 in float64 on the GPU run's inputs, {t_tot:.1f} s wall"}
 
 
 def main(argv=None):
@@ -421,7 +629,11 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="micro", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="diamond", choices=sorted(WORKLOADS))
+    ap.add_argument("--configs", default="tiny,micro,micro3,micro4,water",
+                    help="other workloads timed in the same run ('none' for none)")
+    ap.add_argument("--no-bf16", action="store_true", help="skip the bf16-feature run of the headline workload")
+    ap.add_argument("--no-next", action="store_true", help="skip the calls around the convolution")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (a kernel of known traffic "
@@ -435,112 +647,77 @@ def main(argv=None):
 
     import torch
 
-    import workloads
     from equivariant_interatomic_potentials_amd import etp
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
-    wl = workloads.get(a.workload)
-    L, C, N, E, n_src = wl.L, wl.C, wl.n_dst, wl.E, wl.n
-    cuda = lambda arr: torch.from_numpy(np.ascontiguousarray(arr)).cuda()
-    plan = etp.etp_plan_create(L, C)
-    row_ptr, src, vec, x, w, G = (cuda(wl.row_ptr), cuda(wl.src), cuda(wl.vec), cuda(wl.x), cuda(wl.w),
-                                  cuda(wl.G))
-    ggx, ggw, ggv = cuda(wl.ggx), cuda(wl.ggw), cuda(wl.ggvec)
-    src_ptr = torch.empty(n_src + 1, dtype=torch.int32, device="cuda")
-    perm = torch.empty(E, dtype=torch.int32, device="cuda")
-    perm_dst = torch.empty(E, dtype=torch.int32, device="cuda")
-    ws = torch.empty(etp.etp_csr_transpose_workspace(n_src) // 4 + 1, dtype=torch.int32, device="cuda")
-    g0 = etp.Graph(N, n_src, row_ptr, src)
-    g = etp.Graph(N, n_src, row_ptr, src, src_ptr, perm, perm_dst)
-    out = torch.empty(N, wl.Dout, C, device="cuda")
-    gx, gw, gr = torch.empty_like(x), torch.empty_like(w), torch.empty_like(vec)
-    dx, dw, dr, dG = torch.empty_like(x), torch.empty_like(w), torch.empty_like(vec), torch.empty_like(G)
-
-    ops = {
-        "transpose": lambda: etp.etp_csr_transpose(g0, src_ptr, perm, perm_dst, ws),
-        "fwd": lambda: etp.etp_edge_conv_fwd(plan, g, vec, x, w, out),
-        "vjp": lambda: etp.etp_edge_conv_vjp(plan, g, vec, x, w, G, gx, gw, gr),
-        "vjp2_dst": lambda: etp.etp_edge_conv_vjp2(plan, g, vec, x, w, G, ggx, ggw, ggv, d_grad_out=dG),
-        "vjp2_src": lambda: etp.etp_edge_conv_vjp2(plan, g, vec, x, w, G, ggx, ggw, ggv, d_x=dx, d_w=dw, d_vec=dr),
-    }
-
-    def step(events=None):
-        for i, op in enumerate(OPS):
-            if events is not None:
-                events[i][0].record()
-            ops[op]()
-            if events is not None:
-                events[i][1].record()
-
+    print(f"[bench] {a.workload}: building inputs", file=sys.stderr, flush=True)
     if a.calib_copy_mib:
         n = a.calib_copy_mib * (1 << 20) // 4
         cs, cd = torch.ones(n, device="cuda"), torch.empty(n, device="cuda")
         cd.copy_(cs)
         torch.cuda.synchronize()
         del cs, cd
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in OPS]
-           for _ in range(a.steps)]
-    torch.cuda.synchronize()
+    p = Problem(a.workload)
+    print(f"[bench] {a.workload}: E={p.E}, VJP-of-VJP in {len(p.chunks)} chunk(s); timing", file=sys.stderr,
+          flush=True)
     t0 = time.perf_counter()
-    for s in range(a.steps):
-        step(evs[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_op_ms = {op: float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(a.steps)]))
-                 for i, op in enumerate(OPS)}
-
-    by, fl = algorithmic(L, C, N, E, n_src)
-    ms_step = wall / a.steps * 1e3
-    value = E * a.steps / wall
-    op_report = {}
-    for op in OPS:
-        t = per_op_ms[op] * 1e-3
-        op_report[op] = {"ms": round(per_op_ms[op], 4), "edges_per_s": E / t,
-                         "algo_GBps": by[op] / t / 1e9, "algo_TFLOPs": fl[op] / t / 1e12,
-                         "hbm_frac": by[op] / t / 1e9 / HBM_PEAK_GBS,
-                         "valu_frac": fl[op] / t / 1e12 / VALU_PEAK_TFLOPS}
-    fwd_vjp = E / ((per_op_ms["fwd"] + per_op_ms["vjp"]) * 1e-3)
-    dom = max(("fwd", "vjp", "vjp2_dst", "vjp2_src"), key=lambda o: per_op_ms[o])
-    d = op_report[dom]
-    if d["hbm_frac"] >= d["valu_frac"]:
-        roof = {"bound": "hbm", "achieved": round(d["algo_GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(d["hbm_frac"], 4)}
-    else:
-        roof = {"bound": "alu", "achieved": round(d["algo_TFLOPs"], 2), "peak": VALU_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(d["valu_frac"], 4)}
-    tr = measured_traffic(dom)
-    roof["traffic"] = tr
-    roof["kernel"] = dom
+    per_op, ms_step = p.run(a.steps, a.warmup)
+    timed_s = time.perf_counter() - t0
+    rep, by, fl = p.report(per_op)
+    N, E = p.N, p.E
+    fwd_vjp = E / ((per_op["fwd"] + per_op["vjp"]) * 1e-3)
+    t_roof = {op: max(by[op] / (HBM_PEAK_GBS * 1e9), fl[op] / (VALU_PEAK_TFLOPS * 1e12)) for op in OPS}
+    fwd_vjp_roof = E / (t_roof["fwd"] + t_roof["vjp"])
+    dom = max(("fwd", "vjp", "vjp2"), key=lambda o: per_op[o])
+    roofline = roof(by[dom], fl[dom], per_op[dom] * 1e-3)
+    roofline.update({"traffic": measured_traffic(a.workload, dom), "op": dom,
+                     "basis": "compulsory bytes / FLOPs of the whole op (every kernel it launches), "
+                              "HIP events around each call"})
 
     line = {
-        "metric": METRIC, "value": value, "unit": "edges/s", "n_gpus": 1, "steps": a.steps,
+        "metric": METRIC, "value": fwd_vjp, "unit": "edges/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{a.workload}: {WORKLOADS[a.workload]}", "n_nodes": N, "n_edges": E,
-                   "channels": C, "l_max": L,
-                   "step": "csr_transpose + fwd + vjp + vjp2(dG) + vjp2(dx,dw,dr)"},
-        "fwd_edges_per_s": op_report["fwd"]["edges_per_s"],
+                   "channels": p.C, "l_max": p.L, "x_storage": "f32",
+                   "step": "csr_transpose + fwd + vjp + vjp2", "vjp2_chunks": len(p.chunks)},
+        "value_is": "fwd+VJP edges/s = E / (t_fwd + t_vjp)",
+        "fwd_edges_per_s": rep["fwd"]["edges_per_s"],
         "fwd_vjp_edges_per_s": fwd_vjp,
-        "ops": op_report,
-        "roofline": roof,
+        "fwd_vjp_frac": round(fwd_vjp / fwd_vjp_roof, 4),
+        "step_edges_per_s": E / (sum(per_op.values()) * 1e-3),
+        "ops": rep,
+        "roofline": roofline,
     }
-    line["next_ops"] = {"radial": time_radial(etp, plan, g, vec, x, out, G, L, C, N, E, n_src,
-                                              per_op_ms["fwd"], per_op_ms["vjp"], a.steps),
-                        "channel_mix": time_channel_mix(etp, plan, out, L, C, N, a.steps),
-                        "edge_forces": time_edge_forces(etp, g, gr, N, n_src, E, a.steps)}
-    for name, (pos_np, box) in (("neighbor_list_water", workloads.water_positions(0)),
-                                ("neighbor_list_diamond", workloads.diamond_positions(0))):
-        line["next_ops"][name] = time_neighbor_list(etp, pos_np, box, 6.0, a.steps)
-    line["next_ops"]["edge_tp"] = time_edge_tp(etp, plan, L, C, E, (L + 1) ** 2, wl.P, wl.Dout, vec, w, a.steps)
-    for Lp, nu in ((3, 4), (4, 6)):
-        line["next_ops"][f"node_product_l{Lp}_nu{nu}"] = time_node_product(etp, Lp, nu, a.steps)
+    print(f"[bench] {a.workload} f32: fwd {per_op['fwd']:.3f} ms, vjp {per_op['vjp']:.3f} ms, "
+          f"vjp2 {per_op['vjp2']:.3f} ms ({timed_s:.1f} s)", file=sys.stderr, flush=True)
+    if not a.no_bf16 and p.L >= 1:
+        pb = Problem(a.workload, bf16=True, shared=p.shared())
+        per_b, ms_b = pb.run(a.steps, a.warmup)
+        rep_b, _, _ = pb.report(per_b)
+        line["bf16_x"] = {"fwd_edges_per_s": rep_b["fwd"]["edges_per_s"],
+                          "fwd_vjp_edges_per_s": E / ((per_b["fwd"] + per_b["vjp"]) * 1e-3),
+                          "ms_per_step": ms_b, "ops": rep_b}
+        print(f"[bench] {a.workload} bf16 x: fwd {per_b['fwd']:.3f} ms, vjp {per_b['vjp']:.3f} ms, "
+              f"vjp2 {per_b['vjp2']:.3f} ms", file=sys.stderr, flush=True)
+        del pb
     if not a.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(wl)
+        print("[bench] oracle on the host", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(p)
+    shared_keys = p.shared()
+    del p, shared_keys
+    torch.cuda.empty_cache()
+    names = [] if a.configs == "none" else [c for c in a.configs.split(",") if c and c != a.workload]
+    if names:
+        line["configs"] = {}
+        for c in names:
+            print(f"[bench] config {c}", file=sys.stderr, flush=True)
+            line["configs"][c] = config_entry(c, a.steps, a.warmup)
+    if not a.no_next:
+        print("[bench] calls around the convolution", file=sys.stderr, flush=True)
+        line["next_ops"] = next_ops(etp, a.steps)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -10,8 +10,8 @@ from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
-import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -52,16 +52,28 @@ def units():
     return out
 
 
-def _newest_header():
-    hs = glob.glob(os.path.join(CSRC, "*.hpp")) + [os.path.join(ROOT, "include", "etp.h")]
-    return max(os.path.getmtime(h) for h in hs)
+_INCLUDE = re.compile(r'^\s*#\s*include\s+"([^"]+)"', re.M)
 
 
-def _stale(src, obj, hdr_time):
+def _deps(path, seen=None):
+    """The file and every quoted header it includes, recursively."""
+    seen = set() if seen is None else seen
+    path = os.path.normpath(path)
+    if path in seen or not os.path.exists(path):
+        return seen
+    seen.add(path)
+    with open(path) as f:
+        text = f.read()
+    for inc in _INCLUDE.findall(text):
+        _deps(os.path.join(os.path.dirname(path), inc), seen)
+    return seen
+
+
+def _stale(src, obj):
     if not os.path.exists(obj):
         return True
     t = os.path.getmtime(obj)
-    return t < os.path.getmtime(src) or t < hdr_time
+    return any(t < os.path.getmtime(d) for d in _deps(src))
 
 
 def _compile(job):
@@ -77,8 +89,7 @@ def _compile(job):
 
 def build(force: bool = False, jobs: int | None = None, verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    hdr = _newest_header()
-    todo = [u for u in units() if force or _stale(u[0], u[1], hdr)]
+    todo = [u for u in units() if force or _stale(u[0], u[1])]
     # biggest units first so the slowest ones start early
     todo.sort(key=lambda u: ("_L4" not in u[1], "_L3" not in u[1]))
     if jobs is None:

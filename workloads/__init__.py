@@ -236,6 +236,18 @@ def device_normal(shape, seed: int, name: str, chunk: int, scale: float = 1.0):
     return t
 
 
+def device_normal_(t, seed: int, name: str, chunk: int, scale: float = 1.0):
+    """Fill the float32 device tensor t in place with N(0, scale^2) values from
+    torch's generator seeded as in device_normal (no new allocation: for
+    per-chunk arrays redrawn inside a timing loop)."""
+    import torch
+    key = np.random.SeedSequence([seed, STREAMS.index(name), chunk]).generate_state(1, np.uint64)[0]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(int(key) & ((1 << 63) - 1))
+    t.normal_(0.0, scale, generator=g)
+    return t
+
+
 def random_vectors(E: int, lo: float, hi: float, seed: int) -> np.ndarray:
     d = rng(seed, "dirs").standard_normal((E, 3))
     d /= np.linalg.norm(d, axis=1, keepdims=True)
