@@ -66,6 +66,9 @@ hipError_t launch_forces(int n_dst, int n_src, const int *row_ptr, const int *sr
 size_t transpose_workspace_bytes(int n_src);
 hipError_t launch_transpose(int n_dst, int n_src, int64_t E, const int *row_ptr, const int *src, int *src_ptr,
                             int *perm, int *perm_dst, void *ws, hipStream_t stream);
+int transpose_noalloc_max_sources();
+hipError_t launch_transpose_noalloc(int n_dst, int n_src, int64_t E, const int *row_ptr, const int *src,
+                                    int *src_ptr, int *perm, int *perm_dst, hipStream_t stream);
 size_t neighbor_workspace_bytes(int n, const float *box, float rc);
 hipError_t launch_neighbor_count(int n, const float *pos, const float *box, float rc, int *row_ptr, void *ws,
                                  hipStream_t stream);
@@ -362,6 +365,21 @@ etp_status etp_csr_transpose(const etp_graph *g, int32_t *src_ptr, int32_t *perm
         return ETP_ERR_WORKSPACE;
     return hip_status(etp::launch_transpose(g->n_dst, g->n_src, g->n_edges, g->row_ptr, g->src, src_ptr, perm,
                                             perm_dst, ws, static_cast<hipStream_t>(stream)));
+}
+
+etp_status etp_csr_transpose_noalloc(const etp_graph *g, int32_t *src_ptr, int32_t *perm, int32_t *perm_dst,
+                                     void *stream)
+{
+    etp_status st = check_graph(g, false);
+    if (st != ETP_OK)
+        return st;
+    if (!src_ptr || (g->n_edges > 0 && (!perm || !perm_dst)))
+        return ETP_ERR_INVALID_ARGUMENT;
+    static_assert(ETP_NOALLOC_MAX_SOURCES == (1 << 20), "the header's bound differs from the library's");
+    if (g->n_src > etp::transpose_noalloc_max_sources())
+        return ETP_ERR_WORKSPACE;
+    return hip_status(etp::launch_transpose_noalloc(g->n_dst, g->n_src, g->n_edges, g->row_ptr, g->src, src_ptr,
+                                                    perm, perm_dst, static_cast<hipStream_t>(stream)));
 }
 
 etp_status etp_sh(etp_plan_t plan, int64_t n_edges, const float *vec, float *Y, float *dY, void *stream)

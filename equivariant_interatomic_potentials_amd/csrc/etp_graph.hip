@@ -22,6 +22,7 @@
 
 #include <climits>
 #include <cstdint>
+#include <mutex>
 
 namespace etp {
 
@@ -303,6 +304,60 @@ hipError_t launch_transpose(int n_dst, int n_src, int64_t E, const int *row_ptr,
                            perm_dst);
     }
     return hipGetLastError();
+}
+
+// ---------------------------------------------------- no-allocation variant
+// The transpose's workspace (the per-source cursors and the scan's tile
+// totals) for callers that cannot allocate: a file-scope device array of
+// fixed size, one copy per GPU, shared by every call on that GPU. The
+// transpose writes every word it reads from it within the same call, so its
+// contents need no clearing between calls; calls that overlap on one GPU
+// race on it.
+constexpr int kNoAllocSources = 1 << 20;
+constexpr size_t kNoAllocInts =
+    static_cast<size_t>(kNoAllocSources) + (kNoAllocSources + kScanTile - 1) / kScanTile + 64;
+static __device__ __align__(256) int scratch[kNoAllocInts];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int *g_scratch[kMaxDevices];  // the device address of scratch, per device (set once)
+}  // namespace
+
+// The current device's copy of scratch, looked up once per device (in host
+// code the array's name is not a device address).
+static hipError_t scratch_of_current_device(int **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        g_scratch[dev] = static_cast<int *>(p);
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+
+int transpose_noalloc_max_sources() { return kNoAllocSources; }
+
+hipError_t launch_transpose_noalloc(int n_dst, int n_src, int64_t E, const int *row_ptr, const int *src,
+                                    int *src_ptr, int *perm, int *perm_dst, hipStream_t stream)
+{
+    if (n_src < 0 || n_src > kNoAllocSources || transpose_workspace_bytes(n_src) > sizeof(int) * kNoAllocInts)
+        return hipErrorInvalidValue;
+    int *ws = nullptr;
+    const hipError_t e = scratch_of_current_device(&ws);
+    if (e != hipSuccess)
+        return e;
+    return launch_transpose(n_dst, n_src, E, row_ptr, src, src_ptr, perm, perm_dst, ws, stream);
 }
 
 hipError_t launch_validate(int n_dst, int n_src, int64_t E, const int *row_ptr, const int *src, int *bad,

@@ -34,7 +34,7 @@ ABI_SYMBOLS = ("etp_plan_create", "etp_plan_destroy", "etp_plan_info", "etp_plan
                "etp_edge_conv_vjp", "etp_edge_conv_vjp2", "etp_channel_mix", "etp_edge_forces",
                "etp_neighbor_workspace", "etp_neighbor_count", "etp_neighbor_fill", "etp_node_product", "etp_node_product_vjp", "etp_channel_mix_vjp",
                "etp_edge_tp_fwd", "etp_edge_tp_vjp", "etp_edge_tp_vjp2",
-               "etp_status_string", "etp_version")
+               "etp_csr_transpose_noalloc", "etp_status_string", "etp_version")
 
 
 class EtpError(RuntimeError):
@@ -95,6 +95,7 @@ def _load():
         "etp_plan_tables": (st, [vp, vp, vp, vp, vp, vp]),
         "etp_csr_transpose_workspace": (st, [i32, ctypes.POINTER(ctypes.c_size_t)]),
         "etp_csr_transpose": (st, [ctypes.POINTER(etp_graph), vp, vp, vp, vp, ctypes.c_size_t, vp]),
+        "etp_csr_transpose_noalloc": (st, [ctypes.POINTER(etp_graph), vp, vp, vp, vp]),
         "etp_workspace_size": (st, [vp, i32, ctypes.POINTER(etp_graph), ctypes.POINTER(ctypes.c_size_t)]),
         "etp_sh": (st, [vp, i64, vp, vp, vp, vp]),
         "etp_edge_conv_fwd": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, u32, vp]),
@@ -275,6 +276,19 @@ def etp_csr_transpose(graph: Graph, src_ptr, perm, perm_dst, ws, stream=None):
                                  _ptr(perm_dst, "perm_dst", torch.int32, graph.n_edges, optional=True),
                                  _ptr(ws, "ws", optional=True), ws.numel() * ws.element_size() if ws is not None else 0,
                                  _stream(stream)), "etp_csr_transpose")
+
+
+ETP_NOALLOC_MAX_SOURCES = 1 << 20
+
+
+def etp_csr_transpose_noalloc(graph: Graph, src_ptr, perm, perm_dst, stream=None):
+    """etp_csr_transpose with the library's fixed device workspace (allocates nothing)."""
+    import torch
+    g = graph.struct()
+    _check(lib.etp_csr_transpose_noalloc(ctypes.byref(g), _ptr(src_ptr, "src_ptr", torch.int32, graph.n_src + 1),
+                                         _ptr(perm, "perm", torch.int32, graph.n_edges, optional=True),
+                                         _ptr(perm_dst, "perm_dst", torch.int32, graph.n_edges, optional=True),
+                                         _stream(stream)), "etp_csr_transpose_noalloc")
 
 
 def etp_sh(plan: Plan, vec, Y, dY=None, stream=None):

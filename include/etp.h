@@ -166,6 +166,23 @@ ETP_API etp_status etp_csr_transpose_workspace(int32_t n_src, size_t *bytes);
 ETP_API etp_status etp_csr_transpose(const etp_graph *g, int32_t *src_ptr, int32_t *perm, int32_t *perm_dst, void *ws,
                              size_t ws_bytes, void *stream);
 
+/* etp_csr_transpose for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same transpose with the same result, its workspace taken
+ * from a fixed device array inside the library (one per GPU, held until the
+ * process ends, sized for n_src <= ETP_NOALLOC_MAX_SOURCES: 4 MiB) instead of
+ * a caller buffer. It allocates nothing and calls no allocating routine; the
+ * first call on a device looks up that device's copy of the array, with that
+ * device current (the stream must belong to the current device). Every call
+ * on a GPU shares its array: calls that overlap on one GPU (other streams,
+ * other host threads) race and must be ordered by the caller. Arguments as
+ * etp_csr_transpose. Errors: INVALID_ARGUMENT (as etp_csr_transpose),
+ * WORKSPACE (n_src above ETP_NOALLOC_MAX_SOURCES; nothing is launched),
+ * UNSUPPORTED (n_edges >= 2^31), HIP. */
+#define ETP_NOALLOC_MAX_SOURCES (1 << 20)
+ETP_API etp_status etp_csr_transpose_noalloc(const etp_graph *g, int32_t *src_ptr, int32_t *perm, int32_t *perm_dst,
+                                             void *stream);
+
 /* Device workspace (bytes) that an operation needs on graph g: ETP_OP_FWD,
  * ETP_OP_VJP and ETP_OP_VJP2 need none (0: the convolution keeps its
  * intermediates in registers and LDS and takes no workspace argument);

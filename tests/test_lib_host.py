@@ -32,7 +32,7 @@ def header_symbols():
 
 def test_header_symbols_exported():
     names = header_symbols()
-    assert len(names) == 26
+    assert len(names) == 27
     assert sorted(etp.ABI_SYMBOLS) == names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (etp_\w+)$", out, flags=re.M))
@@ -231,3 +231,21 @@ def test_call_validation_without_device():
     assert lib.etp_workspace_size(None, 0, ctypes.byref(g6), ctypes.byref(wsb)) == INV
     assert lib.etp_workspace_size(plan.handle, 0, ctypes.byref(g2), ctypes.byref(wsb)) == UNS
     assert lib.etp_csr_transpose_workspace(-1, ctypes.byref(b)) == INV
+
+
+def test_noalloc_transpose_rejects_sizes_beyond_its_workspace():
+    """The no-allocation transpose refuses n_src above its fixed workspace
+    with ETP_ERR_WORKSPACE, and bad pointers with INVALID_ARGUMENT, before
+    touching a device."""
+    fake = 0x1000  # never dereferenced: the call returns before any launch
+    g = etp.etp_graph()
+    g.n_dst, g.n_src, g.n_edges = 0, etp.ETP_NOALLOC_MAX_SOURCES + 1, 0
+    st = etp.lib.etp_csr_transpose_noalloc(ctypes.byref(g), fake, None, None, None)
+    assert st == etp.ETP_ERR_WORKSPACE
+    g.n_src = 4
+    assert etp.lib.etp_csr_transpose_noalloc(ctypes.byref(g), None, None, None, None) == etp.ETP_ERR_INVALID_ARGUMENT
+    g.n_dst, g.n_edges = 2, 5
+    g.row_ptr, g.src = fake, fake
+    assert etp.lib.etp_csr_transpose_noalloc(ctypes.byref(g), fake, None, None, None) == etp.ETP_ERR_INVALID_ARGUMENT
+    g.n_edges = 1 << 31
+    assert etp.lib.etp_csr_transpose_noalloc(ctypes.byref(g), fake, fake, fake, None) == etp.ETP_ERR_UNSUPPORTED
