@@ -314,6 +314,30 @@ def vjp_radial(L, row_ptr, src, vec, x, h, Wr, G):
     return gx, gh, gr[:E], gWr
 
 
+def vjp2_radial(L, row_ptr, src, vec, x, h, Wr, G, Xp=None, Hp=None, Rp=None):
+    """VJP of vjp_radial's (gx, gh, gr) with cotangents (X', H', R') on them:
+    S = <X', gx> + <H', gh> + <R', gr>. Since gh = gw Wr (per edge, summed
+    over paths and channels), <H', gh> = <W', gw> with W'[e, p, u] =
+    sum_k H'[e, k] Wr[k, p, u], so the convolution's VJP-of-VJP with (X', W',
+    R') gives (dx, dw, dr, dG); then, through w = h Wr, dh[e, k] =
+    sum_{p,u} dw[e, p, u] Wr[k, p, u], and dWr[k, p, u] = sum_e h[e, k]
+    dw[e, p, u] + sum_e H'[e, k] gw[e, p, u] (S also depends on Wr through
+    gh). Returns (dx, dh[E, K], dr, dG, dWr[K, P, C]); None cotangent = 0."""
+    h = np.asarray(h, np.float64)
+    Wr = np.asarray(Wr, np.float64)
+    E = h.shape[0]
+    w = radial_weights(h, Wr)
+    Wp = radial_weights(Hp, Wr) if Hp is not None else None
+    dx, dw, dr, dG = vjp2(L, row_ptr, src, vec, x, w, G, Xp, Wp, Rp)
+    dw = dw[:E]
+    dh = np.einsum("epu,kpu->ek", dw, Wr)
+    dWr = np.einsum("ek,epu->kpu", h, dw)
+    if Hp is not None:
+        gw = vjp(L, row_ptr, src, vec, x, w, G)[1][:E]
+        dWr = dWr + np.einsum("ek,epu->kpu", np.asarray(Hp, np.float64), gw)
+    return dx, dh, dr[:E], dG, dWr
+
+
 def edge_tp_fwd(L, vec, V, w):
     """Edge-local tensor product: the convolution with every edge its own
     destination and source (out[E, Dout, C], no destination sum)."""

@@ -88,3 +88,63 @@ def test_weight_gradients_single_basis():
         assert abs(gh[e, 0] - float((gw[e] * Wr[0]).sum())) < 1e-12
     want = sum(h[e, 0] * gw[e] for e in range(wl.E))
     np.testing.assert_allclose(gWr[0], want, atol=1e-12)
+
+
+@pytest.mark.parametrize("L,K,cot", [(1, 3, ("x", "h", "r")), (2, 5, ("x", "h", "r")), (2, 2, ("h",)),
+                                     (3, 2, ("x", "r"))])
+def test_vjp2_radial_finite_differences(L, K, cot):
+    """The radial VJP-of-VJP against central differences of
+    S = <X', gx> + <H', gh> + <R', gr> (gx, gh, gr from the oracle's radial
+    VJP, itself pinned by differences of the forward) in x, h, vec, G and Wr."""
+    wl, h, Wr = case(L, 2, K, 40 + L + K)
+    g = np.random.default_rng(50 + L + K)
+    D = oracle.dims(L)
+    G = g.standard_normal((wl.n_dst, D["Dout"], 2))
+    Xp = g.standard_normal(wl.x.shape) if "x" in cot else None
+    Hp = g.standard_normal(h.shape) if "h" in cot else None
+    Rp = g.standard_normal((wl.E, 3)) if "r" in cot else None
+    dx, dh, dr, dG, dWr = oracle.vjp2_radial(L, wl.row_ptr, wl.src, wl.vec, wl.x, h, Wr, G, Xp, Hp, Rp)
+    x0, vec0 = wl.x.astype(np.float64), wl.vec.astype(np.float64)
+
+    def S(x=x0, hh=h, vec=vec0, GG=G, ww=Wr):
+        gx, gh, gr, _ = oracle.vjp_radial(L, wl.row_ptr, wl.src, vec, x, hh, ww, GG)
+        t = 0.0
+        if Xp is not None:
+            t += (Xp * gx).sum()
+        if Hp is not None:
+            t += (Hp * gh).sum()
+        if Rp is not None:
+            t += (Rp * gr).sum()
+        return t
+
+    eps = 1e-6
+    for name, arr, grad, kw in (("x", x0, dx, "x"), ("h", h, dh, "hh"), ("vec", vec0, dr, "vec"),
+                                ("G", G, dG, "GG"), ("Wr", Wr, dWr, "ww")):
+        for t in range(4):
+            idx = tuple(int(g.integers(sz)) for sz in arr.shape)
+            a1, a2 = arr.copy(), arr.copy()
+            a1[idx] += eps
+            a2[idx] -= eps
+            fd = (S(**{kw: a1}) - S(**{kw: a2})) / (2 * eps)
+            assert abs(fd - grad[idx]) < 2e-6 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+
+
+def test_vjp2_radial_single_basis_is_plain_vjp2():
+    """With one basis function and h = 1 the radial VJP-of-VJP is the plain
+    one with w = Wr[0] and W' = H' Wr[0], and dh = sum over paths and
+    channels of dw Wr[0]."""
+    L, C = 2, 3
+    wl, _, Wr = case(L, C, 1, 61)
+    g = np.random.default_rng(62)
+    h = np.ones((wl.E, 1))
+    G = g.standard_normal((wl.n_dst, oracle.dims(L)["Dout"], C))
+    Hp = g.standard_normal((wl.E, 1))
+    Rp = g.standard_normal((wl.E, 3))
+    dx, dh, dr, dG, _ = oracle.vjp2_radial(L, wl.row_ptr, wl.src, wl.vec, wl.x, h, Wr, G, wl.ggx, Hp, Rp)
+    w = np.broadcast_to(Wr[0], (wl.E,) + Wr.shape[1:])
+    Wp = Hp[:, :, None] * Wr[0][None]
+    rdx, rdw, rdr, rdG = oracle.vjp2(L, wl.row_ptr, wl.src, wl.vec, wl.x, w, G, wl.ggx, Wp, Rp)
+    np.testing.assert_allclose(dx, rdx, atol=1e-12)
+    np.testing.assert_allclose(dr, rdr, atol=1e-12)
+    np.testing.assert_allclose(dG, rdG, atol=1e-12)
+    np.testing.assert_allclose(dh[:, 0], (rdw * Wr[0][None]).sum(axis=(1, 2)), atol=1e-12)
