@@ -167,7 +167,7 @@ class Problem:
     cotangents that do not fit beside w, gw and dw are drawn per chunk of
     destination rows (outside the timed ops)."""
 
-    def __init__(self, name, bf16=False, shared=None):
+    def __init__(self, name, bf16=False, shared=None, bwd="auto"):
         import torch
 
         import workloads
@@ -175,6 +175,11 @@ class Problem:
         self.etp, self.torch = etp, torch
         self.name = name
         self.bf16 = bf16
+        # the backward: "auto" = the workspace entry points with the library's
+        # choice of formulation per shape; "dst" forces the walk over each
+        # destination's in-edges (node gradient through a per-edge workspace);
+        # "src" = the entry points without workspace (each source's out-edges)
+        self.bwd = bwd
         wl = shared["wl"] if shared else workloads.get(name)
         self.wl = wl
         L, C, N, E, n_src, P = wl.L, wl.C, wl.n_dst, wl.E, wl.n, wl.P
@@ -183,7 +188,7 @@ class Problem:
         cuda = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
         if shared:
             for k in ("row_ptr", "src", "vec", "ggv", "w", "G", "ggx", "x32", "src_ptr", "perm", "perm_dst", "tws",
-                      "chunks", "out", "gx", "gr", "dx", "dr", "dG", "gw", "ggw_full", "ggw_buf"):
+                      "chunks", "out", "gx", "gr", "dx", "dr", "dG", "gw", "ggw_full", "ggw_buf", "bws"):
                 setattr(self, k, shared[k])
         else:
             self.row_ptr, self.src, self.vec = cuda(wl.row_ptr), cuda(wl.src), cuda(wl.vec)
@@ -205,6 +210,9 @@ class Problem:
             # gw (VJP output) and dw (VJP-of-VJP output) share one buffer: a
             # step writes gw, then dw over it
             self.gw = torch.empty(E, P, C, device="cuda")
+            # the destination-side backward's workspace (one Din-row block per
+            # edge), allocated for both formulations so that either can run
+            self.bws = torch.empty(E * wl.Din * C, device="cuda")
             self._plan_chunks()
         self.x = self.x32.to(torch.bfloat16) if bf16 else self.x32
         self.g0 = etp.Graph(N, n_src, self.row_ptr, self.src)
@@ -213,7 +221,7 @@ class Problem:
     def shared(self):
         return {k: getattr(self, k) for k in (
             "wl", "row_ptr", "src", "vec", "ggv", "w", "G", "ggx", "x32", "src_ptr", "perm", "perm_dst", "tws",
-            "chunks", "out", "gx", "gr", "dx", "dr", "dG", "gw", "ggw_full", "ggw_buf")}
+            "chunks", "out", "gx", "gr", "dx", "dr", "dG", "gw", "ggw_full", "ggw_buf", "bws")}
 
     def _plan_chunks(self):
         """Destination-row chunks for the VJP-of-VJP: one when its per-edge
@@ -283,22 +291,33 @@ class Problem:
                                                              self.tws))
         if "fwd" in ops:
             timed("fwd", lambda: etp.etp_edge_conv_fwd(plan, g, self.vec, self.x, self.w, self.out))
+        dst = self.bwd != "src"
+        force = etp.ETP_FLAG_DST_PASS if self.bwd == "dst" else 0
         if "vjp" in ops:
-            timed("vjp", lambda: etp.etp_edge_conv_vjp(plan, g, self.vec, self.x, self.w, self.G, self.gx,
-                                                       self.gw, self.gr))
+            if dst:
+                timed("vjp", lambda: etp.etp_edge_conv_vjp_ws(plan, g, self.vec, self.x, self.w, self.G, self.gx,
+                                                              self.gw, self.gr, self.bws, force))
+            else:
+                timed("vjp", lambda: etp.etp_edge_conv_vjp(plan, g, self.vec, self.x, self.w, self.G, self.gx,
+                                                           self.gw, self.gr))
         if "vjp2" in ops:
+            def vjp2(gr_, vec, w, G, ggw, ggv, dw, dr, dG, acc):
+                if dst:
+                    etp.etp_edge_conv_vjp2_ws(plan, gr_, vec, self.x, w, G, self.ggx, ggw, ggv, self.dx, dw, dr, dG,
+                                              self.bws, acc | force)
+                else:
+                    etp.etp_edge_conv_vjp2(plan, gr_, vec, self.x, w, G, self.ggx, ggw, ggv, self.dx, dw, dr, dG,
+                                           acc)
             if len(self.chunks) == 1:
-                timed("vjp2", lambda: etp.etp_edge_conv_vjp2(plan, g, self.vec, self.x, self.w, self.G, self.ggx,
-                                                             self.ggw_full, self.ggv, self.dx, self.gw, self.dr,
-                                                             self.dG))
+                timed("vjp2", lambda: vjp2(g, self.vec, self.w, self.G, self.ggw_full, self.ggv, self.gw, self.dr,
+                                           self.dG, 0))
             else:
                 for c, ch in enumerate(self.chunks):
                     ggw = self.fill_ggw(c)
                     r0, r1, e0, e1 = ch["r0"], ch["r1"], ch["e0"], ch["e1"]
                     acc = etp.ETP_FLAG_ACCUMULATE if c else 0
-                    timed("vjp2", lambda: etp.etp_edge_conv_vjp2(
-                        plan, ch["g"], self.vec[e0:e1], self.x, self.w[e0:e1], self.G[r0:r1], self.ggx, ggw,
-                        self.ggv[e0:e1], self.dx, self.gw[e0:e1], self.dr[e0:e1], self.dG[r0:r1], acc))
+                    timed("vjp2", lambda: vjp2(ch["g"], self.vec[e0:e1], self.w[e0:e1], self.G[r0:r1], ggw,
+                                               self.ggv[e0:e1], self.gw[e0:e1], self.dr[e0:e1], self.dG[r0:r1], acc))
 
     def run(self, steps, warmup, ops=OPS):
         """warmup untimed steps, then `steps` timed ones; per-op mean ms over
@@ -336,16 +355,30 @@ class Problem:
         return rep, by, fl
 
 
-def config_entry(name, steps, warmup):
-    """A non-headline workload: fwd, fwd+VJP and per-op figures."""
+def other_bwd(p, steps, warmup):
+    """The VJP and VJP-of-VJP in each forced formulation (destination side,
+    source side), on the same buffers: ms, edges/s and roofline fraction."""
+    out = {}
+    for b in ("dst", "src"):
+        alt = Problem(p.name, bf16=p.bf16, shared=p.shared(), bwd=b)
+        per, _ = alt.run(steps, warmup, ops=("vjp", "vjp2"))
+        rep, _, _ = alt.report(per)
+        out[b] = {op: {k: rep[op][k] for k in ("ms", "edges_per_s", "bound", "frac")} for op in rep}
+    return out
+
+
+def config_entry(name, steps, warmup, bwd):
+    """A non-headline workload: fwd, fwd+VJP and per-op figures (and the
+    other backward formulation beside them)."""
     import torch
-    p = Problem(name)
+    p = Problem(name, bwd=bwd)
     per_op, ms_step = p.run(steps, warmup)
     rep, _, _ = p.report(per_op)
     fwd_vjp = p.E / ((per_op["fwd"] + per_op["vjp"]) * 1e-3)
     d = {"workload": WORKLOADS[name], "n_nodes": p.N, "n_edges": p.E, "channels": p.C, "l_max": p.L,
          "ms_per_step": round(ms_step, 4), "fwd_edges_per_s": rep["fwd"]["edges_per_s"],
-         "fwd_vjp_edges_per_s": fwd_vjp, "vjp2_chunks": len(p.chunks), "ops": rep}
+         "fwd_vjp_edges_per_s": fwd_vjp, "vjp2_chunks": len(p.chunks), "bwd": p.bwd, "ops": rep,
+         "other_bwd": other_bwd(p, steps, warmup)}
     del p
     torch.cuda.empty_cache()
     return d
@@ -635,6 +668,11 @@ def main(argv=None):
     ap.add_argument("--no-bf16", action="store_true", help="skip the bf16-feature run of the headline workload")
     ap.add_argument("--no-next", action="store_true", help="skip the calls around the convolution")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--bwd", default="auto", choices=("auto", "dst", "src"),
+                    help="backward of the step: the workspace entry points with the library's choice per shape "
+                         "(auto) or forced to walk each destination's in-edges (dst), or the entry points without "
+                         "workspace (src); both forced formulations are timed beside it")
+    ap.add_argument("--no-other-bwd", action="store_true", help="skip timing the forced backward formulations")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (a kernel of known traffic "
                          "for scaling hardware byte counters)")
@@ -659,7 +697,7 @@ def main(argv=None):
         cd.copy_(cs)
         torch.cuda.synchronize()
         del cs, cd
-    p = Problem(a.workload)
+    p = Problem(a.workload, bwd=a.bwd)
     print(f"[bench] {a.workload}: E={p.E}, VJP-of-VJP in {len(p.chunks)} chunk(s); timing", file=sys.stderr,
           flush=True)
     t0 = time.perf_counter()
@@ -682,7 +720,7 @@ def main(argv=None):
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{a.workload}: {WORKLOADS[a.workload]}", "n_nodes": N, "n_edges": E,
                    "channels": p.C, "l_max": p.L, "x_storage": "f32",
-                   "step": "csr_transpose + fwd + vjp + vjp2", "vjp2_chunks": len(p.chunks)},
+                   "step": "csr_transpose + fwd + vjp + vjp2", "vjp2_chunks": len(p.chunks), "bwd": p.bwd},
         "value_is": "fwd+VJP edges/s = E / (t_fwd + t_vjp)",
         "fwd_edges_per_s": rep["fwd"]["edges_per_s"],
         "fwd_vjp_edges_per_s": fwd_vjp,
@@ -693,8 +731,13 @@ def main(argv=None):
     }
     print(f"[bench] {a.workload} f32: fwd {per_op['fwd']:.3f} ms, vjp {per_op['vjp']:.3f} ms, "
           f"vjp2 {per_op['vjp2']:.3f} ms ({timed_s:.1f} s)", file=sys.stderr, flush=True)
+    if not a.no_other_bwd:
+        line["other_bwd"] = other_bwd(p, a.steps, a.warmup)
+        for b, o in line["other_bwd"].items():
+            print(f"[bench] {a.workload} backward forced {b}: vjp {o['vjp']['ms']:.3f} ms, "
+                  f"vjp2 {o['vjp2']['ms']:.3f} ms", file=sys.stderr, flush=True)
     if not a.no_bf16 and p.L >= 1:
-        pb = Problem(a.workload, bf16=True, shared=p.shared())
+        pb = Problem(a.workload, bf16=True, shared=p.shared(), bwd=a.bwd)
         per_b, ms_b = pb.run(a.steps, a.warmup)
         rep_b, _, _ = pb.report(per_b)
         line["bf16_x"] = {"fwd_edges_per_s": rep_b["fwd"]["edges_per_s"],
@@ -714,7 +757,7 @@ def main(argv=None):
         line["configs"] = {}
         for c in names:
             print(f"[bench] config {c}", file=sys.stderr, flush=True)
-            line["configs"][c] = config_entry(c, a.steps, a.warmup)
+            line["configs"][c] = config_entry(c, a.steps, a.warmup, a.bwd)
     if not a.no_next:
         print("[bench] calls around the convolution", file=sys.stderr, flush=True)
         line["next_ops"] = next_ops(etp, a.steps)

@@ -42,10 +42,10 @@ def units():
     for L in range(5):
         out.append((os.path.join(CSRC, "etp_edge_tp.hip"), os.path.join(BUILD, f"etp_edge_tp_L{L}.o"),
                     [f"-DETP_L={L}"]))
-    for name in ("etp_dst", "etp_src"):
+    for name, modes in (("etp_dst", (0, 1, 2, 3)), ("etp_src", (0, 1, 2, 3)), ("etp_bwd", (0, 1))):
         for L in range(5):
             for xt in (0, 1):
-                for mode in (0, 1, 2):
+                for mode in modes:
                     out.append((os.path.join(CSRC, name + ".hip"),
                                 os.path.join(BUILD, f"{name}_L{L}_X{xt}_M{mode}.o"),
                                 [f"-DETP_L={L}", f"-DETP_XT={xt}", f"-DETP_MODE={mode}"]))

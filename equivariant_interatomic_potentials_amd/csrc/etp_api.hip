@@ -77,6 +77,13 @@ hipError_t launch_neighbor_fill(int n, const float *pos, const float *box, float
 hipError_t launch_validate(int n_dst, int n_src, int64_t E, const int *row_ptr, const int *src, int *bad,
                            hipStream_t stream);
 
+// the destination-side backward, one translation unit per (l_max, dtype, mode)
+#define ETP_DECLARE_BWD(L, XT, MODE) \
+    hipError_t ETP_RUN_NAME(bwd, L, XT, MODE)(const ConvArgs &a, float *part, int64_t n_edges);
+#define ETP_DECLARE_BWD_L(L) \
+    ETP_DECLARE_BWD(L, 0, 0) ETP_DECLARE_BWD(L, 0, 1) ETP_DECLARE_BWD(L, 1, 0) ETP_DECLARE_BWD(L, 1, 1)
+ETP_DECLARE_BWD_L(0) ETP_DECLARE_BWD_L(1) ETP_DECLARE_BWD_L(2) ETP_DECLARE_BWD_L(3) ETP_DECLARE_BWD_L(4)
+
 const Table *table_for(int L)
 {
     switch (L) {
@@ -195,6 +202,21 @@ hipError_t run_src_radial(int L, bool bf16, const etp::ConvArgs &a)
     }
 }
 
+// the radial VJP-of-VJP: dG (destination pass) and dx / dh / dr (source pass)
+hipError_t run_radial2(bool dst, int L, bool bf16, const etp::ConvArgs &a)
+{
+#define ETP_RADIAL2_CASE(L)                                                                          \
+    case L:                                                                                          \
+        if (dst)                                                                                     \
+            return bf16 ? etp::ETP_RUN_NAME(dst, L, 1, 3)(a) : etp::ETP_RUN_NAME(dst, L, 0, 3)(a);   \
+        return bf16 ? etp::ETP_RUN_NAME(src, L, 1, 3)(a) : etp::ETP_RUN_NAME(src, L, 0, 3)(a);
+    switch (L) {
+        ETP_RADIAL2_CASE(0) ETP_RADIAL2_CASE(1) ETP_RADIAL2_CASE(2) ETP_RADIAL2_CASE(3) ETP_RADIAL2_CASE(4)
+    default: return hipErrorInvalidValue;
+    }
+#undef ETP_RADIAL2_CASE
+}
+
 hipError_t run_src(int L, bool bf16, int mode, const etp::ConvArgs &a)
 {
     switch (L * 4 + (bf16 ? 2 : 0) + mode) {
@@ -203,6 +225,43 @@ hipError_t run_src(int L, bool bf16, int mode, const etp::ConvArgs &a)
         ETP_RUN_CASES(src, 4, 0) ETP_RUN_CASES(src, 4, 1)
     default: return hipErrorInvalidValue;
     }
+}
+
+#define ETP_BWD_CASES(L, XT)                                                                 \
+    case (L * 4 + XT * 2 + 0): return etp::ETP_RUN_NAME(bwd, L, XT, 0)(a, part, n_edges);     \
+    case (L * 4 + XT * 2 + 1): return etp::ETP_RUN_NAME(bwd, L, XT, 1)(a, part, n_edges);
+
+hipError_t run_bwd(int L, bool bf16, int mode, const etp::ConvArgs &a, float *part, int64_t n_edges)
+{
+    switch (L * 4 + (bf16 ? 2 : 0) + mode) {
+        ETP_BWD_CASES(0, 0) ETP_BWD_CASES(0, 1) ETP_BWD_CASES(1, 0) ETP_BWD_CASES(1, 1) ETP_BWD_CASES(2, 0)
+        ETP_BWD_CASES(2, 1) ETP_BWD_CASES(3, 0) ETP_BWD_CASES(3, 1) ETP_BWD_CASES(4, 0) ETP_BWD_CASES(4, 1)
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Which formulation the workspace entry points use when the caller does not
+// force one: the destination-side pass (G rows held per node, node gradient
+// through the workspace) where it measured faster on MI355X -- l_max = 3,
+// and the l_max = 2 VJP with more than 64 channels -- the source-side pass
+// elsewhere (at l_max = 4 the destination side's path groups are too small
+// to pay for their repeated edge walks; at l_max <= 2 the source side's G
+// rows are few).
+bool bwd_uses_dst(int L, int C, bool vjp2, uint32_t flags)
+{
+    if (flags & ETP_FLAG_DST_PASS)
+        return true;
+    if (flags & ETP_FLAG_SRC_PASS)
+        return false;
+    if (vjp2)
+        return L == 3;
+    return L == 3 || (L == 2 && C > 64);
+}
+
+// Workspace of the destination-side backward: one Din-row block per edge.
+size_t bwd_workspace_bytes(const etp_plan_s *plan, int64_t n_edges)
+{
+    return static_cast<size_t>(n_edges) * plan->T->din_rows * plan->C * sizeof(float);
 }
 
 // box: three finite sides, each at least twice the finite, positive cutoff
@@ -276,7 +335,26 @@ etp_status etp_plan_destroy(etp_plan_t plan)
     return ETP_OK;
 }
 
-etp_status etp_plan_info(etp_plan_t plan, etp_plan_info_t *info)
+etp_status etp_plan_info(etp_plan_t plan, int32_t *n_paths, int64_t *din, int64_t *dsh, int64_t *dout,
+                         int32_t *nnz)
+{
+    if (!plan)
+        return ETP_ERR_INVALID_ARGUMENT;
+    const etp::Table &T = *plan->T;
+    if (n_paths)
+        *n_paths = T.P;
+    if (din)
+        *din = static_cast<int64_t>(plan->C) * T.din_rows;
+    if (dsh)
+        *dsh = T.dsh;
+    if (dout)
+        *dout = static_cast<int64_t>(plan->C) * T.dout_rows;
+    if (nnz)
+        *nnz = T.nnz;
+    return ETP_OK;
+}
+
+etp_status etp_plan_describe(etp_plan_t plan, etp_plan_info_t *info)
 {
     if (!plan || !info)
         return ETP_ERR_INVALID_ARGUMENT;
@@ -347,6 +425,10 @@ etp_status etp_workspace_size(etp_plan_t plan, int32_t op, const etp_graph *g, s
         return ETP_OK;
     case ETP_OP_TRANSPOSE:
         *bytes = etp::transpose_workspace_bytes(g->n_src);
+        return ETP_OK;
+    case ETP_OP_VJP_WS:
+    case ETP_OP_VJP2_WS:
+        *bytes = bwd_workspace_bytes(plan, g->n_edges);
         return ETP_OK;
     default:
         return ETP_ERR_INVALID_ARGUMENT;
@@ -514,6 +596,128 @@ etp_status etp_edge_conv_vjp(etp_plan_t plan, const etp_graph *g, const float *v
     return hip_status(run_src(plan->L, plan->dtype == ETP_BF16, etp::SRC_VJP, a));
 }
 
+etp_status etp_edge_conv_vjp_ws(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x, const float *w,
+                                const float *grad_out, float *grad_x, float *grad_w, float *grad_vec, uint32_t flags,
+                                void *ws, size_t ws_bytes, void *stream)
+{
+    if (!plan)
+        return ETP_ERR_INVALID_ARGUMENT;
+    etp_status st = check_graph(g, grad_x != nullptr);
+    if (st != ETP_OK)
+        return st;
+    if (plan->C > 256)
+        return ETP_ERR_UNSUPPORTED;
+    if ((flags & ~15u) || (flags & 12u) == 12u)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (!grad_x && !grad_w && !grad_vec)
+        return ETP_OK;
+    if (g->n_edges > 0 && (!vec || !x || !w || !grad_out))
+        return ETP_ERR_INVALID_ARGUMENT;
+    const bool dst = bwd_uses_dst(plan->L, plan->C, false, flags);
+    if (!dst && grad_x && g->n_src > 0 && (!g->src_ptr || (g->n_edges > 0 && (!g->perm || !g->perm_dst))))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (dst && grad_x && g->n_edges > 0 &&
+        (!ws || ws_bytes < bwd_workspace_bytes(plan, g->n_edges) || (reinterpret_cast<uintptr_t>(ws) & 15u)))
+        return ETP_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (flags & ETP_FLAG_VALIDATE) {
+        st = validate_graph(g, s);
+        if (st != ETP_OK)
+            return st;
+    }
+    etp::ConvArgs a{};
+    a.C = plan->C;
+    a.n_dst = g->n_dst;
+    a.n_src = g->n_src;
+    a.row_ptr = g->row_ptr;
+    a.src = g->src;
+    a.src_ptr = g->src_ptr;
+    a.perm = g->perm;
+    a.perm_dst = g->perm_dst;
+    a.vec = vec;
+    a.x = x;
+    a.w = w;
+    a.G = grad_out;
+    a.ox = grad_x;
+    a.ow = grad_w;
+    a.ovec = grad_vec;
+    a.flags = flags & ETP_FLAG_ACCUMULATE;
+    a.stream = s;
+    if (!dst)
+        return hip_status(run_src(plan->L, plan->dtype == ETP_BF16, etp::SRC_VJP, a));
+    // (with no edges the kernels still write the zero node rows and read no workspace)
+    return hip_status(
+        run_bwd(plan->L, plan->dtype == ETP_BF16, 0, a, grad_x ? static_cast<float *>(ws) : nullptr, g->n_edges));
+}
+
+etp_status etp_edge_conv_vjp2_ws(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x, const float *w,
+                                 const float *grad_out, const float *gg_x, const float *gg_w, const float *gg_vec,
+                                 float *d_x, float *d_w, float *d_vec, float *d_grad_out, uint32_t flags, void *ws,
+                                 size_t ws_bytes, void *stream)
+{
+    if (!plan)
+        return ETP_ERR_INVALID_ARGUMENT;
+    etp_status st = check_graph(g, d_x != nullptr);
+    if (st != ETP_OK)
+        return st;
+    if (plan->C > 256)
+        return ETP_ERR_UNSUPPORTED;
+    if ((flags & ~15u) || (flags & 12u) == 12u)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (!d_x && !d_w && !d_vec && !d_grad_out)
+        return ETP_OK;
+    if (g->n_edges > 0 && (!vec || !x || !w))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if ((d_x || d_w || d_vec) && g->n_edges > 0 && !grad_out)
+        return ETP_ERR_INVALID_ARGUMENT;
+    const bool dst = bwd_uses_dst(plan->L, plan->C, true, flags);
+    if (!dst && (d_x || d_w || d_vec) && g->n_src > 0 &&
+        (!g->src_ptr || (g->n_edges > 0 && (!g->perm || !g->perm_dst))))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (dst && d_x && g->n_edges > 0 &&
+        (!ws || ws_bytes < bwd_workspace_bytes(plan, g->n_edges) || (reinterpret_cast<uintptr_t>(ws) & 15u)))
+        return ETP_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (flags & ETP_FLAG_VALIDATE) {
+        st = validate_graph(g, s);
+        if (st != ETP_OK)
+            return st;
+    }
+    etp::ConvArgs a{};
+    a.C = plan->C;
+    a.n_dst = g->n_dst;
+    a.n_src = g->n_src;
+    a.row_ptr = g->row_ptr;
+    a.src = g->src;
+    a.src_ptr = g->src_ptr;
+    a.perm = g->perm;
+    a.perm_dst = g->perm_dst;
+    a.vec = vec;
+    a.x = x;
+    a.w = w;
+    a.G = grad_out;
+    a.ggx = gg_x;
+    a.ggw = gg_w;
+    a.ggvec = gg_vec;
+    a.out = d_grad_out;
+    a.ox = d_x;
+    a.ow = d_w;
+    a.ovec = d_vec;
+    a.flags = flags & ETP_FLAG_ACCUMULATE;
+    a.stream = s;
+    const bool bf16 = plan->dtype == ETP_BF16;
+    if (d_grad_out) {  // dG: the destination pass (needs no G)
+        st = hip_status(run_dst(plan->L, bf16, etp::DST_DG, a));
+        if (st != ETP_OK)
+            return st;
+    }
+    if (!d_x && !d_w && !d_vec)
+        return ETP_OK;
+    if (!dst)
+        return hip_status(run_src(plan->L, bf16, etp::SRC_VJP2, a));
+    return hip_status(run_bwd(plan->L, bf16, 1, a, d_x ? static_cast<float *>(ws) : nullptr, g->n_edges));
+}
+
 etp_status etp_edge_conv_vjp_radial(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x,
                                     const float *h, int32_t n_basis, const float *Wr, const float *grad_out,
                                     float *grad_x, float *grad_h, float *grad_vec, uint32_t flags, void *stream)
@@ -562,6 +766,69 @@ etp_status etp_edge_conv_vjp_radial(etp_plan_t plan, const etp_graph *g, const f
     a.flags = flags & ETP_FLAG_ACCUMULATE;
     a.stream = s;
     return hip_status(run_src_radial(plan->L, plan->dtype == ETP_BF16, a));
+}
+
+etp_status etp_edge_conv_vjp2_radial(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x,
+                                     const float *h, int32_t n_basis, const float *Wr, const float *grad_out,
+                                     const float *gg_x, const float *gg_h, const float *gg_vec, float *d_x, float *d_h,
+                                     float *d_vec, float *d_grad_out, uint32_t flags, void *stream)
+{
+    if (!plan)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (n_basis < 1 || n_basis > ETP_MAX_RADIAL_BASIS)
+        return ETP_ERR_UNSUPPORTED;
+    etp_status st = check_graph(g, true);
+    if (st != ETP_OK)
+        return st;
+    if (plan->C > 256)
+        return ETP_ERR_UNSUPPORTED;
+    if (flags & ~3u)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (!d_x && !d_h && !d_vec && !d_grad_out)
+        return ETP_OK;
+    if (g->n_edges > 0 && (!vec || !x || !h || !Wr))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if ((d_x || d_h || d_vec) && g->n_edges > 0 && !grad_out)
+        return ETP_ERR_INVALID_ARGUMENT;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (flags & ETP_FLAG_VALIDATE) {
+        st = validate_graph(g, s);
+        if (st != ETP_OK)
+            return st;
+    }
+    etp::ConvArgs a{};
+    a.C = plan->C;
+    a.n_dst = g->n_dst;
+    a.n_src = g->n_src;
+    a.row_ptr = g->row_ptr;
+    a.src = g->src;
+    a.src_ptr = g->src_ptr;
+    a.perm = g->perm;
+    a.perm_dst = g->perm_dst;
+    a.vec = vec;
+    a.x = x;
+    a.h = h;
+    a.wr = Wr;
+    a.nbasis = n_basis;
+    a.G = grad_out;
+    a.ggx = gg_x;
+    a.ggh = gg_h;
+    a.ggvec = gg_vec;
+    a.out = d_grad_out;
+    a.ox = d_x;
+    a.oh = d_h;
+    a.ovec = d_vec;
+    a.flags = flags & ETP_FLAG_ACCUMULATE;
+    a.stream = s;
+    const bool bf16 = plan->dtype == ETP_BF16;
+    if (d_grad_out) {
+        st = hip_status(run_radial2(true, plan->L, bf16, a));
+        if (st != ETP_OK)
+            return st;
+    }
+    if (d_x || d_h || d_vec)
+        return hip_status(run_radial2(false, plan->L, bf16, a));
+    return ETP_OK;
 }
 
 etp_status etp_edge_conv_vjp2(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x, const float *w,

@@ -22,15 +22,16 @@ struct ConvArgs {
     const float *w, *G, *ggx, *ggw, *ggvec;
     float *out, *ox, *ow, *ovec;
     const float *h, *wr;  // radial features [E][nbasis] and last-layer matrix [nbasis][P][C]
-    float *oh;            // radial VJP: grad_h [E][nbasis]
+    const float *ggh;     // radial VJP-of-VJP: cotangent on grad_h [E][nbasis]
+    float *oh;            // radial VJP: grad_h [E][nbasis] (VJP-of-VJP: d_h)
     int nbasis;
     uint32_t flags;
     hipStream_t stream;
 };
 
-enum { DST_FWD = 0, DST_DG = 1, DST_FWD_RADIAL = 2 };
+enum { DST_FWD = 0, DST_DG = 1, DST_FWD_RADIAL = 2, DST_DG_RADIAL = 3 };
 constexpr int kRadialMax = 8;  // radial basis functions per edge (padded to this in LDS)
-enum { SRC_VJP = 0, SRC_VJP2 = 1, SRC_VJP_RADIAL = 2 };
+enum { SRC_VJP = 0, SRC_VJP2 = 1, SRC_VJP_RADIAL = 2, SRC_VJP2_RADIAL = 3 };
 
 // Each kernel source is compiled once per (l_max, x dtype, mode) with
 // -DETP_L, -DETP_XT (0 = f32, 1 = bf16) and -DETP_MODE, so the translation
@@ -42,10 +43,12 @@ enum { SRC_VJP = 0, SRC_VJP2 = 1, SRC_VJP_RADIAL = 2 };
 #define ETP_DECLARE_RUN(kind, L, XT, MODE) hipError_t ETP_RUN_NAME(kind, L, XT, MODE)(const ConvArgs &a);
 #define ETP_DECLARE_RUN_L(kind, L) \
     ETP_DECLARE_RUN(kind, L, 0, 0) ETP_DECLARE_RUN(kind, L, 0, 1) ETP_DECLARE_RUN(kind, L, 1, 0) ETP_DECLARE_RUN(kind, L, 1, 1)
-#define ETP_DECLARE_RUN_RADIAL(L) ETP_DECLARE_RUN(dst, L, 0, 2) ETP_DECLARE_RUN(dst, L, 1, 2)
+#define ETP_DECLARE_RUN_RADIAL(L) \
+    ETP_DECLARE_RUN(dst, L, 0, 2) ETP_DECLARE_RUN(dst, L, 1, 2) ETP_DECLARE_RUN(dst, L, 0, 3) ETP_DECLARE_RUN(dst, L, 1, 3)
 ETP_DECLARE_RUN_RADIAL(0) ETP_DECLARE_RUN_RADIAL(1) ETP_DECLARE_RUN_RADIAL(2) ETP_DECLARE_RUN_RADIAL(3)
 ETP_DECLARE_RUN_RADIAL(4)
-#define ETP_DECLARE_RUN_SRC_RADIAL(L) ETP_DECLARE_RUN(src, L, 0, 2) ETP_DECLARE_RUN(src, L, 1, 2)
+#define ETP_DECLARE_RUN_SRC_RADIAL(L) \
+    ETP_DECLARE_RUN(src, L, 0, 2) ETP_DECLARE_RUN(src, L, 1, 2) ETP_DECLARE_RUN(src, L, 0, 3) ETP_DECLARE_RUN(src, L, 1, 3)
 ETP_DECLARE_RUN_SRC_RADIAL(0) ETP_DECLARE_RUN_SRC_RADIAL(1) ETP_DECLARE_RUN_SRC_RADIAL(2)
 ETP_DECLARE_RUN_SRC_RADIAL(3) ETP_DECLARE_RUN_SRC_RADIAL(4)
 ETP_DECLARE_RUN_L(dst, 0) ETP_DECLARE_RUN_L(dst, 1) ETP_DECLARE_RUN_L(dst, 2) ETP_DECLARE_RUN_L(dst, 3) ETP_DECLARE_RUN_L(dst, 4)

@@ -30,12 +30,14 @@
 //     cached; each path's w row (and each l1 block's x rows) is reloaded
 //     with the next edge's as soon as its last use in the current edge is
 //     done, one edge of look-ahead in one register set;
-//   * radial mode (forward only): instead of a w stream, each path's weight
-//     is formed in registers as w[e, p, u] = sum_k h[e, k] Wr[k, p, u] (the
-//     last layer of a radial network) at the path's first use: the lane's
-//     Wr entries of the group's paths stay in registers for the whole
-//     workgroup, and the edge's h row is written to LDS with its SH and read
-//     back once per edge (a broadcast).
+//   * radial modes (forward, and the dG term of the radial VJP-of-VJP):
+//     instead of a w stream, each path's weight is formed in registers as
+//     w[e, p, u] = sum_k h[e, k] Wr[k, p, u] (the last layer of a radial
+//     network) at the path's first use, and for dG also W' = sum_k H'[e, k]
+//     Wr[k, p, u] from the cotangent H' on grad_h: the lane's Wr entries of
+//     the group's paths stay in registers for the whole workgroup, and the
+//     edge's h (and H') row is written to LDS with its SH and read back once
+//     per edge (a broadcast).
 #include "etp_conv_common.hpp"
 
 namespace etp {
@@ -81,17 +83,20 @@ template <int L, int CPL, int MODE>
 struct DstCfg {
     static constexpr int S = ETP_DST_S;
     static constexpr int B = L <= 2 ? ETP_DST_B2 : (L == 3 ? 16 : 8);
-    static constexpr int ROWS = MODE == DST_FWD_RADIAL ? (L <= 2 ? ETP_DST_ROWS_FWD : ETP_DST_ROWS_RAD)
+    static constexpr int ROWS = MODE == DST_DG_RADIAL ? ETP_DST_ROWS_RAD
+                              : MODE == DST_FWD_RADIAL ? (L <= 2 ? ETP_DST_ROWS_FWD : ETP_DST_ROWS_RAD)
                               : MODE == DST_FWD ? (L <= 2 ? ETP_DST_ROWS_FWD : L == 3 ? ETP_DST_ROWS_FWD3 : ETP_DST_ROWS_FWD4)
                                                 : (L <= 2 ? ETP_DST_ROWS_DG : L == 3 ? ETP_DST_ROWS_DG3 : ETP_DST_ROWS_DG4);
     // (the dG pass with one channel per lane keeps 40-row groups at l <= 3:
     // one 51-row group at l = 2, C = 64 is 19% slower than two)
     static constexpr int MAXROWS =
         (MODE == DST_DG && CPL == 1 && L <= 3) ? ETP_DST_ROWS_DG1 : (ROWS + CPL - 1) / CPL;
-    static constexpr int TCOPIES = MODE == DST_DG ? 2 : 1;  // T (and Td) per edge
+    static constexpr int TCOPIES = (MODE == DST_DG || MODE == DST_DG_RADIAL) ? 2 : 1;  // T (and Td) per edge
+    static constexpr int HROWS = MODE == DST_DG_RADIAL ? 2 : MODE == DST_FWD_RADIAL ? 1 : 0;  // h (, H') per edge
     // waves per SIMD the registers must allow: 3 at l=3 (169 VGPRs otherwise);
     // 2 in the radial mode, whose Wr entries take 8 registers per path
-    static constexpr int WPE = ETP_DST_WPE > 0 ? ETP_DST_WPE : MODE == DST_FWD_RADIAL ? 2 : (L == 3 ? 3 : 1);
+    static constexpr int WPE = ETP_DST_WPE > 0 ? ETP_DST_WPE
+                             : (MODE == DST_FWD_RADIAL || MODE == DST_DG_RADIAL) ? 2 : (L == 3 ? 3 : 1);
 };
 
 template <int L, int CPL, typename XT, int MODE, int G>
@@ -102,12 +107,14 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
                                           const float *__restrict__ ggw, const float *__restrict__ ggvec,
                                           float *__restrict__ out, const uint32_t flags, float *lds,
                                           const float *__restrict__ hrad, const float *__restrict__ wrad,
-                                          const int nbasis)
+                                          const int nbasis, const float *__restrict__ ggh)
 {
     using V = chv_t<CPL>;
     using Cfg = DstCfg<L, CPL, MODE>;
     constexpr int S = Cfg::S, B = Cfg::B, TC = Cfg::TCOPIES;
-    constexpr bool DG = MODE == DST_DG, RAD = MODE == DST_FWD_RADIAL;
+    constexpr bool DG = MODE == DST_DG || MODE == DST_DG_RADIAL;
+    constexpr bool RAD = MODE == DST_FWD_RADIAL || MODE == DST_DG_RADIAL;
+    constexpr int HROWS = Cfg::HROWS;
     constexpr int RK = kRadialMax;
     constexpr Groups GR = make_groups(kTab<L>, Cfg::MAXROWS);
     constexpr GroupInfo GI = group_info(kTab<L>, GR, G);
@@ -127,17 +134,19 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
     const uint32_t off4 = active ? static_cast<uint32_t>(u0) * 4u : kOOB;
     const uint32_t offx = active ? static_cast<uint32_t>(u0) * static_cast<uint32_t>(sizeof(XT)) : kOOB;
     const uint32_t rowb = static_cast<uint32_t>(C) * 4u, rowx = static_cast<uint32_t>(C) * sizeof(XT);
-    const bool has_xp = DG && ggx != nullptr, has_wp = DG && ggw != nullptr, has_rp = DG && ggvec != nullptr;
+    const bool has_xp = DG && ggx != nullptr, has_rp = DG && ggvec != nullptr;
+    // W' comes from memory, or in the radial mode from the edge's H' row
+    const bool has_wp = DG && (RAD ? ggh != nullptr : ggw != nullptr);
 
     const int rb = row_ptr[node], re = row_ptr[node + 1];
     const int len = re - rb;
     const int e_begin = rb + static_cast<int>((static_cast<int64_t>(len) * wv) / S);
     const int e_end = rb + static_cast<int>((static_cast<int64_t>(len) * (wv + 1)) / S);
     float *tl = lds + wv * (TC * B * STRIDE);  // T[B][STRIDE] (then Td[B][STRIDE])
-    // radial mode: after the T slices, per wave the batch's h rows [B][RK]
-    // (zero past nbasis); the lane's Wr[k, p, u] of the group's paths in
-    // registers (zero past nbasis and C)
-    float *hl = lds + S * TC * B * max_stride(kTab<L>, GR) + wv * (B * RK);
+    // radial modes: after the T slices, per wave the batch's h (and H') rows
+    // [B][HROWS * RK] (zero past nbasis); the lane's Wr[k, p, u] of the
+    // group's paths in registers (zero past nbasis and C)
+    float *hl = lds + S * TC * B * max_stride(kTab<L>, GR) + wv * (B * HROWS * RK);
     float wr[RAD ? NP : 1][RK];
     if constexpr (RAD) {
         static_assert(CPL == 1, "the radial mode keeps one channel per lane");
@@ -168,7 +177,8 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
         r.w = make_rsrc(RAD ? nullptr : w + static_cast<int64_t>(e) * (P * C), (!RAD && valid) ? P * C * 4u : 0u);
         r.x = make_rsrc(x + static_cast<int64_t>(j) * (DIN * C), valid ? DIN * C * static_cast<uint32_t>(sizeof(XT)) : 0u);
         // a missing cotangent is a zero-length block: its loads read 0
-        r.wp = make_rsrc(has_wp ? ggw + static_cast<int64_t>(e) * (P * C) : nullptr, has_wp && valid ? P * C * 4u : 0u);
+        r.wp = make_rsrc((has_wp && !RAD) ? ggw + static_cast<int64_t>(e) * (P * C) : nullptr,
+                         (has_wp && !RAD && valid) ? P * C * 4u : 0u);
         r.xp = make_rsrc(has_xp ? ggx + static_cast<int64_t>(j) * (DIN * C) : nullptr, has_xp && valid ? DIN * C * 4u : 0u);
         return r;
     };
@@ -176,7 +186,7 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
     auto load_w = [&](auto q, const EdgeRsrc &r) {  // q: path index within the group
         if constexpr (!RAD)  // (the radial mode forms w at the path's first use)
             o.w[q] = bload<V, kNT>(r.w, off4, (GI.p0 + q) * rowb);
-        if constexpr (DG)
+        if constexpr (DG && !RAD)
             o.wp[q] = bload<V, kNT>(r.wp, off4, (GI.p0 + q) * rowb);
     };
     auto load_x = [&](auto q, const EdgeRsrc &r) {  // q: x row within the group
@@ -217,6 +227,12 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
                 });
                 write_T<L, GI.pr0, GI.npr, STRIDE>(Y, tl + lane * STRIDE);
                 write_T<L, GI.pr0, GI.npr, STRIDE>(Yd, tl + B * STRIDE + lane * STRIDE);
+                if constexpr (RAD)
+                    static_range<0, RK>([&](auto k) {
+                        hl[lane * (2 * RK) + k] = k < nbasis ? hrad[static_cast<int64_t>(e) * nbasis + k] : 0.f;
+                        hl[lane * (2 * RK) + RK + k] =
+                            (has_wp && k < nbasis) ? ggh[static_cast<int64_t>(e) * nbasis + k] : 0.f;
+                    });
             }
         }
         wave_sync_lds();
@@ -229,10 +245,14 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
     auto compute = [&](const float *tk, const float *hk, const EdgeRsrc &nx) {
         float4 tq = make_float4(0.f, 0.f, 0.f, 0.f), tdq = tq;
         V xw[9], y[9], xx[DG ? 9 : 1];
-        float4 h0, h1;
+        float4 h0, h1, hp0, hp1;
         if constexpr (RAD) {
             h0 = *reinterpret_cast<const float4 *>(hk);
             h1 = *reinterpret_cast<const float4 *>(hk + 4);
+            if constexpr (DG) {
+                hp0 = *reinterpret_cast<const float4 *>(hk + RK);
+                hp1 = *reinterpret_cast<const float4 *>(hk + RK + 4);
+            }
         }
         static_range<GI.pr0, GI.pr1>([&](auto q) {
             constexpr Pair pr = kTab<L>.pair[q];
@@ -250,6 +270,16 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
                 t = fmaf(h1.y, wr[WQ][5], t);
                 t = fmaf(h1.z, wr[WQ][6], t);
                 o.w[WQ] = fmaf(h1.w, wr[WQ][7], t);
+                if constexpr (DG) {  // W'[e, p, u] = sum_k H'[e, k] Wr[k, p, u], k in order
+                    float v = hp0.x * wr[WQ][0];
+                    v = fmaf(hp0.y, wr[WQ][1], v);
+                    v = fmaf(hp0.z, wr[WQ][2], v);
+                    v = fmaf(hp0.w, wr[WQ][3], v);
+                    v = fmaf(hp1.x, wr[WQ][4], v);
+                    v = fmaf(hp1.y, wr[WQ][5], v);
+                    v = fmaf(hp1.z, wr[WQ][6], v);
+                    o.wp[WQ] = fmaf(hp1.w, wr[WQ][7], v);
+                }
             }
             if constexpr (XW && q == pa.pr0) {
                 static_range<0, d1>([&](auto k) {
@@ -298,7 +328,7 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
             load_all(edge_rsrc(e, true));
         }
         const bool more = kb + 1 < nb;
-        compute(tl + kb * STRIDE, hl + kb * RK, edge_rsrc(more ? e + 1 : e, more));
+        compute(tl + kb * STRIDE, hl + kb * (HROWS * RK), edge_rsrc(more ? e + 1 : e, more));
         kb = (kb + 1 == nb) ? 0 : kb + 1;
     }
 
@@ -323,7 +353,8 @@ __global__ void __launch_bounds__((64 * DstCfg<L, CPL, MODE>::S)) __attribute__(
                const int *__restrict__ src, const float *__restrict__ vec, const XT *__restrict__ x,
                const float *__restrict__ w, const float *__restrict__ ggx, const float *__restrict__ ggw,
                const float *__restrict__ ggvec, float *__restrict__ out, const uint32_t flags,
-               const float *__restrict__ hrad, const float *__restrict__ wrad, const int nbasis)
+               const float *__restrict__ hrad, const float *__restrict__ wrad, const int nbasis,
+               const float *__restrict__ ggh)
 {
     extern __shared__ float lds[];
     constexpr Groups GR = make_groups(kTab<L>, DstCfg<L, CPL, MODE>::MAXROWS);
@@ -331,7 +362,7 @@ __global__ void __launch_bounds__((64 * DstCfg<L, CPL, MODE>::S)) __attribute__(
     static_range<0, GR.n>([&](auto G) __attribute__((always_inline)) {
         if (g == G)
             dst_group<L, CPL, XT, MODE, G>(n_dst, C, nchunk, row_ptr, src, vec, x, w, ggx, ggw, ggvec, out, flags,
-                                           lds, hrad, wrad, nbasis);
+                                           lds, hrad, wrad, nbasis, ggh);
     });
 }
 
@@ -341,7 +372,7 @@ static hipError_t launch_dst_t(const ConvArgs &a)
     using Cfg = DstCfg<L, CPL, MODE>;
     constexpr Groups GR = make_groups(kTab<L>, Cfg::MAXROWS);
     constexpr int LDS_FLOATS = Cfg::S * Cfg::TCOPIES * Cfg::B * max_stride(kTab<L>, GR) +
-                               (MODE == DST_FWD_RADIAL ? Cfg::S * Cfg::B * kRadialMax : 0);
+                               Cfg::S * Cfg::B * Cfg::HROWS * kRadialMax;
     const int nchunk = (a.C + 64 * CPL - 1) / (64 * CPL);
     const int64_t nblk = static_cast<int64_t>(a.n_dst) * nchunk;
     if (nblk == 0)
@@ -351,12 +382,12 @@ static hipError_t launch_dst_t(const ConvArgs &a)
     dim3 grid(static_cast<unsigned>(nblk), GR.n), block(64 * Cfg::S);
     hipLaunchKernelGGL((dst_kernel<L, CPL, XT, MODE>), grid, block, LDS_FLOATS * sizeof(float), a.stream, a.n_dst,
                        a.C, nchunk, a.row_ptr, a.src, a.vec, static_cast<const XT *>(a.x), a.w, a.ggx, a.ggw,
-                       a.ggvec, a.out, a.flags, a.h, a.wr, a.nbasis);
+                       a.ggvec, a.out, a.flags, a.h, a.wr, a.nbasis, a.ggh);
     return hipGetLastError();
 }
 
 #if !defined(ETP_L) || !defined(ETP_XT) || !defined(ETP_MODE)
-#error "compile this file once per (l_max, dtype, mode) with -DETP_L=0..4 -DETP_XT=0|1 -DETP_MODE=0|1|2"
+#error "compile this file once per (l_max, dtype, mode) with -DETP_L=0..4 -DETP_XT=0|1 -DETP_MODE=0..3"
 #endif
 
 hipError_t ETP_RUN_NAME(dst, ETP_L, ETP_XT, ETP_MODE)(const ConvArgs &a)
@@ -368,7 +399,8 @@ hipError_t ETP_RUN_NAME(dst, ETP_L, ETP_XT, ETP_MODE)(const ConvArgs &a)
 #define ETP_DST_CPL1 0
 #endif
     // (and the radial mode: its Wr slice in LDS doubles with the channels)
-    constexpr bool ONE = (ETP_MODE == DST_DG && ETP_L >= 4) || ETP_MODE == DST_FWD_RADIAL || ETP_DST_CPL1;
+    constexpr bool ONE = (ETP_MODE == DST_DG && ETP_L >= 4) || ETP_MODE == DST_FWD_RADIAL || ETP_MODE == DST_DG_RADIAL ||
+                         ETP_DST_CPL1;
     if constexpr (ONE)
         return launch_dst_t<ETP_L, 1, XT, ETP_MODE>(a);
     else

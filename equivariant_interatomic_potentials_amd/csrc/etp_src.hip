@@ -39,7 +39,10 @@
 //     also stores each edge's h row, w is formed at each path's start, and
 //     instead of storing gw each lane accumulates gh[k] += gw Wr[k, p, u];
 //     the 8 gh sums take the same fixed-order route as gr (wave sum, parked
-//     per chunk, chunks in order, later path groups adding to earlier ones).
+//     per chunk, chunks in order, later path groups adding to earlier ones);
+//   * radial VJP-of-VJP: the same with the cotangent H' on gh as the
+//     cotangent W' = H' Wr on gw (formed like w from the edge's H' row), and
+//     dw contracted into dh[k] += dw Wr[k, p, u] the way gw becomes gh.
 #include "etp_conv_common.hpp"
 
 namespace etp {
@@ -78,6 +81,9 @@ namespace etp {
 #ifndef ETP_SRC_COST_RAD
 #define ETP_SRC_COST_RAD 150
 #endif
+#ifndef ETP_SRC_COST_RAD2
+#define ETP_SRC_COST_RAD2 120
+#endif
 #ifndef ETP_SRC_WPE
 #define ETP_SRC_WPE 0
 #endif
@@ -86,17 +92,18 @@ namespace etp {
 #endif
 template <int L, int MODE>
 struct SrcCfg {
-    static constexpr bool RAD = MODE == SRC_VJP_RADIAL;
-    static constexpr int NV = MODE == SRC_VJP2 ? 2 : 1;             // Y (, Yd) and Z (, Z2) copies
+    static constexpr bool RAD = MODE == SRC_VJP_RADIAL || MODE == SRC_VJP2_RADIAL;
+    static constexpr bool V2 = MODE == SRC_VJP2 || MODE == SRC_VJP2_RADIAL;
+    static constexpr int NV = V2 ? 2 : 1;                           // Y (, Yd) and Z (, Z2) copies
     static constexpr int DSH = (L + 1) * (L + 1), DSHP = (DSH + 3) & ~3;
     static constexpr int GQ = 4 * NV * DSH;                         // gr coefficients, a float4 per (b, copy)
-    static constexpr int HR = RAD ? kRadialMax : 0;                 // the edge's h row (radial mode)
+    static constexpr int HR = RAD ? (V2 ? 2 : 1) * kRadialMax : 0;  // the edge's h (and H') row (radial modes)
     static constexpr int ES = NV * DSHP + GQ + HR;                  // floats per edge in the batch
     static constexpr int PK = RAD ? 12 : 4;                         // parked sums per edge: gr (, gh), padded
     static constexpr int ESP = ES + 2 * PK;                         // + two park slots
     // at two waves per SIMD (VJP2, radial) a wave may take twice the LDS:
     // longer batches keep more of the prologue's lanes busy (l=3 VJP2: 5%)
-    static constexpr int LDS_BATCH = (RAD || MODE == SRC_VJP2) ? 2 * ETP_SRC_LDS_BATCH : ETP_SRC_LDS_BATCH;
+    static constexpr int LDS_BATCH = (RAD || V2) ? 2 * ETP_SRC_LDS_BATCH : ETP_SRC_LDS_BATCH;
     static constexpr int B = [] {
         int b = 64;
         while (b > 8 && b * ESP * 4 > LDS_BATCH)
@@ -105,13 +112,14 @@ struct SrcCfg {
     }();
     // registers per path beyond its G rows: the w row (and W'), or in the
     // radial mode the 8 Wr entries
-    static constexpr int WMUL = RAD ? kRadialMax : (MODE == SRC_VJP2 ? 2 : 1);
-    static constexpr int MAXCOST = RAD ? (L <= 2 ? ETP_SRC_COST_RAD : L == 3 ? 130 : 100)
-                                   : MODE == SRC_VJP2 ? (L <= 2 ? ETP_SRC_COST_VJP2 : L == 3 ? ETP_SRC_COST_VJP2_3
-                                                                                         : ETP_SRC_COST_VJP2_4)
+    static constexpr int WMUL = RAD ? kRadialMax : (V2 ? 2 : 1);
+    static constexpr int MAXCOST = RAD ? (V2 ? (L <= 2 ? ETP_SRC_COST_RAD2 : L == 3 ? 100 : 80)
+                                             : (L <= 2 ? ETP_SRC_COST_RAD : L == 3 ? 130 : 100))
+                                   : V2 ? (L <= 2 ? ETP_SRC_COST_VJP2 : L == 3 ? ETP_SRC_COST_VJP2_3
+                                                                             : ETP_SRC_COST_VJP2_4)
                                                       : (L <= 2 ? ETP_SRC_COST_VJP : L == 3 ? ETP_SRC_COST_VJP_3
                                                                                          : ETP_SRC_COST_VJP_4);
-    static constexpr int WPE = ETP_SRC_WPE > 0 ? ETP_SRC_WPE : (RAD || MODE == SRC_VJP2) ? 2 : (L == 3 ? 3 : 4);
+    static constexpr int WPE = ETP_SRC_WPE > 0 ? ETP_SRC_WPE : (RAD || V2) ? 2 : (L == 3 ? 3 : 4);
 };
 
 // Edge splits per channel chunk: four waves per workgroup in total.
@@ -138,11 +146,11 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                                           float *__restrict__ ow, float *__restrict__ ovec,
                                           const uint32_t flags, float *lds, const float *__restrict__ hrad,
                                           const float *__restrict__ wrad, const int nbasis,
-                                          float *__restrict__ oh)
+                                          float *__restrict__ oh, const float *__restrict__ ggh)
 {
     using Cfg = SrcCfg<L, MODE>;
     constexpr int B = Cfg::B, ES = Cfg::ES, NV = Cfg::NV, DSHP = Cfg::DSHP, PK = Cfg::PK;
-    constexpr bool V2 = MODE == SRC_VJP2, RAD = Cfg::RAD;
+    constexpr bool V2 = Cfg::V2, RAD = Cfg::RAD;
     constexpr int RK = kRadialMax, HO = NV * DSHP + Cfg::GQ;  // h row offset in an edge's batch slot
     constexpr Groups GR = make_src_groups(kTab<L>, Cfg::MAXCOST, Cfg::WMUL);
     constexpr SrcGroupInfo GI = src_group_info(kTab<L>, GR, SG);
@@ -161,7 +169,9 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
     const uint32_t off4 = active ? static_cast<uint32_t>(u) * 4u : kOOB;
     const uint32_t offx = active ? static_cast<uint32_t>(u) * static_cast<uint32_t>(sizeof(XT)) : kOOB;
     const bool want_vec = ovec != nullptr, want_h = RAD && oh != nullptr;
-    const bool has_xp = V2 && ggx != nullptr, has_wp = V2 && ggw != nullptr, has_rp = V2 && ggvec != nullptr;
+    const bool has_xp = V2 && ggx != nullptr, has_rp = V2 && ggvec != nullptr;
+    // W' comes from memory, or in the radial mode from the edge's H' row
+    const bool has_wp = V2 && (RAD ? ggh != nullptr : ggw != nullptr);
     const uint32_t rowb = static_cast<uint32_t>(C) * 4u;
 
     // LDS: per wave the batch [B][ES] and two park slots [2][B][PK]
@@ -218,8 +228,8 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
         EdgeRsrc r;
         r.w = make_rsrc(RAD ? nullptr : w + static_cast<int64_t>(e) * (P * C), (!RAD && valid) ? P * C * 4u : 0u);
         r.g = make_rsrc(G + static_cast<int64_t>(i) * (DOUT * C), valid ? DOUT * C * 4u : 0u);
-        r.wp = make_rsrc(has_wp ? ggw + static_cast<int64_t>(e) * (P * C) : nullptr,
-                         has_wp && valid ? P * C * 4u : 0u);
+        r.wp = make_rsrc((has_wp && !RAD) ? ggw + static_cast<int64_t>(e) * (P * C) : nullptr,
+                         (has_wp && !RAD && valid) ? P * C * 4u : 0u);
         return r;
     };
     Ops o;
@@ -228,7 +238,7 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
         constexpr int GO = pa.out_row - GI.gr0, WQ = p - GI.p0;
         if constexpr (!RAD)  // (the radial mode forms w at the path's start)
             o.w[WQ] = bload<float, kNT>(r.w, off4, p * rowb);
-        if constexpr (V2)
+        if constexpr (V2 && !RAD)
             o.wp[WQ] = bload<float, kNT>(r.wp, off4, p * rowb);
         static_range<0, 2 * pa.l3 + 1>([&](auto m) { o.g[GO + m] = bload<float>(r.g, off4, (pa.out_row + m) * rowb); });
     };
@@ -270,6 +280,11 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                     cp[2 * b] = make_float4(y.b0, y.b1, y.b2, 0.f);
                     cp[2 * b + 1] = make_float4(y.d0, y.d1, y.d2, 0.f);
                 });
+                if constexpr (RAD)
+                    static_range<0, RK>([&](auto k) {
+                        ep[HO + k] = k < nbasis ? hrad[static_cast<int64_t>(e) * nbasis + k] : 0.f;
+                        ep[HO + RK + k] = (has_wp && k < nbasis) ? ggh[static_cast<int64_t>(e) * nbasis + k] : 0.f;
+                    });
             }
         }
         wave_sync_lds();
@@ -342,10 +357,14 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
             }
         });
         const rsrc_t rgw = make_rsrc(ow ? ow + static_cast<int64_t>(e) * (P * C) : nullptr, ow ? P * C * 4u : 0u);
-        float4 h0, h1;
+        float4 h0, h1, hp0, hp1;
         if constexpr (RAD) {
             h0 = *reinterpret_cast<const float4 *>(ep + HO);
             h1 = *reinterpret_cast<const float4 *>(ep + HO + 4);
+            if constexpr (V2) {
+                hp0 = *reinterpret_cast<const float4 *>(ep + HO + RK);
+                hp1 = *reinterpret_cast<const float4 *>(ep + HO + RK + 4);
+            }
             static_range<0, RK>([&](auto k) { ghk[k] = 0.f; });
         }
         static_range<GI.p0, GI.p1>([&](auto p) {
@@ -369,8 +388,18 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                 wp = o.w[WQ];
             }
             float wpp = 0.f;
-            if constexpr (V2)
+            if constexpr (V2 && RAD) {  // W'[e, p, u] = sum_k H'[e, k] Wr[k, p, u], k in order
+                float t = hp0.x * wr[WQ][0];
+                t = fmaf(hp0.y, wr[WQ][1], t);
+                t = fmaf(hp0.z, wr[WQ][2], t);
+                t = fmaf(hp0.w, wr[WQ][3], t);
+                t = fmaf(hp1.x, wr[WQ][4], t);
+                t = fmaf(hp1.y, wr[WQ][5], t);
+                t = fmaf(hp1.z, wr[WQ][6], t);
+                wpp = fmaf(hp1.w, wr[WQ][7], t);
+            } else if constexpr (V2) {
                 wpp = o.wp[WQ];
+            }
             float wx[d1], xx[V2 ? d1 : 1], s[d1], sd[V2 ? d1 : 1];
             static_range<0, d1>([&](auto a) {
                 wx[a] = wp * xr[XO + a];
@@ -571,11 +600,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SrcCfg
                const float *__restrict__ ggw, const float *__restrict__ ggvec, float *__restrict__ ox,
                float *__restrict__ ow, float *__restrict__ ovec, const uint32_t flags,
                const float *__restrict__ hrad, const float *__restrict__ wrad, const int nbasis,
-               float *__restrict__ oh)
+               float *__restrict__ oh, const float *__restrict__ ggh)
 {
     extern __shared__ float lds[];
     src_group<L, XT, MODE, SG>(n_src, C, src_ptr, perm, perm_dst, vec, x, w, G, ggx, ggw, ggvec, ox, ow, ovec, flags,
-                               lds, hrad, wrad, nbasis, oh);
+                               lds, hrad, wrad, nbasis, oh, ggh);
 }
 
 template <int L, typename XT, int MODE>
@@ -595,14 +624,14 @@ static hipError_t launch_src_t(const ConvArgs &a)
             return;
         hipLaunchKernelGGL((src_kernel<L, XT, MODE, g>), dim3(a.n_src), dim3(64 * nch * src_splits(nch)), lds_bytes,
                            a.stream, a.n_src, a.C, a.src_ptr, a.perm, a.perm_dst, a.vec, static_cast<const XT *>(a.x), a.w, a.G, a.ggx,
-                           a.ggw, a.ggvec, a.ox, a.ow, a.ovec, a.flags, a.h, a.wr, a.nbasis, a.oh);
+                           a.ggw, a.ggvec, a.ox, a.ow, a.ovec, a.flags, a.h, a.wr, a.nbasis, a.oh, a.ggh);
         err = hipGetLastError();
     });
     return err;
 }
 
 #if !defined(ETP_L) || !defined(ETP_XT) || !defined(ETP_MODE)
-#error "compile this file once per (l_max, dtype, mode) with -DETP_L=0..4 -DETP_XT=0|1 -DETP_MODE=0|1|2"
+#error "compile this file once per (l_max, dtype, mode) with -DETP_L=0..4 -DETP_XT=0|1 -DETP_MODE=0..3"
 #endif
 
 hipError_t ETP_RUN_NAME(src, ETP_L, ETP_XT, ETP_MODE)(const ConvArgs &a)

@@ -26,15 +26,19 @@ ETP_F32 = 0
 ETP_BF16 = 1
 ETP_FLAG_ACCUMULATE = 1
 ETP_FLAG_VALIDATE = 2
+ETP_FLAG_DST_PASS = 4
+ETP_FLAG_SRC_PASS = 8
 
 # every symbol include/etp.h declares
-ABI_SYMBOLS = ("etp_plan_create", "etp_plan_destroy", "etp_plan_info", "etp_plan_tables",
+ABI_SYMBOLS = ("etp_plan_create", "etp_plan_destroy", "etp_plan_info", "etp_plan_describe", "etp_plan_tables",
                "etp_csr_transpose_workspace", "etp_csr_transpose", "etp_workspace_size", "etp_sh", "etp_edge_conv_fwd",
                "etp_edge_conv_fwd_radial", "etp_edge_conv_vjp_radial",
-               "etp_edge_conv_vjp", "etp_edge_conv_vjp2", "etp_channel_mix", "etp_edge_forces",
+               "etp_edge_conv_vjp", "etp_edge_conv_vjp2", "etp_edge_conv_vjp2_radial", "etp_channel_mix",
+               "etp_edge_forces",
                "etp_neighbor_workspace", "etp_neighbor_count", "etp_neighbor_fill", "etp_node_product", "etp_node_product_vjp", "etp_channel_mix_vjp",
                "etp_edge_tp_fwd", "etp_edge_tp_vjp", "etp_edge_tp_vjp2",
-               "etp_csr_transpose_noalloc", "etp_status_string", "etp_version")
+               "etp_csr_transpose_noalloc", "etp_edge_conv_vjp_ws", "etp_edge_conv_vjp2_ws",
+               "etp_status_string", "etp_version")
 
 
 class EtpError(RuntimeError):
@@ -91,7 +95,10 @@ def _load():
     sig = {
         "etp_plan_create": (st, [ctypes.POINTER(etp_plan_desc), ctypes.POINTER(vp)]),
         "etp_plan_destroy": (st, [vp]),
-        "etp_plan_info": (st, [vp, ctypes.POINTER(etp_plan_info_t)]),
+        "etp_plan_info": (st, [vp, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64),
+                               ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                               ctypes.POINTER(ctypes.c_int32)]),
+        "etp_plan_describe": (st, [vp, ctypes.POINTER(etp_plan_info_t)]),
         "etp_plan_tables": (st, [vp, vp, vp, vp, vp, vp]),
         "etp_csr_transpose_workspace": (st, [i32, ctypes.POINTER(ctypes.c_size_t)]),
         "etp_csr_transpose": (st, [ctypes.POINTER(etp_graph), vp, vp, vp, vp, ctypes.c_size_t, vp]),
@@ -103,8 +110,14 @@ def _load():
         "etp_edge_conv_vjp_radial": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, i32, vp, vp, vp, vp, vp, u32,
                                           vp]),
         "etp_edge_conv_vjp": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, vp, vp, vp, u32, vp]),
+        "etp_edge_conv_vjp2_radial": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
+                                           vp, vp, vp, u32, vp]),
         "etp_edge_conv_vjp2": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                     vp, u32, vp]),
+        "etp_edge_conv_vjp_ws": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, vp, vp, vp, u32, vp,
+                                      ctypes.c_size_t, vp]),
+        "etp_edge_conv_vjp2_ws": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       vp, u32, vp, ctypes.c_size_t, vp]),
         "etp_channel_mix": (st, [vp, i32, vp, vp, vp, u32, vp]),
         "etp_edge_forces": (st, [ctypes.POINTER(etp_graph), vp, vp, u32, vp]),
         "etp_node_product": (st, [vp, i32, i32, vp, vp, vp, u32, vp]),
@@ -212,10 +225,22 @@ def etp_plan_destroy(plan: Plan):
         plan.handle = None
 
 
-def etp_plan_info(plan: Plan) -> dict:
+def etp_plan_describe(plan: Plan) -> dict:
     info = etp_plan_info_t()
-    _check(lib.etp_plan_info(plan.handle, ctypes.byref(info)), "etp_plan_info")
+    _check(lib.etp_plan_describe(plan.handle, ctypes.byref(info)), "etp_plan_describe")
     return {k: getattr(info, k) for k, _ in etp_plan_info_t._fields_}
+
+
+def etp_plan_info(plan: Plan) -> dict:
+    """n_paths, din, dsh, dout (floats per node / SH per edge) and nnz, plus the
+    per-channel row counts and the plan's l_max, channels and dtype."""
+    n_paths, nnz = ctypes.c_int32(), ctypes.c_int32()
+    din, dsh, dout = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.etp_plan_info(plan.handle, ctypes.byref(n_paths), ctypes.byref(din), ctypes.byref(dsh),
+                             ctypes.byref(dout), ctypes.byref(nnz)), "etp_plan_info")
+    d = etp_plan_describe(plan)
+    d.update(n_paths=n_paths.value, nnz=nnz.value, din=din.value, dsh=dsh.value, dout=dout.value)
+    return d
 
 
 def etp_plan_tables(plan: Plan) -> dict:
@@ -258,7 +283,7 @@ def etp_csr_transpose_workspace(n_src: int) -> int:
     return b.value
 
 
-ETP_OP_FWD, ETP_OP_VJP, ETP_OP_VJP2, ETP_OP_TRANSPOSE = 0, 1, 2, 3
+ETP_OP_FWD, ETP_OP_VJP, ETP_OP_VJP2, ETP_OP_TRANSPOSE, ETP_OP_VJP_WS, ETP_OP_VJP2_WS = 0, 1, 2, 3, 4, 5
 
 
 def etp_workspace_size(plan: Plan, op: int, graph: Graph) -> int:
@@ -351,6 +376,32 @@ def etp_edge_conv_vjp_radial(plan: Plan, graph: Graph, vec, x, h, Wr, grad_out, 
         flags, _stream(stream)), "etp_edge_conv_vjp_radial")
 
 
+def etp_edge_conv_vjp2_radial(plan: Plan, graph: Graph, vec, x, h, Wr, grad_out, gg_x=None, gg_h=None, gg_vec=None,
+                              d_x=None, d_h=None, d_vec=None, d_grad_out=None, flags: int = 0, stream=None):
+    """VJP of etp_edge_conv_vjp_radial: d_x, d_h [E, K], d_vec, d_grad_out (each optional)."""
+    import torch
+    E, C = graph.n_edges, plan.C
+    K = int(Wr.shape[0]) if Wr is not None else 0
+    f32 = torch.float32
+    nx, no = graph.n_src * plan.din_rows * C, graph.n_dst * plan.dout_rows * C
+    g = graph.struct()
+    _check(lib.etp_edge_conv_vjp2_radial(
+        plan.handle, ctypes.byref(g),
+        _ptr(vec, "vec", f32, 3 * E, optional=True),
+        _ptr(x, "x", _xdtype(plan), nx, optional=True),
+        _ptr(h, "h", f32, E * K, optional=True), K,
+        _ptr(Wr, "Wr", f32, K * plan.P * C, optional=True),
+        _ptr(grad_out, "grad_out", f32, no, optional=True),
+        _ptr(gg_x, "gg_x", f32, nx, optional=True),
+        _ptr(gg_h, "gg_h", f32, E * K, optional=True),
+        _ptr(gg_vec, "gg_vec", f32, 3 * E, optional=True),
+        _ptr(d_x, "d_x", f32, nx, optional=True),
+        _ptr(d_h, "d_h", f32, E * K, optional=True),
+        _ptr(d_vec, "d_vec", f32, 3 * E, optional=True),
+        _ptr(d_grad_out, "d_grad_out", f32, no, optional=True),
+        flags, _stream(stream)), "etp_edge_conv_vjp2_radial")
+
+
 def etp_edge_conv_vjp(plan: Plan, graph: Graph, vec, x, w, grad_out, grad_x=None, grad_w=None, grad_vec=None,
                       flags: int = 0, stream=None):
     import torch
@@ -388,6 +439,61 @@ def etp_edge_conv_vjp2(plan: Plan, graph: Graph, vec, x, w, grad_out, gg_x=None,
                                   _ptr(d_vec, "d_vec", f32, 3 * E, optional=True),
                                   _ptr(d_grad_out, "d_grad_out", f32, no, optional=True),
                                   flags, _stream(stream)), "etp_edge_conv_vjp2")
+
+
+def _ws(ws):
+    return (None, 0) if ws is None else (_ptr(ws, "ws"), ws.numel() * ws.element_size())
+
+
+def etp_edge_conv_vjp_ws(plan: Plan, graph: Graph, vec, x, w, grad_out, grad_x=None, grad_w=None, grad_vec=None,
+                         ws=None, flags: int = 0, stream=None):
+    """The VJP over each destination's in-edges; ws: device buffer of at least
+    etp_workspace_size(plan, ETP_OP_VJP_WS, graph) bytes when grad_x is wanted."""
+    import torch
+    E, C = graph.n_edges, plan.C
+    f32 = torch.float32
+    g = graph.struct()
+    wp, wb = _ws(ws)
+    _check(lib.etp_edge_conv_vjp_ws(plan.handle, ctypes.byref(g),
+                                    _ptr(vec, "vec", f32, 3 * E, optional=True),
+                                    _ptr(x, "x", _xdtype(plan), graph.n_src * plan.din_rows * C, optional=True),
+                                    _ptr(w, "w", f32, E * plan.P * C, optional=True),
+                                    _ptr(grad_out, "grad_out", f32, graph.n_dst * plan.dout_rows * C, optional=True),
+                                    _ptr(grad_x, "grad_x", f32, graph.n_src * plan.din_rows * C, optional=True),
+                                    _ptr(grad_w, "grad_w", f32, E * plan.P * C, optional=True),
+                                    _ptr(grad_vec, "grad_vec", f32, 3 * E, optional=True),
+                                    flags, wp, wb, _stream(stream)), "etp_edge_conv_vjp_ws")
+
+
+def etp_edge_conv_vjp2_ws(plan: Plan, graph: Graph, vec, x, w, grad_out, gg_x=None, gg_w=None, gg_vec=None,
+                          d_x=None, d_w=None, d_vec=None, d_grad_out=None, ws=None, flags: int = 0, stream=None):
+    """The VJP-of-VJP over each destination's in-edges; ws as for etp_edge_conv_vjp_ws (needed for d_x)."""
+    import torch
+    E, C = graph.n_edges, plan.C
+    f32 = torch.float32
+    nx, nw, no = graph.n_src * plan.din_rows * C, E * plan.P * C, graph.n_dst * plan.dout_rows * C
+    g = graph.struct()
+    wp, wb = _ws(ws)
+    _check(lib.etp_edge_conv_vjp2_ws(plan.handle, ctypes.byref(g),
+                                     _ptr(vec, "vec", f32, 3 * E, optional=True),
+                                     _ptr(x, "x", _xdtype(plan), nx, optional=True),
+                                     _ptr(w, "w", f32, nw, optional=True),
+                                     _ptr(grad_out, "grad_out", f32, no, optional=True),
+                                     _ptr(gg_x, "gg_x", f32, nx, optional=True),
+                                     _ptr(gg_w, "gg_w", f32, nw, optional=True),
+                                     _ptr(gg_vec, "gg_vec", f32, 3 * E, optional=True),
+                                     _ptr(d_x, "d_x", f32, nx, optional=True),
+                                     _ptr(d_w, "d_w", f32, nw, optional=True),
+                                     _ptr(d_vec, "d_vec", f32, 3 * E, optional=True),
+                                     _ptr(d_grad_out, "d_grad_out", f32, no, optional=True),
+                                     flags, wp, wb, _stream(stream)), "etp_edge_conv_vjp2_ws")
+
+
+def bwd_workspace(plan: Plan, graph: Graph, op: int = None):
+    """A device workspace for etp_edge_conv_vjp_ws / _vjp2_ws (torch uint8 tensor, 256-byte aligned)."""
+    import torch
+    n = etp_workspace_size(plan, ETP_OP_VJP_WS if op is None else op, graph)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
 
 
 def mix_rows(plan: Plan):

@@ -135,18 +135,43 @@ typedef struct {
 enum {
     ETP_FLAG_ACCUMULATE = 1u, /* node outputs (out, grad_x, d_x, d_grad_out) are added to, not overwritten */
     ETP_FLAG_VALIDATE = 2u,   /* check the CSR on the device first (allocates and synchronises) */
+    ETP_FLAG_DST_PASS = 4u,   /* workspace VJP / VJP-of-VJP: walk each destination's in-edges */
+    ETP_FLAG_SRC_PASS = 8u,   /* workspace VJP / VJP-of-VJP: walk each source's out-edges */
 };
 
-/* Build a plan for (l_max, channels, x dtype). Host only; immutable after
- * creation and usable from several streams. Errors: INVALID_ARGUMENT (null
- * pointers, l_max outside [0, 4], channels outside [1, 1024], unknown
- * dtype, malformed path list), UNSUPPORTED (unequal l_max, a partial path
- * list, odd channels above 64). */
+/* Build a plan for (l_max, channels, x dtype): the path list and the sparse
+ * real CG table that every convolution call of the plan uses. The pages'
+ * tensor-product kernel keeps the Wigner 3-j coefficients in a compressed
+ * sparse form ("High-performance training and inference for deep
+ * equivariant interatomic potentials", review page, section "Proposed
+ * method"), and the forward, VJP and VJP-of-VJP are separate stages over the
+ * same tensor product ("How does FlashCart make equivariant interatomic
+ * potentials faster and more accurate?", section "Generated kernels beat SH
+ * baselines at high order"); the plan is what they share. desc: HOST. The
+ * table is compiled into the library, so nothing is allocated. Host only;
+ * immutable after creation and usable from several streams. Errors:
+ * INVALID_ARGUMENT (null pointers, l_max outside [0, 4], channels outside
+ * [1, 1024], unknown dtype, malformed path list), UNSUPPORTED (unequal l_max,
+ * a partial path list, odd channels above 64: a valid request this library
+ * does not implement). */
 ETP_API etp_status etp_plan_create(const etp_plan_desc *desc, etp_plan_t *plan);
 ETP_API etp_status etp_plan_destroy(etp_plan_t plan);
-ETP_API etp_status etp_plan_info(etp_plan_t plan, etp_plan_info_t *info);
 
-/* Copy the plan's tables into HOST buffers (any may be NULL):
+/* Sizes of a plan's tensor product (the same source as etp_plan_create),
+ * written through HOST pointers (any may be NULL): n_paths = P; din =
+ * C (l_max+1)^2 floats of x per node; dsh = (l_max+1)^2 SH per edge; dout =
+ * C sum_p (2 l3_p + 1) floats of out per node; nnz = CG entries over all
+ * paths. Errors: INVALID_ARGUMENT (null plan). */
+ETP_API etp_status etp_plan_info(etp_plan_t plan, int32_t *n_paths, int64_t *din, int64_t *dsh, int64_t *dout,
+                                 int32_t *nnz);
+/* The same sizes per channel, with the plan's l_max, channels and dtype, in
+ * one HOST struct. Errors: INVALID_ARGUMENT (null pointers). */
+ETP_API etp_status etp_plan_describe(etp_plan_t plan, etp_plan_info_t *info);
+
+/* The sparse Wigner 3-j table the plan holds ("High-performance training and
+ * inference for deep equivariant interatomic potentials", review page,
+ * section "Proposed method": the coefficients in compressed sparse form),
+ * for verification: copied into HOST buffers (any may be NULL):
  * paths[P][3], out_off[P+1] (first output row of each path), cg_ptr[P+1]
  * (CG entries of path p are [cg_ptr[p], cg_ptr[p+1])), cg_m[nnz][3] (m1, m2,
  * m3, signed, entries ordered by (m1, m2, m3) within a path), cg_val[nnz]
@@ -154,15 +179,24 @@ ETP_API etp_status etp_plan_info(etp_plan_t plan, etp_plan_info_t *info);
 ETP_API etp_status etp_plan_tables(etp_plan_t plan, int32_t *paths, int32_t *out_off, int32_t *cg_ptr, int8_t *cg_m,
                            float *cg_val);
 
-/* Device workspace (bytes) that etp_csr_transpose needs for n_src sources. */
+/* Device workspace (bytes) that etp_csr_transpose needs for n_src sources
+ * (host only; errors: INVALID_ARGUMENT for a null pointer or n_src < 0). */
 ETP_API etp_status etp_csr_transpose_workspace(int32_t n_src, size_t *bytes);
 
 /* Stable transpose of g's CSR (row_ptr, src, counts in g) into src_ptr,
- * perm, perm_dst (the transpose fields of g are ignored). Integer work,
+ * perm, perm_dst (the transpose fields of g are ignored): the neighbour list
+ * the convolution walks ("edges per atom" in "How does FlashCart make
+ * equivariant interatomic potentials faster and more accurate?", section on
+ * the SPICE-MACE-OFF model) grouped by source, which the source-side sums of
+ * the backward need (the aggregation of edge contributions that its section
+ * "Cartesian kernels replace SH coupling" names as the cost). Integer work,
  * bit-exact and deterministic: perm lists edge ids grouped by source, each
- * group in increasing edge id. ws: DEVICE workspace of at least
- * etp_csr_transpose_workspace(n_src) bytes. perm_dst doubles as scratch
- * during the call. */
+ * group in increasing edge id. src_ptr: DEVICE int32 [n_src + 1]; perm,
+ * perm_dst: DEVICE int32 [n_edges]; ws: DEVICE workspace of at least
+ * etp_csr_transpose_workspace(n_src) bytes, contents need not be
+ * initialised. perm_dst doubles as scratch during the call. Errors:
+ * INVALID_ARGUMENT (malformed graph descriptor, null pointers), UNSUPPORTED
+ * (n_edges >= 2^31), WORKSPACE (ws missing or too small), HIP. */
 ETP_API etp_status etp_csr_transpose(const etp_graph *g, int32_t *src_ptr, int32_t *perm, int32_t *perm_dst, void *ws,
                              size_t ws_bytes, void *stream);
 
@@ -183,17 +217,31 @@ ETP_API etp_status etp_csr_transpose(const etp_graph *g, int32_t *src_ptr, int32
 ETP_API etp_status etp_csr_transpose_noalloc(const etp_graph *g, int32_t *src_ptr, int32_t *perm, int32_t *perm_dst,
                                              void *stream);
 
-/* Device workspace (bytes) that an operation needs on graph g: ETP_OP_FWD,
+/* Device workspace (bytes) that an operation needs on graph g (the calls
+ * take caller-owned workspaces so that nothing is allocated inside them; the
+ * kernels keep intermediates out of memory where they can: "High-performance
+ * training and inference for deep equivariant interatomic potentials",
+ * review page, section "Proposed method"): ETP_OP_FWD,
  * ETP_OP_VJP and ETP_OP_VJP2 need none (0: the convolution keeps its
  * intermediates in registers and LDS and takes no workspace argument);
- * ETP_OP_TRANSPOSE needs etp_csr_transpose_workspace(g->n_src). Host only.
+ * ETP_OP_TRANSPOSE needs etp_csr_transpose_workspace(g->n_src);
+ * ETP_OP_VJP_WS and ETP_OP_VJP2_WS (etp_edge_conv_vjp_ws / _vjp2_ws) need
+ * n_edges * Din * C * 4 (one Din-row block of the node gradient per edge).
+ * Host only.
  * Errors: INVALID_ARGUMENT (null pointers, a malformed graph descriptor, an
  * unknown op), UNSUPPORTED (n_edges >= 2^31). */
-enum { ETP_OP_FWD = 0, ETP_OP_VJP = 1, ETP_OP_VJP2 = 2, ETP_OP_TRANSPOSE = 3 };
+enum { ETP_OP_FWD = 0, ETP_OP_VJP = 1, ETP_OP_VJP2 = 2, ETP_OP_TRANSPOSE = 3, ETP_OP_VJP_WS = 4, ETP_OP_VJP2_WS = 5 };
 ETP_API etp_status etp_workspace_size(etp_plan_t plan, int32_t op, const etp_graph *g, size_t *bytes);
 
-/* Spherical harmonics of n_edges bond vectors: Y[n][dsh] and, if dY is not
- * NULL, dY[n][3][dsh] = dY/dr (with respect to the unnormalised vector). */
+/* Real spherical harmonics of n_edges bond vectors, the second operand of the
+ * tensor product (the SH coupling of "How does FlashCart make equivariant
+ * interatomic potentials faster and more accurate?", section "Cartesian
+ * kernels replace SH coupling"; the convolution kernels evaluate them in
+ * registers, this call exposes them): Y[n][dsh] and, if dY is not NULL,
+ * dY[n][3][dsh] = dY/dr (with respect to the unnormalised vector), in the
+ * conventions listed at the top of this file. vec: DEVICE float [n][3]; Y,
+ * dY: DEVICE float. Errors: INVALID_ARGUMENT (null plan or pointers with
+ * n_edges > 0, n_edges < 0), HIP. */
 ETP_API etp_status etp_sh(etp_plan_t plan, int64_t n_edges, const float *vec, float *Y, float *dY, void *stream);
 
 /* Forward: out[n_dst][Dout][C] from vec, x (plan dtype), w. */
@@ -229,6 +277,46 @@ ETP_API etp_status etp_edge_conv_vjp(etp_plan_t plan, const etp_graph *g, const 
                              const float *grad_out, float *grad_x, float *grad_w, float *grad_vec, uint32_t flags,
                              void *stream);
 
+/* The VJP and VJP-of-VJP walked over each destination's in-edges instead of
+ * each source's out-edges, for callers that can lend a workspace. The
+ * backward's widest operand is the cotangent G[i] (Dout rows per node, several
+ * times the Din rows of x), and the pages locate the convolution's cost in
+ * memory access and edge aggregation ("How does FlashCart make equivariant
+ * interatomic potentials faster and more accurate?", section "Cartesian
+ * kernels replace SH coupling"; the VJP and VJP-of-VJP are the stages of its
+ * section "Generated kernels beat SH baselines at high order"): here each
+ * node's G rows are read once and kept in registers while its in-edges
+ * stream w (and W') and gather the x (and X') rows of their sources. The
+ * per-edge weight, bond-vector and (VJP-of-VJP) d_grad_out results come out
+ * of that pass directly; the node gradient grad_x (d_x) is first written as
+ * one Din-row block per edge into ws (ws[e][Din][C] floats) and then summed
+ * over each source's out-edges in the order of the stable transpose (fixed
+ * order, no atomics: bitwise deterministic). The VJP-of-VJP's d_grad_out
+ * comes from the destination pass that etp_edge_conv_vjp2 uses. Where the
+ * source-side walk of etp_edge_conv_vjp / _vjp2 measured faster (l_max 0, 1
+ * and 4, and the l_max = 2 VJP-of-VJP and VJP with C <= 64) these calls run
+ * it instead and leave ws unused; ETP_FLAG_DST_PASS or ETP_FLAG_SRC_PASS
+ * forces one formulation (not both). Results equal those of
+ * etp_edge_conv_vjp / etp_edge_conv_vjp2 up to rounding order (each
+ * formulation is deterministic on its own); arguments, shapes and null
+ * conventions are the same.
+ * ws: DEVICE workspace, 16-byte aligned, of at least
+ * etp_workspace_size(plan, ETP_OP_VJP_WS / ETP_OP_VJP2_WS, g) bytes
+ * (n_edges * Din * C * 4), needed only when grad_x (d_x) is requested from
+ * the destination-side formulation; its contents need not be initialised
+ * and are undefined afterwards. The transpose in g is needed for grad_x
+ * (d_x), and for every output of the source-side formulation. Errors: as
+ * etp_edge_conv_vjp / etp_edge_conv_vjp2, plus WORKSPACE (ws missing,
+ * misaligned or too small while grad_x / d_x is requested). */
+ETP_API etp_status etp_edge_conv_vjp_ws(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x,
+                                        const float *w, const float *grad_out, float *grad_x, float *grad_w,
+                                        float *grad_vec, uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+ETP_API etp_status etp_edge_conv_vjp2_ws(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x,
+                                         const float *w, const float *grad_out, const float *gg_x,
+                                         const float *gg_w, const float *gg_vec, float *d_x, float *d_w,
+                                         float *d_vec, float *d_grad_out, uint32_t flags, void *ws, size_t ws_bytes,
+                                         void *stream);
+
 /* VJP of etp_edge_conv_fwd_radial (the force call of a model whose path
  * weights come from radial features): with w = h Wr formed in the kernel as
  * in the forward, grad_x and grad_vec as etp_edge_conv_vjp gives them, and
@@ -245,6 +333,30 @@ ETP_API etp_status etp_edge_conv_vjp_radial(etp_plan_t plan, const etp_graph *g,
                                             const float *h, int32_t n_basis, const float *Wr,
                                             const float *grad_out, float *grad_x, float *grad_h, float *grad_vec,
                                             uint32_t flags, void *stream);
+
+/* VJP of etp_edge_conv_vjp_radial (force training of a model whose path
+ * weights come from radial features, with no E*P*C weight array in memory:
+ * "High-performance training and inference for deep equivariant interatomic
+ * potentials", review page, section "Proposed method"; the VJP-of-VJP stage
+ * of "How does FlashCart make equivariant interatomic potentials faster and
+ * more accurate?", section "Generated kernels beat SH baselines at high
+ * order"): with cotangents (gg_x, gg_h, gg_vec) on (grad_x, grad_h, grad_vec),
+ * the gradients of S = <gg_x, grad_x> + <gg_h, grad_h> + <gg_vec, grad_vec>
+ * with respect to x (d_x), h (d_h, DEVICE float [n_edges][n_basis]), vec
+ * (d_vec) and grad_out (d_grad_out). Since grad_h = grad_w Wr, the cotangent
+ * gg_h acts as gg_w = gg_h Wr, formed in the kernels like w = h Wr, and the
+ * weight cotangent is contracted back, d_h[e, k] = sum_{p,u} d_w[e, p, u]
+ * Wr[(k*P + p)*C + u]; the result equals etp_edge_conv_vjp2 with w = h Wr,
+ * gg_w = gg_h Wr and d_w contracted with Wr. The gradient with respect to Wr
+ * is not formed. Cotangents may be NULL (zero); outputs may be NULL.
+ * ETP_FLAG_ACCUMULATE applies to d_x and d_grad_out. Sums in a fixed order
+ * (deterministic). Needs the transpose in g; C <= 256. Errors as
+ * etp_edge_conv_vjp_radial. */
+ETP_API etp_status etp_edge_conv_vjp2_radial(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x,
+                                             const float *h, int32_t n_basis, const float *Wr, const float *grad_out,
+                                             const float *gg_x, const float *gg_h, const float *gg_vec, float *d_x,
+                                             float *d_h, float *d_vec, float *d_grad_out, uint32_t flags,
+                                             void *stream);
 
 /* VJP of the VJP: with cotangents (gg_x, gg_w, gg_vec) on (grad_x, grad_w,
  * grad_vec), the gradients of S = <gg_x, grad_x> + <gg_w, grad_w> +

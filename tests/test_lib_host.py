@@ -32,7 +32,7 @@ def header_symbols():
 
 def test_header_symbols_exported():
     names = header_symbols()
-    assert len(names) == 27
+    assert len(names) == 31
     assert sorted(etp.ABI_SYMBOLS) == names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (etp_\w+)$", out, flags=re.M))
@@ -100,6 +100,10 @@ def test_plan_tables_match_oracle(L):
     info = etp.etp_plan_info(plan)
     assert (info["n_paths"], info["nnz"], info["din_rows"], info["dsh"], info["dout_rows"]) == \
         (d["P"], d["nnz"], d["Din"], d["Dsh"], d["Dout"])
+    # the out-parameter form: floats per node (channels included)
+    assert (info["din"], info["dout"]) == (16 * d["Din"], 16 * d["Dout"])
+    assert etp.lib.etp_plan_info(None, None, None, None, None, None) == etp.ETP_ERR_INVALID_ARGUMENT
+    assert etp.lib.etp_plan_info(plan.handle, None, None, None, None, None) == etp.ETP_OK
     np.testing.assert_array_equal(t["paths"], oracle.paths(L))
     ptr, m, val = oracle.cg_sparse(L)
     np.testing.assert_array_equal(t["cg_ptr"], ptr)
