@@ -42,7 +42,7 @@ def units():
     for L in range(5):
         out.append((os.path.join(CSRC, "etp_edge_tp.hip"), os.path.join(BUILD, f"etp_edge_tp_L{L}.o"),
                     [f"-DETP_L={L}"]))
-    for name, modes in (("etp_dst", (0, 1, 2, 3)), ("etp_src", (0, 1, 2, 3)), ("etp_bwd", (0, 1))):
+    for name, modes in (("etp_dst", (0, 1, 2, 3)), ("etp_src", (0, 1, 2, 3, 4, 5)), ("etp_bwd", (0, 1))):
         for L in range(5):
             for xt in (0, 1):
                 for mode in modes:

@@ -70,6 +70,9 @@ int transpose_noalloc_max_sources();
 hipError_t launch_transpose_noalloc(int n_dst, int n_src, int64_t E, const int *row_ptr, const int *src,
                                     int *src_ptr, int *perm, int *perm_dst, hipStream_t stream);
 size_t neighbor_workspace_bytes(int n, const float *box, float rc);
+size_t block_sum_tmp_floats(int total);
+hipError_t launch_block_sum(int64_t n, int64_t stride, int total, const float *part, float *tmp, float *out,
+                            bool accumulate, hipStream_t stream);
 hipError_t launch_neighbor_count(int n, const float *pos, const float *box, float rc, int *row_ptr, void *ws,
                                  hipStream_t stream);
 hipError_t launch_neighbor_fill(int n, const float *pos, const float *box, float rc, const int *row_ptr,
@@ -215,6 +218,29 @@ hipError_t run_radial2(bool dst, int L, bool bf16, const etp::ConvArgs &a)
     default: return hipErrorInvalidValue;
     }
 #undef ETP_RADIAL2_CASE
+}
+
+// the radial source passes that also store weight-gradient partials (modes 4, 5)
+hipError_t run_src_wgrad(int L, bool bf16, bool vjp2, const etp::ConvArgs &a)
+{
+#define ETP_WG_CASE(L)                                                                                 \
+    case L:                                                                                            \
+        if (vjp2)                                                                                      \
+            return bf16 ? etp::ETP_RUN_NAME(src, L, 1, 5)(a) : etp::ETP_RUN_NAME(src, L, 0, 5)(a);     \
+        return bf16 ? etp::ETP_RUN_NAME(src, L, 1, 4)(a) : etp::ETP_RUN_NAME(src, L, 0, 4)(a);
+    switch (L) {
+        ETP_WG_CASE(0) ETP_WG_CASE(1) ETP_WG_CASE(2) ETP_WG_CASE(3) ETP_WG_CASE(4)
+    default: return hipErrorInvalidValue;
+    }
+#undef ETP_WG_CASE
+}
+
+// Workspace of the radial weight gradient: per-source-node partials
+// [n_src][8][P][C] and the ordered sum's 64 runs [64][8 P C].
+size_t wgrad_workspace_bytes(const etp_plan_s *plan, int32_t n_src)
+{
+    const size_t blk = static_cast<size_t>(ETP_MAX_RADIAL_BASIS) * plan->T->P * plan->C;
+    return sizeof(float) * (static_cast<size_t>(n_src) * blk + etp::block_sum_tmp_floats(static_cast<int>(blk)));
 }
 
 hipError_t run_src(int L, bool bf16, int mode, const etp::ConvArgs &a)
@@ -429,6 +455,9 @@ etp_status etp_workspace_size(etp_plan_t plan, int32_t op, const etp_graph *g, s
     case ETP_OP_VJP_WS:
     case ETP_OP_VJP2_WS:
         *bytes = bwd_workspace_bytes(plan, g->n_edges);
+        return ETP_OK;
+    case ETP_OP_RADIAL_WGRAD:
+        *bytes = wgrad_workspace_bytes(plan, g->n_src);
         return ETP_OK;
     default:
         return ETP_ERR_INVALID_ARGUMENT;
@@ -718,9 +747,26 @@ etp_status etp_edge_conv_vjp2_ws(etp_plan_t plan, const etp_graph *g, const floa
     return hip_status(run_bwd(plan->L, bf16, 1, a, d_x ? static_cast<float *>(ws) : nullptr, g->n_edges));
 }
 
-etp_status etp_edge_conv_vjp_radial(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x,
-                                    const float *h, int32_t n_basis, const float *Wr, const float *grad_out,
-                                    float *grad_x, float *grad_h, float *grad_vec, uint32_t flags, void *stream)
+// The source pass with weight-gradient partials, then their ordered sum over
+// the source nodes into grad_Wr [n_basis][P][C] (added to under ACCUMULATE).
+static etp_status wgrad_finish(etp_plan_t plan, const etp_graph *g, int32_t n_basis, float *grad_Wr, uint32_t flags,
+                               void *ws, etp::ConvArgs &a, bool vjp2)
+{
+    const int64_t blk = static_cast<int64_t>(ETP_MAX_RADIAL_BASIS) * plan->T->P * plan->C;
+    float *part = static_cast<float *>(ws);
+    a.owr = part;
+    etp_status st = hip_status(run_src_wgrad(plan->L, plan->dtype == ETP_BF16, vjp2, a));
+    if (st != ETP_OK)
+        return st;
+    const int total = static_cast<int>(static_cast<int64_t>(n_basis) * plan->T->P * plan->C);
+    return hip_status(etp::launch_block_sum(g->n_src, blk, total, part, part + g->n_src * blk, grad_Wr,
+                                            (flags & ETP_FLAG_ACCUMULATE) != 0, a.stream));
+}
+
+static etp_status radial_vjp(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x, const float *h,
+                             int32_t n_basis, const float *Wr, const float *grad_out, float *grad_x, float *grad_h,
+                             float *grad_vec, float *grad_Wr, uint32_t flags, void *ws, size_t ws_bytes,
+                             void *stream)
 {
     if (!plan)
         return ETP_ERR_INVALID_ARGUMENT;
@@ -733,12 +779,15 @@ etp_status etp_edge_conv_vjp_radial(etp_plan_t plan, const etp_graph *g, const f
         return ETP_ERR_UNSUPPORTED;
     if (flags & ~3u)
         return ETP_ERR_INVALID_ARGUMENT;
-    if (!grad_x && !grad_h && !grad_vec)
+    if (!grad_x && !grad_h && !grad_vec && !grad_Wr)
         return ETP_OK;
     if (g->n_src > 0 && (!x || !grad_out))
         return ETP_ERR_INVALID_ARGUMENT;
     if (g->n_edges > 0 && (!vec || !h || !Wr || !grad_out))
         return ETP_ERR_INVALID_ARGUMENT;
+    if (grad_Wr && (!ws || ws_bytes < wgrad_workspace_bytes(plan, g->n_src) ||
+                    (reinterpret_cast<uintptr_t>(ws) & 15u)))
+        return ETP_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (flags & ETP_FLAG_VALIDATE) {
         st = validate_graph(g, s);
@@ -765,13 +814,33 @@ etp_status etp_edge_conv_vjp_radial(etp_plan_t plan, const etp_graph *g, const f
     a.ovec = grad_vec;
     a.flags = flags & ETP_FLAG_ACCUMULATE;
     a.stream = s;
-    return hip_status(run_src_radial(plan->L, plan->dtype == ETP_BF16, a));
+    if (!grad_Wr)
+        return hip_status(run_src_radial(plan->L, plan->dtype == ETP_BF16, a));
+    return wgrad_finish(plan, g, n_basis, grad_Wr, flags, ws, a, false);
 }
 
-etp_status etp_edge_conv_vjp2_radial(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x,
-                                     const float *h, int32_t n_basis, const float *Wr, const float *grad_out,
-                                     const float *gg_x, const float *gg_h, const float *gg_vec, float *d_x, float *d_h,
-                                     float *d_vec, float *d_grad_out, uint32_t flags, void *stream)
+etp_status etp_edge_conv_vjp_radial(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x,
+                                    const float *h, int32_t n_basis, const float *Wr, const float *grad_out,
+                                    float *grad_x, float *grad_h, float *grad_vec, uint32_t flags, void *stream)
+{
+    return radial_vjp(plan, g, vec, x, h, n_basis, Wr, grad_out, grad_x, grad_h, grad_vec, nullptr, flags, nullptr,
+                      0, stream);
+}
+
+etp_status etp_edge_conv_vjp_radial_wgrad(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x,
+                                          const float *h, int32_t n_basis, const float *Wr, const float *grad_out,
+                                          float *grad_x, float *grad_h, float *grad_vec, float *grad_Wr,
+                                          uint32_t flags, void *ws, size_t ws_bytes, void *stream)
+{
+    return radial_vjp(plan, g, vec, x, h, n_basis, Wr, grad_out, grad_x, grad_h, grad_vec, grad_Wr, flags, ws,
+                      ws_bytes, stream);
+}
+
+static etp_status radial_vjp2(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x, const float *h,
+                              int32_t n_basis, const float *Wr, const float *grad_out, const float *gg_x,
+                              const float *gg_h, const float *gg_vec, float *d_x, float *d_h, float *d_vec,
+                              float *d_grad_out, float *d_Wr, uint32_t flags, void *ws, size_t ws_bytes,
+                              void *stream)
 {
     if (!plan)
         return ETP_ERR_INVALID_ARGUMENT;
@@ -784,12 +853,14 @@ etp_status etp_edge_conv_vjp2_radial(etp_plan_t plan, const etp_graph *g, const 
         return ETP_ERR_UNSUPPORTED;
     if (flags & ~3u)
         return ETP_ERR_INVALID_ARGUMENT;
-    if (!d_x && !d_h && !d_vec && !d_grad_out)
+    if (!d_x && !d_h && !d_vec && !d_grad_out && !d_Wr)
         return ETP_OK;
     if (g->n_edges > 0 && (!vec || !x || !h || !Wr))
         return ETP_ERR_INVALID_ARGUMENT;
-    if ((d_x || d_h || d_vec) && g->n_edges > 0 && !grad_out)
+    if ((d_x || d_h || d_vec || d_Wr) && g->n_edges > 0 && !grad_out)
         return ETP_ERR_INVALID_ARGUMENT;
+    if (d_Wr && (!ws || ws_bytes < wgrad_workspace_bytes(plan, g->n_src) || (reinterpret_cast<uintptr_t>(ws) & 15u)))
+        return ETP_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (flags & ETP_FLAG_VALIDATE) {
         st = validate_graph(g, s);
@@ -826,9 +897,30 @@ etp_status etp_edge_conv_vjp2_radial(etp_plan_t plan, const etp_graph *g, const 
         if (st != ETP_OK)
             return st;
     }
+    if (d_Wr)
+        return wgrad_finish(plan, g, n_basis, d_Wr, flags, ws, a, true);
     if (d_x || d_h || d_vec)
         return hip_status(run_radial2(false, plan->L, bf16, a));
     return ETP_OK;
+}
+
+etp_status etp_edge_conv_vjp2_radial(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x,
+                                     const float *h, int32_t n_basis, const float *Wr, const float *grad_out,
+                                     const float *gg_x, const float *gg_h, const float *gg_vec, float *d_x, float *d_h,
+                                     float *d_vec, float *d_grad_out, uint32_t flags, void *stream)
+{
+    return radial_vjp2(plan, g, vec, x, h, n_basis, Wr, grad_out, gg_x, gg_h, gg_vec, d_x, d_h, d_vec, d_grad_out,
+                       nullptr, flags, nullptr, 0, stream);
+}
+
+etp_status etp_edge_conv_vjp2_radial_wgrad(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x,
+                                           const float *h, int32_t n_basis, const float *Wr, const float *grad_out,
+                                           const float *gg_x, const float *gg_h, const float *gg_vec, float *d_x,
+                                           float *d_h, float *d_vec, float *d_grad_out, float *d_Wr, uint32_t flags,
+                                           void *ws, size_t ws_bytes, void *stream)
+{
+    return radial_vjp2(plan, g, vec, x, h, n_basis, Wr, grad_out, gg_x, gg_h, gg_vec, d_x, d_h, d_vec, d_grad_out,
+                       d_Wr, flags, ws, ws_bytes, stream);
 }
 
 etp_status etp_edge_conv_vjp2(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x, const float *w,

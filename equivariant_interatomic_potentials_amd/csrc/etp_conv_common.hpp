@@ -24,6 +24,7 @@ struct ConvArgs {
     const float *h, *wr;  // radial features [E][nbasis] and last-layer matrix [nbasis][P][C]
     const float *ggh;     // radial VJP-of-VJP: cotangent on grad_h [E][nbasis]
     float *oh;            // radial VJP: grad_h [E][nbasis] (VJP-of-VJP: d_h)
+    float *owr;           // radial weight gradient: per-source-node partials [n_src][8][P][C]
     int nbasis;
     uint32_t flags;
     hipStream_t stream;
@@ -31,7 +32,7 @@ struct ConvArgs {
 
 enum { DST_FWD = 0, DST_DG = 1, DST_FWD_RADIAL = 2, DST_DG_RADIAL = 3 };
 constexpr int kRadialMax = 8;  // radial basis functions per edge (padded to this in LDS)
-enum { SRC_VJP = 0, SRC_VJP2 = 1, SRC_VJP_RADIAL = 2, SRC_VJP2_RADIAL = 3 };
+enum { SRC_VJP = 0, SRC_VJP2 = 1, SRC_VJP_RADIAL = 2, SRC_VJP2_RADIAL = 3, SRC_VJP_RADIAL_WG = 4, SRC_VJP2_RADIAL_WG = 5 };
 
 // Each kernel source is compiled once per (l_max, x dtype, mode) with
 // -DETP_L, -DETP_XT (0 = f32, 1 = bf16) and -DETP_MODE, so the translation
@@ -47,8 +48,9 @@ enum { SRC_VJP = 0, SRC_VJP2 = 1, SRC_VJP_RADIAL = 2, SRC_VJP2_RADIAL = 3 };
     ETP_DECLARE_RUN(dst, L, 0, 2) ETP_DECLARE_RUN(dst, L, 1, 2) ETP_DECLARE_RUN(dst, L, 0, 3) ETP_DECLARE_RUN(dst, L, 1, 3)
 ETP_DECLARE_RUN_RADIAL(0) ETP_DECLARE_RUN_RADIAL(1) ETP_DECLARE_RUN_RADIAL(2) ETP_DECLARE_RUN_RADIAL(3)
 ETP_DECLARE_RUN_RADIAL(4)
-#define ETP_DECLARE_RUN_SRC_RADIAL(L) \
-    ETP_DECLARE_RUN(src, L, 0, 2) ETP_DECLARE_RUN(src, L, 1, 2) ETP_DECLARE_RUN(src, L, 0, 3) ETP_DECLARE_RUN(src, L, 1, 3)
+#define ETP_DECLARE_RUN_SRC_RADIAL(L)                                                                           \
+    ETP_DECLARE_RUN(src, L, 0, 2) ETP_DECLARE_RUN(src, L, 1, 2) ETP_DECLARE_RUN(src, L, 0, 3) ETP_DECLARE_RUN(src, L, 1, 3) \
+    ETP_DECLARE_RUN(src, L, 0, 4) ETP_DECLARE_RUN(src, L, 1, 4) ETP_DECLARE_RUN(src, L, 0, 5) ETP_DECLARE_RUN(src, L, 1, 5)
 ETP_DECLARE_RUN_SRC_RADIAL(0) ETP_DECLARE_RUN_SRC_RADIAL(1) ETP_DECLARE_RUN_SRC_RADIAL(2)
 ETP_DECLARE_RUN_SRC_RADIAL(3) ETP_DECLARE_RUN_SRC_RADIAL(4)
 ETP_DECLARE_RUN_L(dst, 0) ETP_DECLARE_RUN_L(dst, 1) ETP_DECLARE_RUN_L(dst, 2) ETP_DECLARE_RUN_L(dst, 3) ETP_DECLARE_RUN_L(dst, 4)

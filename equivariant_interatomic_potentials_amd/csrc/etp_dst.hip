@@ -52,6 +52,12 @@ namespace etp {
 #ifndef ETP_DST_B2
 #define ETP_DST_B2 32
 #endif
+#ifndef ETP_DST_B3
+#define ETP_DST_B3 16
+#endif
+#ifndef ETP_DST_B4
+#define ETP_DST_B4 8
+#endif
 #ifndef ETP_DST_ROWS_FWD
 #define ETP_DST_ROWS_FWD 112
 #endif
@@ -82,7 +88,7 @@ namespace etp {
 template <int L, int CPL, int MODE>
 struct DstCfg {
     static constexpr int S = ETP_DST_S;
-    static constexpr int B = L <= 2 ? ETP_DST_B2 : (L == 3 ? 16 : 8);
+    static constexpr int B = L <= 2 ? ETP_DST_B2 : (L == 3 ? ETP_DST_B3 : ETP_DST_B4);
     static constexpr int ROWS = MODE == DST_DG_RADIAL ? ETP_DST_ROWS_RAD
                               : MODE == DST_FWD_RADIAL ? (L <= 2 ? ETP_DST_ROWS_FWD : ETP_DST_ROWS_RAD)
                               : MODE == DST_FWD ? (L <= 2 ? ETP_DST_ROWS_FWD : L == 3 ? ETP_DST_ROWS_FWD3 : ETP_DST_ROWS_FWD4)

@@ -306,6 +306,54 @@ hipError_t launch_transpose(int n_dst, int n_src, int64_t E, const int *row_ptr,
     return hipGetLastError();
 }
 
+// ------------------------------------------------------- ordered block sum
+// out[t] (+)= sum over j < n of part[j * stride + t], t < total, in the order
+// of j: level 1 sums runs of up to `per` consecutive blocks into tmp[g][t],
+// level 2 adds the runs in order (a fixed order throughout: deterministic).
+// Used for weight gradients that are sums over all nodes of per-node partials.
+constexpr int kBlockSumRuns = 64;
+
+__global__ void __launch_bounds__(256) block_sum_l1_kernel(int64_t n, int64_t stride, int total, int64_t per,
+                                                          const float *__restrict__ part, float *__restrict__ tmp)
+{
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= total)
+        return;
+    const int64_t j0 = blockIdx.y * per, j1 = (j0 + per < n) ? j0 + per : n;
+    float s = 0.f;
+    for (int64_t j = j0; j < j1; ++j)
+        s += part[j * stride + t];
+    tmp[static_cast<int64_t>(blockIdx.y) * total + t] = s;
+}
+
+__global__ void __launch_bounds__(256) block_sum_l2_kernel(int runs, int total, const float *__restrict__ tmp,
+                                                          float *__restrict__ out, int accumulate)
+{
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= total)
+        return;
+    float s = 0.f;
+    for (int g = 0; g < runs; ++g)
+        s += tmp[static_cast<int64_t>(g) * total + t];
+    out[t] = accumulate ? out[t] + s : s;
+}
+
+size_t block_sum_tmp_floats(int total) { return static_cast<size_t>(kBlockSumRuns) * total; }
+
+hipError_t launch_block_sum(int64_t n, int64_t stride, int total, const float *part, float *tmp, float *out,
+                            bool accumulate, hipStream_t stream)
+{
+    if (total <= 0)
+        return hipSuccess;
+    const int64_t per = n > 0 ? (n + kBlockSumRuns - 1) / kBlockSumRuns : 1;
+    const unsigned bx = static_cast<unsigned>((total + 255) / 256);
+    hipLaunchKernelGGL(block_sum_l1_kernel, dim3(bx, kBlockSumRuns), dim3(256), 0, stream, n, stride, total, per, part,
+                       tmp);
+    hipLaunchKernelGGL(block_sum_l2_kernel, dim3(bx), dim3(256), 0, stream, kBlockSumRuns, total, tmp, out,
+                       accumulate ? 1 : 0);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------- no-allocation variant
 // The transpose's workspace (the per-source cursors and the scan's tile
 // totals) for callers that cannot allocate: a file-scope device array of

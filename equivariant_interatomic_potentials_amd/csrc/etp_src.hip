@@ -42,7 +42,12 @@
 //     per chunk, chunks in order, later path groups adding to earlier ones);
 //   * radial VJP-of-VJP: the same with the cotangent H' on gh as the
 //     cotangent W' = H' Wr on gw (formed like w from the edge's H' row), and
-//     dw contracted into dh[k] += dw Wr[k, p, u] the way gw becomes gh.
+//     dw contracted into dh[k] += dw Wr[k, p, u] the way gw becomes gh;
+//   * radial weight gradient (modes with WG): each lane also sums, over the
+//     node's out-edges, h[e, k] gw[e, p, u] (VJP) or h[e, k] dw[e, p, u] +
+//     H'[e, k] gw[e, p, u] (VJP-of-VJP) for its group's paths; the edge
+//     splits meet in a fixed-order LDS sum and the node's [8][P][C] block of
+//     partials is stored, to be summed over nodes in order afterwards.
 #include "etp_conv_common.hpp"
 
 namespace etp {
@@ -92,8 +97,9 @@ namespace etp {
 #endif
 template <int L, int MODE>
 struct SrcCfg {
-    static constexpr bool RAD = MODE == SRC_VJP_RADIAL || MODE == SRC_VJP2_RADIAL;
-    static constexpr bool V2 = MODE == SRC_VJP2 || MODE == SRC_VJP2_RADIAL;
+    static constexpr bool WG = MODE == SRC_VJP_RADIAL_WG || MODE == SRC_VJP2_RADIAL_WG;
+    static constexpr bool RAD = MODE == SRC_VJP_RADIAL || MODE == SRC_VJP2_RADIAL || WG;
+    static constexpr bool V2 = MODE == SRC_VJP2 || MODE == SRC_VJP2_RADIAL || MODE == SRC_VJP2_RADIAL_WG;
     static constexpr int NV = V2 ? 2 : 1;                           // Y (, Yd) and Z (, Z2) copies
     static constexpr int DSH = (L + 1) * (L + 1), DSHP = (DSH + 3) & ~3;
     static constexpr int GQ = 4 * NV * DSH;                         // gr coefficients, a float4 per (b, copy)
@@ -112,7 +118,7 @@ struct SrcCfg {
     }();
     // registers per path beyond its G rows: the w row (and W'), or in the
     // radial mode the 8 Wr entries
-    static constexpr int WMUL = RAD ? kRadialMax : (V2 ? 2 : 1);
+    static constexpr int WMUL = RAD ? (WG ? 2 : 1) * kRadialMax : (V2 ? 2 : 1);
     static constexpr int MAXCOST = RAD ? (V2 ? (L <= 2 ? ETP_SRC_COST_RAD2 : L == 3 ? 100 : 80)
                                              : (L <= 2 ? ETP_SRC_COST_RAD : L == 3 ? 130 : 100))
                                    : V2 ? (L <= 2 ? ETP_SRC_COST_VJP2 : L == 3 ? ETP_SRC_COST_VJP2_3
@@ -132,7 +138,15 @@ constexpr int src_lds_floats(int nch)
     const int nw = nch * src_splits(nch);
     // per wave: the batch (B x ES) and two alternating park slots (B x PK)
     const int batch = nw * Cfg::B * Cfg::ESP;
-    const int reduce = (src_splits(nch) - 1) * nch * kTab<L>.din_rows * 64;  // node rows of the splits
+    int rows = kTab<L>.din_rows;  // node rows of the splits (and the weight-gradient partials)
+    if (Cfg::WG) {
+        const Groups GR = make_src_groups(kTab<L>, Cfg::MAXCOST, Cfg::WMUL);
+        for (int k = 0; k < GR.n; ++k) {
+            const int np = (GR.p1[k] - GR.p0[k]) * kRadialMax;
+            rows = np > rows ? np : rows;
+        }
+    }
+    const int reduce = (src_splits(nch) - 1) * nch * rows * 64;
     return batch > reduce ? batch : reduce;
 }
 
@@ -146,11 +160,12 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                                           float *__restrict__ ow, float *__restrict__ ovec,
                                           const uint32_t flags, float *lds, const float *__restrict__ hrad,
                                           const float *__restrict__ wrad, const int nbasis,
-                                          float *__restrict__ oh, const float *__restrict__ ggh)
+                                          float *__restrict__ oh, const float *__restrict__ ggh,
+                                          float *__restrict__ owr)
 {
     using Cfg = SrcCfg<L, MODE>;
     constexpr int B = Cfg::B, ES = Cfg::ES, NV = Cfg::NV, DSHP = Cfg::DSHP, PK = Cfg::PK;
-    constexpr bool V2 = Cfg::V2, RAD = Cfg::RAD;
+    constexpr bool V2 = Cfg::V2, RAD = Cfg::RAD, WG = Cfg::WG;
     constexpr int RK = kRadialMax, HO = NV * DSHP + Cfg::GQ;  // h row offset in an edge's batch slot
     constexpr Groups GR = make_src_groups(kTab<L>, Cfg::MAXCOST, Cfg::WMUL);
     constexpr SrcGroupInfo GI = src_group_info(kTab<L>, GR, SG);
@@ -335,6 +350,10 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
     // node accumulators, the weight cotangent (stored) and the Z partial
     // sums; then the path's registers take the next edge's rows.
     float Z[DSH], Z2[V2 ? DSH : 1], ghk[RAD ? RK : 1];
+    // the weight-gradient sums of the group's paths over the node's out-edges
+    float wg[WG ? NP : 1][WG ? RK : 1];
+    if constexpr (WG)
+        static_range<0, NP>([&](auto q) { static_range<0, RK>([&](auto k) { wg[q][k] = 0.f; }); });
     static_range<0, DSH>([&](auto b) {
         Z[b] = 0.f;
         if constexpr (V2)
@@ -463,6 +482,19 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                 static_range<0, RK>([&](auto k) { ghk[k] = fmaf(gwv, wr[WQ][k], ghk[k]); });
             else
                 bstore<float, kNT>(gwv, rgw, off4, p * rowb);
+            if constexpr (WG) {
+                // dWr[k, p, u] += h[e, k] gw (VJP), or h[e, k] dw + H'[e, k] gw
+                // with the plain gw = sum_m1 x s (VJP-of-VJP)
+                const float hk[RK] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+                if constexpr (V2) {
+                    float gpl = 0.f;
+                    static_range<0, d1>([&](auto a) { gpl = fmaf(xr[XO + a], s[a], gpl); });
+                    const float hpk[RK] = {hp0.x, hp0.y, hp0.z, hp0.w, hp1.x, hp1.y, hp1.z, hp1.w};
+                    static_range<0, RK>([&](auto k) { wg[WQ][k] = fmaf(hpk[k], gpl, fmaf(hk[k], gwv, wg[WQ][k])); });
+                } else {
+                    static_range<0, RK>([&](auto k) { wg[WQ][k] = fmaf(hk[k], gwv, wg[WQ][k]); });
+                }
+            }
         });
     };
 
@@ -576,6 +608,36 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                 static_range<0, NXR>([&](auto r) { acc[r] += lds[((q - 1) * nch + ch) * (NXR * 64) + r * 64 + lane]; });
     }
 
+    // the weight-gradient partials: the splits meet in wave sp = 0 of each
+    // chunk, in order, and node j's block [8][P][C] (this group's paths) is
+    // stored
+    if constexpr (WG) {
+        if (nsp > 1) {
+            constexpr int NR = NP * RK;
+            __syncthreads();
+            if (sp > 0)
+                static_range<0, NP>([&](auto q) {
+                    static_range<0, RK>([&](auto k) {
+                        lds[((sp - 1) * nch + ch) * (NR * 64) + (q * RK + k) * 64 + lane] = wg[q][k];
+                    });
+                });
+            __syncthreads();
+            if (sp == 0)
+                for (int t = 1; t < nsp; ++t)
+                    static_range<0, NP>([&](auto q) {
+                        static_range<0, RK>([&](auto k) {
+                            wg[q][k] += lds[((t - 1) * nch + ch) * (NR * 64) + (q * RK + k) * 64 + lane];
+                        });
+                    });
+        }
+        if (owr && sp == 0) {
+            const rsrc_t rw = make_rsrc(owr + static_cast<int64_t>(j) * (RK * P * C), RK * P * C * 4u);
+            static_range<0, NP>([&](auto q) {
+                static_range<0, RK>([&](auto k) { bstore<float>(wg[q][k], rw, off4, (k * P + GI.p0 + q) * rowb); });
+            });
+        }
+    }
+
     // node rows of j: stored, or added where the user asked to accumulate or
     // an earlier path group already stored part of the same l1 rows
     if (ox && sp == 0) {
@@ -600,11 +662,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SrcCfg
                const float *__restrict__ ggw, const float *__restrict__ ggvec, float *__restrict__ ox,
                float *__restrict__ ow, float *__restrict__ ovec, const uint32_t flags,
                const float *__restrict__ hrad, const float *__restrict__ wrad, const int nbasis,
-               float *__restrict__ oh, const float *__restrict__ ggh)
+               float *__restrict__ oh, const float *__restrict__ ggh, float *__restrict__ owr)
 {
     extern __shared__ float lds[];
     src_group<L, XT, MODE, SG>(n_src, C, src_ptr, perm, perm_dst, vec, x, w, G, ggx, ggw, ggvec, ox, ow, ovec, flags,
-                               lds, hrad, wrad, nbasis, oh, ggh);
+                               lds, hrad, wrad, nbasis, oh, ggh, owr);
 }
 
 template <int L, typename XT, int MODE>
@@ -624,14 +686,14 @@ static hipError_t launch_src_t(const ConvArgs &a)
             return;
         hipLaunchKernelGGL((src_kernel<L, XT, MODE, g>), dim3(a.n_src), dim3(64 * nch * src_splits(nch)), lds_bytes,
                            a.stream, a.n_src, a.C, a.src_ptr, a.perm, a.perm_dst, a.vec, static_cast<const XT *>(a.x), a.w, a.G, a.ggx,
-                           a.ggw, a.ggvec, a.ox, a.ow, a.ovec, a.flags, a.h, a.wr, a.nbasis, a.oh, a.ggh);
+                           a.ggw, a.ggvec, a.ox, a.ow, a.ovec, a.flags, a.h, a.wr, a.nbasis, a.oh, a.ggh, a.owr);
         err = hipGetLastError();
     });
     return err;
 }
 
 #if !defined(ETP_L) || !defined(ETP_XT) || !defined(ETP_MODE)
-#error "compile this file once per (l_max, dtype, mode) with -DETP_L=0..4 -DETP_XT=0|1 -DETP_MODE=0..3"
+#error "compile this file once per (l_max, dtype, mode) with -DETP_L=0..4 -DETP_XT=0|1 -DETP_MODE=0..5"
 #endif
 
 hipError_t ETP_RUN_NAME(src, ETP_L, ETP_XT, ETP_MODE)(const ConvArgs &a)

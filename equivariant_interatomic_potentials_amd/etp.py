@@ -38,6 +38,7 @@ ABI_SYMBOLS = ("etp_plan_create", "etp_plan_destroy", "etp_plan_info", "etp_plan
                "etp_neighbor_workspace", "etp_neighbor_count", "etp_neighbor_fill", "etp_node_product", "etp_node_product_vjp", "etp_channel_mix_vjp",
                "etp_edge_tp_fwd", "etp_edge_tp_vjp", "etp_edge_tp_vjp2",
                "etp_csr_transpose_noalloc", "etp_edge_conv_vjp_ws", "etp_edge_conv_vjp2_ws",
+               "etp_edge_conv_vjp_radial_wgrad", "etp_edge_conv_vjp2_radial_wgrad",
                "etp_status_string", "etp_version")
 
 
@@ -116,6 +117,10 @@ def _load():
                                     vp, u32, vp]),
         "etp_edge_conv_vjp_ws": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, vp, vp, vp, u32, vp,
                                       ctypes.c_size_t, vp]),
+        "etp_edge_conv_vjp_radial_wgrad": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, i32, vp, vp, vp, vp, vp,
+                                                vp, u32, vp, ctypes.c_size_t, vp]),
+        "etp_edge_conv_vjp2_radial_wgrad": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, i32, vp, vp, vp, vp, vp,
+                                                 vp, vp, vp, vp, vp, u32, vp, ctypes.c_size_t, vp]),
         "etp_edge_conv_vjp2_ws": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        vp, u32, vp, ctypes.c_size_t, vp]),
         "etp_channel_mix": (st, [vp, i32, vp, vp, vp, u32, vp]),
@@ -284,6 +289,7 @@ def etp_csr_transpose_workspace(n_src: int) -> int:
 
 
 ETP_OP_FWD, ETP_OP_VJP, ETP_OP_VJP2, ETP_OP_TRANSPOSE, ETP_OP_VJP_WS, ETP_OP_VJP2_WS = 0, 1, 2, 3, 4, 5
+ETP_OP_RADIAL_WGRAD = 6
 
 
 def etp_workspace_size(plan: Plan, op: int, graph: Graph) -> int:
@@ -400,6 +406,59 @@ def etp_edge_conv_vjp2_radial(plan: Plan, graph: Graph, vec, x, h, Wr, grad_out,
         _ptr(d_vec, "d_vec", f32, 3 * E, optional=True),
         _ptr(d_grad_out, "d_grad_out", f32, no, optional=True),
         flags, _stream(stream)), "etp_edge_conv_vjp2_radial")
+
+
+def etp_edge_conv_vjp_radial_wgrad(plan: Plan, graph: Graph, vec, x, h, Wr, grad_out, grad_x=None, grad_h=None,
+                                   grad_vec=None, grad_Wr=None, ws=None, flags: int = 0, stream=None):
+    """etp_edge_conv_vjp_radial plus grad_Wr [K, P, C]; ws: etp_workspace_size(plan, ETP_OP_RADIAL_WGRAD, graph)
+    bytes."""
+    import torch
+    E, C = graph.n_edges, plan.C
+    K = int(Wr.shape[0]) if Wr is not None else 0
+    f32 = torch.float32
+    g = graph.struct()
+    wp, wb = _ws(ws)
+    _check(lib.etp_edge_conv_vjp_radial_wgrad(
+        plan.handle, ctypes.byref(g),
+        _ptr(vec, "vec", f32, 3 * E, optional=True),
+        _ptr(x, "x", _xdtype(plan), graph.n_src * plan.din_rows * C, optional=True),
+        _ptr(h, "h", f32, E * K, optional=True), K,
+        _ptr(Wr, "Wr", f32, K * plan.P * C, optional=True),
+        _ptr(grad_out, "grad_out", f32, graph.n_dst * plan.dout_rows * C, optional=True),
+        _ptr(grad_x, "grad_x", f32, graph.n_src * plan.din_rows * C, optional=True),
+        _ptr(grad_h, "grad_h", f32, E * K, optional=True),
+        _ptr(grad_vec, "grad_vec", f32, 3 * E, optional=True),
+        _ptr(grad_Wr, "grad_Wr", f32, K * plan.P * C, optional=True),
+        flags, wp, wb, _stream(stream)), "etp_edge_conv_vjp_radial_wgrad")
+
+
+def etp_edge_conv_vjp2_radial_wgrad(plan: Plan, graph: Graph, vec, x, h, Wr, grad_out, gg_x=None, gg_h=None,
+                                    gg_vec=None, d_x=None, d_h=None, d_vec=None, d_grad_out=None, d_Wr=None,
+                                    ws=None, flags: int = 0, stream=None):
+    """etp_edge_conv_vjp2_radial plus d_Wr [K, P, C]; ws as for etp_edge_conv_vjp_radial_wgrad."""
+    import torch
+    E, C = graph.n_edges, plan.C
+    K = int(Wr.shape[0]) if Wr is not None else 0
+    f32 = torch.float32
+    nx, no = graph.n_src * plan.din_rows * C, graph.n_dst * plan.dout_rows * C
+    g = graph.struct()
+    wp, wb = _ws(ws)
+    _check(lib.etp_edge_conv_vjp2_radial_wgrad(
+        plan.handle, ctypes.byref(g),
+        _ptr(vec, "vec", f32, 3 * E, optional=True),
+        _ptr(x, "x", _xdtype(plan), nx, optional=True),
+        _ptr(h, "h", f32, E * K, optional=True), K,
+        _ptr(Wr, "Wr", f32, K * plan.P * C, optional=True),
+        _ptr(grad_out, "grad_out", f32, no, optional=True),
+        _ptr(gg_x, "gg_x", f32, nx, optional=True),
+        _ptr(gg_h, "gg_h", f32, E * K, optional=True),
+        _ptr(gg_vec, "gg_vec", f32, 3 * E, optional=True),
+        _ptr(d_x, "d_x", f32, nx, optional=True),
+        _ptr(d_h, "d_h", f32, E * K, optional=True),
+        _ptr(d_vec, "d_vec", f32, 3 * E, optional=True),
+        _ptr(d_grad_out, "d_grad_out", f32, no, optional=True),
+        _ptr(d_Wr, "d_Wr", f32, K * plan.P * C, optional=True),
+        flags, wp, wb, _stream(stream)), "etp_edge_conv_vjp2_radial_wgrad")
 
 
 def etp_edge_conv_vjp(plan: Plan, graph: Graph, vec, x, w, grad_out, grad_x=None, grad_w=None, grad_vec=None,

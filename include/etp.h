@@ -226,11 +226,22 @@ ETP_API etp_status etp_csr_transpose_noalloc(const etp_graph *g, int32_t *src_pt
  * intermediates in registers and LDS and takes no workspace argument);
  * ETP_OP_TRANSPOSE needs etp_csr_transpose_workspace(g->n_src);
  * ETP_OP_VJP_WS and ETP_OP_VJP2_WS (etp_edge_conv_vjp_ws / _vjp2_ws) need
- * n_edges * Din * C * 4 (one Din-row block of the node gradient per edge).
+ * n_edges * Din * C * 4 (one Din-row block of the node gradient per edge);
+ * ETP_OP_RADIAL_WGRAD (the radial weight gradients) needs
+ * (n_src + 64) * ETP_MAX_RADIAL_BASIS * P * C * 4 (per-source-node partials
+ * and the runs of their ordered sum).
  * Host only.
  * Errors: INVALID_ARGUMENT (null pointers, a malformed graph descriptor, an
  * unknown op), UNSUPPORTED (n_edges >= 2^31). */
-enum { ETP_OP_FWD = 0, ETP_OP_VJP = 1, ETP_OP_VJP2 = 2, ETP_OP_TRANSPOSE = 3, ETP_OP_VJP_WS = 4, ETP_OP_VJP2_WS = 5 };
+enum {
+    ETP_OP_FWD = 0,
+    ETP_OP_VJP = 1,
+    ETP_OP_VJP2 = 2,
+    ETP_OP_TRANSPOSE = 3,
+    ETP_OP_VJP_WS = 4,
+    ETP_OP_VJP2_WS = 5,
+    ETP_OP_RADIAL_WGRAD = 6
+};
 ETP_API etp_status etp_workspace_size(etp_plan_t plan, int32_t op, const etp_graph *g, size_t *bytes);
 
 /* Real spherical harmonics of n_edges bond vectors, the second operand of the
@@ -323,11 +334,11 @@ ETP_API etp_status etp_edge_conv_vjp2_ws(etp_plan_t plan, const etp_graph *g, co
  * instead of grad_w its contraction with the last layer,
  *   grad_h[e, k] = sum_{p,u} grad_w[e, p, u] Wr[(k*P + p)*C + u]
  * (DEVICE float [n_edges][n_basis]; with grad_vec it yields the forces
- * through h's dependence on |r|). The gradient with respect to Wr (a sum
- * over all edges, needed only for training) is not formed. Outputs may be
- * NULL; ETP_FLAG_ACCUMULATE applies to grad_x only. Sums over channels,
+ * through h's dependence on |r|). Outputs may be NULL; ETP_FLAG_ACCUMULATE
+ * applies to grad_x only. Sums over channels,
  * paths and channel chunks are in a fixed order (deterministic). Needs the
- * transpose in g; C <= 256. Errors as etp_edge_conv_fwd_radial, plus
+ * transpose in g; C <= 256. The gradient with respect to Wr comes from
+ * etp_edge_conv_vjp_radial_wgrad. Errors as etp_edge_conv_fwd_radial, plus
  * UNSUPPORTED for C > 256. */
 ETP_API etp_status etp_edge_conv_vjp_radial(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x,
                                             const float *h, int32_t n_basis, const float *Wr,
@@ -348,7 +359,7 @@ ETP_API etp_status etp_edge_conv_vjp_radial(etp_plan_t plan, const etp_graph *g,
  * weight cotangent is contracted back, d_h[e, k] = sum_{p,u} d_w[e, p, u]
  * Wr[(k*P + p)*C + u]; the result equals etp_edge_conv_vjp2 with w = h Wr,
  * gg_w = gg_h Wr and d_w contracted with Wr. The gradient with respect to Wr
- * is not formed. Cotangents may be NULL (zero); outputs may be NULL.
+ * comes from etp_edge_conv_vjp2_radial_wgrad. Cotangents may be NULL (zero); outputs may be NULL.
  * ETP_FLAG_ACCUMULATE applies to d_x and d_grad_out. Sums in a fixed order
  * (deterministic). Needs the transpose in g; C <= 256. Errors as
  * etp_edge_conv_vjp_radial. */
@@ -357,6 +368,39 @@ ETP_API etp_status etp_edge_conv_vjp2_radial(etp_plan_t plan, const etp_graph *g
                                              const float *gg_x, const float *gg_h, const float *gg_vec, float *d_x,
                                              float *d_h, float *d_vec, float *d_grad_out, uint32_t flags,
                                              void *stream);
+
+/* The radial VJP and VJP-of-VJP that also form the gradient with respect to
+ * the last-layer matrix Wr (training the radial network end to end; the
+ * pages weight each path by a learned function of the edge's radial
+ * features: "Scaling the leading accuracy of deep equivariant models to
+ * biomolecular simulations of realistic size", section "Proposed method"):
+ *   etp_edge_conv_vjp_radial_wgrad:  grad_Wr[k, p, u] = sum_e h[e, k] gw[e, p, u]
+ *   etp_edge_conv_vjp2_radial_wgrad: d_Wr[k, p, u] = sum_e h[e, k] dw[e, p, u]
+ *                                                  + sum_e gg_h[e, k] gw[e, p, u]
+ * with gw, dw the per-edge weight cotangents the calls never store (the
+ * second term because grad_h = gw Wr depends on Wr). grad_Wr / d_Wr: DEVICE
+ * float [n_basis][P][C], the layout of Wr. Every other argument, output and
+ * flag as etp_edge_conv_vjp_radial / etp_edge_conv_vjp2_radial, whose results
+ * these calls reproduce up to rounding order (their path groups are cut
+ * smaller to make room for the partial sums). The sum over
+ * edges is formed per source node in the kernels (each lane its channel,
+ * the node's edge splits added in a fixed order) into ws, then added over
+ * the source nodes in index order by a two-level kernel: deterministic, no
+ * atomics. ETP_FLAG_ACCUMULATE also adds into grad_Wr / d_Wr. ws: DEVICE,
+ * 16-byte aligned, at least etp_workspace_size(plan, ETP_OP_RADIAL_WGRAD, g)
+ * bytes, contents undefined afterwards. Errors: as the calls without the
+ * weight gradient, plus WORKSPACE (ws missing, misaligned or too small). */
+ETP_API etp_status etp_edge_conv_vjp_radial_wgrad(etp_plan_t plan, const etp_graph *g, const float *vec,
+                                                  const void *x, const float *h, int32_t n_basis, const float *Wr,
+                                                  const float *grad_out, float *grad_x, float *grad_h,
+                                                  float *grad_vec, float *grad_Wr, uint32_t flags, void *ws,
+                                                  size_t ws_bytes, void *stream);
+ETP_API etp_status etp_edge_conv_vjp2_radial_wgrad(etp_plan_t plan, const etp_graph *g, const float *vec,
+                                                   const void *x, const float *h, int32_t n_basis, const float *Wr,
+                                                   const float *grad_out, const float *gg_x, const float *gg_h,
+                                                   const float *gg_vec, float *d_x, float *d_h, float *d_vec,
+                                                   float *d_grad_out, float *d_Wr, uint32_t flags, void *ws,
+                                                   size_t ws_bytes, void *stream);
 
 /* VJP of the VJP: with cotangents (gg_x, gg_w, gg_vec) on (grad_x, grad_w,
  * grad_vec), the gradients of S = <gg_x, grad_x> + <gg_w, grad_w> +
