@@ -428,6 +428,28 @@ def time_radial(etp, p, fwd_ms, vjp_ms, reps, K=8):
     vf = fl["vjp"] + 4.0 * K * P * C * E
     res.update({"vjp_ms": round(tv * 1e3, 4), "vjp_speedup_vs_vjp": round(vjp_ms * 1e-3 / tv, 3),
                 "vjp_hbm_frac": vb / tv / 1e9 / HBM_PEAK_GBS, "vjp_valu_frac": vf / tv / 1e12 / VALU_PEAK_TFLOPS})
+    # the VJP with the weight gradient (grad_Wr), and the VJP-of-VJP with and
+    # without d_Wr (cotangents on grad_x, grad_h, grad_vec)
+    wsz = etp.etp_workspace_size(p.plan, etp.ETP_OP_RADIAL_WGRAD, p.g)
+    ws = torch.empty(wsz, dtype=torch.uint8, device="cuda")
+    gWr = torch.empty_like(Wr)
+    tw = time_calls(lambda: etp.etp_edge_conv_vjp_radial_wgrad(p.plan, p.g, p.vec, p.x, h, Wr, p.G, gx, gh, gr, gWr,
+                                                               ws), reps)
+    Hp = torch.randn_like(h)
+    dx, dh, dr, dG = torch.empty_like(gx), torch.empty_like(gh), torch.empty_like(gr), torch.empty_like(p.out)
+    t2 = time_calls(lambda: etp.etp_edge_conv_vjp2_radial(p.plan, p.g, p.vec, p.x, h, Wr, p.G, p.ggx, Hp, p.ggv,
+                                                          dx, dh, dr, dG), reps)
+    t2w = time_calls(lambda: etp.etp_edge_conv_vjp2_radial_wgrad(p.plan, p.g, p.vec, p.x, h, Wr, p.G, p.ggx, Hp,
+                                                                 p.ggv, dx, dh, dr, dG, gWr, ws), reps)
+    # VJP-of-VJP bytes: the plain op's with the three E P C streams replaced by
+    # h, H', dh and Wr; FLOPs: the plain op's plus 2 K per (edge, path,
+    # channel) for each of w and W' (and dh)
+    b2 = by["vjp2"] - 12.0 * E * P * C + 4.0 * (3 * E * K + K * P * C)
+    f2 = fl["vjp2"] + 6.0 * K * P * C * E
+    res.update({"vjp_wgrad_ms": round(tw * 1e3, 4), "vjp2_ms": round(t2 * 1e3, 4),
+                "vjp2_wgrad_ms": round(t2w * 1e3, 4), "vjp2_hbm_frac": b2 / t2 / 1e9 / HBM_PEAK_GBS,
+                "vjp2_valu_frac": f2 / t2 / 1e12 / VALU_PEAK_TFLOPS})
+    del ws
     return res
 
 
@@ -450,6 +472,14 @@ def time_channel_mix(etp, plan, out, L, C, N, reps):
     gin = torch.empty_like(out)
     tv = time_calls(lambda: etp.etp_channel_mix_vjp(plan, y, W, gin), reps)
     res.update({"vjp_ms": round(tv * 1e3, 4), "vjp_mfma_frac": flops / tv / 1e12 / MFMA_F32_PEAK_TFLOPS})
+    # bf16 weights (W read at 2 bytes; its own dtype's peak)
+    Wb = W.to(torch.bfloat16)
+    tb = time_calls(lambda: etp.etp_channel_mix_ex(plan, out, Wb, y), reps, 3)
+    tbv = time_calls(lambda: etp.etp_channel_mix_vjp_ex(plan, y, Wb, gin), reps, 3)
+    bb = byts - 2.0 * W.numel()
+    res["bf16"] = {"ms": round(tb * 1e3, 4), "vjp_ms": round(tbv * 1e3, 4), "hbm_frac": bb / tb / 1e9 / HBM_PEAK_GBS,
+                   "mfma_frac": flops / tb / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                   "vjp_hbm_frac": bb / tbv / 1e9 / HBM_PEAK_GBS}
     return res
 
 
@@ -596,6 +626,16 @@ def next_ops(etp, reps):
     d["radial_micro3"] = time_radial(etp, p3, per3["fwd"], per3["vjp"], reps)
     d["channel_mix_micro3"] = time_channel_mix(etp, p3.plan, p3.out, p3.L, p3.C, p3.N, reps)
     del p3
+    # the mixing at the micro4 and diamond node counts and widths (its input
+    # is a convolution output of that shape, drawn at random here)
+    import torch
+    for name, Lm, Cm, Nm in (("micro4", 4, 128, 1024), ("diamond", 3, 128, 32768)):
+        plan = etp.etp_plan_create(Lm, Cm)
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(Nm + Lm)
+        conv = torch.randn(Nm, plan.dout_rows, Cm, generator=gen, device="cuda")
+        d["channel_mix_" + name] = time_channel_mix(etp, plan, conv, Lm, Cm, Nm, reps)
+        del conv
     for Lp, nu in ((3, 4), (4, 6)):
         d[f"node_product_l{Lp}_nu{nu}"] = time_node_product(etp, Lp, nu, reps)
     return d

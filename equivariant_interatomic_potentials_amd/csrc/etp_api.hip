@@ -14,10 +14,10 @@
 namespace etp {
 
 hipError_t launch_sh(int L, int64_t n, const float *vec, float *Y, float *dY, hipStream_t stream);
-hipError_t launch_mix(int L, int C, int n, const float *in, const float *W, float *y, bool accumulate,
+hipError_t launch_mix(int L, int C, int n, const float *in, const void *W, bool bf16, float *y, bool accumulate,
                       hipStream_t stream);
-hipError_t launch_mix_vjp(int L, int C, int n, const float *gy, const float *W, float *gin, bool accumulate,
-                          hipStream_t stream);
+hipError_t launch_mix_vjp(int L, int C, int n, const float *gy, const void *W, bool bf16, float *gin,
+                          bool accumulate, hipStream_t stream);
 hipError_t launch_node_product(int L, int C, int n, int nu, const float *A, const float *W, float *out,
                                bool accumulate, hipStream_t stream);
 // the edge-local product, one translation unit per l_max
@@ -440,9 +440,11 @@ etp_status etp_workspace_size(etp_plan_t plan, int32_t op, const etp_graph *g, s
 {
     if (!plan || !g || !bytes)
         return ETP_ERR_INVALID_ARGUMENT;
-    etp_status st = check_graph(g, false);
-    if (st != ETP_OK)
-        return st;
+    // a size query reads only the counts: the descriptor's pointers may be NULL
+    if (g->n_dst < 0 || g->n_src < 0 || g->n_edges < 0)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (g->n_edges >= kMaxEdges)
+        return ETP_ERR_UNSUPPORTED;
     switch (op) {
     case ETP_OP_FWD:
     case ETP_OP_VJP:
@@ -981,34 +983,48 @@ etp_status etp_edge_conv_vjp2(etp_plan_t plan, const etp_graph *g, const float *
     return ETP_OK;
 }
 
-etp_status etp_channel_mix(etp_plan_t plan, int32_t n_nodes, const float *in, const float *W, float *out,
-                           uint32_t flags, void *stream)
+// Both directions of the mixing: the same checks, then one launch.
+static etp_status channel_mix_call(bool vjp, etp_plan_t plan, int32_t n_nodes, const float *A, const void *W,
+                                   int32_t w_dtype, float *out, uint32_t flags, void *stream)
 {
     if (!plan || n_nodes < 0)
         return ETP_ERR_INVALID_ARGUMENT;
     if (flags & ~static_cast<uint32_t>(ETP_FLAG_ACCUMULATE))
         return ETP_ERR_INVALID_ARGUMENT;
+    if (w_dtype != ETP_F32 && w_dtype != ETP_BF16)
+        return ETP_ERR_INVALID_ARGUMENT;
     if (n_nodes == 0)
         return ETP_OK;
-    if (!in || !W || !out)
+    if (!A || !W || !out)
         return ETP_ERR_INVALID_ARGUMENT;
-    return hip_status(etp::launch_mix(plan->L, plan->C, n_nodes, in, W, out, flags & ETP_FLAG_ACCUMULATE,
-                                      static_cast<hipStream_t>(stream)));
+    const bool bf = w_dtype == ETP_BF16, acc = (flags & ETP_FLAG_ACCUMULATE) != 0;
+    const auto st = static_cast<hipStream_t>(stream);
+    return hip_status(vjp ? etp::launch_mix_vjp(plan->L, plan->C, n_nodes, A, W, bf, out, acc, st)
+                          : etp::launch_mix(plan->L, plan->C, n_nodes, A, W, bf, out, acc, st));
+}
+
+etp_status etp_channel_mix(etp_plan_t plan, int32_t n_nodes, const float *in, const float *W, float *out,
+                           uint32_t flags, void *stream)
+{
+    return channel_mix_call(false, plan, n_nodes, in, W, ETP_F32, out, flags, stream);
+}
+
+etp_status etp_channel_mix_ex(etp_plan_t plan, int32_t n_nodes, const float *in, const void *W, int32_t w_dtype,
+                              float *out, uint32_t flags, void *stream)
+{
+    return channel_mix_call(false, plan, n_nodes, in, W, w_dtype, out, flags, stream);
 }
 
 etp_status etp_channel_mix_vjp(etp_plan_t plan, int32_t n_nodes, const float *grad_y, const float *W, float *grad_in,
                                uint32_t flags, void *stream)
 {
-    if (!plan || n_nodes < 0)
-        return ETP_ERR_INVALID_ARGUMENT;
-    if (flags & ~static_cast<uint32_t>(ETP_FLAG_ACCUMULATE))
-        return ETP_ERR_INVALID_ARGUMENT;
-    if (n_nodes == 0)
-        return ETP_OK;
-    if (!grad_y || !W || !grad_in)
-        return ETP_ERR_INVALID_ARGUMENT;
-    return hip_status(etp::launch_mix_vjp(plan->L, plan->C, n_nodes, grad_y, W, grad_in, flags & ETP_FLAG_ACCUMULATE,
-                                          static_cast<hipStream_t>(stream)));
+    return channel_mix_call(true, plan, n_nodes, grad_y, W, ETP_F32, grad_in, flags, stream);
+}
+
+etp_status etp_channel_mix_vjp_ex(etp_plan_t plan, int32_t n_nodes, const float *grad_y, const void *W,
+                                  int32_t w_dtype, float *grad_in, uint32_t flags, void *stream)
+{
+    return channel_mix_call(true, plan, n_nodes, grad_y, W, w_dtype, grad_in, flags, stream);
 }
 
 etp_status etp_edge_tp_fwd(etp_plan_t plan, int64_t n_edges, const float *vec, const float *V, const float *w,

@@ -1,33 +1,47 @@
 // etp_mix.hip -- the per-irrep channel-mixing linear layer that follows the
-// convolution, on the matrix cores.
+// convolution, and its VJP, on the matrix cores.
 //
 //   y[i, l, m, v] = sum_{p: l3_p = l} sum_u W_l[(q_p C + u), v] out[i, off_p + m, u]
+//   gin[i, off_p + m, u] = sum_v W_l[(q_p C + u), v] gy[i, l*l + m, v]
 //
 // (q_p = rank of path p among the paths of output order l, in path order;
 // W = W_0, W_1, ... back to back, W_l of n_l * C rows and C columns; y has
 // the node-feature layout [n][(l_max + 1)^2][C], so it can feed the next
 // convolution.) The pages name a single dense channel contraction after the
-// tensor product ("Scaling the leading accuracy of deep equivariant models
-// to biomolecular simulations of realistic size", section "Proposed
-// method") without fixing its form; one matrix per output order, shared by
-// its 2l + 1 components, is the plainest equivariant reading.
+// tensor product, in mixed precision ("Scaling the leading accuracy of deep
+// equivariant models to biomolecular simulations of realistic size",
+// section "Proposed method"), without fixing its form; one matrix per
+// output order, shared by its 2l + 1 components, is the plainest
+// equivariant reading.
 //
-// Per order l it is one dense product [n (2l+1)] x [n_l C] times [n_l C] x C.
-// Mapping (gfx950, wave64, v_mfma_f32_16x16x4f32):
-//   * a workgroup of 4 waves owns 64 rows (node, m) of one order and 64
-//     output channels; each wave owns 16 rows and holds four 16 x 16 fp32
-//     accumulator tiles;
-//   * K runs over (path of order l, input channel) in chunks of 32 input
-//     channels: the chunk of W_l (32 x 64) is staged in a double-buffered
-//     LDS tile once per workgroup; each wave reads its A operand straight
-//     from the convolution output (lane l: row l % 16, k = l / 16 + 4 s);
-//     the next chunk's A and W values are loaded into registers while the
-//     current chunk's MFMAs run (one barrier per chunk);
-//   * fp32 in, fp32 accumulate, no atomics; rows, output channels and input
-//     channels past the problem are zero-filled or dropped.
+// Per order l the forward is one dense product [n (2l+1)] x [n_l C] times
+// [n_l C] x C; the VJP is, per path, [n (2l+1)] x C times C x C (W_{l,q}
+// transposed). Mapping (gfx950, wave64):
+//   * a workgroup owns 64 rows (node, m) of one order and 64 output
+//     channels; 4 waves of 16 rows each hold four 16 x 16 fp32 accumulator
+//     tiles; with KW > 1, KW groups of 4 such waves share the tile and take
+//     alternate chunks of K, and groups 1.. hand their tiles to group 0
+//     through LDS at the end, added in group order (more waves per SIMD and
+//     shorter chains on small grids; the result does not depend on timing);
+//   * K runs in chunks of 32 channels. Lane (row r = lane % 16, quarter
+//     kq = lane / 16) loads the 8 consecutive channels 8 kq .. 8 kq + 7 of
+//     the chunk from its A row (two 16-byte loads); the chunk of W (32 x 64)
+//     is staged in a double-buffered LDS tile Bt[column][k] (transposed for
+//     the forward, whose W rows run along the output channel; as read for
+//     the VJP, whose W rows run along k) so that a lane reads its 8 k values
+//     of a column as one 16-byte LDS read; the next chunk is loaded into
+//     registers while the current one's products run (one barrier per
+//     chunk);
+//   * fp32 weights: 8 v_mfma_f32_16x16x4f32 per column tile and chunk (step
+//     i takes channel 8 kq + i of the chunk); bf16 weights: A is rounded to
+//     bf16 (nearest even) in registers and one v_mfma_f32_16x16x32_bf16 per
+//     column tile and chunk takes all 32 channels; fp32 accumulation in
+//     both, no atomics; rows, columns and channels past the problem are
+//     zero-filled or dropped.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "etp_tables.hpp"
 
@@ -44,80 +58,236 @@ struct MixTab {
 };
 
 typedef float mix_f4 __attribute__((ext_vector_type(4)));
+typedef __bf16 mix_bf8 __attribute__((ext_vector_type(8)));
 
 constexpr int kMixCols = 64;  // output channels per workgroup
 
-__global__ void __launch_bounds__(256) mix_kernel(const MixTab tb, const float *__restrict__ in,
-                                                  const float *__restrict__ W, float *__restrict__ y,
-                                                  const int accumulate)
+__device__ __forceinline__ uint16_t mix_f2bf(float f)
 {
-    __shared__ float Bs[2][32][kMixCols + 4];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    // round to nearest even (finite inputs)
+    const uint32_t u = __float_as_uint(f);
+    return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// VJP = false: blockIdx = (64-row tile over the orders, column tile); K over
+// (path of the order, input channel u). VJP = true: blockIdx = (tile, column
+// tile, path q of the order); K over the output channel v.
+template <bool BF, int KW, bool VJP>
+__global__ void __launch_bounds__(256 * KW) mix2_kernel(const MixTab tb, const float *__restrict__ A,
+                                                        const void *__restrict__ Wv, float *__restrict__ out,
+                                                        const int accumulate)
+{
+    constexpr int KS = BF ? 40 : 36;  // Bt row stride (elements): 16-byte aligned rows
+    using BT = std::conditional_t<BF, uint16_t, float>;
+    constexpr int kBtBytes = 2 * KW * kMixCols * KS * static_cast<int>(sizeof(BT));
+    constexpr int kRedBytes = (KW - 1) * 16 * 64 * 16;  // K-group tiles (a float4 per lane and tile)
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kBtBytes > kRedBytes ? kBtBytes : kRedBytes];
+    auto Bt = reinterpret_cast<BT (*)[KW][kMixCols][KS]>(smem);
+    // the wave index, known to the compiler as uniform over the wave (so are
+    // the chunk, path and order indices that follow from it)
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rg = wv & 3, kg = wv >> 2;  // row group of 16 rows, K group
     int l = 0;
     while (l < tb.lout && static_cast<int>(blockIdx.x) >= tb.tiles0[l + 1])
         ++l;
+    const int qv = VJP ? static_cast<int>(blockIdx.z) : 0;
+    if (VJP && qv >= tb.nl[l])
+        return;  // the whole workgroup: this order has fewer paths
     const int tile = blockIdx.x - tb.tiles0[l];
     const int d = 2 * l + 1, M = tb.n * d, C = tb.C;
     const int c0 = blockIdx.y * kMixCols;
     const int kq = lane >> 4, col = lane & 15;
 
-    // this lane's A row
-    const int ra = tile * 64 + wv * 16 + col;
+    const int ra = tile * 64 + rg * 16 + col;
     const bool rok = ra < M;
     const int ia = rok ? ra / d : 0, ma = rok ? ra - ia * d : 0;
-    const float *abase = in + (static_cast<int64_t>(ia) * tb.Dout + ma) * C;
+    // A rows: the convolution output's rows (forward; the path's block is
+    // added per chunk) or the cotangent's order-l rows (VJP)
+    const float *abase = VJP ? A + (static_cast<int64_t>(ia) * tb.Dy + l * l + ma) * C
+                             : A + (static_cast<int64_t>(ia) * tb.Dout + ma) * C;
+    const bool vec4 = (C & 3) == 0 && (reinterpret_cast<uintptr_t>(A) & 15u) == 0;
 
     mix_f4 acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
         acc[t] = mix_f4{0.f, 0.f, 0.f, 0.f};
 
-    // K in chunks of 32 input channels of one path: chunk ci = (q, u0).
-    // The next chunk's A and W values are loaded into registers while the
-    // current chunk's MFMAs run; W goes through a double-buffered LDS tile.
-    const int ncu = (C + 31) / 32, nchunk = tb.nl[l] * ncu;
-    constexpr int BPT = 32 * kMixCols / 256;  // W values staged per thread
-    float a_nx[8], b_nx[BPT];
+    // K group kg takes chunks kg, kg + KW, ...; every wave runs the same
+    // number of iterations (one barrier each)
+    const int ncu = (C + 31) / 32, nchunk = VJP ? ncu : tb.nl[l] * ncu, nit = (nchunk + KW - 1) / KW;
+    float a_nx[8];
+    BT b_nx[8];
+    // W staging, thread t of a K group (t < 256):
+    //   forward fp32: W rows k0 + t / 16 and + 16, columns 4 (t % 16) .. + 3
+    //   forward bf16: W row k0 + t / 8, columns 8 (t % 8) .. + 7
+    //   VJP:          W row c0 + t % 64, entries k0 + 8 ((t / 64) % 4) .. + 7
+    const int t8 = threadIdx.x & 255;
+    const int sr = VJP ? t8 & 63 : (BF ? t8 >> 3 : t8 >> 4);        // W row (within the chunk or tile)
+    const int sc = VJP ? (t8 >> 6) * 8 : (BF ? 8 * (t8 & 7) : 4 * (t8 & 15));  // first W column
+    const bool wal = (C & 7) == 0 && (reinterpret_cast<uintptr_t>(Wv) & 15u) == 0;
     auto fetch = [&](int ci) {
-        const int q = ci / ncu, u0 = (ci - q * ncu) * 32;
-        const float *arow = abase + static_cast<int64_t>(tb.off[l][q]) * C;
-        const float *Wq = W + tb.wofs[l] + static_cast<int64_t>(q) * C * C;
+        if (ci >= nchunk) {
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int u = u0 + 4 * s + kq;
-            a_nx[s] = (rok && u < C) ? arow[u] : 0.f;
+            for (int i = 0; i < 8; ++i) {
+                a_nx[i] = 0.f;
+                b_nx[i] = BT(0);
+            }
+            return;
         }
+        const int q = VJP ? qv : ci / ncu, k0 = (VJP ? ci : ci % ncu) * 32;
+        const float *arow = VJP ? abase : abase + static_cast<int64_t>(tb.off[l][q]) * C;
+        const int kb = k0 + 8 * kq;
+        if (rok && vec4 && kb + 8 <= C) {
+            const float4 v0 = *reinterpret_cast<const float4 *>(arow + kb);
+            const float4 v1 = *reinterpret_cast<const float4 *>(arow + kb + 4);
+            a_nx[0] = v0.x; a_nx[1] = v0.y; a_nx[2] = v0.z; a_nx[3] = v0.w;
+            a_nx[4] = v1.x; a_nx[5] = v1.y; a_nx[6] = v1.z; a_nx[7] = v1.w;
+        } else {
 #pragma unroll
-        for (int k = 0; k < BPT; ++k) {
-            const int t = threadIdx.x + 256 * k;
-            const int kr = t / kMixCols, cc = t % kMixCols;
-            const int u = u0 + kr, c = c0 + cc;
-            b_nx[k] = (u < C && c < C) ? Wq[static_cast<int64_t>(u) * C + c] : 0.f;
+            for (int i = 0; i < 8; ++i) {
+                const bool ok = rok && kb + i < C;
+                const float v = arow[ok ? kb + i : 0];  // in bounds either way
+                a_nx[i] = ok ? v : 0.f;
+            }
+        }
+        const BT *W = static_cast<const BT *>(Wv) + tb.wofs[l] + static_cast<int64_t>(q) * C * C;
+        // element (row, col) of the chunk's W block for this thread, zero past
+        // the problem; loads stay in bounds (index 0 when out)
+        auto wat = [&](int row, int col) -> BT {
+            const bool ok = row < C && col < C;
+            const BT v = W[ok ? static_cast<int64_t>(row) * C + col : 0];
+            return ok ? v : BT(0);
+        };
+        if constexpr (VJP) {
+            const int row = c0 + sr, col = k0 + sc;
+            if (wal && row < C && col + 8 <= C) {
+                const BT *src = W + static_cast<int64_t>(row) * C + col;
+                if constexpr (BF) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(src);
+                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        b_nx[2 * i] = static_cast<uint16_t>(w4[i] & 0xFFFFu);
+                        b_nx[2 * i + 1] = static_cast<uint16_t>(w4[i] >> 16);
+                    }
+                } else {
+                    const float4 v0 = *reinterpret_cast<const float4 *>(src);
+                    const float4 v1 = *reinterpret_cast<const float4 *>(src + 4);
+                    b_nx[0] = v0.x; b_nx[1] = v0.y; b_nx[2] = v0.z; b_nx[3] = v0.w;
+                    b_nx[4] = v1.x; b_nx[5] = v1.y; b_nx[6] = v1.z; b_nx[7] = v1.w;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    b_nx[i] = wat(row, col + i);
+            }
+        } else if constexpr (BF) {
+            const int row = k0 + sr, col = c0 + sc;
+            if (wal && row < C && col + 8 <= C) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(W + static_cast<int64_t>(row) * C + col);
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    b_nx[2 * i] = static_cast<uint16_t>(w4[i] & 0xFFFFu);
+                    b_nx[2 * i + 1] = static_cast<uint16_t>(w4[i] >> 16);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    b_nx[i] = wat(row, col + i);
+            }
+        } else {
+            const int row = k0 + sr, col = c0 + sc;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int rh = row + 16 * h;
+                if (wal && rh < C && col + 4 <= C) {
+                    const float4 v = *reinterpret_cast<const float4 *>(W + static_cast<int64_t>(rh) * C + col);
+                    b_nx[4 * h] = v.x; b_nx[4 * h + 1] = v.y; b_nx[4 * h + 2] = v.z; b_nx[4 * h + 3] = v.w;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        b_nx[4 * h + j] = wat(rh, col + j);
+                }
+            }
         }
     };
-    fetch(0);
-    for (int ci = 0; ci < nchunk; ++ci) {
-        const int buf = ci & 1;
+    // b_nx into the LDS tile Bt[column][k] of this K group
+    auto stage = [&](int buf) {
+        if constexpr (VJP) {
 #pragma unroll
-        for (int k = 0; k < BPT; ++k) {
-            const int t = threadIdx.x + 256 * k;
-            Bs[buf][t / kMixCols][t % kMixCols] = b_nx[k];
+            for (int i = 0; i < 8; ++i)
+                Bt[buf][kg][sr][sc + i] = b_nx[i];
+        } else if constexpr (BF) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                Bt[buf][kg][sc + i][sr] = b_nx[i];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                Bt[buf][kg][sc + j][sr] = b_nx[j];
+                Bt[buf][kg][sc + j][sr + 16] = b_nx[4 + j];
+            }
         }
+    };
+    if (nit > 0)
+        fetch(kg);
+    for (int it = 0; it < nit; ++it) {
+        const int buf = it & 1;
+        const bool live = it * KW + kg < nchunk;  // uniform over the wave
+        stage(buf);
         float a[8];
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-            a[s] = a_nx[s];
-        // one barrier per chunk: the stores above are seen by every wave,
-        // and the buffer written next (buf ^ 1) was last read before it
+        for (int i = 0; i < 8; ++i)
+            a[i] = a_nx[i];
+        // one barrier per iteration: the tile stores above are seen by every
+        // wave, and the buffer written next (buf ^ 1) was last read before it
         __syncthreads();
-        if (ci + 1 < nchunk)
-            fetch(ci + 1);
+        if (it + 1 < nit)
+            fetch((it + 1) * KW + kg);
+        if (!live)
+            continue;
+        if constexpr (BF) {
+            mix_bf8 av;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
+            for (int i = 0; i < 8; ++i)
+                av[i] = __builtin_bit_cast(__bf16, mix_f2bf(a[i]));
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const mix_bf8 bv = *reinterpret_cast<const mix_bf8 *>(&Bt[buf][kg][16 * t + col][8 * kq]);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[t], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float4 b0 = *reinterpret_cast<const float4 *>(&Bt[buf][kg][16 * t + col][8 * kq]);
+                const float4 b1 = *reinterpret_cast<const float4 *>(&Bt[buf][kg][16 * t + col][8 * kq + 4]);
+                const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], bb[i], acc[t], 0, 0, 0);
+            }
+        }
+    }
+
+    if constexpr (KW > 1) {
+        // K groups 1.. hand their tiles to group 0 through LDS (reusing the
+        // staging space); group 0 adds them in group order
+        auto red = reinterpret_cast<mix_f4 (*)[4][4][64]>(smem);
+        __syncthreads();
+        if (kg > 0) {
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], Bs[buf][4 * s + kq][16 * t + col], acc[t], 0,
-                                                              0, 0);
+                red[kg - 1][rg][t][lane] = acc[t];
+        }
+        __syncthreads();
+        if (kg > 0)
+            return;
+#pragma unroll
+        for (int g = 1; g < KW; ++g) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                acc[t] += red[g - 1][rg][t][lane];
         }
     }
 
@@ -127,101 +297,12 @@ __global__ void __launch_bounds__(256) mix_kernel(const MixTab tb, const float *
         const int c = c0 + 16 * t + col;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-            const int r = tile * 64 + wv * 16 + 4 * kq + rr;
+            const int r = tile * 64 + rg * 16 + 4 * kq + rr;
             if (r < M && c < C) {
                 const int i = r / d, m = r - (r / d) * d;
-                float *dst = y + (static_cast<int64_t>(i) * tb.Dy + l * l + m) * C + c;
-                *dst = accumulate ? *dst + acc[t][rr] : acc[t][rr];
-            }
-        }
-    }
-}
-
-// VJP with respect to the input (the mixing is linear: the transposed map):
-//   gin[i, off_p + m, u] = sum_v W_l[(q_p C + u), v] gy[i, l*l + m, v]
-// per order l and path q one product [n (2l+1)] x C times C x C (W_{l,q}
-// transposed). Same tiling as the forward; blockIdx.y = (path q of order l,
-// 64-column tile); the W chunk is read along v (contiguous) and transposed
-// into the LDS tile.
-__global__ void __launch_bounds__(256) mix_vjp_kernel(const MixTab tb, const float *__restrict__ gy,
-                                                      const float *__restrict__ W, float *__restrict__ gin,
-                                                      const int accumulate)
-{
-    __shared__ float Bs[2][32][kMixCols + 4];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    int l = 0;
-    while (l < tb.lout && static_cast<int>(blockIdx.x) >= tb.tiles0[l + 1])
-        ++l;
-    const int C = tb.C, ntc = (C + kMixCols - 1) / kMixCols;
-    const int q = blockIdx.y / ntc, c0 = (blockIdx.y - q * ntc) * kMixCols;
-    if (q >= tb.nl[l])
-        return;  // the whole workgroup: this order has fewer paths
-    const int tile = blockIdx.x - tb.tiles0[l];
-    const int d = 2 * l + 1, M = tb.n * d;
-    const int kq = lane >> 4, col = lane & 15;
-
-    const int ra = tile * 64 + wv * 16 + col;
-    const bool rok = ra < M;
-    const int ia = rok ? ra / d : 0, ma = rok ? ra - ia * d : 0;
-    const float *arow = gy + (static_cast<int64_t>(ia) * tb.Dy + l * l + ma) * C;
-    const float *Wq = W + tb.wofs[l] + static_cast<int64_t>(q) * C * C;
-
-    mix_f4 acc[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-        acc[t] = mix_f4{0.f, 0.f, 0.f, 0.f};
-
-    const int nchunk = (C + 31) / 32;
-    constexpr int BPT = 32 * kMixCols / 256;
-    float a_nx[8], b_nx[BPT];
-    auto fetch = [&](int ci) {
-        const int v0 = ci * 32;
-#pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8) {
-            const int v = v0 + 4 * s8 + kq;
-            a_nx[s8] = (rok && v < C) ? arow[v] : 0.f;
-        }
-#pragma unroll
-        for (int k = 0; k < BPT; ++k) {
-            const int t = threadIdx.x + 256 * k;
-            const int kr = t & 31, cc = t >> 5;  // consecutive threads read consecutive v
-            const int v = v0 + kr, u = c0 + cc;
-            b_nx[k] = (v < C && u < C) ? Wq[static_cast<int64_t>(u) * C + v] : 0.f;
-        }
-    };
-    fetch(0);
-    for (int ci = 0; ci < nchunk; ++ci) {
-        const int buf = ci & 1;
-#pragma unroll
-        for (int k = 0; k < BPT; ++k) {
-            const int t = threadIdx.x + 256 * k;
-            Bs[buf][t & 31][t >> 5] = b_nx[k];
-        }
-        float a[8];
-#pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8)
-            a[s8] = a_nx[s8];
-        __syncthreads();
-        if (ci + 1 < nchunk)
-            fetch(ci + 1);
-#pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s8], Bs[buf][4 * s8 + kq][16 * t + col], acc[t], 0,
-                                                              0, 0);
-        }
-    }
-
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int c = c0 + 16 * t + col;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int r = tile * 64 + wv * 16 + 4 * kq + rr;
-            if (r < M && c < C) {
-                const int i = r / d, m = r - (r / d) * d;
-                float *dst = gin + (static_cast<int64_t>(i) * tb.Dout + tb.off[l][q] + m) * C + c;
+                const int64_t row = VJP ? static_cast<int64_t>(i) * tb.Dout + tb.off[l][qv] + m
+                                        : static_cast<int64_t>(i) * tb.Dy + l * l + m;
+                float *dst = out + row * C + c;
                 *dst = accumulate ? *dst + acc[t][rr] : acc[t][rr];
             }
         }
@@ -265,33 +346,63 @@ static bool mix_table_for(int L, int C, int n, MixTab *tb)
     }
 }
 
-hipError_t launch_mix(int L, int C, int n, const float *in, const float *W, float *y, bool accumulate,
-                      hipStream_t stream)
+// K groups per workgroup: more waves per SIMD and shorter chains when the
+// grid alone would leave the SIMDs with one or two waves each (chosen from
+// timings of the micro, water and diamond shapes).
+static int mix_kgroups(int64_t wgs)
+{
+    return wgs >= 2048 ? 1 : (wgs >= 640 ? 2 : 4);
+}
+
+template <bool VJP>
+static hipError_t launch_mix2(int L, int C, int n, const float *A, const void *W, bool bf16, float *out,
+                              bool accumulate, hipStream_t stream)
 {
     if (n == 0)
         return hipSuccess;
     MixTab tb;
     if (!mix_table_for(L, C, n, &tb))
         return hipErrorInvalidValue;
-    const dim3 grid(tb.tiles0[L + 1], (C + kMixCols - 1) / kMixCols);
-    hipLaunchKernelGGL(mix_kernel, grid, dim3(256), 0, stream, tb, in, W, y, accumulate ? 1 : 0);
+    int maxnl = 1;
+    for (int l = 0; l <= L; ++l)
+        maxnl = tb.nl[l] > maxnl ? tb.nl[l] : maxnl;
+    const dim3 grid(tb.tiles0[L + 1], (C + kMixCols - 1) / kMixCols, VJP ? maxnl : 1);
+    int64_t live = static_cast<int64_t>(grid.y) * (VJP ? 0 : grid.x);
+    if (VJP)  // workgroups past an order's path count leave at once
+        for (int l = 0; l <= L; ++l)
+            live += static_cast<int64_t>(grid.y) * (tb.tiles0[l + 1] - tb.tiles0[l]) * tb.nl[l];
+    const int kw = mix_kgroups(live), acc = accumulate ? 1 : 0;
+#define ETP_MIX2(BF, KWV)                                                                                            \
+    hipLaunchKernelGGL((mix2_kernel<BF, KWV, VJP>), grid, dim3(256 * KWV), 0, stream, tb, A, W, out, acc)
+    if (bf16) {
+        if (kw == 4)
+            ETP_MIX2(true, 4);
+        else if (kw == 2)
+            ETP_MIX2(true, 2);
+        else
+            ETP_MIX2(true, 1);
+    } else {
+        if (kw == 4)
+            ETP_MIX2(false, 4);
+        else if (kw == 2)
+            ETP_MIX2(false, 2);
+        else
+            ETP_MIX2(false, 1);
+    }
+#undef ETP_MIX2
     return hipGetLastError();
 }
 
-hipError_t launch_mix_vjp(int L, int C, int n, const float *gy, const float *W, float *gin, bool accumulate,
-                          hipStream_t stream)
+hipError_t launch_mix(int L, int C, int n, const float *in, const void *W, bool bf16, float *y, bool accumulate,
+                      hipStream_t stream)
 {
-    if (n == 0)
-        return hipSuccess;
-    MixTab tb;
-    if (!mix_table_for(L, C, n, &tb))
-        return hipErrorInvalidValue;
-    int maxnl = 0;
-    for (int l = 0; l <= L; ++l)
-        maxnl = tb.nl[l] > maxnl ? tb.nl[l] : maxnl;
-    const dim3 grid(tb.tiles0[L + 1], maxnl * ((C + kMixCols - 1) / kMixCols));
-    hipLaunchKernelGGL(mix_vjp_kernel, grid, dim3(256), 0, stream, tb, gy, W, gin, accumulate ? 1 : 0);
-    return hipGetLastError();
+    return launch_mix2<false>(L, C, n, in, W, bf16, y, accumulate, stream);
+}
+
+hipError_t launch_mix_vjp(int L, int C, int n, const float *gy, const void *W, bool bf16, float *gin,
+                          bool accumulate, hipStream_t stream)
+{
+    return launch_mix2<true>(L, C, n, gy, W, bf16, gin, accumulate, stream);
 }
 
 }  // namespace etp

@@ -38,7 +38,7 @@ ABI_SYMBOLS = ("etp_plan_create", "etp_plan_destroy", "etp_plan_info", "etp_plan
                "etp_neighbor_workspace", "etp_neighbor_count", "etp_neighbor_fill", "etp_node_product", "etp_node_product_vjp", "etp_channel_mix_vjp",
                "etp_edge_tp_fwd", "etp_edge_tp_vjp", "etp_edge_tp_vjp2",
                "etp_csr_transpose_noalloc", "etp_edge_conv_vjp_ws", "etp_edge_conv_vjp2_ws",
-               "etp_edge_conv_vjp_radial_wgrad", "etp_edge_conv_vjp2_radial_wgrad",
+               "etp_edge_conv_vjp_radial_wgrad", "etp_edge_conv_vjp2_radial_wgrad", "etp_channel_mix_ex", "etp_channel_mix_vjp_ex",
                "etp_status_string", "etp_version")
 
 
@@ -124,6 +124,8 @@ def _load():
         "etp_edge_conv_vjp2_ws": (st, [vp, ctypes.POINTER(etp_graph), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        vp, u32, vp, ctypes.c_size_t, vp]),
         "etp_channel_mix": (st, [vp, i32, vp, vp, vp, u32, vp]),
+        "etp_channel_mix_ex": (st, [vp, i32, vp, vp, i32, vp, u32, vp]),
+        "etp_channel_mix_vjp_ex": (st, [vp, i32, vp, vp, i32, vp, u32, vp]),
         "etp_edge_forces": (st, [ctypes.POINTER(etp_graph), vp, vp, u32, vp]),
         "etp_node_product": (st, [vp, i32, i32, vp, vp, vp, u32, vp]),
         "etp_channel_mix_vjp": (st, [vp, i32, vp, vp, vp, u32, vp]),
@@ -575,6 +577,21 @@ def etp_channel_mix(plan: Plan, inp, W, out, flags: int = 0, stream=None):
                                flags, _stream(stream)), "etp_channel_mix")
 
 
+def etp_channel_mix_ex(plan: Plan, inp, W, out, flags: int = 0, stream=None):
+    """etp_channel_mix with W in fp32 or bf16 (its torch dtype picks)."""
+    import torch
+    C = plan.C
+    n = inp.shape[0] if inp is not None else 0
+    nw = sum(mix_rows(plan)) * C * C
+    bf = W is not None and W.dtype == torch.bfloat16
+    _check(lib.etp_channel_mix_ex(plan.handle, n,
+                                  _ptr(inp, "in", torch.float32, n * plan.dout_rows * C, optional=True),
+                                  _ptr(W, "W", torch.bfloat16 if bf else torch.float32, nw, optional=True),
+                                  ETP_BF16 if bf else ETP_F32,
+                                  _ptr(out, "out", torch.float32, n * (plan.L + 1) ** 2 * C, optional=True),
+                                  flags, _stream(stream)), "etp_channel_mix_ex")
+
+
 def etp_channel_mix_vjp(plan: Plan, grad_y, W, grad_in, flags: int = 0, stream=None):
     """grad_in[n, Dout, C] = the transposed mixing of grad_y[n, (L+1)^2, C]."""
     import torch
@@ -585,6 +602,21 @@ def etp_channel_mix_vjp(plan: Plan, grad_y, W, grad_in, flags: int = 0, stream=N
                                    _ptr(W, "W", torch.float32, sum(mix_rows(plan)) * C * C, optional=True),
                                    _ptr(grad_in, "grad_in", torch.float32, n * plan.dout_rows * C, optional=True),
                                    flags, _stream(stream)), "etp_channel_mix_vjp")
+
+
+def etp_channel_mix_vjp_ex(plan: Plan, grad_y, W, grad_in, flags: int = 0, stream=None):
+    """etp_channel_mix_vjp with W in fp32 or bf16 (its torch dtype picks)."""
+    import torch
+    n = grad_y.shape[0] if grad_y is not None else 0
+    C = plan.C
+    bf = W is not None and W.dtype == torch.bfloat16
+    _check(lib.etp_channel_mix_vjp_ex(plan.handle, n,
+                                      _ptr(grad_y, "grad_y", torch.float32, n * (plan.L + 1) ** 2 * C, optional=True),
+                                      _ptr(W, "W", torch.bfloat16 if bf else torch.float32,
+                                           sum(mix_rows(plan)) * C * C, optional=True),
+                                      ETP_BF16 if bf else ETP_F32,
+                                      _ptr(grad_in, "grad_in", torch.float32, n * plan.dout_rows * C, optional=True),
+                                      flags, _stream(stream)), "etp_channel_mix_vjp_ex")
 
 
 def etp_edge_forces(graph: Graph, grad_vec, forces, flags: int = 0, stream=None):

@@ -230,8 +230,8 @@ ETP_API etp_status etp_csr_transpose_noalloc(const etp_graph *g, int32_t *src_pt
  * ETP_OP_RADIAL_WGRAD (the radial weight gradients) needs
  * (n_src + 64) * ETP_MAX_RADIAL_BASIS * P * C * 4 (per-source-node partials
  * and the runs of their ordered sum).
- * Host only.
- * Errors: INVALID_ARGUMENT (null pointers, a malformed graph descriptor, an
+ * Host only; reads only the counts in g (its pointers may be NULL).
+ * Errors: INVALID_ARGUMENT (null plan, g or bytes, a negative count, an
  * unknown op), UNSUPPORTED (n_edges >= 2^31). */
 enum {
     ETP_OP_FWD = 0,
@@ -431,6 +431,19 @@ ETP_API etp_status etp_edge_conv_vjp2(etp_plan_t plan, const etp_graph *g, const
 ETP_API etp_status etp_channel_mix(etp_plan_t plan, int32_t n_nodes, const float *in, const float *W, float *out,
                                    uint32_t flags, void *stream);
 
+/* etp_channel_mix with a choice of weight precision (the pages run the
+ * dense contraction after the tensor product in mixed precision: "Scaling
+ * the leading accuracy of deep equivariant models to biomolecular
+ * simulations of realistic size", section "Proposed method"). W: DEVICE, the
+ * layout of etp_channel_mix, in w_dtype: ETP_F32 (fp32 matrix-core products,
+ * 16x16x4: the result of etp_channel_mix, bit for bit) or ETP_BF16 (raw
+ * bfloat16; the fp32 input is rounded to bf16, nearest even, as it is
+ * loaded, and 16x16x32 bf16 matrix-core products accumulate in fp32). in,
+ * out and flags as etp_channel_mix; nothing is allocated. Errors:
+ * INVALID_ARGUMENT (as etp_channel_mix, or an unknown w_dtype), HIP. */
+ETP_API etp_status etp_channel_mix_ex(etp_plan_t plan, int32_t n_nodes, const float *in, const void *W, int32_t w_dtype,
+                                      float *out, uint32_t flags, void *stream);
+
 /* VJP of etp_channel_mix with respect to its input (the mixing is linear, so
  * this is the transposed map; forces flow through it):
  *   grad_in[i][off_p + m][u] = sum_v W_l[(q_p*C + u)*C + v] * grad_y[i][l*l + m][v]
@@ -441,6 +454,13 @@ ETP_API etp_status etp_channel_mix(etp_plan_t plan, int32_t n_nodes, const float
  * grad_in. Errors as for etp_channel_mix. */
 ETP_API etp_status etp_channel_mix_vjp(etp_plan_t plan, int32_t n_nodes, const float *grad_y, const float *W,
                                        float *grad_in, uint32_t flags, void *stream);
+
+/* etp_channel_mix_vjp with W in w_dtype (ETP_F32: the result of
+ * etp_channel_mix_vjp, bit for bit; ETP_BF16: grad_y rounded to bf16 as it
+ * is loaded, bf16 matrix-core products, fp32 accumulation), as
+ * etp_channel_mix_ex is to etp_channel_mix. Errors as etp_channel_mix_ex. */
+ETP_API etp_status etp_channel_mix_vjp_ex(etp_plan_t plan, int32_t n_nodes, const float *grad_y, const void *W,
+                                          int32_t w_dtype, float *grad_in, uint32_t flags, void *stream);
 
 /* Edge-local tensor product: the convolution's message without the
  * destination sum, one output block per edge (the pair-wise tensor product of

@@ -1,13 +1,14 @@
-"""GPU parity of the channel-mixing layer (etp_channel_mix, matrix cores)
-against the float64 oracle; bar 1e-5 per output tensor (max |gpu - oracle| /
-max |oracle|)."""
+"""GPU parity of the channel-mixing layer and its VJP (etp_channel_mix*,
+matrix cores) against the float64 oracle; bar 1e-5 per output tensor (max
+|gpu - oracle| / max |oracle|), and for bf16 weights 1e-5 against the oracle
+fed the bf16-rounded operands and 1e-2 against the unrounded ones."""
 import numpy as np
 import pytest
 
 import oracle
 import workloads
 
-from gpu_common import FP32_TOL, dev, np_, rel_err
+from gpu_common import BF16_TOL, FP32_TOL, dev, np_, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -86,3 +87,63 @@ def test_channel_mix_vjp(L, C, n):
     acc = dev(base)
     etp.etp_channel_mix_vjp(plan, dev(gy), dev(W), acc, etp.ETP_FLAG_ACCUMULATE)
     assert rel_err(np_(acc), ref + base) < FP32_TOL
+
+
+# ------------------------------------------------------ weight precision
+
+def _bf16_round(a):
+    """Round float32 values to bfloat16 (nearest even) and back, as torch does."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).float().numpy()
+
+
+@pytest.mark.parametrize("L,C,n", [(0, 8, 5), (1, 64, 37), (2, 128, 100), (2, 96, 70), (3, 130, 33),
+                                   (4, 64, 21), (2, 1, 9), (3, 200, 50), (2, 64, 20000), (2, 128, 6000)])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_channel_mix_ex(L, C, n, bf16):
+    """etp_channel_mix_ex and etp_channel_mix_vjp_ex: fp32 weights within 1e-5
+    of the oracle and bit for bit the fixed-precision entries; bf16 weights
+    (the A operand rounded to bf16 in the kernel) within 1e-5 of the oracle
+    fed the rounded values and 1e-2 of the unrounded; accumulation adds; run
+    twice, bitwise equal. The shapes span grids of a few workgroups to a few
+    thousand (the number of waves sharing an output tile follows the grid)."""
+    import torch
+    from equivariant_interatomic_potentials_amd import etp
+    say("mix_ex", L, C, n, bf16)
+    inp, W = mix_case(L, C, n, seed=L * 100 + C + n + 7)
+    plan = etp.etp_plan_create(L, C)
+    Wd = dev(W).to(torch.bfloat16) if bf16 else dev(W)
+    out = torch.empty(n, (L + 1) ** 2, C, device="cuda")
+    etp.etp_channel_mix_ex(plan, dev(inp), Wd, out)
+    got = np_(out)
+    if bf16:
+        ref_r = oracle.channel_mix(L, _bf16_round(inp), _bf16_round(W))
+        assert rel_err(got, ref_r) < FP32_TOL, rel_err(got, ref_r)
+        assert rel_err(got, oracle.channel_mix(L, inp, W)) < BF16_TOL
+    else:
+        assert rel_err(got, oracle.channel_mix(L, inp, W)) < FP32_TOL
+        plain = torch.empty_like(out)
+        etp.etp_channel_mix(plan, dev(inp), dev(W), plain)
+        assert torch.equal(plain, out)
+    acc = out.clone()
+    etp.etp_channel_mix_ex(plan, dev(inp), Wd, acc, etp.ETP_FLAG_ACCUMULATE)
+    assert rel_err(np_(acc), 2 * got) < FP32_TOL
+    again = torch.empty_like(out)
+    etp.etp_channel_mix_ex(plan, dev(inp), Wd, again)
+    assert torch.equal(again, out)
+
+    gy = workloads.rng(n + 11, "G").standard_normal((n, (L + 1) ** 2, C)).astype(np.float32)
+    gin = torch.empty(n, plan.dout_rows, C, device="cuda")
+    etp.etp_channel_mix_vjp_ex(plan, dev(gy), Wd, gin)
+    if bf16:
+        ref_r = oracle.channel_mix_vjp(L, _bf16_round(gy), _bf16_round(W))
+        assert rel_err(np_(gin), ref_r) < FP32_TOL
+        assert rel_err(np_(gin), oracle.channel_mix_vjp(L, gy, W)) < BF16_TOL
+    else:
+        assert rel_err(np_(gin), oracle.channel_mix_vjp(L, gy, W)) < FP32_TOL
+        plain = torch.empty_like(gin)
+        etp.etp_channel_mix_vjp(plan, dev(gy), dev(W), plain)
+        assert torch.equal(plain, gin)
+    g2 = gin.clone()
+    etp.etp_channel_mix_vjp_ex(plan, dev(gy), Wd, g2, etp.ETP_FLAG_ACCUMULATE)
+    assert rel_err(np_(g2), 2 * np_(gin)) < FP32_TOL

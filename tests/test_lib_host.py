@@ -32,7 +32,7 @@ def header_symbols():
 
 def test_header_symbols_exported():
     names = header_symbols()
-    assert len(names) == 33
+    assert len(names) == 35
     assert sorted(etp.ABI_SYMBOLS) == names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (etp_\w+)$", out, flags=re.M))
@@ -162,6 +162,14 @@ def test_call_validation_without_device():
     assert lib.etp_channel_mix(plan.handle, 4, None, 8, 8, 0, None) == INV
     assert lib.etp_channel_mix(plan.handle, 4, 8, 8, 8, 2, None) == INV      # only ACCUMULATE
     assert lib.etp_channel_mix(plan.handle, 0, None, None, None, 0, None) == 0
+    F32, BF = etp.ETP_F32, etp.ETP_BF16
+    for fn in (lib.etp_channel_mix_ex, lib.etp_channel_mix_vjp_ex):
+        assert fn(None, 4, 8, 8, F32, 8, 0, None) == INV
+        assert fn(plan.handle, -1, 8, 8, F32, 8, 0, None) == INV
+        assert fn(plan.handle, 4, 8, None, BF, 8, 0, None) == INV
+        assert fn(plan.handle, 4, 8, 8, 5, 8, 0, None) == INV   # unknown dtype
+        assert fn(plan.handle, 4, 8, 8, F32, 8, 2, None) == INV
+        assert fn(plan.handle, 0, None, None, BF, None, 0, None) == 0
     assert lib.etp_channel_mix_vjp(None, 4, 8, 8, 8, 0, None) == INV
     assert lib.etp_channel_mix_vjp(plan.handle, 4, 8, None, 8, 0, None) == INV
     assert lib.etp_channel_mix_vjp(plan.handle, 4, 8, 8, 8, 2, None) == INV
@@ -234,6 +242,11 @@ def test_call_validation_without_device():
     assert lib.etp_workspace_size(plan.handle, 9, ctypes.byref(g6), ctypes.byref(wsb)) == INV
     assert lib.etp_workspace_size(None, 0, ctypes.byref(g6), ctypes.byref(wsb)) == INV
     assert lib.etp_workspace_size(plan.handle, 0, ctypes.byref(g2), ctypes.byref(wsb)) == UNS
+    # a size query reads only the counts
+    g7 = etp.etp_graph(1000, 0, 0, None, None, None, None, None)
+    assert lib.etp_workspace_size(plan.handle, etp.ETP_OP_VJP_WS, ctypes.byref(g7), ctypes.byref(wsb)) == 0
+    g8 = etp.etp_graph(-1, 0, 0, None, None, None, None, None)
+    assert lib.etp_workspace_size(plan.handle, etp.ETP_OP_VJP_WS, ctypes.byref(g8), ctypes.byref(wsb)) == INV
     assert lib.etp_csr_transpose_workspace(-1, ctypes.byref(b)) == INV
 
 
