@@ -211,8 +211,10 @@ class Problem:
             # step writes gw, then dw over it
             self.gw = torch.empty(E, P, C, device="cuda")
             # the destination-side backward's workspace (one Din-row block per
-            # edge), allocated for both formulations so that either can run
-            self.bws = torch.empty(E * wl.Din * C, device="cuda")
+            # edge and the bond-vector partials of its path groups), allocated
+            # for both formulations so that either can run
+            g_sz = etp.Graph(N, n_src, self.row_ptr, self.src)
+            self.bws = torch.empty(etp.etp_workspace_size(self.plan, etp.ETP_OP_VJP_WS, g_sz) // 4, device="cuda")
             self._plan_chunks()
         self.x = self.x32.to(torch.bfloat16) if bf16 else self.x32
         self.g0 = etp.Graph(N, n_src, self.row_ptr, self.src)

@@ -82,7 +82,7 @@ hipError_t launch_validate(int n_dst, int n_src, int64_t E, const int *row_ptr, 
 
 // the destination-side backward, one translation unit per (l_max, dtype, mode)
 #define ETP_DECLARE_BWD(L, XT, MODE) \
-    hipError_t ETP_RUN_NAME(bwd, L, XT, MODE)(const ConvArgs &a, float *part, int64_t n_edges);
+    hipError_t ETP_RUN_NAME(bwd, L, XT, MODE)(const ConvArgs &a, float *part, int64_t n_edges, float *grws);
 #define ETP_DECLARE_BWD_L(L) \
     ETP_DECLARE_BWD(L, 0, 0) ETP_DECLARE_BWD(L, 0, 1) ETP_DECLARE_BWD(L, 1, 0) ETP_DECLARE_BWD(L, 1, 1)
 ETP_DECLARE_BWD_L(0) ETP_DECLARE_BWD_L(1) ETP_DECLARE_BWD_L(2) ETP_DECLARE_BWD_L(3) ETP_DECLARE_BWD_L(4)
@@ -254,10 +254,10 @@ hipError_t run_src(int L, bool bf16, int mode, const etp::ConvArgs &a)
 }
 
 #define ETP_BWD_CASES(L, XT)                                                                 \
-    case (L * 4 + XT * 2 + 0): return etp::ETP_RUN_NAME(bwd, L, XT, 0)(a, part, n_edges);     \
-    case (L * 4 + XT * 2 + 1): return etp::ETP_RUN_NAME(bwd, L, XT, 1)(a, part, n_edges);
+    case (L * 4 + XT * 2 + 0): return etp::ETP_RUN_NAME(bwd, L, XT, 0)(a, part, n_edges, grws); \
+    case (L * 4 + XT * 2 + 1): return etp::ETP_RUN_NAME(bwd, L, XT, 1)(a, part, n_edges, grws);
 
-hipError_t run_bwd(int L, bool bf16, int mode, const etp::ConvArgs &a, float *part, int64_t n_edges)
+hipError_t run_bwd(int L, bool bf16, int mode, const etp::ConvArgs &a, float *part, int64_t n_edges, float *grws)
 {
     switch (L * 4 + (bf16 ? 2 : 0) + mode) {
         ETP_BWD_CASES(0, 0) ETP_BWD_CASES(0, 1) ETP_BWD_CASES(1, 0) ETP_BWD_CASES(1, 1) ETP_BWD_CASES(2, 0)
@@ -284,10 +284,21 @@ bool bwd_uses_dst(int L, int C, bool vjp2, uint32_t flags)
     return L == 3 || (L == 2 && C > 64);
 }
 
-// Workspace of the destination-side backward: one Din-row block per edge.
+// Workspace of the destination-side backward: one Din-row block per edge,
+// then kBwdGrSlices gr / dr partials per edge.
 size_t bwd_workspace_bytes(const etp_plan_s *plan, int64_t n_edges)
 {
-    return static_cast<size_t>(n_edges) * plan->T->din_rows * plan->C * sizeof(float);
+    return static_cast<size_t>(n_edges) * (plan->T->din_rows * plan->C + 3 * etp::kBwdGrSlices) * sizeof(float);
+}
+
+// The part rows (when the node gradient is wanted) and the gr / dr partial
+// slices (when the workspace is there and large enough) inside ws.
+void bwd_split_ws(const etp_plan_s *plan, int64_t n_edges, bool want_x, void *ws, size_t ws_bytes, float **part,
+                  float **grws)
+{
+    const bool whole = ws && (reinterpret_cast<uintptr_t>(ws) & 15u) == 0 && ws_bytes >= bwd_workspace_bytes(plan, n_edges);
+    *part = want_x ? static_cast<float *>(ws) : nullptr;
+    *grws = whole ? static_cast<float *>(ws) + static_cast<size_t>(n_edges) * plan->T->din_rows * plan->C : nullptr;
 }
 
 // box: three finite sides, each at least twice the finite, positive cutoff
@@ -677,8 +688,9 @@ etp_status etp_edge_conv_vjp_ws(etp_plan_t plan, const etp_graph *g, const float
     if (!dst)
         return hip_status(run_src(plan->L, plan->dtype == ETP_BF16, etp::SRC_VJP, a));
     // (with no edges the kernels still write the zero node rows and read no workspace)
-    return hip_status(
-        run_bwd(plan->L, plan->dtype == ETP_BF16, 0, a, grad_x ? static_cast<float *>(ws) : nullptr, g->n_edges));
+    float *part, *grws;
+    bwd_split_ws(plan, g->n_edges, grad_x != nullptr, ws, ws_bytes, &part, &grws);
+    return hip_status(run_bwd(plan->L, plan->dtype == ETP_BF16, 0, a, part, g->n_edges, grws));
 }
 
 etp_status etp_edge_conv_vjp2_ws(etp_plan_t plan, const etp_graph *g, const float *vec, const void *x, const float *w,
@@ -746,7 +758,9 @@ etp_status etp_edge_conv_vjp2_ws(etp_plan_t plan, const etp_graph *g, const floa
         return ETP_OK;
     if (!dst)
         return hip_status(run_src(plan->L, bf16, etp::SRC_VJP2, a));
-    return hip_status(run_bwd(plan->L, bf16, 1, a, d_x ? static_cast<float *>(ws) : nullptr, g->n_edges));
+    float *part, *grws;
+    bwd_split_ws(plan, g->n_edges, d_x != nullptr, ws, ws_bytes, &part, &grws);
+    return hip_status(run_bwd(plan->L, bf16, 1, a, part, g->n_edges, grws));
 }
 
 // The source pass with weight-gradient partials, then their ordered sum over

@@ -163,14 +163,16 @@ constexpr int bwd_lds_floats(int nch)
     return nw * Cfg::B * Cfg::ESP;
 }
 
-template <int L, typename XT, int MODE, int SG>
-__device__ __forceinline__ void bwd_group(const int n_dst, const int nslice, const int C, const int *__restrict__ row_ptr,
+template <int L, typename XT, int MODE, int SG, bool CONC>
+__device__ __forceinline__ void bwd_group(const int lb, const int n_dst, const int nslice, const int C,
+                                          const int *__restrict__ row_ptr,
                                           const int *__restrict__ src, const float *__restrict__ vec,
                                           const XT *__restrict__ x, const float *__restrict__ w,
                                           const float *__restrict__ G, const float *__restrict__ ggx,
                                           const float *__restrict__ ggw, const float *__restrict__ ggvec,
                                           float *__restrict__ part, float *__restrict__ ow,
-                                          float *__restrict__ ovec, const uint32_t flags, float *lds)
+                                          float *__restrict__ ovec, const uint32_t flags, float *lds,
+                                          float *__restrict__ grws, const int64_t n_edges)
 {
     using Cfg = BwdCfg<L, MODE>;
     constexpr int B = Cfg::B, ES = Cfg::ES, NV = Cfg::NV, DSHP = Cfg::DSHP, PK = Cfg::PK;
@@ -189,7 +191,6 @@ __device__ __forceinline__ void bwd_group(const int n_dst, const int nslice, con
     // workgroup = (destination node, slice of its in-edges): the in-edges
     // are independent given G[i], so long rows split over several workgroups
     // (more, shorter work units: no tail when there are few nodes)
-    const int lb = xcd_remap(blockIdx.x, gridDim.x);
     const int i = lb / nslice, sl = lb - i * nslice;
     if (i >= n_dst)
         return;
@@ -198,6 +199,12 @@ __device__ __forceinline__ void bwd_group(const int n_dst, const int nslice, con
     const uint32_t off4 = active ? static_cast<uint32_t>(u) * 4u : kOOB;
     const uint32_t offx = active ? static_cast<uint32_t>(u) * static_cast<uint32_t>(sizeof(XT)) : kOOB;
     const bool want_vec = ovec != nullptr, want_x = part != nullptr;
+    // where this group's gr / dr go: in sequence (CONC false) later groups add
+    // to the earlier groups' result in ovec; side by side (CONC true) group 0
+    // writes ovec and group g > 0 its own slice of grws, added in group order
+    // afterwards
+    float *const gdst = (CONC && SG > 0) ? grws + static_cast<int64_t>(SG - 1) * 3 * n_edges : ovec;
+    constexpr bool GADD = !CONC && SG > 0;
     const bool has_xp = V2 && ggx != nullptr, has_wp = V2 && ggw != nullptr, has_rp = V2 && ggvec != nullptr;
     const uint32_t rowb = static_cast<uint32_t>(C) * 4u, rowx = static_cast<uint32_t>(C) * sizeof(XT);
 
@@ -308,8 +315,8 @@ __device__ __forceinline__ void bwd_group(const int n_dst, const int nslice, con
                 g1 += pp[1];
                 g2 += pp[2];
             }
-            float *gp = ovec + 3 * static_cast<int64_t>(epos(t0 + lane));
-            if (SG > 0) {
+            float *gp = gdst + 3 * static_cast<int64_t>(epos(t0 + lane));
+            if (GADD) {
                 g0 += gp[0];
                 g1 += gp[1];
                 g2 += gp[2];
@@ -486,8 +493,8 @@ __device__ __forceinline__ void bwd_group(const int n_dst, const int nslice, con
         if (want_vec) {
             if (nch == 1) {
                 if (lane == 63) {
-                    float *gp = ovec + 3 * static_cast<int64_t>(e);
-                    if (SG > 0) {
+                    float *gp = gdst + 3 * static_cast<int64_t>(e);
+                    if (GADD) {
                         g0 += gp[0];
                         g1 += gp[1];
                         g2 += gp[2];
@@ -525,8 +532,61 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BwdCfg
                float *__restrict__ ovec, const uint32_t flags)
 {
     extern __shared__ float lds[];
-    bwd_group<L, XT, MODE, SG>(n_dst, nslice, C, row_ptr, src, vec, x, w, G, ggx, ggw, ggvec, part, ow, ovec, flags,
-                               lds);
+    bwd_group<L, XT, MODE, SG, false>(xcd_remap(blockIdx.x, gridDim.x), n_dst, nslice, C, row_ptr, src, vec, x, w, G,
+                                      ggx, ggw, ggvec, part, ow, ovec, flags, lds, nullptr, 0);
+}
+
+// Every path group in one launch: one flat grid over (node, in-edge slice,
+// group) with the group varying fastest, so that a node's groups run side by
+// side on one XCD (sharing its edges' indices, bond vectors and x rows in L2)
+// and groups bound by arithmetic overlap with groups bound by memory. Only
+// for tables whose groups write disjoint part rows; gr / dr partials of the
+// groups after the first go to grws.
+template <int L, typename XT, int MODE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BwdCfg<L, MODE>::WPE)))
+    bwd_kernel_all(const int n_dst, const int nslice, const int C, const int *__restrict__ row_ptr,
+                   const int *__restrict__ src, const float *__restrict__ vec, const XT *__restrict__ x,
+                   const float *__restrict__ w, const float *__restrict__ G, const float *__restrict__ ggx,
+                   const float *__restrict__ ggw, const float *__restrict__ ggvec, float *__restrict__ part,
+                   float *__restrict__ ow, float *__restrict__ ovec, const uint32_t flags, float *__restrict__ grws,
+                   const int64_t n_edges)
+{
+    extern __shared__ float lds[];
+    constexpr Groups GR = BwdCfg<L, MODE>::GR;
+    const int flat = xcd_remap(blockIdx.x, gridDim.x);
+    const int g = flat % GR.n, lb = flat / GR.n;
+    static_range<0, GR.n>([&](auto SG) __attribute__((always_inline)) {
+        if (g == SG)
+            bwd_group<L, XT, MODE, SG, true>(lb, n_dst, nslice, C, row_ptr, src, vec, x, w, G, ggx, ggw, ggvec, part,
+                                             ow, ovec, flags, lds, grws, n_edges);
+    });
+}
+
+// gr += the partials of groups 1 .. NX (in group order), per edge.
+template <int NX>
+__global__ void __launch_bounds__(256) bwd_gr_sum_kernel(const int64_t n3, const float *__restrict__ grws,
+                                                         float *__restrict__ ovec)
+{
+    for (int64_t t = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; t < n3;
+         t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        float v = ovec[t];
+#pragma unroll
+        for (int k = 0; k < NX; ++k)
+            v += grws[k * n3 + t];
+        ovec[t] = v;
+    }
+}
+
+// Whether the path groups of a table write disjoint part rows (each l1
+// block inside one group), so that they may run side by side.
+template <int L, int MODE>
+constexpr bool bwd_groups_disjoint()
+{
+    constexpr Groups GR = BwdCfg<L, MODE>::GR;
+    for (int k = 1; k < GR.n; ++k)
+        if (GR.p0[k] > 0 && kTab<L>.path[GR.p0[k] - 1].l1 == kTab<L>.path[GR.p0[k]].l1)
+            return false;
+    return true;
 }
 
 // gx[j] (+)= sum over j's out-edges, in the order of the stable transpose, of
@@ -571,7 +631,7 @@ __global__ void __launch_bounds__(256) bwd_gather_kernel(const int64_t total, co
 }
 
 template <int L, typename XT, int MODE>
-static hipError_t launch_bwd_t(const ConvArgs &a, float *part, int64_t E)
+static hipError_t launch_bwd_t(const ConvArgs &a, float *part, int64_t E, float *grws)
 {
     using Cfg = BwdCfg<L, MODE>;
     constexpr Groups GR = Cfg::GR;
@@ -585,19 +645,41 @@ static hipError_t launch_bwd_t(const ConvArgs &a, float *part, int64_t E)
         const int64_t by_deg = E / (16 * static_cast<int64_t>(a.n_dst));
         nslice = static_cast<int>(nslice < by_deg ? nslice : by_deg);
         nslice = nslice < 1 ? 1 : (nslice > 16 ? 16 : nslice);
-        if (static_cast<int64_t>(a.n_dst) * nslice > 0x7FFFFFFF)
+        if (static_cast<int64_t>(a.n_dst) * nslice * GR.n > 0x7FFFFFFF)
             return hipErrorInvalidValue;
-        // one launch per path group, in order: later groups add to gr / dr
-        // and to the part rows of an l1 block an earlier group began
-        static_range<0, GR.n>([&](auto g) {
-            if (err != hipSuccess)
-                return;
-            hipLaunchKernelGGL((bwd_kernel<L, XT, MODE, g>), dim3(a.n_dst * nslice), dim3(64 * nch * bwd_splits(nch)),
-                               lds_bytes, a.stream, a.n_dst, nslice, a.C, a.row_ptr, a.src, a.vec,
-                               static_cast<const XT *>(a.x), a.w, a.G, a.ggx, a.ggw, a.ggvec, part, a.ow, a.ovec,
-                               a.flags);
-            err = hipGetLastError();
-        });
+        constexpr bool side_by_side = GR.n > 1 && GR.n - 1 <= kBwdGrSlices && bwd_groups_disjoint<L, MODE>();
+        bool one_launch = false;
+        if constexpr (side_by_side) {
+            one_launch = grws || !a.ovec;  // gr partials need their slices
+            if (one_launch) {
+                const int64_t nb = static_cast<int64_t>(a.n_dst) * nslice * GR.n;
+                hipLaunchKernelGGL((bwd_kernel_all<L, XT, MODE>), dim3(static_cast<unsigned>(nb)),
+                                   dim3(64 * nch * bwd_splits(nch)), lds_bytes, a.stream, a.n_dst, nslice, a.C,
+                                   a.row_ptr, a.src, a.vec, static_cast<const XT *>(a.x), a.w, a.G, a.ggx, a.ggw,
+                                   a.ggvec, part, a.ow, a.ovec, a.flags, grws, E);
+                err = hipGetLastError();
+                if (err == hipSuccess && a.ovec && E > 0) {
+                    const int64_t n3 = 3 * E, blocks = (n3 + 255) / 256;
+                    hipLaunchKernelGGL((bwd_gr_sum_kernel<GR.n - 1>),
+                                       dim3(static_cast<unsigned>(blocks < 65536 ? blocks : 65536)), dim3(256), 0,
+                                       a.stream, n3, grws, a.ovec);
+                    err = hipGetLastError();
+                }
+            }
+        }
+        if (!one_launch) {
+            // one launch per path group, in order: later groups add to gr / dr
+            // and to the part rows of an l1 block an earlier group began
+            static_range<0, GR.n>([&](auto g) {
+                if (err != hipSuccess)
+                    return;
+                hipLaunchKernelGGL((bwd_kernel<L, XT, MODE, g>), dim3(a.n_dst * nslice),
+                                   dim3(64 * nch * bwd_splits(nch)), lds_bytes, a.stream, a.n_dst, nslice, a.C,
+                                   a.row_ptr, a.src, a.vec, static_cast<const XT *>(a.x), a.w, a.G, a.ggx, a.ggw,
+                                   a.ggvec, part, a.ow, a.ovec, a.flags);
+                err = hipGetLastError();
+            });
+        }
     }
     if (err != hipSuccess || !a.ox || a.n_src == 0)
         return err;
@@ -620,10 +702,10 @@ static hipError_t launch_bwd_t(const ConvArgs &a, float *part, int64_t E)
 #error "compile this file once per (l_max, dtype, mode) with -DETP_L=0..4 -DETP_XT=0|1 -DETP_MODE=0|1"
 #endif
 
-hipError_t ETP_RUN_NAME(bwd, ETP_L, ETP_XT, ETP_MODE)(const ConvArgs &a, float *part, int64_t n_edges)
+hipError_t ETP_RUN_NAME(bwd, ETP_L, ETP_XT, ETP_MODE)(const ConvArgs &a, float *part, int64_t n_edges, float *grws)
 {
     using XT = std::conditional_t<ETP_XT == 1, bf16raw, float>;
-    return launch_bwd_t<ETP_L, XT, ETP_MODE>(a, part, n_edges);
+    return launch_bwd_t<ETP_L, XT, ETP_MODE>(a, part, n_edges, grws);
 }
 
 }  // namespace etp

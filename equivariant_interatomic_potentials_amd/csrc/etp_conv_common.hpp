@@ -32,6 +32,10 @@ struct ConvArgs {
 
 enum { DST_FWD = 0, DST_DG = 1, DST_FWD_RADIAL = 2, DST_DG_RADIAL = 3 };
 constexpr int kRadialMax = 8;  // radial basis functions per edge (padded to this in LDS)
+// gr / dr partial slices (3 floats per edge each) that the destination-side
+// backward's workspace holds after the per-edge part rows: path groups
+// 1 .. kBwdGrSlices may then run side by side with group 0
+constexpr int kBwdGrSlices = 2;
 enum { SRC_VJP = 0, SRC_VJP2 = 1, SRC_VJP_RADIAL = 2, SRC_VJP2_RADIAL = 3, SRC_VJP_RADIAL_WG = 4, SRC_VJP2_RADIAL_WG = 5 };
 
 // Each kernel source is compiled once per (l_max, x dtype, mode) with

@@ -226,7 +226,8 @@ ETP_API etp_status etp_csr_transpose_noalloc(const etp_graph *g, int32_t *src_pt
  * intermediates in registers and LDS and takes no workspace argument);
  * ETP_OP_TRANSPOSE needs etp_csr_transpose_workspace(g->n_src);
  * ETP_OP_VJP_WS and ETP_OP_VJP2_WS (etp_edge_conv_vjp_ws / _vjp2_ws) need
- * n_edges * Din * C * 4 (one Din-row block of the node gradient per edge);
+ * n_edges * (Din * C + 6) * 4 (one Din-row block of the node gradient per
+ * edge, then two three-float partials of the bond-vector gradient per edge);
  * ETP_OP_RADIAL_WGRAD (the radial weight gradients) needs
  * (n_src + 64) * ETP_MAX_RADIAL_BASIS * P * C * 4 (per-source-node partials
  * and the runs of their ordered sum).
@@ -313,9 +314,12 @@ ETP_API etp_status etp_edge_conv_vjp(etp_plan_t plan, const etp_graph *g, const 
  * conventions are the same.
  * ws: DEVICE workspace, 16-byte aligned, of at least
  * etp_workspace_size(plan, ETP_OP_VJP_WS / ETP_OP_VJP2_WS, g) bytes
- * (n_edges * Din * C * 4), needed only when grad_x (d_x) is requested from
- * the destination-side formulation; its contents need not be initialised
- * and are undefined afterwards. The transpose in g is needed for grad_x
+ * (n_edges * (Din * C + 6) * 4), needed when grad_x (d_x) is requested from
+ * the destination-side formulation; without grad_x it may be NULL, and
+ * when given it lets the path groups of l_max = 3 run in one launch (their
+ * bond-vector partials are added in group order afterwards: the same
+ * result, bit for bit); its contents need not be initialised and are
+ * undefined afterwards. The transpose in g is needed for grad_x
  * (d_x), and for every output of the source-side formulation. Errors: as
  * etp_edge_conv_vjp / etp_edge_conv_vjp2, plus WORKSPACE (ws missing,
  * misaligned or too small while grad_x / d_x is requested). */

@@ -49,7 +49,8 @@ def vjp_ws(p, want=("gx", "gw", "gr"), flags=FORCE, gx=None, ws=True):
     return gx, gw, gr
 
 
-def vjp2_ws(p, cot=("ggx", "ggw", "ggvec"), want=("dx", "dw", "dr", "dG"), flags=FORCE, dx=None, dG=None):
+def vjp2_ws(p, cot=("ggx", "ggw", "ggvec"), want=("dx", "dw", "dr", "dG"), flags=FORCE, dx=None, dG=None,
+            ws=True):
     wl, etp = p.wl, p.etp
     ggx = dev(wl.ggx) if "ggx" in cot else None
     ggw = dev(wl.ggw) if "ggw" in cot else None
@@ -60,7 +61,7 @@ def vjp2_ws(p, cot=("ggx", "ggw", "ggvec"), want=("dx", "dw", "dr", "dG"), flags
     dr = p.empty(wl.E, 3) if "dr" in want else None
     if dG is None and "dG" in want:
         dG = p.empty(wl.n_dst, wl.Dout, wl.C)
-    w = etp.bwd_workspace(p.plan, p.graph, etp.ETP_OP_VJP2_WS)
+    w = etp.bwd_workspace(p.plan, p.graph, etp.ETP_OP_VJP2_WS) if ws else None
     etp.etp_edge_conv_vjp2_ws(p.plan, p.graph, p.vec, p.x, p.w, p.G, ggx, ggw, ggv, dx, dw, dr, dG, w, flags)
     return dx, dw, dr, dG
 
@@ -150,7 +151,7 @@ def test_ws_workspace_checks():
     p = DeviceProblem(wl)
     gx = p.empty(wl.n, wl.Din, wl.C)
     need = etp.etp_workspace_size(p.plan, etp.ETP_OP_VJP_WS, p.graph)
-    assert need == wl.E * wl.Din * wl.C * 4
+    assert need == wl.E * (wl.Din * wl.C + 6) * 4
     assert etp.etp_workspace_size(p.plan, etp.ETP_OP_VJP2_WS, p.graph) == need
     small = torch.empty(need - 4, dtype=torch.uint8, device="cuda")
     for ws in (None, small):
@@ -257,3 +258,25 @@ def test_ws_default_and_forced_formulations(L, C):
         vjp_ws(p, flags=etp.ETP_FLAG_SRC_PASS | etp.ETP_FLAG_DST_PASS)
     assert ei.value.status == etp.ETP_ERR_INVALID_ARGUMENT
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("L,C,kind", [(3, 128, "ragged"), (3, 64, "fan_in"), (3, 16, "fan_out")])
+def test_ws_groups_in_one_launch_match_in_sequence(L, C, kind):
+    """With a workspace the l_max = 3 path groups run in one launch and their
+    bond-vector partials are added in group order afterwards; without one
+    (no node gradient wanted) they run one launch after another, each adding
+    to the last. Both give the same gr / dr bit for bit, and the same gw / dw."""
+    import torch
+    say("ws groups one launch vs sequence", L, C, kind)
+    p = DeviceProblem(small_wl(L, C, kind))
+    _, gw1, gr1 = vjp_ws(p, want=("gw", "gr"), ws=True)
+    _, gw2, gr2 = vjp_ws(p, want=("gw", "gr"), ws=False)
+    assert torch.equal(gr1, gr2) and torch.equal(gw1, gw2)
+    _, dw1, dr1, _ = vjp2_ws(p, want=("dw", "dr"), ws=True)
+    _, dw2, dr2, _ = vjp2_ws(p, want=("dw", "dr"), ws=False)
+    assert torch.equal(dr1, dr2) and torch.equal(dw1, dw2)
+    wl = p.wl
+    gx, gw, gr = vjp_ws(p)
+    ref = oracle.vjp(L, wl.row_ptr, wl.src, wl.vec, wl.x, wl.w, wl.G)
+    for got, exp in zip((gx, gw, gr), ref):
+        assert rel_err(np_(got), exp) < FP32_TOL
