@@ -122,14 +122,19 @@ def roof(byts, flops, t):
             "frac": round(tv / t, 4)}
 
 
+# the device code of the timed step (transpose, forward, VJP, VJP-of-VJP)
+# and the headers it includes; the host-side C-ABI file and the kernels of
+# the calls around the convolution are left out (they do not change what the
+# step's kernels move)
+STEP_SOURCES = ("etp_graph.hip", "etp_dst.hip", "etp_src.hip", "etp_bwd.hip", "etp_device.hpp",
+                "etp_conv_common.hpp", "etp_groups.hpp", "etp_tables.hpp")
+
+
 def kernel_source_hash():
-    """Hash of the device-code sources (the host-side C-ABI file is left out:
-    argument checks and dispatch do not change what a kernel moves)."""
+    """Hash of the step's device-code sources."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "equivariant_interatomic_potentials_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f == "etp_api.hip":
-            continue
+    for f in STEP_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
