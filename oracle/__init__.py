@@ -89,6 +89,8 @@ def _load():
         lib.oracle_node_product_vjp.argtypes = [ctypes.c_int] * 4 + [_f64p, _f64p, _f64p, _f64p]
         lib.oracle_channel_mix_vjp.restype = ctypes.c_int
         lib.oracle_channel_mix_vjp.argtypes = [ctypes.c_int] * 5 + [_f64p, _f64p, _f64p]
+        lib.oracle_channel_mix_wgrad.restype = ctypes.c_int
+        lib.oracle_channel_mix_wgrad.argtypes = [ctypes.c_int] * 5 + [_f64p, _f64p, _f64p]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -257,6 +259,19 @@ def channel_mix_vjp(L, gy, W):
                                       _p(_nz(gin.reshape(-1)), _f64p)):
         raise ValueError("oracle_channel_mix_vjp failed")
     return gin
+
+
+def channel_mix_wgrad(L, out, gy):
+    """gW = W_0, W_1, ... back to back: the gradient of <gy, channel_mix(out, W)>
+    with respect to W (the sum over nodes and components of out (x) gy per path)."""
+    lin, lsh, lout = _lmax(L)
+    out, gy = _f64(out), _f64(gy)
+    n, _, C = out.shape
+    gW = np.zeros(sum(mix_rows(L)) * C * C)
+    if _load().oracle_channel_mix_wgrad(lin, lsh, lout, C, n, _p(_nz(out.reshape(-1)), _f64p),
+                                        _p(_nz(gy.reshape(-1)), _f64p), _p(_nz(gW), _f64p)):
+        raise ValueError("oracle_channel_mix_wgrad failed")
+    return gW
 
 
 def edge_forces(row_ptr, src, n_src, gr):

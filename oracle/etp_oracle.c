@@ -746,6 +746,44 @@ int oracle_channel_mix_vjp(int lin, int lsh, int lout, int C, int n, const doubl
     return 0;
 }
 
+/* Gradient of the channel mixing with respect to its weights (the mixing is
+ * linear in W; a sum over every node and component):
+ * gW_l[(q_p C + u) C + v] = sum_i sum_m out[i][off_p + m][u] gy[i][l*l + m][v]
+ * for every path p of order l = l3_p. Nodes in index order, serially. */
+int oracle_channel_mix_wgrad(int lin, int lsh, int lout, int C, int n, const double *out, const double *gy, double *gW)
+{
+    table t;
+    if (table_make(lin, lsh, lout, &t))
+        return -1;
+    const int Dout = t.Dout, Dy = (lout + 1) * (lout + 1);
+    int64_t wofs[OR_LMAX + 2];
+    int prank[128], pcount[OR_LMAX + 1] = {0};
+    for (int p = 0; p < t.P; ++p) {
+        const int l3 = t.path[3 * p + 2];
+        prank[p] = pcount[l3]++;
+    }
+    wofs[0] = 0;
+    for (int l = 0; l <= lout; ++l)
+        wofs[l + 1] = wofs[l] + (int64_t)pcount[l] * C * C;
+    for (int64_t q = 0; q < wofs[lout + 1]; ++q)
+        gW[q] = 0.0;
+#pragma omp parallel for schedule(static)
+    for (int p = 0; p < t.P; ++p) {  /* each path owns its block of gW */
+        const int l = t.path[3 * p + 2];
+        double *G = gW + wofs[l] + (int64_t)prank[p] * C * C;
+        for (int i = 0; i < n; ++i)
+            for (int mi = 0; mi < 2 * l + 1; ++mi) {
+                const double *o = out + ((int64_t)i * Dout + t.off[p] + mi) * C;
+                const double *gyr = gy + ((int64_t)i * Dy + l * l + mi) * C;
+                for (int u = 0; u < C; ++u)
+                    for (int v = 0; v < C; ++v)
+                        G[(int64_t)u * C + v] += o[u] * gyr[v];
+            }
+    }
+    table_free(&t);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Forces on the atoms                                                       */
 /* ------------------------------------------------------------------------ */

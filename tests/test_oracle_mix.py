@@ -106,3 +106,60 @@ def test_vjp_identity_blocks_copy_cotangent():
     gin = oracle.channel_mix_vjp(L, gy, W)
     for q, (l1, l2, l3) in enumerate(p):
         np.testing.assert_allclose(gin[:, off[q]:off[q + 1]], gy[:, l3 * l3:(l3 + 1) ** 2], atol=1e-14)
+
+
+# ------------------------------------------------------- weight gradient
+
+@pytest.mark.parametrize("L,C", [(1, 3), (2, 4), (3, 2), (4, 1)])
+def test_wgrad_is_the_gradient_of_the_pairing(L, C):
+    """The mixing is linear in W, so <gW, W> = <gy, mix(in, W)> for every W
+    (mix from the oracle's forward loops, gW from its weight-gradient loops)."""
+    g = np.random.default_rng(40 + L)
+    p, off = offsets(L)
+    n = 5
+    inp = g.standard_normal((n, off[-1], C))
+    gy = g.standard_normal((n, (L + 1) ** 2, C))
+    gW = oracle.channel_mix_wgrad(L, inp, gy)
+    for trial in range(3):
+        W = g.standard_normal(sum(oracle.mix_rows(L)) * C * C)
+        lhs = (gW * W).sum()
+        rhs = (gy * oracle.channel_mix(L, inp, W)).sum()
+        assert abs(lhs - rhs) < 1e-10 * max(1.0, abs(rhs))
+
+
+def test_wgrad_outer_product_of_one_path():
+    """One node, one nonzero path block of the input and one nonzero component
+    row of gy: gW is that path's block, the outer product in (x) gy, and zero
+    elsewhere."""
+    L, C = 2, 3
+    g = np.random.default_rng(12)
+    p, off = offsets(L)
+    rows = oracle.mix_rows(L)
+    q = 7                                  # a path of order l3
+    l3 = int(p[q][2])
+    m = 1 if l3 > 0 else 0
+    inp = np.zeros((1, off[-1], C))
+    a = g.standard_normal(C)
+    inp[0, off[q] + m] = a
+    gy = np.zeros((1, (L + 1) ** 2, C))
+    b = g.standard_normal(C)
+    gy[0, l3 * l3 + m] = b
+    gW = oracle.channel_mix_wgrad(L, inp, gy)
+    rank = int(sum(1 for r in range(q) if p[r][2] == l3))
+    start = sum(rows[:l3]) * C * C + rank * C * C
+    expect = np.zeros_like(gW)
+    expect[start:start + C * C] = np.outer(a, b).reshape(-1)
+    np.testing.assert_allclose(gW, expect, atol=1e-15)
+
+
+def test_wgrad_sums_over_nodes_and_components():
+    """gW of a batch = the sum of the per-node gW (a sum over nodes), and a
+    mismatched component (gy on another m) contributes nothing."""
+    L, C = 3, 2
+    g = np.random.default_rng(13)
+    p, off = offsets(L)
+    inp = g.standard_normal((6, off[-1], C))
+    gy = g.standard_normal((6, 16, C))
+    whole = oracle.channel_mix_wgrad(L, inp, gy)
+    parts = sum(oracle.channel_mix_wgrad(L, inp[i:i + 1], gy[i:i + 1]) for i in range(6))
+    np.testing.assert_allclose(whole, parts, rtol=1e-13, atol=1e-13)

@@ -46,6 +46,9 @@ MUTANTS = [
     ("hyperdual_mixed", "x.a * y.d + x.b * y.c + x.c * y.b + x.d * y.a};", "x.a * y.d + x.b * y.c + x.d * y.a};"),
     ("mix_rank", "rank[p] = count[l3]++;", "rank[p] = count[l3];"),
     ("mix_transposed_W", "yr[v] += Wl[(int64_t)u * C + v] * o[u];", "yr[v] += Wl[(int64_t)v * C + u] * o[u];"),
+    ("mix_wgrad_transposed", "G[(int64_t)u * C + v] += o[u] * gyr[v];", "G[(int64_t)v * C + u] += o[u] * gyr[v];"),
+    ("mix_wgrad_component", "const double *gyr = gy + ((int64_t)i * Dy + l * l + mi) * C;",
+     "const double *gyr = gy + ((int64_t)i * Dy + l * l + (2 * l - mi)) * C;"),
     ("forces_sign", "F[3 * (int64_t)src[e] + c] -= gr[3 * e + c];", "F[3 * (int64_t)src[e] + c] += gr[3 * e + c];"),
     ("forces_dst_index", "F[3 * i + c] += gr[3 * e + c];", "F[3 * (int64_t)src[e] + c] += gr[3 * e + c];"),
     ("nl_not_strict", "if (r2 < rc2) {", "if (r2 <= rc2) {"),
