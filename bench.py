@@ -487,6 +487,12 @@ def time_channel_mix(etp, plan, out, L, C, N, reps):
     res["bf16"] = {"ms": round(tb * 1e3, 4), "vjp_ms": round(tbv * 1e3, 4), "hbm_frac": bb / tb / 1e9 / HBM_PEAK_GBS,
                    "mfma_frac": flops / tb / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                    "vjp_hbm_frac": bb / tbv / 1e9 / HBM_PEAK_GBS}
+    # the weight gradient (a sum over the nodes: the same FLOPs; reads the
+    # input and the cotangent once, writes grad_W)
+    wws = etp.mix_wgrad_workspace(plan, N)
+    gW = torch.empty_like(W)
+    tg = time_calls(lambda: etp.etp_channel_mix_wgrad(plan, out, y, gW, wws), reps, 3)
+    res.update({"wgrad_ms": round(tg * 1e3, 4), "wgrad_mfma_frac": flops / tg / 1e12 / MFMA_F32_PEAK_TFLOPS})
     return res
 
 

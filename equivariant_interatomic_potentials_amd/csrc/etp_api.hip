@@ -18,6 +18,9 @@ hipError_t launch_mix(int L, int C, int n, const float *in, const void *W, bool 
                       hipStream_t stream);
 hipError_t launch_mix_vjp(int L, int C, int n, const float *gy, const void *W, bool bf16, float *gin,
                           bool accumulate, hipStream_t stream);
+size_t mix_wgrad_workspace_bytes(int L, int C, int n);
+hipError_t launch_mix_wgrad(int L, int C, int n, const float *in, const float *gy, float *gW, bool accumulate,
+                            float *ws, size_t ws_bytes, hipStream_t stream);
 hipError_t launch_node_product(int L, int C, int n, int nu, const float *A, const float *W, float *out,
                                bool accumulate, hipStream_t stream);
 // the edge-local product, one translation unit per l_max
@@ -471,6 +474,9 @@ etp_status etp_workspace_size(etp_plan_t plan, int32_t op, const etp_graph *g, s
         return ETP_OK;
     case ETP_OP_RADIAL_WGRAD:
         *bytes = wgrad_workspace_bytes(plan, g->n_src);
+        return ETP_OK;
+    case ETP_OP_MIX_WGRAD:
+        *bytes = etp::mix_wgrad_workspace_bytes(plan->L, plan->C, g->n_dst);
         return ETP_OK;
     default:
         return ETP_ERR_INVALID_ARGUMENT;
@@ -1039,6 +1045,22 @@ etp_status etp_channel_mix_vjp_ex(etp_plan_t plan, int32_t n_nodes, const float 
                                   int32_t w_dtype, float *grad_in, uint32_t flags, void *stream)
 {
     return channel_mix_call(true, plan, n_nodes, grad_y, W, w_dtype, grad_in, flags, stream);
+}
+
+etp_status etp_channel_mix_wgrad(etp_plan_t plan, int32_t n_nodes, const float *in, const float *grad_y,
+                                 float *grad_W, uint32_t flags, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!plan || n_nodes < 0 || !grad_W)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (flags & ~static_cast<uint32_t>(ETP_FLAG_ACCUMULATE))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (n_nodes > 0 && (!in || !grad_y))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (ws && (reinterpret_cast<uintptr_t>(ws) & 15u))
+        return ETP_ERR_WORKSPACE;
+    return hip_status(etp::launch_mix_wgrad(plan->L, plan->C, n_nodes, in, grad_y, grad_W,
+                                            (flags & ETP_FLAG_ACCUMULATE) != 0, static_cast<float *>(ws),
+                                            ws ? ws_bytes : 0, static_cast<hipStream_t>(stream)));
 }
 
 etp_status etp_edge_tp_fwd(etp_plan_t plan, int64_t n_edges, const float *vec, const float *V, const float *w,

@@ -47,6 +47,10 @@
 
 namespace etp {
 
+#ifndef ETP_MIX_WG_ROWS
+#define ETP_MIX_WG_ROWS 32
+#endif
+
 constexpr int kMixMaxPaths = 17;  // most paths of one output order (l_max 4, l3 = 3)
 
 struct MixTab {
@@ -309,6 +313,156 @@ __global__ void __launch_bounds__(256 * KW) mix2_kernel(const MixTab tb, const f
     }
 }
 
+// Weight gradient of the mixing (the sum over nodes that training needs):
+//   gW_l[(q C + u), v] = sum_{i, m} in[i, off_q + m, u] gy[i, l*l + m, v]
+// per path q of order l: a product [C] x [n (2l+1)] times [n (2l+1)] x [C]
+// whose long K runs over (node, component) rows. blockIdx.x = (path, 64-row
+// block of u, 64-column block of v), blockIdx.y = split s of K: the split
+// takes the nodes [n s / S, n (s + 1) / S) and writes its partial block to
+// part[s] (or, with S = 1, the result to gW); 4 waves of 16 u rows hold
+// four 16 x 16 accumulator tiles each (v_mfma_f32_16x16x4f32).
+//   * K in chunks of 32 rows: one component m of 32 nodes; chunk row
+//     r = 4 st + kq is K step st's row for lane quarter kq;
+//   * A (the input's channels u) is read by one wave only: each lane loads
+//     its channel of its 8 rows straight from memory (16 lanes, 64
+//     contiguous bytes per row); B (the cotangent's 64 channels v, shared by
+//     the 4 waves) is loaded with 16-byte loads into a double-buffered LDS
+//     tile Bs[row][col][t] laid out so that a lane reads its four column
+//     tiles' values as one 16-byte LDS read; the next chunk loads into
+//     registers while the current chunk's products run (one barrier per
+//     chunk).
+constexpr int kMixWgRows = ETP_MIX_WG_ROWS;  // K rows per chunk (a component of that many nodes)
+constexpr int kMixWgBS = 68;  // Bs row stride (floats): 16-byte rows, banks shifted per row
+
+struct MixWgTab {
+    int P, C, n, Dout, Dy, nub, nvb, nsplit;
+    int l3[kMixMaxPaths * 5];      // order of each path
+    int off[kMixMaxPaths * 5];     // first output row of each path
+    int64_t wofs[kMixMaxPaths * 5];  // start of each path's block in gW
+};
+
+__global__ void __launch_bounds__(256) mix_wgrad_kernel(const MixWgTab tb, const float *__restrict__ in,
+                                                        const float *__restrict__ gy, float *__restrict__ out,
+                                                        const int accumulate)
+{
+    __shared__ __attribute__((aligned(16))) float Bs[2][kMixWgRows * kMixWgBS];
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kq = lane >> 4, col = lane & 15;
+    const int blk = blockIdx.x, s = blockIdx.y;
+    const int vb = blk % tb.nvb, ub = (blk / tb.nvb) % tb.nub, p = blk / (tb.nvb * tb.nub);
+    const int l = tb.l3[p], d = 2 * l + 1, C = tb.C;
+    const int u0 = ub * 64, v0 = vb * 64;
+    const int i0 = static_cast<int>(static_cast<int64_t>(tb.n) * s / tb.nsplit);
+    const int i1 = static_cast<int>(static_cast<int64_t>(tb.n) * (s + 1) / tb.nsplit);
+    const bool vec4 = (C & 3) == 0 && (reinterpret_cast<uintptr_t>(gy) & 15u) == 0;
+    const int u = u0 + 16 * wv + col;
+    const bool uok = u < C;
+
+    mix_f4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        acc[t] = mix_f4{0.f, 0.f, 0.f, 0.f};
+
+    // A (this wave's 16 u rows; no other wave reads them): the lane loads its
+    // channel u of chunk rows 4 st + kq straight from memory. B: thread t
+    // stages chunk rows t / 16 + 16 h, channels 4 (t % 16) .. + 3.
+    constexpr int NS = kMixWgRows / 4, NH = kMixWgRows / 16;  // K steps, staged rows per thread
+    const int sr = threadIdx.x >> 4, sc = 4 * (threadIdx.x & 15);
+    float na[NS], nb[NH][4];
+    const int nblk = (i1 - i0 + kMixWgRows - 1) / kMixWgRows, nit = nblk * d;
+    auto fetch = [&](int it) {
+        const int ib = i0 + (it / d) * kMixWgRows, m = it % d;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            const int i = ib + 4 * st + kq;
+            const bool ok = i < i1 && uok;
+            const int64_t ic = i < i1 ? i : i0;  // rows past the split load a valid row, then count 0
+            const float v = in[(ic * tb.Dout + tb.off[p] + m) * C + (uok ? u : 0)];
+            na[st] = ok ? v : 0.f;
+        }
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const int i = ib + sr + 16 * h;
+            const bool iok = i < i1;
+            const int64_t ic = iok ? i : i0;
+            const float *brow = gy + (ic * tb.Dy + l * l + m) * C;
+            if (vec4 && v0 + sc + 4 <= C) {
+                const float4 v = *reinterpret_cast<const float4 *>(brow + v0 + sc);
+                nb[h][0] = iok ? v.x : 0.f; nb[h][1] = iok ? v.y : 0.f;
+                nb[h][2] = iok ? v.z : 0.f; nb[h][3] = iok ? v.w : 0.f;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool ok = iok && v0 + sc + j < C;
+                    const float v = brow[ok ? v0 + sc + j : 0];  // in bounds either way
+                    nb[h][j] = ok ? v : 0.f;
+                }
+            }
+        }
+    };
+    if (nit > 0)
+        fetch(0);
+    for (int it = 0; it < nit; ++it) {
+        const int buf = it & 1;
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const int r = sr + 16 * h;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int v = sc + j;
+                Bs[buf][r * kMixWgBS + (v & 15) * 4 + (v >> 4)] = nb[h][j];
+            }
+        }
+        float av[NS];
+#pragma unroll
+        for (int st = 0; st < NS; ++st)
+            av[st] = na[st];
+        // one barrier per chunk: the stores above are seen by every wave,
+        // and the buffer written next (buf ^ 1) was last read before it
+        __syncthreads();
+        if (it + 1 < nit)
+            fetch(it + 1);
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            const float4 bv = *reinterpret_cast<const float4 *>(&Bs[buf][(4 * st + kq) * kMixWgBS + col * 4]);
+            acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[st], bv.x, acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[st], bv.y, acc[1], 0, 0, 0);
+            acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[st], bv.z, acc[2], 0, 0, 0);
+            acc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[st], bv.w, acc[3], 0, 0, 0);
+        }
+    }
+
+    // lane l holds u rows 4 (l / 16) + rr of the wave's 16, v column 16 t + l % 16
+    float *dst0 = tb.nsplit > 1 ? out + static_cast<int64_t>(s) * tb.wofs[tb.P] : out;
+    const bool add = tb.nsplit == 1 && accumulate;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int v = v0 + 16 * t + col;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int uu = u0 + wv * 16 + 4 * kq + rr;
+            if (uu < C && v < C) {
+                float *o = dst0 + tb.wofs[p] + static_cast<int64_t>(uu) * C + v;
+                *o = add ? *o + acc[t][rr] : acc[t][rr];
+            }
+        }
+    }
+}
+
+// gW (+)= sum over s < nsplit of part[s] (in order of s), count floats each.
+__global__ void __launch_bounds__(256) mix_wgrad_sum_kernel(const int64_t count, const int nsplit,
+                                                            const float *__restrict__ part, float *__restrict__ gW,
+                                                            const int accumulate)
+{
+    for (int64_t t = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; t < count;
+         t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        float v = 0.f;
+        for (int s = 0; s < nsplit; ++s)
+            v += part[s * count + t];
+        gW[t] = accumulate ? gW[t] + v : v;
+    }
+}
+
 // Path layout of one l_max for the mixing (from the compile-time table).
 template <int L>
 static MixTab mix_table(int C, int n)
@@ -403,6 +557,80 @@ hipError_t launch_mix_vjp(int L, int C, int n, const float *gy, const void *W, b
                           bool accumulate, hipStream_t stream)
 {
     return launch_mix2<true>(L, C, n, gy, W, bf16, gin, accumulate, stream);
+}
+
+// Splits of the weight gradient's K over the nodes: enough workgroups to
+// fill the chip a few times over, each split at least 64 nodes.
+static int mix_wgrad_splits(int L, int C, int n)
+{
+    MixTab tb;
+    if (n <= 0 || !mix_table_for(L, C, n, &tb))
+        return 1;
+    int P = 0;
+    for (int l = 0; l <= L; ++l)
+        P += tb.nl[l];
+    const int64_t tiles = static_cast<int64_t>(P) * ((C + 63) / 64) * ((C + 63) / 64);
+    int64_t s = (2048 + tiles - 1) / tiles;
+    const int64_t by_nodes = n / 64;  // at least 64 nodes per split
+    s = s < by_nodes ? s : by_nodes;
+    s = s < 1 ? 1 : (s > 64 ? 64 : s);
+    return static_cast<int>(s);
+}
+
+size_t mix_wgrad_workspace_bytes(int L, int C, int n)
+{
+    MixTab tb;
+    if (n <= 0 || !mix_table_for(L, C, n, &tb))
+        return 0;
+    const int S = mix_wgrad_splits(L, C, n);
+    return S > 1 ? sizeof(float) * static_cast<size_t>(S) * static_cast<size_t>(tb.wofs[L + 1]) : 0;
+}
+
+hipError_t launch_mix_wgrad(int L, int C, int n, const float *in, const float *gy, float *gW, bool accumulate,
+                            float *ws, size_t ws_bytes, hipStream_t stream)
+{
+    MixTab mt;
+    if (!mix_table_for(L, C, n, &mt))
+        return hipErrorInvalidValue;
+    MixWgTab tb{};
+    tb.C = C;
+    tb.n = n;
+    tb.Dout = mt.Dout;
+    tb.Dy = mt.Dy;
+    tb.nub = (C + 63) / 64;
+    tb.nvb = tb.nub;
+    int P = 0;
+    for (int l = 0; l <= L; ++l)
+        for (int q = 0; q < mt.nl[l]; ++q) {
+            tb.l3[P] = l;
+            tb.off[P] = mt.off[l][q];
+            tb.wofs[P] = mt.wofs[l] + static_cast<int64_t>(q) * C * C;
+            ++P;
+        }
+    tb.P = P;
+    tb.wofs[P] = mt.wofs[L + 1];
+    const int64_t count = mt.wofs[L + 1];
+    if (n == 0) {  // an empty sum: zero (or leave the accumulated gradient)
+        if (accumulate)
+            return hipSuccess;
+        const int64_t blocks = (count + 255) / 256;
+        hipLaunchKernelGGL(mix_wgrad_sum_kernel, dim3(static_cast<unsigned>(blocks < 65536 ? blocks : 65536)),
+                           dim3(256), 0, stream, count, 0, ws, gW, 0);
+        return hipGetLastError();
+    }
+    int S = mix_wgrad_splits(L, C, n);
+    if (S > 1 && (!ws || ws_bytes < mix_wgrad_workspace_bytes(L, C, n)))
+        S = 1;
+    tb.nsplit = S;
+    const dim3 grid(static_cast<unsigned>(P * tb.nub * tb.nvb), S);
+    hipLaunchKernelGGL(mix_wgrad_kernel, grid, dim3(256), 0, stream, tb, in, gy, S > 1 ? ws : gW,
+                       accumulate ? 1 : 0);
+    if (S > 1) {
+        const int64_t blocks = (count + 255) / 256;
+        hipLaunchKernelGGL(mix_wgrad_sum_kernel, dim3(static_cast<unsigned>(blocks < 65536 ? blocks : 65536)),
+                           dim3(256), 0, stream, count, S, ws, gW, accumulate ? 1 : 0);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace etp

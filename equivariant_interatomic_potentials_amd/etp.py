@@ -38,7 +38,7 @@ ABI_SYMBOLS = ("etp_plan_create", "etp_plan_destroy", "etp_plan_info", "etp_plan
                "etp_neighbor_workspace", "etp_neighbor_count", "etp_neighbor_fill", "etp_node_product", "etp_node_product_vjp", "etp_channel_mix_vjp",
                "etp_edge_tp_fwd", "etp_edge_tp_vjp", "etp_edge_tp_vjp2",
                "etp_csr_transpose_noalloc", "etp_edge_conv_vjp_ws", "etp_edge_conv_vjp2_ws",
-               "etp_edge_conv_vjp_radial_wgrad", "etp_edge_conv_vjp2_radial_wgrad", "etp_channel_mix_ex", "etp_channel_mix_vjp_ex",
+               "etp_edge_conv_vjp_radial_wgrad", "etp_edge_conv_vjp2_radial_wgrad", "etp_channel_mix_ex", "etp_channel_mix_vjp_ex", "etp_channel_mix_wgrad",
                "etp_status_string", "etp_version")
 
 
@@ -126,6 +126,7 @@ def _load():
         "etp_channel_mix": (st, [vp, i32, vp, vp, vp, u32, vp]),
         "etp_channel_mix_ex": (st, [vp, i32, vp, vp, i32, vp, u32, vp]),
         "etp_channel_mix_vjp_ex": (st, [vp, i32, vp, vp, i32, vp, u32, vp]),
+        "etp_channel_mix_wgrad": (st, [vp, i32, vp, vp, vp, u32, vp, ctypes.c_size_t, vp]),
         "etp_edge_forces": (st, [ctypes.POINTER(etp_graph), vp, vp, u32, vp]),
         "etp_node_product": (st, [vp, i32, i32, vp, vp, vp, u32, vp]),
         "etp_channel_mix_vjp": (st, [vp, i32, vp, vp, vp, u32, vp]),
@@ -292,6 +293,7 @@ def etp_csr_transpose_workspace(n_src: int) -> int:
 
 ETP_OP_FWD, ETP_OP_VJP, ETP_OP_VJP2, ETP_OP_TRANSPOSE, ETP_OP_VJP_WS, ETP_OP_VJP2_WS = 0, 1, 2, 3, 4, 5
 ETP_OP_RADIAL_WGRAD = 6
+ETP_OP_MIX_WGRAD = 7
 
 
 def etp_workspace_size(plan: Plan, op: int, graph: Graph) -> int:
@@ -617,6 +619,31 @@ def etp_channel_mix_vjp_ex(plan: Plan, grad_y, W, grad_in, flags: int = 0, strea
                                       ETP_BF16 if bf else ETP_F32,
                                       _ptr(grad_in, "grad_in", torch.float32, n * plan.dout_rows * C, optional=True),
                                       flags, _stream(stream)), "etp_channel_mix_vjp_ex")
+
+
+def mix_wgrad_workspace(plan: Plan, n: int):
+    """A device workspace for etp_channel_mix_wgrad on n nodes (None when it does not split)."""
+    import torch
+    g = etp_graph()
+    g.n_dst, g.n_src, g.n_edges = n, 0, 0  # the size query reads only the counts
+    b = ctypes.c_size_t()
+    _check(lib.etp_workspace_size(plan.handle, ETP_OP_MIX_WGRAD, ctypes.byref(g), ctypes.byref(b)),
+           "etp_workspace_size")
+    return torch.empty(b.value, dtype=torch.uint8, device="cuda") if b.value else None
+
+
+def etp_channel_mix_wgrad(plan: Plan, inp, grad_y, grad_W, ws=None, flags: int = 0, stream=None):
+    """grad_W (the layout of W) = per path, the sum over nodes and components of
+    the input block times the cotangent row; ws from mix_wgrad_workspace."""
+    import torch
+    n = inp.shape[0] if inp is not None else 0
+    C = plan.C
+    wp, wb = _ws(ws)
+    _check(lib.etp_channel_mix_wgrad(plan.handle, n,
+                                     _ptr(inp, "in", torch.float32, n * plan.dout_rows * C, optional=True),
+                                     _ptr(grad_y, "grad_y", torch.float32, n * (plan.L + 1) ** 2 * C, optional=True),
+                                     _ptr(grad_W, "grad_W", torch.float32, sum(mix_rows(plan)) * C * C),
+                                     flags, wp, wb, _stream(stream)), "etp_channel_mix_wgrad")
 
 
 def etp_edge_forces(graph: Graph, grad_vec, forces, flags: int = 0, stream=None):

@@ -230,7 +230,9 @@ ETP_API etp_status etp_csr_transpose_noalloc(const etp_graph *g, int32_t *src_pt
  * edge, then two three-float partials of the bond-vector gradient per edge);
  * ETP_OP_RADIAL_WGRAD (the radial weight gradients) needs
  * (n_src + 64) * ETP_MAX_RADIAL_BASIS * P * C * 4 (per-source-node partials
- * and the runs of their ordered sum).
+ * and the runs of their ordered sum); ETP_OP_MIX_WGRAD
+ * (etp_channel_mix_wgrad on g->n_dst nodes) needs S * (number of weights) * 4
+ * for the S-way split over nodes it uses (0 when it does not split).
  * Host only; reads only the counts in g (its pointers may be NULL).
  * Errors: INVALID_ARGUMENT (null plan, g or bytes, a negative count, an
  * unknown op), UNSUPPORTED (n_edges >= 2^31). */
@@ -241,7 +243,8 @@ enum {
     ETP_OP_TRANSPOSE = 3,
     ETP_OP_VJP_WS = 4,
     ETP_OP_VJP2_WS = 5,
-    ETP_OP_RADIAL_WGRAD = 6
+    ETP_OP_RADIAL_WGRAD = 6,
+    ETP_OP_MIX_WGRAD = 7
 };
 ETP_API etp_status etp_workspace_size(etp_plan_t plan, int32_t op, const etp_graph *g, size_t *bytes);
 
@@ -465,6 +468,29 @@ ETP_API etp_status etp_channel_mix_vjp(etp_plan_t plan, int32_t n_nodes, const f
  * etp_channel_mix_ex is to etp_channel_mix. Errors as etp_channel_mix_ex. */
 ETP_API etp_status etp_channel_mix_vjp_ex(etp_plan_t plan, int32_t n_nodes, const float *grad_y, const void *W,
                                           int32_t w_dtype, float *grad_in, uint32_t flags, void *stream);
+
+/* Gradient of the channel mixing with respect to its weights (training the
+ * dense contraction after the tensor product: "Scaling the leading accuracy
+ * of deep equivariant models to biomolecular simulations of realistic size",
+ * section "Proposed method"):
+ *   grad_W_l[(q_p*C + u)*C + v] = sum_{i < n_nodes} sum_{m < 2l+1}
+ *                                 in[i][off_p + m][u] * grad_y[i][l*l + m][v]
+ * for every path p of order l = l3_p, in the layout of W (etp_channel_mix).
+ * in: DEVICE float [n_nodes][dout_rows][C]; grad_y: DEVICE float
+ * [n_nodes][(l_max+1)^2][C]; grad_W: DEVICE float, the size of W. fp32
+ * matrix-core products (16x16x4), fp32 accumulation; the sum over nodes is
+ * split over S workgroups per output tile, whose partial blocks go to ws and
+ * are added in split order (deterministic, no atomics). ws: NULL, or a
+ * 16-byte aligned DEVICE workspace of etp_workspace_size(plan,
+ * ETP_OP_MIX_WGRAD, g with n_dst = n_nodes) bytes; NULL or a smaller one
+ * means one workgroup per tile takes every node (same result up to rounding
+ * order, slower). flags: ETP_FLAG_ACCUMULATE adds into grad_W; with
+ * n_nodes = 0 grad_W is zeroed (or left as it is when accumulating).
+ * Errors: INVALID_ARGUMENT (null plan or grad_W, null in / grad_y with
+ * n_nodes > 0, negative n_nodes, other flags), WORKSPACE (misaligned ws),
+ * HIP. */
+ETP_API etp_status etp_channel_mix_wgrad(etp_plan_t plan, int32_t n_nodes, const float *in, const float *grad_y,
+                                         float *grad_W, uint32_t flags, void *ws, size_t ws_bytes, void *stream);
 
 /* Edge-local tensor product: the convolution's message without the
  * destination sum, one output block per edge (the pair-wise tensor product of

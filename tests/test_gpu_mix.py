@@ -147,3 +147,49 @@ def test_channel_mix_ex(L, C, n, bf16):
     g2 = gin.clone()
     etp.etp_channel_mix_vjp_ex(plan, dev(gy), Wd, g2, etp.ETP_FLAG_ACCUMULATE)
     assert rel_err(np_(g2), 2 * np_(gin)) < FP32_TOL
+
+
+# ------------------------------------------------------- weight gradient
+
+@pytest.mark.parametrize("L,C,n,ws", [(0, 8, 5, True), (1, 64, 37, True), (2, 128, 300, True), (2, 128, 300, False),
+                                      (3, 130, 600, True), (4, 64, 257, True), (2, 1, 9, True), (3, 200, 520, False),
+                                      (2, 128, 6000, True), (3, 64, 1024, True)])
+def test_channel_mix_wgrad(L, C, n, ws):
+    """etp_channel_mix_wgrad against the oracle within 1e-5: with the split over
+    nodes (workspace) and without; accumulation adds; run twice, bitwise equal."""
+    import torch
+    from equivariant_interatomic_potentials_amd import etp
+    say("mix wgrad", L, C, n, ws)
+    inp, _ = mix_case(L, C, n, seed=L * 10 + C + n)
+    gy = workloads.rng(n + C, "G").standard_normal((n, (L + 1) ** 2, C)).astype(np.float32)
+    plan = etp.etp_plan_create(L, C)
+    w = etp.mix_wgrad_workspace(plan, n) if ws else None
+    gW = torch.full((sum(oracle.mix_rows(L)) * C * C,), float("nan"), device="cuda")
+    etp.etp_channel_mix_wgrad(plan, dev(inp), dev(gy), gW, w)
+    ref = oracle.channel_mix_wgrad(L, inp, gy)
+    assert rel_err(np_(gW), ref) < FP32_TOL, rel_err(np_(gW), ref)
+    again = torch.empty_like(gW)
+    etp.etp_channel_mix_wgrad(plan, dev(inp), dev(gy), again, w)
+    assert torch.equal(again, gW)
+    acc = gW.clone()
+    etp.etp_channel_mix_wgrad(plan, dev(inp), dev(gy), acc, w, etp.ETP_FLAG_ACCUMULATE)
+    assert rel_err(np_(acc), 2 * ref) < FP32_TOL
+
+
+def test_channel_mix_wgrad_empty_and_split_used():
+    """No nodes: grad_W zeroed (left as it is when accumulating); the workspace
+    form splits at the micro node count."""
+    import torch
+    from equivariant_interatomic_potentials_amd import etp
+    say("mix wgrad empty")
+    L, C = 2, 64
+    plan = etp.etp_plan_create(L, C)
+    nw = sum(oracle.mix_rows(L)) * C * C
+    gW = torch.full((nw,), 3.0, device="cuda")
+    etp.etp_channel_mix_wgrad(plan, torch.zeros(0, plan.dout_rows, C, device="cuda"),
+                              torch.zeros(0, 9, C, device="cuda"), gW, None, etp.ETP_FLAG_ACCUMULATE)
+    assert torch.all(gW == 3.0)
+    etp.etp_channel_mix_wgrad(plan, torch.zeros(0, plan.dout_rows, C, device="cuda"),
+                              torch.zeros(0, 9, C, device="cuda"), gW)
+    assert torch.all(gW == 0.0)
+    assert etp.mix_wgrad_workspace(plan, 1024) is not None

@@ -32,7 +32,7 @@ def header_symbols():
 
 def test_header_symbols_exported():
     names = header_symbols()
-    assert len(names) == 35
+    assert len(names) == 36
     assert sorted(etp.ABI_SYMBOLS) == names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (etp_\w+)$", out, flags=re.M))
@@ -170,6 +170,13 @@ def test_call_validation_without_device():
         assert fn(plan.handle, 4, 8, 8, 5, 8, 0, None) == INV   # unknown dtype
         assert fn(plan.handle, 4, 8, 8, F32, 8, 2, None) == INV
         assert fn(plan.handle, 0, None, None, BF, None, 0, None) == 0
+    wg = lib.etp_channel_mix_wgrad
+    assert wg(None, 4, 8, 8, 8, 0, None, 0, None) == INV
+    assert wg(plan.handle, -1, 8, 8, 8, 0, None, 0, None) == INV
+    assert wg(plan.handle, 4, 8, 8, None, 0, None, 0, None) == INV          # grad_W required
+    assert wg(plan.handle, 4, None, 8, 8, 0, None, 0, None) == INV
+    assert wg(plan.handle, 4, 8, 8, 8, 2, None, 0, None) == INV             # only ACCUMULATE
+    assert wg(plan.handle, 4, 16, 16, 16, 0, 8, 64, None) == etp.ETP_ERR_WORKSPACE
     assert lib.etp_channel_mix_vjp(None, 4, 8, 8, 8, 0, None) == INV
     assert lib.etp_channel_mix_vjp(plan.handle, 4, 8, None, 8, 0, None) == INV
     assert lib.etp_channel_mix_vjp(plan.handle, 4, 8, 8, 8, 2, None) == INV
