@@ -43,7 +43,7 @@
 #include <cstdint>
 #include <type_traits>
 
-#include "etp_tables.hpp"
+#include "etp_device.hpp"
 
 namespace etp {
 
@@ -55,6 +55,7 @@ constexpr int kMixMaxPaths = 17;  // most paths of one output order (l_max 4, l3
 
 struct MixTab {
     int lout, C, n, Dout, Dy;
+    int nlmax;                   // most paths of one order
     int nl[5];                   // paths per output order
     int tiles0[6];               // prefix of 64-row tiles over the orders
     int off[5][kMixMaxPaths];    // first output row of each path of order l
@@ -79,27 +80,51 @@ __device__ __forceinline__ uint16_t mix_f2bf(float f)
 template <bool BF, int KW, bool VJP>
 __global__ void __launch_bounds__(256 * KW) mix2_kernel(const MixTab tb, const float *__restrict__ A,
                                                         const void *__restrict__ Wv, float *__restrict__ out,
-                                                        const int accumulate)
+                                                        const int accumulate, const int qg)
 {
     constexpr int KS = BF ? 40 : 36;  // Bt row stride (elements): 16-byte aligned rows
+    // 32-channel sub-chunks per iteration: two for bf16, whose products are
+    // four times shorter, so that each barrier covers as many loads in flight
+    constexpr int SUB = BF ? 2 : 1;
     using BT = std::conditional_t<BF, uint16_t, float>;
-    constexpr int kBtBytes = 2 * KW * kMixCols * KS * static_cast<int>(sizeof(BT));
+    constexpr int kBtBytes = 2 * KW * SUB * kMixCols * KS * static_cast<int>(sizeof(BT));
     constexpr int kRedBytes = (KW - 1) * 16 * 64 * 16;  // K-group tiles (a float4 per lane and tile)
     __shared__ __attribute__((aligned(16))) unsigned char smem[kBtBytes > kRedBytes ? kBtBytes : kRedBytes];
-    auto Bt = reinterpret_cast<BT (*)[KW][kMixCols][KS]>(smem);
+    auto Bt = reinterpret_cast<BT (*)[KW][SUB][kMixCols][KS]>(smem);
+    // VJP: each wave's 16 x 64 result rows pass through LDS so that they
+    // leave as whole 256-byte rows (the VJP's output is its largest stream)
+    constexpr int kOS = kMixCols + 4;
+    __shared__ __attribute__((aligned(16))) float otile[VJP ? 4 * 16 * kOS : 4];
     // the wave index, known to the compiler as uniform over the wave (so are
     // the chunk, path and order indices that follow from it)
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rg = wv & 3, kg = wv >> 2;  // row group of 16 rows, K group
+    // blockIdx.x -> (64-row tile over the orders, path (VJP), column tile):
+    // workgroups b and b + 8 run on the same XCD, so b = (g nw + w) 8 + x
+    // takes row tile 8 g + x and the w-th (path, column tile) pair: the
+    // workgroups that read a row tile's A rows run side by side on one XCD
+    // and read them through one L2, while consecutive row tiles (and the
+    // orders' unequal tiles) still spread over all XCDs. The grid is padded
+    // to whole groups of 8 row tiles (and, for the VJP, to the most paths of
+    // an order).
+    const int ncol = (tb.C + kMixCols - 1) / kMixCols, nw = VJP ? ncol * qg : ncol;
+    const int bx = blockIdx.x, xq = bx >> 3, w8 = xq % nw;
+    const int tflat = (xq / nw) * 8 + (bx & 7), ctile = w8 % ncol;
+    if (tflat >= tb.tiles0[tb.lout + 1])
+        return;  // the whole workgroup: padding of the last group
     int l = 0;
-    while (l < tb.lout && static_cast<int>(blockIdx.x) >= tb.tiles0[l + 1])
+    while (l < tb.lout && tflat >= tb.tiles0[l + 1])
         ++l;
-    const int qv = VJP ? static_cast<int>(blockIdx.z) : 0;
+    // VJP: this workgroup's paths are qv, qv + qg, ... below the order's
+    // count (qg = 1: all of them, one after another; qg = the most paths of
+    // an order: one path)
+    const int qv = VJP ? w8 / ncol : 0;
     if (VJP && qv >= tb.nl[l])
         return;  // the whole workgroup: this order has fewer paths
-    const int tile = blockIdx.x - tb.tiles0[l];
+    const int npath = VJP ? (tb.nl[l] - qv + qg - 1) / qg : 1;
+    const int tile = tflat - tb.tiles0[l];
     const int d = 2 * l + 1, M = tb.n * d, C = tb.C;
-    const int c0 = blockIdx.y * kMixCols;
+    const int c0 = ctile * kMixCols;
     const int kq = lane >> 4, col = lane & 15;
 
     const int ra = tile * 64 + rg * 16 + col;
@@ -115,12 +140,68 @@ __global__ void __launch_bounds__(256 * KW) mix2_kernel(const MixTab tb, const f
 #pragma unroll
     for (int t = 0; t < 4; ++t)
         acc[t] = mix_f4{0.f, 0.f, 0.f, 0.f};
+    // the tile's results (path q's rows for the VJP): lane l holds rows
+    // 4 (l / 16) + rr, column 16 t + l % 16 of each tile
+    auto store = [&](int q) {
+        if constexpr (VJP) {
+            float *ot = otile + rg * (16 * kOS);
+            wave_sync_lds();  // this wave's previous reads of its rows are done
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    ot[(4 * kq + rr) * kOS + 16 * t + col] = acc[t][rr];
+            wave_sync_lds();
+            const bool ovec = (C & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int e = lane + 64 * k, row = e >> 4, c4 = (e & 15) * 4;
+                const int r = tile * 64 + rg * 16 + row;
+                if (r >= M)
+                    continue;
+                const int i = r / d, m = r - i * d;
+                float *dst = out + (static_cast<int64_t>(i) * tb.Dout + tb.off[l][q] + m) * C + c0 + c4;
+                const float4 v = *reinterpret_cast<const float4 *>(ot + row * kOS + c4);
+                if (ovec && c0 + c4 + 4 <= C) {
+                    float4 o = v;
+                    if (accumulate) {
+                        const float4 p0 = *reinterpret_cast<const float4 *>(dst);
+                        o = make_float4(p0.x + v.x, p0.y + v.y, p0.z + v.z, p0.w + v.w);
+                    }
+                    *reinterpret_cast<float4 *>(dst) = o;
+                } else {
+                    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (c0 + c4 + j < C)
+                            dst[j] = accumulate ? dst[j] + vv[j] : vv[j];
+                }
+            }
+            return;
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int c = c0 + 16 * t + col;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = tile * 64 + rg * 16 + 4 * kq + rr;
+                if (r < M && c < C) {
+                    const int i = r / d, m = r - (r / d) * d;
+                    const int64_t row = VJP ? static_cast<int64_t>(i) * tb.Dout + tb.off[l][q] + m
+                                            : static_cast<int64_t>(i) * tb.Dy + l * l + m;
+                    float *dst = out + row * C + c;
+                    *dst = accumulate ? *dst + acc[t][rr] : acc[t][rr];
+                }
+            }
+        }
+    };
 
     // K group kg takes chunks kg, kg + KW, ...; every wave runs the same
     // number of iterations (one barrier each)
-    const int ncu = (C + 31) / 32, nchunk = VJP ? ncu : tb.nl[l] * ncu, nit = (nchunk + KW - 1) / KW;
-    float a_nx[8];
-    BT b_nx[8];
+    const int ncu = (C + 32 * SUB - 1) / (32 * SUB), nchunk = (VJP ? npath : tb.nl[l]) * ncu,
+              nit = (nchunk + KW - 1) / KW;
+    float a_nx[SUB][8];
+    BT b_nx[SUB][8];
     // W staging, thread t of a K group (t < 256):
     //   forward fp32: W rows k0 + t / 16 and + 16, columns 4 (t % 16) .. + 3
     //   forward bf16: W row k0 + t / 8, columns 8 (t % 8) .. + 7
@@ -132,105 +213,114 @@ __global__ void __launch_bounds__(256 * KW) mix2_kernel(const MixTab tb, const f
     auto fetch = [&](int ci) {
         if (ci >= nchunk) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                a_nx[i] = 0.f;
-                b_nx[i] = BT(0);
-            }
+            for (int j = 0; j < SUB; ++j)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    a_nx[j][i] = 0.f;
+                    b_nx[j][i] = BT(0);
+                }
             return;
         }
-        const int q = VJP ? qv : ci / ncu, k0 = (VJP ? ci : ci % ncu) * 32;
+        const int q = VJP ? qv + (ci / ncu) * qg : ci / ncu, kc = (ci % ncu) * 32 * SUB;
         const float *arow = VJP ? abase : abase + static_cast<int64_t>(tb.off[l][q]) * C;
-        const int kb = k0 + 8 * kq;
-        if (rok && vec4 && kb + 8 <= C) {
-            const float4 v0 = *reinterpret_cast<const float4 *>(arow + kb);
-            const float4 v1 = *reinterpret_cast<const float4 *>(arow + kb + 4);
-            a_nx[0] = v0.x; a_nx[1] = v0.y; a_nx[2] = v0.z; a_nx[3] = v0.w;
-            a_nx[4] = v1.x; a_nx[5] = v1.y; a_nx[6] = v1.z; a_nx[7] = v1.w;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const bool ok = rok && kb + i < C;
-                const float v = arow[ok ? kb + i : 0];  // in bounds either way
-                a_nx[i] = ok ? v : 0.f;
-            }
-        }
         const BT *W = static_cast<const BT *>(Wv) + tb.wofs[l] + static_cast<int64_t>(q) * C * C;
-        // element (row, col) of the chunk's W block for this thread, zero past
-        // the problem; loads stay in bounds (index 0 when out)
-        auto wat = [&](int row, int col) -> BT {
-            const bool ok = row < C && col < C;
-            const BT v = W[ok ? static_cast<int64_t>(row) * C + col : 0];
-            return ok ? v : BT(0);
-        };
-        if constexpr (VJP) {
-            const int row = c0 + sr, col = k0 + sc;
-            if (wal && row < C && col + 8 <= C) {
-                const BT *src = W + static_cast<int64_t>(row) * C + col;
-                if constexpr (BF) {
-                    const uint4 v = *reinterpret_cast<const uint4 *>(src);
+#pragma unroll
+        for (int j = 0; j < SUB; ++j) {
+            const int k0 = kc + 32 * j;
+            const int kb = k0 + 8 * kq;
+            if (rok && vec4 && kb + 8 <= C) {
+                const float4 v0 = *reinterpret_cast<const float4 *>(arow + kb);
+                const float4 v1 = *reinterpret_cast<const float4 *>(arow + kb + 4);
+                a_nx[j][0] = v0.x; a_nx[j][1] = v0.y; a_nx[j][2] = v0.z; a_nx[j][3] = v0.w;
+                a_nx[j][4] = v1.x; a_nx[j][5] = v1.y; a_nx[j][6] = v1.z; a_nx[j][7] = v1.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const bool ok = rok && kb + i < C;
+                    const float v = arow[ok ? kb + i : 0];  // in bounds either way
+                    a_nx[j][i] = ok ? v : 0.f;
+                }
+            }
+            // element (row, col) of the chunk's W block for this thread, zero past
+            // the problem; loads stay in bounds (index 0 when out)
+            auto wat = [&](int row, int col) -> BT {
+                const bool ok = row < C && col < C;
+                const BT v = W[ok ? static_cast<int64_t>(row) * C + col : 0];
+                return ok ? v : BT(0);
+            };
+            if constexpr (VJP) {
+                const int row = c0 + sr, col = k0 + sc;
+                if (wal && row < C && col + 8 <= C) {
+                    const BT *src = W + static_cast<int64_t>(row) * C + col;
+                    if constexpr (BF) {
+                        const uint4 v = *reinterpret_cast<const uint4 *>(src);
+                        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            b_nx[j][2 * i] = static_cast<uint16_t>(w4[i] & 0xFFFFu);
+                            b_nx[j][2 * i + 1] = static_cast<uint16_t>(w4[i] >> 16);
+                        }
+                    } else {
+                        const float4 v0 = *reinterpret_cast<const float4 *>(src);
+                        const float4 v1 = *reinterpret_cast<const float4 *>(src + 4);
+                        b_nx[j][0] = v0.x; b_nx[j][1] = v0.y; b_nx[j][2] = v0.z; b_nx[j][3] = v0.w;
+                        b_nx[j][4] = v1.x; b_nx[j][5] = v1.y; b_nx[j][6] = v1.z; b_nx[j][7] = v1.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        b_nx[j][i] = wat(row, col + i);
+                }
+            } else if constexpr (BF) {
+                const int row = k0 + sr, col = c0 + sc;
+                if (wal && row < C && col + 8 <= C) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(W + static_cast<int64_t>(row) * C + col);
                     const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        b_nx[2 * i] = static_cast<uint16_t>(w4[i] & 0xFFFFu);
-                        b_nx[2 * i + 1] = static_cast<uint16_t>(w4[i] >> 16);
+                        b_nx[j][2 * i] = static_cast<uint16_t>(w4[i] & 0xFFFFu);
+                        b_nx[j][2 * i + 1] = static_cast<uint16_t>(w4[i] >> 16);
                     }
                 } else {
-                    const float4 v0 = *reinterpret_cast<const float4 *>(src);
-                    const float4 v1 = *reinterpret_cast<const float4 *>(src + 4);
-                    b_nx[0] = v0.x; b_nx[1] = v0.y; b_nx[2] = v0.z; b_nx[3] = v0.w;
-                    b_nx[4] = v1.x; b_nx[5] = v1.y; b_nx[6] = v1.z; b_nx[7] = v1.w;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        b_nx[j][i] = wat(row, col + i);
                 }
             } else {
+                const int row = k0 + sr, col = c0 + sc;
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    b_nx[i] = wat(row, col + i);
-            }
-        } else if constexpr (BF) {
-            const int row = k0 + sr, col = c0 + sc;
-            if (wal && row < C && col + 8 <= C) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(W + static_cast<int64_t>(row) * C + col);
-                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+                for (int h = 0; h < 2; ++h) {
+                    const int rh = row + 16 * h;
+                    if (wal && rh < C && col + 4 <= C) {
+                        const float4 v = *reinterpret_cast<const float4 *>(W + static_cast<int64_t>(rh) * C + col);
+                        b_nx[j][4 * h] = v.x; b_nx[j][4 * h + 1] = v.y; b_nx[j][4 * h + 2] = v.z; b_nx[j][4 * h + 3] = v.w;
+                    } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    b_nx[2 * i] = static_cast<uint16_t>(w4[i] & 0xFFFFu);
-                    b_nx[2 * i + 1] = static_cast<uint16_t>(w4[i] >> 16);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    b_nx[i] = wat(row, col + i);
-            }
-        } else {
-            const int row = k0 + sr, col = c0 + sc;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int rh = row + 16 * h;
-                if (wal && rh < C && col + 4 <= C) {
-                    const float4 v = *reinterpret_cast<const float4 *>(W + static_cast<int64_t>(rh) * C + col);
-                    b_nx[4 * h] = v.x; b_nx[4 * h + 1] = v.y; b_nx[4 * h + 2] = v.z; b_nx[4 * h + 3] = v.w;
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        b_nx[4 * h + j] = wat(rh, col + j);
+                        for (int i = 0; i < 4; ++i)
+                            b_nx[j][4 * h + i] = wat(rh, col + i);
+                    }
                 }
             }
         }
     };
     // b_nx into the LDS tile Bt[column][k] of this K group
     auto stage = [&](int buf) {
-        if constexpr (VJP) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                Bt[buf][kg][sr][sc + i] = b_nx[i];
-        } else if constexpr (BF) {
+        for (int j = 0; j < SUB; ++j) {
+            if constexpr (VJP) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                Bt[buf][kg][sc + i][sr] = b_nx[i];
-        } else {
+                for (int i = 0; i < 8; ++i)
+                    Bt[buf][kg][j][sr][sc + i] = b_nx[j][i];
+            } else if constexpr (BF) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                Bt[buf][kg][sc + j][sr] = b_nx[j];
-                Bt[buf][kg][sc + j][sr + 16] = b_nx[4 + j];
+                for (int i = 0; i < 8; ++i)
+                    Bt[buf][kg][j][sc + i][sr] = b_nx[j][i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    Bt[buf][kg][j][sc + i][sr] = b_nx[j][i];
+                    Bt[buf][kg][j][sc + i][sr + 16] = b_nx[j][4 + i];
+                }
             }
         }
     };
@@ -240,10 +330,12 @@ __global__ void __launch_bounds__(256 * KW) mix2_kernel(const MixTab tb, const f
         const int buf = it & 1;
         const bool live = it * KW + kg < nchunk;  // uniform over the wave
         stage(buf);
-        float a[8];
+        float a[SUB][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            a[i] = a_nx[i];
+        for (int j = 0; j < SUB; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                a[j][i] = a_nx[j][i];
         // one barrier per iteration: the tile stores above are seen by every
         // wave, and the buffer written next (buf ^ 1) was last read before it
         __syncthreads();
@@ -251,25 +343,36 @@ __global__ void __launch_bounds__(256 * KW) mix2_kernel(const MixTab tb, const f
             fetch((it + 1) * KW + kg);
         if (!live)
             continue;
-        if constexpr (BF) {
-            mix_bf8 av;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                av[i] = __builtin_bit_cast(__bf16, mix_f2bf(a[i]));
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const mix_bf8 bv = *reinterpret_cast<const mix_bf8 *>(&Bt[buf][kg][16 * t + col][8 * kq]);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[t], 0, 0, 0);
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float4 b0 = *reinterpret_cast<const float4 *>(&Bt[buf][kg][16 * t + col][8 * kq]);
-                const float4 b1 = *reinterpret_cast<const float4 *>(&Bt[buf][kg][16 * t + col][8 * kq + 4]);
-                const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        for (int j = 0; j < SUB; ++j) {
+            if constexpr (BF) {
+                mix_bf8 av;
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], bb[i], acc[t], 0, 0, 0);
+                    av[i] = __builtin_bit_cast(__bf16, mix_f2bf(a[j][i]));
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const mix_bf8 bv = *reinterpret_cast<const mix_bf8 *>(&Bt[buf][kg][j][16 * t + col][8 * kq]);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[t], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float4 b0 = *reinterpret_cast<const float4 *>(&Bt[buf][kg][j][16 * t + col][8 * kq]);
+                    const float4 b1 = *reinterpret_cast<const float4 *>(&Bt[buf][kg][j][16 * t + col][8 * kq + 4]);
+                    const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j][i], bb[i], acc[t], 0, 0, 0);
+                }
+            }
+        }
+        if constexpr (VJP && KW == 1) {
+            if ((it + 1) % ncu == 0) {  // the path's last chunk: store it, start the next
+                store(qv + (it / ncu) * qg);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    acc[t] = mix_f4{0.f, 0.f, 0.f, 0.f};
             }
         }
     }
@@ -295,22 +398,9 @@ __global__ void __launch_bounds__(256 * KW) mix2_kernel(const MixTab tb, const f
         }
     }
 
-    // lane l holds rows 4 (l / 16) + rr, column 16 t + l % 16 of each tile
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int c = c0 + 16 * t + col;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int r = tile * 64 + rg * 16 + 4 * kq + rr;
-            if (r < M && c < C) {
-                const int i = r / d, m = r - (r / d) * d;
-                const int64_t row = VJP ? static_cast<int64_t>(i) * tb.Dout + tb.off[l][qv] + m
-                                        : static_cast<int64_t>(i) * tb.Dy + l * l + m;
-                float *dst = out + row * C + c;
-                *dst = accumulate ? *dst + acc[t][rr] : acc[t][rr];
-            }
-        }
-    }
+    // (the VJP with one K group stored each path as it finished)
+    if constexpr (!VJP || KW > 1)
+        store(qv);
 }
 
 // Weight gradient of the mixing (the sum over nodes that training needs):
@@ -478,6 +568,9 @@ static MixTab mix_table(int C, int n)
         const int l3 = T.path[p].l3;
         tb.off[l3][tb.nl[l3]++] = T.path[p].out_row;
     }
+    tb.nlmax = 1;
+    for (int l = 0; l <= L; ++l)
+        tb.nlmax = tb.nl[l] > tb.nlmax ? tb.nl[l] : tb.nlmax;
     tb.tiles0[0] = 0;
     tb.wofs[0] = 0;
     for (int l = 0; l <= L; ++l) {
@@ -517,17 +610,27 @@ static hipError_t launch_mix2(int L, int C, int n, const float *A, const void *W
     MixTab tb;
     if (!mix_table_for(L, C, n, &tb))
         return hipErrorInvalidValue;
-    int maxnl = 1;
-    for (int l = 0; l <= L; ++l)
-        maxnl = tb.nl[l] > maxnl ? tb.nl[l] : maxnl;
-    const dim3 grid(tb.tiles0[L + 1], (C + kMixCols - 1) / kMixCols, VJP ? maxnl : 1);
-    int64_t live = static_cast<int64_t>(grid.y) * (VJP ? 0 : grid.x);
-    if (VJP)  // workgroups past an order's path count leave at once
+    const int ncol = (C + kMixCols - 1) / kMixCols;
+    // workgroups: one per (row tile, column tile); the VJP also gives each
+    // path its own workgroup (qg = most paths of an order) unless that grid
+    // is large enough without (qg = 1: a workgroup walks all its order's
+    // paths, storing each as it finishes)
+    const int64_t tiles = static_cast<int64_t>(tb.tiles0[L + 1]) * ncol;
+    int qg = 1, kw = mix_kgroups(tiles);
+    if (VJP && kw > 1) {
+        qg = tb.nlmax;
+        int64_t live = 0;  // workgroups past an order's path count leave at once
         for (int l = 0; l <= L; ++l)
-            live += static_cast<int64_t>(grid.y) * (tb.tiles0[l + 1] - tb.tiles0[l]) * tb.nl[l];
-    const int kw = mix_kgroups(live), acc = accumulate ? 1 : 0;
+            live += static_cast<int64_t>(ncol) * (tb.tiles0[l + 1] - tb.tiles0[l]) * tb.nl[l];
+        kw = mix_kgroups(live);
+    }
+    const int64_t nwg = static_cast<int64_t>((tb.tiles0[L + 1] + 7) / 8) * 8 * ncol * qg;
+    if (nwg > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(nwg));
+    const int acc = accumulate ? 1 : 0;
 #define ETP_MIX2(BF, KWV)                                                                                            \
-    hipLaunchKernelGGL((mix2_kernel<BF, KWV, VJP>), grid, dim3(256 * KWV), 0, stream, tb, A, W, out, acc)
+    hipLaunchKernelGGL((mix2_kernel<BF, KWV, VJP>), grid, dim3(256 * KWV), 0, stream, tb, A, W, out, acc, qg)
     if (bf16) {
         if (kw == 4)
             ETP_MIX2(true, 4);
