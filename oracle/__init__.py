@@ -89,6 +89,8 @@ def _load():
         lib.oracle_node_product_vjp.argtypes = [ctypes.c_int] * 4 + [_f64p, _f64p, _f64p, _f64p]
         lib.oracle_channel_mix_vjp.restype = ctypes.c_int
         lib.oracle_channel_mix_vjp.argtypes = [ctypes.c_int] * 5 + [_f64p, _f64p, _f64p]
+        lib.oracle_node_product_wgrad.restype = ctypes.c_int
+        lib.oracle_node_product_wgrad.argtypes = [ctypes.c_int] * 4 + [_f64p, _f64p, _f64p, _f64p]
         lib.oracle_channel_mix_wgrad.restype = ctypes.c_int
         lib.oracle_channel_mix_wgrad.argtypes = [ctypes.c_int] * 5 + [_f64p, _f64p, _f64p]
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -398,6 +400,20 @@ def node_product_vjp(L, A, W, G, nu):
     if _load().oracle_node_product_vjp(L, C, n, nu, _p(A, _f64p), _p(W, _f64p), _p(G, _f64p), _p(gA, _f64p)):
         raise ValueError("bad arguments")
     return gA
+
+
+def node_product_wgrad(L, A, W, G, nu):
+    """gW[nu-1, P, C] = d<G, node_product(L, A, W, nu)>/dW (a sum over nodes)."""
+    A = np.ascontiguousarray(A, np.float64)
+    n, D, C = A.shape
+    G = np.ascontiguousarray(G, np.float64)
+    P = len(paths(L))
+    W = np.ascontiguousarray(np.zeros((1,)) if W is None else W, np.float64)
+    gW = np.zeros((max(nu - 1, 0), P, C))
+    if _load().oracle_node_product_wgrad(L, C, n, nu, _p(A, _f64p), _p(W, _f64p), _p(G, _f64p),
+                                         _p(_nz(gW.reshape(-1)), _f64p)):
+        raise ValueError("bad arguments")
+    return gW
 
 
 def neighbor_row(pos, box, rc, i):

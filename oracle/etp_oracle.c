@@ -936,6 +936,72 @@ int oracle_node_product_vjp(int L, int C, int n, int nu, const double *A, const 
     return 0;
 }
 
+/* Gradient of <G, out> of the node-local product with respect to its weights
+ * (a sum over every node; training the ladder): with Bbar_{k+1} the adjoint of
+ * B_{k+1} from the reverse recursion of oracle_node_product_vjp,
+ *   gW[k-1][p][u] = sum_i sum_{(m1, m2, m3) in p} C * Bbar_{k+1}[l3,m3,u] * B_k[l1,m1,u] * A[l2,m2,u]
+ * for k = 1 .. nu-1. Nodes in index order, serially. */
+int oracle_node_product_wgrad(int L, int C, int n, int nu, const double *A, const double *W, const double *G,
+                              double *gW)
+{
+    table t;
+    if (nu < 1 || table_make(L, L, L, &t))
+        return -1;
+    const int D = (L + 1) * (L + 1), P = t.P;
+    for (int64_t q = 0; q < (int64_t)(nu - 1) * P * C; ++q)
+        gW[q] = 0.0;
+    double *B = (double *)malloc(sizeof(double) * (size_t)nu * D * C); /* B_1 .. B_nu of one node */
+    double *adj = (double *)malloc(sizeof(double) * D * C);            /* adjoint of B_{k+1} */
+    double *nadj = (double *)malloc(sizeof(double) * D * C);
+    for (int i = 0; i < n; ++i) {
+        const double *Ai = A + (int64_t)i * D * C, *Gi = G + (int64_t)i * D * C;
+        for (int q = 0; q < D * C; ++q)
+            B[q] = Ai[q];
+        for (int k = 1; k < nu; ++k) {
+            double *Bk = B + (int64_t)(k - 1) * D * C, *Bn = B + (int64_t)k * D * C;
+            for (int q = 0; q < D * C; ++q)
+                Bn[q] = 0.0;
+            for (int p = 0; p < P; ++p) {
+                const int l1 = t.path[3 * p], l2 = t.path[3 * p + 1], l3 = t.path[3 * p + 2];
+                const double *Wv = W + ((int64_t)(k - 1) * P + p) * C;
+                for (int q = t.ptr[p]; q < t.ptr[p + 1]; ++q) {
+                    const int s1 = l1 * l1 + l1 + t.m[3 * q], s2 = l2 * l2 + l2 + t.m[3 * q + 1];
+                    const int s3 = l3 * l3 + l3 + t.m[3 * q + 2];
+                    for (int u = 0; u < C; ++u)
+                        Bn[s3 * C + u] += Wv[u] * t.val[q] * Bk[s1 * C + u] * Ai[s2 * C + u];
+                }
+            }
+        }
+        for (int q = 0; q < D * C; ++q)
+            adj[q] = Gi[q];                       /* adjoint of B_nu */
+        for (int k = nu - 1; k >= 1; --k) {      /* step k maps B_k to B_{k+1} */
+            const double *Bk = B + (int64_t)(k - 1) * D * C;
+            for (int q = 0; q < D * C; ++q)
+                nadj[q] = Gi[q];
+            for (int p = 0; p < P; ++p) {
+                const int l1 = t.path[3 * p], l2 = t.path[3 * p + 1], l3 = t.path[3 * p + 2];
+                const double *Wv = W + ((int64_t)(k - 1) * P + p) * C;
+                double *gWp = gW + ((int64_t)(k - 1) * P + p) * C;
+                for (int q = t.ptr[p]; q < t.ptr[p + 1]; ++q) {
+                    const int s1 = l1 * l1 + l1 + t.m[3 * q], s2 = l2 * l2 + l2 + t.m[3 * q + 1];
+                    const int s3 = l3 * l3 + l3 + t.m[3 * q + 2];
+                    for (int u = 0; u < C; ++u) {
+                        gWp[u] += t.val[q] * adj[s3 * C + u] * Bk[s1 * C + u] * Ai[s2 * C + u];
+                        nadj[s1 * C + u] += Wv[u] * t.val[q] * adj[s3 * C + u] * Ai[s2 * C + u];
+                    }
+                }
+            }
+            for (int q = 0; q < D * C; ++q)
+                adj[q] = nadj[q];
+        }
+    }
+    free(B);
+    free(adj);
+    free(nadj);
+    table_free(&t);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Neighbour list                                                            */
 /* ------------------------------------------------------------------------ */

@@ -59,6 +59,10 @@ MUTANTS = [
      "const float dc = qi[c] - or_wrap(pos[3 * j + c], box[c]);"),
     ("nl_self", "if (j == i)\n            continue;", "if (j == i && i < 0)\n            continue;"),
     ("nl_no_wrap", "qi[c] = or_wrap(pos[3 * i + c], box[c]);", "qi[c] = pos[3 * i + c];"),
+    ("np_wgrad_drop_B", "gWp[u] += t.val[q] * adj[s3 * C + u] * Bk[s1 * C + u] * Ai[s2 * C + u];",
+     "gWp[u] += t.val[q] * adj[s3 * C + u] * Ai[s1 * C + u] * Ai[s2 * C + u];"),
+    ("np_wgrad_step", "double *gWp = gW + ((int64_t)(k - 1) * P + p) * C;",
+     "double *gWp = gW + ((int64_t)(nu - 1 - k) * P + p) * C;"),
     ("np_weight_step", "const double *Wp = W + ((int64_t)(k - 1) * P + p) * C;",
      "const double *Wp = W + ((int64_t)(nu - 1 - k) * P + p) * C;"),
     ("np_operands_swapped", "NB[r3 * C + u] += Wp[u] * t.val[q] * B[r1 * C + u] * Ai[r2 * C + u];",

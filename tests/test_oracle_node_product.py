@@ -168,3 +168,57 @@ def test_vjp_rotation_covariance():
 
     lhs = oracle.node_product_vjp(L, rot(A), W, rot(G), nu)
     np.testing.assert_allclose(lhs, rot(oracle.node_product_vjp(L, A, W, G, nu)), atol=1e-9)
+
+
+# ------------------------------------------------------- weight gradient
+
+def _case(L, nu, n=3, C=2, seed=0):
+    g = np.random.default_rng(seed)
+    P = len(paths(L))
+    A = g.standard_normal((n, (L + 1) ** 2, C))
+    W = g.standard_normal((nu - 1, P, C)) / math.sqrt(P)
+    G = g.standard_normal((n, (L + 1) ** 2, C))
+    return A, W, G
+
+
+@pytest.mark.parametrize("L,nu", [(1, 2), (2, 3), (3, 4), (2, 5)])
+def test_wgrad_euler_identity(L, nu):
+    """B_k is homogeneous of degree k - 1 in the weights, so
+    <gW, W> = sum_{k >= 2} (k - 1) <G, B_k>, with B_k = out(nu = k) - out(nu = k - 1)
+    from the forward ladder."""
+    A, W, G = _case(L, nu, seed=L + nu)
+    gW = oracle.node_product_wgrad(L, A, W, G, nu)
+    lhs = (gW * W).sum()
+    rhs = 0.0
+    prev = oracle.node_product(L, A, None, 1)
+    for k in range(2, nu + 1):
+        cur = oracle.node_product(L, A, W[:k - 1], k)
+        rhs += (k - 1) * (G * (cur - prev)).sum()
+        prev = cur
+    assert abs(lhs - rhs) < 1e-10 * max(1.0, abs(rhs))
+
+
+@pytest.mark.parametrize("L,nu", [(2, 3), (3, 4)])
+def test_wgrad_finite_differences(L, nu):
+    """Central differences of <G, out> in single weights (every step, several paths)."""
+    A, W, G = _case(L, nu, seed=7 * L + nu)
+    gW = oracle.node_product_wgrad(L, A, W, G, nu)
+    g = np.random.default_rng(11)
+    h = 1e-5
+    for _ in range(12):
+        idx = tuple(int(g.integers(0, s)) for s in W.shape)
+        Wp, Wm = W.copy(), W.copy()
+        Wp[idx] += h
+        Wm[idx] -= h
+        fd = ((G * oracle.node_product(L, A, Wp, nu)).sum() - (G * oracle.node_product(L, A, Wm, nu)).sum()) / (2 * h)
+        assert abs(fd - gW[idx]) < 1e-7 * max(1.0, abs(fd)), (idx, fd, gW[idx])
+
+
+def test_wgrad_order_one_is_empty_and_additive():
+    """nu = 1 has no weights; gW of a batch is the sum of the per-node gW."""
+    A, W, G = _case(2, 1)
+    assert oracle.node_product_wgrad(2, A, None, G, 1).size == 0
+    A, W, G = _case(2, 3, n=4, seed=5)
+    whole = oracle.node_product_wgrad(2, A, W, G, 3)
+    parts = sum(oracle.node_product_wgrad(2, A[i:i + 1], W, G[i:i + 1], 3) for i in range(4))
+    np.testing.assert_allclose(whole, parts, rtol=1e-12, atol=1e-12)
