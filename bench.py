@@ -615,6 +615,12 @@ def time_node_product(etp, L, nu, reps, n=4096, C=128):
     fv = float(n) * C * ((nu - 1) * (nu - 2) // 2 * f_step + (nu - 1) * (dout + 2 * nnz + 4 * groups))
     res.update({"vjp_ms": round(tv * 1e3, 4), "vjp_algo_TFLOPs": fv / tv / 1e12,
                 "vjp_valu_frac": fv / tv / 1e12 / VALU_PEAK_TFLOPS})
+    # the VJP with the weight gradient (per-node partials, then their ordered
+    # sum over the nodes)
+    ws = etp.node_product_wgrad_workspace(plan, n, nu)
+    gW = torch.empty_like(W)
+    tw = time_calls(lambda: etp.etp_node_product_vjp_wgrad(plan, A, W, G, gA, gW, nu, ws), reps)
+    res.update({"vjp_wgrad_ms": round(tw * 1e3, 4)})
     return res
 
 

@@ -56,6 +56,9 @@ hipError_t launch_edge_tp_vjp(int L, int C, int64_t E, const float *vec, const f
 {
     ETP_BY_L(edge_tp_vjp_l, C, E, vec, V, w, G, gV, gw, gr, accumulate, stream)
 }
+size_t node_product_wgrad_workspace_bytes(int L, int C, int n, int nu);
+hipError_t launch_node_product_wgrad(int L, int C, int n, int nu, const float *A, const float *W, const float *G,
+                                     float *gA, float *gW, bool accumulate, float *ws, hipStream_t stream);
 hipError_t launch_node_product_vjp(int L, int C, int n, int nu, const float *A, const float *W, const float *G,
                                    float *gA, bool accumulate, hipStream_t stream);
 hipError_t launch_edge_tp_vjp2(int L, int C, int64_t E, const float *vec, const float *V, const float *w,
@@ -1150,6 +1153,34 @@ etp_status etp_node_product_vjp(etp_plan_t plan, int32_t n_nodes, int32_t corr_o
         return ETP_ERR_INVALID_ARGUMENT;
     return hip_status(etp::launch_node_product_vjp(plan->L, plan->C, n_nodes, corr_order, A, W, grad_out, grad_A,
                                                    flags & ETP_FLAG_ACCUMULATE, static_cast<hipStream_t>(stream)));
+}
+
+etp_status etp_node_product_wgrad_workspace(etp_plan_t plan, int32_t n_nodes, int32_t corr_order, size_t *bytes)
+{
+    if (!plan || !bytes || n_nodes < 0 || corr_order < 2 || corr_order > 8)
+        return ETP_ERR_INVALID_ARGUMENT;
+    *bytes = etp::node_product_wgrad_workspace_bytes(plan->L, plan->C, n_nodes, corr_order);
+    return ETP_OK;
+}
+
+etp_status etp_node_product_vjp_wgrad(etp_plan_t plan, int32_t n_nodes, int32_t corr_order, const float *A,
+                                      const float *W, const float *grad_out, float *grad_A, float *grad_W,
+                                      uint32_t flags, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!plan || n_nodes < 0 || corr_order < 2 || corr_order > 8 || !grad_W)
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (flags & ~static_cast<uint32_t>(ETP_FLAG_ACCUMULATE))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (plan->dtype != ETP_F32)
+        return ETP_ERR_UNSUPPORTED;
+    if (n_nodes > 0 && (!A || !grad_out || !W))
+        return ETP_ERR_INVALID_ARGUMENT;
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & 15u) ||
+        ws_bytes < etp::node_product_wgrad_workspace_bytes(plan->L, plan->C, n_nodes, corr_order))
+        return ETP_ERR_WORKSPACE;
+    return hip_status(etp::launch_node_product_wgrad(plan->L, plan->C, n_nodes, corr_order, A, W, grad_out, grad_A,
+                                                     grad_W, (flags & ETP_FLAG_ACCUMULATE) != 0,
+                                                     static_cast<float *>(ws), static_cast<hipStream_t>(stream)));
 }
 
 etp_status etp_edge_forces(const etp_graph *g, const float *grad_vec, float *forces, uint32_t flags, void *stream)

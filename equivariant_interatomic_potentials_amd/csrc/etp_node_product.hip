@@ -26,6 +26,21 @@
 
 namespace etp {
 
+size_t block_sum_tmp_floats(int total);
+hipError_t launch_block_sum(int64_t n, int64_t stride, int total, const float *part, float *tmp, float *out,
+                            bool accumulate, hipStream_t stream);
+
+static const Table &table_for_l(int L)
+{
+    switch (L) {
+    case 0: return kTab<0>;
+    case 1: return kTab<1>;
+    case 2: return kTab<2>;
+    case 3: return kTab<3>;
+    default: return kTab<4>;
+    }
+}
+
 // Registers: A, B_k, B_{k+1} and the running sum (4 (l_max+1)^2 values) plus
 // a ring of kNpPrefetch weights, slot = path % kNpPrefetch. While path p
 // computes, its slot is refilled for its next user (path p + kNpPrefetch, or
@@ -148,16 +163,23 @@ __device__ __forceinline__ void np_step(const float *a, const float *b, float *n
     });
 }
 
-template <int L>
+template <int L, bool WG>
 constexpr int np_vjp_waves_per_eu()
 {
-    return L <= 2 ? 4 : (L == 3 ? 3 : 2);
+    // (the weight-gradient form holds one more product per group: one step
+    // lower in occupancy at l_max >= 3, where it would spill otherwise)
+    return L <= 2 ? 4 : (L == 3 ? (WG ? 2 : 3) : (WG ? 1 : 2));
 }
 
-template <int L, bool ACC>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(np_vjp_waves_per_eu<L>())))
+// WG: also the weight gradient's per-node partials, gwp[i][k][p][u] =
+// sum_{(m1, m2, m3) in p} C Bbar_{k+2}[l3, m3] B_{k+1}[l1, m1] A[l2, m2] for
+// forward step k (W[k]), to be summed over the nodes in order afterwards;
+// gA is then optional (NULL: not stored).
+template <int L, bool ACC, bool WG>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(np_vjp_waves_per_eu<L, WG>())))
 node_product_vjp_kernel(const int n, const int C, const int nu, const float *__restrict__ A,
-                        const float *__restrict__ W, const float *__restrict__ G, float *__restrict__ gA)
+                        const float *__restrict__ W, const float *__restrict__ G, float *__restrict__ gA,
+                        float *__restrict__ gwp)
 {
     constexpr int D = (L + 1) * (L + 1), P = kTab<L>.P, PF = kNpPrefetch;
     const int lane = threadIdx.x & 63;
@@ -173,6 +195,9 @@ node_product_vjp_kernel(const int n, const int C, const int nu, const float *__r
     const rsrc_t rg = make_rsrc(G + static_cast<int64_t>(i) * D * C, D * rowb);
     const rsrc_t rw = make_rsrc(W, static_cast<uint32_t>((nu - 1) * P * C * 4));
     auto wload = [&](int k, int q) { return bload<float>(rw, vo, static_cast<uint32_t>((k * P + q) * C * 4)); };
+    // this node's block of weight-gradient partials ([nu-1][P][C])
+    const rsrc_t rgw = make_rsrc(WG ? gwp + static_cast<int64_t>(i) * (nu - 1) * P * C : nullptr,
+                                 WG ? static_cast<uint32_t>((nu - 1) * P * C * 4) : 0u);
 
     float a[D], ga[D], bb[D];
     static_range<0, D>([&](auto r) {
@@ -200,23 +225,46 @@ node_product_vjp_kernel(const int n, const int C, const int nu, const float *__r
             const float w = wr[p % PF];
             if constexpr (p + PF < P)
                 wr[p % PF] = wload(k, p + PF);
-            float wb[2 * pa.l3 + 1];
-            static_range<0, 2 * pa.l3 + 1>([&](auto m) { wb[m] = w * bb[pa.l3 * pa.l3 + m]; });
-            static_range<kTab<L>.path_ab0[p], kTab<L>.path_ab0[p + 1]>([&](auto gc) {
-                constexpr ABGroup g = kTab<L>.ab[gc];
-                constexpr int r1 = pa.l1 * pa.l1 + pa.l1 + g.m1, r2 = pa.l2 * pa.l2 + pa.l2 + g.m2;
-                float c = 0.f;
-                static_range<g.t0, g.t1>([&](auto ec) {
-                    constexpr Entry e = kTab<L>.nz[kTab<L>.ab_entries[ec]];
-                    c = __builtin_fmaf(e.fval, wb[e.m3 + pa.l3], c);
+            if constexpr (!WG) {
+                float wb[2 * pa.l3 + 1];
+                static_range<0, 2 * pa.l3 + 1>([&](auto m) { wb[m] = w * bb[pa.l3 * pa.l3 + m]; });
+                static_range<kTab<L>.path_ab0[p], kTab<L>.path_ab0[p + 1]>([&](auto gc) {
+                    constexpr ABGroup g = kTab<L>.ab[gc];
+                    constexpr int r1 = pa.l1 * pa.l1 + pa.l1 + g.m1, r2 = pa.l2 * pa.l2 + pa.l2 + g.m2;
+                    float c = 0.f;
+                    static_range<g.t0, g.t1>([&](auto ec) {
+                        constexpr Entry e = kTab<L>.nz[kTab<L>.ab_entries[ec]];
+                        c = __builtin_fmaf(e.fval, wb[e.m3 + pa.l3], c);
+                    });
+                    nbb[r1] = __builtin_fmaf(c, a[r2], nbb[r1]);
+                    ga[r2] = __builtin_fmaf(c, b[r1], ga[r2]);
                 });
-                nbb[r1] = __builtin_fmaf(c, a[r2], nbb[r1]);
-                ga[r2] = __builtin_fmaf(c, b[r1], ga[r2]);
-            });
+            } else {
+                // the same with the weight factored out: cq = sum C Bbar (per
+                // (m1, m2) group), c = w cq, and the weight's cotangent
+                // sum cq B[l1, m1] A[l2, m2] of this node
+                float gw = 0.f;
+                static_range<kTab<L>.path_ab0[p], kTab<L>.path_ab0[p + 1]>([&](auto gc) {
+                    constexpr ABGroup g = kTab<L>.ab[gc];
+                    constexpr int r1 = pa.l1 * pa.l1 + pa.l1 + g.m1, r2 = pa.l2 * pa.l2 + pa.l2 + g.m2;
+                    float cq = 0.f;
+                    static_range<g.t0, g.t1>([&](auto ec) {
+                        constexpr Entry e = kTab<L>.nz[kTab<L>.ab_entries[ec]];
+                        cq = __builtin_fmaf(e.fval, bb[pa.l3 * pa.l3 + e.m3 + pa.l3], cq);
+                    });
+                    const float c = w * cq;
+                    nbb[r1] = __builtin_fmaf(c, a[r2], nbb[r1]);
+                    ga[r2] = __builtin_fmaf(c, b[r1], ga[r2]);
+                    gw = __builtin_fmaf(cq, b[r1] * a[r2], gw);
+                });
+                bstore<float>(gw, rgw, vo, static_cast<uint32_t>((k * P + p) * C * 4));
+            }
             __builtin_amdgcn_sched_barrier(0);
         });
         static_range<0, D>([&](auto r) { bb[r] = nbb[r]; });
     }
+    if (WG && !gA)
+        return;
     const rsrc_t ro = make_rsrc(gA + static_cast<int64_t>(i) * D * C, D * rowb);
     static_range<0, D>([&](auto r) {
         float v = ga[r] + bb[r];  // B_1 = A
@@ -236,11 +284,11 @@ hipError_t launch_node_product_vjp(int L, int C, int n, int nu, const float *A, 
 #define ETP_NPV_CASE(LL)                                                                                      \
     case LL:                                                                                                  \
         if (accumulate)                                                                                       \
-            hipLaunchKernelGGL(HIP_KERNEL_NAME(node_product_vjp_kernel<LL, true>), grid, block, 0, stream, n, \
-                               C, nu, A, W, G, gA);                                                           \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(node_product_vjp_kernel<LL, true, false>), grid, block, 0,     \
+                               stream, n, C, nu, A, W, G, gA, nullptr);                                       \
         else                                                                                                  \
-            hipLaunchKernelGGL(HIP_KERNEL_NAME(node_product_vjp_kernel<LL, false>), grid, block, 0, stream,   \
-                               n, C, nu, A, W, G, gA);                                                        \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(node_product_vjp_kernel<LL, false, false>), grid, block, 0,    \
+                               stream, n, C, nu, A, W, G, gA, nullptr);                                       \
         break;
     switch (L) {
         ETP_NPV_CASE(0) ETP_NPV_CASE(1) ETP_NPV_CASE(2) ETP_NPV_CASE(3) ETP_NPV_CASE(4)
@@ -248,6 +296,51 @@ hipError_t launch_node_product_vjp(int L, int C, int n, int nu, const float *A, 
     }
 #undef ETP_NPV_CASE
     return hipGetLastError();
+}
+
+// Workspace of the weight gradient: per-node partial blocks of (nu-1) P C
+// floats, then the ordered sum's runs.
+size_t node_product_wgrad_workspace_bytes(int L, int C, int n, int nu)
+{
+    if (L < 0 || L > 4 || nu < 2 || n < 0)
+        return 0;
+    const int P = table_for_l(L).P;
+    const int64_t blk = static_cast<int64_t>(nu - 1) * P * C;
+    return sizeof(float) * (static_cast<size_t>(n) * blk + block_sum_tmp_floats(static_cast<int>(blk)));
+}
+
+hipError_t launch_node_product_wgrad(int L, int C, int n, int nu, const float *A, const float *W, const float *G,
+                                     float *gA, float *gW, bool accumulate, float *ws, hipStream_t stream)
+{
+    const int P = table_for_l(L).P;
+    const int64_t blk = static_cast<int64_t>(nu - 1) * P * C;
+    if (blk <= 0)
+        return hipSuccess;
+    if (n > 0) {
+        const int64_t waves = static_cast<int64_t>(n) * ((C + 63) / 64);
+        const dim3 grid(static_cast<unsigned>((waves + 3) / 4)), block(256);
+#define ETP_NPW_CASE(LL)                                                                                      \
+    case LL:                                                                                                  \
+        if (accumulate)                                                                                       \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(node_product_vjp_kernel<LL, true, true>), grid, block, 0,      \
+                               stream, n, C, nu, A, W, G, gA, ws);                                            \
+        else                                                                                                  \
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(node_product_vjp_kernel<LL, false, true>), grid, block, 0,     \
+                               stream, n, C, nu, A, W, G, gA, ws);                                            \
+        break;
+        switch (L) {
+            ETP_NPW_CASE(0) ETP_NPW_CASE(1) ETP_NPW_CASE(2) ETP_NPW_CASE(3) ETP_NPW_CASE(4)
+        default: return hipErrorInvalidValue;
+        }
+#undef ETP_NPW_CASE
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    // the partials summed over the nodes in index order (with no nodes: zero,
+    // or left as they are when accumulating)
+    return launch_block_sum(n, blk, static_cast<int>(blk), ws, ws + static_cast<size_t>(n) * blk, gW, accumulate,
+                            stream);
 }
 
 hipError_t launch_node_product(int L, int C, int n, int nu, const float *A, const float *W, float *out,

@@ -38,7 +38,7 @@ ABI_SYMBOLS = ("etp_plan_create", "etp_plan_destroy", "etp_plan_info", "etp_plan
                "etp_neighbor_workspace", "etp_neighbor_count", "etp_neighbor_fill", "etp_node_product", "etp_node_product_vjp", "etp_channel_mix_vjp",
                "etp_edge_tp_fwd", "etp_edge_tp_vjp", "etp_edge_tp_vjp2",
                "etp_csr_transpose_noalloc", "etp_edge_conv_vjp_ws", "etp_edge_conv_vjp2_ws",
-               "etp_edge_conv_vjp_radial_wgrad", "etp_edge_conv_vjp2_radial_wgrad", "etp_channel_mix_ex", "etp_channel_mix_vjp_ex", "etp_channel_mix_wgrad",
+               "etp_edge_conv_vjp_radial_wgrad", "etp_edge_conv_vjp2_radial_wgrad", "etp_channel_mix_ex", "etp_channel_mix_vjp_ex", "etp_channel_mix_wgrad", "etp_node_product_vjp_wgrad", "etp_node_product_wgrad_workspace",
                "etp_status_string", "etp_version")
 
 
@@ -127,6 +127,8 @@ def _load():
         "etp_channel_mix_ex": (st, [vp, i32, vp, vp, i32, vp, u32, vp]),
         "etp_channel_mix_vjp_ex": (st, [vp, i32, vp, vp, i32, vp, u32, vp]),
         "etp_channel_mix_wgrad": (st, [vp, i32, vp, vp, vp, u32, vp, ctypes.c_size_t, vp]),
+        "etp_node_product_vjp_wgrad": (st, [vp, i32, i32, vp, vp, vp, vp, vp, u32, vp, ctypes.c_size_t, vp]),
+        "etp_node_product_wgrad_workspace": (st, [vp, i32, i32, vp]),
         "etp_edge_forces": (st, [ctypes.POINTER(etp_graph), vp, vp, u32, vp]),
         "etp_node_product": (st, [vp, i32, i32, vp, vp, vp, u32, vp]),
         "etp_channel_mix_vjp": (st, [vp, i32, vp, vp, vp, u32, vp]),
@@ -679,6 +681,33 @@ def etp_node_product_vjp(plan: Plan, A, W, grad_out, grad_A, corr_order: int, fl
                                     _ptr(grad_out, "grad_out", f32, n * D * C, optional=True),
                                     _ptr(grad_A, "grad_A", f32, n * D * C, optional=True), flags, _stream(stream)),
            "etp_node_product_vjp")
+
+
+def node_product_wgrad_workspace(plan: Plan, n: int, corr_order: int):
+    """A device workspace for etp_node_product_vjp_wgrad on n nodes."""
+    import torch
+    b = ctypes.c_size_t()
+    _check(lib.etp_node_product_wgrad_workspace(plan.handle, n, corr_order, ctypes.byref(b)),
+           "etp_node_product_wgrad_workspace")
+    return torch.empty(max(b.value, 16), dtype=torch.uint8, device="cuda")
+
+
+def etp_node_product_vjp_wgrad(plan: Plan, A, W, grad_out, grad_A, grad_W, corr_order: int, ws, flags: int = 0,
+                               stream=None):
+    """grad_A (may be None) and grad_W [corr_order-1, P, C] of <grad_out, etp_node_product(A, W)>."""
+    import torch
+    f32 = torch.float32
+    n = A.shape[0] if A is not None else 0
+    D = (plan.L + 1) ** 2
+    C = plan.C
+    P = len(etp_plan_tables(plan)["paths"])
+    wp, wb = _ws(ws)
+    _check(lib.etp_node_product_vjp_wgrad(plan.handle, n, corr_order, _ptr(A, "A", f32, n * D * C, optional=True),
+                                          _ptr(W, "W", f32, (corr_order - 1) * P * C, optional=True),
+                                          _ptr(grad_out, "grad_out", f32, n * D * C, optional=True),
+                                          _ptr(grad_A, "grad_A", f32, n * D * C, optional=True),
+                                          _ptr(grad_W, "grad_W", f32, (corr_order - 1) * P * C),
+                                          flags, wp, wb, _stream(stream)), "etp_node_product_vjp_wgrad")
 
 
 def etp_edge_tp_fwd(plan: Plan, vec, V, w, out, flags: int = 0, stream=None):

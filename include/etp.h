@@ -555,6 +555,35 @@ ETP_API etp_status etp_node_product_vjp(etp_plan_t plan, int32_t n_nodes, int32_
                                         const float *W, const float *grad_out, float *grad_A, uint32_t flags,
                                         void *stream);
 
+/* etp_node_product_vjp that also forms the gradient with respect to the
+ * weights (training the ladder; a sum over every node):
+ *   grad_W[k][p][u] = sum_i d<grad_out, out>/dW[k][p][u]
+ *                   = sum_i sum_{(m1, m2, m3) in p} C_p * Bbar_{k+2}[i][l3 row, m3][u]
+ *                         * B_{k+1}[i][l1 row, m1][u] * A[i][l2 row, m2][u]
+ * (Bbar the adjoints of the reverse pass, k = 0 .. corr_order-2). The
+ * reverse pass writes each node's [corr_order-1][P][C] block of partials to
+ * ws, and they are added over the nodes in index order (runs of nodes, then
+ * the runs in order): deterministic, no atomics. grad_A: as
+ * etp_node_product_vjp, or NULL (not computed); grad_W: DEVICE float
+ * [corr_order-1][P][C], the layout of W. ETP_FLAG_ACCUMULATE adds into
+ * grad_A and grad_W (with n_nodes = 0 grad_W is zeroed, or left as it is when
+ * accumulating). ws: DEVICE, 16-byte aligned, at least
+ * etp_node_product_wgrad_workspace(plan, n_nodes, corr_order) bytes, contents
+ * undefined afterwards. Errors: INVALID_ARGUMENT (null plan or grad_W, null A,
+ * W or grad_out with n_nodes > 0, negative n_nodes, corr_order outside
+ * [2, 8], other flags), UNSUPPORTED (a bf16 plan), WORKSPACE (ws missing,
+ * misaligned or too small), HIP. */
+ETP_API etp_status etp_node_product_vjp_wgrad(etp_plan_t plan, int32_t n_nodes, int32_t corr_order, const float *A,
+                                              const float *W, const float *grad_out, float *grad_A, float *grad_W,
+                                              uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace (bytes) of etp_node_product_vjp_wgrad: n_nodes * (corr_order-1)
+ * * P * C * 4 for the per-node partials plus 64 * (corr_order-1) * P * C * 4
+ * for the runs of their ordered sum. Host only. Errors: INVALID_ARGUMENT
+ * (null plan or bytes, negative n_nodes, corr_order outside [2, 8]). */
+ETP_API etp_status etp_node_product_wgrad_workspace(etp_plan_t plan, int32_t n_nodes, int32_t corr_order,
+                                                    size_t *bytes);
+
 /* Forces on the atoms from the per-edge energy gradient grad_vec = dE/dvec
  * (the VJP's grad_vec), with vec_e = pos[src_e] - pos[dst_e]:
  *   forces[k] = sum_{e in in(k)} grad_vec[e] - sum_{e in out(k)} grad_vec[e]

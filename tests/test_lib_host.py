@@ -32,7 +32,7 @@ def header_symbols():
 
 def test_header_symbols_exported():
     names = header_symbols()
-    assert len(names) == 36
+    assert len(names) == 38
     assert sorted(etp.ABI_SYMBOLS) == names
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (etp_\w+)$", out, flags=re.M))
@@ -170,6 +170,19 @@ def test_call_validation_without_device():
         assert fn(plan.handle, 4, 8, 8, 5, 8, 0, None) == INV   # unknown dtype
         assert fn(plan.handle, 4, 8, 8, F32, 8, 2, None) == INV
         assert fn(plan.handle, 0, None, None, BF, None, 0, None) == 0
+    npw = lib.etp_node_product_vjp_wgrad
+    assert npw(None, 4, 3, 8, 8, 8, None, 8, 0, 8, 1 << 20, None) == INV
+    assert npw(plan.handle, 4, 1, 8, 8, 8, None, 8, 0, 8, 1 << 20, None) == INV     # no weights at order 1
+    assert npw(plan.handle, 4, 9, 8, 8, 8, None, 8, 0, 8, 1 << 20, None) == INV
+    assert npw(plan.handle, 4, 3, 8, 8, 8, None, None, 0, 8, 1 << 20, None) == INV  # grad_W required
+    assert npw(plan.handle, 4, 3, None, 8, 8, None, 8, 0, 8, 1 << 20, None) == INV
+    assert npw(plan.handle, 4, 3, 16, 16, 16, None, 16, 2, 16, 1 << 20, None) == INV
+    assert npw(plan.handle, 4, 3, 16, 16, 16, None, 16, 0, None, 0, None) == etp.ETP_ERR_WORKSPACE
+    assert npw(plan.handle, 4, 3, 16, 16, 16, None, 16, 0, 16, 8, None) == etp.ETP_ERR_WORKSPACE
+    nb = ctypes.c_size_t()
+    assert lib.etp_node_product_wgrad_workspace(plan.handle, 10, 3, ctypes.byref(nb)) == 0
+    assert nb.value == 4 * (10 + 64) * 2 * len(oracle.paths(2)) * 128     # the plan: l_max 2, C 128
+    assert lib.etp_node_product_wgrad_workspace(plan.handle, 10, 1, ctypes.byref(nb)) == INV
     wg = lib.etp_channel_mix_wgrad
     assert wg(None, 4, 8, 8, 8, 0, None, 0, None) == INV
     assert wg(plan.handle, -1, 8, 8, 8, 0, None, 0, None) == INV
