@@ -67,6 +67,9 @@ namespace etp {
 #ifndef ETP_DST_ROWS_FWD3
 #define ETP_DST_ROWS_FWD3 ETP_DST_ROWS_FWD
 #endif
+#ifndef ETP_DST_ROWS_FWD3_BF16
+#define ETP_DST_ROWS_FWD3_BF16 88  // bf16 features, two channels per lane (112 spills there)
+#endif
 #ifndef ETP_DST_ROWS_FWD4
 #define ETP_DST_ROWS_FWD4 80
 #endif
@@ -85,13 +88,14 @@ namespace etp {
 #ifndef ETP_DST_WPE
 #define ETP_DST_WPE 0
 #endif
-template <int L, int CPL, int MODE>
+template <int L, int CPL, int MODE, bool BF>
 struct DstCfg {
     static constexpr int S = ETP_DST_S;
     static constexpr int B = L <= 2 ? ETP_DST_B2 : (L == 3 ? ETP_DST_B3 : ETP_DST_B4);
+    static constexpr int ROWS3 = (BF && CPL == 2) ? ETP_DST_ROWS_FWD3_BF16 : ETP_DST_ROWS_FWD3;
     static constexpr int ROWS = MODE == DST_DG_RADIAL ? ETP_DST_ROWS_RAD
                               : MODE == DST_FWD_RADIAL ? (L <= 2 ? ETP_DST_ROWS_FWD : ETP_DST_ROWS_RAD)
-                              : MODE == DST_FWD ? (L <= 2 ? ETP_DST_ROWS_FWD : L == 3 ? ETP_DST_ROWS_FWD3 : ETP_DST_ROWS_FWD4)
+                              : MODE == DST_FWD ? (L <= 2 ? ETP_DST_ROWS_FWD : L == 3 ? ROWS3 : ETP_DST_ROWS_FWD4)
                                                 : (L <= 2 ? ETP_DST_ROWS_DG : L == 3 ? ETP_DST_ROWS_DG3 : ETP_DST_ROWS_DG4);
     // (the dG pass with one channel per lane keeps 40-row groups at l <= 3:
     // one 51-row group at l = 2, C = 64 is 19% slower than two)
@@ -116,7 +120,7 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
                                           const int nbasis, const float *__restrict__ ggh)
 {
     using V = chv_t<CPL>;
-    using Cfg = DstCfg<L, CPL, MODE>;
+    using Cfg = DstCfg<L, CPL, MODE, sizeof(XT) == 2>;
     constexpr int S = Cfg::S, B = Cfg::B, TC = Cfg::TCOPIES;
     constexpr bool DG = MODE == DST_DG || MODE == DST_DG_RADIAL;
     constexpr bool RAD = MODE == DST_FWD_RADIAL || MODE == DST_DG_RADIAL;
@@ -354,7 +358,8 @@ __device__ __forceinline__ void dst_group(const int n_dst, const int C, const in
 }
 
 template <int L, int CPL, typename XT, int MODE>
-__global__ void __launch_bounds__((64 * DstCfg<L, CPL, MODE>::S)) __attribute__((amdgpu_waves_per_eu(DstCfg<L, CPL, MODE>::WPE)))
+__global__ void __launch_bounds__((64 * DstCfg<L, CPL, MODE, sizeof(XT) == 2>::S))
+    __attribute__((amdgpu_waves_per_eu(DstCfg<L, CPL, MODE, sizeof(XT) == 2>::WPE)))
     dst_kernel(const int n_dst, const int C, const int nchunk, const int *__restrict__ row_ptr,
                const int *__restrict__ src, const float *__restrict__ vec, const XT *__restrict__ x,
                const float *__restrict__ w, const float *__restrict__ ggx, const float *__restrict__ ggw,
@@ -363,7 +368,7 @@ __global__ void __launch_bounds__((64 * DstCfg<L, CPL, MODE>::S)) __attribute__(
                const float *__restrict__ ggh)
 {
     extern __shared__ float lds[];
-    constexpr Groups GR = make_groups(kTab<L>, DstCfg<L, CPL, MODE>::MAXROWS);
+    constexpr Groups GR = make_groups(kTab<L>, DstCfg<L, CPL, MODE, sizeof(XT) == 2>::MAXROWS);
     const int g = blockIdx.y;
     static_range<0, GR.n>([&](auto G) __attribute__((always_inline)) {
         if (g == G)
@@ -375,7 +380,7 @@ __global__ void __launch_bounds__((64 * DstCfg<L, CPL, MODE>::S)) __attribute__(
 template <int L, int CPL, typename XT, int MODE>
 static hipError_t launch_dst_t(const ConvArgs &a)
 {
-    using Cfg = DstCfg<L, CPL, MODE>;
+    using Cfg = DstCfg<L, CPL, MODE, sizeof(XT) == 2>;
     constexpr Groups GR = make_groups(kTab<L>, Cfg::MAXROWS);
     constexpr int LDS_FLOATS = Cfg::S * Cfg::TCOPIES * Cfg::B * max_stride(kTab<L>, GR) +
                                Cfg::S * Cfg::B * Cfg::HROWS * kRadialMax;
