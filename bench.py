@@ -407,10 +407,11 @@ def time_calls(f, reps, warm=2):
     return a.elapsed_time(b) / reps * 1e-3
 
 
-def time_radial(etp, p, fwd_ms, vjp_ms, reps, K=8):
+def time_radial(etp, p, reps, K=8):
     """The forward and VJP with radial weights formed in the kernel (w = h Wr,
     K basis functions) on the same graph and features as the step: ms per
-    call against the plain calls that read w (and write gw). Algorithmic
+    call against the plain calls that read w (and write gw), each timed the
+    same way (back-to-back calls) just before the radial one. Algorithmic
     bytes: the plain call's with the E P C weight streams replaced by h (and
     grad_h) and Wr; FLOPs: the plain call's plus 2 K per (edge, path,
     channel) to form w (and 2 K more for grad_h)."""
@@ -421,19 +422,24 @@ def time_radial(etp, p, fwd_ms, vjp_ms, reps, K=8):
     h, Wr = workloads.radial_inputs(E, K, L, C, seed=0)
     h, Wr = torch.from_numpy(h).cuda(), torch.from_numpy(Wr).cuda()
     y = torch.empty_like(p.out)
+    t_plain = time_calls(lambda: etp.etp_edge_conv_fwd(p.plan, p.g, p.vec, p.x, p.w, y), reps, 3)
     t = time_calls(lambda: etp.etp_edge_conv_fwd_radial(p.plan, p.g, p.vec, p.x, h, Wr, y), reps, 3)
     by, fl = compulsory(L, C, p.N, E, p.n_src)
     byts = by["fwd"] - 4.0 * E * P * C + 4.0 * (E * K + K * P * C)
     flops = fl["fwd"] + 2.0 * K * P * C * E
     res = {"ms": round(t * 1e3, 4), "edges_per_s": E / t, "n_basis": K,
-           "speedup_vs_fwd": round(fwd_ms * 1e-3 / t, 3), "algo_GBps": byts / t / 1e9,
+           "plain_fwd_ms": round(t_plain * 1e3, 4), "speedup_vs_fwd": round(t_plain / t, 3),
+           "algo_GBps": byts / t / 1e9,
            "algo_TFLOPs": flops / t / 1e12, "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS,
            "valu_frac": flops / t / 1e12 / VALU_PEAK_TFLOPS}
     gx, gh, gr = torch.empty_like(p.gx), torch.empty(E, K, device="cuda"), torch.empty_like(p.gr)
+    tv_plain = time_calls(lambda: etp.etp_edge_conv_vjp_ws(p.plan, p.g, p.vec, p.x, p.w, p.G, gx, p.gw, gr, p.bws),
+                          reps)
     tv = time_calls(lambda: etp.etp_edge_conv_vjp_radial(p.plan, p.g, p.vec, p.x, h, Wr, p.G, gx, gh, gr), reps)
     vb = by["vjp"] - 8.0 * E * P * C + 4.0 * (2 * E * K + K * P * C)
     vf = fl["vjp"] + 4.0 * K * P * C * E
-    res.update({"vjp_ms": round(tv * 1e3, 4), "vjp_speedup_vs_vjp": round(vjp_ms * 1e-3 / tv, 3),
+    res.update({"vjp_ms": round(tv * 1e3, 4), "plain_vjp_ms": round(tv_plain * 1e3, 4),
+                "vjp_speedup_vs_vjp": round(tv_plain / tv, 3),
                 "vjp_hbm_frac": vb / tv / 1e9 / HBM_PEAK_GBS, "vjp_valu_frac": vf / tv / 1e12 / VALU_PEAK_TFLOPS})
     # the VJP with the weight gradient (grad_Wr), and the VJP-of-VJP with and
     # without d_Wr (cotangents on grad_x, grad_h, grad_vec)
@@ -629,9 +635,8 @@ def next_ops(etp, reps):
     workload unless named."""
     import workloads
     p = Problem("micro")
-    per_op, _ = p.run(3, 1, ops=("transpose", "fwd", "vjp"))
     p.step(None, ("transpose", "fwd", "vjp"))
-    d = {"radial": time_radial(etp, p, per_op["fwd"], per_op["vjp"], reps),
+    d = {"radial": time_radial(etp, p, reps),
          "channel_mix": time_channel_mix(etp, p.plan, p.out, p.L, p.C, p.N, reps),
          "edge_forces": time_edge_forces(etp, p.g, p.gr, p.N, p.n_src, p.E, reps)}
     for name, (pos_np, box) in (("neighbor_list_water", workloads.water_positions(0)),
@@ -640,9 +645,8 @@ def next_ops(etp, reps):
     d["edge_tp"] = time_edge_tp(etp, p.plan, p.L, p.C, p.E, (p.L + 1) ** 2, p.P, p.wl.Dout, p.vec, p.w, reps)
     del p
     p3 = Problem("micro3")
-    per3, _ = p3.run(3, 1, ops=("transpose", "fwd", "vjp"))
     p3.step(None, ("transpose", "fwd", "vjp"))
-    d["radial_micro3"] = time_radial(etp, p3, per3["fwd"], per3["vjp"], reps)
+    d["radial_micro3"] = time_radial(etp, p3, reps)
     d["channel_mix_micro3"] = time_channel_mix(etp, p3.plan, p3.out, p3.L, p3.C, p3.N, reps)
     del p3
     # the mixing at the micro4 and diamond node counts and widths (its input
