@@ -222,7 +222,7 @@ def test_validate_flag_rejects_malformed_graph():
 
 # ------------------------------------------------------------------- bf16
 
-@pytest.mark.parametrize("L,C", [(1, 8), (2, 128), (3, 128)])
+@pytest.mark.parametrize("L,C", [(1, 8), (2, 128), (3, 128), (3, 200), (4, 130)])
 def test_bf16_features(L, C):
     say("bf16", L, C)
     wl = small_wl(L, C, "ragged")
