@@ -152,6 +152,12 @@ struct BwdCfg {
     static constexpr int WPE = V2 ? ETP_BWD_WPE_VJP2 : ETP_BWD_WPE_VJP;
 };
 
+// Whether paths a and b (both in range) have the same l1.
+constexpr bool same_l1(const Table &T, int a, int b)
+{
+    return a >= 0 && b < T.P && T.path[a].l1 == T.path[b].l1;
+}
+
 // Waves per workgroup: 64-channel chunks x edge splits, four in all.
 constexpr int bwd_splits(int nch) { return nch >= 4 ? 1 : 4 / nch; }
 
@@ -361,8 +367,8 @@ __device__ __forceinline__ void bwd_group(const int lb, const int n_dst, const i
             constexpr Path pa = kTab<L>.path[p];
             constexpr int d1 = 2 * pa.l1 + 1;
             constexpr int XO = pa.x_row - GI.xr0, GO = pa.out_row - GI.gr0, WQ = p - GI.p0;
-            constexpr bool FIRST_OF_L1 = (p == GI.p0) || kTab<L>.path[p - 1].l1 != pa.l1;
-            constexpr bool LAST_OF_L1 = (p + 1 == GI.p1) || kTab<L>.path[p + 1].l1 != pa.l1;
+            constexpr bool FIRST_OF_L1 = p == GI.p0 || !same_l1(kTab<L>, p - 1, p);
+            constexpr bool LAST_OF_L1 = p + 1 == GI.p1 || !same_l1(kTab<L>, p, p + 1);
             const float wv_ = o.w[WQ];
             float wpp = 0.f;
             if constexpr (V2)

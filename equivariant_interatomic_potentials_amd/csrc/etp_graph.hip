@@ -288,11 +288,15 @@ hipError_t launch_transpose(int n_dst, int n_src, int64_t E, const int *row_ptr,
     int *cursor = static_cast<int *>(ws);
     const int64_t ntile = (static_cast<int64_t>(n_src) + kScanTile - 1) / kScanTile;
     int *bsum = cursor + n_src;
-    fill_int<kTagTranspose>(src_ptr, static_cast<int64_t>(n_src) + 1, 0, stream);
+    hipError_t err = fill_int<kTagTranspose>(src_ptr, static_cast<int64_t>(n_src) + 1, 0, stream);
+    if (err != hipSuccess)
+        return err;
     if (E > 0)
         hipLaunchKernelGGL(hist_kernel, dim3(grid_for(E)), dim3(256), 0, stream, E, src, src_ptr + 1);
     if (n_src > 0) {
-        counts_to_offsets<kTagTranspose>(src_ptr, n_src, bsum, stream);
+        err = counts_to_offsets<kTagTranspose>(src_ptr, n_src, bsum, stream);
+        if (err != hipSuccess)
+            return err;
         hipLaunchKernelGGL(copy_kernel, dim3(grid_for(n_src)), dim3(256), 0, stream, cursor, src_ptr,
                            static_cast<int64_t>(n_src));
     }
