@@ -72,6 +72,13 @@ enum { BWD_VJP = 0, BWD_VJP2 = 1 };
 #ifndef ETP_BWD_LDS_BATCH
 #define ETP_BWD_LDS_BATCH 16384
 #endif
+// VJP-of-VJP contraction order: 1 = per (m1, m2) group the three products
+// u, v (X' K, x K over m1) and part += eta K, the SH factors applied per
+// (path, m2) afterwards, on the paths where that takes fewer operations;
+// 0 = s, sd (Y K, Yd K over m2) and Z, Z2 per group on every path
+#ifndef ETP_BWD_UV
+#define ETP_BWD_UV 1
+#endif
 
 // Path groups of the destination-side backward: contiguous paths whose
 // registers fit: gmul per resident G row (G, and dG for the VJP-of-VJP),
@@ -363,7 +370,83 @@ __device__ __forceinline__ void bwd_group(const int lb, const int n_dst, const i
         const rsrc_t rpt = make_rsrc(want_x ? part + static_cast<int64_t>(e) * (DIN * C) : nullptr,
                                      want_x ? DIN * C * 4u : 0u);
         float acc[NXR];  // the edge's part rows of the group's l1 blocks
+        // VJP-of-VJP per path in the order that needs one FMA fewer per
+        // (m1, m2) group: with K[a, b] = sum_c C g[c] and, per m2 = b,
+        //   u[b] = sum_a X'[a] K,  v[b] = sum_a x[a] K,  eta[b] = W' Y_b + w Yd_b,
+        // the part rows take part[a] += eta[b] K per group, and
+        //   dw = sum_b Y_b u[b] + Yd_b v[b],  Z[b] += w u[b] + W' v[b],  Z2[b] += w v[b]
+        // per (path, b): the same sums as s, sd, xx, wx below, regrouped.
+        auto path_uv = [&](auto p) {
+            constexpr Path pa = kTab<L>.path[p];
+            constexpr int d1 = 2 * pa.l1 + 1, d2 = 2 * pa.l2 + 1, YB = pa.y_row;
+            constexpr int XO = pa.x_row - GI.xr0, GO = pa.out_row - GI.gr0, WQ = p - GI.p0;
+            constexpr int PA0 = kTab<L>.path_ab0[p], PA1 = kTab<L>.path_ab0[p + 1];
+            constexpr bool FIRST_OF_L1 = p == GI.p0 || !same_l1(kTab<L>, p - 1, p);
+            constexpr bool LAST_OF_L1 = p + 1 == GI.p1 || !same_l1(kTab<L>, p, p + 1);
+            const float wv_ = o.w[WQ], wpp = o.wp[WQ];
+            float eta[d2], u[d2], v[d2];
+            static_range<0, d2>([&](auto m) {
+                if constexpr (ab_touches_b(kTab<L>, PA0, PA1, YB + m))
+                    eta[m] = fmaf(wv_, Ydb[YB + m], wpp * Yb[YB + m]);
+            });
+            static_range<PA0, PA1>([&](auto gq) {
+                constexpr ABGroup ag = kTab<L>.ab[gq];
+                constexpr int a = ag.m1 + pa.l1, m = pa.l2 + ag.m2;
+                float K;
+                static_range<ag.t0, ag.t1>([&](auto ti) {
+                    constexpr Entry en = kTab<L>.nz[kTab<L>.ab_entries[ti]];
+                    if constexpr (ti == ag.t0)
+                        K = en.fval * g[GO + en.m3 + pa.l3];
+                    else
+                        K = fmaf(en.fval, g[GO + en.m3 + pa.l3], K);
+                });
+                if constexpr (ab_first_b(kTab<L>, PA0, gq)) {
+                    u[m] = o.xp[XO + a] * K;
+                    v[m] = o.x[XO + a] * K;
+                } else {
+                    u[m] = fmaf(o.xp[XO + a], K, u[m]);
+                    v[m] = fmaf(o.x[XO + a], K, v[m]);
+                }
+                if constexpr (FIRST_OF_L1 && ab_first_m1(kTab<L>, gq))
+                    acc[XO + a] = eta[m] * K;
+                else
+                    acc[XO + a] = fmaf(eta[m], K, acc[XO + a]);
+            });
+            // the path's weight row takes the next edge's
+            load_w(p, nx);
+            float gwv = 0.f;
+            bool started = false;
+            static_range<0, d2>([&](auto m) {
+                constexpr int b = YB + m;
+                if constexpr (ab_touches_b(kTab<L>, PA0, PA1, b)) {
+                    gwv = started ? fmaf(Yb[b], u[m], fmaf(Ydb[b], v[m], gwv)) : fmaf(Yb[b], u[m], Ydb[b] * v[m]);
+                    started = true;
+                    if constexpr (!ab_touches_b(kTab<L>, GI.ab0, PA0, b)) {  // b's first path in the group
+                        Z[b] = fmaf(wv_, u[m], wpp * v[m]);
+                        Z2[b] = wv_ * v[m];
+                    } else {
+                        Z[b] = fmaf(wv_, u[m], fmaf(wpp, v[m], Z[b]));
+                        Z2[b] = fmaf(wv_, v[m], Z2[b]);
+                    }
+                }
+            });
+            bstore<float, kNT>(gwv, rgw, off4, p * rowb);
+            if constexpr (LAST_OF_L1) {
+                static_range<0, d1>([&](auto a) {
+                    constexpr int r = XO + a;
+                    float val = acc[r];
+                    if constexpr (r < SHARED_ROWS)
+                        val += bload<float>(rpt, off4, (GI.xr0 + r) * rowb);
+                    bstore<float, kNT>(val, rpt, off4, (GI.xr0 + r) * rowb);
+                });
+                static_range<0, d1>([&](auto a) { load_x(ic<XO + a>{}, nx); });
+            }
+        };
         static_range<GI.p0, GI.p1>([&](auto p) {
+            if constexpr (V2 && ETP_BWD_UV && uv_cheaper(kTab<L>, p)) {
+                path_uv(p);
+                return;
+            }
             constexpr Path pa = kTab<L>.path[p];
             constexpr int d1 = 2 * pa.l1 + 1;
             constexpr int XO = pa.x_row - GI.xr0, GO = pa.out_row - GI.gr0, WQ = p - GI.p0;

@@ -185,6 +185,18 @@ constexpr bool ab_touches_b(const Table &T, int g0, int g1, int b)
     return false;
 }
 
+// Whether the VJP-of-VJP of path p takes fewer VALU operations per channel
+// in the u / v order (per (m1, m2) group: K + 3; per m2 used: 7) than in the
+// s / sd order (per group: K + 4; per m1: 7).
+constexpr bool uv_cheaper(const Table &T, int p)
+{
+    const int nab = T.path_ab0[p + 1] - T.path_ab0[p];
+    int nb = 0;
+    for (int m = 0; m < 2 * T.path[p].l2 + 1; ++m)
+        nb += ab_touches_b(T, T.path_ab0[p], T.path_ab0[p + 1], T.path[p].y_row + m) ? 1 : 0;
+    return nab + 7 * (2 * T.path[p].l1 + 1) > 7 * nb;
+}
+
 // SH indices touched by the paths [p0, p1): [lo, hi).
 constexpr int sh_lo(const Table &T, int p0, int p1)
 {

@@ -68,6 +68,13 @@ namespace etp {
 #ifndef ETP_SRC_COST_VJP
 #define ETP_SRC_COST_VJP 60
 #endif
+// VJP-of-VJP contraction order (plain mode): 1 = per (m1, m2) group u, v
+// (X' K, x K over m1) and dx += eta K, the SH factors applied per (path, m2)
+// afterwards, on the paths where that takes fewer operations; 0 = s, sd and
+// Z, Z2 per group on every path
+#ifndef ETP_SRC_UV
+#define ETP_SRC_UV 1
+#endif
 #ifndef ETP_SRC_COST_VJP2
 #define ETP_SRC_COST_VJP2 100  // one group at l = 2 (two waves per SIMD; 40: four groups, 15% slower)
 #endif
@@ -386,10 +393,71 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
             }
             static_range<0, RK>([&](auto k) { ghk[k] = 0.f; });
         }
+        // VJP-of-VJP of one path in the order with one FMA fewer per (m1, m2)
+        // group: u[b] = sum_a X'[a] K, v[b] = sum_a x[a] K, eta[b] = W' Y_b + w Yd_b;
+        // dx[a] += eta[b] K per group, then per (path, b) used
+        //   dw = sum_b Y_b u[b] + Yd_b v[b],  Z[b] += w u[b] + W' v[b],  Z2[b] += w v[b]
+        // (the sums of s, sd, xx and wx below, regrouped)
+        auto path_uv = [&](auto p) {
+            constexpr Path pa = kTab<L>.path[p];
+            constexpr int d2 = 2 * pa.l2 + 1, YB = pa.y_row;
+            constexpr int XO = pa.x_row - GI.xr0, GO = pa.out_row - GI.gr0, WQ = p - GI.p0;
+            constexpr int PA0 = kTab<L>.path_ab0[p], PA1 = kTab<L>.path_ab0[p + 1];
+            const float wp = o.w[WQ], wpp = o.wp[WQ];
+            float eta[d2], u[d2], v[d2];
+            static_range<0, d2>([&](auto m) {
+                if constexpr (ab_touches_b(kTab<L>, PA0, PA1, YB + m))
+                    eta[m] = fmaf(wp, Ydb[YB + m], wpp * Yb[YB + m]);
+            });
+            static_range<PA0, PA1>([&](auto g) {
+                constexpr ABGroup ag = kTab<L>.ab[g];
+                constexpr int a = ag.m1 + pa.l1, m = pa.l2 + ag.m2;
+                float K;
+                static_range<ag.t0, ag.t1>([&](auto ti) {
+                    constexpr Entry en = kTab<L>.nz[kTab<L>.ab_entries[ti]];
+                    if constexpr (ti == ag.t0)
+                        K = en.fval * o.g[GO + en.m3 + pa.l3];
+                    else
+                        K = fmaf(en.fval, o.g[GO + en.m3 + pa.l3], K);
+                });
+                if constexpr (ab_first_b(kTab<L>, PA0, g)) {
+                    u[m] = xpr[XO + a] * K;
+                    v[m] = xr[XO + a] * K;
+                } else {
+                    u[m] = fmaf(xpr[XO + a], K, u[m]);
+                    v[m] = fmaf(xr[XO + a], K, v[m]);
+                }
+                acc[XO + a] = fmaf(eta[m], K, acc[XO + a]);
+            });
+            load_path(p, nx);
+            float gwv = 0.f;
+            bool started = false;
+            static_range<0, d2>([&](auto m) {
+                constexpr int b = YB + m;
+                if constexpr (ab_touches_b(kTab<L>, PA0, PA1, b)) {
+                    gwv = started ? fmaf(Yb[b], u[m], fmaf(Ydb[b], v[m], gwv)) : fmaf(Yb[b], u[m], Ydb[b] * v[m]);
+                    started = true;
+                    if constexpr (!ab_touches_b(kTab<L>, GI.ab0, PA0, b)) {  // b's first path in the group
+                        Z[b] = fmaf(wp, u[m], wpp * v[m]);
+                        Z2[b] = wp * v[m];
+                    } else {
+                        Z[b] = fmaf(wp, u[m], fmaf(wpp, v[m], Z[b]));
+                        Z2[b] = fmaf(wp, v[m], Z2[b]);
+                    }
+                }
+            });
+            bstore<float, kNT>(gwv, rgw, off4, p * rowb);
+        };
         static_range<GI.p0, GI.p1>([&](auto p) {
 #ifdef ETP_SRC_SCHED_FENCE
             __builtin_amdgcn_sched_barrier(0);
 #endif
+            // (l_max <= 2 only: at 3 and 4 its extra live values spill in the
+            // larger path groups)
+            if constexpr (MODE == SRC_VJP2 && ETP_SRC_UV && L <= 2 && uv_cheaper(kTab<L>, p)) {
+                path_uv(p);
+                return;
+            }
             constexpr Path pa = kTab<L>.path[p];
             constexpr int d1 = 2 * pa.l1 + 1;
             constexpr int XO = pa.x_row - GI.xr0, GO = pa.out_row - GI.gr0, WQ = p - GI.p0;
