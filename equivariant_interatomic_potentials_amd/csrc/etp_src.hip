@@ -452,9 +452,12 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
 #ifdef ETP_SRC_SCHED_FENCE
             __builtin_amdgcn_sched_barrier(0);
 #endif
-            // (l_max <= 2 only: at 3 and 4 its extra live values spill in the
-            // larger path groups)
-            if constexpr (MODE == SRC_VJP2 && ETP_SRC_UV && L <= 2 && uv_cheaper(kTab<L>, p)) {
+            // (at l_max = 3 only on paths whose u, v, eta take no more registers
+            // than s, sd, wx, xx; at l_max = 4 on none: its larger path groups
+            // spill either way)
+            if constexpr (MODE == SRC_VJP2 && ETP_SRC_UV && uv_cheaper(kTab<L>, p) &&
+                          (L <= 2 ||
+                           (L == 3 && 3 * (2 * kTab<L>.path[p].l2 + 1) <= 4 * (2 * kTab<L>.path[p].l1 + 1)))) {
                 path_uv(p);
                 return;
             }
