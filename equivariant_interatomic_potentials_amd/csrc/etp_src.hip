@@ -68,7 +68,7 @@ namespace etp {
 #ifndef ETP_SRC_COST_VJP
 #define ETP_SRC_COST_VJP 60
 #endif
-// VJP-of-VJP contraction order (plain mode): 1 = per (m1, m2) group u, v
+// VJP-of-VJP contraction order (plain and radial modes): 1 = per (m1, m2) group u, v
 // (X' K, x K over m1) and dx += eta K, the SH factors applied per (path, m2)
 // afterwards, on the paths where that takes fewer operations; 0 = s, sd and
 // Z, Z2 per group on every path
@@ -393,6 +393,18 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
             }
             static_range<0, RK>([&](auto k) { ghk[k] = 0.f; });
         }
+        // the radial weight of path slot q: sum_k a[k] Wr[k, p, u], k in order
+        // (a = the edge's h row for w, its H' row for W')
+        auto wr_dot = [&](auto q, const float4 &a0, const float4 &a1) {
+            float t = a0.x * wr[q][0];
+            t = fmaf(a0.y, wr[q][1], t);
+            t = fmaf(a0.z, wr[q][2], t);
+            t = fmaf(a0.w, wr[q][3], t);
+            t = fmaf(a1.x, wr[q][4], t);
+            t = fmaf(a1.y, wr[q][5], t);
+            t = fmaf(a1.z, wr[q][6], t);
+            return fmaf(a1.w, wr[q][7], t);
+        };
         // VJP-of-VJP of one path in the order with one FMA fewer per (m1, m2)
         // group: u[b] = sum_a X'[a] K, v[b] = sum_a x[a] K, eta[b] = W' Y_b + w Yd_b;
         // dx[a] += eta[b] K per group, then per (path, b) used
@@ -403,7 +415,14 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
             constexpr int d2 = 2 * pa.l2 + 1, YB = pa.y_row;
             constexpr int XO = pa.x_row - GI.xr0, GO = pa.out_row - GI.gr0, WQ = p - GI.p0;
             constexpr int PA0 = kTab<L>.path_ab0[p], PA1 = kTab<L>.path_ab0[p + 1];
-            const float wp = o.w[WQ], wpp = o.wp[WQ];
+            float wp, wpp;
+            if constexpr (RAD) {
+                wp = wr_dot(ic<WQ>{}, h0, h1);
+                wpp = wr_dot(ic<WQ>{}, hp0, hp1);
+            } else {
+                wp = o.w[WQ];
+                wpp = o.wp[WQ];
+            }
             float eta[d2], u[d2], v[d2];
             static_range<0, d2>([&](auto m) {
                 if constexpr (ab_touches_b(kTab<L>, PA0, PA1, YB + m))
@@ -446,18 +465,33 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
                     }
                 }
             });
-            bstore<float, kNT>(gwv, rgw, off4, p * rowb);
+            if constexpr (RAD)  // d_h[e, k] += d_w[e, p, u] Wr[k, p, u] (summed over lanes later)
+                static_range<0, RK>([&](auto k) { ghk[k] = fmaf(gwv, wr[WQ][k], ghk[k]); });
+            else
+                bstore<float, kNT>(gwv, rgw, off4, p * rowb);
+            if constexpr (WG) {
+                // dWr[k, p, u] += h[e, k] dw + H'[e, k] gw, with the plain
+                // gw = sum_m1 x s = sum_b Y_b v[b]
+                float gpl = 0.f;
+                static_range<0, d2>([&](auto m) {
+                    if constexpr (ab_touches_b(kTab<L>, PA0, PA1, YB + m))
+                        gpl = fmaf(Yb[YB + m], v[m], gpl);
+                });
+                const float hk[RK] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+                const float hpk[RK] = {hp0.x, hp0.y, hp0.z, hp0.w, hp1.x, hp1.y, hp1.z, hp1.w};
+                static_range<0, RK>([&](auto k) { wg[WQ][k] = fmaf(hpk[k], gpl, fmaf(hk[k], gwv, wg[WQ][k])); });
+            }
         };
         static_range<GI.p0, GI.p1>([&](auto p) {
 #ifdef ETP_SRC_SCHED_FENCE
             __builtin_amdgcn_sched_barrier(0);
 #endif
-            // (at l_max = 3 only on paths whose u, v, eta take no more registers
-            // than s, sd, wx, xx; at l_max = 4 on none: its larger path groups
-            // spill either way)
-            if constexpr (MODE == SRC_VJP2 && ETP_SRC_UV && uv_cheaper(kTab<L>, p) &&
-                          (L <= 2 ||
-                           (L == 3 && 3 * (2 * kTab<L>.path[p].l2 + 1) <= 4 * (2 * kTab<L>.path[p].l1 + 1)))) {
+            // (at l_max = 3 only without radial weights and on paths whose u, v,
+            // eta take no more registers than s, sd, wx, xx; at l_max = 4 on
+            // none: the larger path groups spill either way)
+            if constexpr (V2 && ETP_SRC_UV && uv_cheaper(kTab<L>, p) &&
+                          (L <= 2 || (L == 3 && !RAD &&
+                                      3 * (2 * kTab<L>.path[p].l2 + 1) <= 4 * (2 * kTab<L>.path[p].l1 + 1)))) {
                 path_uv(p);
                 return;
             }
@@ -465,31 +499,15 @@ __device__ __forceinline__ void src_group(const int n_src, const int C, const in
             constexpr int d1 = 2 * pa.l1 + 1;
             constexpr int XO = pa.x_row - GI.xr0, GO = pa.out_row - GI.gr0, WQ = p - GI.p0;
             float wp;
-            if constexpr (RAD) {  // w[e, p, u] = sum_k h[e, k] Wr[k, p, u], k in order
-                float t = h0.x * wr[WQ][0];
-                t = fmaf(h0.y, wr[WQ][1], t);
-                t = fmaf(h0.z, wr[WQ][2], t);
-                t = fmaf(h0.w, wr[WQ][3], t);
-                t = fmaf(h1.x, wr[WQ][4], t);
-                t = fmaf(h1.y, wr[WQ][5], t);
-                t = fmaf(h1.z, wr[WQ][6], t);
-                wp = fmaf(h1.w, wr[WQ][7], t);
-            } else {
+            if constexpr (RAD)  // w[e, p, u] = sum_k h[e, k] Wr[k, p, u]
+                wp = wr_dot(ic<WQ>{}, h0, h1);
+            else
                 wp = o.w[WQ];
-            }
             float wpp = 0.f;
-            if constexpr (V2 && RAD) {  // W'[e, p, u] = sum_k H'[e, k] Wr[k, p, u], k in order
-                float t = hp0.x * wr[WQ][0];
-                t = fmaf(hp0.y, wr[WQ][1], t);
-                t = fmaf(hp0.z, wr[WQ][2], t);
-                t = fmaf(hp0.w, wr[WQ][3], t);
-                t = fmaf(hp1.x, wr[WQ][4], t);
-                t = fmaf(hp1.y, wr[WQ][5], t);
-                t = fmaf(hp1.z, wr[WQ][6], t);
-                wpp = fmaf(hp1.w, wr[WQ][7], t);
-            } else if constexpr (V2) {
+            if constexpr (V2 && RAD)  // W'[e, p, u] = sum_k H'[e, k] Wr[k, p, u]
+                wpp = wr_dot(ic<WQ>{}, hp0, hp1);
+            else if constexpr (V2)
                 wpp = o.wp[WQ];
-            }
             float wx[d1], xx[V2 ? d1 : 1], s[d1], sd[V2 ? d1 : 1];
             static_range<0, d1>([&](auto a) {
                 wx[a] = wp * xr[XO + a];
